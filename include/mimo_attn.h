@@ -1,0 +1,200 @@
+/*
+ * mimo_attn.h -- C ABI of the MI355X (gfx950) MiMo-V2-Flash hybrid attention library.
+ *
+ * The operation (Hugging Face Transformers model doc "MiMo-V2-Flash"):
+ *   - Key features: sliding-window attention (SWA) and global attention (GA)
+ *     layers alternate 5:1; the window is 128 tokens; a learnable attention
+ *     sink bias keeps long-context quality.
+ *   - MiMoV2FlashConfig: num_attention_heads (64), num_key_value_heads (4,
+ *     grouped-query attention), head_dim (192, queries and keys), v_head_dim
+ *     (128), sliding_window (129), attention_value_scale (0.707).
+ *   - MiMoV2FlashModel.forward / past_key_values: a cache holds the keys and
+ *     values of earlier tokens, and with a cache only the unprocessed tokens are
+ *     passed.  The decoder is causal (MiMoV2FlashForCausalLM).
+ *
+ * For a query token at position p of its sequence and query head h, with
+ * G = num_q_heads / num_kv_heads and g = h / G:
+ *   keys       j in [lo, p],  lo = 0 (GA)  or  max(0, p - (sliding_window - 1)) (SWA)
+ *   s_j        = softmax_scale * dot(q[p,h,:], k[j,g,:])
+ *   M          = max(max_j s_j, sink[h])            (sink left out when absent)
+ *   Z          = sum_j exp(s_j - M) + exp(sink[h] - M)
+ *   lse[p,h]   = M + ln Z                            (natural log, sink included)
+ *   out[p,h,e] = value_scale * sum_j exp(s_j - lse) * v[j,g,e]
+ * The sink joins the softmax denominator only; it has no value row.  A NULL
+ * sink pointer, or a sink value of -inf, means "no sink".
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers on the current HIP device unless
+ *     marked (host).  bf16 tensors are passed as uint16_t bit patterns.
+ *   - Layouts are dense, row-major, token-major:
+ *       q   [T][Hq][192]     k [T][Hkv][192]     v [T][Hkv][128]
+ *       out [T][Hq][128]     lse [T][Hq] (fp32)  sink [Hq] (fp32)
+ *     Every tensor must be 16-byte aligned.
+ *   - The caller allocates and owns every buffer (caches, workspace included).
+ *     The library allocates nothing, keeps no state between calls, never
+ *     synchronises the device and never writes ctx_lens.
+ *   - Work is enqueued asynchronously on `stream` (NULL = the null stream).
+ *   - Misuse detectable on the host returns a status BEFORE anything is
+ *     enqueued.  A failed launch returns MIMO_ERR_HIP.  mimo_last_error()
+ *     gives a message for the calling thread's most recent failure.
+ *   - Supported shapes: head_dim_qk == 192, head_dim_v == 128 and
+ *     num_q_heads == 16 * num_kv_heads; anything else is MIMO_ERR_UNSUPPORTED.
+ *   - Inputs must be finite.  Device-resident preconditions (monotone
+ *     cu_seqlens, ctx_lens within the stated bounds) are not checked on the
+ *     device except where an entry point says so.
+ *   - Calls are reentrant; calls on different streams may run concurrently
+ *     when their output buffers do not overlap.
+ */
+#ifndef MIMO_ATTN_H
+#define MIMO_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MIMO_ATTN_ABI_VERSION 1
+
+/* Layer type: which key set a query sees (model doc, Key features; config
+ * layer_types). */
+typedef enum {
+    MIMO_LAYER_SWA = 0, /* keys p-(sliding_window-1) .. p */
+    MIMO_LAYER_GA = 1   /* keys 0 .. p (global causal)    */
+} mimo_layer_type;
+
+typedef enum {
+    MIMO_OK = 0,
+    MIMO_ERR_INVALID_ARG = 1, /* NULL pointer, negative size, bad layer type ... */
+    MIMO_ERR_UNSUPPORTED = 2, /* shape outside the specialised kernels        */
+    MIMO_ERR_WORKSPACE = 3,   /* decode workspace missing or too small         */
+    MIMO_ERR_HIP = 4          /* a HIP launch or query failed                  */
+} mimo_status;
+
+/* Attention shape, mirroring MiMoV2FlashConfig (model doc, MiMoV2FlashConfig):
+ * num_attention_heads, num_key_value_heads, head_dim, v_head_dim,
+ * sliding_window and attention_value_scale; softmax_scale is 1/sqrt(head_dim)
+ * for the model.  Passed by host pointer. */
+typedef struct {
+    int32_t num_q_heads;    /* Hq  = 64                                       */
+    int32_t num_kv_heads;   /* Hkv = 4; Hq / Hkv must be 16                   */
+    int32_t head_dim_qk;    /* 192                                            */
+    int32_t head_dim_v;     /* 128                                            */
+    int32_t sliding_window; /* W = 129: SWA keys p-(W-1)..p; ignored for GA   */
+    float softmax_scale;    /* multiplies q.k; 1/sqrt(192) for the model      */
+    float value_scale;      /* multiplies the output; 1.0, or 0.707 for the   */
+                            /* model's attention_value_scale                  */
+} mimo_attn_dims;
+
+/*
+ * Prefill: attention of every token of num_seqs packed variable-length
+ * sequences over keys of its own sequence (model doc, MiMoV2FlashModel.forward:
+ * a batch of sequences without a cache; padding replaced by packing).
+ *
+ *   q, k, v      packed tokens, layouts above; sequence b owns tokens
+ *                cu_seqlens[b] .. cu_seqlens[b+1]-1 and its positions start at 0.
+ *   cu_seqlens   [num_seqs+1] int32 (device), cu_seqlens[0] == 0, non-decreasing.
+ *   num_seqs     >= 1 (host).
+ *   max_seqlen   (host) >= every sequence length; sizes the grid.  Tokens of a
+ *                longer sequence beyond max_seqlen are left unwritten.
+ *   sink         [Hq] fp32 (device) or NULL.
+ *   out          [T][Hq][128] bf16, rounded to nearest even.
+ *   lse          [T][Hq] fp32, or NULL to skip it.
+ * A call with max_seqlen == 0 enqueues nothing and returns MIMO_OK.
+ */
+int mimo_attn_prefill(const mimo_attn_dims* dims, int layer_type,
+                      const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                      const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+                      const float* sink, uint16_t* out, float* lse, hipStream_t stream);
+
+/*
+ * Bytes of device workspace mimo_attn_decode needs for these arguments.  SWA
+ * needs none (returns 0).  GA needs batch * ceil((max_ctx+1)/split) * Hq * 130
+ * * 4 bytes for the per-split partial results.  split_tokens <= 0 selects the
+ * default (2048).  Returns 0 for arguments mimo_attn_decode would reject.
+ */
+size_t mimo_attn_decode_workspace_size(const mimo_attn_dims* dims, int layer_type,
+                                       int32_t batch, int32_t max_ctx, int32_t split_tokens);
+
+/*
+ * Decode: attention of ONE new token per sequence, at position p = ctx_lens[b],
+ * over cached keys and itself (model doc, past_key_values: only the
+ * unprocessed token is passed; earlier keys come from the cache).
+ *
+ *   q            [batch][Hq][192] bf16, the new tokens' queries.
+ *   k_new, v_new [batch][Hkv][192], [batch][Hkv][128]: the new tokens' key and
+ *                value (position p is read from here, not from the cache).
+ *   k_cache, v_cache
+ *                SWA: ring [batch][W-1][Hkv][192], [batch][W-1][Hkv][128];
+ *                     position j of sequence b lives in slot j mod (W-1).
+ *                GA:  pool [N][Hkv][192], [N][Hkv][128]; position j of
+ *                     sequence b lives in row kv_base[b] + j.
+ *   kv_base      GA: [batch] int64 (device); SWA: ignored (may be NULL).
+ *   ctx_lens     [batch] int32 (device): tokens already cached; 0 <= p <= max_ctx.
+ *   batch        >= 1 (host).
+ *   max_ctx      (host) >= every ctx_lens[b]; sizes the GA split grid.  A GA
+ *                sequence with ctx_lens[b] > max_ctx gets NaN outputs.
+ *   split_tokens GA keys per split workgroup (host); <= 0 selects 2048;
+ *                rounded up to a multiple of 32.  Results do not depend on it
+ *                beyond fp32 rounding.
+ *   sink, out, lse  as for prefill, with T = batch; lse may be NULL.
+ *   workspace    device buffer of >= mimo_attn_decode_workspace_size(...) bytes
+ *                (GA only; NULL allowed for SWA).  Its contents need no
+ *                initialisation and are scratch after the call.
+ * Order for a decode step is attend, then append: this call reads cache
+ * positions < p only, so the caller appends position p (mimo_kv_append) after
+ * it.  For SWA this order is required, because slot p mod (W-1) still holds
+ * position p-(W-1), which query p needs.
+ */
+int mimo_attn_decode(const mimo_attn_dims* dims, int layer_type,
+                     const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                     const uint16_t* k_cache, const uint16_t* v_cache,
+                     const int64_t* kv_base, const int32_t* ctx_lens,
+                     int32_t batch, int32_t max_ctx, int32_t split_tokens,
+                     const float* sink, uint16_t* out, float* lse,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * KV append: writes new tokens' keys and values into the caches (model doc,
+ * past_key_values / use_cache).  New token i of sequence b has position
+ * ctx_lens[b] + i.
+ *
+ *   k, v         packed new tokens [Tn][Hkv][192], [Tn][Hkv][128] bf16.
+ *   cu_newlens   [batch+1] int32 (device): sequence b owns new tokens
+ *                cu_newlens[b] .. cu_newlens[b+1]-1 (prefill: cu_seqlens with
+ *                ctx_lens all 0; decode step: 0,1,..,batch).
+ *   ctx_lens     [batch] int32 (device): positions already cached.
+ *   batch        >= 1 (host).
+ *   total_new    (host) == cu_newlens[batch]; sizes the grid.
+ *   k_cache, v_cache  as for decode.
+ *   kv_base, kv_capacity  GA: [batch] int64 (device) -- sequence b may use pool
+ *                rows kv_base[b] .. kv_base[b] + kv_capacity[b] - 1.  A
+ *                sequence whose ctx_lens[b] + new tokens exceeds its capacity is
+ *                skipped entirely (nothing written for it).  SWA: ignored.
+ * SWA keeps, per sequence, only the last W-1 positions: a token is written to
+ * slot position mod (W-1) when position >= ctx_lens[b] + n_b - (W-1).
+ * Repeating a call with the same arguments writes the same bytes.
+ */
+int mimo_kv_append(const mimo_attn_dims* dims, int layer_type,
+                   const uint16_t* k, const uint16_t* v,
+                   const int32_t* cu_newlens, const int32_t* ctx_lens,
+                   int32_t batch, int32_t total_new,
+                   uint16_t* k_cache, uint16_t* v_cache,
+                   const int64_t* kv_base, const int64_t* kv_capacity, hipStream_t stream);
+
+/* Static English name of a status code ("MIMO_OK", ...). */
+const char* mimo_status_string(int status);
+
+/* Message describing the calling thread's most recent non-OK return ("" if none). */
+const char* mimo_last_error(void);
+
+/* MIMO_ATTN_ABI_VERSION of the loaded library. */
+int mimo_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MIMO_ATTN_H */

@@ -1,0 +1,186 @@
+"""fp64 CPU oracle for MiMo-V2-Flash hybrid SWA/GA attention with a per-head sink.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  It shares no code with
+the GPU library: the arithmetic lives in ``mimo_oracle.c`` (plain C, double
+precision, libm ``exp``/``log``), built with gcc into ``libmimo_oracle.so`` next
+to this file.  The definition it follows is written out in the header comment
+of ``mimo_oracle.c`` with its citations (Hugging Face Transformers model doc
+"MiMo-V2-Flash": Key features; MiMoV2FlashConfig; MiMoV2FlashModel.forward).
+
+Arrays are numpy.  bf16 tensors travel as their uint16 bit patterns; the C code
+widens them exactly to double.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(HERE, "mimo_oracle.c")
+LIBRARY = os.path.join(HERE, "libmimo_oracle.so")
+
+SWA = 0
+GA = 1
+
+OK = 0
+EINVAL = 1
+ECAPACITY = 2
+
+
+def build(source: str = SOURCE, output: str = LIBRARY, extra_flags: tuple = ()) -> str:
+    """Compile the oracle with gcc (always recompiles)."""
+    tmp = output + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared", *extra_flags,
+           "-o", tmp, source, "-lpthread", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, output)
+    return output
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_I64 = ctypes.c_int64
+
+
+class Oracle:
+    """ctypes handle on one build of the oracle library."""
+
+    def __init__(self, path: str = LIBRARY):
+        if not os.path.exists(path):
+            raise FileNotFoundError(f"oracle library {path} is not built; run oracle.build()")
+        self.path = path
+        lib = ctypes.CDLL(path)
+        lib.oracle_prefill.restype = _I
+        lib.oracle_prefill.argtypes = [_I, _I, _I, _I, _I, _I, _F, _F, _P, _P, _P, _P, _I, _P,
+                                       _P, _I64, _P, _P, _P, _I, _I]
+        lib.oracle_decode.restype = _I
+        lib.oracle_decode.argtypes = [_I, _I, _I, _I, _I, _I, _F, _F, _P, _P, _P, _P, _P, _I,
+                                      _P, _P, _I, _P, _P, _P, _I]
+        lib.oracle_kv_append.restype = _I
+        lib.oracle_kv_append.argtypes = [_I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P]
+        lib.oracle_default_threads.restype = _I
+        lib.oracle_default_threads.argtypes = []
+        self.lib = lib
+
+    def default_threads(self) -> int:
+        return int(self.lib.oracle_default_threads())
+
+    # -- helpers ----------------------------------------------------------
+    @staticmethod
+    def _u16(a: np.ndarray, shape_tail) -> np.ndarray:
+        a = np.ascontiguousarray(a)
+        if a.dtype != np.uint16:
+            raise TypeError("bf16 tensors are passed as uint16 bit patterns")
+        if tuple(a.shape[1:]) != tuple(shape_tail):
+            raise ValueError(f"shape {a.shape} does not end in {shape_tail}")
+        return a
+
+    @staticmethod
+    def _ptr(a: Optional[np.ndarray]):
+        return None if a is None else a.ctypes.data
+
+    def prefill(self, q, k, v, cu_seqlens, *, layer_type: int, window: int = 129,
+                scale: float, value_scale: float = 1.0, sink=None, rows=None,
+                want_weights: bool = False, nthreads: int = 0):
+        """Attention of packed varlen sequences.
+
+        q [T][Hq][Dqk], k [T][Hkv][Dqk], v [T][Hkv][Dv] as uint16 bf16 bits;
+        cu_seqlens [B+1] int32; sink [Hq] float32 or None; rows: optional int64
+        packed token indices.  Returns (out [R][Hq][Dv] f64, lse [R][Hq] f64)
+        and, if want_weights, weights [R][Hq][maxlen+1] (sink mass last).
+        """
+        q = np.ascontiguousarray(q)
+        hq, dqk = q.shape[1], q.shape[2]
+        hkv, dv = k.shape[1], v.shape[2]
+        q = self._u16(q, (hq, dqk))
+        k = self._u16(k, (hkv, dqk))
+        v = self._u16(v, (hkv, dv))
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        nseq = cu.shape[0] - 1
+        sk = None if sink is None else np.ascontiguousarray(sink, dtype=np.float32)
+        rw = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+        nrows = int(cu[-1]) if rw is None else int(rw.shape[0])
+        out = np.empty((nrows, hq, dv), np.float64)
+        lse = np.empty((nrows, hq), np.float64)
+        maxlen = int(np.max(np.diff(cu))) if nseq > 0 else 0
+        wstride = maxlen + 1
+        wts = np.empty((nrows, hq, wstride), np.float64) if want_weights else None
+        nth = nthreads if nthreads > 0 else self.default_threads()
+        rc = self.lib.oracle_prefill(hq, hkv, dqk, dv, layer_type, window, scale, value_scale,
+                                     self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(cu), nseq,
+                                     self._ptr(sk), self._ptr(rw), nrows, self._ptr(out),
+                                     self._ptr(lse), self._ptr(wts), wstride, nth)
+        if rc != OK:
+            raise ValueError(f"oracle_prefill rejected its arguments (status {rc})")
+        return (out, lse, wts) if want_weights else (out, lse)
+
+    def decode(self, q, k_new, v_new, k_cache, v_cache, ctx_lens, *, layer_type: int,
+               window: int = 129, scale: float, value_scale: float = 1.0, sink=None,
+               kv_base=None, nthreads: int = 0):
+        """One new token per sequence; SWA reads ring [B][W-1][Hkv][D], GA reads
+        pool [N][Hkv][D] at kv_base[b] + position.  Returns (out [B][Hq][Dv], lse [B][Hq])."""
+        q = np.ascontiguousarray(q)
+        batch, hq, dqk = q.shape
+        hkv, dv = v_new.shape[1], v_new.shape[2]
+        q = self._u16(q, (hq, dqk))
+        kn = self._u16(k_new, (hkv, dqk))
+        vn = self._u16(v_new, (hkv, dv))
+        kc = None if k_cache is None else np.ascontiguousarray(k_cache)
+        vc = None if v_cache is None else np.ascontiguousarray(v_cache)
+        ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+        base = None if kv_base is None else np.ascontiguousarray(kv_base, dtype=np.int64)
+        sk = None if sink is None else np.ascontiguousarray(sink, dtype=np.float32)
+        ring = window - 1 if layer_type == SWA else 0
+        out = np.empty((batch, hq, dv), np.float64)
+        lse = np.empty((batch, hq), np.float64)
+        nth = nthreads if nthreads > 0 else self.default_threads()
+        rc = self.lib.oracle_decode(hq, hkv, dqk, dv, layer_type, window, scale, value_scale,
+                                    self._ptr(q), self._ptr(kn), self._ptr(vn), self._ptr(kc),
+                                    self._ptr(vc), ring, self._ptr(base), self._ptr(ctx), batch,
+                                    self._ptr(sk), self._ptr(out), self._ptr(lse), nth)
+        if rc != OK:
+            raise ValueError(f"oracle_decode rejected its arguments (status {rc})")
+        return out, lse
+
+    def kv_append(self, k, v, cu_newlens, ctx_lens, k_cache, v_cache, *, layer_type: int,
+                  window: int = 129, kv_base=None, kv_capacity=None) -> int:
+        """Writes new tokens into the caches in place; returns the status code."""
+        k = np.ascontiguousarray(k)
+        v = np.ascontiguousarray(v)
+        hkv, dqk, dv = k.shape[1], k.shape[2], v.shape[2]
+        for c in (k_cache, v_cache):
+            if not (c.flags["C_CONTIGUOUS"] and c.dtype == np.uint16):
+                raise TypeError("caches must be C-contiguous uint16 arrays")
+        cu = np.ascontiguousarray(cu_newlens, dtype=np.int32)
+        ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+        base = None if kv_base is None else np.ascontiguousarray(kv_base, dtype=np.int64)
+        cap = None if kv_capacity is None else np.ascontiguousarray(kv_capacity, dtype=np.int64)
+        ring = window - 1 if layer_type == SWA else 0
+        return int(self.lib.oracle_kv_append(hkv, dqk, dv, layer_type, ring, self._ptr(k),
+                                             self._ptr(v), self._ptr(cu), self._ptr(ctx),
+                                             cu.shape[0] - 1, self._ptr(k_cache), self._ptr(v_cache),
+                                             self._ptr(base), self._ptr(cap)))
+
+
+_default: Optional[Oracle] = None
+
+
+def get() -> Oracle:
+    """The oracle built from this directory's source (built on first use if absent)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(LIBRARY):
+            build()
+        _default = Oracle(LIBRARY)
+    return _default
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns (uint16) to float64."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)

@@ -1,0 +1,365 @@
+/*
+ * mimo_oracle.c -- plain, slow, fp64 CPU oracle for MiMo-V2-Flash hybrid attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library.  The GPU library never
+ * links, includes or calls anything here, and nothing here comes from the GPU
+ * sources: the two share only the documented buffer layouts, which are written
+ * out again below from the definitions.
+ *
+ * What it computes (Hugging Face Transformers model doc "MiMo-V2-Flash"):
+ *   - Key features: sliding-window attention (SWA) and global attention (GA)
+ *     layers interleaved 5:1, a 128-token window, and a learnable attention
+ *     sink bias.
+ *   - MiMoV2FlashConfig: num_attention_heads=64, num_key_value_heads=4 (GQA,
+ *     heads grouped), head_dim=192 for queries and keys, v_head_dim=128,
+ *     sliding_window=129, attention_value_scale=0.707.
+ *   - MiMoV2FlashModel.forward, past_key_values: with a cache only the tokens
+ *     not yet processed are passed; earlier keys and values come from the cache.
+ *   - MiMoV2FlashForCausalLM: a causal decoder, so global attention is causal.
+ *
+ * For a query token at position p (0-based, within its sequence) and query
+ * head h:
+ *   g      = h / (Hq / Hkv)                      contiguous GQA groups
+ *   J      = { j : lo <= j <= p },  lo = 0 (GA) or max(0, p - (W - 1)) (SWA)
+ *   s_j    = scale * sum_d q[p,h,d] * k[j,g,d]
+ *   M      = max(max_j s_j, sigma_h)             sigma_h left out when absent
+ *   Z      = sum_j exp(s_j - M) + exp(sigma_h - M)   (sink term 0 when absent)
+ *   LSE    = M + ln Z
+ *   o[e]   = value_scale * sum_j exp(s_j - LSE) * v[j,g,e]
+ * The sink only joins the denominator; it contributes no value row.  A sink
+ * pointer of NULL, or a sink value of -inf, means "no sink".
+ *
+ * Inputs are the bf16 bit patterns the GPU receives, widened exactly to double;
+ * sink, scale and value_scale are fp32 widened to double.  Everything else is
+ * double with libm exp/log.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+#define ORACLE_OK 0
+#define ORACLE_EINVAL 1
+#define ORACLE_ECAPACITY 2
+
+enum { ORACLE_SWA = 0, ORACLE_GA = 1 };
+
+/* bf16 -> double: a bf16 value is the upper 16 bits of an IEEE binary32. */
+static double bf16_to_double(uint16_t bits) {
+    uint32_t w = ((uint32_t)bits) << 16;
+    float f;
+    memcpy(&f, &w, sizeof f);
+    return (double)f;
+}
+
+typedef struct {
+    int hq, hkv, dqk, dv, layer_type, window;
+    double scale, value_scale;
+} dims_t;
+
+/* One attention row: query vector qrow (length dqk), keys given as arrays of
+ * row pointers (one per key in J, in increasing position order).  Writes
+ * o[dv] and *lse.  If wkeys is non-NULL it receives exp(s_j - LSE) for each
+ * key, and *wsink the sink mass exp(sigma - LSE) (0 without a sink). */
+static void attend_row(const dims_t* d, const uint16_t* qrow, int nkeys,
+                       const uint16_t* const* krows, const uint16_t* const* vrows,
+                       int has_sink, double sigma, double* scores,
+                       double* o, double* lse, double* wkeys, double* wsink) {
+    double m = -INFINITY;
+    for (int j = 0; j < nkeys; ++j) {
+        double acc = 0.0;
+        for (int x = 0; x < d->dqk; ++x)
+            acc += bf16_to_double(qrow[x]) * bf16_to_double(krows[j][x]);
+        scores[j] = d->scale * acc;
+        if (scores[j] > m) m = scores[j];
+    }
+    if (has_sink && sigma > m) m = sigma;
+    double z = 0.0;
+    for (int j = 0; j < nkeys; ++j) z += exp(scores[j] - m);
+    if (has_sink) z += exp(sigma - m);
+    double l = m + log(z);
+    for (int e = 0; e < d->dv; ++e) o[e] = 0.0;
+    for (int j = 0; j < nkeys; ++j) {
+        double w = exp(scores[j] - l);
+        if (wkeys) wkeys[j] = w;
+        for (int e = 0; e < d->dv; ++e) o[e] += w * bf16_to_double(vrows[j][e]);
+    }
+    for (int e = 0; e < d->dv; ++e) o[e] *= d->value_scale;
+    if (wkeys) *wsink = has_sink ? exp(sigma - l) : 0.0;
+    *lse = l;
+}
+
+static int sink_present(const float* sink, int h, double* sigma) {
+    if (!sink) return 0;
+    double s = (double)sink[h];
+    if (isinf(s) && s < 0) return 0;
+    *sigma = s;
+    return 1;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Prefill: packed variable-length sequences, keys from the same sequence.  */
+
+typedef struct {
+    const dims_t* d;
+    const uint16_t *q, *k, *v;
+    const int32_t* cu;
+    int nseq;
+    const float* sink;
+    const int64_t* rows; /* packed token indices to evaluate, or NULL = all */
+    int64_t nrows;
+    double *out, *lse, *weights;
+    int wstride; /* weights row length (longest sequence + 1) */
+    int64_t next;
+    pthread_mutex_t mu;
+} prefill_job_t;
+
+static int seq_of_token(const int32_t* cu, int nseq, int64_t t) {
+    int lo = 0, hi = nseq - 1;
+    while (lo < hi) { /* last b with cu[b] <= t */
+        int mid = (lo + hi + 1) / 2;
+        if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+static void* prefill_worker(void* arg) {
+    prefill_job_t* jb = (prefill_job_t*)arg;
+    const dims_t* d = jb->d;
+    int maxkeys = 0;
+    for (int b = 0; b < jb->nseq; ++b) {
+        int L = jb->cu[b + 1] - jb->cu[b];
+        if (L > maxkeys) maxkeys = L;
+    }
+    const uint16_t** kr = malloc(sizeof(*kr) * (size_t)(maxkeys + 1));
+    const uint16_t** vr = malloc(sizeof(*vr) * (size_t)(maxkeys + 1));
+    double* sc = malloc(sizeof(double) * (size_t)(maxkeys + 1));
+    int group = d->hq / d->hkv;
+    for (;;) {
+        pthread_mutex_lock(&jb->mu);
+        int64_t r = jb->next++;
+        pthread_mutex_unlock(&jb->mu);
+        if (r >= jb->nrows) break;
+        int64_t t = jb->rows ? jb->rows[r] : r;
+        int b = seq_of_token(jb->cu, jb->nseq, t);
+        int64_t base = jb->cu[b];
+        int p = (int)(t - base);
+        int lo = 0;
+        if (d->layer_type == ORACLE_SWA) lo = p - (d->window - 1) > 0 ? p - (d->window - 1) : 0;
+        for (int h = 0; h < d->hq; ++h) {
+            int g = h / group;
+            int n = 0;
+            for (int j = lo; j <= p; ++j, ++n) {
+                kr[n] = jb->k + ((size_t)(base + j) * d->hkv + g) * d->dqk;
+                vr[n] = jb->v + ((size_t)(base + j) * d->hkv + g) * d->dv;
+            }
+            double sigma = 0.0;
+            int hs = sink_present(jb->sink, h, &sigma);
+            double* w = jb->weights ? jb->weights + ((size_t)r * d->hq + h) * jb->wstride : NULL;
+            attend_row(d, jb->q + ((size_t)t * d->hq + h) * d->dqk, n, kr, vr, hs, sigma, sc,
+                       jb->out + ((size_t)r * d->hq + h) * d->dv, jb->lse + (size_t)r * d->hq + h,
+                       w ? w + lo : NULL, w ? w + jb->wstride - 1 : NULL);
+        }
+    }
+    free(kr); free(vr); free(sc);
+    return NULL;
+}
+
+static int check_dims(const dims_t* d) {
+    if (d->hq <= 0 || d->hkv <= 0 || d->hq % d->hkv) return 0;
+    if (d->dqk <= 0 || d->dv <= 0) return 0;
+    if (d->layer_type != ORACLE_SWA && d->layer_type != ORACLE_GA) return 0;
+    if (d->layer_type == ORACLE_SWA && d->window < 1) return 0;
+    return 1;
+}
+
+static int run_threads(void* (*fn)(void*), void* job, int nthreads) {
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    pthread_t th[256];
+    int started = 0;
+    for (int i = 0; i < nthreads; ++i)
+        if (pthread_create(&th[i], NULL, fn, job) == 0) started++; else break;
+    if (started == 0) fn(job);
+    for (int i = 0; i < started; ++i) pthread_join(th[i], NULL);
+    return ORACLE_OK;
+}
+
+/* Attention of every packed query token (or of the listed ones) over its own
+ * sequence.  out: [rows][hq][dv], lse: [rows][hq]; weights (optional, the
+ * post-softmax attention weights of the model doc's `attentions` output):
+ * [rows][hq][wstride], entry j = weight of key position j of the sequence
+ * (0 outside the key set), last entry = sink mass; wstride must be at least
+ * the longest sequence + 1. */
+int oracle_prefill(int hq, int hkv, int dqk, int dv, int layer_type, int window,
+                   float scale, float value_scale,
+                   const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                   const int32_t* cu_seqlens, int nseq, const float* sink,
+                   const int64_t* rows, int64_t nrows,
+                   double* out, double* lse, double* weights, int wstride, int nthreads) {
+    dims_t d = {hq, hkv, dqk, dv, layer_type, window, (double)scale, (double)value_scale};
+    if (!check_dims(&d) || nseq < 1 || !q || !k || !v || !cu_seqlens || !out || !lse) return ORACLE_EINVAL;
+    int64_t T = cu_seqlens[nseq];
+    int maxlen = 0;
+    for (int b = 0; b < nseq; ++b) {
+        if (cu_seqlens[b + 1] < cu_seqlens[b]) return ORACLE_EINVAL;
+        if (cu_seqlens[b + 1] - cu_seqlens[b] > maxlen) maxlen = cu_seqlens[b + 1] - cu_seqlens[b];
+    }
+    if (cu_seqlens[0] != 0) return ORACLE_EINVAL;
+    if (!rows) nrows = T;
+    for (int64_t r = 0; rows && r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= T) return ORACLE_EINVAL;
+    if (weights) {
+        if (wstride < maxlen + 1) return ORACLE_EINVAL;
+        memset(weights, 0, sizeof(double) * (size_t)nrows * hq * wstride);
+    }
+    prefill_job_t jb;
+    memset(&jb, 0, sizeof jb);
+    jb.d = &d; jb.q = q; jb.k = k; jb.v = v; jb.cu = cu_seqlens; jb.nseq = nseq; jb.sink = sink;
+    jb.rows = rows; jb.nrows = nrows; jb.out = out; jb.lse = lse; jb.weights = weights; jb.wstride = wstride;
+    pthread_mutex_init(&jb.mu, NULL);
+    run_threads(prefill_worker, &jb, nthreads);
+    pthread_mutex_destroy(&jb.mu);
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Decode: one new token per sequence at position p = ctx_lens[b].          */
+/* Cache readers, written from the layout definitions:                      */
+/*   SWA ring  [B][R][Hkv][D], R = W - 1 slots; position j lives in slot j mod R.
+ *   GA pool   [N][Hkv][D]; position j of sequence b lives at row base_b + j. */
+
+typedef struct {
+    const dims_t* d;
+    const uint16_t *q, *k_new, *v_new, *k_cache, *v_cache;
+    const int64_t* kv_base;
+    const int32_t* ctx;
+    int batch, ring;
+    const float* sink;
+    double *out, *lse;
+    int64_t next;
+    pthread_mutex_t mu;
+} decode_job_t;
+
+static const uint16_t* cache_row(const decode_job_t* jb, int b, int j, int g, int isv) {
+    const dims_t* d = jb->d;
+    int D = isv ? d->dv : d->dqk;
+    const uint16_t* base = isv ? jb->v_cache : jb->k_cache;
+    size_t row;
+    if (d->layer_type == ORACLE_SWA) row = (size_t)b * jb->ring + (size_t)(j % jb->ring);
+    else row = (size_t)(jb->kv_base[b] + j);
+    return base + (row * d->hkv + g) * D;
+}
+
+static void* decode_worker(void* arg) {
+    decode_job_t* jb = (decode_job_t*)arg;
+    const dims_t* d = jb->d;
+    int maxkeys = 1;
+    for (int b = 0; b < jb->batch; ++b) if (jb->ctx[b] + 1 > maxkeys) maxkeys = jb->ctx[b] + 1;
+    const uint16_t** kr = malloc(sizeof(*kr) * (size_t)maxkeys);
+    const uint16_t** vr = malloc(sizeof(*vr) * (size_t)maxkeys);
+    double* sc = malloc(sizeof(double) * (size_t)maxkeys);
+    int group = d->hq / d->hkv;
+    for (;;) {
+        pthread_mutex_lock(&jb->mu);
+        int64_t item = jb->next++;
+        pthread_mutex_unlock(&jb->mu);
+        if (item >= (int64_t)jb->batch * d->hq) break;
+        int b = (int)(item / d->hq), h = (int)(item % d->hq), g = h / group;
+        int p = jb->ctx[b];
+        int lo = 0;
+        if (d->layer_type == ORACLE_SWA) lo = p - (d->window - 1) > 0 ? p - (d->window - 1) : 0;
+        int n = 0;
+        for (int j = lo; j < p; ++j, ++n) {
+            kr[n] = cache_row(jb, b, j, g, 0);
+            vr[n] = cache_row(jb, b, j, g, 1);
+        }
+        kr[n] = jb->k_new + ((size_t)b * d->hkv + g) * d->dqk;
+        vr[n] = jb->v_new + ((size_t)b * d->hkv + g) * d->dv;
+        n++;
+        double sigma = 0.0;
+        int hs = sink_present(jb->sink, h, &sigma);
+        attend_row(d, jb->q + ((size_t)b * d->hq + h) * d->dqk, n, kr, vr, hs, sigma, sc,
+                   jb->out + ((size_t)b * d->hq + h) * d->dv, jb->lse + (size_t)b * d->hq + h, NULL, NULL);
+    }
+    free(kr); free(vr); free(sc);
+    return NULL;
+}
+
+/* Decode attention for one new token per sequence.  SWA reads the ring
+ * (ring_slots = W - 1 required), GA reads the pool at kv_base[b] + j. */
+int oracle_decode(int hq, int hkv, int dqk, int dv, int layer_type, int window,
+                  float scale, float value_scale,
+                  const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                  const uint16_t* k_cache, const uint16_t* v_cache, int ring_slots,
+                  const int64_t* kv_base, const int32_t* ctx_lens, int batch,
+                  const float* sink, double* out, double* lse, int nthreads) {
+    dims_t d = {hq, hkv, dqk, dv, layer_type, window, (double)scale, (double)value_scale};
+    if (!check_dims(&d) || batch < 1 || !q || !k_new || !v_new || !ctx_lens || !out || !lse) return ORACLE_EINVAL;
+    if (layer_type == ORACLE_SWA && ring_slots != window - 1) return ORACLE_EINVAL;
+    if (layer_type == ORACLE_GA && !kv_base) return ORACLE_EINVAL;
+    for (int b = 0; b < batch; ++b) {
+        if (ctx_lens[b] < 0) return ORACLE_EINVAL;
+        if (ctx_lens[b] > 0 && (!k_cache || !v_cache)) return ORACLE_EINVAL;
+    }
+    decode_job_t jb;
+    memset(&jb, 0, sizeof jb);
+    jb.d = &d; jb.q = q; jb.k_new = k_new; jb.v_new = v_new; jb.k_cache = k_cache; jb.v_cache = v_cache;
+    jb.kv_base = kv_base; jb.ctx = ctx_lens; jb.batch = batch; jb.ring = ring_slots; jb.sink = sink;
+    jb.out = out; jb.lse = lse;
+    pthread_mutex_init(&jb.mu, NULL);
+    run_threads(decode_worker, &jb, nthreads);
+    pthread_mutex_destroy(&jb.mu);
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* KV append: new token i of sequence b sits at position ctx_lens[b] + i.   */
+/* SWA: written, in position order, to slot (position mod R); later writes  */
+/* replace earlier ones, so the ring ends with the last R positions.        */
+/* GA: written to pool row kv_base[b] + position, which must stay below     */
+/* kv_base[b] + kv_capacity[b] (ORACLE_ECAPACITY otherwise, nothing written */
+/* for that sequence).                                                      */
+int oracle_kv_append(int hkv, int dqk, int dv, int layer_type, int ring_slots,
+                     const uint16_t* k, const uint16_t* v, const int32_t* cu_newlens,
+                     const int32_t* ctx_lens, int batch,
+                     uint16_t* k_cache, uint16_t* v_cache,
+                     const int64_t* kv_base, const int64_t* kv_capacity) {
+    if (hkv <= 0 || dqk <= 0 || dv <= 0 || batch < 1 || !k || !v || !cu_newlens || !ctx_lens ||
+        !k_cache || !v_cache)
+        return ORACLE_EINVAL;
+    if (layer_type == ORACLE_SWA && ring_slots < 1) return ORACLE_EINVAL;
+    if (layer_type == ORACLE_GA && (!kv_base || !kv_capacity)) return ORACLE_EINVAL;
+    if (layer_type != ORACLE_SWA && layer_type != ORACLE_GA) return ORACLE_EINVAL;
+    int status = ORACLE_OK;
+    size_t krow = (size_t)hkv * dqk, vrow = (size_t)hkv * dv;
+    for (int b = 0; b < batch; ++b) {
+        int n = cu_newlens[b + 1] - cu_newlens[b];
+        if (n < 0) return ORACLE_EINVAL;
+        if (layer_type == ORACLE_GA && (int64_t)ctx_lens[b] + n > kv_capacity[b]) {
+            status = ORACLE_ECAPACITY;
+            continue;
+        }
+        for (int i = 0; i < n; ++i) {
+            int64_t pos = (int64_t)ctx_lens[b] + i;
+            size_t src = (size_t)cu_newlens[b] + i;
+            size_t dst = layer_type == ORACLE_SWA ? (size_t)b * ring_slots + (size_t)(pos % ring_slots)
+                                                  : (size_t)(kv_base[b] + pos);
+            memcpy(k_cache + dst * krow, k + src * krow, krow * sizeof(uint16_t));
+            memcpy(v_cache + dst * vrow, v + src * vrow, vrow * sizeof(uint16_t));
+        }
+    }
+    return status;
+}
+
+/* Number of oracle worker threads a caller gets with nthreads <= 0. */
+int oracle_default_threads(void) {
+    long n = 1;
+#ifdef _SC_NPROCESSORS_ONLN
+    n = sysconf(_SC_NPROCESSORS_ONLN);
+#endif
+    return n > 0 ? (int)n : 1;
+}

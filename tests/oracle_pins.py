@@ -1,0 +1,386 @@
+"""Pins that tie the fp64 oracle to facts other than its own code.
+
+Each ``pin_*`` takes an ``oracle.Oracle`` handle and raises AssertionError when
+the oracle disagrees with:
+  * a structurally different brute force (dense masked score matrix with the
+    sink appended as an extra zero-value column, softmax by torch);
+  * torch's fp64 scaled_dot_product_attention in the special cases that reduce
+    to it (no sink; sink as an extra key with zero key and value vectors and an
+    additive mask of sigma);
+  * closed forms (first query of a sequence; all-equal scores);
+  * invariants (weights plus sink mass sum to one; a sink of -inf is no sink;
+    SWA equals GA when the window covers the sequence; GQA equals MHA with the
+    K/V heads repeated; value_scale is linear; decode at position p equals row
+    p of prefill; ring-slot contents after appends).
+
+The attention definition pinned here is the one from the Hugging Face
+Transformers model doc "MiMo-V2-Flash" (Key features: 5:1 SWA/GA, 128-token
+window, learnable attention sink bias; MiMoV2FlashConfig: 64/4 heads, head_dim
+192, v_head_dim 128, sliding_window 129, attention_value_scale 0.707).
+
+``run_all(path)`` runs every pin against the library at ``path`` and returns
+the names of the pins that failed; the mutation test uses it on planted-mistake
+builds of the oracle.
+"""
+from __future__ import annotations
+
+import math
+import os
+import sys
+
+import numpy as np
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import oracle  # noqa: E402
+from global_attention_mimo_amd import synth  # noqa: E402
+
+SWA, GA = oracle.SWA, oracle.GA
+
+
+def _bits(t):
+    return synth.bf16_bits(t)
+
+
+def _f64(t):
+    return t.detach().to(torch.float64)
+
+
+def _make(lengths, seed=0, hq=64, hkv=4, dqk=192, dv=128, sink=True):
+    return synth.prefill_inputs(lengths, seed=seed, hq=hq, hkv=hkv, dqk=dqk, dv=dv, with_sink=sink)
+
+
+def _run_prefill(orc, x, layer_type, window, scale, value_scale=1.0, sink="inputs", **kw):
+    s = x.sink if isinstance(sink, str) else sink
+    s = None if s is None else np.asarray(s.numpy() if torch.is_tensor(s) else s, dtype=np.float32)
+    return orc.prefill(_bits(x.q), _bits(x.k), _bits(x.v), x.cu_seqlens.numpy(), layer_type=layer_type,
+                       window=window, scale=scale, value_scale=value_scale, sink=s, **kw)
+
+
+def _allowed(L, layer_type, window):
+    i = np.arange(L)[:, None]
+    j = np.arange(L)[None, :]
+    ok = j <= i
+    if layer_type == SWA:
+        ok &= j >= i - (window - 1)
+    return ok
+
+
+def _brute(x, layer_type, window, scale, value_scale, sink):
+    """Dense brute force: full LxL score matrix per head, masked with -inf, the
+    sink appended as one more column whose value row is zero, torch.softmax."""
+    hq, hkv = x.q.shape[1], x.k.shape[1]
+    G = hq // hkv
+    outs, lses = [], []
+    cu = x.cu_seqlens.tolist()
+    for b in range(len(cu) - 1):
+        s0, s1 = cu[b], cu[b + 1]
+        L = s1 - s0
+        q = _f64(x.q[s0:s1])  # [L][Hq][D]
+        k = _f64(x.k[s0:s1])
+        v = _f64(x.v[s0:s1])
+        ok = torch.from_numpy(_allowed(L, layer_type, window))
+        o_b = torch.empty(L, hq, v.shape[2], dtype=torch.float64)
+        l_b = torch.empty(L, hq, dtype=torch.float64)
+        for h in range(hq):
+            g = h // G
+            S = float(scale) * (q[:, h, :] @ k[:, g, :].T)
+            S = S.masked_fill(~ok, -math.inf)
+            sig = -math.inf if sink is None else float(sink[h])
+            S_aug = torch.cat([S, torch.full((L, 1), sig, dtype=torch.float64)], dim=1)
+            P = torch.softmax(S_aug, dim=1)
+            V_aug = torch.cat([v[:, g, :], torch.zeros(1, v.shape[2], dtype=torch.float64)], dim=0)
+            o_b[:, h, :] = float(value_scale) * (P @ V_aug)
+            l_b[:, h] = torch.logsumexp(S_aug, dim=1)
+        outs.append(o_b)
+        lses.append(l_b)
+    return torch.cat(outs).numpy(), torch.cat(lses).numpy()
+
+
+def _close(a, b, tol, what):
+    err = float(np.max(np.abs(np.asarray(a) - np.asarray(b)))) if np.size(a) else 0.0
+    assert err <= tol, f"{what}: max abs diff {err:.3e} > {tol:.1e}"
+
+
+# ---------------------------------------------------------------------------
+def pin_bruteforce_small(orc):
+    """Small shapes, two ragged sequences, SWA and GA, with and without sink."""
+    x = _make([7, 11], seed=1, hq=4, hkv=2, dqk=8, dv=4)
+    sink = x.sink.clone()
+    sink[3] = -math.inf
+    for lt in (SWA, GA):
+        for W in (1, 3, 5):
+            for s in (sink, None):
+                o, l = _run_prefill(orc, x, lt, W, 0.37, 0.9, sink=s)
+                bo, bl = _brute(x, lt, W, np.float32(0.37), np.float32(0.9), None if s is None else s.numpy())
+                _close(o, bo, 1e-12, f"brute out lt={lt} W={W}")
+                _close(l, bl, 1e-12, f"brute lse lt={lt} W={W}")
+
+
+def pin_bruteforce_full_dims(orc):
+    """Model dims (64/4 heads, 192/128), window 129 reached (L = 140)."""
+    x = _make([140, 16], seed=2)
+    scale = np.float32(synth.SOFTMAX_SCALE)
+    for lt in (SWA, GA):
+        o, l = _run_prefill(orc, x, lt, 129, float(scale))
+        bo, bl = _brute(x, lt, 129, scale, np.float32(1.0), x.sink.numpy())
+        _close(o, bo, 1e-12, f"brute full out lt={lt}")
+        _close(l, bl, 1e-12, f"brute full lse lt={lt}")
+
+
+def _sdpa_rows(x, layer_type, window, scale, sink):
+    """torch fp64 SDPA per sequence: boolean mask, KV repeated per group; with a
+    sink, one extra key (k = 0, v = 0) whose additive mask entry is sigma."""
+    hq, hkv = x.q.shape[1], x.k.shape[1]
+    G = hq // hkv
+    cu = x.cu_seqlens.tolist()
+    outs, lses = [], []
+    for b in range(len(cu) - 1):
+        s0, s1 = cu[b], cu[b + 1]
+        L = s1 - s0
+        q = _f64(x.q[s0:s1]).transpose(0, 1)  # [Hq][L][D]
+        k = _f64(x.k[s0:s1]).repeat_interleave(G, dim=1).transpose(0, 1).contiguous()
+        v = _f64(x.v[s0:s1]).repeat_interleave(G, dim=1).transpose(0, 1).contiguous()
+        ok = torch.from_numpy(_allowed(L, layer_type, window))
+        if sink is None:
+            mask = ok.unsqueeze(0).expand(hq, L, L)
+            o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=float(scale))
+            sc = (q @ k.transpose(1, 2)) * float(scale)
+            lse = torch.logsumexp(sc.masked_fill(~mask, -math.inf), dim=2)
+        else:
+            kz = torch.cat([k, torch.zeros(hq, 1, k.shape[2], dtype=torch.float64)], dim=1)
+            vz = torch.cat([v, torch.zeros(hq, 1, v.shape[2], dtype=torch.float64)], dim=1)
+            add = torch.zeros(hq, L, L + 1, dtype=torch.float64)
+            add[:, :, :L] = add[:, :, :L].masked_fill(~ok, -math.inf)
+            add[:, :, L] = torch.as_tensor(sink, dtype=torch.float64)[:, None]
+            o = torch.nn.functional.scaled_dot_product_attention(q, kz, vz, attn_mask=add, scale=float(scale))
+            sc = (q @ kz.transpose(1, 2)) * float(scale) + add
+            lse = torch.logsumexp(sc, dim=2)
+        outs.append(o.transpose(0, 1))
+        lses.append(lse.transpose(0, 1))
+    return torch.cat(outs).numpy(), torch.cat(lses).numpy()
+
+
+def pin_sdpa_no_sink(orc):
+    x = _make([50, 33], seed=3)
+    scale = np.float32(synth.SOFTMAX_SCALE)
+    for lt, W in ((SWA, 129), (SWA, 17), (GA, 129)):
+        ref_o, ref_l = _sdpa_rows(x, lt, W, scale, None)
+        for s in (None, np.full(64, -np.inf, np.float32)):
+            o, l = _run_prefill(orc, x, lt, W, float(scale), sink=s)
+            _close(o, ref_o, 1e-10, f"sdpa no-sink out lt={lt} W={W}")
+            _close(l, ref_l, 1e-10, f"sdpa no-sink lse lt={lt} W={W}")
+
+
+def pin_sdpa_sink_as_extra_key(orc):
+    x = _make([45, 21], seed=4)
+    scale = np.float32(synth.SOFTMAX_SCALE)
+    sink = (x.sink * 3.0).numpy().astype(np.float32)  # spread: some sinks dominate
+    for lt, W in ((SWA, 129), (SWA, 9), (GA, 129)):
+        ref_o, ref_l = _sdpa_rows(x, lt, W, scale, sink)
+        o, l = _run_prefill(orc, x, lt, W, float(scale), sink=sink)
+        _close(o, ref_o, 1e-10, f"sdpa sink out lt={lt} W={W}")
+        _close(l, ref_l, 1e-10, f"sdpa sink lse lt={lt} W={W}")
+
+
+def pin_first_query_closed_form(orc):
+    """Position 0 sees only itself: o = vs * v0 / (1 + exp(sigma - s0)),
+    lse = ln(exp(s0) + exp(sigma))."""
+    x = _make([5, 9, 3], seed=5)
+    scale = float(np.float32(synth.SOFTMAX_SCALE))
+    vs = 0.707
+    o, l = _run_prefill(orc, x, SWA, 129, scale, vs)
+    cu = x.cu_seqlens.tolist()
+    q, k, v, sk = _f64(x.q), _f64(x.k), _f64(x.v), x.sink.double()
+    for b in range(3):
+        t = cu[b]
+        for h in range(64):
+            g = h // 16
+            s0 = scale * float(torch.dot(q[t, h], k[t, g]))
+            sig = float(sk[h])
+            exp_o = float(np.float32(vs)) * v[t, g].numpy() / (1.0 + math.exp(sig - s0))
+            exp_l = max(s0, sig) + math.log1p(math.exp(-abs(s0 - sig)))
+            _close(o[t, h], exp_o, 1e-12, "first-query out")
+            _close(l[t, h], exp_l, 1e-12, "first-query lse")
+
+
+def pin_equal_scores_closed_form(orc):
+    """K = 0 makes every score 0: o = vs * sum_J v_j / (|J| + e^sigma),
+    lse = ln(|J| + e^sigma); |J| = min(p+1, W) for SWA, p+1 for GA."""
+    x = _make([300], seed=6)
+    x.k.zero_()
+    vs = 0.5
+    v = _f64(x.v)[:, :, :].numpy()
+    csum = np.concatenate([np.zeros((1,) + v.shape[1:]), np.cumsum(v, axis=0)])
+    sk = x.sink.double().numpy()
+    for lt, W in ((SWA, 129), (GA, 129), (SWA, 2)):
+        o, l = _run_prefill(orc, x, lt, W, 0.25, vs)
+        for p in (0, 1, 2, 127, 128, 129, 130, 200, 299):
+            lo = max(0, p - (W - 1)) if lt == SWA else 0
+            n = p + 1 - lo
+            vsum = csum[p + 1] - csum[lo]  # [Hkv][Dv]
+            for h in (0, 15, 16, 40, 63):
+                den = n + math.exp(sk[h])
+                _close(o[p, h], vs * vsum[h // 16] / den, 1e-12, f"equal-scores out lt={lt} W={W} p={p}")
+                _close(l[p, h], math.log(den), 1e-12, f"equal-scores lse lt={lt} W={W} p={p}")
+
+
+def pin_weights_normalised(orc):
+    """Per query: weights + sink mass = 1, and weights vanish outside [lo, p]."""
+    x = _make([40, 140], seed=7)
+    for lt, W in ((SWA, 129), (SWA, 10), (GA, 129)):
+        o, l, w = _run_prefill(orc, x, lt, W, float(np.float32(synth.SOFTMAX_SCALE)), want_weights=True)
+        tot = w.sum(axis=2)
+        _close(tot, np.ones_like(tot), 1e-12, f"weights sum lt={lt} W={W}")
+        cu = x.cu_seqlens.tolist()
+        for b in range(2):
+            L = cu[b + 1] - cu[b]
+            for p in range(L):
+                lo = max(0, p - (W - 1)) if lt == SWA else 0
+                row = w[cu[b] + p]
+                assert np.all(row[:, :lo] == 0.0), "weight on a key left of the window"
+                assert np.all(row[:, p + 1:-1] == 0.0), "weight on a future key"
+                assert np.all(row[:, lo:p + 1] > 0.0), "a key in the set got zero weight"
+                assert np.all(row[:, -1] > 0.0), "sink mass missing"
+
+
+def pin_sink_neg_inf_is_no_sink(orc):
+    x = _make([70], seed=8)
+    sc = float(np.float32(synth.SOFTMAX_SCALE))
+    for lt in (SWA, GA):
+        o0, l0 = _run_prefill(orc, x, lt, 129, sc, sink=None)
+        o1, l1 = _run_prefill(orc, x, lt, 129, sc, sink=np.full(64, -np.inf, np.float32))
+        o2, l2 = _run_prefill(orc, x, lt, 129, sc, sink=np.full(64, -1e30, np.float32))
+        assert np.array_equal(o0, o1) and np.array_equal(l0, l1), "-inf sink differs from no sink"
+        assert np.array_equal(o0, o2) and np.array_equal(l0, l2), "-1e30 sink differs from no sink"
+        o3, l3 = _run_prefill(orc, x, lt, 129, sc)
+        assert not np.array_equal(l0, l3), "a finite sink changed nothing"
+
+
+def pin_swa_equals_ga_when_window_covers(orc):
+    x = _make([60, 100], seed=9)
+    sc = float(np.float32(synth.SOFTMAX_SCALE))
+    og, lg = _run_prefill(orc, x, GA, 129, sc)
+    os_, ls = _run_prefill(orc, x, SWA, 129, sc)  # 129 >= 100
+    assert np.array_equal(og, os_) and np.array_equal(lg, ls), "SWA(W>=L) != GA"
+    os2, _ = _run_prefill(orc, x, SWA, 30, sc)
+    assert not np.array_equal(og, os2), "a narrow window changed nothing"
+
+
+def pin_gqa_equals_repeated_mha(orc):
+    x = _make([37, 12], seed=10)
+    sc = float(np.float32(synth.SOFTMAX_SCALE))
+    rep = synth.PrefillInputs(x.q, x.k.repeat_interleave(16, dim=1).contiguous(),
+                              x.v.repeat_interleave(16, dim=1).contiguous(), x.sink, x.cu_seqlens, x.lengths)
+    for lt in (SWA, GA):
+        o, l = _run_prefill(orc, x, lt, 20, sc)
+        o2, l2 = _run_prefill(orc, rep, lt, 20, sc)
+        assert np.array_equal(o, o2) and np.array_equal(l, l2), "GQA != MHA with repeated K/V"
+
+
+def pin_value_scale_linear(orc):
+    x = _make([90], seed=11)
+    sc = float(np.float32(synth.SOFTMAX_SCALE))
+    o1, l1 = _run_prefill(orc, x, SWA, 129, sc, 1.0)
+    o2, l2 = _run_prefill(orc, x, SWA, 129, sc, 0.707)
+    assert np.array_equal(l1, l2), "value_scale changed the LSE"
+    _close(o2, float(np.float32(0.707)) * o1, 1e-14, "value_scale linearity")
+    assert abs(math.sqrt(4096 / (64 * 128)) - 0.707) < 5e-4
+
+
+def _append_positions(orc, kc, vc, k_tok, v_tok, chunks, layer_type, window=129, base=None, cap=None):
+    """Appends the tokens of one sequence in the given chunk sizes."""
+    pos = 0
+    for n in chunks:
+        cu = np.array([0, n], np.int32)
+        st = orc.kv_append(k_tok[pos:pos + n], v_tok[pos:pos + n], cu, np.array([pos], np.int32), kc, vc,
+                           layer_type=layer_type, window=window, kv_base=base, kv_capacity=cap)
+        assert st == oracle.OK, f"append status {st}"
+        pos += n
+    return pos
+
+
+def pin_decode_equals_prefill_row(orc):
+    """Cache positions 0..p-1 (bulk, then single tokens), decode token p: equals
+    row p of prefill over the first p+1 tokens."""
+    L = 300
+    x = _make([L], seed=12)
+    sc = float(np.float32(synth.SOFTMAX_SCALE))
+    kb, vb, qb = _bits(x.k), _bits(x.v), _bits(x.q)
+    sink = x.sink.numpy()
+    for lt in (SWA, GA):
+        ofull, lfull = _run_prefill(orc, x, lt, 129, sc)
+        for p in (0, 1, 127, 128, 129, 200, 299):
+            if lt == SWA:
+                kc = np.zeros((1, 128, 4, 192), np.uint16)
+                vc = np.zeros((1, 128, 4, 128), np.uint16)
+                base = cap = None
+            else:
+                kc = np.zeros((L + 5, 4, 192), np.uint16)
+                vc = np.zeros((L + 5, 4, 128), np.uint16)
+                base = np.array([3], np.int64)
+                cap = np.array([L], np.int64)
+            chunks = [p // 2, p - p // 2 - min(3, p - p // 2)] + [1] * min(3, p - p // 2)
+            chunks = [c for c in chunks if c > 0]
+            _append_positions(orc, kc, vc, kb, vb, chunks, lt, 129, base, cap)
+            o, l = orc.decode(qb[p:p + 1], kb[p:p + 1], vb[p:p + 1], kc, vc, np.array([p], np.int32),
+                              layer_type=lt, window=129, scale=sc, sink=sink, kv_base=base)
+            _close(o[0], ofull[p], 1e-13, f"decode vs prefill out lt={lt} p={p}")
+            _close(l[0], lfull[p], 1e-13, f"decode vs prefill lse lt={lt} p={p}")
+
+
+def pin_ring_contents(orc):
+    """After positions 0..p-1 are appended, ring slot r holds the unique
+    position t = r (mod 128) with p-128 <= t <= p-1."""
+    R = 128
+    for p, chunks in ((5, [5]), (128, [100, 28]), (300, [250, 1, 1, 48]), (129, [129])):
+        tok = np.zeros((p, 1, 2), np.uint16)
+        tok[:, 0, 0] = np.arange(p) + 1  # position tag (non-zero)
+        kc = np.zeros((1, R, 1, 2), np.uint16)
+        vc = np.zeros((1, R, 1, 2), np.uint16)
+        pos = 0
+        for n in chunks:
+            st = orc.kv_append(tok[pos:pos + n], tok[pos:pos + n], np.array([0, n], np.int32),
+                               np.array([pos], np.int32), kc, vc, layer_type=SWA, window=R + 1)
+            assert st == oracle.OK
+            pos += n
+        for r in range(R):
+            want = [t for t in range(max(0, p - R), p) if t % R == r]
+            got = int(kc[0, r, 0, 0])
+            assert got == (want[0] + 1 if want else 0), f"ring slot {r} after {p}: {got}"
+
+
+def pin_ga_capacity(orc):
+    tok = np.ones((4, 1, 2), np.uint16)
+    kc = np.zeros((10, 1, 2), np.uint16)
+    vc = np.zeros((10, 1, 2), np.uint16)
+    st = orc.kv_append(tok, tok, np.array([0, 4], np.int32), np.array([3], np.int32), kc, vc, layer_type=GA,
+                       kv_base=np.array([2], np.int64), kv_capacity=np.array([6], np.int64))
+    assert st == oracle.ECAPACITY and not kc.any(), "capacity overflow not refused"
+    st = orc.kv_append(tok, tok, np.array([0, 4], np.int32), np.array([2], np.int32), kc, vc, layer_type=GA,
+                       kv_base=np.array([2], np.int64), kv_capacity=np.array([6], np.int64))
+    assert st == oracle.OK and kc[4:8].all() and not kc[:4].any() and not kc[8:].any()
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]
+
+
+def run_all(path: str):
+    orc = oracle.Oracle(path)
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            failed.append(pin.__name__)
+    return failed
+
+
+if __name__ == "__main__":  # used by the mutation test: prints failing pin names
+    torch.set_num_threads(2)
+    names = run_all(sys.argv[1])
+    print("FAILED:" + ",".join(names))

@@ -1,0 +1,80 @@
+"""Mutation check of the oracle's pins, on the CPU.
+
+Each case plants one plausible mistake (a dropped term, a wrong sign, index or
+bound, a transposed operand) in a private copy of ``oracle/mimo_oracle.c``,
+builds it with gcc into a temporary directory, runs every pin of
+``oracle_pins`` against that build in a subprocess, and requires at least one
+pin to fail.  The planted source never leaves the temporary directory.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+MUTANTS = {
+    "sink dropped from the denominator": ("    if (has_sink) z += exp(sigma - m);\n", "\n"),
+    "sink given a value row (key 0)": (
+        "    for (int e = 0; e < d->dv; ++e) o[e] *= d->value_scale;\n",
+        "    if (has_sink) for (int e = 0; e < d->dv; ++e) o[e] += exp(sigma - l) * bf16_to_double(vrows[0][e]);\n"
+        "    for (int e = 0; e < d->dv; ++e) o[e] *= d->value_scale;\n"),
+    "sink scaled like a score": ("    *sigma = s;\n", "    *sigma = s * 0.0721687836;\n"),
+    "window one key too wide (prefill)": (
+        "        if (d->layer_type == ORACLE_SWA) lo = p - (d->window - 1) > 0 ? p - (d->window - 1) : 0;\n"
+        "        for (int h = 0;",
+        "        if (d->layer_type == ORACLE_SWA) lo = p - d->window > 0 ? p - d->window : 0;\n"
+        "        for (int h = 0;"),
+    "causal bound excludes self": ("            for (int j = lo; j <= p; ++j, ++n) {\n",
+                                   "            for (int j = lo; j < p; ++j, ++n) {\n"),
+    "GQA heads interleaved instead of grouped": ("            int g = h / group;\n",
+                                                 "            int g = h % d->hkv;\n"),
+    "wrong KV head for keys": (
+        "                kr[n] = jb->k + ((size_t)(base + j) * d->hkv + g) * d->dqk;\n",
+        "                kr[n] = jb->k + ((size_t)(base + j) * d->hkv + (g + 1) % d->hkv) * d->dqk;\n"),
+    "value_scale not applied": ("    for (int e = 0; e < d->dv; ++e) o[e] *= d->value_scale;\n", "\n"),
+    "softmax scale not applied": ("        scores[j] = d->scale * acc;\n", "        scores[j] = acc;\n"),
+    "LSE without the max": ("    double l = m + log(z);\n", "    double l = log(z);\n"),
+    "score sign flipped": ("        scores[j] = d->scale * acc;\n", "        scores[j] = -d->scale * acc;\n"),
+    "weights not normalised by the sink": ("        double w = exp(scores[j] - l);\n",
+                                           "        double w = exp(scores[j] - l) * (has_sink ? z / (z - exp(sigma - m)) : 1.0);\n"),
+    "ring slot off by one (decode read)": (
+        "    if (d->layer_type == ORACLE_SWA) row = (size_t)b * jb->ring + (size_t)(j % jb->ring);\n",
+        "    if (d->layer_type == ORACLE_SWA) row = (size_t)b * jb->ring + (size_t)((j + 1) % jb->ring);\n"),
+    "decode new token read from the cache": (
+        "        kr[n] = jb->k_new + ((size_t)b * d->hkv + g) * d->dqk;\n",
+        "        kr[n] = cache_row(jb, b, p > 0 ? p - 1 : 0, g, 0);\n"),
+    "decode window one key too narrow": (
+        "        if (d->layer_type == ORACLE_SWA) lo = p - (d->window - 1) > 0 ? p - (d->window - 1) : 0;\n"
+        "        int n = 0;",
+        "        if (d->layer_type == ORACLE_SWA) lo = p - (d->window - 2) > 0 ? p - (d->window - 2) : 0;\n"
+        "        int n = 0;"),
+    "append ring slot off by one": (
+        "            size_t dst = layer_type == ORACLE_SWA ? (size_t)b * ring_slots + (size_t)(pos % ring_slots)\n",
+        "            size_t dst = layer_type == ORACLE_SWA ? (size_t)b * ring_slots + (size_t)((pos + 1) % ring_slots)\n"),
+    "append capacity check off by one": ("        if (layer_type == ORACLE_GA && (int64_t)ctx_lens[b] + n > kv_capacity[b]) {\n",
+                                         "        if (layer_type == ORACLE_GA && (int64_t)ctx_lens[b] + n >= kv_capacity[b]) {\n"),
+    "bf16 widened from the wrong half": ("    uint32_t w = ((uint32_t)bits) << 16;\n", "    uint32_t w = ((uint32_t)bits) << 15;\n"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(oracle.SOURCE).read()
+    assert src.count(old) == 1, f"mutation site for '{name}' not found exactly once"
+    mpath = tmp_path / "mutant.c"
+    mpath.write_text(src.replace(old, new))
+    lib = str(tmp_path / "libmutant.so")
+    oracle.build(str(mpath), lib)
+    env = dict(os.environ, OMP_NUM_THREADS="2")
+    res = subprocess.run([sys.executable, os.path.join(HERE, "oracle_pins.py"), lib],
+                         capture_output=True, text=True, timeout=600, env=env)
+    lines = [l for l in res.stdout.splitlines() if l.startswith("FAILED:")]
+    # A crash of the planted build also counts as caught, but only a clean run
+    # that names failing pins tells which pin caught it.
+    caught = (res.returncode != 0) or (lines and lines[-1] != "FAILED:")
+    assert caught, f"no pin caught mutant '{name}'\n{res.stdout[-2000:]}\n{res.stderr[-2000:]}"
