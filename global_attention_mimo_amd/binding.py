@@ -1,0 +1,180 @@
+"""ctypes binding of libmimo_attn.so (C ABI: include/mimo_attn.h).
+
+Function names match the C entry points.  The wrappers only marshal
+arguments: they take torch tensors that already live on the GPU, pass their
+device pointers and the current HIP stream, and raise ``MimoError`` on a
+non-OK status.  Every step of the computation runs in the HIP kernels; there is
+no fallback path, and a missing library raises ``ImportError`` on first use.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(PKG, "libmimo_attn.so")
+
+MIMO_LAYER_SWA = 0
+MIMO_LAYER_GA = 1
+MIMO_OK = 0
+MIMO_ERR_INVALID_ARG = 1
+MIMO_ERR_UNSUPPORTED = 2
+MIMO_ERR_WORKSPACE = 3
+MIMO_ERR_HIP = 4
+
+ENTRY_POINTS = ("mimo_attn_prefill", "mimo_attn_decode_workspace_size", "mimo_attn_decode", "mimo_kv_append",
+                "mimo_status_string", "mimo_last_error", "mimo_abi_version")
+
+
+class mimo_attn_dims(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim_qk", ctypes.c_int32), ("head_dim_v", ctypes.c_int32),
+                ("sliding_window", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("value_scale", ctypes.c_float)]
+
+
+class MimoError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_SZ = ctypes.c_size_t
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library; raises ImportError when it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY):
+            raise ImportError(f"{LIBRARY} is missing: build it with `python -m global_attention_mimo_amd.build`")
+        L = ctypes.CDLL(LIBRARY)
+        dims_p = ctypes.POINTER(mimo_attn_dims)
+        L.mimo_attn_prefill.restype = ctypes.c_int
+        L.mimo_attn_prefill.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P]
+        L.mimo_attn_decode_workspace_size.restype = _SZ
+        L.mimo_attn_decode_workspace_size.argtypes = [dims_p, ctypes.c_int, _I32, _I32, _I32]
+        L.mimo_attn_decode.restype = ctypes.c_int
+        L.mimo_attn_decode.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P,
+                                       _P, _P, _SZ, _P]
+        L.mimo_kv_append.restype = ctypes.c_int
+        L.mimo_kv_append.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _P]
+        L.mimo_status_string.restype = ctypes.c_char_p
+        L.mimo_status_string.argtypes = [ctypes.c_int]
+        L.mimo_last_error.restype = ctypes.c_char_p
+        L.mimo_last_error.argtypes = []
+        L.mimo_abi_version.restype = ctypes.c_int
+        L.mimo_abi_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def make_dims(num_q_heads=64, num_kv_heads=4, head_dim_qk=192, head_dim_v=128, sliding_window=129,
+              softmax_scale: Optional[float] = None, value_scale=1.0) -> mimo_attn_dims:
+    if softmax_scale is None:
+        softmax_scale = head_dim_qk ** -0.5
+    return mimo_attn_dims(num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, sliding_window, softmax_scale,
+                          value_scale)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _check(status: int):
+    if status != MIMO_OK:
+        raise MimoError(status, lib().mimo_last_error().decode() or mimo_status_string(status))
+
+
+def mimo_status_string(status: int) -> str:
+    return lib().mimo_status_string(status).decode()
+
+
+def mimo_last_error() -> str:
+    return lib().mimo_last_error().decode()
+
+
+def mimo_abi_version() -> int:
+    return int(lib().mimo_abi_version())
+
+
+def mimo_attn_prefill(dims: mimo_attn_dims, layer_type: int, q, k, v, cu_seqlens, num_seqs: int, max_seqlen: int,
+                      sink, out, lse, stream=None) -> None:
+    _check(lib().mimo_attn_prefill(ctypes.byref(dims), layer_type, _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens),
+                                   num_seqs, max_seqlen, _ptr(sink), _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def mimo_attn_decode_workspace_size(dims: mimo_attn_dims, layer_type: int, batch: int, max_ctx: int,
+                                    split_tokens: int = 0) -> int:
+    return int(lib().mimo_attn_decode_workspace_size(ctypes.byref(dims), layer_type, batch, max_ctx, split_tokens))
+
+
+def mimo_attn_decode(dims: mimo_attn_dims, layer_type: int, q, k_new, v_new, k_cache, v_cache, kv_base, ctx_lens,
+                     batch: int, max_ctx: int, split_tokens: int, sink, out, lse, workspace, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().mimo_attn_decode(ctypes.byref(dims), layer_type, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                  _ptr(v_cache), _ptr(kv_base), _ptr(ctx_lens), batch, max_ctx, split_tokens,
+                                  _ptr(sink), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def mimo_kv_append(dims: mimo_attn_dims, layer_type: int, k, v, cu_newlens, ctx_lens, batch: int, total_new: int,
+                   k_cache, v_cache, kv_base=None, kv_capacity=None, stream=None) -> None:
+    _check(lib().mimo_kv_append(ctypes.byref(dims), layer_type, _ptr(k), _ptr(v), _ptr(cu_newlens), _ptr(ctx_lens),
+                                batch, total_new, _ptr(k_cache), _ptr(v_cache), _ptr(kv_base), _ptr(kv_capacity),
+                                _stream(stream)))
+
+
+# -- tensor-level conveniences (allocation of outputs + the calls above) -------
+
+def prefill(q, k, v, cu_seqlens, max_seqlen: int, layer_type: int, sink=None, dims=None, out=None, lse=None,
+            want_lse: bool = True, stream=None):
+    dims = dims or make_dims()
+    T = q.shape[0]
+    if out is None:
+        out = torch.empty((T, dims.num_q_heads, dims.head_dim_v), dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((T, dims.num_q_heads), dtype=torch.float32, device=q.device)
+    mimo_attn_prefill(dims, layer_type, q, k, v, cu_seqlens, cu_seqlens.numel() - 1, max_seqlen, sink, out, lse,
+                      stream)
+    return out, lse
+
+
+def decode(q, k_new, v_new, k_cache, v_cache, ctx_lens, max_ctx: int, layer_type: int, sink=None, kv_base=None,
+           split_tokens: int = 0, dims=None, out=None, lse=None, workspace=None, stream=None):
+    dims = dims or make_dims()
+    B = q.shape[0]
+    if out is None:
+        out = torch.empty((B, dims.num_q_heads, dims.head_dim_v), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, dims.num_q_heads), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = mimo_attn_decode_workspace_size(dims, layer_type, B, max_ctx, split_tokens)
+        workspace = torch.empty(max(nbytes, 16) // 4 + 4, dtype=torch.float32, device=q.device) if nbytes else None
+    mimo_attn_decode(dims, layer_type, q, k_new, v_new, k_cache, v_cache, kv_base, ctx_lens, B, max_ctx,
+                     split_tokens, sink, out, lse, workspace, stream)
+    return out, lse
+
+
+def kv_append(k, v, cu_newlens, ctx_lens, k_cache, v_cache, layer_type: int, kv_base=None, kv_capacity=None,
+              dims=None, total_new: Optional[int] = None, stream=None):
+    dims = dims or make_dims()
+    if total_new is None:
+        total_new = k.shape[0]
+    mimo_kv_append(dims, layer_type, k, v, cu_newlens, ctx_lens, cu_newlens.numel() - 1, total_new, k_cache, v_cache,
+                   kv_base, kv_capacity, stream)

@@ -1,0 +1,169 @@
+// api.cpp -- the C ABI of include/mimo_attn.h: host-side argument validation and dispatch.
+//
+// Every check here runs on the host before anything is enqueued, so misuse is
+// reported by status code without touching the device.
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "../../include/mimo_attn.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_last_error[0] = '\0';
+    return MIMO_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int kDefaultSplit = 2048;
+constexpr int kMaxGridYZ = 65535;
+
+// Shape checks shared by every entry point.  min_window: 1 for prefill
+// (window W keeps keys p-(W-1)..p), 2 where an SWA ring of W-1 slots exists.
+int check_dims(const mimo_attn_dims* d, int layer_type, int min_window) {
+    if (!d) return fail(MIMO_ERR_INVALID_ARG, "dims is NULL");
+    if (layer_type != MIMO_LAYER_SWA && layer_type != MIMO_LAYER_GA)
+        return fail(MIMO_ERR_INVALID_ARG, "layer_type %d is neither SWA (0) nor GA (1)", layer_type);
+    if (d->num_q_heads <= 0 || d->num_kv_heads <= 0)
+        return fail(MIMO_ERR_INVALID_ARG, "head counts must be positive (q %d, kv %d)", d->num_q_heads,
+                    d->num_kv_heads);
+    if (d->num_q_heads % d->num_kv_heads != 0)
+        return fail(MIMO_ERR_UNSUPPORTED, "num_q_heads %d is not a multiple of num_kv_heads %d", d->num_q_heads,
+                    d->num_kv_heads);
+    if (d->num_q_heads != 16 * d->num_kv_heads)
+        return fail(MIMO_ERR_UNSUPPORTED, "kernels need 16 query heads per KV head (got %d/%d)", d->num_q_heads,
+                    d->num_kv_heads);
+    if (d->head_dim_qk != 192 || d->head_dim_v != 128)
+        return fail(MIMO_ERR_UNSUPPORTED, "kernels need head_dim_qk 192 and head_dim_v 128 (got %d/%d)",
+                    d->head_dim_qk, d->head_dim_v);
+    if (d->num_kv_heads > kMaxGridYZ) return fail(MIMO_ERR_UNSUPPORTED, "too many KV heads");
+    if (layer_type == MIMO_LAYER_SWA && d->sliding_window < min_window)
+        return fail(MIMO_ERR_INVALID_ARG, "sliding_window %d is below %d", d->sliding_window, min_window);
+    if (!std::isfinite(d->softmax_scale) || !std::isfinite(d->value_scale))
+        return fail(MIMO_ERR_INVALID_ARG, "softmax_scale and value_scale must be finite");
+    return MIMO_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(MIMO_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+int effective_split(int32_t split_tokens) {
+    int s = split_tokens <= 0 ? kDefaultSplit : split_tokens;
+    if (s > (1 << 30)) s = 1 << 30;
+    return (s + 31) / 32 * 32;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mimo_attn_prefill(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, const uint16_t* k,
+                      const uint16_t* v, const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+                      const float* sink, uint16_t* out, float* lse, hipStream_t stream) {
+    if (int st = check_dims(dims, layer_type, 1)) return st;
+    if (!q || !k || !v || !cu_seqlens || !out)
+        return fail(MIMO_ERR_INVALID_ARG, "q, k, v, cu_seqlens and out must be non-NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(MIMO_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+    if (num_seqs < 1 || num_seqs > kMaxGridYZ)
+        return fail(MIMO_ERR_INVALID_ARG, "num_seqs %d outside [1, %d]", num_seqs, kMaxGridYZ);
+    if (max_seqlen < 0) return fail(MIMO_ERR_INVALID_ARG, "max_seqlen %d is negative", max_seqlen);
+    if (max_seqlen == 0) return ok();
+    mimo::PrefillArgs a{q, k, v, cu_seqlens, sink, out, lse, num_seqs, max_seqlen, dims->num_q_heads,
+                        dims->num_kv_heads, dims->sliding_window, dims->softmax_scale, dims->value_scale,
+                        layer_type == MIMO_LAYER_SWA};
+    return hip_status(mimo::launch_prefill(a, stream), "prefill launch");
+}
+
+size_t mimo_attn_decode_workspace_size(const mimo_attn_dims* dims, int layer_type, int32_t batch, int32_t max_ctx,
+                                       int32_t split_tokens) {
+    if (check_dims(dims, layer_type, 2) != MIMO_OK || batch < 1 || max_ctx < 0) return 0;
+    if (layer_type == MIMO_LAYER_SWA) return 0;
+    return mimo::ga_workspace_bytes(batch, max_ctx, effective_split(split_tokens), dims->num_q_heads);
+}
+
+int mimo_attn_decode(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, const uint16_t* k_new,
+                     const uint16_t* v_new, const uint16_t* k_cache, const uint16_t* v_cache, const int64_t* kv_base,
+                     const int32_t* ctx_lens, int32_t batch, int32_t max_ctx, int32_t split_tokens, const float* sink,
+                     uint16_t* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (int st = check_dims(dims, layer_type, 2)) return st;
+    if (!q || !k_new || !v_new || !ctx_lens || !out)
+        return fail(MIMO_ERR_INVALID_ARG, "q, k_new, v_new, ctx_lens and out must be non-NULL");
+    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out))
+        return fail(MIMO_ERR_INVALID_ARG, "q, k_new, v_new and out must be 16-byte aligned");
+    if (batch < 1) return fail(MIMO_ERR_INVALID_ARG, "batch %d < 1", batch);
+    if (max_ctx < 0 || max_ctx == INT32_MAX) return fail(MIMO_ERR_INVALID_ARG, "max_ctx %d out of range", max_ctx);
+    if (!k_cache || !v_cache) return fail(MIMO_ERR_INVALID_ARG, "k_cache and v_cache must be non-NULL");
+    if (!aligned16(k_cache) || !aligned16(v_cache))
+        return fail(MIMO_ERR_INVALID_ARG, "k_cache and v_cache must be 16-byte aligned");
+    const int split = effective_split(split_tokens);
+    mimo::DecodeArgs a{q, k_new, v_new, k_cache, v_cache, kv_base, ctx_lens, sink, out, lse, workspace, batch,
+                       max_ctx, split, dims->num_q_heads, dims->num_kv_heads, dims->sliding_window,
+                       dims->softmax_scale, dims->value_scale};
+    if (layer_type == MIMO_LAYER_SWA) {
+        if (batch > INT32_MAX / 2) return fail(MIMO_ERR_UNSUPPORTED, "batch too large");
+        return hip_status(mimo::launch_decode_swa(a, stream), "SWA decode launch");
+    }
+    if (!kv_base) return fail(MIMO_ERR_INVALID_ARG, "GA decode needs kv_base");
+    if (batch > kMaxGridYZ) return fail(MIMO_ERR_UNSUPPORTED, "GA decode batch %d above %d", batch, kMaxGridYZ);
+    const size_t need = mimo::ga_workspace_bytes(batch, max_ctx, split, dims->num_q_heads);
+    if (!workspace || workspace_bytes < need)
+        return fail(MIMO_ERR_WORKSPACE, "GA decode needs %zu workspace bytes (got %zu%s)", need, workspace_bytes,
+                    workspace ? "" : ", NULL");
+    if (!aligned16(workspace)) return fail(MIMO_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    return hip_status(mimo::launch_decode_ga(a, stream), "GA decode launch");
+}
+
+int mimo_kv_append(const mimo_attn_dims* dims, int layer_type, const uint16_t* k, const uint16_t* v,
+                   const int32_t* cu_newlens, const int32_t* ctx_lens, int32_t batch, int32_t total_new,
+                   uint16_t* k_cache, uint16_t* v_cache, const int64_t* kv_base, const int64_t* kv_capacity,
+                   hipStream_t stream) {
+    if (int st = check_dims(dims, layer_type, 2)) return st;
+    if (!k || !v || !cu_newlens || !ctx_lens || !k_cache || !v_cache)
+        return fail(MIMO_ERR_INVALID_ARG, "k, v, cu_newlens, ctx_lens, k_cache and v_cache must be non-NULL");
+    if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+        return fail(MIMO_ERR_INVALID_ARG, "k, v, k_cache and v_cache must be 16-byte aligned");
+    if (batch < 1) return fail(MIMO_ERR_INVALID_ARG, "batch %d < 1", batch);
+    if (total_new < 0) return fail(MIMO_ERR_INVALID_ARG, "total_new %d is negative", total_new);
+    if (layer_type == MIMO_LAYER_GA && (!kv_base || !kv_capacity))
+        return fail(MIMO_ERR_INVALID_ARG, "GA append needs kv_base and kv_capacity");
+    const int64_t blocks = ((int64_t)total_new * dims->num_kv_heads * 40 + 255) / 256;
+    if (blocks > INT32_MAX) return fail(MIMO_ERR_UNSUPPORTED, "append of %d tokens is too large", total_new);
+    if (total_new == 0) return ok();
+    mimo::AppendArgs a{k, v, cu_newlens, ctx_lens, k_cache, v_cache, kv_base, kv_capacity, batch, total_new,
+                       dims->num_kv_heads, dims->sliding_window, layer_type == MIMO_LAYER_SWA};
+    return hip_status(mimo::launch_kv_append(a, stream), "KV append launch");
+}
+
+const char* mimo_status_string(int status) {
+    switch (status) {
+        case MIMO_OK: return "MIMO_OK";
+        case MIMO_ERR_INVALID_ARG: return "MIMO_ERR_INVALID_ARG";
+        case MIMO_ERR_UNSUPPORTED: return "MIMO_ERR_UNSUPPORTED";
+        case MIMO_ERR_WORKSPACE: return "MIMO_ERR_WORKSPACE";
+        case MIMO_ERR_HIP: return "MIMO_ERR_HIP";
+        default: return "MIMO_ERR_UNKNOWN";
+    }
+}
+
+const char* mimo_last_error(void) { return g_last_error; }
+
+int mimo_abi_version(void) { return MIMO_ATTN_ABI_VERSION; }
+
+}  // extern "C"

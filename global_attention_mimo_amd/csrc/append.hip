@@ -1,0 +1,70 @@
+// append.hip -- writes new tokens' keys and values into the SWA ring or the GA pool.
+//
+// Operation (Hugging Face Transformers model doc "MiMo-V2-Flash",
+// MiMoV2FlashModel.forward, past_key_values / use_cache): the cache keeps the
+// keys and values of processed tokens so later steps pass only new tokens.
+// SWA layers need only the last sliding_window-1 = 128 positions (the new
+// token is the 129th key), so their cache is a ring of 128 slots per sequence,
+// position j in slot j mod 128; GA layers keep every position in a pool row
+// kv_base[b] + j.
+//
+// One thread moves one 16-byte chunk: a token is Hkv*24 chunks of K and
+// Hkv*16 chunks of V, so consecutive threads copy consecutive bytes of a row.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace mimo {
+namespace {
+
+constexpr int kDqk = 192;
+constexpr int kDv = 128;
+
+__global__ __launch_bounds__(256) void kv_append_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const int32_t* __restrict__ cu_newlens,
+    const int32_t* __restrict__ ctx_lens, int batch, int total_new, uint16_t* __restrict__ k_cache,
+    uint16_t* __restrict__ v_cache, const int64_t* __restrict__ kv_base, const int64_t* __restrict__ kv_capacity,
+    int hkv, int ring, int swa) {
+    const int kchunks = hkv * (kDqk / 8), per_tok = hkv * ((kDqk + kDv) / 8);
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t tok = idx / per_tok;
+    const int c = (int)(idx % per_tok);
+    if (tok >= total_new) return;
+    // Sequence owning packed token `tok`: the last b with cu_newlens[b] <= tok.
+    int lo = 0, hi = batch - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cu_newlens[mid] <= tok) lo = mid; else hi = mid - 1;
+    }
+    const int b = lo;
+    const int n = cu_newlens[b + 1] - cu_newlens[b];
+    const int64_t ctx = ctx_lens[b];
+    const int64_t pos = ctx + (tok - cu_newlens[b]);
+    int64_t row;
+    if (swa) {
+        if (pos < ctx + n - ring) return;  // overwritten later in this same append
+        row = (int64_t)b * ring + pos % ring;
+    } else {
+        if (ctx + n > kv_capacity[b]) return;  // the whole sequence is refused
+        row = kv_base[b] + pos;
+    }
+    if (c < kchunks) {
+        reinterpret_cast<u32x4*>(k_cache + row * hkv * kDqk)[c] = reinterpret_cast<const u32x4*>(k + tok * hkv * kDqk)[c];
+    } else {
+        const int cv = c - kchunks;
+        reinterpret_cast<u32x4*>(v_cache + row * hkv * kDv)[cv] = reinterpret_cast<const u32x4*>(v + tok * hkv * kDv)[cv];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream) {
+    if (a.total_new <= 0) return hipSuccess;
+    const int64_t threads = (int64_t)a.total_new * a.hkv * ((kDqk + kDv) / 8);
+    const int64_t blocks = (threads + 255) / 256;
+    hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a.k, a.v, a.cu_newlens,
+                       a.ctx_lens, a.batch, a.total_new, a.k_cache, a.v_cache, a.kv_base, a.kv_capacity, a.hkv,
+                       a.window - 1, a.swa ? 1 : 0);
+    return hipGetLastError();
+}
+
+}  // namespace mimo

@@ -1,0 +1,92 @@
+// device_common.hpp -- gfx950 (CDNA4) building blocks shared by the attention kernels.
+//
+// MFMA operand/result lane layouts used throughout (wave64, bf16 inputs, fp32 accumulate):
+//
+//   v_mfma_f32_32x32x16_bf16   D[32x32] += A[32x16] * B[16x32]
+//     lane l supplies A[l%32][8*(l/32) + t] and B[8*(l/32) + t][l%32], t = 0..7
+//     lane l holds    D[8*(r/4) + 4*(l/32) + r%4][l%32],            r = 0..15
+//
+//   v_mfma_f32_16x16x32_bf16   D[16x16] += A[16x32] * B[32x16]
+//     lane l supplies A[l%16][8*(l/16) + t] and B[8*(l/16) + t][l%16], t = 0..7
+//     lane l holds    D[4*(l/16) + r][l%16],                         r = 0..3
+//
+//   ds_read_b64_tr_b16 (per 16-lane group, lanes i and j = 0..15 of the group):
+//     lane i receives element (i%4) of the 4 x bf16 chunk addressed by lane
+//     4*t + i/4, for t = 0..3.  If lane 4*t + c addresses row R(t), column
+//     C0 + 4*c of a row-major bf16 tile, lane i receives column C0 + i of rows
+//     R(0..3): a 4 x 16 block arrives transposed, one column per lane.
+//
+// The attention kernels compute S^T = K * Q^T (keys on the MFMA M side, the
+// query rows on the N side) so that every lane owns whole query rows: row
+// maxima and sums stay inside a lane except for one exchange between the two
+// 32-lane halves (v_permlane32_swap).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mimo {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
+// Finite stand-in for a running maximum of -inf: exp2(x - kNoMax) never
+// produces NaN, and exp2(kNoMax - finite) is exactly 0.
+constexpr float kNoMax = -1.0e30f;
+
+__device__ __forceinline__ f32x16 mfma_32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 4 x bf16 transposed LDS read (see the layout note above).
+__device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
+}
+
+__device__ __forceinline__ bf16x8 join_tr(const i16x4& lo, const i16x4& hi) {
+    i16x4 x[2] = {lo, hi};
+    return __builtin_bit_cast(bf16x8, x);
+}
+
+// Value held by lane l^32.  Returned as the pair (own, partner) ordered so that
+// max/sum of the two gives the same result in both halves.
+__device__ __forceinline__ float max_with_partner_half(float x) {
+    uint32_t u = __builtin_bit_cast(uint32_t, x);
+    auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__builtin_bit_cast(float, (uint32_t)p[0]), __builtin_bit_cast(float, (uint32_t)p[1]));
+}
+__device__ __forceinline__ float sum_with_partner_half(float x) {
+    uint32_t u = __builtin_bit_cast(uint32_t, x);
+    auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (uint32_t)p[0]) + __builtin_bit_cast(float, (uint32_t)p[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Round-to-nearest-even fp32 -> bf16 pair packed in one dword (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    __bf16 x = (__bf16)a, y = (__bf16)b;
+    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+__device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3, float a4, float a5,
+                                              float a6, float a7) {
+    u32x4 u = {pack_bf16x2(a0, a1), pack_bf16x2(a2, a3), pack_bf16x2(a4, a5), pack_bf16x2(a6, a7)};
+    return __builtin_bit_cast(bf16x8, u);
+}
+
+// Orders this wave's earlier LDS writes before its later LDS reads (the
+// compiler must not move accesses across it; the hardware keeps a wave's LDS
+// operations in order).
+__device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
+
+}  // namespace mimo

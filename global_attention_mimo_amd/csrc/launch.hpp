@@ -1,0 +1,61 @@
+// launch.hpp -- host-side launchers of the attention kernels (internal to the library).
+// Arguments reach these only after the C-ABI layer has validated them.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mimo {
+
+struct PrefillArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const int32_t* cu_seqlens;
+    const float* sink;
+    uint16_t* out;
+    float* lse;
+    int num_seqs, max_seqlen, hq, hkv, window;
+    float softmax_scale, value_scale;
+    bool swa;
+};
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+struct DecodeArgs {
+    const uint16_t* q;
+    const uint16_t* k_new;
+    const uint16_t* v_new;
+    const uint16_t* k_cache;
+    const uint16_t* v_cache;
+    const int64_t* kv_base;
+    const int32_t* ctx_lens;
+    const float* sink;
+    uint16_t* out;
+    float* lse;
+    void* workspace;
+    int batch, max_ctx, split, hq, hkv, window;
+    float softmax_scale, value_scale;
+};
+// Number of GA splits of `split` keys covering positions 0..max_ctx.
+inline int ga_num_splits(int max_ctx, int split) { return (max_ctx + 1 + split - 1) / split; }
+// Bytes of GA workspace: per (sequence, split, head) an (m, l) pair and 128 partial outputs.
+inline size_t ga_workspace_bytes(int batch, int max_ctx, int split, int hq) {
+    return (size_t)batch * (size_t)ga_num_splits(max_ctx, split) * (size_t)hq * (2 + 128) * sizeof(float);
+}
+hipError_t launch_decode_swa(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_ga(const DecodeArgs& a, hipStream_t stream);
+
+struct AppendArgs {
+    const uint16_t* k;
+    const uint16_t* v;
+    const int32_t* cu_newlens;
+    const int32_t* ctx_lens;
+    uint16_t* k_cache;
+    uint16_t* v_cache;
+    const int64_t* kv_base;
+    const int64_t* kv_capacity;
+    int batch, total_new, hkv, window;
+    bool swa;
+};
+hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
+
+}  // namespace mimo

@@ -1,0 +1,150 @@
+"""The C-ABI library on the CPU: it loads, exports every function include/*.h
+declares, and rejects misuse on the host with the documented status before
+anything is enqueued.  Every call below carries at least one invalid argument,
+so no kernel is ever launched; the pointer values are never dereferenced."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from global_attention_mimo_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # 16-byte-aligned stand-in pointer; validation never reads it
+FAKE_ODD = 0x10008  # 8-byte aligned only
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w\s\*]*?\b(mimo_\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIBRARY):
+        from global_attention_mimo_amd import build
+        build.build()
+    return B.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = declared_functions()
+    assert names == set(B.ENTRY_POINTS), names
+    for n in names:
+        assert hasattr(L, n), f"{n} not exported"
+
+
+def test_version_and_status_strings(L):
+    assert B.mimo_abi_version() == 1
+    assert B.mimo_status_string(0) == "MIMO_OK"
+    assert B.mimo_status_string(3) == "MIMO_ERR_WORKSPACE"
+    assert B.mimo_status_string(99) == "MIMO_ERR_UNKNOWN"
+
+
+def prefill_call(L, dims=None, layer=0, q=FAKE, k=FAKE, v=FAKE, cu=FAKE, nseq=1, maxlen=16, out=FAKE):
+    d = dims if dims is not None else B.make_dims()
+    return L.mimo_attn_prefill(ctypes.byref(d) if d is not False else None, layer, q, k, v, cu, nseq, maxlen, None,
+                               out, None, None)
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(dims=False), B.MIMO_ERR_INVALID_ARG),
+    (dict(layer=2), B.MIMO_ERR_INVALID_ARG),
+    (dict(q=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(out=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(cu=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(k=FAKE_ODD), B.MIMO_ERR_INVALID_ARG),
+    (dict(nseq=0), B.MIMO_ERR_INVALID_ARG),
+    (dict(maxlen=-1), B.MIMO_ERR_INVALID_ARG),
+    (dict(dims=B.make_dims(num_q_heads=64, num_kv_heads=8)), B.MIMO_ERR_UNSUPPORTED),
+    (dict(dims=B.make_dims(num_q_heads=60, num_kv_heads=8)), B.MIMO_ERR_UNSUPPORTED),
+    (dict(dims=B.make_dims(head_dim_qk=128)), B.MIMO_ERR_UNSUPPORTED),
+    (dict(dims=B.make_dims(head_dim_v=192)), B.MIMO_ERR_UNSUPPORTED),
+    (dict(dims=B.make_dims(num_kv_heads=0)), B.MIMO_ERR_INVALID_ARG),
+    (dict(dims=B.make_dims(sliding_window=0)), B.MIMO_ERR_INVALID_ARG),
+    (dict(dims=B.make_dims(softmax_scale=float("nan"))), B.MIMO_ERR_INVALID_ARG),
+    (dict(dims=B.make_dims(value_scale=float("inf"))), B.MIMO_ERR_INVALID_ARG),
+])
+def test_prefill_rejects(L, case, status):
+    assert prefill_call(L, **case) == status
+    assert B.mimo_last_error() != ""
+
+
+def test_prefill_empty_is_ok_without_launch(L):
+    assert prefill_call(L, maxlen=0) == B.MIMO_OK
+
+
+def decode_call(L, dims=None, layer=1, q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, base=FAKE, ctx=FAKE, batch=2,
+                max_ctx=100, split=0, out=FAKE, ws=None, ws_bytes=0):
+    d = dims or B.make_dims()
+    return L.mimo_attn_decode(ctypes.byref(d), layer, q, kn, vn, kc, vc, base, ctx, batch, max_ctx, split, None, out,
+                              None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(layer=5), B.MIMO_ERR_INVALID_ARG),
+    (dict(q=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(ctx=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(kc=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(vn=FAKE_ODD), B.MIMO_ERR_INVALID_ARG),
+    (dict(batch=0), B.MIMO_ERR_INVALID_ARG),
+    (dict(max_ctx=-3), B.MIMO_ERR_INVALID_ARG),
+    (dict(base=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(ws=None), B.MIMO_ERR_WORKSPACE),
+    (dict(ws=FAKE, ws_bytes=100), B.MIMO_ERR_WORKSPACE),
+    (dict(layer=0, dims=B.make_dims(sliding_window=1)), B.MIMO_ERR_INVALID_ARG),
+    (dict(dims=B.make_dims(head_dim_qk=64)), B.MIMO_ERR_UNSUPPORTED),
+])
+def test_decode_rejects(L, case, status):
+    assert decode_call(L, **case) == status
+
+
+def test_workspace_size(L):
+    d = B.make_dims()
+    # GA: batch * ceil((max_ctx+1)/split) * Hq * (2 + 128) * 4 bytes.
+    assert B.mimo_attn_decode_workspace_size(d, 1, 3, 4095, 2048) == 3 * 2 * 64 * 130 * 4
+    assert B.mimo_attn_decode_workspace_size(d, 1, 3, 4096, 2048) == 3 * 3 * 64 * 130 * 4
+    assert B.mimo_attn_decode_workspace_size(d, 1, 1, 0, 0) == 1 * 1 * 64 * 130 * 4
+    assert B.mimo_attn_decode_workspace_size(d, 1, 2, 100, 33) == 2 * 2 * 64 * 130 * 4  # split rounds to 64
+    assert B.mimo_attn_decode_workspace_size(d, 0, 128, 262144, 0) == 0
+    assert B.mimo_attn_decode_workspace_size(d, 1, 0, 10, 0) == 0
+    assert B.mimo_attn_decode_workspace_size(B.make_dims(head_dim_v=64), 1, 1, 10, 0) == 0
+
+
+def append_call(L, dims=None, layer=1, k=FAKE, v=FAKE, cu=FAKE, ctx=FAKE, batch=1, total=4, kc=FAKE, vc=FAKE,
+                base=FAKE, cap=FAKE):
+    d = dims or B.make_dims()
+    return L.mimo_kv_append(ctypes.byref(d), layer, k, v, cu, ctx, batch, total, kc, vc, base, cap, None)
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(k=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(kc=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(cap=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(base=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(batch=0), B.MIMO_ERR_INVALID_ARG),
+    (dict(total=-1), B.MIMO_ERR_INVALID_ARG),
+    (dict(vc=FAKE_ODD), B.MIMO_ERR_INVALID_ARG),
+    (dict(layer=0, dims=B.make_dims(sliding_window=1)), B.MIMO_ERR_INVALID_ARG),
+    (dict(dims=B.make_dims(num_q_heads=32)), B.MIMO_ERR_UNSUPPORTED),
+])
+def test_append_rejects(L, case, status):
+    assert append_call(L, **case) == status
+
+
+def test_append_nothing_is_ok_without_launch(L):
+    assert append_call(L, total=0) == B.MIMO_OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIBRARY", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        B.lib()
