@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""Throughput of the MiMo-V2-Flash hybrid attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic inputs:
+  1. SWA prefill layer: 4 sequences x 8192 tokens, window 129, sink;
+  2. GA prefill layer: 1 sequence x 32768 tokens, sink;
+  3. one decode step for 128 sequences with contexts uniform in [4096, 262144]:
+     SWA layer (128-slot ring) and GA layer (full bf16 pool, split-K), each
+     attend-then-append, then the host-visible context counters advance.
+Shapes: 64 query heads over 4 KV heads, head dims 192 (q/k) and 128 (v); all
+inputs N(0,1) bf16 and sinks N(0,1) fp32, seeded; everything resident in HBM
+before timing starts.
+
+Prints ONE JSON line.  `value` is the step's algorithmic attention FLOPs
+(640 per unmasked query-key-head triple, prefill and decode) divided by the
+step time; per-phase TFLOP/s, tokens/s and GB/s are in `breakdown`.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from global_attention_mimo_amd import binding as B  # noqa: E402
+from global_attention_mimo_amd import synth  # noqa: E402
+
+HQ, HKV, DQK, DV, W = 64, 4, 192, 128, 129
+FLOP_PER_TRIPLE = 2 * (DQK + DV)                      # 640
+TOKEN_BYTES = HQ * DQK * 2 + HKV * (DQK + DV) * 2 + HQ * DV * 2 + HQ * 4  # q,k,v,o,lse = 43,776
+KV_TOKEN_BYTES = HKV * (DQK + DV) * 2                 # 2,560
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBPS = 8000.0
+METRIC = "attention TFLOP/s (prefill) + decode tokens/s & HBM GB/s, SWA and GA, 1 GPU"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def prefill_pairs(lengths, layer_type, window=W):
+    tot = 0
+    for L in lengths:
+        if layer_type == 1:
+            tot += L * (L + 1) // 2
+        else:
+            n = min(L, window)
+            tot += n * (n + 1) // 2 + (L - n) * window
+    return tot
+
+
+def decode_stats(ctx, layer_type, window=W):
+    ctx = np.asarray(ctx, dtype=np.int64)
+    if layer_type == 1:
+        keys = ctx + 1
+        cached = ctx
+    else:
+        keys = np.minimum(ctx + 1, window)
+        cached = np.minimum(ctx, window - 1)
+    flops = int(keys.sum()) * HQ * FLOP_PER_TRIPLE
+    bytes_ = int(cached.sum()) * KV_TOKEN_BYTES + len(ctx) * TOKEN_BYTES
+    return flops, bytes_
+
+
+def cpu_baseline(swa, ga, dga, ctx, budget_s):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload."""
+    import oracle
+    orc = oracle.get()
+    nth = orc.default_threads()
+    scale = float(np.float32(synth.SOFTMAX_SCALE))
+    rng = np.random.default_rng(0)
+    flops = 0
+    t0 = time.perf_counter()
+    parts = []
+    # SWA prefill rows: 64 random tokens of the 4x8192 batch (all their heads).
+    T = swa.q.shape[0]
+    rows = np.sort(rng.choice(T, 64, replace=False))
+    take = torch.as_tensor(rows)
+    # The oracle reads host copies of the device buffers; only the rows' keys are needed,
+    # but the SWA batch is small enough to copy whole.
+    qb, kb, vb = (synth.bf16_bits(t) for t in (swa.q, swa.k, swa.v))
+    orc.prefill(qb, kb, vb, swa.cu_seqlens.cpu().numpy(), layer_type=0, scale=scale, sink=swa.sink.cpu().numpy(),
+                rows=rows, nthreads=nth)
+    cu = swa.cu_seqlens.cpu().numpy()
+    pos = rows - cu[np.searchsorted(cu, rows, side="right") - 1]
+    flops += int(np.minimum(pos + 1, W).sum()) * HQ * FLOP_PER_TRIPLE
+    parts.append("64 SWA-prefill query tokens")
+    del take
+    # GA prefill rows: random tokens of the 32768 sequence until the budget's half is used.
+    qb, kb, vb = (synth.bf16_bits(t) for t in (ga.q, ga.k, ga.v))
+    cu = ga.cu_seqlens.cpu().numpy()
+    n_ga = 0
+    while time.perf_counter() - t0 < 0.5 * budget_s and n_ga < 256:
+        r = np.sort(rng.choice(qb.shape[0], 8, replace=False))
+        orc.prefill(qb, kb, vb, cu, layer_type=1, scale=scale, sink=ga.sink.cpu().numpy(), rows=r, nthreads=nth)
+        flops += int((r + 1).sum()) * HQ * FLOP_PER_TRIPLE
+        n_ga += 8
+    parts.append(f"{n_ga} GA-prefill query tokens")
+    del qb, kb, vb
+    # GA decode: whole sequences of the 128-sequence batch until the budget is used.
+    base = dga.kv_base.cpu().numpy()
+    n_dec = 0
+    order = rng.permutation(len(ctx))
+    for b in order:
+        if time.perf_counter() - t0 >= budget_s or n_dec >= 8:
+            break
+        c = int(ctx[b])
+        kc = synth.bf16_bits(dga.k_cache[base[b]:base[b] + c])
+        vc = synth.bf16_bits(dga.v_cache[base[b]:base[b] + c])
+        orc.decode(synth.bf16_bits(dga.q[b:b + 1]), synth.bf16_bits(dga.k_new[b:b + 1]),
+                   synth.bf16_bits(dga.v_new[b:b + 1]), kc, vc, np.array([c], np.int32), layer_type=1, scale=scale,
+                   sink=dga.sink.cpu().numpy(), kv_base=np.zeros(1, np.int64), nthreads=nth)
+        flops += (c + 1) * HQ * FLOP_PER_TRIPLE
+        n_dec += 1
+    parts.append(f"{n_dec} GA-decode sequences")
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": nth, "kind": "oracle",
+            "sample": "; ".join(parts) + f" of the bench workload ({flops / 1e9:.1f} GFLOP in {dt:.1f} s, fp64)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--split", type=int, default=0, help="GA decode split (keys per workgroup), 0 = default")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain 1 GiB device copy (a known-size reference for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this path runs on one MI355X with no collectives)", file=sys.stderr)
+        sys.exit(2)
+    headroom = args.steps + args.warmup + 1
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    log("generating inputs on the device")
+    swa = synth.prefill_inputs([8192] * 4, seed=0, device=dev)
+    ga = synth.prefill_inputs([32768], seed=0, device=dev)
+    ctx0 = synth.long_context_lengths(128, 4096, 262144, seed=0)
+    dga = synth.decode_inputs(ctx0, 1, seed=0, device=dev, headroom=headroom)
+    dswa = synth.decode_inputs(ctx0, 0, seed=0, device=dev)
+    T_swa, T_ga = swa.q.shape[0], ga.q.shape[0]
+    out_swa = torch.empty((T_swa, HQ, DV), dtype=torch.bfloat16, device=dev)
+    lse_swa = torch.empty((T_swa, HQ), dtype=torch.float32, device=dev)
+    out_ga = torch.empty((T_ga, HQ, DV), dtype=torch.bfloat16, device=dev)
+    lse_ga = torch.empty((T_ga, HQ), dtype=torch.float32, device=dev)
+    Bd = len(ctx0)
+    out_d = torch.empty((2, Bd, HQ, DV), dtype=torch.bfloat16, device=dev)
+    lse_d = torch.empty((2, Bd, HQ), dtype=torch.float32, device=dev)
+    ctx_ga = dga.ctx_lens.clone()
+    ctx_swa = dswa.ctx_lens.clone()
+    max_ctx = max(ctx0) + headroom
+    dims = B.make_dims()
+    ws_bytes = B.mimo_attn_decode_workspace_size(dims, 1, Bd, max_ctx, args.split)
+    ws = torch.empty(ws_bytes // 4 + 4, dtype=torch.float32, device=dev)
+    cu_dec = torch.arange(Bd + 1, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    log(f"inputs ready: GA pool {dga.k_cache.numel() * 2 / 1e9 + dga.v_cache.numel() * 2 / 1e9:.1f} GB, "
+        f"workspace {ws_bytes / 1e6:.0f} MB")
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 29, dtype=torch.int16, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)  # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
+        log("copy calibration: 1 GiB device-to-device copy done")
+
+    stream = torch.cuda.current_stream()
+    names = ["prefill_swa", "prefill_ga", "decode_swa", "append_swa", "decode_ga", "append_ga", "ctx_advance"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        B.mimo_attn_prefill(dims, 0, swa.q, swa.k, swa.v, swa.cu_seqlens, 4, 8192, swa.sink, out_swa, lse_swa, stream)
+        mark(1)
+        B.mimo_attn_prefill(dims, 1, ga.q, ga.k, ga.v, ga.cu_seqlens, 1, 32768, ga.sink, out_ga, lse_ga, stream)
+        mark(2)
+        B.mimo_attn_decode(dims, 0, dswa.q, dswa.k_new, dswa.v_new, dswa.k_cache, dswa.v_cache, None, ctx_swa, Bd,
+                           max_ctx, 0, dswa.sink, out_d[0], lse_d[0], None, stream)
+        mark(3)
+        B.mimo_kv_append(dims, 0, dswa.k_new, dswa.v_new, cu_dec, ctx_swa, Bd, Bd, dswa.k_cache, dswa.v_cache, None,
+                         None, stream)
+        mark(4)
+        B.mimo_attn_decode(dims, 1, dga.q, dga.k_new, dga.v_new, dga.k_cache, dga.v_cache, dga.kv_base, ctx_ga, Bd,
+                           max_ctx, args.split, dga.sink, out_d[1], lse_d[1], ws, stream)
+        mark(5)
+        B.mimo_kv_append(dims, 1, dga.k_new, dga.v_new, cu_dec, ctx_ga, Bd, Bd, dga.k_cache, dga.v_cache,
+                         dga.kv_base, dga.kv_capacity, stream)
+        mark(6)
+        ctx_ga.add_(1)
+        ctx_swa.add_(1)
+        mark(7)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"warmup step {i + 1}/{args.warmup} done")
+    # The timed steps start from the contexts the warmup left.
+    ctx_host = [np.asarray(ctx0) + args.warmup + s for s in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"timed {args.steps} steps in {wall:.3f} s")
+
+    per = {n: [] for n in names}
+    for ev in events:
+        for i, n in enumerate(names):
+            per[n].append(ev[i].elapsed_time(ev[i + 1]))  # ms
+    avg = {n: float(np.mean(v)) for n, v in per.items()}
+    step_ms = wall * 1e3 / args.steps
+
+    f_pswa = prefill_pairs([8192] * 4, 0) * HQ * FLOP_PER_TRIPLE
+    f_pga = prefill_pairs([32768], 1) * HQ * FLOP_PER_TRIPLE
+    b_pswa, b_pga = T_swa * TOKEN_BYTES, T_ga * TOKEN_BYTES
+    dec = {lt: [decode_stats(c, lt) for c in ctx_host] for lt in (0, 1)}
+    f_dswa = float(np.mean([d[0] for d in dec[0]]))
+    b_dswa = float(np.mean([d[1] for d in dec[0]]))
+    f_dga = float(np.mean([d[0] for d in dec[1]]))
+    b_dga = float(np.mean([d[1] for d in dec[1]]))
+    app_bytes = 2 * Bd * KV_TOKEN_BYTES
+    total_flops = f_pswa + f_pga + f_dswa + f_dga
+    value = total_flops / (step_ms * 1e-3) / 1e12
+
+    def tf(f, ms):
+        return f / (ms * 1e-3) / 1e12
+
+    def gbs(b, ms):
+        return b / (ms * 1e-3) / 1e9
+
+    breakdown = {
+        "prefill_swa": {"ms": avg["prefill_swa"], "TFLOP/s": tf(f_pswa, avg["prefill_swa"]),
+                        "GB/s": gbs(b_pswa, avg["prefill_swa"]),
+                        "frac_hbm_peak": gbs(b_pswa, avg["prefill_swa"]) / PEAK_HBM_GBPS,
+                        "frac_mfma_peak": tf(f_pswa, avg["prefill_swa"]) / PEAK_BF16_TFLOPS},
+        "prefill_ga": {"ms": avg["prefill_ga"], "TFLOP/s": tf(f_pga, avg["prefill_ga"]),
+                       "frac_mfma_peak": tf(f_pga, avg["prefill_ga"]) / PEAK_BF16_TFLOPS},
+        "decode_swa": {"ms": avg["decode_swa"], "tokens/s": Bd / (avg["decode_swa"] * 1e-3),
+                       "GB/s": gbs(b_dswa, avg["decode_swa"]),
+                       "frac_hbm_peak": gbs(b_dswa, avg["decode_swa"]) / PEAK_HBM_GBPS},
+        "decode_ga": {"ms": avg["decode_ga"], "tokens/s": Bd / (avg["decode_ga"] * 1e-3),
+                      "GB/s": gbs(b_dga, avg["decode_ga"]),
+                      "frac_hbm_peak": gbs(b_dga, avg["decode_ga"]) / PEAK_HBM_GBPS},
+        "append_swa": {"ms": avg["append_swa"], "GB/s": gbs(app_bytes / 2, avg["append_swa"])},
+        "append_ga": {"ms": avg["append_ga"], "GB/s": gbs(app_bytes / 2, avg["append_ga"])},
+        "ctx_advance": {"ms": avg["ctx_advance"]},
+    }
+    # Dominant kernel of the step: the GA prefill launch (MFMA-bound).
+    roof = {"kernel": "prefill_kernel<GA>", "bound": "mfma", "achieved": tf(f_pga, avg["prefill_ga"]),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": tf(f_pga, avg["prefill_ga"]) / PEAK_BF16_TFLOPS,
+            "traffic": None}
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 q/k/v, N(0,1) fp32 sinks; no weights involved)",
+        "config": {"workload": "one hybrid-attention pass: SWA prefill 4x8192 + GA prefill 1x32768 + decode step "
+                               "B=128 ctx~U[4096,262144] (SWA ring 128 slots + GA bf16 pool, attend then append)",
+                   "heads": "64q/4kv", "head_dim_qk": DQK, "head_dim_v": DV, "sliding_window": W,
+                   "global_batch": {"prefill_swa": 4, "prefill_ga": 1, "decode": Bd},
+                   "seq_len": {"prefill_swa": 8192, "prefill_ga": 32768, "decode_ctx_mean": float(np.mean(ctx0))},
+                   "parallelism": "none (1 GPU)"},
+        "breakdown": breakdown,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on a bounded sample (cpu_baseline)")
+        res["cpu_baseline"] = cpu_baseline(swa, ga, dga, ctx0, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
