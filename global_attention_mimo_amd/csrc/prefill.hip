@@ -32,28 +32,39 @@ constexpr int kGroup = 16;         // query heads per KV head
 constexpr int kKStride = kDqk + 8;  // LDS row stride of K tiles (bf16): 400 B, conflict-free b128 reads
 constexpr int kVStride = kDv + 16;  // LDS row stride of V tiles (bf16): 288 B, conflict-free tr reads
 
-template <int NB, int NK, bool SWA>
+// Tile shape of one workgroup: WV waves, each owning NB blocks of 32 query
+// rows (2 tokens x 16 heads), and NK keys per K/V tile.
+template <int WV, int NB, int NK>
 struct PrefillCfg {
-    static constexpr int kWaves = 4;
-    static constexpr int kThreads = 64 * kWaves;
-    static constexpr int kRowsPerWave = 32 * NB;
-    static constexpr int kTokens = kWaves * kRowsPerWave / kGroup;  // query tokens per workgroup
-    static constexpr int kKChunks = NK * (kDqk / 8) / kThreads;      // 16-byte chunks per thread
-    static constexpr int kVChunks = NK * (kDv / 8) / kThreads;
+    static constexpr int kWaves = WV;
+    static constexpr int kThreads = 64 * WV;
+    static constexpr int kTokens = WV * NB * 2;  // query tokens per workgroup
+    static constexpr int kKChunks = NK * (kDqk / 8);  // 16-byte chunks per K tile
+    static constexpr int kVChunks = NK * (kDv / 8);
+    static constexpr int kKPer = (kKChunks + kThreads - 1) / kThreads;
+    static constexpr int kVPer = (kVChunks + kThreads - 1) / kThreads;
+    static constexpr int kLdsK = NK * kKStride;  // bf16 elements per K buffer
+    static constexpr int kLdsV = NK * kVStride;
     static_assert(NK % 32 == 0, "key tile must be a multiple of 32");
-    static_assert(NK * (kDqk / 8) % kThreads == 0 && NK * (kDv / 8) % kThreads == 0, "tile/thread mismatch");
 };
 
-template <int NB, int NK, bool SWA, int WAVES_PER_EU>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
+// The running max is only raised when a row's new maximum exceeds it by more
+// than this many powers of two; until then exp2(s - m) <= 2^8 stays exact
+// enough in fp32 and bf16 and the O/l rescale is skipped.
+constexpr float kRescaleThreshold = 8.0f;
+
+template <int WV, int NB, int NK, bool SWA, int WAVES_PER_EU>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * WV, 64 * WV),
+                          amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
 void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                     const uint16_t* __restrict__ v, const int32_t* __restrict__ cu_seqlens,
                     const float* __restrict__ sink, uint16_t* __restrict__ out, float* __restrict__ lse,
                     int hq, int hkv, int window, float c_log2, float value_scale, int num_qblocks) {
-    using Cfg = PrefillCfg<NB, NK, SWA>;
+    using Cfg = PrefillCfg<WV, NB, NK>;
     constexpr int QT = Cfg::kTokens;
-    __shared__ __attribute__((aligned(16))) uint16_t lds_k[NK * kKStride];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_v[NK * kVStride];
+    // Two K/V buffers: tile t is computed from buffer t%2 while tile t+1 is staged into the other.
+    __shared__ __attribute__((aligned(16))) uint16_t lds_k[2 * Cfg::kLdsK];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_v[2 * Cfg::kLdsV];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -116,57 +127,86 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     const int kt_begin = k_lo / NK;
     const int kt_end = q_last / NK;
 
-    // Global -> register staging of one K/V tile (zero rows past the sequence end).
-    u32x4 kreg[Cfg::kKChunks], vreg[Cfg::kVChunks];
+    // Global -> register staging of one K/V tile.  Each thread always moves the
+    // same (row, 16-byte column) slots of a tile, so its source pointers are
+    // fixed up to the tile's key offset.  Keys past the sequence end are
+    // clamped to its last key: they are masked (key > every query position),
+    // so they only need to be finite.
+    const uint16_t* kp[Cfg::kKPer];
+    const uint16_t* vp[Cfg::kVPer];
+    int krow_of[Cfg::kKPer], vrow_of[Cfg::kVPer];
+#pragma unroll
+    for (int i = 0; i < Cfg::kKPer; ++i) {
+        const int c = min(tid + Cfg::kThreads * i, Cfg::kKChunks - 1);
+        krow_of[i] = c / (kDqk / 8);
+        kp[i] = k + ((size_t)s0 * hkv + g) * kDqk + (c % (kDqk / 8)) * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < Cfg::kVPer; ++i) {
+        const int c = min(tid + Cfg::kThreads * i, Cfg::kVChunks - 1);
+        vrow_of[i] = c / (kDv / 8);
+        vp[i] = v + ((size_t)s0 * hkv + g) * kDv + (c % (kDv / 8)) * 8;
+    }
+    const size_t kstride = (size_t)hkv * kDqk, vstride = (size_t)hkv * kDv;
+    u32x4 kreg[Cfg::kKPer], vreg[Cfg::kVPer];
     auto load_tile = [&](int kt) {
         const int kbase = kt * NK;
+        if (kbase + NK <= L) {
 #pragma unroll
-        for (int i = 0; i < Cfg::kKChunks; ++i) {
-            const int c = tid + Cfg::kThreads * i;
-            const int row = c / (kDqk / 8), col = c % (kDqk / 8);
-            const int key = kbase + row;
-            kreg[i] = key < L ? reinterpret_cast<const u32x4*>(k + ((size_t)(s0 + key) * hkv + g) * kDqk)[col]
-                              : u32x4{0, 0, 0, 0};
-        }
+            for (int i = 0; i < Cfg::kKPer; ++i)
+                kreg[i] = *reinterpret_cast<const u32x4*>(kp[i] + (size_t)(kbase + krow_of[i]) * kstride);
 #pragma unroll
-        for (int i = 0; i < Cfg::kVChunks; ++i) {
-            const int c = tid + Cfg::kThreads * i;
-            const int row = c / (kDv / 8), col = c % (kDv / 8);
-            const int key = kbase + row;
-            vreg[i] = key < L ? reinterpret_cast<const u32x4*>(v + ((size_t)(s0 + key) * hkv + g) * kDv)[col]
-                              : u32x4{0, 0, 0, 0};
+            for (int i = 0; i < Cfg::kVPer; ++i)
+                vreg[i] = *reinterpret_cast<const u32x4*>(vp[i] + (size_t)(kbase + vrow_of[i]) * vstride);
+        } else {
+#pragma unroll
+            for (int i = 0; i < Cfg::kKPer; ++i)
+                kreg[i] = *reinterpret_cast<const u32x4*>(kp[i] + (size_t)min(kbase + krow_of[i], L - 1) * kstride);
+#pragma unroll
+            for (int i = 0; i < Cfg::kVPer; ++i)
+                vreg[i] = *reinterpret_cast<const u32x4*>(vp[i] + (size_t)min(kbase + vrow_of[i], L - 1) * vstride);
         }
     };
-    auto store_tile = [&]() {
+    auto store_tile = [&](int buf) {
+        uint16_t* kb_ = lds_k + buf * Cfg::kLdsK;
+        uint16_t* vb_ = lds_v + buf * Cfg::kLdsV;
 #pragma unroll
-        for (int i = 0; i < Cfg::kKChunks; ++i) {
+        for (int i = 0; i < Cfg::kKPer; ++i) {
             const int c = tid + Cfg::kThreads * i;
-            const int row = c / (kDqk / 8), col = c % (kDqk / 8);
-            *reinterpret_cast<u32x4*>(lds_k + row * kKStride + col * 8) = kreg[i];
+            if (c < Cfg::kKChunks)
+                *reinterpret_cast<u32x4*>(kb_ + (c / (kDqk / 8)) * kKStride + (c % (kDqk / 8)) * 8) = kreg[i];
         }
 #pragma unroll
-        for (int i = 0; i < Cfg::kVChunks; ++i) {
+        for (int i = 0; i < Cfg::kVPer; ++i) {
             const int c = tid + Cfg::kThreads * i;
-            const int row = c / (kDv / 8), col = c % (kDv / 8);
-            *reinterpret_cast<u32x4*>(lds_v + row * kVStride + col * 8) = vreg[i];
+            if (c < Cfg::kVChunks)
+                *reinterpret_cast<u32x4*>(vb_ + (c / (kDv / 8)) * kVStride + (c % (kDv / 8)) * 8) = vreg[i];
         }
     };
 
     load_tile(kt_begin);
-    for (int kt = kt_begin; kt <= kt_end; ++kt) {
-        __syncthreads();  // every wave is done reading the previous tile
-        store_tile();
-        __syncthreads();
-        if (kt < kt_end) load_tile(kt + 1);  // in flight while this tile is computed
+    store_tile(0);
+    __syncthreads();
+    // Source address of this lane for the transposed V reads: row 4*hh + (lane%16)/4
+    // of a K-step, columns 16*((lane/16)%2) + 4*(lane%4) of a 32-column block.
+    const int vsrc_off = (4 * hh + ((lane & 15) >> 2)) * kVStride + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const int ksrc_off = r32 * kKStride + 8 * hh;
 
+    for (int kt = kt_begin; kt <= kt_end; ++kt) {
+        const int buf = (kt - kt_begin) & 1;
+        const bool more = kt < kt_end;
+        if (more) load_tile(kt + 1);  // in flight while this tile is computed
+        const uint16_t* ktile = lds_k + buf * Cfg::kLdsK;
+        const uint16_t* vtile = lds_v + buf * Cfg::kLdsV;
         const int kbase = kt * NK;
+
         // ---- S^T = K * Q^T ---------------------------------------------------
         f32x16 sacc[NK / 32][NB];
 #pragma unroll
         for (int kb = 0; kb < NK / 32; ++kb) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) sacc[kb][nb] = f32x16{};
-            const uint16_t* krow = lds_k + (kb * 32 + r32) * kKStride + 8 * hh;
+            const uint16_t* krow = ktile + kb * 32 * kKStride + ksrc_off;
 #pragma unroll
             for (int s = 0; s < kDqk / 16; ++s) {
                 const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 16 * s);
@@ -174,67 +214,72 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                 for (int nb = 0; nb < NB; ++nb) sacc[kb][nb] = mfma_32x32x16(a, qf[nb][s], sacc[kb][nb]);
             }
         }
-        // ---- mask, online softmax --------------------------------------------
+        // ---- mask, online softmax, P^T -> bf16, O^T += V^T * P^T -----------------
         const bool interior = (kbase + NK - 1 <= q0) && (!SWA || kbase >= q_last - (window - 1));
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
+            // Band/causal mask, only on tiles that cross a boundary: key kk of the
+            // tile sits at offset 32*kb + 8*(r/4) + (r%4) + 4*hh; it is kept when
+            // tok-(W-1) <= key <= tok (GA: no lower bound).
+            if (!interior) {
+                const int hi_off = tok[nb] - kbase - 4 * hh;
+                const int lo_off = SWA ? hi_off - (window - 1) : -(1 << 30);
+#pragma unroll
+                for (int kb = 0; kb < NK / 32; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
+                        const bool ok = off <= hi_off && off >= lo_off;
+                        sacc[kb][nb][r] = ok ? sacc[kb][nb][r] : -__builtin_inff();
+                    }
+            }
+            // Row max over raw scores (c_log2 > 0 preserves order).
             float mx = -__builtin_inff();
 #pragma unroll
-            for (int kb = 0; kb < NK / 32; ++kb) {
+            for (int kb = 0; kb < NK / 32; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float s = sacc[kb][nb][r] * c_log2;
-                    if (!interior) {
-                        const int key = kbase + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                        const bool ok = key <= tok[nb] && (!SWA || key >= tok[nb] - (window - 1));
-                        s = ok ? s : -__builtin_inff();
-                    }
-                    sacc[kb][nb][r] = s;
-                    mx = fmaxf(mx, s);
-                }
-            }
+                for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[kb][nb][r], sacc[kb][nb][r + 1]));
             mx = max_with_partner_half(mx);
-            const float m_new = fmaxf(m_run[nb], mx);
-            const float alpha = fast_exp2(m_run[nb] - m_new);
+            const float m_cand = fmaxf(m_run[nb], mx * c_log2);
+            if (__builtin_amdgcn_ballot_w64(m_cand > m_run[nb] + kRescaleThreshold)) {
+                const float alpha = fast_exp2(m_run[nb] - m_cand);
+                l_run[nb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < kDv / 32; ++db) oacc[db][nb] *= alpha;
+                m_run[nb] = m_cand;
+            }
+            const float neg_m = -m_run[nb];
             float rs = 0.0f;
 #pragma unroll
             for (int kb = 0; kb < NK / 32; ++kb) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float p = fast_exp2(sacc[kb][nb][r] - m_new);
+                    const float p = fast_exp2(__builtin_fmaf(sacc[kb][nb][r], c_log2, neg_m));
                     sacc[kb][nb][r] = p;
                     rs += p;
                 }
             }
-            l_run[nb] = l_run[nb] * alpha + rs;
-            m_run[nb] = m_new;
-#pragma unroll
-            for (int db = 0; db < kDv / 32; ++db) oacc[db][nb] *= alpha;
-        }
-        // ---- O^T += V^T * P^T ------------------------------------------------
-        bf16x8 pf[NK / 16][NB];
-#pragma unroll
-        for (int ks = 0; ks < NK / 16; ++ks)
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const f32x16& sv = sacc[ks >> 1][nb];
-                const int o = 8 * (ks & 1);
-                pf[ks][nb] = pack_bf16x8(sv[o + 0], sv[o + 1], sv[o + 2], sv[o + 3], sv[o + 4], sv[o + 5],
-                                         sv[o + 6], sv[o + 7]);
-            }
-        // Source address of this lane for the transposed V reads: row 4*hh + (lane%16)/4
-        // of the K-step, columns 16*((lane/16)%2) + 4*(lane%4) of the 32-column block.
-        const uint16_t* vsrc = lds_v + (4 * hh + ((lane & 15) >> 2)) * kVStride + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll
-        for (int db = 0; db < kDv / 32; ++db) {
+            l_run[nb] += rs;
+            bf16x8 pf[NK / 16];
 #pragma unroll
             for (int ks = 0; ks < NK / 16; ++ks) {
-                const uint16_t* p = vsrc + ks * 16 * kVStride + db * 32;
-                const bf16x8 a = join_tr(lds_read_tr16(p), lds_read_tr16(p + 8 * kVStride));
+                const f32x16& sv = sacc[ks >> 1][nb];
+                const int o = 8 * (ks & 1);
+                pf[ks] = pack_bf16x8(sv[o + 0], sv[o + 1], sv[o + 2], sv[o + 3], sv[o + 4], sv[o + 5], sv[o + 6],
+                                     sv[o + 7]);
+            }
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) oacc[db][nb] = mfma_32x32x16(a, pf[ks][nb], oacc[db][nb]);
+            for (int db = 0; db < kDv / 32; ++db) {
+#pragma unroll
+                for (int ks = 0; ks < NK / 16; ++ks) {
+                    const uint16_t* p = vtile + vsrc_off + ks * 16 * kVStride + db * 32;
+                    const bf16x8 a = join_tr(lds_read_tr16(p), lds_read_tr16(p + 8 * kVStride));
+                    oacc[db][nb] = mfma_32x32x16(a, pf[ks], oacc[db][nb]);
+                }
             }
         }
+        if (more) store_tile(buf ^ 1);
+        __syncthreads();
     }
 
     // ---- epilogue --------------------------------------------------------------
@@ -259,23 +304,37 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
 }
 
-template <int NB, int NK, bool SWA, int WPE>
+template <int WV, int NB, int NK, bool SWA, int WPE>
 hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
-    using Cfg = PrefillCfg<NB, NK, SWA>;
+    using Cfg = PrefillCfg<WV, NB, NK>;
     const int nqb = (a.max_seqlen + Cfg::kTokens - 1) / Cfg::kTokens;
     dim3 grid(nqb, a.hkv, a.num_seqs);
-    hipLaunchKernelGGL((prefill_kernel<NB, NK, SWA, WPE>), grid, dim3(Cfg::kThreads), 0, stream, a.q, a.k, a.v,
+    hipLaunchKernelGGL((prefill_kernel<WV, NB, NK, SWA, WPE>), grid, dim3(Cfg::kThreads), 0, stream, a.q, a.k, a.v,
                        a.cu_seqlens, a.sink, a.out, a.lse, a.hq, a.hkv, a.window, a.softmax_scale * kLog2e,
                        a.value_scale, nqb);
     return hipGetLastError();
 }
 
+// Tile configurations (waves per workgroup, 32-row blocks per wave, keys per
+// tile, waves per SIMD), overridable at build time for tuning sweeps.
+#ifndef MIMO_GA_CFG
+#define MIMO_GA_CFG 8, 1, 64, 2
+#endif
+#ifndef MIMO_SWA_CFG
+#define MIMO_SWA_CFG 4, 1, 32, 2
+#endif
+
+template <int WV, int NB, int NK, int WPE>
+hipError_t launch_ga(const PrefillArgs& a, hipStream_t s) { return launch<WV, NB, NK, false, WPE>(a, s); }
+template <int WV, int NB, int NK, int WPE>
+hipError_t launch_swa(const PrefillArgs& a, hipStream_t s) { return launch<WV, NB, NK, true, WPE>(a, s); }
+
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     if (a.max_seqlen <= 0) return hipSuccess;
-    if (a.swa) return launch<2, 32, true, 1>(a, stream);
-    return launch<2, 32, false, 1>(a, stream);
+    if (a.swa) return launch_swa<MIMO_SWA_CFG>(a, stream);
+    return launch_ga<MIMO_GA_CFG>(a, stream);
 }
 
 }  // namespace mimo

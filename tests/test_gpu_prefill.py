@@ -64,10 +64,17 @@ def test_value_scale():
 
 
 def test_swa_with_wide_window_equals_ga():
+    """SWA with a window covering the whole sequence is GA.  The two layer types
+    run different tile shapes (different fp32 summation order), so they agree
+    to rounding, and each matches the GA oracle."""
     x = synth.prefill_inputs([150, 90], seed=7)
     o_s, l_s = gpu_prefill(x, SWA, window=200)
     o_g, l_g = gpu_prefill(x, GA)
-    assert torch.equal(o_s, o_g) and torch.equal(l_s, l_g)
+    ref_o, ref_l = oracle_prefill(x, GA)
+    compare(o_s, l_s, ref_o, ref_l, "SWA window 200 vs GA oracle")
+    compare(o_g, l_g, ref_o, ref_l, "GA vs GA oracle")
+    assert (o_s.float() - o_g.float()).abs().max().item() <= 1.6e-2
+    assert (l_s - l_g).abs().max().item() <= 1e-4
 
 
 def test_deterministic():
