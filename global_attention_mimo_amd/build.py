@@ -53,7 +53,7 @@ def build(verbose: bool = False) -> str:
                 print(msg, file=sys.stderr)
         if failed:
             raise RuntimeError("hipcc failed:\n" + "\n".join(failed))
-        tmp_lib = LIBRARY + ".tmp"
+        tmp_lib = f"{LIBRARY}.{os.getpid()}.tmp"
         cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:

@@ -112,6 +112,12 @@ int mimo_attn_decode(const mimo_attn_dims* dims, int layer_type, const uint16_t*
     if (!k_cache || !v_cache) return fail(MIMO_ERR_INVALID_ARG, "k_cache and v_cache must be non-NULL");
     if (!aligned16(k_cache) || !aligned16(v_cache))
         return fail(MIMO_ERR_INVALID_ARG, "k_cache and v_cache must be 16-byte aligned");
+    // The kernels address a sequence's cache rows with 32-bit byte offsets.
+    const int64_t row_bytes = (int64_t)dims->num_kv_heads * dims->head_dim_qk * 2;
+    const int64_t rows = layer_type == MIMO_LAYER_SWA ? (int64_t)dims->sliding_window : (int64_t)max_ctx + 1;
+    if (rows * row_bytes > INT32_MAX)
+        return fail(MIMO_ERR_UNSUPPORTED, "a sequence's cached keys exceed 2 GiB (%lld rows of %lld bytes)",
+                    (long long)rows, (long long)row_bytes);
     const int split = effective_split(split_tokens);
     mimo::DecodeArgs a{q, k_new, v_new, k_cache, v_cache, kv_base, ctx_lens, sink, out, lse, workspace, batch,
                        max_ctx, split, dims->num_q_heads, dims->num_kv_heads, dims->sliding_window,

@@ -8,24 +8,27 @@
 // heads, head_dim 192 for q/k and 128 for v (MiMoV2FlashConfig).
 //
 // Shared building block: one wave attends the 16 query heads of one KV group
-// (GQA packing into the MFMA N dimension) over a 32-key tile with
-// v_mfma_f32_16x16x32_bf16: S^T = K*Q^T with K fragments loaded straight from
-// HBM into registers (16 B per lane), then an online softmax whose row
-// reductions cross only the four 16-lane groups, then O^T += V^T*P^T where the
-// V tile is written row-major to wave-private LDS and read transposed with
-// ds_read_b64_tr_b16.  The next tile's loads are issued before the current
-// tile is computed.
+// (GQA packing into the MFMA N dimension) over 32-key tiles with
+// v_mfma_f32_16x16x32_bf16.  Loads go through buffer descriptors whose record
+// count ends at the last cached key of the sequence: rows past it read as
+// zero, so there are no per-key branches, and a tile's position is a scalar
+// offset.  K rows are loaded straight into MFMA A-operand registers; V rows are
+// loaded into registers, written to a wave-private LDS tile (row-major, the
+// 16-byte chunks of row r XOR-swizzled by 2*(r%4) so the transposed reads are
+// bank-conflict free) and read back transposed with ds_read_b64_tr_b16.  Two
+// tiles are in flight per wave: the next tile's loads are issued before the
+// current one is computed.
 //
-// SWA decode (one workgroup per (sequence, KV group)): the 128 ring slots plus
-// the new token are 129 "virtual keys" in 32-key tiles spread over the 4
-// waves, so every load of the window is issued at once; the waves' partial
-// (m, l, O) are merged in LDS together with the sink.
+// SWA decode (one workgroup per (sequence, KV group)): the ring slots are
+// split into 32-key tiles over the 4 waves, the new token is one more tile,
+// and the waves' partial (m, l, O) are merged in LDS together with the sink.
 //
 // GA decode: split-K.  Workgroup (split s, sequence b) covers keys
-// [s*C, (s+1)*C) of the sequence with one wave per KV group, streaming the
-// pool rows (each 384 B of K and 256 B of V) and writing an unnormalised
-// partial (m, l, O) without the sink.  A second kernel merges the splits of
-// each (sequence, head), adds the sink exactly once, and writes O and LSE.
+// [s*C, (s+1)*C) of the sequence with one wave per KV group, streaming pool
+// rows (384 B of K and 256 B of V per group) and writing an unnormalised
+// partial (m, l, O) without the sink; the split holding position p adds the
+// new token as its last tile.  A second kernel merges the splits of each
+// (sequence, head), adds the sink exactly once, and writes O and LSE.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -35,9 +38,28 @@ namespace {
 constexpr int kDqk = 192;
 constexpr int kDv = 128;
 constexpr int kGroup = 16;
-constexpr int kTile = 32;              // keys per wave tile
-constexpr int kVStride = kDv + 16;     // LDS row stride (bf16) of a V tile: 288 B
-constexpr int kWaveLds = kTile * kVStride;
+constexpr int kTile = 32;                         // keys per wave tile
+constexpr int kVTileBytes = kTile * kDv * 2;      // 8 KB: 32 rows of 256 B
+constexpr int kBlockLdsBytes = 4 * kVTileBytes;   // one V tile per wave
+constexpr uint32_t kRsrcWord3 = 0x00020000;       // raw 32-bit buffer, gfx9-family descriptor
+#ifndef MIMO_GA_DECODE_DEPTH
+#define MIMO_GA_DECODE_DEPTH 2
+#endif
+constexpr int kGaDepth = MIMO_GA_DECODE_DEPTH;    // GA split: tiles in flight beyond the current one
+constexpr int kSwaDepth = 1;                      // SWA: a wave owns at most a few tiles
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRsrcWord3);
+}
+
+// One 32-key tile of a wave: where its K and V rows come from.
+struct TileSrc {
+    rsrc_t k, v;     // descriptors; bytes past their record count read as zero
+    int koff, voff;  // byte offset of the tile's first key row (wave-uniform)
+    int nvalid;      // keys [0, nvalid) of the tile are in the key set
+};
 
 // Per-wave running state for 16 heads.  Lane l owns head (l % 16); o[db][r]
 // is O^T[dv = 16*db + 4*(l/16) + r][head]; m is the same in the 4 lanes of a
@@ -47,68 +69,77 @@ struct WaveAcc {
     float m, l;
 };
 
-struct TileRegs {
-    u32x4 k[2 * (kDqk / 32)];  // K rows (16*blk + lane%16), 16 B chunk 4*st + lane/16
-    u32x4 v[kTile * (kDv / 8) / 64];  // V rows (lane/16 + 4*i), 16 B chunk lane%16
+// Lane-constant byte offsets inside a tile.  K: lane l supplies MFMA A rows
+// key = l%16 (+16 for the second block), d = 8*(l/16) .. +7 of each 32-wide
+// K-step (the K-step adds 64 bytes).  V: load i takes key 4i + l/16, 16-byte
+// chunk l%16 of that row.
+struct LaneOffsets {
+    int k0, k1, v;
 };
 
-// Loads the K/V rows of tile keys j0..j0+31 into registers.  src.krow(j) and
-// src.vrow(j) give row pointers, or nullptr for keys outside the key set
-// (their registers are zero).
-template <class Src>
-__device__ __forceinline__ void load_tile(TileRegs& t, const Src& src, int j0, int lane) {
+__device__ __forceinline__ LaneOffsets lane_offsets(int lane, int g, int rowk, int rowv) {
     const int G = lane >> 4;
+    LaneOffsets o;
+    o.k0 = (lane & 15) * rowk + g * (kDqk * 2) + G * 16;
+    o.k1 = o.k0 + 16 * rowk;
+    o.v = G * rowv + g * (kDv * 2) + (lane & 15) * 16;
+    return o;
+}
+
+__device__ __forceinline__ void issue_k(const TileSrc& t, const LaneOffsets& lo, u32x4 (&k)[12]) {
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-        const uint16_t* kp = src.krow(j0 + 16 * blk + (lane & 15));
-#pragma unroll
-        for (int st = 0; st < kDqk / 32; ++st)
-            t.k[blk * (kDqk / 32) + st] = kp ? reinterpret_cast<const u32x4*>(kp)[4 * st + G] : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int i = 0; i < kTile * (kDv / 8) / 64; ++i) {
-        const uint16_t* vp = src.vrow(j0 + G + 4 * i);
-        t.v[i] = vp ? reinterpret_cast<const u32x4*>(vp)[lane & 15] : u32x4{0, 0, 0, 0};
+    for (int st = 0; st < kDqk / 32; ++st) {
+        k[st] = __builtin_amdgcn_raw_buffer_load_b128(t.k, lo.k0 + 64 * st, t.koff, 0);
+        k[6 + st] = __builtin_amdgcn_raw_buffer_load_b128(t.k, lo.k1 + 64 * st, t.koff, 0);
     }
 }
 
-template <class Src>
-__device__ __forceinline__ void attend_tile(WaveAcc& acc, const bf16x8 (&qf)[kDqk / 32], const TileRegs& t,
-                                            uint16_t* lds_v, const Src& src, int j0, float c_log2, int lane) {
-    const int G = lane >> 4;
-    // V rows to wave-private LDS, row-major.
+__device__ __forceinline__ void issue_v(const TileSrc& t, const LaneOffsets& lo, int rowv, u32x4 (&v)[kTile / 4]) {
 #pragma unroll
-    for (int i = 0; i < kTile * (kDv / 8) / 64; ++i)
-        *reinterpret_cast<u32x4*>(lds_v + (G + 4 * i) * kVStride + (lane & 15) * 8) = t.v[i];
-    wave_lds_fence();
+    for (int i = 0; i < kTile / 4; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(t.v, lo.v, t.voff + 4 * i * rowv, 0);
+}
 
+// V rows to the wave's LDS tile: row 4i + G, logical chunk lane%16 stored at
+// chunk position (lane%16) ^ 2G.  The previous tile's transposed reads were
+// issued earlier by this wave, and a wave's LDS operations run in order.
+__device__ __forceinline__ void stage_v(const u32x4 (&v)[kTile / 4], char* vbuf, int lane) {
+    const int G = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < kTile / 4; ++i)
+        *reinterpret_cast<u32x4*>(vbuf + (4 * i + G) * (kDv * 2) + (((lane & 15) ^ (2 * G)) * 16)) = v[i];
+    wave_lds_fence();
+}
+
+// One tile whose K rows are in `k` and whose V rows are staged in `vbuf`.
+__device__ __forceinline__ void attend_tile(WaveAcc& acc, const bf16x8 (&qf)[kDqk / 32], const u32x4 (&k)[12],
+                                            const char* vbuf, int nvalid, float c_log2, int lane) {
+    const int G = lane >> 4;
     f32x4 s[2] = {f32x4{}, f32x4{}};
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int st = 0; st < kDqk / 32; ++st)
-            s[blk] = mfma_16x16x32(__builtin_bit_cast(bf16x8, t.k[blk * (kDqk / 32) + st]), qf[st], s[blk]);
-
+    for (int st = 0; st < kDqk / 32; ++st) {
+        s[0] = mfma_16x16x32(__builtin_bit_cast(bf16x8, k[st]), qf[st], s[0]);
+        s[1] = mfma_16x16x32(__builtin_bit_cast(bf16x8, k[6 + st]), qf[st], s[1]);
+    }
+    // Key of s[blk][r] inside the tile: 16*blk + 4*G + r.
     float mx = -__builtin_inff();
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const bool ok = src.valid(j0 + 16 * blk + 4 * G + r);
-            const float x = ok ? s[blk][r] * c_log2 : -__builtin_inff();
+            const float x = (16 * blk + 4 * G + r < nvalid) ? s[blk][r] : -__builtin_inff();
             s[blk][r] = x;
             mx = fmaxf(mx, x);
         }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(acc.m, mx);
+    const float m_new = fmaxf(acc.m, mx * c_log2);
     const float alpha = fast_exp2(acc.m - m_new);
     float rs = 0.0f;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float p = fast_exp2(s[blk][r] - m_new);
+            const float p = fast_exp2(__builtin_fmaf(s[blk][r], c_log2, -m_new));
             s[blk][r] = p;
             rs += p;
         }
@@ -116,14 +147,71 @@ __device__ __forceinline__ void attend_tile(WaveAcc& acc, const bf16x8 (&qf)[kDq
     acc.m = m_new;
     // P^T as the B operand: position 8*G + t holds key 4*G + t (t < 4) or 16 + 4*G + t - 4.
     const bf16x8 pf = pack_bf16x8(s[0][0], s[0][1], s[0][2], s[0][3], s[1][0], s[1][1], s[1][2], s[1][3]);
-    const uint16_t* vsrc = lds_v + (4 * G + ((lane & 15) >> 2)) * kVStride + 4 * (lane & 3);
+    // V^T as the A operand, transposed out of the swizzled row-major tile: this
+    // lane addresses row 4*G + t' (t' = (lane%16)/4), columns 16*db + 4*(lane%4).
+    const int tq = (lane & 15) >> 2;
+    const char* vrow = vbuf + (4 * G + tq) * (kDv * 2) + 8 * (lane & 3);
 #pragma unroll
     for (int db = 0; db < kDv / 16; ++db) {
-        const uint16_t* p = vsrc + 16 * db;
-        const bf16x8 a = join_tr(lds_read_tr16(p), lds_read_tr16(p + 16 * kVStride));
+        const char* p = vrow + 32 * (db ^ tq);
+        const bf16x8 a = join_tr(lds_read_tr16(reinterpret_cast<const uint16_t*>(p)),
+                                 lds_read_tr16(reinterpret_cast<const uint16_t*>(p + 16 * kDv * 2)));
         acc.o[db] = mfma_16x16x32(a, pf, acc.o[db] * alpha);
     }
     wave_lds_fence();  // the next tile's V writes come after these reads
+}
+
+// Runs tiles 0..ntiles-1 (get(i) describes tile i) with the loads of the next
+// D tiles in flight: D + 1 register sets rotate, and tile i+D is issued right
+// before tile i is staged and computed.  Every step issues its loads
+// unconditionally: past the last tile, get() returns an empty tile (a
+// descriptor with no records, so the loads return zeros without touching
+// memory, and no valid key, so the attention update is an exact no-op).  The
+// count of loads in flight is then the same on every path, which keeps the
+// compiler's vmcnt bookkeeping exact.
+template <int D, class GetTile>
+__device__ __forceinline__ void run_tiles(WaveAcc& acc, const bf16x8 (&qf)[kDqk / 32], char* vbuf, int ntiles,
+                                          const GetTile& get, const LaneOffsets& lo, int rowv, float c_log2,
+                                          int lane) {
+    if (ntiles <= 0) return;
+    u32x4 kr[D + 1][12], vr[D + 1][kTile / 4];
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+        const TileSrc t = get(j);
+        issue_k(t, lo, kr[j]);
+        issue_v(t, lo, rowv, vr[j]);
+    }
+    for (int i0 = 0; i0 < ntiles; i0 += D + 1) {
+#pragma unroll
+        for (int j = 0; j <= D; ++j) {
+            const TileSrc t = get(i0 + j + D);
+            issue_k(t, lo, kr[(j + D) % (D + 1)]);
+            issue_v(t, lo, rowv, vr[(j + D) % (D + 1)]);
+            stage_v(vr[j], vbuf, lane);
+            attend_tile(acc, qf, kr[j], vbuf, get(i0 + j).nvalid, c_log2, lane);
+        }
+    }
+}
+
+// At most two tiles (a wave's share of a ring of up to 224 slots plus the
+// new token): both tiles' loads are issued up front, unconditionally (tile 1
+// may be empty), and only the second tile's compute depends on ntiles.
+template <class GetTile>
+__device__ __forceinline__ void run_two_tiles(WaveAcc& acc, const bf16x8 (&qf)[kDqk / 32], char* vbuf, int ntiles,
+                                              const GetTile& get, const LaneOffsets& lo, int rowv, float c_log2,
+                                              int lane) {
+    u32x4 ka[12], kb[12], v[kTile / 4];
+    const TileSrc t0 = get(0), t1 = get(1);
+    issue_k(t0, lo, ka);
+    issue_v(t0, lo, rowv, v);
+    issue_k(t1, lo, kb);
+    stage_v(v, vbuf, lane);
+    issue_v(t1, lo, rowv, v);  // tile 1's V reuses the registers tile 0's V was staged from
+    attend_tile(acc, qf, ka, vbuf, ntiles > 0 ? t0.nvalid : 0, c_log2, lane);
+    if (ntiles > 1) {
+        stage_v(v, vbuf, lane);
+        attend_tile(acc, qf, kb, vbuf, t1.nvalid, c_log2, lane);
+    }
 }
 
 // Q^T fragments of the 16 heads of group g for batch row b: lane holds
@@ -141,69 +229,68 @@ __device__ __forceinline__ void acc_init(WaveAcc& acc) {
     acc.l = 0.0f;
 }
 
-// Runs tiles j0 = first, first + stride, ... < end with one tile of loads in flight.
-template <class Src>
-__device__ __forceinline__ void run_tiles(WaveAcc& acc, const bf16x8 (&qf)[kDqk / 32], uint16_t* lds_v,
-                                          const Src& src, int first, int stride, int end, float c_log2,
-                                          int lane) {
-    if (first >= end) return;
-    TileRegs cur, nxt;
-    load_tile(cur, src, first, lane);
-    for (int j0 = first; j0 < end; j0 += stride) {
-        const bool more = j0 + stride < end;
-        if (more) load_tile(nxt, src, j0 + stride, lane);
-        attend_tile(acc, qf, cur, lds_v, src, j0, c_log2, lane);
-        if (more) cur = nxt;
+__device__ __forceinline__ float sink_log2(const float* sink, int head, bool& has) {
+    has = false;
+    if (!sink) return kNoMax;
+    const float sv = sink[head] * kLog2e;
+    if (sv > -__builtin_inff()) {
+        has = true;
+        return sv;
     }
+    return kNoMax;
 }
 
 // ---------------------------------------------------------------------------
-// SWA: virtual key j < R is ring slot j, virtual key R is the new token.
-struct SwaSource {
-    const uint16_t* ring_k;  // this sequence's ring, group g already applied
-    const uint16_t* ring_v;
-    const uint16_t* new_k;
-    const uint16_t* new_v;
-    int R, p, hkv;
-    // Slot j holds position p-R+((j-p) mod R); it is in the window unless that
-    // position is negative, i.e. unless p < R and j >= p.
-    __device__ bool valid(int j) const { return j < R ? (p >= R || j < p) : j == R; }
-    __device__ const uint16_t* krow(int j) const {
-        if (!valid(j)) return nullptr;
-        return j == R ? new_k : ring_k + (size_t)j * hkv * kDqk;
-    }
-    __device__ const uint16_t* vrow(int j) const {
-        if (!valid(j)) return nullptr;
-        return j == R ? new_v : ring_v + (size_t)j * hkv * kDv;
-    }
-};
-
-__global__ __launch_bounds__(256) void swa_decode_kernel(
+// kShortRing: the ring has at most 224 slots, so every wave owns at most two tiles.
+template <bool kShortRing>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(kShortRing ? 2 : 1, kShortRing ? 2 : 1))) void swa_decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const uint16_t* __restrict__ ring_k, const uint16_t* __restrict__ ring_v, const int32_t* __restrict__ ctx_lens,
     const float* __restrict__ sink, uint16_t* __restrict__ out, float* __restrict__ lse, int hq, int hkv, int R,
     float c_log2, float value_scale) {
-    // V staging for 4 waves, reused afterwards for the cross-wave merge.
-    __shared__ __attribute__((aligned(16))) uint16_t lds[4 * kWaveLds];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // V tiles of the 4 waves, reused afterwards for the cross-wave merge.
+    __shared__ __attribute__((aligned(1024))) char lds[kBlockLdsBytes];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int b = blockIdx.x, g = blockIdx.y;
     const int p = ctx_lens[b];
+    const int rowk = hkv * kDqk * 2, rowv = hkv * kDv * 2;
 
     bf16x8 qf[kDqk / 32];
     load_q(qf, q, b, g, hq, lane);
-    SwaSource src{ring_k + ((size_t)b * R * hkv + g) * kDqk, ring_v + ((size_t)b * R * hkv + g) * kDv,
-                  k_new + ((size_t)b * hkv + g) * kDqk, v_new + ((size_t)b * hkv + g) * kDv, R, p, hkv};
+    // Slot j holds position p-R+((j-p) mod R); all R slots are in the window
+    // once p >= R, otherwise slots 0..p-1 are.
+    const int nring = min(p, R);
+    const rsrc_t rk = make_rsrc(ring_k + (size_t)b * R * hkv * kDqk, (uint32_t)nring * rowk);
+    const rsrc_t rv = make_rsrc(ring_v + (size_t)b * R * hkv * kDv, (uint32_t)nring * rowv);
+    const rsrc_t nk = make_rsrc(k_new + (size_t)b * hkv * kDqk, (uint32_t)rowk);
+    const rsrc_t nv = make_rsrc(v_new + (size_t)b * hkv * kDv, (uint32_t)rowv);
+    const int ring_tiles = (R + kTile - 1) / kTile;
+    const int mine = (ring_tiles - wave + 3) / 4;             // ring tiles wave, wave+4, ...
+    const int ntiles = mine + (wave == ring_tiles % 4 ? 1 : 0);  // plus the new token's tile
+    const rsrc_t none = make_rsrc(k_new, 0);
+    auto get = [&](int i) -> TileSrc {
+        if (i < mine) {
+            const int rt = wave + 4 * i;
+            return TileSrc{rk, rv, rt * kTile * rowk, rt * kTile * rowv, min(max(nring - rt * kTile, 0), kTile)};
+        }
+        if (i < ntiles) return TileSrc{nk, nv, 0, 0, 1};
+        return TileSrc{none, none, 0, 0, 0};
+    };
+    const LaneOffsets lo = lane_offsets(lane, g, rowk, rowv);
     WaveAcc acc;
     acc_init(acc);
-    run_tiles(acc, qf, lds + wave * kWaveLds, src, wave * kTile, 4 * kTile, R + 1, c_log2, lane);
+    if constexpr (kShortRing)
+        run_two_tiles(acc, qf, lds + wave * kVTileBytes, ntiles, get, lo, rowv, c_log2, lane);
+    else
+        run_tiles<kSwaDepth>(acc, qf, lds + wave * kVTileBytes, ntiles, get, lo, rowv, c_log2, lane);
     acc.l += __shfl_xor(acc.l, 16);
     acc.l += __shfl_xor(acc.l, 32);
 
     // Merge the 4 waves: per wave 16 x (m, l) and O [16 heads][128 dv] in fp32.
     __syncthreads();
-    float* mrg = reinterpret_cast<float*>(lds);
-    float* mrg_ml = mrg;                      // [wave][16][2]
-    float* mrg_o = mrg + 4 * kGroup * 2;      // [wave][16][128]
+    float* mrg_ml = reinterpret_cast<float*>(lds);  // [wave][16][2]
+    float* mrg_o = mrg_ml + 4 * kGroup * 2;         // [wave][16][128]
     const int G = lane >> 4, h = lane & 15;
     if (G == 0) {
         mrg_ml[(wave * kGroup + h) * 2 + 0] = acc.m;
@@ -214,16 +301,12 @@ __global__ __launch_bounds__(256) void swa_decode_kernel(
         *reinterpret_cast<f32x4*>(mrg_o + (wave * kGroup + h) * kDv + 16 * db + 4 * G) = acc.o[db];
     __syncthreads();
 
-    const int hl = tid >> 4;          // local head 0..15
-    const int e0 = (tid & 15) * 8;    // 8 output columns
+    const int hl = tid >> 4;        // local head 0..15
+    const int e0 = (tid & 15) * 8;  // 8 output columns
     const int head = g * kGroup + hl;
-    float sl = kNoMax;
-    bool has = false;
-    if (sink) {
-        const float sv = sink[head] * kLog2e;
-        if (sv > -__builtin_inff()) { sl = sv; has = true; }
-    }
-    float M = has ? sl : kNoMax;
+    bool has;
+    const float sl = sink_log2(sink, head, has);
+    float M = sl;
 #pragma unroll
     for (int w = 0; w < 4; ++w) M = fmaxf(M, mrg_ml[(w * kGroup + hl) * 2]);
     float Z = has ? fast_exp2(sl - M) : 0.0f;
@@ -244,47 +327,46 @@ __global__ __launch_bounds__(256) void swa_decode_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// GA: keys [k0, k1) of one sequence; position j < p from the pool, j == p new.
-struct GaSource {
-    const uint16_t* pool_k;  // row kv_base[b] of the pool, group g applied
-    const uint16_t* pool_v;
-    const uint16_t* new_k;
-    const uint16_t* new_v;
-    int k1, p, hkv;
-    __device__ bool valid(int j) const { return j < k1; }
-    __device__ const uint16_t* krow(int j) const {
-        if (j >= k1) return nullptr;
-        return j == p ? new_k : pool_k + (size_t)j * hkv * kDqk;
-    }
-    __device__ const uint16_t* vrow(int j) const {
-        if (j >= k1) return nullptr;
-        return j == p ? new_v : pool_v + (size_t)j * hkv * kDv;
-    }
-};
-
-__global__ __launch_bounds__(256) void ga_split_kernel(
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void ga_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const uint16_t* __restrict__ pool_k, const uint16_t* __restrict__ pool_v, const int64_t* __restrict__ kv_base,
     const int32_t* __restrict__ ctx_lens, int hq, int hkv, int split, int nsplit, float c_log2,
     float* __restrict__ ws_ml, float* __restrict__ ws_o) {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[4 * kWaveLds];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __shared__ __attribute__((aligned(1024))) char lds[kBlockLdsBytes];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int s = blockIdx.x, b = blockIdx.y;
     const int g = blockIdx.z * 4 + wave;
     if (g >= hkv) return;
     const int p = ctx_lens[b];
     const int k0 = s * split;
     if (k0 > p) return;
-    const int k1 = min(k0 + split, p + 1);
+    const int k1 = min(k0 + split, p + 1);  // keys [k0, k1) of this split
+    const int kend = min(k1, p);            // of which [k0, kend) live in the pool
+    const int rowk = hkv * kDqk * 2, rowv = hkv * kDv * 2;
 
     bf16x8 qf[kDqk / 32];
     load_q(qf, q, b, g, hq, lane);
     const size_t base = (size_t)kv_base[b];
-    GaSource src{pool_k + (base * hkv + g) * kDqk, pool_v + (base * hkv + g) * kDv,
-                 k_new + ((size_t)b * hkv + g) * kDqk, v_new + ((size_t)b * hkv + g) * kDv, k1, p, hkv};
+    const rsrc_t pk = make_rsrc(pool_k + base * hkv * kDqk, (uint32_t)p * rowk);
+    const rsrc_t pv = make_rsrc(pool_v + base * hkv * kDv, (uint32_t)p * rowv);
+    const rsrc_t nk = make_rsrc(k_new + (size_t)b * hkv * kDqk, (uint32_t)rowk);
+    const rsrc_t nv = make_rsrc(v_new + (size_t)b * hkv * kDv, (uint32_t)rowv);
+    const int npool = (kend - k0 + kTile - 1) / kTile;
+    const int ntiles = npool + (p < k1 ? 1 : 0);
+    const rsrc_t none = make_rsrc(k_new, 0);
+    auto get = [&](int i) -> TileSrc {
+        if (i < npool) {
+            const int j0 = k0 + i * kTile;
+            return TileSrc{pk, pv, j0 * rowk, j0 * rowv, min(kend - j0, kTile)};
+        }
+        if (i < ntiles) return TileSrc{nk, nv, 0, 0, 1};
+        return TileSrc{none, none, 0, 0, 0};
+    };
+    const LaneOffsets lo = lane_offsets(lane, g, rowk, rowv);
     WaveAcc acc;
     acc_init(acc);
-    run_tiles(acc, qf, lds + wave * kWaveLds, src, k0, kTile, k1, c_log2, lane);
+    run_tiles<kGaDepth>(acc, qf, lds + wave * kVTileBytes, ntiles, get, lo, rowv, c_log2, lane);
     acc.l += __shfl_xor(acc.l, 16);
     acc.l += __shfl_xor(acc.l, 32);
 
@@ -298,49 +380,43 @@ __global__ __launch_bounds__(256) void ga_split_kernel(
     for (int db = 0; db < kDv / 16; ++db) *reinterpret_cast<f32x4*>(ws_o + row * kDv + 16 * db + 4 * G) = acc.o[db];
 }
 
-// Merge of the splits of one sequence: block (b, 64-head chunk), thread = (head, 32 columns).
+// Merge of the splits of one sequence: block (b, 16 heads), thread = (head, 8 columns).
 __global__ __launch_bounds__(256) void ga_combine_kernel(const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
                                                          const int32_t* __restrict__ ctx_lens, const float* __restrict__ sink,
                                                          uint16_t* __restrict__ out, float* __restrict__ lse, int hq,
                                                          int split, int nsplit, float value_scale) {
     const int b = blockIdx.x;
-    const int head = blockIdx.y * 64 + (threadIdx.x >> 2);
+    const int head = blockIdx.y * kGroup + (threadIdx.x >> 4);
     if (head >= hq) return;
-    const int e0 = (threadIdx.x & 3) * 32;
+    const int e0 = (threadIdx.x & 15) * 8;
     const int p = ctx_lens[b];
     const int ns = (p + 1 + split - 1) / split;
     uint16_t* orow = out + ((size_t)b * hq + head) * kDv + e0;
     if (ns > nsplit) {  // the grid did not cover this context: refuse loudly
-        const uint16_t nan_bf16 = 0x7fc0;
-        for (int e = 0; e < 32; ++e) orow[e] = nan_bf16;
+        *reinterpret_cast<u32x4*>(orow) = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
         if (lse && e0 == 0) lse[(size_t)b * hq + head] = __builtin_nanf("");
         return;
     }
-    float sl = kNoMax;
-    bool has = false;
-    if (sink) {
-        const float sv = sink[head] * kLog2e;
-        if (sv > -__builtin_inff()) { sl = sv; has = true; }
-    }
-    float M = has ? sl : kNoMax;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, ws_ml[(((size_t)b * nsplit + s) * hq + head) * 2]);
+    bool has;
+    const float sl = sink_log2(sink, head, has);
+    const size_t stride = (size_t)hq;  // rows between consecutive splits of one (b, head)
+    const size_t row0 = (size_t)b * nsplit * hq + head;
+    float M = sl;
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, ws_ml[(row0 + s * stride) * 2]);
     float Z = has ? fast_exp2(sl - M) : 0.0f;
-    f32x4 o[8] = {};
+    f32x4 o0 = {}, o1 = {};
+#pragma unroll 4
     for (int s = 0; s < ns; ++s) {
-        const size_t row = ((size_t)b * nsplit + s) * hq + head;
+        const size_t row = row0 + s * stride;
         const float wt = fast_exp2(ws_ml[row * 2] - M);
         Z += wt * ws_ml[row * 2 + 1];
         const f32x4* src = reinterpret_cast<const f32x4*>(ws_o + row * kDv + e0);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] += wt * src[i];
+        o0 += wt * src[0];
+        o1 += wt * src[1];
     }
     const float inv = value_scale / Z;
-#pragma unroll
-    for (int i = 0; i < 8; i += 2) {
-        u32x4 w = {pack_bf16x2(o[i][0] * inv, o[i][1] * inv), pack_bf16x2(o[i][2] * inv, o[i][3] * inv),
-                   pack_bf16x2(o[i + 1][0] * inv, o[i + 1][1] * inv), pack_bf16x2(o[i + 1][2] * inv, o[i + 1][3] * inv)};
-        *reinterpret_cast<u32x4*>(orow + 4 * i) = w;
-    }
+    *reinterpret_cast<u32x4*>(orow) = u32x4{pack_bf16x2(o0[0] * inv, o0[1] * inv), pack_bf16x2(o0[2] * inv, o0[3] * inv),
+                                           pack_bf16x2(o1[0] * inv, o1[1] * inv), pack_bf16x2(o1[2] * inv, o1[3] * inv)};
     if (lse && e0 == 0) lse[(size_t)b * hq + head] = (M + __log2f(Z)) * kLn2;
 }
 
@@ -348,9 +424,10 @@ __global__ __launch_bounds__(256) void ga_combine_kernel(const float* __restrict
 
 hipError_t launch_decode_swa(const DecodeArgs& a, hipStream_t stream) {
     const int R = a.window - 1;
-    hipLaunchKernelGGL(swa_decode_kernel, dim3(a.batch, a.hkv), dim3(256), 0, stream, a.q, a.k_new, a.v_new,
-                       a.k_cache, a.v_cache, a.ctx_lens, a.sink, a.out, a.lse, a.hq, a.hkv, R,
-                       a.softmax_scale * kLog2e, a.value_scale);
+    const bool short_ring = (R + kTile - 1) / kTile + 1 <= 8;
+    hipLaunchKernelGGL(short_ring ? swa_decode_kernel<true> : swa_decode_kernel<false>, dim3(a.batch, a.hkv),
+                       dim3(256), 0, stream, a.q, a.k_new, a.v_new, a.k_cache, a.v_cache, a.ctx_lens, a.sink, a.out,
+                       a.lse, a.hq, a.hkv, R, a.softmax_scale * kLog2e, a.value_scale);
     return hipGetLastError();
 }
 
@@ -363,7 +440,7 @@ hipError_t launch_decode_ga(const DecodeArgs& a, hipStream_t stream) {
                        a.softmax_scale * kLog2e, ws_ml, ws_o);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(ga_combine_kernel, dim3(a.batch, (a.hq + 63) / 64), dim3(256), 0, stream, ws_ml, ws_o,
+    hipLaunchKernelGGL(ga_combine_kernel, dim3(a.batch, (a.hq + kGroup - 1) / kGroup), dim3(256), 0, stream, ws_ml, ws_o,
                        a.ctx_lens, a.sink, a.out, a.lse, a.hq, a.split, nsplit, a.value_scale);
     return hipGetLastError();
 }

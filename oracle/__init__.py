@@ -34,7 +34,7 @@ ECAPACITY = 2
 
 def build(source: str = SOURCE, output: str = LIBRARY, extra_flags: tuple = ()) -> str:
     """Compile the oracle with gcc (always recompiles)."""
-    tmp = output + ".tmp"
+    tmp = f"{output}.{os.getpid()}.tmp"
     cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared", *extra_flags,
            "-o", tmp, source, "-lpthread", "-lm"]
     subprocess.run(cmd, check=True)

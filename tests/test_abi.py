@@ -101,6 +101,8 @@ def decode_call(L, dims=None, layer=1, q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAK
     (dict(ws=FAKE, ws_bytes=100), B.MIMO_ERR_WORKSPACE),
     (dict(layer=0, dims=B.make_dims(sliding_window=1)), B.MIMO_ERR_INVALID_ARG),
     (dict(dims=B.make_dims(head_dim_qk=64)), B.MIMO_ERR_UNSUPPORTED),
+    (dict(max_ctx=1_400_000), B.MIMO_ERR_UNSUPPORTED),  # > 2 GiB of K rows for one sequence
+    (dict(layer=0, dims=B.make_dims(sliding_window=2_000_000)), B.MIMO_ERR_UNSUPPORTED),
 ])
 def test_decode_rejects(L, case, status):
     assert decode_call(L, **case) == status

@@ -14,10 +14,10 @@ SWA, GA = 0, 1
 SCALE = float(np.float32(synth.SOFTMAX_SCALE))
 
 
-def gpu_decode(x, layer_type, max_ctx=None, split=0, sink="inputs", value_scale=1.0):
+def gpu_decode(x, layer_type, max_ctx=None, split=0, sink="inputs", value_scale=1.0, window=129):
     s = x.sink if isinstance(sink, str) else sink
     mc = int(x.ctx_lens.max()) if max_ctx is None else max_ctx
-    dims = B.make_dims(value_scale=value_scale)
+    dims = B.make_dims(value_scale=value_scale, sliding_window=window)
     out, lse = B.decode(to_dev(x.q), to_dev(x.k_new), to_dev(x.v_new), to_dev(x.k_cache), to_dev(x.v_cache),
                         to_dev(x.ctx_lens), mc, layer_type, sink=to_dev(s), kv_base=to_dev(x.kv_base),
                         split_tokens=split, dims=dims)
@@ -25,10 +25,11 @@ def gpu_decode(x, layer_type, max_ctx=None, split=0, sink="inputs", value_scale=
     return out, lse
 
 
-def oracle_decode(x, layer_type, sink="inputs", value_scale=1.0):
+def oracle_decode(x, layer_type, sink="inputs", value_scale=1.0, window=129):
     s = x.sink if isinstance(sink, str) else sink
     return orc().decode(bits(x.q), bits(x.k_new), bits(x.v_new), bits(x.k_cache), bits(x.v_cache),
-                        x.ctx_lens.cpu().numpy(), layer_type=layer_type, scale=SCALE, value_scale=value_scale,
+                        x.ctx_lens.cpu().numpy(), layer_type=layer_type, window=window, scale=SCALE,
+                        value_scale=value_scale,
                         sink=sink_array(s), kv_base=None if x.kv_base is None else x.kv_base.cpu().numpy())
 
 
@@ -42,6 +43,17 @@ def test_decode_context_sweep(layer_type):
     out, lse = gpu_decode(x, layer_type)
     ro, rl = oracle_decode(x, layer_type)
     compare(out, lse, ro, rl, f"decode layer {layer_type}")
+
+
+@pytest.mark.parametrize("window", [2, 33, 97, 225, 226, 300])
+def test_swa_decode_ring_sizes(window):
+    """Rings of window-1 slots: 1 slot, partial tiles, the two-tile limit (224
+    slots) and rings long enough that waves loop over several tiles."""
+    log(f"[case] SWA decode window={window}")
+    x = synth.decode_inputs([0, 1, window - 2, window - 1, window, 3 * window + 5, 1000], SWA, seed=29, window=window)
+    out, lse = gpu_decode(x, SWA, window=window)
+    ro, rl = oracle_decode(x, SWA, window=window)
+    compare(out, lse, ro, rl, f"SWA decode window {window}")
 
 
 @pytest.mark.parametrize("split", [32, 64, 96, 1000, 2048, 8192])
