@@ -70,6 +70,22 @@ def decode_stats(ctx, layer_type, window=W):
     return flops, bytes_
 
 
+def measured_traffic(record="profiles/prefill_ga_1x32768_traffic.json"):
+    """HBM bytes per GA-prefill launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    record (copy-calibrated), or None when the kernel sources changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, record)
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        h.update(open(os.path.join(ROOT, src), "rb").read())
+    if h.hexdigest() != rec["sources_sha256"]:
+        return None
+    return rec["read_bytes"] + rec["write_bytes"]
+
+
 def cpu_baseline(swa, ga, dga, ctx, budget_s):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload."""
     import oracle
@@ -266,7 +282,8 @@ def main():
     # Dominant kernel of the step: the GA prefill launch (MFMA-bound).
     roof = {"kernel": "prefill_kernel<GA>", "bound": "mfma", "achieved": tf(f_pga, avg["prefill_ga"]),
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": tf(f_pga, avg["prefill_ga"]) / PEAK_BF16_TFLOPS,
-            "traffic": None}
+            "traffic": measured_traffic(), "traffic_unit": "bytes per launch (HBM read + write)",
+            "algorithmic_bytes": b_pga}
     res = {
         "metric": METRIC,
         "value": value,
