@@ -1,0 +1,113 @@
+"""Hybrid attention stack driver: the 5 SWA : 1 GA layer pattern over a ragged batch.
+
+Sequences the C-ABI calls of a MiMo-V2-Flash attention stack (model doc
+"MiMo-V2-Flash": Key features, 5:1 SWA/GA with a 128-token window;
+MiMoV2FlashConfig, num_hidden_layers 48 and layer_types; MiMoV2FlashModel.forward,
+past_key_values): a varlen prefill of every layer followed by decode steps,
+each step attending and then appending one token per sequence per layer.
+
+There are no weights, so each layer's queries, keys and values come from a
+caller-supplied source (seeded synthetic tensors in tests and benchmarks) and
+layers are independent.  This module owns the per-layer KV caches (a 128-slot
+ring per SWA layer, a pooled region per GA layer) and the per-step context
+counters; all attention arithmetic runs in the HIP library.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Callable, List, Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import binding as B
+from . import synth
+
+SWA, GA = 0, 1
+
+
+@dataclass
+class LayerCache:
+    layer_type: int
+    k: torch.Tensor
+    v: torch.Tensor
+    kv_base: Optional[torch.Tensor] = None
+    kv_capacity: Optional[torch.Tensor] = None
+
+
+@dataclass
+class HybridStack:
+    lengths: Sequence[int]
+    num_layers: int = 48
+    period: int = 6
+    decode_steps: int = 64
+    device: str = "cuda"
+    window: int = synth.WINDOW
+    hq: int = synth.HQ
+    hkv: int = synth.HKV
+    layer_types: List[int] = field(init=False)
+    caches: List[LayerCache] = field(init=False)
+
+    def __post_init__(self):
+        self.lengths = [int(x) for x in self.lengths]
+        self.layer_types = synth.hybrid_layer_types(self.num_layers, self.period)
+        self.batch = len(self.lengths)
+        self.total = sum(self.lengths)
+        self.max_len = max(self.lengths)
+        self.dims = B.make_dims(num_q_heads=self.hq, num_kv_heads=self.hkv, sliding_window=self.window)
+        dev = self.device
+        self.cu = synth.cu_from_lengths(self.lengths, dev)
+        caps = [L + self.decode_steps for L in self.lengths]
+        base = np.concatenate([[0], np.cumsum(caps)[:-1]]).astype(np.int64)
+        self.pool_rows = int(sum(caps))
+        self.kv_base = torch.tensor(base, dtype=torch.int64, device=dev)
+        self.kv_capacity = torch.tensor(caps, dtype=torch.int64, device=dev)
+        R = self.window - 1
+        self.caches = []
+        for lt in self.layer_types:
+            if lt == SWA:
+                k = torch.zeros((self.batch, R, self.hkv, synth.DQK), dtype=torch.bfloat16, device=dev)
+                v = torch.zeros((self.batch, R, self.hkv, synth.DV), dtype=torch.bfloat16, device=dev)
+                self.caches.append(LayerCache(SWA, k, v))
+            else:
+                k = torch.zeros((self.pool_rows, self.hkv, synth.DQK), dtype=torch.bfloat16, device=dev)
+                v = torch.zeros((self.pool_rows, self.hkv, synth.DV), dtype=torch.bfloat16, device=dev)
+                self.caches.append(LayerCache(GA, k, v, self.kv_base, self.kv_capacity))
+        # Positions already cached once every layer has been prefilled: decode step 0
+        # attends at position L_b (prefill appends use zero_ctx).
+        self.ctx = torch.tensor(self.lengths, dtype=torch.int32, device=dev)
+        self.zero_ctx = torch.zeros(self.batch, dtype=torch.int32, device=dev)
+        self.cu_step = torch.arange(self.batch + 1, dtype=torch.int32, device=dev)
+        self.max_ctx = self.max_len + self.decode_steps
+        self.workspace = None
+        ws = B.mimo_attn_decode_workspace_size(self.dims, GA, self.batch, self.max_ctx, 0)
+        if ws:
+            self.workspace = torch.empty(ws // 4 + 4, dtype=torch.float32, device=dev)
+
+    def prefill_layer(self, layer: int, q, k, v, sink, out, lse=None, stream=None):
+        """Varlen prefill of one layer, then its KV append (cache positions 0..L-1)."""
+        lt = self.layer_types[layer]
+        c = self.caches[layer]
+        B.mimo_attn_prefill(self.dims, lt, q, k, v, self.cu, self.batch, self.max_len, sink, out, lse, stream)
+        B.mimo_kv_append(self.dims, lt, k, v, self.cu, self.zero_ctx, self.batch, self.total, c.k, c.v, c.kv_base,
+                         c.kv_capacity, stream)
+
+    def decode_layer(self, layer: int, q, k_new, v_new, sink, out, lse=None, stream=None):
+        """One decode step of one layer: attend over the cache + new token, then append it."""
+        lt = self.layer_types[layer]
+        c = self.caches[layer]
+        B.mimo_attn_decode(self.dims, lt, q, k_new, v_new, c.k, c.v, c.kv_base, self.ctx, self.batch, self.max_ctx,
+                           0, sink, out, lse, self.workspace if lt == GA else None, stream)
+        B.mimo_kv_append(self.dims, lt, k_new, v_new, self.cu_step, self.ctx, self.batch, self.batch, c.k, c.v,
+                         c.kv_base, c.kv_capacity, stream)
+
+    def advance(self):
+        """All layers of a decode step are done: every sequence is one token longer."""
+        self.ctx.add_(1)
+
+    def kv_bytes(self) -> dict:
+        """KV-cache bytes actually allocated, and what an all-GA stack would need."""
+        per_tok = self.hkv * (synth.DQK + synth.DV) * 2
+        ga_rows = sum(1 for t in self.layer_types if t == GA) * self.pool_rows
+        swa_rows = sum(1 for t in self.layer_types if t == SWA) * self.batch * (self.window - 1)
+        return {"hybrid": (ga_rows + swa_rows) * per_tok, "all_ga": self.num_layers * self.pool_rows * per_tok}
