@@ -394,7 +394,7 @@ __global__ __launch_bounds__(256) void ga_combine_kernel(const float* __restrict
     uint16_t* orow = out + ((size_t)b * hq + head) * kDv + e0;
     if (ns > nsplit) {  // the grid did not cover this context: refuse loudly
         *reinterpret_cast<u32x4*>(orow) = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
-        if (lse && e0 == 0) lse[(size_t)b * hq + head] = __builtin_nanf("");
+        if (lse && e0 == 0) reinterpret_cast<uint32_t*>(lse)[(size_t)b * hq + head] = 0x7fc00000u;  // quiet NaN bits
         return;
     }
     bool has;
