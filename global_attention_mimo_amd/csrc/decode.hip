@@ -41,18 +41,11 @@ constexpr int kGroup = 16;
 constexpr int kTile = 32;                         // keys per wave tile
 constexpr int kVTileBytes = kTile * kDv * 2;      // 8 KB: 32 rows of 256 B
 constexpr int kBlockLdsBytes = 4 * kVTileBytes;   // one V tile per wave
-constexpr uint32_t kRsrcWord3 = 0x00020000;       // raw 32-bit buffer, gfx9-family descriptor
 #ifndef MIMO_GA_DECODE_DEPTH
 #define MIMO_GA_DECODE_DEPTH 2
 #endif
 constexpr int kGaDepth = MIMO_GA_DECODE_DEPTH;    // GA split: tiles in flight beyond the current one
 constexpr int kSwaDepth = 1;                      // SWA: a wave owns at most a few tiles
-
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRsrcWord3);
-}
 
 // One 32-key tile of a wave: where its K and V rows come from.
 struct TileSrc {

@@ -92,4 +92,13 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, floa
 // operations in order).
 __device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
 
+// Raw buffer resource (gfx9-family descriptor) over `bytes` bytes at `base`:
+// the hardware range check turns loads at byte offsets past the record count
+// into zeros and drops such stores.
+constexpr uint32_t kRsrcWord3 = 0x00020000;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRsrcWord3);
+}
+
 }  // namespace mimo

@@ -59,7 +59,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * WV, 64 * WV),
 void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                     const uint16_t* __restrict__ v, const int32_t* __restrict__ cu_seqlens,
                     const float* __restrict__ sink, uint16_t* __restrict__ out, float* __restrict__ lse,
-                    int hq, int hkv, int window, float c_log2, float value_scale, int num_qblocks) {
+                    int hq, int hkv, int window, float c_log2, float value_scale, int num_qblocks,
+                    int max_seqlen) {
     using Cfg = PrefillCfg<WV, NB, NK>;
     constexpr int QT = Cfg::kTokens;
     // Two K/V buffers: tile t is computed from buffer t%2 while tile t+1 is staged into the other.
@@ -76,7 +77,7 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     // GA: heaviest (last) query blocks first so the causal tail does not straggle.
     const int qb = SWA ? (int)blockIdx.x : num_qblocks - 1 - (int)blockIdx.x;
     const int s0 = cu_seqlens[b];
-    const int L = cu_seqlens[b + 1] - s0;
+    const int L = min(cu_seqlens[b + 1] - s0, max_seqlen);  // tokens past max_seqlen stay unwritten
     const int q0 = qb * QT;
     if (q0 >= L) return;
 
@@ -304,6 +305,271 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
 }
 
+// ---------------------------------------------------------------------------
+// SWA prefill, streaming form (windows up to kStreamMaxWindow).  One
+// workgroup of 8 waves walks a strip of consecutive 16-token query blocks of
+// one (sequence, KV group); wave w owns tokens q0+2w and q0+2w+1 of the block
+// at q0 (x 16 heads = one 32-row MFMA block).  The block sees keys
+// q0-(W-1) .. q0+15, covered by five 32-key tiles starting at key q0-144.
+// K/V live in an LDS ring of 16-key slots: a block's tiles are ten
+// consecutive slots, the next block needs nine of them again, so each block
+// stages only the 16 keys the next one adds.  While a block is computed, the
+// next block's Q (registers) and its 16 new keys are in flight; one barrier
+// per block.  Against the tiled kernel above this removes the per-tile wait
+// on global loads and the re-staging of every K/V tile by all 17 query
+// blocks that see it.
+constexpr int kStreamTokens = 16;   // query tokens per block
+constexpr int kSlotKeys = 16;       // keys per ring slot
+constexpr int kStreamTiles = 5;     // 32-key tiles per block
+constexpr int kStreamLead = 144;    // a block's first tile starts at key q0 - kStreamLead
+constexpr int kStreamMaxWindow = kStreamLead + 1;
+constexpr int kRingSlots = 2 * kStreamTiles + 1;  // ten in use + the one being staged
+constexpr int kSlotKChunks = kSlotKeys * kDqk / 8;  // 16-byte chunks per slot: 384 of K
+constexpr int kSlotVChunks = kSlotKeys * kDv / 8;   // 256 of V
+constexpr int kStreamThreads = 512;
+static_assert(kSlotKChunks % 64 == 0 && kSlotKChunks + kSlotVChunks <= 2 * kStreamThreads &&
+                  kSlotKChunks + kSlotVChunks > kStreamThreads && kSlotKChunks < kStreamThreads,
+              "slot staging assumes chunk 1 of every thread is K (first 384) or V, chunk 2 is V");
+
+__device__ __forceinline__ int ring_slot(int h) { return (h + kRingSlots * 16) % kRingSlots; }  // h >= -176
+
+__global__ __attribute__((amdgpu_flat_work_group_size(kStreamThreads, kStreamThreads), amdgpu_waves_per_eu(2, 2)))
+void swa_stream_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                       const uint16_t* __restrict__ v, const int32_t* __restrict__ cu_seqlens,
+                       const float* __restrict__ sink, uint16_t* __restrict__ out, float* __restrict__ lse,
+                       int hq, int hkv, int window, float c_log2, float value_scale, int strip_blocks,
+                       int max_seqlen) {
+    __shared__ __attribute__((aligned(16))) uint16_t ring_k[kRingSlots * kSlotKeys * kKStride];
+    __shared__ __attribute__((aligned(16))) uint16_t ring_v[kRingSlots * kSlotKeys * kVStride];
+    // Threads without a second chunk of their own write it here, so that every
+    // load is consumed on every path (no load stays in flight across the loop).
+    __shared__ __attribute__((aligned(16))) uint16_t discard[(2 * kStreamThreads - kSlotKChunks - kSlotVChunks) * 8];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int r32 = lane & 31;
+    const int hh = lane >> 5;
+    const int b = blockIdx.z;
+    const int g = blockIdx.y;
+    const int s0 = cu_seqlens[b];
+    const int L = min(cu_seqlens[b + 1] - s0, max_seqlen);  // tokens past max_seqlen stay unwritten
+    const int blk_begin = blockIdx.x * strip_blocks;
+    const int blk_end = min(blk_begin + strip_blocks, (L + kStreamTokens - 1) / kStreamTokens);
+    if (blk_begin >= blk_end) return;
+    const int head = g * kGroup + (r32 & 15);
+    const int tok_in_blk = 2 * wave + (r32 >> 4);
+
+    // Staging of one 16-key slot: chunk A of this thread is K (threads < 384)
+    // or V, chunk B (threads < 128) is V; the split is wave-uniform.  Keys
+    // below 0 are staged as zeros, keys past the end repeat the last key
+    // (masked either way; they only need to be finite).
+    const size_t kstride = (size_t)hkv * kDqk, vstride = (size_t)hkv * kDv;
+    const uint16_t* ga_src;
+    size_t ga_stride;
+    int ga_row;
+    uint16_t* la_dst;
+    int la_slot;
+    if (tid < kSlotKChunks) {
+        ga_row = tid / (kDqk / 8);
+        ga_src = k + ((size_t)s0 * hkv + g) * kDqk + (tid % (kDqk / 8)) * 8;
+        ga_stride = kstride;
+        la_dst = ring_k + ga_row * kKStride + (tid % (kDqk / 8)) * 8;
+        la_slot = kSlotKeys * kKStride;
+    } else {
+        const int c = tid - kSlotKChunks;
+        ga_row = c / (kDv / 8);
+        ga_src = v + ((size_t)s0 * hkv + g) * kDv + (c % (kDv / 8)) * 8;
+        ga_stride = vstride;
+        la_dst = ring_v + ga_row * kVStride + (c % (kDv / 8)) * 8;
+        la_slot = kSlotKeys * kVStride;
+    }
+    constexpr int kNumB = kSlotKChunks + kSlotVChunks - kStreamThreads;  // threads with a chunk B: 128
+    const bool has_b = tid < kNumB;
+    const int cb = (kStreamThreads - kSlotKChunks) + (tid % kNumB);  // others re-load a valid V chunk
+    const int gb_row = cb / (kDv / 8);
+    const uint16_t* gb_src = v + ((size_t)s0 * hkv + g) * kDv + (cb % (kDv / 8)) * 8;
+    uint16_t* lb_dst = has_b ? ring_v + gb_row * kVStride + (cb % (kDv / 8)) * 8 : discard + (tid - kNumB) * 8;
+    const int lb_slot = has_b ? kSlotKeys * kVStride : 0;
+
+    // Keys below 0 are zeroed at the LDS write, where the loaded value is
+    // waited for anyway.
+    auto load_slot = [&](int h, u32x4& ra, u32x4& rb) {
+        ra = *reinterpret_cast<const u32x4*>(ga_src + (size_t)min(max(h * kSlotKeys + ga_row, 0), L - 1) * ga_stride);
+        rb = *reinterpret_cast<const u32x4*>(gb_src + (size_t)min(max(h * kSlotKeys + gb_row, 0), L - 1) * vstride);
+    };
+    auto store_slot = [&](int h, const u32x4& ra, const u32x4& rb) {
+        const int sl = ring_slot(h);
+        const u32x4 zero = {0, 0, 0, 0};
+        *reinterpret_cast<u32x4*>(la_dst + sl * la_slot) = h * kSlotKeys + ga_row < 0 ? zero : ra;
+        *reinterpret_cast<u32x4*>(lb_dst + sl * lb_slot) = h * kSlotKeys + gb_row < 0 ? zero : rb;
+    };
+    // Q^T fragments of one block (MFMA B operand); rows past the end repeat the last token.
+    auto load_q = [&](int blk, bf16x8 (&qv)[kDqk / 16]) {
+        const int t = min(blk * kStreamTokens + tok_in_blk, L - 1);
+        const u32x4* src = reinterpret_cast<const u32x4*>(q + ((size_t)(s0 + t) * hq + head) * kDqk);
+#pragma unroll
+        for (int s = 0; s < kDqk / 16; ++s) qv[s] = __builtin_bit_cast(bf16x8, src[2 * s + hh]);
+    };
+
+    // Outputs of the block at q0 through buffer descriptors that cover only
+    // its first `rows` rows: stores of rows past the sequence end are dropped
+    // by the hardware range check, so every lane takes the same path.
+    auto store_outputs = [&](int q0, int rows, const f32x16 (&oacc)[kDv / 32], float inv, float lse_v) {
+        const rsrc_t orsrc = make_rsrc(out + (size_t)(s0 + q0) * hq * kDv, (uint32_t)(rows * hq * kDv * 2));
+        const rsrc_t lrsrc =
+            lse ? make_rsrc(lse + (size_t)(s0 + q0) * hq, (uint32_t)(rows * hq * 4)) : make_rsrc(lse, 0u);
+        const int orow = (tok_in_blk * hq + head) * kDv * 2 + 8 * hh;  // byte offset in the block
+#pragma unroll
+        for (int db = 0; db < kDv / 32; ++db) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const f32x16& ov = oacc[db];
+                const u32x2 w = {pack_bf16x2(ov[4 * jj + 0] * inv, ov[4 * jj + 1] * inv),
+                                 pack_bf16x2(ov[4 * jj + 2] * inv, ov[4 * jj + 3] * inv)};
+                __builtin_amdgcn_raw_buffer_store_b64(w, orsrc, orow + (db * 32 + 8 * jj) * 2, 0, 0);
+            }
+        }
+        // One LSE per row: the upper half-wave's copy is sent out of range.
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lse_v), lrsrc,
+                                              hh ? (int)0x7ffffff0 : (tok_in_blk * hq + head) * 4, 0, 0);
+    };
+
+    float sink_l2 = kNoMax;
+    bool has_sink = false;
+    if (sink) {
+        const float sv = sink[head] * kLog2e;
+        if (sv > -__builtin_inff()) { sink_l2 = sv; has_sink = true; }
+    }
+
+    // Prologue: the first block's Q and its ten slots, then the second
+    // block's Q and new slot in flight.
+    bf16x8 qf[kDqk / 16], qn[kDqk / 16];
+    u32x4 na, nb;
+    load_q(blk_begin, qf);
+    {
+        const int h0 = blk_begin * (kStreamTokens / kSlotKeys) - 2 * kStreamTiles + 1;
+        u32x4 pa[2 * kStreamTiles], pb[2 * kStreamTiles];
+#pragma unroll
+        for (int i = 0; i < 2 * kStreamTiles; ++i) load_slot(h0 + i, pa[i], pb[i]);
+        load_q(min(blk_begin + 1, blk_end - 1), qn);
+        load_slot(h0 + 2 * kStreamTiles, na, nb);
+        // The loop waits for these loads with the previous block's output
+        // stores issued after them; the same stores, with no rows to write,
+        // keep that count equal on entry (the compiler's wait counts are
+        // conservative where paths differ).
+        {
+            f32x16 none[kDv / 32];
+#pragma unroll
+            for (int db = 0; db < kDv / 32; ++db) none[db] = f32x16{};
+            store_outputs(blk_begin * kStreamTokens, 0, none, 0.0f, 0.0f);
+        }
+#pragma unroll
+        for (int i = 0; i < 2 * kStreamTiles; ++i) store_slot(h0 + i, pa[i], pb[i]);
+    }
+    __syncthreads();
+
+    const int vsrc_off = (4 * hh + ((lane & 15) >> 2)) * kVStride + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const int ksrc_off = (r32 & 15) * kKStride + 8 * hh;
+
+    for (int blk = blk_begin; blk < blk_end; ++blk) {
+        const int q0 = blk * kStreamTokens;
+        const int hq0 = q0 / kSlotKeys;  // slot index of the block's own keys
+        const int tok = q0 + tok_in_blk;
+        float m_run = has_sink ? sink_l2 : kNoMax;
+        float l_run = (has_sink && hh == 0) ? 1.0f : 0.0f;
+        f32x16 oacc[kDv / 32];
+#pragma unroll
+        for (int db = 0; db < kDv / 32; ++db) oacc[db] = f32x16{};
+
+#pragma unroll
+        for (int j = 0; j < kStreamTiles; ++j) {
+            const int kbase = q0 - kStreamLead + 32 * j;
+            // Tiles wholly before key 0 or before the band of the block's first token.
+            if (kbase + 31 < 0 || kbase + 31 < q0 - (window - 1)) continue;
+            const int h = hq0 - 2 * kStreamTiles + 1 + 2 * j;
+            const uint16_t* klo = ring_k + ring_slot(h) * (kSlotKeys * kKStride);
+            const uint16_t* khi = ring_k + ring_slot(h + 1) * (kSlotKeys * kKStride);
+            const uint16_t* krow = (r32 < 16 ? klo : khi) + ksrc_off;
+            f32x16 sacc = f32x16{};
+#pragma unroll
+            for (int s = 0; s < kDqk / 16; ++s)
+                sacc = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(krow + 16 * s), qf[s], sacc);
+
+            // Mask unless every key of the tile is in every token's band: key
+            // offset 8*(r/4) + (r%4) + 4*hh is kept when max(0, tok-(W-1)) <= key <= tok.
+            const bool interior = kbase >= 0 && kbase + 31 <= q0 && kbase >= q0 + kStreamTokens - 1 - (window - 1);
+            if (!interior) {
+                const int hi_off = tok - kbase - 4 * hh;
+                const int lo_off = max(hi_off - (window - 1), -kbase - 4 * hh);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int off = 8 * (r >> 2) + (r & 3);
+                    const bool ok = off <= hi_off && off >= lo_off;
+                    sacc[r] = ok ? sacc[r] : -__builtin_inff();
+                }
+            }
+            float mx = -__builtin_inff();
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[r], sacc[r + 1]));
+            mx = max_with_partner_half(mx);
+            const float m_cand = fmaxf(m_run, mx * c_log2);
+            if (__builtin_amdgcn_ballot_w64(m_cand > m_run + kRescaleThreshold)) {
+                const float alpha = fast_exp2(m_run - m_cand);
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < kDv / 32; ++db) oacc[db] *= alpha;
+                m_run = m_cand;
+            }
+            const float neg_m = -m_run;
+            float rs = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = fast_exp2(__builtin_fmaf(sacc[r], c_log2, neg_m));
+                sacc[r] = p;
+                rs += p;
+            }
+            l_run += rs;
+            const bf16x8 p0 = pack_bf16x8(sacc[0], sacc[1], sacc[2], sacc[3], sacc[4], sacc[5], sacc[6], sacc[7]);
+            const bf16x8 p1 =
+                pack_bf16x8(sacc[8], sacc[9], sacc[10], sacc[11], sacc[12], sacc[13], sacc[14], sacc[15]);
+            const uint16_t* vlo = ring_v + ring_slot(h) * (kSlotKeys * kVStride) + vsrc_off;
+            const uint16_t* vhi = ring_v + ring_slot(h + 1) * (kSlotKeys * kVStride) + vsrc_off;
+#pragma unroll
+            for (int db = 0; db < kDv / 32; ++db) {
+                const bf16x8 a0 = join_tr(lds_read_tr16(vlo + db * 32), lds_read_tr16(vlo + db * 32 + 8 * kVStride));
+                oacc[db] = mfma_32x32x16(a0, p0, oacc[db]);
+                const bf16x8 a1 = join_tr(lds_read_tr16(vhi + db * 32), lds_read_tr16(vhi + db * 32 + 8 * kVStride));
+                oacc[db] = mfma_32x32x16(a1, p1, oacc[db]);
+            }
+        }
+
+        // Hand-over, ordered so that a block's loads never queue behind the
+        // stores of the block before it:
+        //  1. the next block's slot and Q (loaded one block ago) go to LDS and
+        //     qf; the slot replaces key block hq0+1-11, which no block from
+        //     here on reads;
+        //  2. the loads for the block after next are issued;
+        //  3. only then this block's outputs are stored.
+        store_slot(hq0 + 1, na, nb);
+#pragma unroll
+        for (int s = 0; s < kDqk / 16; ++s) {
+            qf[s] = qn[s];
+            // Materialise the copy here (an empty asm that claims to modify the
+            // register) so that it, and the wait for the Q loads, cannot be
+            // deferred past the loads and stores below.
+            asm volatile("" : "+v"(qf[s]));
+        }
+        load_q(min(blk + 2, blk_end - 1), qn);
+        load_slot(hq0 + 2, na, nb);
+
+        const float l_tot = sum_with_partner_half(l_run);
+        const int rows = min(kStreamTokens, L - q0);
+        store_outputs(q0, rows, oacc, value_scale / l_tot, (m_run + __log2f(l_tot)) * kLn2);
+        __syncthreads();
+    }
+}
+
 template <int WV, int NB, int NK, bool SWA, int WPE>
 hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
     using Cfg = PrefillCfg<WV, NB, NK>;
@@ -311,7 +577,7 @@ hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
     dim3 grid(nqb, a.hkv, a.num_seqs);
     hipLaunchKernelGGL((prefill_kernel<WV, NB, NK, SWA, WPE>), grid, dim3(Cfg::kThreads), 0, stream, a.q, a.k, a.v,
                        a.cu_seqlens, a.sink, a.out, a.lse, a.hq, a.hkv, a.window, a.softmax_scale * kLog2e,
-                       a.value_scale, nqb);
+                       a.value_scale, nqb, a.max_seqlen);
     return hipGetLastError();
 }
 
@@ -329,10 +595,39 @@ hipError_t launch_ga(const PrefillArgs& a, hipStream_t s) { return launch<WV, NB
 template <int WV, int NB, int NK, int WPE>
 hipError_t launch_swa(const PrefillArgs& a, hipStream_t s) { return launch<WV, NB, NK, true, WPE>(a, s); }
 
+// Streaming SWA grid: strips per compute unit it aims for (one workgroup fits
+// a CU), and the longest strip.  The cap keeps ragged batches balanced: the
+// host sizes strips from max_seqlen, not from the actual lengths.
+#ifndef MIMO_STREAM_ROUNDS
+#define MIMO_STREAM_ROUNDS 1
+#endif
+#ifndef MIMO_STREAM_MAX_STRIP
+#define MIMO_STREAM_MAX_STRIP 32
+#endif
+
+hipError_t launch_swa_stream(const PrefillArgs& a, hipStream_t stream) {
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    // Strip length: spread the (upper bound of the) query blocks over the CUs.
+    const long long per_seq = (a.max_seqlen + kStreamTokens - 1) / kStreamTokens;
+    const long long total = per_seq * a.hkv * a.num_seqs;
+    const long long target = (long long)max(cus, 1) * MIMO_STREAM_ROUNDS;
+    const int strip = (int)max(1LL, min(min(per_seq, (long long)MIMO_STREAM_MAX_STRIP), (total + target - 1) / target));
+    dim3 grid((unsigned)((per_seq + strip - 1) / strip), a.hkv, a.num_seqs);
+    hipLaunchKernelGGL(swa_stream_kernel, grid, dim3(kStreamThreads), 0, stream, a.q, a.k, a.v, a.cu_seqlens, a.sink,
+                       a.out, a.lse, a.hq, a.hkv, a.window, a.softmax_scale * kLog2e, a.value_scale, strip,
+                       a.max_seqlen);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     if (a.max_seqlen <= 0) return hipSuccess;
+    if (a.swa && a.window <= kStreamMaxWindow) return launch_swa_stream(a, stream);
     if (a.swa) return launch_swa<MIMO_SWA_CFG>(a, stream);
     return launch_ga<MIMO_GA_CFG>(a, stream);
 }

@@ -36,6 +36,12 @@ def test_ragged_edge_lengths(layer_type):
     check(synth.prefill_inputs(lengths, seed=2), layer_type, "ragged edges")
 
 
+def test_swa_strips_across_ragged_sequences():
+    """SWA prefill over sequences long enough for several query strips each, with
+    strip ends falling inside sequences and sequences shorter than one block."""
+    check(synth.prefill_inputs([1500, 513, 16, 700, 33, 1], seed=12), SWA, "swa strips")
+
+
 @pytest.mark.parametrize("layer_type", [SWA, GA])
 @pytest.mark.parametrize("sink", [None, -math.inf, -5.0, 0.0, 5.0, 30.0])
 def test_sink_values(layer_type, sink):
@@ -51,7 +57,7 @@ def test_sharp_softmax(layer_type):
     check(x, layer_type, "q x4")
 
 
-@pytest.mark.parametrize("window", [1, 2, 17, 64, 300])
+@pytest.mark.parametrize("window", [1, 2, 17, 64, 129, 145, 146, 300])
 def test_windows(window):
     check(synth.prefill_inputs([260, 45], seed=5), SWA, f"window {window}", window=window)
 
@@ -113,15 +119,18 @@ def test_poison_and_guard(layer_type):
     compare(out_buf[:T], lse_buf[:T], ref_o, ref_l, "poisoned buffers")
 
 
-def test_max_seqlen_bounds_the_grid():
-    """Tokens of a sequence longer than max_seqlen are left unwritten (documented)."""
+@pytest.mark.parametrize("layer_type", [SWA, GA])
+@pytest.mark.parametrize("max_seqlen", [48, 45])
+def test_max_seqlen_bounds_the_grid(layer_type, max_seqlen):
+    """Tokens of a sequence beyond max_seqlen are left unwritten (documented)."""
+    log(f"[case] prefill max_seqlen {max_seqlen} layer={layer_type}")
     x = synth.prefill_inputs([64, 40], seed=11)
     out = torch.zeros((104, 64, 128), dtype=torch.bfloat16, device="cuda")
-    B.mimo_attn_prefill(B.make_dims(), GA, to_dev(x.q), to_dev(x.k), to_dev(x.v), to_dev(x.cu_seqlens), 2, 48,
-                        to_dev(x.sink), out, None)
+    B.mimo_attn_prefill(B.make_dims(), layer_type, to_dev(x.q), to_dev(x.k), to_dev(x.v), to_dev(x.cu_seqlens), 2,
+                        max_seqlen, to_dev(x.sink), out, None)
     torch.cuda.synchronize()
-    ref_o, _ = oracle_prefill(x, GA)
+    ref_o, _ = oracle_prefill(x, layer_type)
     got = out.float().cpu().numpy()
-    assert np.abs(got[:48] - ref_o[:48]).max() <= 2e-2
-    assert not got[48:64].any()
+    assert np.abs(got[:max_seqlen] - ref_o[:max_seqlen]).max() <= 2e-2
+    assert not got[max_seqlen:64].any()
     assert np.abs(got[64:] - ref_o[64:]).max() <= 2e-2
