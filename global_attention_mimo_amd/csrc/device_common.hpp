@@ -101,4 +101,23 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRsrcWord3);
 }
 
+// Scheduling hint for a straight-line run of MFMAs fed from LDS: issue
+// `ahead` LDS reads first, then alternate one MFMA with `per` reads, so that
+// each MFMA's operands were requested several MFMAs earlier instead of right
+// before it.  Only orders instructions already in the block; no code.
+template <int kMfmas, int kReads, int kAhead, int kPer>
+__device__ __forceinline__ void interleave_lds_mfma() {
+#ifndef MIMO_NO_INTERLEAVE
+    static_assert(kAhead + (kMfmas - 1) * kPer >= kReads, "reads must all be placed");
+    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+    for (int i = 0; i < kMfmas; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+            if (kAhead + i * kPer + j < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#endif
+}
+
 }  // namespace mimo

@@ -48,6 +48,20 @@ struct PrefillCfg {
     static_assert(NK % 32 == 0, "key tile must be a multiple of 32");
 };
 
+// LDS reads issued ahead of the first MFMA of the QK^T and PV runs.
+#ifndef MIMO_S_AHEAD
+#define MIMO_S_AHEAD 4
+#endif
+#ifndef MIMO_PV_AHEAD
+#define MIMO_PV_AHEAD 4
+#endif
+#ifndef MIMO_STREAM_S_AHEAD
+#define MIMO_STREAM_S_AHEAD 4
+#endif
+#ifndef MIMO_STREAM_PV_AHEAD
+#define MIMO_STREAM_PV_AHEAD 4
+#endif
+
 // The running max is only raised when a row's new maximum exceeds it by more
 // than this many powers of two; until then exp2(s - m) <= 2^8 stays exact
 // enough in fp32 and bf16 and the O/l rescale is skipped.
@@ -215,6 +229,7 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                 for (int nb = 0; nb < NB; ++nb) sacc[kb][nb] = mfma_32x32x16(a, qf[nb][s], sacc[kb][nb]);
             }
         }
+        interleave_lds_mfma<(NK / 32) * (kDqk / 16) * NB, (NK / 32) * (kDqk / 16), MIMO_S_AHEAD, 1>();
         // ---- mask, online softmax, P^T -> bf16, O^T += V^T * P^T -----------------
         const bool interior = (kbase + NK - 1 <= q0) && (!SWA || kbase >= q_last - (window - 1));
 #pragma unroll
@@ -278,6 +293,7 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     oacc[db][nb] = mfma_32x32x16(a, pf[ks], oacc[db][nb]);
                 }
             }
+            interleave_lds_mfma<(kDv / 32) * (NK / 16), 2 * (kDv / 32) * (NK / 16), MIMO_PV_AHEAD, 2>();
         }
         if (more) store_tile(buf ^ 1);
         __syncthreads();
@@ -495,6 +511,7 @@ void swa_stream_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
 #pragma unroll
             for (int s = 0; s < kDqk / 16; ++s)
                 sacc = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(krow + 16 * s), qf[s], sacc);
+            interleave_lds_mfma<kDqk / 16, kDqk / 16, MIMO_STREAM_S_AHEAD, 1>();
 
             // Mask unless every key of the tile is in every token's band: key
             // offset 8*(r/4) + (r%4) + 4*hh is kept when max(0, tok-(W-1)) <= key <= tok.
@@ -542,6 +559,7 @@ void swa_stream_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
                 const bf16x8 a1 = join_tr(lds_read_tr16(vhi + db * 32), lds_read_tr16(vhi + db * 32 + 8 * kVStride));
                 oacc[db] = mfma_32x32x16(a1, p1, oacc[db]);
             }
+            interleave_lds_mfma<2 * (kDv / 32), 4 * (kDv / 32), MIMO_STREAM_PV_AHEAD, 2>();
         }
 
         // Hand-over, ordered so that a block's loads never queue behind the
