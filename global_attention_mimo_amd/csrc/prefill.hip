@@ -5,7 +5,10 @@
 // MiMoV2FlashConfig (64 query heads over 4 KV heads, head_dim 192 for q/k,
 // v_head_dim 128, sliding_window 129 = keys p-128..p, attention_value_scale).
 //
-// Work decomposition (one workgroup = 4 waves):
+// Two kernels: the tiled kernel below serves GA and SWA windows wider than
+// 145 keys; swa_stream_kernel (further down) serves SWA up to 145 keys.
+//
+// Tiled kernel, work decomposition (one workgroup = WV waves):
 //   * a workgroup owns one (sequence, KV group g, block of QT query tokens);
 //     its rows are the QT tokens x the 16 query heads of group g, so the 16
 //     heads that share K/V head g form the MFMA N dimension together (GQA
