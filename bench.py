@@ -70,18 +70,31 @@ def decode_stats(ctx, layer_type, window=W):
     return flops, bytes_
 
 
+def code_digest(paths):
+    """sha256 over the given sources with comments and whitespace removed, so that a
+    record stays valid across comment edits but not across any change to the code."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for src in paths:
+        text = open(os.path.join(ROOT, src), encoding="utf-8").read()
+        if src.endswith(".py"):
+            text = re.sub(r"#[^\n]*", "", text)
+        else:
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", "", text)
+        h.update(re.sub(r"\s+", "", text).encode())
+    return h.hexdigest()
+
+
 def measured_traffic(record="profiles/prefill_ga_1x32768_traffic.json"):
     """HBM bytes per GA-prefill launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    record (copy-calibrated), or None when the kernel sources changed since it was taken."""
-    import hashlib
+    record (copy-calibrated), or None when the kernel code changed since it was taken."""
     path = os.path.join(ROOT, record)
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    h = hashlib.sha256()
-    for src in rec["sources"]:
-        h.update(open(os.path.join(ROOT, src), "rb").read())
-    if h.hexdigest() != rec["sources_sha256"]:
+    if code_digest(rec["sources"]) != rec.get("code_sha256"):
         return None
     return rec["read_bytes"] + rec["write_bytes"]
 
