@@ -32,8 +32,19 @@ namespace {
 constexpr int kDqk = 192;
 constexpr int kDv = 128;
 constexpr int kGroup = 16;         // query heads per KV head
-constexpr int kKStride = kDqk + 8;  // LDS row stride of K tiles (bf16): 400 B, conflict-free b128 reads
-constexpr int kVStride = kDv + 16;  // LDS row stride of V tiles (bf16): 288 B, conflict-free tr reads
+// LDS row strides (bf16 elements).  K: 400 B, so the 16 rows one
+// ds_read_b128 cycle serves start 100 dwords apart and cover all 64 banks
+// once.  V: 320 B (80 dwords, 16 mod 64), so the four rows x 2 column groups
+// that 32 lanes of a ds_read_b64_tr_b16 address land in disjoint bank ranges
+// (a 288-byte stride leaves 2-way conflicts on 24 of 32 lanes).
+#ifndef MIMO_KSTRIDE_PAD
+#define MIMO_KSTRIDE_PAD 8
+#endif
+#ifndef MIMO_VSTRIDE_PAD
+#define MIMO_VSTRIDE_PAD 32
+#endif
+constexpr int kKStride = kDqk + MIMO_KSTRIDE_PAD;
+constexpr int kVStride = kDv + MIMO_VSTRIDE_PAD;
 
 // Tile shape of one workgroup: WV waves, each owning NB blocks of 32 query
 // rows (2 tokens x 16 heads), and NK keys per K/V tile.
@@ -65,10 +76,16 @@ struct PrefillCfg {
 #define MIMO_STREAM_PV_AHEAD 4
 #endif
 
-// The running max is only raised when a row's new maximum exceeds it by more
-// than this many powers of two; until then exp2(s - m) <= 2^8 stays exact
-// enough in fp32 and bf16 and the O/l rescale is skipped.
-constexpr float kRescaleThreshold = 8.0f;
+// The running max is only raised (and O, l rescaled) when a row's new maximum
+// exceeds it by more than this many powers of two, so most tiles skip the
+// rescale.  Kept small on purpose: a key that dominates its row by more than
+// the threshold then gets p = exp2(0) = 1, exact in bf16, so rounding P to
+// bf16 barely moves the output of a sharp softmax (with 2^8 the dominant p
+// could be any value up to 256 and carry a 2^-9 relative error into O).
+#ifndef MIMO_RESCALE_THRESHOLD
+#define MIMO_RESCALE_THRESHOLD 2.0f
+#endif
+constexpr float kRescaleThreshold = MIMO_RESCALE_THRESHOLD;
 
 template <int WV, int NB, int NK, bool SWA, int WAVES_PER_EU>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WV, 64 * WV),
@@ -218,6 +235,8 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         const uint16_t* vtile = lds_v + buf * Cfg::kLdsV;
         const int kbase = kt * NK;
 
+        const bool interior = (kbase + NK - 1 <= q0) && (!SWA || kbase >= q_last - (window - 1));
+
         // ---- S^T = K * Q^T ---------------------------------------------------
         f32x16 sacc[NK / 32][NB];
 #pragma unroll
@@ -234,7 +253,6 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         }
         interleave_lds_mfma<(NK / 32) * (kDqk / 16) * NB, (NK / 32) * (kDqk / 16), MIMO_S_AHEAD, 1>();
         // ---- mask, online softmax, P^T -> bf16, O^T += V^T * P^T -----------------
-        const bool interior = (kbase + NK - 1 <= q0) && (!SWA || kbase >= q_last - (window - 1));
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             // Band/causal mask, only on tiles that cross a boundary: key kk of the
@@ -270,15 +288,12 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             const float neg_m = -m_run[nb];
             float rs = 0.0f;
 #pragma unroll
-            for (int kb = 0; kb < NK / 32; ++kb) {
+            for (int kb = 0; kb < NK / 32; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float p = fast_exp2(__builtin_fmaf(sacc[kb][nb][r], c_log2, neg_m));
-                    sacc[kb][nb][r] = p;
-                    rs += p;
+                    sacc[kb][nb][r] = fast_exp2(__builtin_fmaf(sacc[kb][nb][r], c_log2, neg_m));
+                    rs += sacc[kb][nb][r];
                 }
-            }
-            l_run[nb] += rs;
             bf16x8 pf[NK / 16];
 #pragma unroll
             for (int ks = 0; ks < NK / 16; ++ks) {
@@ -287,6 +302,7 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                 pf[ks] = pack_bf16x8(sv[o + 0], sv[o + 1], sv[o + 2], sv[o + 3], sv[o + 4], sv[o + 5], sv[o + 6],
                                      sv[o + 7]);
             }
+            l_run[nb] += rs;
 #pragma unroll
             for (int db = 0; db < kDv / 32; ++db) {
 #pragma unroll
@@ -461,8 +477,7 @@ void swa_stream_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
         if (sv > -__builtin_inff()) { sink_l2 = sv; has_sink = true; }
     }
 
-    // Prologue: the first block's Q and its ten slots, then the second
-    // block's Q and new slot in flight.
+    // Prologue: the first block's Q and its ten slots.
     bf16x8 qf[kDqk / 16], qn[kDqk / 16];
     u32x4 na, nb;
     load_q(blk_begin, qf);
@@ -471,18 +486,6 @@ void swa_stream_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
         u32x4 pa[2 * kStreamTiles], pb[2 * kStreamTiles];
 #pragma unroll
         for (int i = 0; i < 2 * kStreamTiles; ++i) load_slot(h0 + i, pa[i], pb[i]);
-        load_q(min(blk_begin + 1, blk_end - 1), qn);
-        load_slot(h0 + 2 * kStreamTiles, na, nb);
-        // The loop waits for these loads with the previous block's output
-        // stores issued after them; the same stores, with no rows to write,
-        // keep that count equal on entry (the compiler's wait counts are
-        // conservative where paths differ).
-        {
-            f32x16 none[kDv / 32];
-#pragma unroll
-            for (int db = 0; db < kDv / 32; ++db) none[db] = f32x16{};
-            store_outputs(blk_begin * kStreamTokens, 0, none, 0.0f, 0.0f);
-        }
 #pragma unroll
         for (int i = 0; i < 2 * kStreamTiles; ++i) store_slot(h0 + i, pa[i], pb[i]);
     }
@@ -494,6 +497,9 @@ void swa_stream_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
     for (int blk = blk_begin; blk < blk_end; ++blk) {
         const int q0 = blk * kStreamTokens;
         const int hq0 = q0 / kSlotKeys;  // slot index of the block's own keys
+        // In flight while this block computes: the next block's Q and new slot.
+        load_q(min(blk + 1, blk_end - 1), qn);
+        load_slot(hq0 + 1, na, nb);
         const int tok = q0 + tok_in_blk;
         float m_run = has_sink ? sink_l2 : kNoMax;
         float l_run = (has_sink && hh == 0) ? 1.0f : 0.0f;
@@ -545,14 +551,13 @@ void swa_stream_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
             float rs = 0.0f;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float p = fast_exp2(__builtin_fmaf(sacc[r], c_log2, neg_m));
-                sacc[r] = p;
-                rs += p;
+                sacc[r] = fast_exp2(__builtin_fmaf(sacc[r], c_log2, neg_m));
+                rs += sacc[r];
             }
-            l_run += rs;
             const bf16x8 p0 = pack_bf16x8(sacc[0], sacc[1], sacc[2], sacc[3], sacc[4], sacc[5], sacc[6], sacc[7]);
             const bf16x8 p1 =
                 pack_bf16x8(sacc[8], sacc[9], sacc[10], sacc[11], sacc[12], sacc[13], sacc[14], sacc[15]);
+            l_run += rs;
             const uint16_t* vlo = ring_v + ring_slot(h) * (kSlotKeys * kVStride) + vsrc_off;
             const uint16_t* vhi = ring_v + ring_slot(h + 1) * (kSlotKeys * kVStride) + vsrc_off;
 #pragma unroll
@@ -565,24 +570,19 @@ void swa_stream_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
             interleave_lds_mfma<2 * (kDv / 32), 4 * (kDv / 32), MIMO_STREAM_PV_AHEAD, 2>();
         }
 
-        // Hand-over, ordered so that a block's loads never queue behind the
-        // stores of the block before it:
-        //  1. the next block's slot and Q (loaded one block ago) go to LDS and
-        //     qf; the slot replaces key block hq0+1-11, which no block from
-        //     here on reads;
-        //  2. the loads for the block after next are issued;
-        //  3. only then this block's outputs are stored.
+        // Hand-over before this block's output stores (so that waiting for the
+        // loads does not also wait for the stores): the next block's slot goes
+        // to LDS, replacing key block hq0+1-11, which no block from here on
+        // reads, and its Q to qf.
         store_slot(hq0 + 1, na, nb);
 #pragma unroll
         for (int s = 0; s < kDqk / 16; ++s) {
             qf[s] = qn[s];
             // Materialise the copy here (an empty asm that claims to modify the
             // register) so that it, and the wait for the Q loads, cannot be
-            // deferred past the loads and stores below.
+            // deferred past the stores below.
             asm volatile("" : "+v"(qf[s]));
         }
-        load_q(min(blk + 2, blk_end - 1), qn);
-        load_slot(hq0 + 2, na, nb);
 
         const float l_tot = sum_with_partner_half(l_run);
         const int rows = min(kStreamTokens, L - q0);
