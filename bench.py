@@ -99,6 +99,32 @@ def measured_traffic(record="profiles/prefill_ga_1x32768_traffic.json"):
     return rec["read_bytes"] + rec["write_bytes"]
 
 
+def device_context():
+    """The box's own figures next to the spec-sheet peaks: CU count and a measured
+    device-to-device copy rate (read + write bytes per second, 2 GiB buffers)."""
+    props = torch.cuda.get_device_properties(0)
+    n = 2 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"name": props.name, "compute_units": props.multi_processor_count,
+            "copy_GBps": 2 * n / (ms * 1e-3) / 1e9,
+            "note": "copy_GBps: torch device-to-device copy of 2 GiB, read + write bytes; peaks used are the spec "
+                    "sheet's (2500 TFLOP/s bf16 dense, 8000 GB/s HBM)"}
+
+
 def cpu_baseline(swa, ga, dga, ctx, budget_s):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload."""
     import oracle
@@ -235,6 +261,7 @@ def main():
         ctx_swa.add_(1)
         mark(7)
 
+    dev_ctx = device_context()
     for i in range(args.warmup):
         step()
         torch.cuda.synchronize()
@@ -318,6 +345,7 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "breakdown": breakdown,
         "roofline": roof,
+        "device": dev_ctx,
     }
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample (cpu_baseline)")
