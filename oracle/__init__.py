@@ -62,6 +62,9 @@ class Oracle:
         lib.oracle_decode.restype = _I
         lib.oracle_decode.argtypes = [_I, _I, _I, _I, _I, _I, _F, _F, _P, _P, _P, _P, _P, _I,
                                       _P, _P, _I, _P, _P, _P, _I]
+        lib.oracle_prefill_chunk.restype = _I
+        lib.oracle_prefill_chunk.argtypes = [_I, _I, _I, _I, _I, _I, _F, _F, _P, _P, _P, _P, _I, _P, _P, _I,
+                                             _P, _P, _P, _P, _P, _I]
         lib.oracle_kv_append.restype = _I
         lib.oracle_kv_append.argtypes = [_I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P]
         lib.oracle_default_threads.restype = _I
@@ -146,6 +149,38 @@ class Oracle:
                                     self._ptr(sk), self._ptr(out), self._ptr(lse), nth)
         if rc != OK:
             raise ValueError(f"oracle_decode rejected its arguments (status {rc})")
+        return out, lse
+
+    def prefill_chunk(self, q, k, v, cu_newlens, k_cache, v_cache, ctx_lens, *, layer_type: int,
+                      window: int = 129, scale: float, value_scale: float = 1.0, sink=None, kv_base=None,
+                      nthreads: int = 0):
+        """Chunked prefill: new tokens (packed by cu_newlens) at positions ctx_lens[b] + i attend
+        to the cached positions (SWA ring [B][W-1][Hkv][D] / GA pool at kv_base[b] + j) and to
+        the chunk's own earlier tokens.  Returns (out [Tn][Hq][Dv], lse [Tn][Hq])."""
+        q = np.ascontiguousarray(q)
+        hq, dqk = q.shape[1], q.shape[2]
+        hkv, dv = k.shape[1], v.shape[2]
+        q = self._u16(q, (hq, dqk))
+        k = self._u16(k, (hkv, dqk))
+        v = self._u16(v, (hkv, dv))
+        cu = np.ascontiguousarray(cu_newlens, dtype=np.int32)
+        batch = cu.shape[0] - 1
+        ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+        kc = None if k_cache is None else np.ascontiguousarray(k_cache)
+        vc = None if v_cache is None else np.ascontiguousarray(v_cache)
+        base = None if kv_base is None else np.ascontiguousarray(kv_base, dtype=np.int64)
+        sk = None if sink is None else np.ascontiguousarray(sink, dtype=np.float32)
+        ring = window - 1 if layer_type == SWA else 0
+        tn = int(cu[-1])
+        out = np.empty((tn, hq, dv), np.float64)
+        lse = np.empty((tn, hq), np.float64)
+        nth = nthreads if nthreads > 0 else self.default_threads()
+        rc = self.lib.oracle_prefill_chunk(hq, hkv, dqk, dv, layer_type, window, scale, value_scale,
+                                           self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(cu), batch,
+                                           self._ptr(kc), self._ptr(vc), ring, self._ptr(base), self._ptr(ctx),
+                                           self._ptr(sk), self._ptr(out), self._ptr(lse), nth)
+        if rc != OK:
+            raise ValueError(f"oracle_prefill_chunk rejected its arguments (status {rc})")
         return out, lse
 
     def kv_append(self, k, v, cu_newlens, ctx_lens, k_cache, v_cache, *, layer_type: int,

@@ -244,14 +244,18 @@ typedef struct {
     pthread_mutex_t mu;
 } decode_job_t;
 
-static const uint16_t* cache_row(const decode_job_t* jb, int b, int j, int g, int isv) {
-    const dims_t* d = jb->d;
+/* Row of cached position j of sequence b, KV head g, in the ring or pool. */
+static const uint16_t* cached_row(const dims_t* d, const uint16_t* cache, int ring, const int64_t* kv_base,
+                                  int b, int j, int g, int isv) {
     int D = isv ? d->dv : d->dqk;
-    const uint16_t* base = isv ? jb->v_cache : jb->k_cache;
     size_t row;
-    if (d->layer_type == ORACLE_SWA) row = (size_t)b * jb->ring + (size_t)(j % jb->ring);
-    else row = (size_t)(jb->kv_base[b] + j);
-    return base + (row * d->hkv + g) * D;
+    if (d->layer_type == ORACLE_SWA) row = (size_t)b * ring + (size_t)(j % ring);
+    else row = (size_t)(kv_base[b] + j);
+    return cache + (row * d->hkv + g) * D;
+}
+
+static const uint16_t* cache_row(const decode_job_t* jb, int b, int j, int g, int isv) {
+    return cached_row(jb->d, isv ? jb->v_cache : jb->k_cache, jb->ring, jb->kv_base, b, j, g, isv);
 }
 
 static void* decode_worker(void* arg) {
@@ -312,6 +316,101 @@ int oracle_decode(int hq, int hkv, int dqk, int dv, int layer_type, int window,
     jb.out = out; jb.lse = lse;
     pthread_mutex_init(&jb.mu, NULL);
     run_threads(decode_worker, &jb, nthreads);
+    pthread_mutex_destroy(&jb.mu);
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Chunked prefill: sequence b has ctx_lens[b] positions cached and brings  */
+/* n_b = cu_newlens[b+1] - cu_newlens[b] new tokens, token i at position    */
+/* p = ctx_lens[b] + i (model doc, MiMoV2FlashModel.forward: with a cache   */
+/* only the tokens not yet processed are passed).  Its key set is lo..p as  */
+/* above: positions below ctx_lens[b] are read from the cache (ring or pool,*/
+/* as in decode), the others from the chunk's own k/v rows.  The cache is   */
+/* read, never written (appending the chunk is a separate call).            */
+
+typedef struct {
+    const dims_t* d;
+    const uint16_t *q, *k, *v, *k_cache, *v_cache;
+    const int32_t* cu;
+    const int64_t* kv_base;
+    const int32_t* ctx;
+    int batch, ring, maxkeys;
+    const float* sink;
+    double *out, *lse;
+    int64_t next, total;
+    pthread_mutex_t mu;
+} chunk_job_t;
+
+static void* chunk_worker(void* arg) {
+    chunk_job_t* jb = (chunk_job_t*)arg;
+    const dims_t* d = jb->d;
+    const uint16_t** kr = malloc(sizeof(*kr) * (size_t)jb->maxkeys);
+    const uint16_t** vr = malloc(sizeof(*vr) * (size_t)jb->maxkeys);
+    double* sc = malloc(sizeof(double) * (size_t)jb->maxkeys);
+    int group = d->hq / d->hkv;
+    for (;;) {
+        pthread_mutex_lock(&jb->mu);
+        int64_t item = jb->next++;
+        pthread_mutex_unlock(&jb->mu);
+        if (item >= jb->total * d->hq) break;
+        int64_t t = item / d->hq;
+        int h = (int)(item % d->hq), g = h / group;
+        int b = seq_of_token(jb->cu, jb->batch, t);
+        int c = jb->ctx[b];
+        int p = c + (int)(t - jb->cu[b]);
+        int lo = 0;
+        if (d->layer_type == ORACLE_SWA) lo = p - (d->window - 1) > 0 ? p - (d->window - 1) : 0;
+        int n = 0;
+        for (int j = lo; j <= p; ++j, ++n) {
+            if (j < c) {
+                kr[n] = cached_row(d, jb->k_cache, jb->ring, jb->kv_base, b, j, g, 0);
+                vr[n] = cached_row(d, jb->v_cache, jb->ring, jb->kv_base, b, j, g, 1);
+            } else {
+                size_t row = (size_t)jb->cu[b] + (size_t)(j - c);
+                kr[n] = jb->k + (row * d->hkv + g) * d->dqk;
+                vr[n] = jb->v + (row * d->hkv + g) * d->dv;
+            }
+        }
+        double sigma = 0.0;
+        int hs = sink_present(jb->sink, h, &sigma);
+        attend_row(d, jb->q + ((size_t)t * d->hq + h) * d->dqk, n, kr, vr, hs, sigma, sc,
+                   jb->out + ((size_t)t * d->hq + h) * d->dv, jb->lse + (size_t)t * d->hq + h, NULL, NULL);
+    }
+    free(kr); free(vr); free(sc);
+    return NULL;
+}
+
+/* q [Tn][hq][dqk], k [Tn][hkv][dqk], v [Tn][hkv][dv] packed by cu_newlens
+ * [batch+1]; caches as for decode (SWA ring_slots = W - 1, GA kv_base).
+ * out [Tn][hq][dv], lse [Tn][hq]. */
+int oracle_prefill_chunk(int hq, int hkv, int dqk, int dv, int layer_type, int window,
+                         float scale, float value_scale,
+                         const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         const int32_t* cu_newlens, int batch,
+                         const uint16_t* k_cache, const uint16_t* v_cache, int ring_slots,
+                         const int64_t* kv_base, const int32_t* ctx_lens,
+                         const float* sink, double* out, double* lse, int nthreads) {
+    dims_t d = {hq, hkv, dqk, dv, layer_type, window, (double)scale, (double)value_scale};
+    if (!check_dims(&d) || batch < 1 || !q || !k || !v || !cu_newlens || !ctx_lens || !out || !lse)
+        return ORACLE_EINVAL;
+    if (layer_type == ORACLE_SWA && ring_slots != window - 1) return ORACLE_EINVAL;
+    if (layer_type == ORACLE_GA && !kv_base) return ORACLE_EINVAL;
+    if (cu_newlens[0] != 0) return ORACLE_EINVAL;
+    int maxkeys = 1;
+    for (int b = 0; b < batch; ++b) {
+        int n = cu_newlens[b + 1] - cu_newlens[b];
+        if (n < 0 || ctx_lens[b] < 0) return ORACLE_EINVAL;
+        if (ctx_lens[b] > 0 && (!k_cache || !v_cache)) return ORACLE_EINVAL;
+        if (ctx_lens[b] + n > maxkeys) maxkeys = ctx_lens[b] + n;
+    }
+    chunk_job_t jb;
+    memset(&jb, 0, sizeof jb);
+    jb.d = &d; jb.q = q; jb.k = k; jb.v = v; jb.k_cache = k_cache; jb.v_cache = v_cache;
+    jb.cu = cu_newlens; jb.kv_base = kv_base; jb.ctx = ctx_lens; jb.batch = batch; jb.ring = ring_slots;
+    jb.maxkeys = maxkeys; jb.sink = sink; jb.out = out; jb.lse = lse; jb.total = cu_newlens[batch];
+    pthread_mutex_init(&jb.mu, NULL);
+    run_threads(chunk_worker, &jb, nthreads);
     pthread_mutex_destroy(&jb.mu);
     return ORACLE_OK;
 }

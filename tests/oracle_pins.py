@@ -366,6 +366,108 @@ def pin_ga_capacity(orc):
     assert st == oracle.OK and kc[4:8].all() and not kc[:4].any() and not kc[8:].any()
 
 
+def _caches(layer_type, batch, rows):
+    if layer_type == SWA:
+        return np.zeros((batch, 128, 4, 192), np.uint16), np.zeros((batch, 128, 4, 128), np.uint16)
+    return np.zeros((rows, 4, 192), np.uint16), np.zeros((rows, 4, 128), np.uint16)
+
+
+def _pack(a, lengths, starts):
+    """Rows [starts[b], starts[b] + lengths[b]) of each sequence of a packed array."""
+    return np.concatenate([a[s:s + n] for s, n in zip(starts, lengths)]) if sum(lengths) else a[:0]
+
+
+def pin_chunk_without_cache_is_prefill(orc):
+    """Chunked prefill with nothing cached is plain prefill."""
+    x = _make([1, 40, 300, 129], seed=30)
+    sc = float(np.float32(synth.SOFTMAX_SCALE))
+    for lt in (SWA, GA):
+        of, lf = _run_prefill(orc, x, lt, 129, sc)
+        kc, vc = _caches(lt, 4, 8)
+        base = np.zeros(4, np.int64) if lt == GA else None
+        o, l = orc.prefill_chunk(_bits(x.q), _bits(x.k), _bits(x.v), x.cu_seqlens.numpy(), kc, vc,
+                                 np.zeros(4, np.int32), layer_type=lt, scale=sc, sink=x.sink.numpy(), kv_base=base)
+        _close(o, of, 1e-13, f"chunk without cache out lt={lt}")
+        _close(l, lf, 1e-13, f"chunk without cache lse lt={lt}")
+
+
+def pin_chunk_continues_prefill(orc):
+    """Sequences of a ragged batch with their first c_b tokens cached (appended
+    to the ring or pool) and the rest passed as one packed chunk: the chunk's
+    rows equal rows c_b..L_b-1 of prefill over the whole sequences."""
+    lengths = [300, 170, 64, 129, 260]
+    cached = [0, 1, 63, 128, 131]
+    x = _make(lengths, seed=31)
+    sc = float(np.float32(synth.SOFTMAX_SCALE))
+    qb, kb, vb = _bits(x.q), _bits(x.k), _bits(x.v)
+    cu = x.cu_seqlens.numpy()
+    rest = [L - c for L, c in zip(lengths, cached)]
+    starts = [int(cu[b]) + cached[b] for b in range(len(lengths))]
+    cu_new = np.concatenate([[0], np.cumsum(rest)]).astype(np.int32)
+    for lt in (SWA, GA):
+        of, lf = _run_prefill(orc, x, lt, 129, sc)
+        kc, vc = _caches(lt, len(lengths), sum(lengths) + 7)
+        base = cap = None
+        if lt == GA:
+            base = np.concatenate([[5], 5 + np.cumsum(lengths)[:-1]]).astype(np.int64)
+            cap = np.asarray(lengths, np.int64)
+        pre_cu = np.concatenate([[0], np.cumsum(cached)]).astype(np.int32)
+        pre_k, pre_v = _pack(kb, cached, cu[:-1]), _pack(vb, cached, cu[:-1])
+        st = orc.kv_append(pre_k, pre_v, pre_cu, np.zeros(len(lengths), np.int32), kc, vc, layer_type=lt,
+                           kv_base=base, kv_capacity=cap)
+        assert st == oracle.OK
+        o, l = orc.prefill_chunk(_pack(qb, rest, starts), _pack(kb, rest, starts), _pack(vb, rest, starts), cu_new,
+                                 kc, vc, np.asarray(cached, np.int32), layer_type=lt, scale=sc,
+                                 sink=x.sink.numpy(), kv_base=base)
+        rows = np.concatenate([np.arange(s, s + n) for s, n in zip(starts, rest)])
+        _close(o, of[rows], 1e-13, f"chunk vs prefill out lt={lt}")
+        _close(l, lf[rows], 1e-13, f"chunk vs prefill lse lt={lt}")
+
+
+def pin_chunk_of_one_token_is_decode(orc):
+    """A chunk of one token per sequence is a decode step."""
+    ctx = [0, 5, 127, 128, 400]
+    sc = float(np.float32(synth.SOFTMAX_SCALE))
+    for lt in (SWA, GA):
+        x = synth.decode_inputs(ctx, lt, seed=32)
+        args = (_bits(x.q), _bits(x.k_new), _bits(x.v_new))
+        base = None if x.kv_base is None else x.kv_base.numpy()
+        od, ld = orc.decode(*args, _bits(x.k_cache), _bits(x.v_cache), x.ctx_lens.numpy(), layer_type=lt,
+                            scale=sc, sink=x.sink.numpy(), kv_base=base)
+        oc, lc = orc.prefill_chunk(*args, np.arange(len(ctx) + 1, dtype=np.int32), _bits(x.k_cache),
+                                   _bits(x.v_cache), x.ctx_lens.numpy(), layer_type=lt, scale=sc,
+                                   sink=x.sink.numpy(), kv_base=base)
+        _close(oc, od, 1e-13, f"one-token chunk vs decode out lt={lt}")
+        _close(lc, ld, 1e-13, f"one-token chunk vs decode lse lt={lt}")
+
+
+def pin_chunks_in_sequence_rebuild_prefill(orc):
+    """One sequence fed as chunks [50, 1, 100, 149], each attended and then
+    appended: the concatenated chunk outputs equal the whole prefill."""
+    L = 300
+    x = _make([L], seed=33)
+    sc = float(np.float32(synth.SOFTMAX_SCALE))
+    qb, kb, vb = _bits(x.q), _bits(x.k), _bits(x.v)
+    for lt in (SWA, GA):
+        of, lf = _run_prefill(orc, x, lt, 129, sc)
+        kc, vc = _caches(lt, 1, L + 3)
+        base = np.array([3], np.int64) if lt == GA else None
+        cap = np.array([L], np.int64) if lt == GA else None
+        pos, outs, lses = 0, [], []
+        for n in (50, 1, 100, 149):
+            cu = np.array([0, n], np.int32)
+            ctx = np.array([pos], np.int32)
+            o, l = orc.prefill_chunk(qb[pos:pos + n], kb[pos:pos + n], vb[pos:pos + n], cu, kc, vc, ctx,
+                                     layer_type=lt, scale=sc, sink=x.sink.numpy(), kv_base=base)
+            outs.append(o)
+            lses.append(l)
+            assert orc.kv_append(kb[pos:pos + n], vb[pos:pos + n], cu, ctx, kc, vc, layer_type=lt, kv_base=base,
+                                 kv_capacity=cap) == oracle.OK
+            pos += n
+        _close(np.concatenate(outs), of, 1e-13, f"chunks in sequence out lt={lt}")
+        _close(np.concatenate(lses), lf, 1e-13, f"chunks in sequence lse lt={lt}")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]
 
 

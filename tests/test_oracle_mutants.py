@@ -41,17 +41,25 @@ MUTANTS = {
     "score sign flipped": ("        scores[j] = d->scale * acc;\n", "        scores[j] = -d->scale * acc;\n"),
     "weights not normalised by the sink": ("        double w = exp(scores[j] - l);\n",
                                            "        double w = exp(scores[j] - l) * (has_sink ? z / (z - exp(sigma - m)) : 1.0);\n"),
-    "ring slot off by one (decode read)": (
-        "    if (d->layer_type == ORACLE_SWA) row = (size_t)b * jb->ring + (size_t)(j % jb->ring);\n",
-        "    if (d->layer_type == ORACLE_SWA) row = (size_t)b * jb->ring + (size_t)((j + 1) % jb->ring);\n"),
+    "ring slot off by one (cache read)": (
+        "    if (d->layer_type == ORACLE_SWA) row = (size_t)b * ring + (size_t)(j % ring);\n",
+        "    if (d->layer_type == ORACLE_SWA) row = (size_t)b * ring + (size_t)((j + 1) % ring);\n"),
     "decode new token read from the cache": (
         "        kr[n] = jb->k_new + ((size_t)b * d->hkv + g) * d->dqk;\n",
         "        kr[n] = cache_row(jb, b, p > 0 ? p - 1 : 0, g, 0);\n"),
     "decode window one key too narrow": (
         "        if (d->layer_type == ORACLE_SWA) lo = p - (d->window - 1) > 0 ? p - (d->window - 1) : 0;\n"
-        "        int n = 0;",
+        "        int n = 0;\n        for (int j = lo; j < p; ++j, ++n) {",
         "        if (d->layer_type == ORACLE_SWA) lo = p - (d->window - 2) > 0 ? p - (d->window - 2) : 0;\n"
-        "        int n = 0;"),
+        "        int n = 0;\n        for (int j = lo; j < p; ++j, ++n) {"),
+    "chunk reads its first own key from the cache": ("            if (j < c) {\n", "            if (j <= c) {\n"),
+    "chunk query position without the cached offset": ("        int p = c + (int)(t - jb->cu[b]);\n",
+                                                       "        int p = (int)(t - jb->cu[b]);\n"),
+    "chunk window one key too wide": (
+        "        if (d->layer_type == ORACLE_SWA) lo = p - (d->window - 1) > 0 ? p - (d->window - 1) : 0;\n"
+        "        int n = 0;\n        for (int j = lo; j <= p; ++j, ++n) {",
+        "        if (d->layer_type == ORACLE_SWA) lo = p - d->window > 0 ? p - d->window : 0;\n"
+        "        int n = 0;\n        for (int j = lo; j <= p; ++j, ++n) {"),
     "append ring slot off by one": (
         "            size_t dst = layer_type == ORACLE_SWA ? (size_t)b * ring_slots + (size_t)(pos % ring_slots)\n",
         "            size_t dst = layer_type == ORACLE_SWA ? (size_t)b * ring_slots + (size_t)((pos + 1) % ring_slots)\n"),
