@@ -25,8 +25,8 @@ MIMO_ERR_UNSUPPORTED = 2
 MIMO_ERR_WORKSPACE = 3
 MIMO_ERR_HIP = 4
 
-ENTRY_POINTS = ("mimo_attn_prefill", "mimo_attn_decode_workspace_size", "mimo_attn_decode", "mimo_kv_append",
-                "mimo_status_string", "mimo_last_error", "mimo_abi_version")
+ENTRY_POINTS = ("mimo_attn_prefill", "mimo_attn_prefill_chunk", "mimo_attn_decode_workspace_size",
+                "mimo_attn_decode", "mimo_kv_append", "mimo_status_string", "mimo_last_error", "mimo_abi_version")
 
 
 class mimo_attn_dims(ctypes.Structure):
@@ -58,6 +58,9 @@ def lib() -> ctypes.CDLL:
         dims_p = ctypes.POINTER(mimo_attn_dims)
         L.mimo_attn_prefill.restype = ctypes.c_int
         L.mimo_attn_prefill.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P]
+        L.mimo_attn_prefill_chunk.restype = ctypes.c_int
+        L.mimo_attn_prefill_chunk.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _P,
+                                              _P, _P, _P]
         L.mimo_attn_decode_workspace_size.restype = _SZ
         L.mimo_attn_decode_workspace_size.argtypes = [dims_p, ctypes.c_int, _I32, _I32, _I32]
         L.mimo_attn_decode.restype = ctypes.c_int
@@ -120,6 +123,13 @@ def mimo_attn_prefill(dims: mimo_attn_dims, layer_type: int, q, k, v, cu_seqlens
                                    num_seqs, max_seqlen, _ptr(sink), _ptr(out), _ptr(lse), _stream(stream)))
 
 
+def mimo_attn_prefill_chunk(dims: mimo_attn_dims, layer_type: int, q, k, v, cu_newlens, num_seqs: int,
+                            max_newlen: int, k_cache, v_cache, kv_base, ctx_lens, sink, out, lse, stream=None) -> None:
+    _check(lib().mimo_attn_prefill_chunk(ctypes.byref(dims), layer_type, _ptr(q), _ptr(k), _ptr(v), _ptr(cu_newlens),
+                                         num_seqs, max_newlen, _ptr(k_cache), _ptr(v_cache), _ptr(kv_base),
+                                         _ptr(ctx_lens), _ptr(sink), _ptr(out), _ptr(lse), _stream(stream)))
+
+
 def mimo_attn_decode_workspace_size(dims: mimo_attn_dims, layer_type: int, batch: int, max_ctx: int,
                                     split_tokens: int = 0) -> int:
     return int(lib().mimo_attn_decode_workspace_size(ctypes.byref(dims), layer_type, batch, max_ctx, split_tokens))
@@ -152,6 +162,19 @@ def prefill(q, k, v, cu_seqlens, max_seqlen: int, layer_type: int, sink=None, di
         lse = torch.empty((T, dims.num_q_heads), dtype=torch.float32, device=q.device)
     mimo_attn_prefill(dims, layer_type, q, k, v, cu_seqlens, cu_seqlens.numel() - 1, max_seqlen, sink, out, lse,
                       stream)
+    return out, lse
+
+
+def prefill_chunk(q, k, v, cu_newlens, max_newlen: int, k_cache, v_cache, ctx_lens, layer_type: int, sink=None,
+                  kv_base=None, dims=None, out=None, lse=None, stream=None):
+    dims = dims or make_dims()
+    T = q.shape[0]
+    if out is None:
+        out = torch.empty((T, dims.num_q_heads, dims.head_dim_v), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, dims.num_q_heads), dtype=torch.float32, device=q.device)
+    mimo_attn_prefill_chunk(dims, layer_type, q, k, v, cu_newlens, cu_newlens.numel() - 1, max_newlen, k_cache,
+                            v_cache, kv_base, ctx_lens, sink, out, lse, stream)
     return out, lse
 
 

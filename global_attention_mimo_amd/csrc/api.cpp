@@ -91,6 +91,32 @@ int mimo_attn_prefill(const mimo_attn_dims* dims, int layer_type, const uint16_t
     return hip_status(mimo::launch_prefill(a, stream), "prefill launch");
 }
 
+int mimo_attn_prefill_chunk(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, const uint16_t* k,
+                            const uint16_t* v, const int32_t* cu_newlens, int32_t num_seqs, int32_t max_newlen,
+                            const uint16_t* k_cache, const uint16_t* v_cache, const int64_t* kv_base,
+                            const int32_t* ctx_lens, const float* sink, uint16_t* out, float* lse,
+                            hipStream_t stream) {
+    if (int st = check_dims(dims, layer_type, 2)) return st;
+    if (!q || !k || !v || !cu_newlens || !out || !k_cache || !v_cache || !ctx_lens)
+        return fail(MIMO_ERR_INVALID_ARG, "q, k, v, cu_newlens, out, k_cache, v_cache and ctx_lens must be non-NULL");
+    if (layer_type == MIMO_LAYER_GA && !kv_base) return fail(MIMO_ERR_INVALID_ARG, "GA needs kv_base");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(k_cache) ||
+        !aligned16(v_cache))
+        return fail(MIMO_ERR_INVALID_ARG, "q, k, v, out and the caches must be 16-byte aligned");
+    if (num_seqs < 1 || num_seqs > kMaxGridYZ)
+        return fail(MIMO_ERR_INVALID_ARG, "num_seqs %d outside [1, %d]", num_seqs, kMaxGridYZ);
+    if (max_newlen < 0) return fail(MIMO_ERR_INVALID_ARG, "max_newlen %d is negative", max_newlen);
+    if (max_newlen == 0) return ok();
+    mimo::PrefillArgs a{q, k, v, cu_newlens, sink, out, lse, num_seqs, max_newlen, dims->num_q_heads,
+                        dims->num_kv_heads, dims->sliding_window, dims->softmax_scale, dims->value_scale,
+                        layer_type == MIMO_LAYER_SWA};
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.kv_base = kv_base;
+    a.ctx_lens = ctx_lens;
+    return hip_status(mimo::launch_prefill_chunk(a, stream), "chunked prefill launch");
+}
+
 size_t mimo_attn_decode_workspace_size(const mimo_attn_dims* dims, int layer_type, int32_t batch, int32_t max_ctx,
                                        int32_t split_tokens) {
     if (check_dims(dims, layer_type, 2) != MIMO_OK || batch < 1 || max_ctx < 0) return 0;

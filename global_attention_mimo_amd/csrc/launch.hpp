@@ -17,8 +17,14 @@ struct PrefillArgs {
     int num_seqs, max_seqlen, hq, hkv, window;
     float softmax_scale, value_scale;
     bool swa;
+    // Chunked prefill only: the caches the sequences continue and their lengths.
+    const uint16_t* k_cache = nullptr;
+    const uint16_t* v_cache = nullptr;
+    const int64_t* kv_base = nullptr;
+    const int32_t* ctx_lens = nullptr;
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_chunk(const PrefillArgs& a, hipStream_t stream);
 
 struct DecodeArgs {
     const uint16_t* q;

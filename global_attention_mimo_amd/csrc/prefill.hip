@@ -87,14 +87,19 @@ struct PrefillCfg {
 #endif
 constexpr float kRescaleThreshold = MIMO_RESCALE_THRESHOLD;
 
-template <int WV, int NB, int NK, bool SWA, int WAVES_PER_EU>
+// CHUNK: the sequences continue cached ones.  Sequence b has ctx_lens[b]
+// positions in the cache (GA pool rows kv_base[b] + j, SWA ring slots j mod
+// ring) and its packed tokens sit at positions ctx_lens[b] + i; a key row is
+// staged from the cache below that length and from the chunk above it.
+template <int WV, int NB, int NK, bool SWA, int WAVES_PER_EU, bool CHUNK>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WV, 64 * WV),
                           amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
 void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                     const uint16_t* __restrict__ v, const int32_t* __restrict__ cu_seqlens,
                     const float* __restrict__ sink, uint16_t* __restrict__ out, float* __restrict__ lse,
                     int hq, int hkv, int window, float c_log2, float value_scale, int num_qblocks,
-                    int max_seqlen) {
+                    int max_seqlen, const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
+                    const int64_t* __restrict__ kv_base, const int32_t* __restrict__ ctx_lens, int ring) {
     using Cfg = PrefillCfg<WV, NB, NK>;
     constexpr int QT = Cfg::kTokens;
     // Two K/V buffers: tile t is computed from buffer t%2 while tile t+1 is staged into the other.
@@ -114,6 +119,8 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     const int L = min(cu_seqlens[b + 1] - s0, max_seqlen);  // tokens past max_seqlen stay unwritten
     const int q0 = qb * QT;
     if (q0 >= L) return;
+    // Position of the first token of the sequence (local token t sits at ctx0 + t).
+    const int ctx0 = CHUNK ? ctx_lens[b] : 0;
 
     const int head = g * kGroup + (r32 & 15);
     int tok[NB];
@@ -158,9 +165,10 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         for (int nb = 0; nb < NB; ++nb) oacc[db][nb] = f32x16{};
 
     const int q_last = min(q0 + QT, L) - 1;
-    const int k_lo = SWA ? max(0, q0 - (window - 1)) : 0;
+    // Key tiles cover positions; the block's queries sit at ctx0 + q0 .. ctx0 + q_last.
+    const int k_lo = SWA ? max(0, ctx0 + q0 - (window - 1)) : 0;
     const int kt_begin = k_lo / NK;
-    const int kt_end = q_last / NK;
+    const int kt_end = (ctx0 + q_last) / NK;
 
     // Global -> register staging of one K/V tile.  Each thread always moves the
     // same (row, 16-byte column) slots of a tile, so its source pointers are
@@ -183,10 +191,34 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         vp[i] = v + ((size_t)s0 * hkv + g) * kDv + (c % (kDv / 8)) * 8;
     }
     const size_t kstride = (size_t)hkv * kDqk, vstride = (size_t)hkv * kDv;
+    // Cache sources (CHUNK only): same per-thread columns, rows by position.
+    const uint16_t* kcp[Cfg::kKPer];
+    const uint16_t* vcp[Cfg::kVPer];
+    int64_t cache_row0 = 0;
+    if constexpr (CHUNK) {
+        cache_row0 = SWA ? (int64_t)b * ring : kv_base[b];
+#pragma unroll
+        for (int i = 0; i < Cfg::kKPer; ++i) kcp[i] = k_cache + (kp[i] - k) - (size_t)s0 * kstride;
+#pragma unroll
+        for (int i = 0; i < Cfg::kVPer; ++i) vcp[i] = v_cache + (vp[i] - v) - (size_t)s0 * vstride;
+    }
     u32x4 kreg[Cfg::kKPer], vreg[Cfg::kVPer];
     auto load_tile = [&](int kt) {
         const int kbase = kt * NK;
-        if (kbase + NK <= L) {
+        if constexpr (CHUNK) {
+            // Position j: cache row below ctx0, else chunk row j - ctx0 (past the
+            // chunk's last token clamped to it: such keys are masked).
+            auto src_row = [&](const uint16_t* cache_col, const uint16_t* chunk_col, size_t stride, int j) {
+                if (j < ctx0) return cache_col + (size_t)(cache_row0 + (SWA ? j % ring : j)) * stride;
+                return chunk_col + (size_t)min(j - ctx0, L - 1) * stride;
+            };
+#pragma unroll
+            for (int i = 0; i < Cfg::kKPer; ++i)
+                kreg[i] = *reinterpret_cast<const u32x4*>(src_row(kcp[i], kp[i], kstride, kbase + krow_of[i]));
+#pragma unroll
+            for (int i = 0; i < Cfg::kVPer; ++i)
+                vreg[i] = *reinterpret_cast<const u32x4*>(src_row(vcp[i], vp[i], vstride, kbase + vrow_of[i]));
+        } else if (kbase + NK <= L) {
 #pragma unroll
             for (int i = 0; i < Cfg::kKPer; ++i)
                 kreg[i] = *reinterpret_cast<const u32x4*>(kp[i] + (size_t)(kbase + krow_of[i]) * kstride);
@@ -235,7 +267,8 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         const uint16_t* vtile = lds_v + buf * Cfg::kLdsV;
         const int kbase = kt * NK;
 
-        const bool interior = (kbase + NK - 1 <= q0) && (!SWA || kbase >= q_last - (window - 1));
+        const bool interior =
+            (kbase + NK - 1 <= ctx0 + q0) && (!SWA || kbase >= ctx0 + q_last - (window - 1));
 
         // ---- S^T = K * Q^T ---------------------------------------------------
         f32x16 sacc[NK / 32][NB];
@@ -259,7 +292,7 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             // tile sits at offset 32*kb + 8*(r/4) + (r%4) + 4*hh; it is kept when
             // tok-(W-1) <= key <= tok (GA: no lower bound).
             if (!interior) {
-                const int hi_off = tok[nb] - kbase - 4 * hh;
+                const int hi_off = ctx0 + tok[nb] - kbase - 4 * hh;
                 const int lo_off = SWA ? hi_off - (window - 1) : -(1 << 30);
 #pragma unroll
                 for (int kb = 0; kb < NK / 32; ++kb)
@@ -591,14 +624,15 @@ void swa_stream_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
     }
 }
 
-template <int WV, int NB, int NK, bool SWA, int WPE>
+template <int WV, int NB, int NK, bool SWA, int WPE, bool CHUNK = false>
 hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
     using Cfg = PrefillCfg<WV, NB, NK>;
     const int nqb = (a.max_seqlen + Cfg::kTokens - 1) / Cfg::kTokens;
     dim3 grid(nqb, a.hkv, a.num_seqs);
-    hipLaunchKernelGGL((prefill_kernel<WV, NB, NK, SWA, WPE>), grid, dim3(Cfg::kThreads), 0, stream, a.q, a.k, a.v,
-                       a.cu_seqlens, a.sink, a.out, a.lse, a.hq, a.hkv, a.window, a.softmax_scale * kLog2e,
-                       a.value_scale, nqb, a.max_seqlen);
+    hipLaunchKernelGGL((prefill_kernel<WV, NB, NK, SWA, WPE, CHUNK>), grid, dim3(Cfg::kThreads), 0, stream, a.q, a.k,
+                       a.v, a.cu_seqlens, a.sink, a.out, a.lse, a.hq, a.hkv, a.window, a.softmax_scale * kLog2e,
+                       a.value_scale, nqb, a.max_seqlen, a.k_cache, a.v_cache, a.kv_base, a.ctx_lens,
+                       a.window - 1);
     return hipGetLastError();
 }
 
@@ -615,6 +649,10 @@ template <int WV, int NB, int NK, int WPE>
 hipError_t launch_ga(const PrefillArgs& a, hipStream_t s) { return launch<WV, NB, NK, false, WPE>(a, s); }
 template <int WV, int NB, int NK, int WPE>
 hipError_t launch_swa(const PrefillArgs& a, hipStream_t s) { return launch<WV, NB, NK, true, WPE>(a, s); }
+template <int WV, int NB, int NK, int WPE>
+hipError_t launch_ga_chunk(const PrefillArgs& a, hipStream_t s) { return launch<WV, NB, NK, false, WPE, true>(a, s); }
+template <int WV, int NB, int NK, int WPE>
+hipError_t launch_swa_chunk(const PrefillArgs& a, hipStream_t s) { return launch<WV, NB, NK, true, WPE, true>(a, s); }
 
 // Streaming SWA grid: strips per compute unit it aims for (one workgroup fits
 // a CU), and the longest strip.  The cap keeps ragged batches balanced: the
@@ -645,6 +683,12 @@ hipError_t launch_swa_stream(const PrefillArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_prefill_chunk(const PrefillArgs& a, hipStream_t stream) {
+    if (a.max_seqlen <= 0) return hipSuccess;
+    if (a.swa) return launch_swa_chunk<MIMO_SWA_CFG>(a, stream);
+    return launch_ga_chunk<MIMO_GA_CFG>(a, stream);
+}
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     if (a.max_seqlen <= 0) return hipSuccess;

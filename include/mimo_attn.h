@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MIMO_ATTN_ABI_VERSION 1
+#define MIMO_ATTN_ABI_VERSION 2
 
 /* Layer type: which key set a query sees (model doc, Key features; config
  * layer_types). */
@@ -108,6 +108,37 @@ int mimo_attn_prefill(const mimo_attn_dims* dims, int layer_type,
                       const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
                       const float* sink, uint16_t* out, float* lse, hipStream_t stream);
+
+/*
+ * Chunked prefill: attention of new tokens that continue cached sequences
+ * (model doc, MiMoV2FlashModel.forward, past_key_values: with a cache only the
+ * unprocessed tokens are passed).  New token i of sequence b sits at position
+ * p = ctx_lens[b] + i and sees keys lo..p (lo as above): positions below
+ * ctx_lens[b] are read from the cache, the others from this call's k, v.
+ *
+ *   q, k, v      packed new tokens [Tn][Hq][192], [Tn][Hkv][192], [Tn][Hkv][128].
+ *   cu_newlens   [num_seqs+1] int32 (device), cu_newlens[0] == 0, non-decreasing.
+ *   num_seqs     >= 1 (host).
+ *   max_newlen   (host) >= every chunk length; tokens of a longer chunk beyond
+ *                max_newlen are left unwritten.
+ *   k_cache, v_cache, kv_base  as for mimo_attn_decode (SWA ring of W-1 slots
+ *                per sequence, W >= 2; GA pool with base rows kv_base[b]).
+ *   ctx_lens     [num_seqs] int32 (device): positions already cached.  For GA,
+ *                pool rows kv_base[b] .. kv_base[b] + ctx_lens[b] - 1 are read;
+ *                for SWA the ring must hold positions max(0, ctx_lens[b]-(W-1))
+ *                .. ctx_lens[b]-1 (what mimo_kv_append leaves behind).
+ *   sink, out, lse  as for prefill, with T = Tn; lse may be NULL.
+ * The cache is only read.  Order: attend, then append the chunk with
+ * mimo_kv_append (same cu_newlens and ctx_lens) -- for SWA the append may
+ * overwrite ring slots this call still reads.
+ * A call with max_newlen == 0 enqueues nothing and returns MIMO_OK.
+ */
+int mimo_attn_prefill_chunk(const mimo_attn_dims* dims, int layer_type,
+                            const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                            const int32_t* cu_newlens, int32_t num_seqs, int32_t max_newlen,
+                            const uint16_t* k_cache, const uint16_t* v_cache,
+                            const int64_t* kv_base, const int32_t* ctx_lens,
+                            const float* sink, uint16_t* out, float* lse, hipStream_t stream);
 
 /*
  * Bytes of device workspace mimo_attn_decode needs for these arguments.  SWA

@@ -42,7 +42,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_version_and_status_strings(L):
-    assert B.mimo_abi_version() == 1
+    assert B.mimo_abi_version() == 2
     assert B.mimo_status_string(0) == "MIMO_OK"
     assert B.mimo_status_string(3) == "MIMO_ERR_WORKSPACE"
     assert B.mimo_status_string(99) == "MIMO_ERR_UNKNOWN"
@@ -79,6 +79,40 @@ def test_prefill_rejects(L, case, status):
 
 def test_prefill_empty_is_ok_without_launch(L):
     assert prefill_call(L, maxlen=0) == B.MIMO_OK
+
+
+def chunk_call(L, dims=None, layer=1, q=FAKE, k=FAKE, v=FAKE, cu=FAKE, nseq=2, maxlen=16, kc=FAKE, vc=FAKE,
+               base=FAKE, ctx=FAKE, out=FAKE):
+    d = dims if dims is not None else B.make_dims()
+    return L.mimo_attn_prefill_chunk(ctypes.byref(d) if d is not False else None, layer, q, k, v, cu, nseq, maxlen,
+                                     kc, vc, base, ctx, None, out, None, None)
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(dims=False), B.MIMO_ERR_INVALID_ARG),
+    (dict(layer=2), B.MIMO_ERR_INVALID_ARG),
+    (dict(q=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(cu=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(kc=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(vc=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(ctx=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(base=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(out=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(kc=FAKE_ODD), B.MIMO_ERR_INVALID_ARG),
+    (dict(nseq=0), B.MIMO_ERR_INVALID_ARG),
+    (dict(nseq=70000), B.MIMO_ERR_INVALID_ARG),
+    (dict(maxlen=-1), B.MIMO_ERR_INVALID_ARG),
+    (dict(layer=0, dims=B.make_dims(sliding_window=1)), B.MIMO_ERR_INVALID_ARG),
+    (dict(dims=B.make_dims(head_dim_v=64)), B.MIMO_ERR_UNSUPPORTED),
+])
+def test_prefill_chunk_rejects(L, case, status):
+    assert chunk_call(L, **case) == status
+    assert B.mimo_last_error() != ""
+
+
+def test_prefill_chunk_empty_is_ok_and_swa_needs_no_base(L):
+    assert chunk_call(L, maxlen=0) == B.MIMO_OK
+    assert chunk_call(L, layer=0, base=None, maxlen=0) == B.MIMO_OK
 
 
 def decode_call(L, dims=None, layer=1, q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, base=FAKE, ctx=FAKE, batch=2,
