@@ -99,6 +99,66 @@ def measured_traffic(record="profiles/prefill_ga_1x32768_traffic.json"):
     return rec["read_bytes"] + rec["write_bytes"]
 
 
+def chunk_rows(dims, ga, swa, reps=5):
+    """Chunked prefill (prefill continuing cached sequences), timed apart from the
+    step: GA, one sequence with its first 28672 positions cached and the last
+    4096 as the chunk (the GA prefill input, split); SWA, the 4 x 8192 input as
+    chunks that continue 8192 cached positions each (the ring holds the last 128).
+    Caches are filled by the library's append before timing."""
+    dev = "cuda"
+    res = {}
+    # GA: pool rows 0..32767 for the sequence, first 28672 appended.
+    c, n = 28672, 4096
+    kc = torch.zeros((32768, HKV, DQK), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros((32768, HKV, DV), dtype=torch.bfloat16, device=dev)
+    base = torch.zeros(1, dtype=torch.int64, device=dev)
+    cap = torch.full((1,), 32768, dtype=torch.int64, device=dev)
+    zero = torch.zeros(1, dtype=torch.int32, device=dev)
+    B.mimo_kv_append(dims, 1, ga.k[:c], ga.v[:c], torch.tensor([0, c], dtype=torch.int32, device=dev), zero, 1, c,
+                     kc, vc, base, cap)
+    cu = torch.tensor([0, n], dtype=torch.int32, device=dev)
+    ctx = torch.full((1,), c, dtype=torch.int32, device=dev)
+    q, k, v = ga.q[c:].contiguous(), ga.k[c:].contiguous(), ga.v[c:].contiguous()
+    out = torch.empty((n, HQ, DV), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((n, HQ), dtype=torch.float32, device=dev)
+    call = lambda: B.mimo_attn_prefill_chunk(dims, 1, q, k, v, cu, 1, n, kc, vc, base, ctx, ga.sink, out, lse)
+    ms = _time_ms(call, reps)
+    pairs = n * c + n * (n + 1) // 2
+    tfs = pairs * HQ * FLOP_PER_TRIPLE / (ms * 1e-3) / 1e12
+    res["prefill_chunk_ga"] = {"workload": "1 sequence, 28672 cached + 4096 new", "ms": ms, "TFLOP/s": tfs,
+                               "frac_mfma_peak": tfs / PEAK_BF16_TFLOPS}
+    del kc, vc, q, k, v, out, lse
+    # SWA: ring [4][128] after appending 8192 positions per sequence; chunks are the 4 x 8192 input.
+    kc = torch.zeros((4, W - 1, HKV, DQK), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros((4, W - 1, HKV, DV), dtype=torch.bfloat16, device=dev)
+    zeros = torch.zeros(4, dtype=torch.int32, device=dev)
+    B.mimo_kv_append(dims, 0, swa.k, swa.v, swa.cu_seqlens, zeros, 4, swa.k.shape[0], kc, vc, None, None)
+    ctx = torch.full((4,), 8192, dtype=torch.int32, device=dev)
+    out = torch.empty((swa.q.shape[0], HQ, DV), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((swa.q.shape[0], HQ), dtype=torch.float32, device=dev)
+    call = lambda: B.mimo_attn_prefill_chunk(dims, 0, swa.q, swa.k, swa.v, swa.cu_seqlens, 4, 8192, kc, vc, None,
+                                             ctx, swa.sink, out, lse)
+    ms = _time_ms(call, reps)
+    nbytes = swa.q.shape[0] * TOKEN_BYTES + 4 * (W - 1) * KV_TOKEN_BYTES
+    res["prefill_chunk_swa"] = {"workload": "4 sequences, 8192 cached + 8192 new each", "ms": ms,
+                                "TFLOP/s": 4 * 8192 * W * HQ * FLOP_PER_TRIPLE / (ms * 1e-3) / 1e12,
+                                "GB/s": nbytes / (ms * 1e-3) / 1e9,
+                                "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+    return res
+
+
+def _time_ms(call, reps):
+    call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
 def device_context():
     """The box's own figures next to the spec-sheet peaks: CU count and a measured
     device-to-device copy rate (read + write bytes per second, 2 GiB buffers)."""
@@ -346,6 +406,8 @@ def main():
         "breakdown": breakdown,
         "roofline": roof,
         "device": dev_ctx,
+        # Rows beyond the step (continuing cached sequences); not part of `value`.
+        "next_rows": chunk_rows(dims, ga, swa),
     }
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample (cpu_baseline)")

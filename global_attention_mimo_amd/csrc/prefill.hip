@@ -401,12 +401,18 @@ static_assert(kSlotKChunks % 64 == 0 && kSlotKChunks + kSlotVChunks <= 2 * kStre
 
 __device__ __forceinline__ int ring_slot(int h) { return (h + kRingSlots * 16) % kRingSlots; }  // h >= -176
 
+// CHUNK: the sequences continue cached ones (ctx_lens[b] positions, the last
+// W-1 of them in the ring k_cache/v_cache [B][W-1][Hkv][D]).  Keys are counted
+// from the chunk's first token; a key at negative index j is cached position
+// ctx_lens[b] + j, staged from the ring instead of as zeros.
+template <bool CHUNK>
 __global__ __attribute__((amdgpu_flat_work_group_size(kStreamThreads, kStreamThreads), amdgpu_waves_per_eu(2, 2)))
 void swa_stream_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                        const uint16_t* __restrict__ v, const int32_t* __restrict__ cu_seqlens,
                        const float* __restrict__ sink, uint16_t* __restrict__ out, float* __restrict__ lse,
                        int hq, int hkv, int window, float c_log2, float value_scale, int strip_blocks,
-                       int max_seqlen) {
+                       int max_seqlen, const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
+                       const int32_t* __restrict__ ctx_lens) {
     __shared__ __attribute__((aligned(16))) uint16_t ring_k[kRingSlots * kSlotKeys * kKStride];
     __shared__ __attribute__((aligned(16))) uint16_t ring_v[kRingSlots * kSlotKeys * kVStride];
     // Threads without a second chunk of their own write it here, so that every
@@ -422,6 +428,8 @@ void swa_stream_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
     const int g = blockIdx.y;
     const int s0 = cu_seqlens[b];
     const int L = min(cu_seqlens[b + 1] - s0, max_seqlen);  // tokens past max_seqlen stay unwritten
+    const int ctx0 = CHUNK ? ctx_lens[b] : 0;                // keys from -ctx0 exist
+    const int ring = window - 1;
     const int blk_begin = blockIdx.x * strip_blocks;
     const int blk_end = min(blk_begin + strip_blocks, (L + kStreamTokens - 1) / kStreamTokens);
     if (blk_begin >= blk_end) return;
@@ -462,15 +470,30 @@ void swa_stream_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
 
     // Keys below 0 are zeroed at the LDS write, where the loaded value is
     // waited for anyway.
-    auto load_slot = [&](int h, u32x4& ra, u32x4& rb) {
-        ra = *reinterpret_cast<const u32x4*>(ga_src + (size_t)min(max(h * kSlotKeys + ga_row, 0), L - 1) * ga_stride);
-        rb = *reinterpret_cast<const u32x4*>(gb_src + (size_t)min(max(h * kSlotKeys + gb_row, 0), L - 1) * vstride);
+    // Cache sources of the same columns (CHUNK): ring rows of sequence b.
+    const uint16_t* ga_cache = nullptr;
+    const uint16_t* gb_cache = nullptr;
+    if constexpr (CHUNK) {
+        ga_cache = (tid < kSlotKChunks ? k_cache : v_cache) + (ga_src - (tid < kSlotKChunks ? k : v)) -
+                   (size_t)s0 * ga_stride + (size_t)b * ring * ga_stride;
+        gb_cache = v_cache + (gb_src - v) - (size_t)s0 * vstride + (size_t)b * ring * vstride;
+    }
+    // A slot is all negative keys or all non-negative ones (16 | slot start), so
+    // the source choice is uniform per slot.
+    auto row_ptr = [&](const uint16_t* chunk, const uint16_t* cache, size_t stride, int j) {
+        if (CHUNK && j < 0) return cache + (size_t)(max(ctx0 + j, 0) % ring) * stride;
+        return chunk + (size_t)min(max(j, 0), L - 1) * stride;
     };
+    auto load_slot = [&](int h, u32x4& ra, u32x4& rb) {
+        ra = *reinterpret_cast<const u32x4*>(row_ptr(ga_src, ga_cache, ga_stride, h * kSlotKeys + ga_row));
+        rb = *reinterpret_cast<const u32x4*>(row_ptr(gb_src, gb_cache, vstride, h * kSlotKeys + gb_row));
+    };
+    // Keys before the sequence start are staged as zeros (masked, but finite).
     auto store_slot = [&](int h, const u32x4& ra, const u32x4& rb) {
         const int sl = ring_slot(h);
         const u32x4 zero = {0, 0, 0, 0};
-        *reinterpret_cast<u32x4*>(la_dst + sl * la_slot) = h * kSlotKeys + ga_row < 0 ? zero : ra;
-        *reinterpret_cast<u32x4*>(lb_dst + sl * lb_slot) = h * kSlotKeys + gb_row < 0 ? zero : rb;
+        *reinterpret_cast<u32x4*>(la_dst + sl * la_slot) = ctx0 + h * kSlotKeys + ga_row < 0 ? zero : ra;
+        *reinterpret_cast<u32x4*>(lb_dst + sl * lb_slot) = ctx0 + h * kSlotKeys + gb_row < 0 ? zero : rb;
     };
     // Q^T fragments of one block (MFMA B operand); rows past the end repeat the last token.
     auto load_q = [&](int blk, bf16x8 (&qv)[kDqk / 16]) {
@@ -544,7 +567,7 @@ void swa_stream_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
         for (int j = 0; j < kStreamTiles; ++j) {
             const int kbase = q0 - kStreamLead + 32 * j;
             // Tiles wholly before key 0 or before the band of the block's first token.
-            if (kbase + 31 < 0 || kbase + 31 < q0 - (window - 1)) continue;
+            if (kbase + 31 < -ctx0 || kbase + 31 < q0 - (window - 1)) continue;
             const int h = hq0 - 2 * kStreamTiles + 1 + 2 * j;
             const uint16_t* klo = ring_k + ring_slot(h) * (kSlotKeys * kKStride);
             const uint16_t* khi = ring_k + ring_slot(h + 1) * (kSlotKeys * kKStride);
@@ -557,10 +580,11 @@ void swa_stream_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
 
             // Mask unless every key of the tile is in every token's band: key
             // offset 8*(r/4) + (r%4) + 4*hh is kept when max(0, tok-(W-1)) <= key <= tok.
-            const bool interior = kbase >= 0 && kbase + 31 <= q0 && kbase >= q0 + kStreamTokens - 1 - (window - 1);
+            const bool interior =
+                kbase >= -ctx0 && kbase + 31 <= q0 && kbase >= q0 + kStreamTokens - 1 - (window - 1);
             if (!interior) {
                 const int hi_off = tok - kbase - 4 * hh;
-                const int lo_off = max(hi_off - (window - 1), -kbase - 4 * hh);
+                const int lo_off = max(hi_off - (window - 1), -ctx0 - kbase - 4 * hh);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int off = 8 * (r >> 2) + (r & 3);
@@ -664,6 +688,7 @@ hipError_t launch_swa_chunk(const PrefillArgs& a, hipStream_t s) { return launch
 #define MIMO_STREAM_MAX_STRIP 32
 #endif
 
+template <bool CHUNK>
 hipError_t launch_swa_stream(const PrefillArgs& a, hipStream_t stream) {
     int dev = 0, cus = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -676,9 +701,9 @@ hipError_t launch_swa_stream(const PrefillArgs& a, hipStream_t stream) {
     const long long target = (long long)max(cus, 1) * MIMO_STREAM_ROUNDS;
     const int strip = (int)max(1LL, min(min(per_seq, (long long)MIMO_STREAM_MAX_STRIP), (total + target - 1) / target));
     dim3 grid((unsigned)((per_seq + strip - 1) / strip), a.hkv, a.num_seqs);
-    hipLaunchKernelGGL(swa_stream_kernel, grid, dim3(kStreamThreads), 0, stream, a.q, a.k, a.v, a.cu_seqlens, a.sink,
-                       a.out, a.lse, a.hq, a.hkv, a.window, a.softmax_scale * kLog2e, a.value_scale, strip,
-                       a.max_seqlen);
+    hipLaunchKernelGGL(swa_stream_kernel<CHUNK>, grid, dim3(kStreamThreads), 0, stream, a.q, a.k, a.v, a.cu_seqlens,
+                       a.sink, a.out, a.lse, a.hq, a.hkv, a.window, a.softmax_scale * kLog2e, a.value_scale, strip,
+                       a.max_seqlen, a.k_cache, a.v_cache, a.ctx_lens);
     return hipGetLastError();
 }
 
@@ -686,13 +711,14 @@ hipError_t launch_swa_stream(const PrefillArgs& a, hipStream_t stream) {
 
 hipError_t launch_prefill_chunk(const PrefillArgs& a, hipStream_t stream) {
     if (a.max_seqlen <= 0) return hipSuccess;
+    if (a.swa && a.window <= kStreamMaxWindow) return launch_swa_stream<true>(a, stream);
     if (a.swa) return launch_swa_chunk<MIMO_SWA_CFG>(a, stream);
     return launch_ga_chunk<MIMO_GA_CFG>(a, stream);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     if (a.max_seqlen <= 0) return hipSuccess;
-    if (a.swa && a.window <= kStreamMaxWindow) return launch_swa_stream(a, stream);
+    if (a.swa && a.window <= kStreamMaxWindow) return launch_swa_stream<false>(a, stream);
     if (a.swa) return launch_swa<MIMO_SWA_CFG>(a, stream);
     return launch_ga<MIMO_GA_CFG>(a, stream);
 }

@@ -28,11 +28,11 @@ def _split(x, cached):
     return pre, new, rest
 
 
-def _caches(layer_type, lengths, headroom=8):
+def _caches(layer_type, lengths, headroom=8, window=129):
     n = len(lengths)
     if layer_type == SWA:
-        return (torch.zeros((n, 128, 4, 192), dtype=torch.bfloat16, device=DEV),
-                torch.zeros((n, 128, 4, 128), dtype=torch.bfloat16, device=DEV), None, None)
+        return (torch.zeros((n, window - 1, 4, 192), dtype=torch.bfloat16, device=DEV),
+                torch.zeros((n, window - 1, 4, 128), dtype=torch.bfloat16, device=DEV), None, None)
     caps = [L + headroom for L in lengths]
     base = torch.tensor(np.concatenate([[3], 3 + np.cumsum(caps)[:-1]]), dtype=torch.int64, device=DEV)
     rows = int(base[-1]) + caps[-1]
@@ -41,41 +41,42 @@ def _caches(layer_type, lengths, headroom=8):
             torch.tensor(caps, dtype=torch.int64, device=DEV))
 
 
-def _fill(x, layer_type, cached, kc, vc, base, cap):
+def _fill(x, layer_type, cached, kc, vc, base, cap, window=129):
     pre, _, _ = _split(x, cached)
     cu_pre = synth.cu_from_lengths(cached, DEV)
     zeros = torch.zeros(len(cached), dtype=torch.int32, device=DEV)
     if sum(cached):
         B.kv_append(to_dev(x.k[pre]), to_dev(x.v[pre]), cu_pre, zeros, kc, vc, layer_type, kv_base=base,
-                    kv_capacity=cap)
+                    kv_capacity=cap, dims=B.make_dims(sliding_window=window))
 
 
-def _chunk(x, layer_type, cached, kc, vc, base, max_newlen=None):
+def _chunk(x, layer_type, cached, kc, vc, base, max_newlen=None, window=129):
     _, new, rest = _split(x, cached)
     cu_new = synth.cu_from_lengths(rest, DEV)
     ctx = torch.tensor(cached, dtype=torch.int32, device=DEV)
     out, lse = B.prefill_chunk(to_dev(x.q[new]), to_dev(x.k[new]), to_dev(x.v[new]), cu_new,
                                max(rest) if max_newlen is None else max_newlen, kc, vc, ctx, layer_type,
-                               sink=to_dev(x.sink), kv_base=base)
+                               sink=to_dev(x.sink), kv_base=base, dims=B.make_dims(sliding_window=window))
     torch.cuda.synchronize()
     return out, lse, new, rest, cu_new, ctx
 
 
-@pytest.mark.parametrize("layer_type", [SWA, GA])
-def test_chunk_against_oracle_ragged(layer_type):
+@pytest.mark.parametrize("layer_type,window", [(SWA, 129), (SWA, 64), (SWA, 300), (GA, 129)])
+def test_chunk_against_oracle_ragged(layer_type, window):
     """Prefixes of 0, 1, 63, 128, 131 and 1000 tokens cached; chunks of 300, 169,
-    1, 1, 129 and 500 tokens, in one packed call."""
+    1, 1, 129 and 500 tokens, in one packed call.  SWA windows up to 145 keys run
+    the streaming kernel, wider ones the tiled kernel."""
     lengths = [300, 170, 64, 129, 260, 1500]
     cached = [0, 1, 63, 128, 131, 1000]
-    log(f"[case] chunked prefill layer={layer_type} lengths={lengths} cached={cached}")
+    log(f"[case] chunked prefill layer={layer_type} window={window} lengths={lengths} cached={cached}")
     x = synth.prefill_inputs(lengths, seed=40)
-    kc, vc, base, cap = _caches(layer_type, lengths)
-    _fill(x, layer_type, cached, kc, vc, base, cap)
-    out, lse, new, rest, cu_new, ctx = _chunk(x, layer_type, cached, kc, vc, base)
+    kc, vc, base, cap = _caches(layer_type, lengths, window=window)
+    _fill(x, layer_type, cached, kc, vc, base, cap, window=window)
+    out, lse, new, rest, cu_new, ctx = _chunk(x, layer_type, cached, kc, vc, base, window=window)
     ro, rl = orc().prefill_chunk(bits(x.q[new]), bits(x.k[new]), bits(x.v[new]), cu_new.cpu().numpy(), bits(kc),
-                                 bits(vc), ctx.cpu().numpy(), layer_type=layer_type, scale=SCALE,
+                                 bits(vc), ctx.cpu().numpy(), layer_type=layer_type, window=window, scale=SCALE,
                                  sink=sink_array(x.sink), kv_base=None if base is None else base.cpu().numpy())
-    compare(out, lse, ro, rl, f"chunked prefill layer {layer_type}")
+    compare(out, lse, ro, rl, f"chunked prefill layer {layer_type} window {window}")
 
 
 @pytest.mark.parametrize("layer_type", [SWA, GA])
