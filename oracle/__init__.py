@@ -67,6 +67,14 @@ class Oracle:
                                              _P, _P, _P, _P, _P, _I]
         lib.oracle_kv_append.restype = _I
         lib.oracle_kv_append.argtypes = [_I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P]
+        lib.oracle_decode_paged.restype = _I
+        lib.oracle_decode_paged.argtypes = [_I, _I, _I, _I, _F, _F, _P, _P, _P, _P, _P, _P, _I, _I, _I64, _P, _I,
+                                            _P, _P, _P, _I]
+        lib.oracle_prefill_chunk_paged.restype = _I
+        lib.oracle_prefill_chunk_paged.argtypes = [_I, _I, _I, _I, _F, _F, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I,
+                                                   _I64, _P, _P, _P, _P, _I]
+        lib.oracle_kv_append_paged.restype = _I
+        lib.oracle_kv_append_paged.argtypes = [_I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I64]
         lib.oracle_default_threads.restype = _I
         lib.oracle_default_threads.argtypes = []
         self.lib = lib
@@ -202,6 +210,85 @@ class Oracle:
                                              cu.shape[0] - 1, self._ptr(k_cache), self._ptr(v_cache),
                                              self._ptr(base), self._ptr(cap)))
 
+
+    # -- paged GA pool ----------------------------------------------------
+    @staticmethod
+    def _table(block_table, page_size, k_cache):
+        tb = np.ascontiguousarray(block_table, dtype=np.int32)
+        if tb.ndim != 2:
+            raise ValueError("block_table is [batch][max_blocks]")
+        if k_cache.shape[0] % page_size:
+            raise ValueError("a paged pool holds whole pages")
+        return tb, tb.shape[1], k_cache.shape[0] // page_size
+
+    def decode_paged(self, q, k_new, v_new, k_pool, v_pool, block_table, page_size: int, ctx_lens, *,
+                     scale: float, value_scale: float = 1.0, sink=None, nthreads: int = 0):
+        """GA decode over a paged pool [num_pages*page_size][Hkv][D]: position j of sequence b is row
+        block_table[b][j // page_size] * page_size + j % page_size.  Returns (out, lse) as decode."""
+        q = np.ascontiguousarray(q)
+        batch, hq, dqk = q.shape
+        hkv, dv = v_new.shape[1], v_new.shape[2]
+        q = self._u16(q, (hq, dqk))
+        kn = self._u16(k_new, (hkv, dqk))
+        vn = self._u16(v_new, (hkv, dv))
+        kc = self._u16(k_pool, (hkv, dqk))
+        vc = self._u16(v_pool, (hkv, dv))
+        tb, mb, npages = self._table(block_table, page_size, kc)
+        ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+        sk = None if sink is None else np.ascontiguousarray(sink, dtype=np.float32)
+        out = np.empty((batch, hq, dv), np.float64)
+        lse = np.empty((batch, hq), np.float64)
+        nth = nthreads if nthreads > 0 else self.default_threads()
+        rc = self.lib.oracle_decode_paged(hq, hkv, dqk, dv, scale, value_scale, self._ptr(q), self._ptr(kn),
+                                          self._ptr(vn), self._ptr(kc), self._ptr(vc), self._ptr(tb), mb,
+                                          page_size, npages, self._ptr(ctx), batch, self._ptr(sk), self._ptr(out),
+                                          self._ptr(lse), nth)
+        if rc != OK:
+            raise ValueError(f"oracle_decode_paged rejected its arguments (status {rc})")
+        return out, lse
+
+    def prefill_chunk_paged(self, q, k, v, cu_newlens, k_pool, v_pool, block_table, page_size: int, ctx_lens, *,
+                            scale: float, value_scale: float = 1.0, sink=None, nthreads: int = 0):
+        """GA chunked prefill whose cached positions live in a paged pool (as decode_paged)."""
+        q = np.ascontiguousarray(q)
+        hq, dqk = q.shape[1], q.shape[2]
+        hkv, dv = k.shape[1], v.shape[2]
+        q = self._u16(q, (hq, dqk))
+        k = self._u16(k, (hkv, dqk))
+        v = self._u16(v, (hkv, dv))
+        kc = self._u16(k_pool, (hkv, dqk))
+        vc = self._u16(v_pool, (hkv, dv))
+        tb, mb, npages = self._table(block_table, page_size, kc)
+        cu = np.ascontiguousarray(cu_newlens, dtype=np.int32)
+        batch = cu.shape[0] - 1
+        ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+        sk = None if sink is None else np.ascontiguousarray(sink, dtype=np.float32)
+        tn = int(cu[-1])
+        out = np.empty((tn, hq, dv), np.float64)
+        lse = np.empty((tn, hq), np.float64)
+        nth = nthreads if nthreads > 0 else self.default_threads()
+        rc = self.lib.oracle_prefill_chunk_paged(hq, hkv, dqk, dv, scale, value_scale, self._ptr(q), self._ptr(k),
+                                                 self._ptr(v), self._ptr(cu), batch, self._ptr(kc), self._ptr(vc),
+                                                 self._ptr(tb), mb, page_size, npages, self._ptr(ctx), self._ptr(sk),
+                                                 self._ptr(out), self._ptr(lse), nth)
+        if rc != OK:
+            raise ValueError(f"oracle_prefill_chunk_paged rejected its arguments (status {rc})")
+        return out, lse
+
+    def kv_append_paged(self, k, v, cu_newlens, ctx_lens, k_pool, v_pool, block_table, page_size: int) -> int:
+        """Writes new tokens into a paged pool in place; returns the status code."""
+        k = np.ascontiguousarray(k)
+        v = np.ascontiguousarray(v)
+        hkv, dqk, dv = k.shape[1], k.shape[2], v.shape[2]
+        for c in (k_pool, v_pool):
+            if not (c.flags["C_CONTIGUOUS"] and c.dtype == np.uint16):
+                raise TypeError("caches must be C-contiguous uint16 arrays")
+        tb, mb, npages = self._table(block_table, page_size, k_pool)
+        cu = np.ascontiguousarray(cu_newlens, dtype=np.int32)
+        ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+        return int(self.lib.oracle_kv_append_paged(hkv, dqk, dv, self._ptr(k), self._ptr(v), self._ptr(cu),
+                                                   self._ptr(ctx), cu.shape[0] - 1, self._ptr(k_pool),
+                                                   self._ptr(v_pool), self._ptr(tb), mb, page_size, npages))
 
 _default: Optional[Oracle] = None
 

@@ -230,12 +230,24 @@ int oracle_prefill(int hq, int hkv, int dqk, int dv, int layer_type, int window,
 /* Decode: one new token per sequence at position p = ctx_lens[b].          */
 /* Cache readers, written from the layout definitions:                      */
 /*   SWA ring  [B][R][Hkv][D], R = W - 1 slots; position j lives in slot j mod R.
- *   GA pool   [N][Hkv][D]; position j of sequence b lives at row base_b + j. */
+ *   GA pool   [N][Hkv][D]; position j of sequence b lives at row base_b + j.
+ *   GA paged pool [num_pages * P][Hkv][D], P rows per page: block i of
+ *             sequence b (positions i*P .. i*P + P-1) is page table[b][i], so
+ *             position j lives at row table[b][j / P] * P + j mod P.  (Paging is
+ *             a serving layout of the same cache, not something the model
+ *             defines; it changes where rows live, not what is computed.) */
+
+typedef struct {
+    const int32_t* table;  /* [batch][max_blocks] */
+    int max_blocks, page_size;
+    int64_t num_pages;
+} pages_t;
 
 typedef struct {
     const dims_t* d;
     const uint16_t *q, *k_new, *v_new, *k_cache, *v_cache;
     const int64_t* kv_base;
+    const pages_t* pages;
     const int32_t* ctx;
     int batch, ring;
     const float* sink;
@@ -244,18 +256,39 @@ typedef struct {
     pthread_mutex_t mu;
 } decode_job_t;
 
-/* Row of cached position j of sequence b, KV head g, in the ring or pool. */
+/* Pool row of position j of sequence b in a paged pool. */
+static int64_t paged_row(const pages_t* pg, int b, int64_t j) {
+    int64_t page = pg->table[(size_t)b * pg->max_blocks + (size_t)(j / pg->page_size)];
+    return page * pg->page_size + j % pg->page_size;
+}
+
+/* Row of cached position j of sequence b, KV head g, in the ring, the pool or
+ * the paged pool (pages != NULL). */
 static const uint16_t* cached_row(const dims_t* d, const uint16_t* cache, int ring, const int64_t* kv_base,
-                                  int b, int j, int g, int isv) {
+                                  const pages_t* pages, int b, int j, int g, int isv) {
     int D = isv ? d->dv : d->dqk;
     size_t row;
     if (d->layer_type == ORACLE_SWA) row = (size_t)b * ring + (size_t)(j % ring);
+    else if (pages) row = (size_t)paged_row(pages, b, j);
     else row = (size_t)(kv_base[b] + j);
     return cache + (row * d->hkv + g) * D;
 }
 
 static const uint16_t* cache_row(const decode_job_t* jb, int b, int j, int g, int isv) {
-    return cached_row(jb->d, isv ? jb->v_cache : jb->k_cache, jb->ring, jb->kv_base, b, j, g, isv);
+    return cached_row(jb->d, isv ? jb->v_cache : jb->k_cache, jb->ring, jb->kv_base, jb->pages, b, j, g, isv);
+}
+
+/* Every block holding a position below npos[b] maps to a page of the pool. */
+static int pages_cover(const pages_t* pg, const int32_t* npos, int batch) {
+    if (!pg->table || pg->max_blocks < 1 || pg->page_size < 1 || pg->num_pages < 1) return 0;
+    for (int b = 0; b < batch; ++b) {
+        if (npos[b] > (int64_t)pg->max_blocks * pg->page_size) return 0;
+        for (int i = 0; (int64_t)i * pg->page_size < npos[b]; ++i) {
+            int32_t page = pg->table[(size_t)b * pg->max_blocks + i];
+            if (page < 0 || page >= pg->num_pages) return 0;
+        }
+    }
+    return 1;
 }
 
 static void* decode_worker(void* arg) {
@@ -293,6 +326,29 @@ static void* decode_worker(void* arg) {
     return NULL;
 }
 
+static int decode_impl(const dims_t* d, const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                       const uint16_t* k_cache, const uint16_t* v_cache, int ring_slots, const int64_t* kv_base,
+                       const pages_t* pages, const int32_t* ctx_lens, int batch, const float* sink, double* out,
+                       double* lse, int nthreads) {
+    if (!check_dims(d) || batch < 1 || !q || !k_new || !v_new || !ctx_lens || !out || !lse) return ORACLE_EINVAL;
+    if (d->layer_type == ORACLE_SWA && ring_slots != d->window - 1) return ORACLE_EINVAL;
+    if (d->layer_type == ORACLE_GA && !kv_base && !pages) return ORACLE_EINVAL;
+    for (int b = 0; b < batch; ++b) {
+        if (ctx_lens[b] < 0) return ORACLE_EINVAL;
+        if (ctx_lens[b] > 0 && (!k_cache || !v_cache)) return ORACLE_EINVAL;
+    }
+    if (pages && !pages_cover(pages, ctx_lens, batch)) return ORACLE_EINVAL;
+    decode_job_t jb;
+    memset(&jb, 0, sizeof jb);
+    jb.d = d; jb.q = q; jb.k_new = k_new; jb.v_new = v_new; jb.k_cache = k_cache; jb.v_cache = v_cache;
+    jb.kv_base = kv_base; jb.pages = pages; jb.ctx = ctx_lens; jb.batch = batch; jb.ring = ring_slots;
+    jb.sink = sink; jb.out = out; jb.lse = lse;
+    pthread_mutex_init(&jb.mu, NULL);
+    run_threads(decode_worker, &jb, nthreads);
+    pthread_mutex_destroy(&jb.mu);
+    return ORACLE_OK;
+}
+
 /* Decode attention for one new token per sequence.  SWA reads the ring
  * (ring_slots = W - 1 required), GA reads the pool at kv_base[b] + j. */
 int oracle_decode(int hq, int hkv, int dqk, int dv, int layer_type, int window,
@@ -302,22 +358,23 @@ int oracle_decode(int hq, int hkv, int dqk, int dv, int layer_type, int window,
                   const int64_t* kv_base, const int32_t* ctx_lens, int batch,
                   const float* sink, double* out, double* lse, int nthreads) {
     dims_t d = {hq, hkv, dqk, dv, layer_type, window, (double)scale, (double)value_scale};
-    if (!check_dims(&d) || batch < 1 || !q || !k_new || !v_new || !ctx_lens || !out || !lse) return ORACLE_EINVAL;
-    if (layer_type == ORACLE_SWA && ring_slots != window - 1) return ORACLE_EINVAL;
-    if (layer_type == ORACLE_GA && !kv_base) return ORACLE_EINVAL;
-    for (int b = 0; b < batch; ++b) {
-        if (ctx_lens[b] < 0) return ORACLE_EINVAL;
-        if (ctx_lens[b] > 0 && (!k_cache || !v_cache)) return ORACLE_EINVAL;
-    }
-    decode_job_t jb;
-    memset(&jb, 0, sizeof jb);
-    jb.d = &d; jb.q = q; jb.k_new = k_new; jb.v_new = v_new; jb.k_cache = k_cache; jb.v_cache = v_cache;
-    jb.kv_base = kv_base; jb.ctx = ctx_lens; jb.batch = batch; jb.ring = ring_slots; jb.sink = sink;
-    jb.out = out; jb.lse = lse;
-    pthread_mutex_init(&jb.mu, NULL);
-    run_threads(decode_worker, &jb, nthreads);
-    pthread_mutex_destroy(&jb.mu);
-    return ORACLE_OK;
+    return decode_impl(&d, q, k_new, v_new, k_cache, v_cache, ring_slots, kv_base, NULL, ctx_lens, batch, sink,
+                       out, lse, nthreads);
+}
+
+/* GA decode over a paged pool: block_table [batch][max_blocks] maps block i
+ * of sequence b to a page of page_size rows.  Every block below ctx_lens[b]
+ * must map to a page in [0, num_pages) (ORACLE_EINVAL otherwise). */
+int oracle_decode_paged(int hq, int hkv, int dqk, int dv, float scale, float value_scale,
+                        const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                        const uint16_t* k_cache, const uint16_t* v_cache,
+                        const int32_t* block_table, int max_blocks, int page_size, int64_t num_pages,
+                        const int32_t* ctx_lens, int batch, const float* sink, double* out, double* lse,
+                        int nthreads) {
+    dims_t d = {hq, hkv, dqk, dv, ORACLE_GA, 0, (double)scale, (double)value_scale};
+    pages_t pg = {block_table, max_blocks, page_size, num_pages};
+    return decode_impl(&d, q, k_new, v_new, k_cache, v_cache, 0, NULL, &pg, ctx_lens, batch, sink, out, lse,
+                       nthreads);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -334,6 +391,7 @@ typedef struct {
     const uint16_t *q, *k, *v, *k_cache, *v_cache;
     const int32_t* cu;
     const int64_t* kv_base;
+    const pages_t* pages;
     const int32_t* ctx;
     int batch, ring, maxkeys;
     const float* sink;
@@ -364,8 +422,8 @@ static void* chunk_worker(void* arg) {
         int n = 0;
         for (int j = lo; j <= p; ++j, ++n) {
             if (j < c) {
-                kr[n] = cached_row(d, jb->k_cache, jb->ring, jb->kv_base, b, j, g, 0);
-                vr[n] = cached_row(d, jb->v_cache, jb->ring, jb->kv_base, b, j, g, 1);
+                kr[n] = cached_row(d, jb->k_cache, jb->ring, jb->kv_base, jb->pages, b, j, g, 0);
+                vr[n] = cached_row(d, jb->v_cache, jb->ring, jb->kv_base, jb->pages, b, j, g, 1);
             } else {
                 size_t row = (size_t)jb->cu[b] + (size_t)(j - c);
                 kr[n] = jb->k + (row * d->hkv + g) * d->dqk;
@@ -381,6 +439,35 @@ static void* chunk_worker(void* arg) {
     return NULL;
 }
 
+static int chunk_impl(const dims_t* d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                      const int32_t* cu_newlens, int batch, const uint16_t* k_cache, const uint16_t* v_cache,
+                      int ring_slots, const int64_t* kv_base, const pages_t* pages, const int32_t* ctx_lens,
+                      const float* sink, double* out, double* lse, int nthreads) {
+    if (!check_dims(d) || batch < 1 || !q || !k || !v || !cu_newlens || !ctx_lens || !out || !lse)
+        return ORACLE_EINVAL;
+    if (d->layer_type == ORACLE_SWA && ring_slots != d->window - 1) return ORACLE_EINVAL;
+    if (d->layer_type == ORACLE_GA && !kv_base && !pages) return ORACLE_EINVAL;
+    if (cu_newlens[0] != 0) return ORACLE_EINVAL;
+    int maxkeys = 1;
+    for (int b = 0; b < batch; ++b) {
+        int n = cu_newlens[b + 1] - cu_newlens[b];
+        if (n < 0 || ctx_lens[b] < 0) return ORACLE_EINVAL;
+        if (ctx_lens[b] > 0 && (!k_cache || !v_cache)) return ORACLE_EINVAL;
+        if (ctx_lens[b] + n > maxkeys) maxkeys = ctx_lens[b] + n;
+    }
+    if (pages && !pages_cover(pages, ctx_lens, batch)) return ORACLE_EINVAL;
+    chunk_job_t jb;
+    memset(&jb, 0, sizeof jb);
+    jb.d = d; jb.q = q; jb.k = k; jb.v = v; jb.k_cache = k_cache; jb.v_cache = v_cache;
+    jb.cu = cu_newlens; jb.kv_base = kv_base; jb.pages = pages; jb.ctx = ctx_lens; jb.batch = batch;
+    jb.ring = ring_slots; jb.maxkeys = maxkeys; jb.sink = sink; jb.out = out; jb.lse = lse;
+    jb.total = cu_newlens[batch];
+    pthread_mutex_init(&jb.mu, NULL);
+    run_threads(chunk_worker, &jb, nthreads);
+    pthread_mutex_destroy(&jb.mu);
+    return ORACLE_OK;
+}
+
 /* q [Tn][hq][dqk], k [Tn][hkv][dqk], v [Tn][hkv][dv] packed by cu_newlens
  * [batch+1]; caches as for decode (SWA ring_slots = W - 1, GA kv_base).
  * out [Tn][hq][dv], lse [Tn][hq]. */
@@ -392,27 +479,23 @@ int oracle_prefill_chunk(int hq, int hkv, int dqk, int dv, int layer_type, int w
                          const int64_t* kv_base, const int32_t* ctx_lens,
                          const float* sink, double* out, double* lse, int nthreads) {
     dims_t d = {hq, hkv, dqk, dv, layer_type, window, (double)scale, (double)value_scale};
-    if (!check_dims(&d) || batch < 1 || !q || !k || !v || !cu_newlens || !ctx_lens || !out || !lse)
-        return ORACLE_EINVAL;
-    if (layer_type == ORACLE_SWA && ring_slots != window - 1) return ORACLE_EINVAL;
-    if (layer_type == ORACLE_GA && !kv_base) return ORACLE_EINVAL;
-    if (cu_newlens[0] != 0) return ORACLE_EINVAL;
-    int maxkeys = 1;
-    for (int b = 0; b < batch; ++b) {
-        int n = cu_newlens[b + 1] - cu_newlens[b];
-        if (n < 0 || ctx_lens[b] < 0) return ORACLE_EINVAL;
-        if (ctx_lens[b] > 0 && (!k_cache || !v_cache)) return ORACLE_EINVAL;
-        if (ctx_lens[b] + n > maxkeys) maxkeys = ctx_lens[b] + n;
-    }
-    chunk_job_t jb;
-    memset(&jb, 0, sizeof jb);
-    jb.d = &d; jb.q = q; jb.k = k; jb.v = v; jb.k_cache = k_cache; jb.v_cache = v_cache;
-    jb.cu = cu_newlens; jb.kv_base = kv_base; jb.ctx = ctx_lens; jb.batch = batch; jb.ring = ring_slots;
-    jb.maxkeys = maxkeys; jb.sink = sink; jb.out = out; jb.lse = lse; jb.total = cu_newlens[batch];
-    pthread_mutex_init(&jb.mu, NULL);
-    run_threads(chunk_worker, &jb, nthreads);
-    pthread_mutex_destroy(&jb.mu);
-    return ORACLE_OK;
+    return chunk_impl(&d, q, k, v, cu_newlens, batch, k_cache, v_cache, ring_slots, kv_base, NULL, ctx_lens, sink,
+                      out, lse, nthreads);
+}
+
+/* GA chunked prefill whose cached positions live in a paged pool (as for
+ * oracle_decode_paged). */
+int oracle_prefill_chunk_paged(int hq, int hkv, int dqk, int dv, float scale, float value_scale,
+                               const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                               const int32_t* cu_newlens, int batch,
+                               const uint16_t* k_cache, const uint16_t* v_cache,
+                               const int32_t* block_table, int max_blocks, int page_size, int64_t num_pages,
+                               const int32_t* ctx_lens, const float* sink, double* out, double* lse,
+                               int nthreads) {
+    dims_t d = {hq, hkv, dqk, dv, ORACLE_GA, 0, (double)scale, (double)value_scale};
+    pages_t pg = {block_table, max_blocks, page_size, num_pages};
+    return chunk_impl(&d, q, k, v, cu_newlens, batch, k_cache, v_cache, 0, NULL, &pg, ctx_lens, sink, out, lse,
+                      nthreads);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -447,6 +530,44 @@ int oracle_kv_append(int hkv, int dqk, int dv, int layer_type, int ring_slots,
             size_t src = (size_t)cu_newlens[b] + i;
             size_t dst = layer_type == ORACLE_SWA ? (size_t)b * ring_slots + (size_t)(pos % ring_slots)
                                                   : (size_t)(kv_base[b] + pos);
+            memcpy(k_cache + dst * krow, k + src * krow, krow * sizeof(uint16_t));
+            memcpy(v_cache + dst * vrow, v + src * vrow, vrow * sizeof(uint16_t));
+        }
+    }
+    return status;
+}
+
+/* KV append into a paged GA pool: position pos of sequence b goes to row
+ * table[b][pos / P] * P + pos mod P.  A sequence whose ctx_lens[b] + n needs
+ * more than max_blocks blocks is skipped whole, and a token whose block maps
+ * outside [0, num_pages) is not written; either makes the status
+ * ORACLE_ECAPACITY. */
+int oracle_kv_append_paged(int hkv, int dqk, int dv, const uint16_t* k, const uint16_t* v,
+                           const int32_t* cu_newlens, const int32_t* ctx_lens, int batch,
+                           uint16_t* k_cache, uint16_t* v_cache,
+                           const int32_t* block_table, int max_blocks, int page_size, int64_t num_pages) {
+    if (hkv <= 0 || dqk <= 0 || dv <= 0 || batch < 1 || !k || !v || !cu_newlens || !ctx_lens || !k_cache ||
+        !v_cache || !block_table || max_blocks < 1 || page_size < 1 || num_pages < 1)
+        return ORACLE_EINVAL;
+    pages_t pg = {block_table, max_blocks, page_size, num_pages};
+    int status = ORACLE_OK;
+    size_t krow = (size_t)hkv * dqk, vrow = (size_t)hkv * dv;
+    for (int b = 0; b < batch; ++b) {
+        int n = cu_newlens[b + 1] - cu_newlens[b];
+        if (n < 0) return ORACLE_EINVAL;
+        if ((int64_t)ctx_lens[b] + n > (int64_t)max_blocks * page_size) {
+            status = ORACLE_ECAPACITY;
+            continue;
+        }
+        for (int i = 0; i < n; ++i) {
+            int64_t pos = (int64_t)ctx_lens[b] + i;
+            int32_t page = block_table[(size_t)b * max_blocks + (size_t)(pos / page_size)];
+            if (page < 0 || page >= num_pages) {
+                status = ORACLE_ECAPACITY;
+                continue;
+            }
+            size_t src = (size_t)cu_newlens[b] + i;
+            size_t dst = (size_t)paged_row(&pg, b, pos);
             memcpy(k_cache + dst * krow, k + src * krow, krow * sizeof(uint16_t));
             memcpy(v_cache + dst * vrow, v + src * vrow, vrow * sizeof(uint16_t));
         }

@@ -468,6 +468,112 @@ def pin_chunks_in_sequence_rebuild_prefill(orc):
         _close(np.concatenate(lses), lf, 1e-13, f"chunks in sequence lse lt={lt}")
 
 
+
+def _paged_from_flat(flats, starts, lengths, page_size, max_blocks, rng, spare=3):
+    """Rearranges flat pools (sequence b at rows starts[b] .. + lengths[b]-1) into
+    paged pools with the blocks on randomly permuted pages (plus spare pages),
+    by plain numpy slicing, one table for all.  Returns (paged pools, block
+    table); unused table entries are -1."""
+    nblk = [(L + page_size - 1) // page_size for L in lengths]
+    npages = sum(nblk) + spare
+    perm = rng.permutation(npages)
+    table = np.full((len(lengths), max_blocks), -1, np.int32)
+    pools = [np.zeros((npages * page_size,) + f.shape[1:], f.dtype) for f in flats]
+    used = 0
+    for b, (s0, L) in enumerate(zip(starts, lengths)):
+        for i in range(nblk[b]):
+            page = int(perm[used])
+            used += 1
+            table[b, i] = page
+            n = min(page_size, L - i * page_size)
+            for pool, f in zip(pools, flats):
+                pool[page * page_size:page * page_size + n] = f[s0 + i * page_size:s0 + i * page_size + n]
+    return pools, table
+
+
+def pin_paged_decode_is_flat_decode(orc):
+    """GA decode over a paged pool whose pages hold the flat pool's rows in a
+    shuffled order equals decode over the flat pool, for page sizes 1, 3, 16
+    and 64 and contexts on and around page boundaries."""
+    ctx = [0, 1, 15, 16, 17, 64, 200]
+    sc = float(np.float32(synth.SOFTMAX_SCALE))
+    x = synth.decode_inputs(ctx, GA, seed=34)
+    base = x.kv_base.numpy()
+    args = (_bits(x.q), _bits(x.k_new), _bits(x.v_new))
+    kc, vc = _bits(x.k_cache), _bits(x.v_cache)
+    od, ld = orc.decode(*args, kc, vc, x.ctx_lens.numpy(), layer_type=GA, scale=sc, sink=x.sink.numpy(),
+                        kv_base=base)
+    rng = np.random.default_rng(34)
+    for P in (1, 3, 16, 64):
+        mb = max((c + P - 1) // P for c in ctx) + 1
+        (kp, vp), tb = _paged_from_flat([kc, vc], base, ctx, P, mb, rng)
+        op, lp = orc.decode_paged(*args, kp, vp, tb, P, x.ctx_lens.numpy(), scale=sc, sink=x.sink.numpy())
+        assert np.array_equal(op, od) and np.array_equal(lp, ld), f"paged decode differs from flat (page {P})"
+
+
+def pin_paged_chunk_is_flat_chunk(orc):
+    """GA chunked prefill with the cached prefixes in a shuffled paged pool
+    equals chunked prefill over the flat pool."""
+    lengths = [40, 170, 64, 33]
+    cached = [0, 33, 64, 32]
+    x = _make(lengths, seed=35)
+    sc = float(np.float32(synth.SOFTMAX_SCALE))
+    qb, kb, vb = _bits(x.q), _bits(x.k), _bits(x.v)
+    cu = x.cu_seqlens.numpy()
+    rest = [L - c for L, c in zip(lengths, cached)]
+    starts = [int(cu[b]) + cached[b] for b in range(len(lengths))]
+    cu_new = np.concatenate([[0], np.cumsum(rest)]).astype(np.int32)
+    # flat pool: the cached prefix of sequence b sits at its packed rows cu[b] ..
+    base = cu[:-1].astype(np.int64)
+    of, lf = orc.prefill_chunk(_pack(qb, rest, starts), _pack(kb, rest, starts), _pack(vb, rest, starts), cu_new,
+                               kb, vb, np.asarray(cached, np.int32), layer_type=GA, scale=sc, sink=x.sink.numpy(),
+                               kv_base=base)
+    for P in (1, 16, 32):
+        mb = max((c + P - 1) // P for c in cached) + 2
+        rng = np.random.default_rng(P)
+        (kp, vp), tb = _paged_from_flat([kb, vb], base, cached, P, mb, rng)
+        op, lp = orc.prefill_chunk_paged(_pack(qb, rest, starts), _pack(kb, rest, starts), _pack(vb, rest, starts),
+                                         cu_new, kp, vp, tb, P, np.asarray(cached, np.int32), scale=sc,
+                                         sink=x.sink.numpy())
+        assert np.array_equal(op, of) and np.array_equal(lp, lf), f"paged chunk differs from flat (page {P})"
+
+
+def pin_paged_append_places_positions(orc):
+    """Appending to a paged pool (bulk, then single tokens) puts position j of
+    sequence b at row table[b][j // P] * P + j % P, checked against a position
+    tag; nothing else is written.  A sequence that would need more than
+    max_blocks blocks is refused whole (filling exactly max_blocks * P is
+    accepted), and a token on an unmapped block is not written."""
+    P, mb = 4, 3
+    table = np.array([[5, 0, 2], [1, -1, 3]], np.int32)  # page -1: unmapped
+    npages = 7
+    kc = np.zeros((npages * P, 1, 2), np.uint16)
+    vc = np.zeros((npages * P, 1, 2), np.uint16)
+    lengths = [12, 6]
+    tags = [np.arange(L, dtype=np.uint16) + 1 + 100 * b for b, L in enumerate(lengths)]
+    pos = [0, 0]
+    for chunk in ((7, 3), (1, 1), (4, 2)):
+        tok = np.zeros((sum(chunk), 1, 2), np.uint16)
+        tok[:, 0, 0] = np.concatenate([tags[b][pos[b]:pos[b] + n] for b, n in enumerate(chunk)])
+        cu = np.array([0, chunk[0], sum(chunk)], np.int32)
+        st = orc.kv_append_paged(tok, tok, cu, np.array(pos, np.int32), kc, vc, table, P)
+        # sequence 1's positions 4..7 sit on the unmapped block 1
+        want = oracle.ECAPACITY if any(4 <= p < 8 for p in range(pos[1], pos[1] + chunk[1])) else oracle.OK
+        assert st == want, f"append status {st}, expected {want}"
+        pos = [p + n for p, n in zip(pos, chunk)]
+    expect = np.zeros(npages * P, np.uint16)
+    for b, L in enumerate(lengths):
+        for j in range(L):
+            page = table[b, j // P]
+            if page >= 0:
+                expect[page * P + j % P] = tags[b][j]
+    assert np.array_equal(kc[:, 0, 0], expect) and np.array_equal(vc[:, 0, 0], expect), "paged append placement"
+    assert not kc[:, 0, 1].any()
+    before = kc.copy()
+    one = np.ones((1, 1, 2), np.uint16)
+    st = orc.kv_append_paged(one, one, np.array([0, 1, 1], np.int32), np.array([12, 0], np.int32), kc, vc, table, P)
+    assert st == oracle.ECAPACITY and np.array_equal(kc, before), "append past max_blocks * page_size not refused"
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]
 
 

@@ -65,6 +65,18 @@ MUTANTS = {
         "            size_t dst = layer_type == ORACLE_SWA ? (size_t)b * ring_slots + (size_t)((pos + 1) % ring_slots)\n"),
     "append capacity check off by one": ("        if (layer_type == ORACLE_GA && (int64_t)ctx_lens[b] + n > kv_capacity[b]) {\n",
                                          "        if (layer_type == ORACLE_GA && (int64_t)ctx_lens[b] + n >= kv_capacity[b]) {\n"),
+    "paged row inside the page from the block index": (
+        "    return page * pg->page_size + j % pg->page_size;\n",
+        "    return page * pg->page_size + (j / pg->page_size) % pg->page_size;\n"),
+    "paged block table rows strided by the page size": (
+        "    int64_t page = pg->table[(size_t)b * pg->max_blocks + (size_t)(j / pg->page_size)];\n",
+        "    int64_t page = pg->table[(size_t)b * pg->page_size + (size_t)(j / pg->page_size)];\n"),
+    "paged append capacity check off by one": (
+        "        if ((int64_t)ctx_lens[b] + n > (int64_t)max_blocks * page_size) {\n",
+        "        if ((int64_t)ctx_lens[b] + n >= (int64_t)max_blocks * page_size) {\n"),
+    "paged append writes tokens on unmapped blocks": (
+        "            if (page < 0 || page >= num_pages) {\n                status = ORACLE_ECAPACITY;\n                continue;\n            }\n",
+        "            if (page >= num_pages) {\n                status = ORACLE_ECAPACITY;\n                continue;\n            }\n"),
     "bf16 widened from the wrong half": ("    uint32_t w = ((uint32_t)bits) << 16;\n", "    uint32_t w = ((uint32_t)bits) << 15;\n"),
 }
 
