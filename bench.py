@@ -147,6 +147,63 @@ def chunk_rows(dims, ga, swa, reps=5):
     return res
 
 
+def paged_rows(dims, dga, ctx, max_ctx, ws, ga, page_size=16, reps=5):
+    """Paged GA pool, timed apart from the step: the decode step's GA attention
+    (128 sequences at the contexts the timed steps left) with the pool in pages
+    of 16 rows on a seeded random page order, next to the same call over the
+    contiguous pool; and the GA chunk (28672 cached + 4096 new) over a paged pool."""
+    dev = "cuda"
+    res = {}
+    ctx_list = [int(c) for c in ctx.cpu()]
+    table, npages = synth.paged_block_table(ctx_list, page_size, seed=1, device=dev)
+    kp = torch.empty((npages * page_size, HKV, DQK), dtype=torch.bfloat16, device=dev)
+    vp = torch.empty((npages * page_size, HKV, DV), dtype=torch.bfloat16, device=dev)
+    for b, c in enumerate(ctx_list):
+        j = torch.arange(c, device=dev)
+        dst = table[b, j // page_size].long() * page_size + j % page_size
+        src = int(dga.kv_base[b]) + j
+        kp[dst] = dga.k_cache[src]
+        vp[dst] = dga.v_cache[src]
+    pages = B.make_pages(table, page_size, npages)
+    Bd = len(ctx_list)
+    out = torch.empty((Bd, HQ, DV), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((Bd, HQ), dtype=torch.float32, device=dev)
+    paged = lambda: B.mimo_attn_decode_paged(dims, dga.q, dga.k_new, dga.v_new, kp, vp, pages, ctx, Bd, max_ctx, 0,
+                                             dga.sink, out, lse, ws)
+    flat = lambda: B.mimo_attn_decode(dims, 1, dga.q, dga.k_new, dga.v_new, dga.k_cache, dga.v_cache, dga.kv_base,
+                                      ctx, Bd, max_ctx, 0, dga.sink, out, lse, ws)
+    ms_p, ms_f = _time_ms(paged, reps), _time_ms(flat, reps)
+    _, nbytes = decode_stats(ctx_list, 1)
+    res["decode_ga_paged"] = {"workload": f"decode step B=128, GA pool in pages of {page_size} (random order)",
+                              "ms": ms_p, "tokens/s": Bd / (ms_p * 1e-3), "GB/s": nbytes / (ms_p * 1e-3) / 1e9,
+                              "frac_hbm_peak": nbytes / (ms_p * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                              "contiguous_ms": ms_f}
+    del kp, vp, table
+    torch.cuda.empty_cache()
+    # GA chunk over a paged pool: 28672 cached positions in pages of 16.
+    c, n = 28672, 4096
+    table, npages = synth.paged_block_table([c], page_size, seed=2, extra_tokens=0, device=dev)
+    kp = torch.empty((npages * page_size, HKV, DQK), dtype=torch.bfloat16, device=dev)
+    vp = torch.empty((npages * page_size, HKV, DV), dtype=torch.bfloat16, device=dev)
+    zero = torch.zeros(1, dtype=torch.int32, device=dev)
+    B.kv_append_paged(ga.k[:c].contiguous(), ga.v[:c].contiguous(), torch.tensor([0, c], dtype=torch.int32,
+                      device=dev), zero, kp, vp, table, page_size, dims=dims)
+    pages = B.make_pages(table, page_size, npages)
+    cu = torch.tensor([0, n], dtype=torch.int32, device=dev)
+    ctxc = torch.full((1,), c, dtype=torch.int32, device=dev)
+    q, k, v = ga.q[c:].contiguous(), ga.k[c:].contiguous(), ga.v[c:].contiguous()
+    out = torch.empty((n, HQ, DV), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((n, HQ), dtype=torch.float32, device=dev)
+    call = lambda: B.mimo_attn_prefill_chunk_paged(dims, q, k, v, cu, 1, n, kp, vp, pages, ctxc, ga.sink, out, lse)
+    ms = _time_ms(call, reps)
+    tfs = (n * c + n * (n + 1) // 2) * HQ * FLOP_PER_TRIPLE / (ms * 1e-3) / 1e12
+    res["prefill_chunk_ga_paged"] = {"workload": f"1 sequence, 28672 cached (pages of {page_size}) + 4096 new",
+                                     "ms": ms, "TFLOP/s": tfs, "frac_mfma_peak": tfs / PEAK_BF16_TFLOPS}
+    del kp, vp, q, k, v, out, lse
+    torch.cuda.empty_cache()
+    return res
+
+
 def _time_ms(call, reps):
     call()
     torch.cuda.synchronize()
@@ -179,10 +236,30 @@ def device_context():
     ms = e0.elapsed_time(e1) / reps
     del src, dst
     torch.cuda.empty_cache()
-    return {"name": props.name, "compute_units": props.multi_processor_count,
+    clock_mhz = _hip_attribute("hipDeviceAttributeClockRate", 5) / 1e3  # kHz -> MHz
+    cus = props.multi_processor_count
+    # 4 SIMDs per CU, 1024 dense bf16 flops per SIMD per clock (v_mfma_f32_32x32x16_bf16: 32768 flops in 32 clocks).
+    peak_from_clock = cus * 4 * 1024 * clock_mhz * 1e6 / 1e12 if clock_mhz > 0 else None
+    return {"name": props.name, "compute_units": cus, "max_clock_MHz": clock_mhz,
+            "bf16_dense_peak_from_clock_TFLOPs": peak_from_clock,
             "copy_GBps": 2 * n / (ms * 1e-3) / 1e9,
             "note": "copy_GBps: torch device-to-device copy of 2 GiB, read + write bytes; peaks used are the spec "
                     "sheet's (2500 TFLOP/s bf16 dense, 8000 GB/s HBM)"}
+
+
+def _hip_attribute(name, value):
+    """hipDeviceGetAttribute(value) on device 0 through the HIP runtime torch loaded; 0 if unavailable."""
+    import ctypes
+    for lib in ("libamdhip64.so", "libamdhip64.so.7", "libamdhip64.so.6"):
+        try:
+            hip = ctypes.CDLL(lib)
+            break
+        except OSError:
+            hip = None
+    if hip is None:
+        return 0
+    out = ctypes.c_int(0)
+    return out.value if hip.hipDeviceGetAttribute(ctypes.byref(out), value, 0) == 0 else 0
 
 
 def cpu_baseline(swa, ga, dga, ctx, budget_s):
@@ -406,8 +483,8 @@ def main():
         "breakdown": breakdown,
         "roofline": roof,
         "device": dev_ctx,
-        # Rows beyond the step (continuing cached sequences); not part of `value`.
-        "next_rows": chunk_rows(dims, ga, swa),
+        # Rows beyond the step (continuing cached sequences, paged pool); not part of `value`.
+        "next_rows": {**chunk_rows(dims, ga, swa), **paged_rows(dims, dga, ctx_ga, max_ctx, ws, ga)},
     }
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample (cpu_baseline)")

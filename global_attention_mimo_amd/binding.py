@@ -26,7 +26,8 @@ MIMO_ERR_WORKSPACE = 3
 MIMO_ERR_HIP = 4
 
 ENTRY_POINTS = ("mimo_attn_prefill", "mimo_attn_prefill_chunk", "mimo_attn_decode_workspace_size",
-                "mimo_attn_decode", "mimo_kv_append", "mimo_status_string", "mimo_last_error", "mimo_abi_version")
+                "mimo_attn_decode", "mimo_kv_append", "mimo_kv_append_paged", "mimo_attn_decode_paged",
+                "mimo_attn_prefill_chunk_paged", "mimo_status_string", "mimo_last_error", "mimo_abi_version")
 
 
 class mimo_attn_dims(ctypes.Structure):
@@ -34,6 +35,11 @@ class mimo_attn_dims(ctypes.Structure):
                 ("head_dim_qk", ctypes.c_int32), ("head_dim_v", ctypes.c_int32),
                 ("sliding_window", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
                 ("value_scale", ctypes.c_float)]
+
+
+class mimo_kv_pages(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("max_blocks", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_pages", ctypes.c_int64)]
 
 
 class MimoError(RuntimeError):
@@ -68,6 +74,15 @@ def lib() -> ctypes.CDLL:
                                        _P, _P, _SZ, _P]
         L.mimo_kv_append.restype = ctypes.c_int
         L.mimo_kv_append.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _P]
+        pages_p = ctypes.POINTER(mimo_kv_pages)
+        L.mimo_kv_append_paged.restype = ctypes.c_int
+        L.mimo_kv_append_paged.argtypes = [dims_p, _P, _P, _P, _P, _I32, _I32, _P, _P, pages_p, _P]
+        L.mimo_attn_decode_paged.restype = ctypes.c_int
+        L.mimo_attn_decode_paged.argtypes = [dims_p, _P, _P, _P, _P, _P, pages_p, _P, _I32, _I32, _I32, _P, _P, _P,
+                                             _P, _SZ, _P]
+        L.mimo_attn_prefill_chunk_paged.restype = ctypes.c_int
+        L.mimo_attn_prefill_chunk_paged.argtypes = [dims_p, _P, _P, _P, _P, _I32, _I32, _P, _P, pages_p, _P, _P, _P,
+                                                    _P, _P]
         L.mimo_status_string.restype = ctypes.c_char_p
         L.mimo_status_string.argtypes = [ctypes.c_int]
         L.mimo_last_error.restype = ctypes.c_char_p
@@ -150,6 +165,41 @@ def mimo_kv_append(dims: mimo_attn_dims, layer_type: int, k, v, cu_newlens, ctx_
                                 _stream(stream)))
 
 
+def make_pages(block_table: torch.Tensor, page_size: int, num_pages: int) -> mimo_kv_pages:
+    """mimo_kv_pages for a [batch][max_blocks] int32 device table (kept alive by the caller)."""
+    if block_table.dtype != torch.int32 or block_table.dim() != 2:
+        raise ValueError("block_table must be a 2-D int32 tensor")
+    return mimo_kv_pages(_ptr(block_table), block_table.shape[1], page_size, num_pages)
+
+
+def _pages_ref(pages: Optional[mimo_kv_pages]):
+    return None if pages is None else ctypes.byref(pages)
+
+
+def mimo_kv_append_paged(dims: mimo_attn_dims, k, v, cu_newlens, ctx_lens, batch: int, total_new: int, k_cache,
+                         v_cache, pages: Optional[mimo_kv_pages], stream=None) -> None:
+    _check(lib().mimo_kv_append_paged(ctypes.byref(dims), _ptr(k), _ptr(v), _ptr(cu_newlens), _ptr(ctx_lens), batch,
+                                      total_new, _ptr(k_cache), _ptr(v_cache), _pages_ref(pages), _stream(stream)))
+
+
+def mimo_attn_decode_paged(dims: mimo_attn_dims, q, k_new, v_new, k_cache, v_cache, pages: Optional[mimo_kv_pages],
+                           ctx_lens, batch: int, max_ctx: int, split_tokens: int, sink, out, lse, workspace,
+                           stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().mimo_attn_decode_paged(ctypes.byref(dims), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                        _ptr(v_cache), _pages_ref(pages), _ptr(ctx_lens), batch, max_ctx,
+                                        split_tokens, _ptr(sink), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+                                        _stream(stream)))
+
+
+def mimo_attn_prefill_chunk_paged(dims: mimo_attn_dims, q, k, v, cu_newlens, num_seqs: int, max_newlen: int, k_cache,
+                                  v_cache, pages: Optional[mimo_kv_pages], ctx_lens, sink, out, lse,
+                                  stream=None) -> None:
+    _check(lib().mimo_attn_prefill_chunk_paged(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_newlens),
+                                               num_seqs, max_newlen, _ptr(k_cache), _ptr(v_cache), _pages_ref(pages),
+                                               _ptr(ctx_lens), _ptr(sink), _ptr(out), _ptr(lse), _stream(stream)))
+
+
 # -- tensor-level conveniences (allocation of outputs + the calls above) -------
 
 def prefill(q, k, v, cu_seqlens, max_seqlen: int, layer_type: int, sink=None, dims=None, out=None, lse=None,
@@ -201,3 +251,44 @@ def kv_append(k, v, cu_newlens, ctx_lens, k_cache, v_cache, layer_type: int, kv_
         total_new = k.shape[0]
     mimo_kv_append(dims, layer_type, k, v, cu_newlens, ctx_lens, cu_newlens.numel() - 1, total_new, k_cache, v_cache,
                    kv_base, kv_capacity, stream)
+
+
+def kv_append_paged(k, v, cu_newlens, ctx_lens, k_pool, v_pool, block_table, page_size: int, dims=None,
+                    total_new: Optional[int] = None, stream=None):
+    dims = dims or make_dims()
+    if total_new is None:
+        total_new = k.shape[0]
+    pages = make_pages(block_table, page_size, k_pool.shape[0] // page_size)
+    mimo_kv_append_paged(dims, k, v, cu_newlens, ctx_lens, cu_newlens.numel() - 1, total_new, k_pool, v_pool, pages,
+                         stream)
+
+
+def decode_paged(q, k_new, v_new, k_pool, v_pool, block_table, page_size: int, ctx_lens, max_ctx: int, sink=None,
+                 split_tokens: int = 0, dims=None, out=None, lse=None, workspace=None, stream=None):
+    dims = dims or make_dims()
+    B = q.shape[0]
+    if out is None:
+        out = torch.empty((B, dims.num_q_heads, dims.head_dim_v), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, dims.num_q_heads), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = mimo_attn_decode_workspace_size(dims, MIMO_LAYER_GA, B, max_ctx, split_tokens)
+        workspace = torch.empty(max(nbytes, 16) // 4 + 4, dtype=torch.float32, device=q.device)
+    pages = make_pages(block_table, page_size, k_pool.shape[0] // page_size)
+    mimo_attn_decode_paged(dims, q, k_new, v_new, k_pool, v_pool, pages, ctx_lens, B, max_ctx, split_tokens, sink,
+                           out, lse, workspace, stream)
+    return out, lse
+
+
+def prefill_chunk_paged(q, k, v, cu_newlens, max_newlen: int, k_pool, v_pool, block_table, page_size: int, ctx_lens,
+                        sink=None, dims=None, out=None, lse=None, stream=None):
+    dims = dims or make_dims()
+    T = q.shape[0]
+    if out is None:
+        out = torch.empty((T, dims.num_q_heads, dims.head_dim_v), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, dims.num_q_heads), dtype=torch.float32, device=q.device)
+    pages = make_pages(block_table, page_size, k_pool.shape[0] // page_size)
+    mimo_attn_prefill_chunk_paged(dims, q, k, v, cu_newlens, cu_newlens.numel() - 1, max_newlen, k_pool, v_pool,
+                                  pages, ctx_lens, sink, out, lse, stream)
+    return out, lse

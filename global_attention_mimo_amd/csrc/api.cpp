@@ -63,6 +63,27 @@ int hip_status(hipError_t e, const char* what) {
     return ok();
 }
 
+// Paged pool description -> internal page table; MIMO_OK or a failure status.
+int check_pages(const mimo_kv_pages* pg, mimo::PageTable* out) {
+    if (!pg) return fail(MIMO_ERR_INVALID_ARG, "pages is NULL");
+    if (!pg->block_table) return fail(MIMO_ERR_INVALID_ARG, "pages->block_table is NULL");
+    if (pg->max_blocks < 1) return fail(MIMO_ERR_INVALID_ARG, "pages->max_blocks %d < 1", pg->max_blocks);
+    if (pg->num_pages < 1) return fail(MIMO_ERR_INVALID_ARG, "pages->num_pages %lld < 1", (long long)pg->num_pages);
+    if (pg->page_size <= 0) return fail(MIMO_ERR_INVALID_ARG, "pages->page_size %d is not positive", pg->page_size);
+    if (pg->page_size < 16 || pg->page_size > 65536 || (pg->page_size & (pg->page_size - 1)))
+        return fail(MIMO_ERR_UNSUPPORTED, "page_size %d is not a power of two in [16, 65536]", pg->page_size);
+    // Pool rows are addressed as (page << shift) in 64 bits, positions in 32.
+    if (pg->num_pages > (INT64_MAX / 65536) / 4096)
+        return fail(MIMO_ERR_INVALID_ARG, "num_pages %lld is implausibly large", (long long)pg->num_pages);
+    int shift = 0;
+    while ((1 << shift) < pg->page_size) ++shift;
+    out->table = pg->block_table;
+    out->max_blocks = pg->max_blocks;
+    out->shift = shift;
+    out->num_pages = pg->num_pages;
+    return MIMO_OK;
+}
+
 int effective_split(int32_t split_tokens) {
     int s = split_tokens <= 0 ? kDefaultSplit : split_tokens;
     if (s > (1 << 30)) s = 1 << 30;
@@ -91,15 +112,24 @@ int mimo_attn_prefill(const mimo_attn_dims* dims, int layer_type, const uint16_t
     return hip_status(mimo::launch_prefill(a, stream), "prefill launch");
 }
 
-int mimo_attn_prefill_chunk(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, const uint16_t* k,
-                            const uint16_t* v, const int32_t* cu_newlens, int32_t num_seqs, int32_t max_newlen,
-                            const uint16_t* k_cache, const uint16_t* v_cache, const int64_t* kv_base,
-                            const int32_t* ctx_lens, const float* sink, uint16_t* out, float* lse,
-                            hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+int prefill_chunk_impl(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, const uint16_t* k,
+                       const uint16_t* v, const int32_t* cu_newlens, int32_t num_seqs, int32_t max_newlen,
+                       const uint16_t* k_cache, const uint16_t* v_cache, const int64_t* kv_base,
+                       const mimo_kv_pages* pages, const int32_t* ctx_lens, const float* sink, uint16_t* out,
+                       float* lse, hipStream_t stream) {
     if (int st = check_dims(dims, layer_type, 2)) return st;
     if (!q || !k || !v || !cu_newlens || !out || !k_cache || !v_cache || !ctx_lens)
         return fail(MIMO_ERR_INVALID_ARG, "q, k, v, cu_newlens, out, k_cache, v_cache and ctx_lens must be non-NULL");
-    if (layer_type == MIMO_LAYER_GA && !kv_base) return fail(MIMO_ERR_INVALID_ARG, "GA needs kv_base");
+    mimo::PageTable pt;
+    if (pages) {
+        if (int st = check_pages(pages, &pt)) return st;
+    } else if (layer_type == MIMO_LAYER_GA && !kv_base) {
+        return fail(MIMO_ERR_INVALID_ARG, "GA needs kv_base");
+    }
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(k_cache) ||
         !aligned16(v_cache))
         return fail(MIMO_ERR_INVALID_ARG, "q, k, v, out and the caches must be 16-byte aligned");
@@ -114,7 +144,31 @@ int mimo_attn_prefill_chunk(const mimo_attn_dims* dims, int layer_type, const ui
     a.v_cache = v_cache;
     a.kv_base = kv_base;
     a.ctx_lens = ctx_lens;
+    a.pages = pt;
     return hip_status(mimo::launch_prefill_chunk(a, stream), "chunked prefill launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int mimo_attn_prefill_chunk(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, const uint16_t* k,
+                            const uint16_t* v, const int32_t* cu_newlens, int32_t num_seqs, int32_t max_newlen,
+                            const uint16_t* k_cache, const uint16_t* v_cache, const int64_t* kv_base,
+                            const int32_t* ctx_lens, const float* sink, uint16_t* out, float* lse,
+                            hipStream_t stream) {
+    return prefill_chunk_impl(dims, layer_type, q, k, v, cu_newlens, num_seqs, max_newlen, k_cache, v_cache, kv_base,
+                              nullptr, ctx_lens, sink, out, lse, stream);
+}
+
+int mimo_attn_prefill_chunk_paged(const mimo_attn_dims* dims, const uint16_t* q, const uint16_t* k,
+                                  const uint16_t* v, const int32_t* cu_newlens, int32_t num_seqs, int32_t max_newlen,
+                                  const uint16_t* k_cache, const uint16_t* v_cache, const mimo_kv_pages* pages,
+                                  const int32_t* ctx_lens, const float* sink, uint16_t* out, float* lse,
+                                  hipStream_t stream) {
+    if (!pages) return fail(MIMO_ERR_INVALID_ARG, "pages is NULL");
+    return prefill_chunk_impl(dims, MIMO_LAYER_GA, q, k, v, cu_newlens, num_seqs, max_newlen, k_cache, v_cache,
+                              nullptr, pages, ctx_lens, sink, out, lse, stream);
 }
 
 size_t mimo_attn_decode_workspace_size(const mimo_attn_dims* dims, int layer_type, int32_t batch, int32_t max_ctx,
@@ -124,10 +178,15 @@ size_t mimo_attn_decode_workspace_size(const mimo_attn_dims* dims, int layer_typ
     return mimo::ga_workspace_bytes(batch, max_ctx, effective_split(split_tokens), dims->num_q_heads);
 }
 
-int mimo_attn_decode(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, const uint16_t* k_new,
-                     const uint16_t* v_new, const uint16_t* k_cache, const uint16_t* v_cache, const int64_t* kv_base,
-                     const int32_t* ctx_lens, int32_t batch, int32_t max_ctx, int32_t split_tokens, const float* sink,
-                     uint16_t* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+int decode_impl(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, const uint16_t* k_new,
+                const uint16_t* v_new, const uint16_t* k_cache, const uint16_t* v_cache, const int64_t* kv_base,
+                const mimo_kv_pages* pages, const int32_t* ctx_lens, int32_t batch, int32_t max_ctx,
+                int32_t split_tokens, const float* sink, uint16_t* out, float* lse, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
     if (int st = check_dims(dims, layer_type, 2)) return st;
     if (!q || !k_new || !v_new || !ctx_lens || !out)
         return fail(MIMO_ERR_INVALID_ARG, "q, k_new, v_new, ctx_lens and out must be non-NULL");
@@ -138,21 +197,33 @@ int mimo_attn_decode(const mimo_attn_dims* dims, int layer_type, const uint16_t*
     if (!k_cache || !v_cache) return fail(MIMO_ERR_INVALID_ARG, "k_cache and v_cache must be non-NULL");
     if (!aligned16(k_cache) || !aligned16(v_cache))
         return fail(MIMO_ERR_INVALID_ARG, "k_cache and v_cache must be 16-byte aligned");
-    // The kernels address a sequence's cache rows with 32-bit byte offsets.
-    const int64_t row_bytes = (int64_t)dims->num_kv_heads * dims->head_dim_qk * 2;
-    const int64_t rows = layer_type == MIMO_LAYER_SWA ? (int64_t)dims->sliding_window : (int64_t)max_ctx + 1;
-    if (rows * row_bytes > INT32_MAX)
-        return fail(MIMO_ERR_UNSUPPORTED, "a sequence's cached keys exceed 2 GiB (%lld rows of %lld bytes)",
-                    (long long)rows, (long long)row_bytes);
     const int split = effective_split(split_tokens);
+    mimo::PageTable pt;
+    if (pages) {
+        if (int st = check_pages(pages, &pt)) return st;
+        // The split kernel preloads the pages of its keys: at most kMaxSplitPages.
+        const int P = pages->page_size;
+        const int span = split % P == 0 ? split / P : split / P + 2;
+        if (span > mimo::kMaxSplitPages)
+            return fail(MIMO_ERR_UNSUPPORTED, "a split of %d keys spans up to %d pages of %d (at most %d)", split,
+                        span, P, mimo::kMaxSplitPages);
+    } else {
+        // The kernels address a sequence's cache rows with 32-bit byte offsets.
+        const int64_t row_bytes = (int64_t)dims->num_kv_heads * dims->head_dim_qk * 2;
+        const int64_t rows = layer_type == MIMO_LAYER_SWA ? (int64_t)dims->sliding_window : (int64_t)max_ctx + 1;
+        if (rows * row_bytes > INT32_MAX)
+            return fail(MIMO_ERR_UNSUPPORTED, "a sequence's cached keys exceed 2 GiB (%lld rows of %lld bytes)",
+                        (long long)rows, (long long)row_bytes);
+    }
     mimo::DecodeArgs a{q, k_new, v_new, k_cache, v_cache, kv_base, ctx_lens, sink, out, lse, workspace, batch,
                        max_ctx, split, dims->num_q_heads, dims->num_kv_heads, dims->sliding_window,
                        dims->softmax_scale, dims->value_scale};
+    a.pages = pt;
     if (layer_type == MIMO_LAYER_SWA) {
         if (batch > INT32_MAX / 2) return fail(MIMO_ERR_UNSUPPORTED, "batch too large");
         return hip_status(mimo::launch_decode_swa(a, stream), "SWA decode launch");
     }
-    if (!kv_base) return fail(MIMO_ERR_INVALID_ARG, "GA decode needs kv_base");
+    if (!kv_base && !pages) return fail(MIMO_ERR_INVALID_ARG, "GA decode needs kv_base");
     if (batch > kMaxGridYZ) return fail(MIMO_ERR_UNSUPPORTED, "GA decode batch %d above %d", batch, kMaxGridYZ);
     const size_t need = mimo::ga_workspace_bytes(batch, max_ctx, split, dims->num_q_heads);
     if (!workspace || workspace_bytes < need)
@@ -162,10 +233,10 @@ int mimo_attn_decode(const mimo_attn_dims* dims, int layer_type, const uint16_t*
     return hip_status(mimo::launch_decode_ga(a, stream), "GA decode launch");
 }
 
-int mimo_kv_append(const mimo_attn_dims* dims, int layer_type, const uint16_t* k, const uint16_t* v,
+int kv_append_impl(const mimo_attn_dims* dims, int layer_type, const uint16_t* k, const uint16_t* v,
                    const int32_t* cu_newlens, const int32_t* ctx_lens, int32_t batch, int32_t total_new,
                    uint16_t* k_cache, uint16_t* v_cache, const int64_t* kv_base, const int64_t* kv_capacity,
-                   hipStream_t stream) {
+                   const mimo_kv_pages* pages, hipStream_t stream) {
     if (int st = check_dims(dims, layer_type, 2)) return st;
     if (!k || !v || !cu_newlens || !ctx_lens || !k_cache || !v_cache)
         return fail(MIMO_ERR_INVALID_ARG, "k, v, cu_newlens, ctx_lens, k_cache and v_cache must be non-NULL");
@@ -173,14 +244,57 @@ int mimo_kv_append(const mimo_attn_dims* dims, int layer_type, const uint16_t* k
         return fail(MIMO_ERR_INVALID_ARG, "k, v, k_cache and v_cache must be 16-byte aligned");
     if (batch < 1) return fail(MIMO_ERR_INVALID_ARG, "batch %d < 1", batch);
     if (total_new < 0) return fail(MIMO_ERR_INVALID_ARG, "total_new %d is negative", total_new);
-    if (layer_type == MIMO_LAYER_GA && (!kv_base || !kv_capacity))
+    mimo::PageTable pt;
+    if (pages) {
+        if (int st = check_pages(pages, &pt)) return st;
+    } else if (layer_type == MIMO_LAYER_GA && (!kv_base || !kv_capacity)) {
         return fail(MIMO_ERR_INVALID_ARG, "GA append needs kv_base and kv_capacity");
+    }
     const int64_t blocks = ((int64_t)total_new * dims->num_kv_heads * 40 + 255) / 256;
     if (blocks > INT32_MAX) return fail(MIMO_ERR_UNSUPPORTED, "append of %d tokens is too large", total_new);
     if (total_new == 0) return ok();
     mimo::AppendArgs a{k, v, cu_newlens, ctx_lens, k_cache, v_cache, kv_base, kv_capacity, batch, total_new,
                        dims->num_kv_heads, dims->sliding_window, layer_type == MIMO_LAYER_SWA};
+    a.pages = pt;
     return hip_status(mimo::launch_kv_append(a, stream), "KV append launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int mimo_attn_decode(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, const uint16_t* k_new,
+                     const uint16_t* v_new, const uint16_t* k_cache, const uint16_t* v_cache, const int64_t* kv_base,
+                     const int32_t* ctx_lens, int32_t batch, int32_t max_ctx, int32_t split_tokens, const float* sink,
+                     uint16_t* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return decode_impl(dims, layer_type, q, k_new, v_new, k_cache, v_cache, kv_base, nullptr, ctx_lens, batch,
+                       max_ctx, split_tokens, sink, out, lse, workspace, workspace_bytes, stream);
+}
+
+int mimo_attn_decode_paged(const mimo_attn_dims* dims, const uint16_t* q, const uint16_t* k_new,
+                           const uint16_t* v_new, const uint16_t* k_cache, const uint16_t* v_cache,
+                           const mimo_kv_pages* pages, const int32_t* ctx_lens, int32_t batch, int32_t max_ctx,
+                           int32_t split_tokens, const float* sink, uint16_t* out, float* lse, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+    if (!pages) return fail(MIMO_ERR_INVALID_ARG, "pages is NULL");
+    return decode_impl(dims, MIMO_LAYER_GA, q, k_new, v_new, k_cache, v_cache, nullptr, pages, ctx_lens, batch,
+                       max_ctx, split_tokens, sink, out, lse, workspace, workspace_bytes, stream);
+}
+
+int mimo_kv_append(const mimo_attn_dims* dims, int layer_type, const uint16_t* k, const uint16_t* v,
+                   const int32_t* cu_newlens, const int32_t* ctx_lens, int32_t batch, int32_t total_new,
+                   uint16_t* k_cache, uint16_t* v_cache, const int64_t* kv_base, const int64_t* kv_capacity,
+                   hipStream_t stream) {
+    return kv_append_impl(dims, layer_type, k, v, cu_newlens, ctx_lens, batch, total_new, k_cache, v_cache, kv_base,
+                          kv_capacity, nullptr, stream);
+}
+
+int mimo_kv_append_paged(const mimo_attn_dims* dims, const uint16_t* k, const uint16_t* v,
+                         const int32_t* cu_newlens, const int32_t* ctx_lens, int32_t batch, int32_t total_new,
+                         uint16_t* k_cache, uint16_t* v_cache, const mimo_kv_pages* pages, hipStream_t stream) {
+    if (!pages) return fail(MIMO_ERR_INVALID_ARG, "pages is NULL");
+    return kv_append_impl(dims, MIMO_LAYER_GA, k, v, cu_newlens, ctx_lens, batch, total_new, k_cache, v_cache,
+                          nullptr, nullptr, pages, stream);
 }
 
 const char* mimo_status_string(int status) {

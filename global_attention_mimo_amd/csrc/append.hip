@@ -6,7 +6,8 @@
 // SWA layers need only the last sliding_window-1 = 128 positions (the new
 // token is the 129th key), so their cache is a ring of 128 slots per sequence,
 // position j in slot j mod 128; GA layers keep every position in a pool row
-// kv_base[b] + j.
+// kv_base[b] + j, or, in a paged pool, in row j mod P of the page the block
+// table gives for block j / P.
 //
 // One thread moves one 16-byte chunk: a token is Hkv*24 chunks of K and
 // Hkv*16 chunks of V, so consecutive threads copy consecutive bytes of a row.
@@ -23,7 +24,8 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const int32_t* __restrict__ cu_newlens,
     const int32_t* __restrict__ ctx_lens, int batch, int total_new, uint16_t* __restrict__ k_cache,
     uint16_t* __restrict__ v_cache, const int64_t* __restrict__ kv_base, const int64_t* __restrict__ kv_capacity,
-    int hkv, int ring, int swa) {
+    int hkv, int ring, int swa, const int32_t* __restrict__ block_table, int max_blocks, int page_shift,
+    long long num_pages) {
     const int kchunks = hkv * (kDqk / 8), per_tok = hkv * ((kDqk + kDv) / 8);
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t tok = idx / per_tok;
@@ -43,6 +45,11 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     if (swa) {
         if (pos < ctx + n - ring) return;  // overwritten later in this same append
         row = (int64_t)b * ring + pos % ring;
+    } else if (block_table) {
+        if (ctx + n > ((int64_t)max_blocks << page_shift)) return;  // the whole sequence is refused
+        const int64_t page = block_table[(int64_t)b * max_blocks + (pos >> page_shift)];
+        if (page < 0 || page >= num_pages) return;  // unmapped block: not written
+        row = (page << page_shift) | (pos & ((1 << page_shift) - 1));
     } else {
         if (ctx + n > kv_capacity[b]) return;  // the whole sequence is refused
         row = kv_base[b] + pos;
@@ -63,7 +70,8 @@ hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream) {
     const int64_t blocks = (threads + 255) / 256;
     hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a.k, a.v, a.cu_newlens,
                        a.ctx_lens, a.batch, a.total_new, a.k_cache, a.v_cache, a.kv_base, a.kv_capacity, a.hkv,
-                       a.window - 1, a.swa ? 1 : 0);
+                       a.window - 1, a.swa ? 1 : 0, a.pages.table, a.pages.max_blocks, a.pages.shift,
+                       a.pages.num_pages);
     return hipGetLastError();
 }
 

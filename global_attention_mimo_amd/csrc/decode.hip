@@ -29,6 +29,13 @@
 // partial (m, l, O) without the sink; the split holding position p adds the
 // new token as its last tile.  A second kernel merges the splits of each
 // (sequence, head), adds the sink exactly once, and writes O and LSE.
+//
+// Paged GA pool: pages of P >= 16 rows (a power of two), so each 16-key half
+// of a tile lies in one page and gets a descriptor of its own.  The split's
+// page numbers (at most 128) are loaded once per wave into two registers and
+// picked out per half-tile with a lane read, so the streaming loop issues no
+// dependent table loads; tiles, their order and the arithmetic are those of
+// the contiguous pool.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -52,6 +59,13 @@ struct TileSrc {
     rsrc_t k, v;     // descriptors; bytes past their record count read as zero
     int koff, voff;  // byte offset of the tile's first key row (wave-uniform)
     int nvalid;      // keys [0, nvalid) of the tile are in the key set
+};
+
+// A tile of a paged pool: keys 0..15 and 16..31 through descriptors of their
+// own (each half lies inside one page), all offsets zero.
+struct PagedTileSrc {
+    rsrc_t k[2], v[2];
+    int nvalid;
 };
 
 // Per-wave running state for 16 heads.  Lane l owns head (l % 16); o[db][r]
@@ -90,6 +104,23 @@ __device__ __forceinline__ void issue_k(const TileSrc& t, const LaneOffsets& lo,
 __device__ __forceinline__ void issue_v(const TileSrc& t, const LaneOffsets& lo, int rowv, u32x4 (&v)[kTile / 4]) {
 #pragma unroll
     for (int i = 0; i < kTile / 4; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(t.v, lo.v, t.voff + 4 * i * rowv, 0);
+}
+
+// Paged halves: rows l%16 of each half for K; V load i takes key 4i + l/16,
+// i.e. half i/4 at row 4(i%4) + l/16.
+__device__ __forceinline__ void issue_k(const PagedTileSrc& t, const LaneOffsets& lo, u32x4 (&k)[12]) {
+#pragma unroll
+    for (int st = 0; st < kDqk / 32; ++st) {
+        k[st] = __builtin_amdgcn_raw_buffer_load_b128(t.k[0], lo.k0 + 64 * st, 0, 0);
+        k[6 + st] = __builtin_amdgcn_raw_buffer_load_b128(t.k[1], lo.k0 + 64 * st, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void issue_v(const PagedTileSrc& t, const LaneOffsets& lo, int rowv,
+                                        u32x4 (&v)[kTile / 4]) {
+#pragma unroll
+    for (int i = 0; i < kTile / 4; ++i)
+        v[i] = __builtin_amdgcn_raw_buffer_load_b128(t.v[i / 4], lo.v, 4 * (i % 4) * rowv, 0);
 }
 
 // V rows to the wave's LDS tile: row 4i + G, logical chunk lane%16 stored at
@@ -170,14 +201,14 @@ __device__ __forceinline__ void run_tiles(WaveAcc& acc, const bf16x8 (&qf)[kDqk 
     u32x4 kr[D + 1][12], vr[D + 1][kTile / 4];
 #pragma unroll
     for (int j = 0; j < D; ++j) {
-        const TileSrc t = get(j);
+        const auto t = get(j);
         issue_k(t, lo, kr[j]);
         issue_v(t, lo, rowv, vr[j]);
     }
     for (int i0 = 0; i0 < ntiles; i0 += D + 1) {
 #pragma unroll
         for (int j = 0; j <= D; ++j) {
-            const TileSrc t = get(i0 + j + D);
+            const auto t = get(i0 + j + D);
             issue_k(t, lo, kr[(j + D) % (D + 1)]);
             issue_v(t, lo, rowv, vr[(j + D) % (D + 1)]);
             stage_v(vr[j], vbuf, lane);
@@ -320,11 +351,15 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 }
 
 // ---------------------------------------------------------------------------
+// PAGED: pool rows come through block_table (page_shift = log2 P); otherwise
+// sequence b's rows start at kv_base[b].
+template <bool PAGED>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void ga_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const uint16_t* __restrict__ pool_k, const uint16_t* __restrict__ pool_v, const int64_t* __restrict__ kv_base,
     const int32_t* __restrict__ ctx_lens, int hq, int hkv, int split, int nsplit, float c_log2,
-    float* __restrict__ ws_ml, float* __restrict__ ws_o) {
+    float* __restrict__ ws_ml, float* __restrict__ ws_o, const int32_t* __restrict__ block_table, int max_blocks,
+    int page_shift, long long num_pages) {
     __shared__ __attribute__((aligned(1024))) char lds[kBlockLdsBytes];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -340,26 +375,60 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 
     bf16x8 qf[kDqk / 32];
     load_q(qf, q, b, g, hq, lane);
-    const size_t base = (size_t)kv_base[b];
-    const rsrc_t pk = make_rsrc(pool_k + base * hkv * kDqk, (uint32_t)p * rowk);
-    const rsrc_t pv = make_rsrc(pool_v + base * hkv * kDv, (uint32_t)p * rowv);
     const rsrc_t nk = make_rsrc(k_new + (size_t)b * hkv * kDqk, (uint32_t)rowk);
     const rsrc_t nv = make_rsrc(v_new + (size_t)b * hkv * kDv, (uint32_t)rowv);
     const int npool = (kend - k0 + kTile - 1) / kTile;
     const int ntiles = npool + (p < k1 ? 1 : 0);
     const rsrc_t none = make_rsrc(k_new, 0);
-    auto get = [&](int i) -> TileSrc {
-        if (i < npool) {
-            const int j0 = k0 + i * kTile;
-            return TileSrc{pk, pv, j0 * rowk, j0 * rowv, min(kend - j0, kTile)};
-        }
-        if (i < ntiles) return TileSrc{nk, nv, 0, 0, 1};
-        return TileSrc{none, none, 0, 0, 0};
-    };
     const LaneOffsets lo = lane_offsets(lane, g, rowk, rowv);
     WaveAcc acc;
     acc_init(acc);
-    run_tiles<kGaDepth>(acc, qf, lds + wave * kVTileBytes, ntiles, get, lo, rowv, c_log2, lane);
+    if constexpr (PAGED) {
+        // Pages of blocks first .. first+127 of this split, two per lane; -1
+        // past the table's end.
+        const int first = k0 >> page_shift;
+        const int32_t* tb = block_table + (size_t)b * max_blocks;
+        const int pg_lo = first + lane < max_blocks ? tb[first + lane] : -1;
+        const int pg_hi = first + 64 + lane < max_blocks ? tb[first + 64 + lane] : -1;
+        const int pmask = (1 << page_shift) - 1;
+        // Descriptor of the n valid keys from position j on (inside one page);
+        // no records when n <= 0 or the block is unmapped (reads as zero keys).
+        // Branch-free: the page number is picked with lane reads and selects.
+        auto half = [&](const uint16_t* pool, int row_elems, int j, int n) -> rsrc_t {
+            const int blk = (j >> page_shift) - first;  // 0..127 whenever n > 0 (host split check)
+            const int pa = __builtin_amdgcn_readlane(pg_lo, blk & 63);
+            const int pb = __builtin_amdgcn_readlane(pg_hi, blk & 63);
+            const int pg = (blk & 64) ? pb : pa;
+            const bool ok = n > 0 && pg >= 0 && pg < num_pages;
+            const size_t row = ((size_t)(ok ? pg : 0) << page_shift) + (size_t)(j & pmask);
+            return make_rsrc(pool + row * row_elems, ok ? (uint32_t)n * (uint32_t)(row_elems * 2) : 0u);
+        };
+        auto get = [&](int i) -> PagedTileSrc {
+            if (i < npool) {
+                const int j0 = k0 + i * kTile;
+                const int n = min(kend - j0, kTile);
+                return PagedTileSrc{{half(pool_k, hkv * kDqk, j0, min(n, 16)), half(pool_k, hkv * kDqk, j0 + 16, n - 16)},
+                                    {half(pool_v, hkv * kDv, j0, min(n, 16)), half(pool_v, hkv * kDv, j0 + 16, n - 16)},
+                                    n};
+            }
+            if (i < ntiles) return PagedTileSrc{{nk, none}, {nv, none}, 1};
+            return PagedTileSrc{{none, none}, {none, none}, 0};
+        };
+        run_tiles<kGaDepth>(acc, qf, lds + wave * kVTileBytes, ntiles, get, lo, rowv, c_log2, lane);
+    } else {
+        const size_t base = (size_t)kv_base[b];
+        const rsrc_t pk = make_rsrc(pool_k + base * hkv * kDqk, (uint32_t)p * rowk);
+        const rsrc_t pv = make_rsrc(pool_v + base * hkv * kDv, (uint32_t)p * rowv);
+        auto get = [&](int i) -> TileSrc {
+            if (i < npool) {
+                const int j0 = k0 + i * kTile;
+                return TileSrc{pk, pv, j0 * rowk, j0 * rowv, min(kend - j0, kTile)};
+            }
+            if (i < ntiles) return TileSrc{nk, nv, 0, 0, 1};
+            return TileSrc{none, none, 0, 0, 0};
+        };
+        run_tiles<kGaDepth>(acc, qf, lds + wave * kVTileBytes, ntiles, get, lo, rowv, c_log2, lane);
+    }
     acc.l += __shfl_xor(acc.l, 16);
     acc.l += __shfl_xor(acc.l, 32);
 
@@ -428,9 +497,11 @@ hipError_t launch_decode_ga(const DecodeArgs& a, hipStream_t stream) {
     const int nsplit = ga_num_splits(a.max_ctx, a.split);
     float* ws_ml = static_cast<float*>(a.workspace);
     float* ws_o = ws_ml + (size_t)a.batch * nsplit * a.hq * 2;
-    hipLaunchKernelGGL(ga_split_kernel, dim3(nsplit, a.batch, (a.hkv + 3) / 4), dim3(256), 0, stream, a.q, a.k_new,
-                       a.v_new, a.k_cache, a.v_cache, a.kv_base, a.ctx_lens, a.hq, a.hkv, a.split, nsplit,
-                       a.softmax_scale * kLog2e, ws_ml, ws_o);
+    hipLaunchKernelGGL(a.pages.table ? ga_split_kernel<true> : ga_split_kernel<false>,
+                       dim3(nsplit, a.batch, (a.hkv + 3) / 4), dim3(256), 0, stream, a.q, a.k_new, a.v_new,
+                       a.k_cache, a.v_cache, a.kv_base, a.ctx_lens, a.hq, a.hkv, a.split, nsplit,
+                       a.softmax_scale * kLog2e, ws_ml, ws_o, a.pages.table, a.pages.max_blocks, a.pages.shift,
+                       a.pages.num_pages);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(ga_combine_kernel, dim3(a.batch, (a.hq + kGroup - 1) / kGroup), dim3(256), 0, stream, ws_ml, ws_o,

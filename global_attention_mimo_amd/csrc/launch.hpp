@@ -6,6 +6,16 @@
 
 namespace mimo {
 
+// A paged GA pool: position j of sequence b lives in row
+// table[b * max_blocks + (j >> shift)] << shift | (j & ((1 << shift) - 1)).
+// table == nullptr means the contiguous pool addressed through kv_base.
+struct PageTable {
+    const int32_t* table = nullptr;
+    int max_blocks = 0;
+    int shift = 0;
+    long long num_pages = 0;
+};
+
 struct PrefillArgs {
     const uint16_t* q;
     const uint16_t* k;
@@ -22,6 +32,7 @@ struct PrefillArgs {
     const uint16_t* v_cache = nullptr;
     const int64_t* kv_base = nullptr;
     const int32_t* ctx_lens = nullptr;
+    PageTable pages;
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_chunk(const PrefillArgs& a, hipStream_t stream);
@@ -40,7 +51,10 @@ struct DecodeArgs {
     void* workspace;
     int batch, max_ctx, split, hq, hkv, window;
     float softmax_scale, value_scale;
+    PageTable pages;
 };
+// Pages a GA split kernel preloads per workgroup (two per lane of a wave).
+constexpr int kMaxSplitPages = 128;
 // Number of GA splits of `split` keys covering positions 0..max_ctx.
 inline int ga_num_splits(int max_ctx, int split) { return (max_ctx + 1 + split - 1) / split; }
 // Bytes of GA workspace: per (sequence, split, head) an (m, l) pair and 128 partial outputs.
@@ -61,6 +75,7 @@ struct AppendArgs {
     const int64_t* kv_capacity;
     int batch, total_new, hkv, window;
     bool swa;
+    PageTable pages;
 };
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 

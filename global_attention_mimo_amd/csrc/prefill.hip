@@ -91,7 +91,9 @@ constexpr float kRescaleThreshold = MIMO_RESCALE_THRESHOLD;
 // positions in the cache (GA pool rows kv_base[b] + j, SWA ring slots j mod
 // ring) and its packed tokens sit at positions ctx_lens[b] + i; a key row is
 // staged from the cache below that length and from the chunk above it.
-template <int WV, int NB, int NK, bool SWA, int WAVES_PER_EU, bool CHUNK>
+// PAGED (GA chunks only): the pool is paged, position j in row j mod P of page
+// block_table[b][j / P] (P = 2^page_shift); each staged row looks its page up.
+template <int WV, int NB, int NK, bool SWA, int WAVES_PER_EU, bool CHUNK, bool PAGED = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WV, 64 * WV),
                           amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
 void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -99,7 +101,9 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     const float* __restrict__ sink, uint16_t* __restrict__ out, float* __restrict__ lse,
                     int hq, int hkv, int window, float c_log2, float value_scale, int num_qblocks,
                     int max_seqlen, const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
-                    const int64_t* __restrict__ kv_base, const int32_t* __restrict__ ctx_lens, int ring) {
+                    const int64_t* __restrict__ kv_base, const int32_t* __restrict__ ctx_lens, int ring,
+                    const int32_t* __restrict__ block_table, int max_blocks, int page_shift, long long num_pages) {
+    static_assert(!PAGED || (CHUNK && !SWA), "only GA chunks read a paged pool");
     using Cfg = PrefillCfg<WV, NB, NK>;
     constexpr int QT = Cfg::kTokens;
     // Two K/V buffers: tile t is computed from buffer t%2 while tile t+1 is staged into the other.
@@ -195,21 +199,59 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     const uint16_t* kcp[Cfg::kKPer];
     const uint16_t* vcp[Cfg::kVPer];
     int64_t cache_row0 = 0;
+    if constexpr (CHUNK && !PAGED) cache_row0 = SWA ? (int64_t)b * ring : kv_base[b];
     if constexpr (CHUNK) {
-        cache_row0 = SWA ? (int64_t)b * ring : kv_base[b];
 #pragma unroll
         for (int i = 0; i < Cfg::kKPer; ++i) kcp[i] = k_cache + (kp[i] - k) - (size_t)s0 * kstride;
 #pragma unroll
         for (int i = 0; i < Cfg::kVPer; ++i) vcp[i] = v_cache + (vp[i] - v) - (size_t)s0 * vstride;
     }
     u32x4 kreg[Cfg::kKPer], vreg[Cfg::kVPer];
+    // PAGED: a tile of NK keys (NK a multiple of 16, kbase a multiple of NK)
+    // spans max(1, NK / P) whole pages.  Their numbers come one tile ahead:
+    // load_tile(kt) reads tile kt's from `pgv` (lane t holds block kt*NK/P + t)
+    // and issues the load of tile kt+1's, so no row load waits on the table.
+    constexpr int kTilePages = NK / 16;
+    const int32_t* tb = PAGED ? block_table + (size_t)b * max_blocks : nullptr;
+    auto fetch_pages = [&](int kt) -> int {
+        if constexpr (PAGED) {
+            const int blk = ((kt * NK) >> page_shift) + (lane & (kTilePages - 1));
+            return tb[min(blk, max_blocks - 1)];
+        }
+        return 0;
+    };
+    int pgv = fetch_pages(kt_begin);
     auto load_tile = [&](int kt) {
         const int kbase = kt * NK;
         if constexpr (CHUNK) {
+            int pg[kTilePages];
+            if constexpr (PAGED) {
+                const int blk0 = kbase >> page_shift;
+#pragma unroll
+                for (int t = 0; t < kTilePages; ++t) {
+                    // An unmapped block reads page 0: wrong keys, but inside the pool.
+                    const int blk = blk0 + t;
+                    const int e = __builtin_amdgcn_readlane(pgv, t);
+                    const bool ok = blk < max_blocks && ((long long)blk << page_shift) < ctx0 && e >= 0 &&
+                                    e < num_pages;
+                    pg[t] = ok ? e : 0;
+                }
+                pgv = fetch_pages(kt + 1);
+            }
             // Position j: cache row below ctx0, else chunk row j - ctx0 (past the
             // chunk's last token clamped to it: such keys are masked).
             auto src_row = [&](const uint16_t* cache_col, const uint16_t* chunk_col, size_t stride, int j) {
-                if (j < ctx0) return cache_col + (size_t)(cache_row0 + (SWA ? j % ring : j)) * stride;
+                if (j < ctx0) {
+                    if constexpr (PAGED) {
+                        const int t = ((j - kbase) >> page_shift) & (kTilePages - 1);  // 0 when P >= NK
+                        int page = pg[0];
+#pragma unroll
+                        for (int u = 1; u < kTilePages; ++u) page = t == u ? pg[u] : page;
+                        const size_t row = ((size_t)page << page_shift) | (size_t)(j & ((1 << page_shift) - 1));
+                        return cache_col + row * stride;
+                    }
+                    return cache_col + (size_t)(cache_row0 + (SWA ? j % ring : j)) * stride;
+                }
                 return chunk_col + (size_t)min(j - ctx0, L - 1) * stride;
             };
 #pragma unroll
@@ -648,15 +690,16 @@ void swa_stream_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
     }
 }
 
-template <int WV, int NB, int NK, bool SWA, int WPE, bool CHUNK = false>
+template <int WV, int NB, int NK, bool SWA, int WPE, bool CHUNK = false, bool PAGED = false>
 hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
     using Cfg = PrefillCfg<WV, NB, NK>;
     const int nqb = (a.max_seqlen + Cfg::kTokens - 1) / Cfg::kTokens;
     dim3 grid(nqb, a.hkv, a.num_seqs);
-    hipLaunchKernelGGL((prefill_kernel<WV, NB, NK, SWA, WPE, CHUNK>), grid, dim3(Cfg::kThreads), 0, stream, a.q, a.k,
-                       a.v, a.cu_seqlens, a.sink, a.out, a.lse, a.hq, a.hkv, a.window, a.softmax_scale * kLog2e,
-                       a.value_scale, nqb, a.max_seqlen, a.k_cache, a.v_cache, a.kv_base, a.ctx_lens,
-                       a.window - 1);
+    hipLaunchKernelGGL((prefill_kernel<WV, NB, NK, SWA, WPE, CHUNK, PAGED>), grid, dim3(Cfg::kThreads), 0, stream,
+                       a.q, a.k, a.v, a.cu_seqlens, a.sink, a.out, a.lse, a.hq, a.hkv, a.window,
+                       a.softmax_scale * kLog2e, a.value_scale, nqb, a.max_seqlen, a.k_cache, a.v_cache, a.kv_base,
+                       a.ctx_lens, a.window - 1, a.pages.table, a.pages.max_blocks, a.pages.shift,
+                       a.pages.num_pages);
     return hipGetLastError();
 }
 
@@ -674,7 +717,10 @@ hipError_t launch_ga(const PrefillArgs& a, hipStream_t s) { return launch<WV, NB
 template <int WV, int NB, int NK, int WPE>
 hipError_t launch_swa(const PrefillArgs& a, hipStream_t s) { return launch<WV, NB, NK, true, WPE>(a, s); }
 template <int WV, int NB, int NK, int WPE>
-hipError_t launch_ga_chunk(const PrefillArgs& a, hipStream_t s) { return launch<WV, NB, NK, false, WPE, true>(a, s); }
+hipError_t launch_ga_chunk(const PrefillArgs& a, hipStream_t s) {
+    if (a.pages.table) return launch<WV, NB, NK, false, WPE, true, true>(a, s);
+    return launch<WV, NB, NK, false, WPE, true>(a, s);
+}
 template <int WV, int NB, int NK, int WPE>
 hipError_t launch_swa_chunk(const PrefillArgs& a, hipStream_t s) { return launch<WV, NB, NK, true, WPE, true>(a, s); }
 

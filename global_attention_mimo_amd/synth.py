@@ -134,6 +134,24 @@ def hybrid_layer_types(num_layers: int = 48, period: int = 6) -> List[int]:
     return [1 if (l % period) == period - 1 else 0 for l in range(num_layers)]
 
 
+def paged_block_table(ctx_lens: Sequence[int], page_size: int, *, seed: int = 0, extra_tokens: int = 1,
+                      spare_pages: int = 3, max_blocks: Optional[int] = None, device="cpu"):
+    """Seeded page assignment of a paged GA pool: sequence b gets enough blocks
+    for ctx_lens[b] + extra_tokens positions, on distinct pages drawn from a
+    random permutation of all pages (spare_pages stay unused).  Unused table
+    entries are -1.  Returns (block_table [B][max_blocks] int32, num_pages)."""
+    nblk = [(int(c) + extra_tokens + page_size - 1) // page_size for c in ctx_lens]
+    mb = max_blocks if max_blocks is not None else max(max(nblk), 1)
+    npages = sum(nblk) + spare_pages
+    perm = torch.randperm(npages, generator=_gen(seed, "cpu")).to(torch.int32)
+    table = torch.full((len(nblk), mb), -1, dtype=torch.int32)
+    used = 0
+    for b, n in enumerate(nblk):
+        table[b, :n] = perm[used:used + n]
+        used += n
+    return table.to(device), npages
+
+
 def bf16_bits(t: torch.Tensor) -> np.ndarray:
     """Host numpy uint16 view of a bf16 tensor's bit patterns."""
     if t.dtype != torch.bfloat16:

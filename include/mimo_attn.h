@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MIMO_ATTN_ABI_VERSION 2
+#define MIMO_ATTN_ABI_VERSION 3
 
 /* Layer type: which key set a query sees (model doc, Key features; config
  * layer_types). */
@@ -214,6 +214,76 @@ int mimo_kv_append(const mimo_attn_dims* dims, int layer_type,
                    int32_t batch, int32_t total_new,
                    uint16_t* k_cache, uint16_t* v_cache,
                    const int64_t* kv_base, const int64_t* kv_capacity, hipStream_t stream);
+
+/*
+ * Paged GA pool.  The cache of past_key_values (model doc,
+ * MiMoV2FlashModel.forward) for a GA layer may live in fixed-size pages of one
+ * shared pool instead of one contiguous range per sequence; paging is a
+ * serving layout of the same cache and changes nothing that is computed.
+ *
+ *   k_cache, v_cache  [num_pages * page_size][Hkv][192], [...][Hkv][128] bf16:
+ *                page n is rows n*page_size .. n*page_size + page_size - 1.
+ *   block_table  [batch][max_blocks] int32 (device): entry [b][i] is the page
+ *                holding positions i*page_size .. i*page_size + page_size - 1
+ *                of sequence b, so position j lives in row
+ *                block_table[b][j / page_size] * page_size + j % page_size.
+ *   page_size    tokens per page (host): a power of two in [16, 65536].
+ *   max_blocks   columns of block_table (host), >= 1.
+ *   num_pages    pages in the pool (host), >= 1.
+ * Entries for blocks a call reads must lie in [0, num_pages).  An entry
+ * outside that range is never dereferenced: decode reads its keys as zero
+ * vectors, chunked prefill reads them from page 0, append skips the tokens on
+ * it -- the results for that sequence are then meaningless, but no memory
+ * outside the pool is touched.  Passed by host pointer.
+ */
+typedef struct {
+    const int32_t* block_table;
+    int32_t max_blocks;
+    int32_t page_size;
+    int64_t num_pages;
+} mimo_kv_pages;
+
+/*
+ * mimo_kv_append for a GA layer whose cache is a paged pool: position pos of
+ * sequence b is written to row block_table[b][pos / page_size] * page_size +
+ * pos % page_size.  A sequence whose ctx_lens[b] + new tokens exceeds
+ * max_blocks * page_size is skipped entirely; a token whose block entry is
+ * outside [0, num_pages) is not written.  Other arguments as mimo_kv_append.
+ */
+int mimo_kv_append_paged(const mimo_attn_dims* dims,
+                         const uint16_t* k, const uint16_t* v,
+                         const int32_t* cu_newlens, const int32_t* ctx_lens,
+                         int32_t batch, int32_t total_new,
+                         uint16_t* k_cache, uint16_t* v_cache,
+                         const mimo_kv_pages* pages, hipStream_t stream);
+
+/*
+ * GA decode (as mimo_attn_decode with layer_type GA) over a paged pool.
+ * split_tokens must span at most 128 pages: with the default split of 2048
+ * every page_size >= 16 qualifies; otherwise MIMO_ERR_UNSUPPORTED.  The
+ * workspace is mimo_attn_decode_workspace_size(dims, MIMO_LAYER_GA, batch,
+ * max_ctx, split_tokens) bytes.  Results are bit-identical to
+ * mimo_attn_decode over a contiguous pool holding the same rows.
+ */
+int mimo_attn_decode_paged(const mimo_attn_dims* dims,
+                           const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                           const uint16_t* k_cache, const uint16_t* v_cache,
+                           const mimo_kv_pages* pages, const int32_t* ctx_lens,
+                           int32_t batch, int32_t max_ctx, int32_t split_tokens,
+                           const float* sink, uint16_t* out, float* lse,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * GA chunked prefill (as mimo_attn_prefill_chunk with layer_type GA) whose
+ * cached positions live in a paged pool.  Results are bit-identical to
+ * mimo_attn_prefill_chunk over a contiguous pool holding the same rows.
+ */
+int mimo_attn_prefill_chunk_paged(const mimo_attn_dims* dims,
+                                  const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                  const int32_t* cu_newlens, int32_t num_seqs, int32_t max_newlen,
+                                  const uint16_t* k_cache, const uint16_t* v_cache,
+                                  const mimo_kv_pages* pages, const int32_t* ctx_lens,
+                                  const float* sink, uint16_t* out, float* lse, hipStream_t stream);
 
 /* Static English name of a status code ("MIMO_OK", ...). */
 const char* mimo_status_string(int status);

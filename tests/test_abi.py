@@ -42,7 +42,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_version_and_status_strings(L):
-    assert B.mimo_abi_version() == 2
+    assert B.mimo_abi_version() == 3
     assert B.mimo_status_string(0) == "MIMO_OK"
     assert B.mimo_status_string(3) == "MIMO_ERR_WORKSPACE"
     assert B.mimo_status_string(99) == "MIMO_ERR_UNKNOWN"
@@ -177,6 +177,86 @@ def test_append_rejects(L, case, status):
 
 def test_append_nothing_is_ok_without_launch(L):
     assert append_call(L, total=0) == B.MIMO_OK
+
+
+def pages(table=FAKE, max_blocks=8, page_size=16, num_pages=100):
+    return B.mimo_kv_pages(table, max_blocks, page_size, num_pages)
+
+
+PAGES_BAD = [
+    (dict(table=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(max_blocks=0), B.MIMO_ERR_INVALID_ARG),
+    (dict(num_pages=0), B.MIMO_ERR_INVALID_ARG),
+    (dict(page_size=0), B.MIMO_ERR_INVALID_ARG),
+    (dict(page_size=8), B.MIMO_ERR_UNSUPPORTED),
+    (dict(page_size=48), B.MIMO_ERR_UNSUPPORTED),
+    (dict(page_size=1 << 17), B.MIMO_ERR_UNSUPPORTED),
+]
+
+
+def paged_decode_call(L, pg=None, q=FAKE, kc=FAKE, ctx=FAKE, batch=2, max_ctx=100, split=0, ws=FAKE,
+                      ws_bytes=1 << 30, dims=None):
+    d = dims or B.make_dims()
+    pref = None if pg is False else ctypes.byref(pg or pages())
+    return L.mimo_attn_decode_paged(ctypes.byref(d), q, FAKE, FAKE, kc, FAKE, pref, ctx, batch, max_ctx, split, None,
+                                    FAKE, None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,status", [(dict(pg=pages(**c)), st) for c, st in PAGES_BAD] + [
+    (dict(pg=False), B.MIMO_ERR_INVALID_ARG),
+    (dict(q=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(kc=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(ctx=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(batch=0), B.MIMO_ERR_INVALID_ARG),
+    (dict(ws=None), B.MIMO_ERR_WORKSPACE),
+    (dict(ws_bytes=100), B.MIMO_ERR_WORKSPACE),
+    (dict(split=4096), B.MIMO_ERR_UNSUPPORTED),                 # 256 pages of 16 per split
+    (dict(pg=pages(page_size=64), split=8192 + 32), B.MIMO_ERR_UNSUPPORTED),
+    (dict(dims=B.make_dims(head_dim_qk=64)), B.MIMO_ERR_UNSUPPORTED),
+])
+def test_decode_paged_rejects(L, case, status):
+    assert paged_decode_call(L, **case) == status
+    assert B.mimo_last_error() != ""
+
+
+def paged_chunk_call(L, pg=None, q=FAKE, kc=FAKE, ctx=FAKE, nseq=2, maxlen=16):
+    pref = None if pg is False else ctypes.byref(pg or pages())
+    return L.mimo_attn_prefill_chunk_paged(ctypes.byref(B.make_dims()), q, FAKE, FAKE, FAKE, nseq, maxlen, kc, FAKE,
+                                           pref, ctx, None, FAKE, None, None)
+
+
+@pytest.mark.parametrize("case,status", [(dict(pg=pages(**c)), st) for c, st in PAGES_BAD] + [
+    (dict(pg=False), B.MIMO_ERR_INVALID_ARG),
+    (dict(q=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(kc=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(ctx=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(nseq=0), B.MIMO_ERR_INVALID_ARG),
+    (dict(maxlen=-1), B.MIMO_ERR_INVALID_ARG),
+])
+def test_prefill_chunk_paged_rejects(L, case, status):
+    assert paged_chunk_call(L, **case) == status
+
+
+def paged_append_call(L, pg=None, k=FAKE, kc=FAKE, batch=1, total=4):
+    pref = None if pg is False else ctypes.byref(pg or pages())
+    return L.mimo_kv_append_paged(ctypes.byref(B.make_dims()), k, FAKE, FAKE, FAKE, batch, total, kc, FAKE, pref,
+                                  None)
+
+
+@pytest.mark.parametrize("case,status", [(dict(pg=pages(**c)), st) for c, st in PAGES_BAD] + [
+    (dict(pg=False), B.MIMO_ERR_INVALID_ARG),
+    (dict(k=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(kc=FAKE_ODD), B.MIMO_ERR_INVALID_ARG),
+    (dict(batch=0), B.MIMO_ERR_INVALID_ARG),
+    (dict(total=-1), B.MIMO_ERR_INVALID_ARG),
+])
+def test_append_paged_rejects(L, case, status):
+    assert paged_append_call(L, **case) == status
+
+
+def test_paged_empty_calls_are_ok(L):
+    assert paged_chunk_call(L, maxlen=0) == B.MIMO_OK
+    assert paged_append_call(L, total=0) == B.MIMO_OK
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
