@@ -73,6 +73,15 @@ class Oracle:
         lib.oracle_prefill_chunk_paged.restype = _I
         lib.oracle_prefill_chunk_paged.argtypes = [_I, _I, _I, _I, _F, _F, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I,
                                                    _I64, _P, _P, _P, _P, _I]
+        lib.oracle_decode_fp8.restype = _I
+        lib.oracle_decode_fp8.argtypes = [_I, _I, _I, _I, _F, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P,
+                                          _P, _I]
+        lib.oracle_kv_append_fp8.restype = _I
+        lib.oracle_kv_append_fp8.argtypes = [_I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P]
+        lib.oracle_e4m3_encode.restype = None
+        lib.oracle_e4m3_encode.argtypes = [_P, _P, _I64]
+        lib.oracle_e4m3_decode.restype = None
+        lib.oracle_e4m3_decode.argtypes = [_P, _P, _I64]
         lib.oracle_kv_append_paged.restype = _I
         lib.oracle_kv_append_paged.argtypes = [_I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I64]
         lib.oracle_default_threads.restype = _I
@@ -289,6 +298,76 @@ class Oracle:
         return int(self.lib.oracle_kv_append_paged(hkv, dqk, dv, self._ptr(k), self._ptr(v), self._ptr(cu),
                                                    self._ptr(ctx), cu.shape[0] - 1, self._ptr(k_pool),
                                                    self._ptr(v_pool), self._ptr(tb), mb, page_size, npages))
+
+    # -- FP8 (OCP E4M3) GA pool ----------------------------------------------
+    def e4m3_encode(self, x) -> np.ndarray:
+        """E4M3 codes (uint8) of float32 values: |x| clamped to 448, nearest, ties to even."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        out = np.empty(x.shape, np.uint8)
+        self.lib.oracle_e4m3_encode(self._ptr(x), self._ptr(out), x.size)
+        return out
+
+    def e4m3_decode(self, codes) -> np.ndarray:
+        """Values (float64) of E4M3 codes."""
+        c = np.ascontiguousarray(codes, dtype=np.uint8)
+        out = np.empty(c.shape, np.float64)
+        self.lib.oracle_e4m3_decode(self._ptr(c), self._ptr(out), c.size)
+        return out
+
+    @staticmethod
+    def _scales(s, hkv):
+        s = np.ascontiguousarray(s, dtype=np.float32)
+        if s.shape != (hkv,):
+            raise ValueError(f"scales must have shape ({hkv},)")
+        return s
+
+    def decode_fp8(self, q, k_new, v_new, k_pool, v_pool, kv_base, k_scale, v_scale, ctx_lens, *, scale: float,
+                   value_scale: float = 1.0, sink=None, nthreads: int = 0):
+        """GA decode over an FP8 pool of E4M3 codes [N][Hkv][D] (uint8): cached position j of sequence b
+        is code[kv_base[b] + j] * scale[g]; the new token comes from k_new / v_new (bf16)."""
+        q = np.ascontiguousarray(q)
+        batch, hq, dqk = q.shape
+        hkv, dv = v_new.shape[1], v_new.shape[2]
+        q = self._u16(q, (hq, dqk))
+        kn = self._u16(k_new, (hkv, dqk))
+        vn = self._u16(v_new, (hkv, dv))
+        kc = np.ascontiguousarray(k_pool, dtype=np.uint8)
+        vc = np.ascontiguousarray(v_pool, dtype=np.uint8)
+        if kc.shape[1:] != (hkv, dqk) or vc.shape[1:] != (hkv, dv):
+            raise ValueError("FP8 pools are [N][Hkv][D] uint8")
+        base = np.ascontiguousarray(kv_base, dtype=np.int64)
+        ks, vs = self._scales(k_scale, hkv), self._scales(v_scale, hkv)
+        ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+        sk = None if sink is None else np.ascontiguousarray(sink, dtype=np.float32)
+        out = np.empty((batch, hq, dv), np.float64)
+        lse = np.empty((batch, hq), np.float64)
+        nth = nthreads if nthreads > 0 else self.default_threads()
+        rc = self.lib.oracle_decode_fp8(hq, hkv, dqk, dv, scale, value_scale, self._ptr(q), self._ptr(kn),
+                                        self._ptr(vn), self._ptr(kc), self._ptr(vc), self._ptr(base), self._ptr(ks),
+                                        self._ptr(vs), self._ptr(ctx), batch, self._ptr(sk), self._ptr(out),
+                                        self._ptr(lse), nth)
+        if rc != OK:
+            raise ValueError(f"oracle_decode_fp8 rejected its arguments (status {rc})")
+        return out, lse
+
+    def kv_append_fp8(self, k, v, cu_newlens, ctx_lens, k_pool, v_pool, kv_base, kv_capacity, k_scale,
+                      v_scale) -> int:
+        """Quantises new tokens into an FP8 GA pool in place; returns the status code."""
+        k = np.ascontiguousarray(k)
+        v = np.ascontiguousarray(v)
+        hkv, dqk, dv = k.shape[1], k.shape[2], v.shape[2]
+        for c in (k_pool, v_pool):
+            if not (c.flags["C_CONTIGUOUS"] and c.dtype == np.uint8):
+                raise TypeError("FP8 pools must be C-contiguous uint8 arrays")
+        cu = np.ascontiguousarray(cu_newlens, dtype=np.int32)
+        ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+        base = np.ascontiguousarray(kv_base, dtype=np.int64)
+        cap = np.ascontiguousarray(kv_capacity, dtype=np.int64)
+        ks, vs = self._scales(k_scale, hkv), self._scales(v_scale, hkv)
+        return int(self.lib.oracle_kv_append_fp8(hkv, dqk, dv, self._ptr(k), self._ptr(v), self._ptr(cu),
+                                                 self._ptr(ctx), cu.shape[0] - 1, self._ptr(k_pool),
+                                                 self._ptr(v_pool), self._ptr(base), self._ptr(cap), self._ptr(ks),
+                                                 self._ptr(vs)))
 
 _default: Optional[Oracle] = None
 

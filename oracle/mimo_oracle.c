@@ -33,6 +33,13 @@
  * Inputs are the bf16 bit patterns the GPU receives, widened exactly to double;
  * sink, scale and value_scale are fp32 widened to double.  Everything else is
  * double with libm exp/log.
+ *
+ * An FP8 GA cache (a storage format of the same cache; the model doc does not
+ * define one) holds OCP E4M3 codes with one fp32 scale per KV head: a cached
+ * key or value element x is stored as E4M3(clamp(x / scale, -448, 448)), the
+ * division done in fp32 and the rounding to nearest-even, and read back as
+ * value(code) * scale.  The new token of a decode step is read from k_new /
+ * v_new as given (bf16), as for the bf16 cache.
  */
 #include <math.h>
 #include <pthread.h>
@@ -55,24 +62,79 @@ static double bf16_to_double(uint16_t bits) {
     return (double)f;
 }
 
+/* OCP 8-bit floating point, E4M3 (OCP "OCP 8-bit Floating Point Specification
+ * (OFP8)"): sign bit, 4 exponent bits with bias 7, 3 mantissa bits.  Exponent
+ * field 0 holds zero and the subnormals m/8 * 2^-6; fields 1..15 hold
+ * (1 + m/8) * 2^(e-7), except S.1111.111, which is NaN.  No infinities; the
+ * largest finite magnitude is 448. */
+static double e4m3_to_double(uint8_t c) {
+    int e = (c >> 3) & 15, m = c & 7;
+    double sgn = (c & 0x80) ? -1.0 : 1.0;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) return sgn * ldexp((double)m / 8.0, -6);
+    return sgn * ldexp(1.0 + (double)m / 8.0, e - 7);
+}
+
+/* E4M3 code nearest to x after clamping |x| to 448, ties to the even code;
+ * the sign of x (zero included) is kept.  x must not be NaN. */
+static uint8_t e4m3_from_float(float x) {
+    uint8_t sgn = signbit(x) ? 0x80 : 0;
+    double a = fabs((double)x);
+    if (a > 448.0) a = 448.0;
+    /* grid step: 2^-9 below 2^-6 (subnormals), else 2^(b-3) in binade [2^b, 2^(b+1)) */
+    int b = -6;
+    if (a >= 0x1p-6) {
+        frexp(a, &b);
+        b -= 1;
+    }
+    double step = ldexp(1.0, b - 3);
+    double r = nearbyint(a / step) * step; /* a / step is exact; nearbyint rounds half to even */
+    if (r < 0x1p-6) return (uint8_t)(sgn | (uint8_t)(r / 0x1p-9));
+    frexp(r, &b);
+    b -= 1;
+    int m = (int)(r / ldexp(1.0, b) * 8.0) - 8;
+    return (uint8_t)(sgn | ((b + 7) << 3) | m);
+}
+
+/* Stored code of element x (bf16 bits) of a KV head with the given scale. */
+static uint8_t e4m3_quantize(uint16_t x, float scale) {
+    uint32_t w = ((uint32_t)x) << 16;
+    float f;
+    memcpy(&f, &w, sizeof f);
+    return e4m3_from_float(f / scale);
+}
+
 typedef struct {
     int hq, hkv, dqk, dv, layer_type, window;
     double scale, value_scale;
 } dims_t;
 
+/* Rows of an FP8 cache: per key, E4M3 code rows (NULL = take the bf16 row)
+ * and the scales that turn codes into values. */
+typedef struct {
+    const uint8_t* const* k8;
+    const uint8_t* const* v8;
+    double kscale, vscale;
+} fp8_rows_t;
+
 /* One attention row: query vector qrow (length dqk), keys given as arrays of
  * row pointers (one per key in J, in increasing position order).  Writes
  * o[dv] and *lse.  If wkeys is non-NULL it receives exp(s_j - LSE) for each
- * key, and *wsink the sink mass exp(sigma - LSE) (0 without a sink). */
+ * key, and *wsink the sink mass exp(sigma - LSE) (0 without a sink).  With f8
+ * non-NULL, a key whose f8 row is set is read from E4M3 codes times the scale. */
 static void attend_row(const dims_t* d, const uint16_t* qrow, int nkeys,
-                       const uint16_t* const* krows, const uint16_t* const* vrows,
+                       const uint16_t* const* krows, const uint16_t* const* vrows, const fp8_rows_t* f8,
                        int has_sink, double sigma, double* scores,
                        double* o, double* lse, double* wkeys, double* wsink) {
     double m = -INFINITY;
     for (int j = 0; j < nkeys; ++j) {
         double acc = 0.0;
-        for (int x = 0; x < d->dqk; ++x)
-            acc += bf16_to_double(qrow[x]) * bf16_to_double(krows[j][x]);
+        if (f8 && f8->k8[j])
+            for (int x = 0; x < d->dqk; ++x)
+                acc += bf16_to_double(qrow[x]) * (e4m3_to_double(f8->k8[j][x]) * f8->kscale);
+        else
+            for (int x = 0; x < d->dqk; ++x)
+                acc += bf16_to_double(qrow[x]) * bf16_to_double(krows[j][x]);
         scores[j] = d->scale * acc;
         if (scores[j] > m) m = scores[j];
     }
@@ -85,7 +147,10 @@ static void attend_row(const dims_t* d, const uint16_t* qrow, int nkeys,
     for (int j = 0; j < nkeys; ++j) {
         double w = exp(scores[j] - l);
         if (wkeys) wkeys[j] = w;
-        for (int e = 0; e < d->dv; ++e) o[e] += w * bf16_to_double(vrows[j][e]);
+        if (f8 && f8->v8[j])
+            for (int e = 0; e < d->dv; ++e) o[e] += w * (e4m3_to_double(f8->v8[j][e]) * f8->vscale);
+        else
+            for (int e = 0; e < d->dv; ++e) o[e] += w * bf16_to_double(vrows[j][e]);
     }
     for (int e = 0; e < d->dv; ++e) o[e] *= d->value_scale;
     if (wkeys) *wsink = has_sink ? exp(sigma - l) : 0.0;
@@ -159,7 +224,7 @@ static void* prefill_worker(void* arg) {
             double sigma = 0.0;
             int hs = sink_present(jb->sink, h, &sigma);
             double* w = jb->weights ? jb->weights + ((size_t)r * d->hq + h) * jb->wstride : NULL;
-            attend_row(d, jb->q + ((size_t)t * d->hq + h) * d->dqk, n, kr, vr, hs, sigma, sc,
+            attend_row(d, jb->q + ((size_t)t * d->hq + h) * d->dqk, n, kr, vr, NULL, hs, sigma, sc,
                        jb->out + ((size_t)r * d->hq + h) * d->dv, jb->lse + (size_t)r * d->hq + h,
                        w ? w + lo : NULL, w ? w + jb->wstride - 1 : NULL);
         }
@@ -246,6 +311,8 @@ typedef struct {
 typedef struct {
     const dims_t* d;
     const uint16_t *q, *k_new, *v_new, *k_cache, *v_cache;
+    const uint8_t *k8, *v8;          /* FP8 GA pool (codes), or NULL */
+    const float *k8scale, *v8scale;  /* [hkv] scales of the FP8 pool */
     const int64_t* kv_base;
     const pages_t* pages;
     const int32_t* ctx;
@@ -298,6 +365,8 @@ static void* decode_worker(void* arg) {
     for (int b = 0; b < jb->batch; ++b) if (jb->ctx[b] + 1 > maxkeys) maxkeys = jb->ctx[b] + 1;
     const uint16_t** kr = malloc(sizeof(*kr) * (size_t)maxkeys);
     const uint16_t** vr = malloc(sizeof(*vr) * (size_t)maxkeys);
+    const uint8_t** k8r = malloc(sizeof(*k8r) * (size_t)maxkeys);
+    const uint8_t** v8r = malloc(sizeof(*v8r) * (size_t)maxkeys);
     double* sc = malloc(sizeof(double) * (size_t)maxkeys);
     int group = d->hq / d->hkv;
     for (;;) {
@@ -311,18 +380,28 @@ static void* decode_worker(void* arg) {
         if (d->layer_type == ORACLE_SWA) lo = p - (d->window - 1) > 0 ? p - (d->window - 1) : 0;
         int n = 0;
         for (int j = lo; j < p; ++j, ++n) {
-            kr[n] = cache_row(jb, b, j, g, 0);
-            vr[n] = cache_row(jb, b, j, g, 1);
+            if (jb->k8) { /* FP8 pool: codes of row kv_base[b] + j */
+                size_t row = (size_t)(jb->kv_base[b] + j);
+                kr[n] = vr[n] = NULL;
+                k8r[n] = jb->k8 + (row * d->hkv + g) * d->dqk;
+                v8r[n] = jb->v8 + (row * d->hkv + g) * d->dv;
+            } else {
+                kr[n] = cache_row(jb, b, j, g, 0);
+                vr[n] = cache_row(jb, b, j, g, 1);
+                k8r[n] = v8r[n] = NULL;
+            }
         }
         kr[n] = jb->k_new + ((size_t)b * d->hkv + g) * d->dqk;
         vr[n] = jb->v_new + ((size_t)b * d->hkv + g) * d->dv;
+        k8r[n] = v8r[n] = NULL;
         n++;
         double sigma = 0.0;
         int hs = sink_present(jb->sink, h, &sigma);
-        attend_row(d, jb->q + ((size_t)b * d->hq + h) * d->dqk, n, kr, vr, hs, sigma, sc,
+        fp8_rows_t f8 = {k8r, v8r, jb->k8 ? (double)jb->k8scale[g] : 1.0, jb->k8 ? (double)jb->v8scale[g] : 1.0};
+        attend_row(d, jb->q + ((size_t)b * d->hq + h) * d->dqk, n, kr, vr, jb->k8 ? &f8 : NULL, hs, sigma, sc,
                    jb->out + ((size_t)b * d->hq + h) * d->dv, jb->lse + (size_t)b * d->hq + h, NULL, NULL);
     }
-    free(kr); free(vr); free(sc);
+    free(kr); free(vr); free(k8r); free(v8r); free(sc);
     return NULL;
 }
 
@@ -432,7 +511,7 @@ static void* chunk_worker(void* arg) {
         }
         double sigma = 0.0;
         int hs = sink_present(jb->sink, h, &sigma);
-        attend_row(d, jb->q + ((size_t)t * d->hq + h) * d->dqk, n, kr, vr, hs, sigma, sc,
+        attend_row(d, jb->q + ((size_t)t * d->hq + h) * d->dqk, n, kr, vr, NULL, hs, sigma, sc,
                    jb->out + ((size_t)t * d->hq + h) * d->dv, jb->lse + (size_t)t * d->hq + h, NULL, NULL);
     }
     free(kr); free(vr); free(sc);
@@ -573,6 +652,82 @@ int oracle_kv_append_paged(int hkv, int dqk, int dv, const uint16_t* k, const ui
         }
     }
     return status;
+}
+
+/* ------------------------------------------------------------------------ */
+/* FP8 GA cache (see the header): pool [N][Hkv][D] of E4M3 codes, position j */
+/* of sequence b at row kv_base[b] + j, one scale per KV head for K and V.   */
+
+static int scales_ok(const float* s, int hkv) {
+    if (!s) return 0;
+    for (int g = 0; g < hkv; ++g)
+        if (!(s[g] > 0.0f) || isinf(s[g])) return 0;
+    return 1;
+}
+
+/* GA decode over an FP8 pool: cached positions j < p read as code * scale. */
+int oracle_decode_fp8(int hq, int hkv, int dqk, int dv, float scale, float value_scale,
+                      const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                      const uint8_t* k_cache, const uint8_t* v_cache, const int64_t* kv_base,
+                      const float* k_scale, const float* v_scale, const int32_t* ctx_lens, int batch,
+                      const float* sink, double* out, double* lse, int nthreads) {
+    dims_t d = {hq, hkv, dqk, dv, ORACLE_GA, 0, (double)scale, (double)value_scale};
+    if (!check_dims(&d) || batch < 1 || !q || !k_new || !v_new || !ctx_lens || !out || !lse || !kv_base ||
+        !k_cache || !v_cache || !scales_ok(k_scale, hkv) || !scales_ok(v_scale, hkv))
+        return ORACLE_EINVAL;
+    for (int b = 0; b < batch; ++b)
+        if (ctx_lens[b] < 0) return ORACLE_EINVAL;
+    decode_job_t jb;
+    memset(&jb, 0, sizeof jb);
+    jb.d = &d; jb.q = q; jb.k_new = k_new; jb.v_new = v_new; jb.k8 = k_cache; jb.v8 = v_cache;
+    jb.k8scale = k_scale; jb.v8scale = v_scale; jb.kv_base = kv_base; jb.ctx = ctx_lens; jb.batch = batch;
+    jb.sink = sink; jb.out = out; jb.lse = lse;
+    pthread_mutex_init(&jb.mu, NULL);
+    run_threads(decode_worker, &jb, nthreads);
+    pthread_mutex_destroy(&jb.mu);
+    return ORACLE_OK;
+}
+
+/* KV append into an FP8 GA pool: as oracle_kv_append for GA (rows kv_base[b]
+ * + position, a sequence past its capacity skipped whole with
+ * ORACLE_ECAPACITY), each element stored as its E4M3 code under the scale of
+ * its KV head. */
+int oracle_kv_append_fp8(int hkv, int dqk, int dv, const uint16_t* k, const uint16_t* v,
+                         const int32_t* cu_newlens, const int32_t* ctx_lens, int batch,
+                         uint8_t* k_cache, uint8_t* v_cache, const int64_t* kv_base, const int64_t* kv_capacity,
+                         const float* k_scale, const float* v_scale) {
+    if (hkv <= 0 || dqk <= 0 || dv <= 0 || batch < 1 || !k || !v || !cu_newlens || !ctx_lens || !k_cache ||
+        !v_cache || !kv_base || !kv_capacity || !scales_ok(k_scale, hkv) || !scales_ok(v_scale, hkv))
+        return ORACLE_EINVAL;
+    int status = ORACLE_OK;
+    for (int b = 0; b < batch; ++b) {
+        int n = cu_newlens[b + 1] - cu_newlens[b];
+        if (n < 0) return ORACLE_EINVAL;
+        if ((int64_t)ctx_lens[b] + n > kv_capacity[b]) {
+            status = ORACLE_ECAPACITY;
+            continue;
+        }
+        for (int i = 0; i < n; ++i) {
+            size_t src = (size_t)cu_newlens[b] + i;
+            size_t dst = (size_t)(kv_base[b] + ctx_lens[b] + i);
+            for (int g = 0; g < hkv; ++g) {
+                for (int x = 0; x < dqk; ++x)
+                    k_cache[(dst * hkv + g) * dqk + x] = e4m3_quantize(k[(src * hkv + g) * dqk + x], k_scale[g]);
+                for (int x = 0; x < dv; ++x)
+                    v_cache[(dst * hkv + g) * dv + x] = e4m3_quantize(v[(src * hkv + g) * dv + x], v_scale[g]);
+            }
+        }
+    }
+    return status;
+}
+
+/* The E4M3 codec on its own (for the pins): codes of n floats, values of n codes. */
+void oracle_e4m3_encode(const float* x, uint8_t* codes, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) codes[i] = e4m3_from_float(x[i]);
+}
+
+void oracle_e4m3_decode(const uint8_t* codes, double* x, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) x[i] = e4m3_to_double(codes[i]);
 }
 
 /* Number of oracle worker threads a caller gets with nthreads <= 0. */

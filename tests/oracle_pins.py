@@ -11,7 +11,12 @@ the oracle disagrees with:
   * invariants (weights plus sink mass sum to one; a sink of -inf is no sink;
     SWA equals GA when the window covers the sequence; GQA equals MHA with the
     K/V heads repeated; value_scale is linear; decode at position p equals row
-    p of prefill; ring-slot contents after appends).
+    p of prefill; ring-slot contents after appends);
+  * for the FP8 (OCP E4M3) GA cache: the format's own table
+    (tests/golden/ocp_e4m3.json) and torch's float8_e4m3fn conversions (a
+    library implementation of the same format); FP8 decode equals bf16 decode
+    where the dequantised values are exact in bf16, and a dense numpy brute
+    force elsewhere.
 
 The attention definition pinned here is the one from the Hugging Face
 Transformers model doc "MiMo-V2-Flash" (Key features: 5:1 SWA/GA, 128-token
@@ -573,6 +578,156 @@ def pin_paged_append_places_positions(orc):
     one = np.ones((1, 1, 2), np.uint16)
     st = orc.kv_append_paged(one, one, np.array([0, 1, 1], np.int32), np.array([12, 0], np.int32), kc, vc, table, P)
     assert st == oracle.ECAPACITY and np.array_equal(kc, before), "append past max_blocks * page_size not refused"
+
+
+# -- FP8 (OCP E4M3) GA cache -------------------------------------------------
+
+def _torch_e4m3_codes(x):
+    """Codes of float32 values through torch's float8_e4m3fn (nearest, ties to even)."""
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _e4m3_probe_values():
+    """Every rounding midpoint between neighbouring positive codes, 1-3 float32
+    ulps either side, the codes themselves, both signs, plus random values."""
+    grid = _torch_decode_all()[:0x7f]
+    xs = []
+    for a, b in zip(grid[:-1], grid[1:]):
+        for v in (np.float32(a), np.float32((a + b) / 2)):
+            xs.append(v)
+            up = dn = v
+            for _ in range(3):
+                up = np.nextafter(up, np.float32(np.inf), dtype=np.float32)
+                dn = np.nextafter(dn, np.float32(-np.inf), dtype=np.float32)
+                xs += [up, dn]
+    xs = np.array(xs, np.float32)
+    rng = np.random.default_rng(60)
+    r = np.concatenate([rng.uniform(-448, 448, 20000), rng.normal(0, 1, 20000) * rng.choice([1e-3, 0.1, 10], 20000)])
+    return np.concatenate([xs, -xs, r.astype(np.float32), np.float32([0.0, -0.0])])
+
+
+def _torch_decode_all():
+    return torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def pin_e4m3_decode_spec_table_and_torch(orc):
+    """Decoding every code agrees with torch's float8_e4m3fn, and the named values
+    of the format's table (largest/smallest normal and subnormal, NaN, zeros)."""
+    import json
+    d = orc.e4m3_decode(np.arange(256, dtype=np.uint8))
+    t = _torch_decode_all()
+    assert np.all((d == t) | (np.isnan(d) & np.isnan(t))), "E4M3 decode differs from torch float8_e4m3fn"
+    spec = json.load(open(os.path.join(HERE, "golden", "ocp_e4m3.json")))
+    for key in ("max_normal", "min_normal", "max_subnormal", "min_subnormal"):
+        c = int(spec[key]["code"], 16)
+        assert d[c] == spec[key]["value"] and d[c | 0x80] == -spec[key]["value"], key
+    assert all(np.isnan(d[int(c, 16)]) for c in spec["nan"]["codes"])
+    assert int(np.isnan(d).sum()) == 2 and not np.isinf(d).any()
+    assert all(d[int(c, 16)] == 0.0 for c in spec["zeros"]["codes"])
+    assert d[0x38] == 1.0 and (0x38 >> 3) == spec["exponent_bias"]["value"]
+
+
+def pin_e4m3_encode_nearest_even_saturating(orc):
+    """Encoding equals torch's float8_e4m3fn rounding (nearest, ties to even) on
+    every midpoint and its neighbouring floats, and saturates beyond +-448."""
+    x = _e4m3_probe_values()
+    assert np.array_equal(orc.e4m3_encode(x), _torch_e4m3_codes(x)), "E4M3 encode differs from torch"
+    big = np.float32([448.0, 449.0, 463.9, 464.0, 500.0, 1e9, -449.0, -1e30])
+    assert np.array_equal(orc.e4m3_encode(big), np.uint8([0x7e] * 6 + [0xfe] * 2)), "no saturation at 448"
+    c = np.arange(256, dtype=np.uint8)
+    finite = ~np.isnan(orc.e4m3_decode(c))
+    assert np.array_equal(orc.e4m3_encode(orc.e4m3_decode(c[finite]).astype(np.float32)), c[finite]), "round trip"
+
+
+def _fp8_pool_case(ctx, seed, k_scale, v_scale, exact_bf16):
+    """Random E4M3 code pools (no NaN codes) for GA decode, and the bf16 pools of
+    their values when those are exact in bf16 (power-of-two scales)."""
+    x = synth.decode_inputs(ctx, GA, seed=seed)
+    rng = np.random.default_rng(seed)
+    n = x.k_cache.shape[0]
+    kc = rng.integers(0, 256, (n, 4, 192)).astype(np.uint8)
+    vc = rng.integers(0, 256, (n, 4, 128)).astype(np.uint8)
+    kc[(kc & 0x7f) == 0x7f] ^= 1   # NaN codes -> neighbouring finite codes
+    vc[(vc & 0x7f) == 0x7f] ^= 1
+    pools = None
+    if exact_bf16:
+        dec = _torch_decode_all()
+        kf = (dec[kc] * np.asarray(k_scale)[None, :, None]).astype(np.float32)
+        vf = (dec[vc] * np.asarray(v_scale)[None, :, None]).astype(np.float32)
+        kb = torch.from_numpy(kf).to(torch.bfloat16)
+        vb = torch.from_numpy(vf).to(torch.bfloat16)
+        assert np.array_equal(kb.float().numpy(), kf) and np.array_equal(vb.float().numpy(), vf)
+        pools = (_bits(kb), _bits(vb))
+    return x, kc, vc, pools
+
+
+def pin_fp8_decode_equals_bf16_where_exact(orc):
+    """With power-of-two scales (different per head, for K and V) every
+    dequantised value is exact in bf16: FP8 decode over the codes equals bf16
+    decode over those values, for contexts 0, 1, 31, 32, 33, 300."""
+    ctx = [0, 1, 31, 32, 33, 300]
+    ks, vs = np.float32([0.5, 1.0, 2.0, 0.25]), np.float32([2.0, 0.125, 1.0, 4.0])
+    x, kc, vc, (kb, vb) = _fp8_pool_case(ctx, 61, ks, vs, True)
+    sc = float(np.float32(synth.SOFTMAX_SCALE))
+    args = (_bits(x.q), _bits(x.k_new), _bits(x.v_new))
+    o8, l8 = orc.decode_fp8(*args, kc, vc, x.kv_base.numpy(), ks, vs, x.ctx_lens.numpy(), scale=sc,
+                            sink=x.sink.numpy())
+    ob, lb = orc.decode(*args, kb, vb, x.ctx_lens.numpy(), layer_type=GA, scale=sc, sink=x.sink.numpy(),
+                        kv_base=x.kv_base.numpy())
+    assert np.array_equal(o8, ob) and np.array_equal(l8, lb), "FP8 decode differs from bf16 decode on exact values"
+
+
+def pin_fp8_decode_brute_force(orc):
+    """Scales that are not powers of two: FP8 decode against a dense numpy brute
+    force (dequantise, scores, sink-seeded softmax, weighted values)."""
+    ctx = [0, 5, 64]
+    ks, vs = np.float32([0.37, 0.011, 1.7, 0.05]), np.float32([0.021, 0.9, 0.33, 3.1])
+    x, kc, vc, _ = _fp8_pool_case(ctx, 62, ks, vs, False)
+    sc = float(np.float32(synth.SOFTMAX_SCALE))
+    sink = x.sink.numpy()
+    o8, l8 = orc.decode_fp8(_bits(x.q), _bits(x.k_new), _bits(x.v_new), kc, vc, x.kv_base.numpy(), ks, vs,
+                            x.ctx_lens.numpy(), scale=sc, value_scale=0.707, sink=sink)
+    dec = _torch_decode_all()
+    q, kn, vn = _f64(x.q).numpy(), _f64(x.k_new).numpy(), _f64(x.v_new).numpy()
+    base = x.kv_base.numpy()
+    for b, p in enumerate(ctx):
+        for h in range(64):
+            g = h // 16
+            K = np.concatenate([dec[kc[base[b]:base[b] + p, g]] * float(ks[g]), kn[b, g][None]])
+            V = np.concatenate([dec[vc[base[b]:base[b] + p, g]] * float(vs[g]), vn[b, g][None]])
+            s = np.float64(sc) * (K @ q[b, h])
+            allv = np.append(s, float(sink[h]))
+            mx = allv.max()
+            lse = mx + np.log(np.exp(allv - mx).sum())
+            o = float(np.float32(0.707)) * (np.exp(s - lse) @ V)
+            # fp64 rounding-order differences scale with the value magnitudes (|V| up to ~1400 here)
+            _close(o8[b, h], o, 1e-13 * (1 + np.abs(V).max()), f"fp8 decode brute force b={b} h={h}")
+            assert abs(l8[b, h] - lse) < 1e-13 * (1 + np.abs(s).max())
+
+
+def pin_fp8_append_codes(orc):
+    """Appending to an FP8 pool stores torch's E4M3 code of (bf16 value / head
+    scale) computed in float32, clamped to +-448, at row kv_base + position; a
+    sequence past its capacity is skipped whole."""
+    lengths = [5, 3]
+    x = _make(lengths, seed=63)
+    ks, vs = np.float32([0.37, 0.011, 1.7, 0.05]), np.float32([0.021, 0.9, 0.33, 3.1])
+    kb, vb = _bits(x.k).copy(), _bits(x.v).copy()
+    big = torch.tensor([1000.0, -3e5, 7.0], dtype=torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    kb[0, 1, :3] = big  # beyond 448 after scaling: saturates
+    vb[1, 3, :3] = big
+    kc = np.zeros((20, 4, 192), np.uint8)
+    vc = np.zeros((20, 4, 128), np.uint8)
+    base, cap = np.array([2, 12], np.int64), np.array([8, 4], np.int64)
+    st = orc.kv_append_fp8(kb, vb, x.cu_seqlens.numpy(), np.array([1, 2], np.int32), kc, vc, base, cap, ks, vs)
+    assert st == oracle.ECAPACITY  # sequence 1: 2 + 3 > 4
+    kf = (kb.astype(np.uint32) << 16).view(np.float32)
+    vf = (vb.astype(np.uint32) << 16).view(np.float32)
+    want_k = _torch_e4m3_codes(np.clip(kf[:5] / ks[None, :, None], -448, 448))
+    want_v = _torch_e4m3_codes(np.clip(vf[:5] / vs[None, :, None], -448, 448))
+    assert np.array_equal(kc[3:8], want_k) and np.array_equal(vc[3:8], want_v), "FP8 append codes"
+    assert not kc[:3].any() and not kc[8:].any() and not vc[8:].any(), "FP8 append wrote outside its rows"
+    assert kc[3, 1, 0] == 0x7e and kc[3, 1, 1] == 0xfe, "saturation"
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]
 

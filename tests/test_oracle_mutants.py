@@ -77,6 +77,21 @@ MUTANTS = {
     "paged append writes tokens on unmapped blocks": (
         "            if (page < 0 || page >= num_pages) {\n                status = ORACLE_ECAPACITY;\n                continue;\n            }\n",
         "            if (page >= num_pages) {\n                status = ORACLE_ECAPACITY;\n                continue;\n            }\n"),
+    "E4M3 rounds half away from zero": ("    double r = nearbyint(a / step) * step;", "    double r = round(a / step) * step;"),
+    "E4M3 not saturated at 448": ("    if (a > 448.0) a = 448.0;\n", "\n"),
+    "E4M3 subnormal step one binade off": ("    int b = -6;\n", "    int b = -7;\n"),
+    "E4M3 decode exponent bias off by one": ("    return sgn * ldexp(1.0 + (double)m / 8.0, e - 7);\n",
+                                             "    return sgn * ldexp(1.0 + (double)m / 8.0, e - 8);\n"),
+    "FP8 decode ignores the K scale": (
+        "                acc += bf16_to_double(qrow[x]) * (e4m3_to_double(f8->k8[j][x]) * f8->kscale);\n",
+        "                acc += bf16_to_double(qrow[x]) * e4m3_to_double(f8->k8[j][x]);\n"),
+    "FP8 decode applies the K scale to values": (
+        "            for (int e = 0; e < d->dv; ++e) o[e] += w * (e4m3_to_double(f8->v8[j][e]) * f8->vscale);\n",
+        "            for (int e = 0; e < d->dv; ++e) o[e] += w * (e4m3_to_double(f8->v8[j][e]) * f8->kscale);\n"),
+    "FP8 append uses head 0's scale": (
+        "                    k_cache[(dst * hkv + g) * dqk + x] = e4m3_quantize(k[(src * hkv + g) * dqk + x], k_scale[g]);\n",
+        "                    k_cache[(dst * hkv + g) * dqk + x] = e4m3_quantize(k[(src * hkv + g) * dqk + x], k_scale[0]);\n"),
+    "FP8 quantiser multiplies by the scale": ("    return e4m3_from_float(f / scale);\n", "    return e4m3_from_float(f * scale);\n"),
     "bf16 widened from the wrong half": ("    uint32_t w = ((uint32_t)bits) << 16;\n", "    uint32_t w = ((uint32_t)bits) << 15;\n"),
 }
 
