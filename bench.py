@@ -204,6 +204,46 @@ def paged_rows(dims, dga, ctx, max_ctx, ws, ga, page_size=16, reps=5):
     return res
 
 
+def fp8_rows(dims, dga, ctx, max_ctx, ws, reps=5):
+    """FP8 (OCP E4M3) GA pool, timed apart from the step: the decode step's GA
+    attention (128 sequences at the contexts the timed steps left) over the
+    pool quantised by the library's append with one scale per KV head (an amax
+    calibration of N(0,1) data: 4.5 / 448), next to the same call over the bf16
+    pool.  The quantising append of all cached positions is timed too."""
+    dev = "cuda"
+    ctx_list = [int(c) for c in ctx.cpu()]
+    Bd = len(ctx_list)
+    rows = dga.k_cache.shape[0]
+    k8 = torch.empty((rows, HKV, DQK), dtype=torch.uint8, device=dev)
+    v8 = torch.empty((rows, HKV, DV), dtype=torch.uint8, device=dev)
+    ks = torch.full((HKV,), 4.5 / 448, dtype=torch.float32, device=dev)
+    vs = torch.full((HKV,), 4.5 / 448, dtype=torch.float32, device=dev)
+    # every cached row of the pool, as one packed append per sequence region
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(dga.kv_capacity.cpu().numpy())]), dtype=torch.int32, device=dev)
+    zeros = torch.zeros(Bd, dtype=torch.int32, device=dev)
+    app = lambda: B.mimo_kv_append_fp8(dims, dga.k_cache, dga.v_cache, cu, zeros, Bd, rows, k8, v8, dga.kv_base,
+                                       dga.kv_capacity, ks, vs)
+    ms_app = _time_ms(app, 2)
+    out = torch.empty((Bd, HQ, DV), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((Bd, HQ), dtype=torch.float32, device=dev)
+    f8 = lambda: B.mimo_attn_decode_fp8(dims, dga.q, dga.k_new, dga.v_new, k8, v8, dga.kv_base, ks, vs, ctx, Bd,
+                                        max_ctx, 0, dga.sink, out, lse, ws)
+    bf = lambda: B.mimo_attn_decode(dims, 1, dga.q, dga.k_new, dga.v_new, dga.k_cache, dga.v_cache, dga.kv_base,
+                                    ctx, Bd, max_ctx, 0, dga.sink, out, lse, ws)
+    ms_8, ms_b = _time_ms(f8, reps), _time_ms(bf, reps)
+    cached = int(sum(ctx_list))
+    nbytes = cached * KV_TOKEN_BYTES // 2 + Bd * TOKEN_BYTES
+    res = {"decode_ga_fp8": {"workload": "decode step B=128, GA pool of E4M3 codes (1280 B per cached token)",
+                             "ms": ms_8, "tokens/s": Bd / (ms_8 * 1e-3), "GB/s": nbytes / (ms_8 * 1e-3) / 1e9,
+                             "frac_hbm_peak": nbytes / (ms_8 * 1e-3) / 1e9 / PEAK_HBM_GBPS, "bf16_pool_ms": ms_b,
+                             "speedup_vs_bf16_pool": ms_b / ms_8},
+           "append_fp8_bulk": {"workload": f"quantise {rows} pool rows (bf16 -> E4M3)", "ms": ms_app,
+                               "GB/s": rows * (KV_TOKEN_BYTES + KV_TOKEN_BYTES // 2) / (ms_app * 1e-3) / 1e9}}
+    del k8, v8
+    torch.cuda.empty_cache()
+    return res
+
+
 def _time_ms(call, reps):
     call()
     torch.cuda.synchronize()
@@ -483,8 +523,9 @@ def main():
         "breakdown": breakdown,
         "roofline": roof,
         "device": dev_ctx,
-        # Rows beyond the step (continuing cached sequences, paged pool); not part of `value`.
-        "next_rows": {**chunk_rows(dims, ga, swa), **paged_rows(dims, dga, ctx_ga, max_ctx, ws, ga)},
+        # Rows beyond the step (continuing cached sequences, paged pool, FP8 pool); not part of `value`.
+        "next_rows": {**chunk_rows(dims, ga, swa), **paged_rows(dims, dga, ctx_ga, max_ctx, ws, ga),
+                      **fp8_rows(dims, dga, ctx_ga, max_ctx, ws)},
     }
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample (cpu_baseline)")

@@ -27,7 +27,8 @@ MIMO_ERR_HIP = 4
 
 ENTRY_POINTS = ("mimo_attn_prefill", "mimo_attn_prefill_chunk", "mimo_attn_decode_workspace_size",
                 "mimo_attn_decode", "mimo_kv_append", "mimo_kv_append_paged", "mimo_attn_decode_paged",
-                "mimo_attn_prefill_chunk_paged", "mimo_status_string", "mimo_last_error", "mimo_abi_version")
+                "mimo_attn_prefill_chunk_paged", "mimo_kv_append_fp8", "mimo_attn_decode_fp8", "mimo_status_string",
+                "mimo_last_error", "mimo_abi_version")
 
 
 class mimo_attn_dims(ctypes.Structure):
@@ -83,6 +84,11 @@ def lib() -> ctypes.CDLL:
         L.mimo_attn_prefill_chunk_paged.restype = ctypes.c_int
         L.mimo_attn_prefill_chunk_paged.argtypes = [dims_p, _P, _P, _P, _P, _I32, _I32, _P, _P, pages_p, _P, _P, _P,
                                                     _P, _P]
+        L.mimo_kv_append_fp8.restype = ctypes.c_int
+        L.mimo_kv_append_fp8.argtypes = [dims_p, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P]
+        L.mimo_attn_decode_fp8.restype = ctypes.c_int
+        L.mimo_attn_decode_fp8.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P,
+                                           _P, _SZ, _P]
         L.mimo_status_string.restype = ctypes.c_char_p
         L.mimo_status_string.argtypes = [ctypes.c_int]
         L.mimo_last_error.restype = ctypes.c_char_p
@@ -200,6 +206,22 @@ def mimo_attn_prefill_chunk_paged(dims: mimo_attn_dims, q, k, v, cu_newlens, num
                                                _ptr(ctx_lens), _ptr(sink), _ptr(out), _ptr(lse), _stream(stream)))
 
 
+def mimo_kv_append_fp8(dims: mimo_attn_dims, k, v, cu_newlens, ctx_lens, batch: int, total_new: int, k_cache, v_cache,
+                       kv_base, kv_capacity, k_scale, v_scale, stream=None) -> None:
+    _check(lib().mimo_kv_append_fp8(ctypes.byref(dims), _ptr(k), _ptr(v), _ptr(cu_newlens), _ptr(ctx_lens), batch,
+                                    total_new, _ptr(k_cache), _ptr(v_cache), _ptr(kv_base), _ptr(kv_capacity),
+                                    _ptr(k_scale), _ptr(v_scale), _stream(stream)))
+
+
+def mimo_attn_decode_fp8(dims: mimo_attn_dims, q, k_new, v_new, k_cache, v_cache, kv_base, k_scale, v_scale, ctx_lens,
+                         batch: int, max_ctx: int, split_tokens: int, sink, out, lse, workspace, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().mimo_attn_decode_fp8(ctypes.byref(dims), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                      _ptr(v_cache), _ptr(kv_base), _ptr(k_scale), _ptr(v_scale), _ptr(ctx_lens),
+                                      batch, max_ctx, split_tokens, _ptr(sink), _ptr(out), _ptr(lse), _ptr(workspace),
+                                      ws_bytes, _stream(stream)))
+
+
 # -- tensor-level conveniences (allocation of outputs + the calls above) -------
 
 def prefill(q, k, v, cu_seqlens, max_seqlen: int, layer_type: int, sink=None, dims=None, out=None, lse=None,
@@ -291,4 +313,29 @@ def prefill_chunk_paged(q, k, v, cu_newlens, max_newlen: int, k_pool, v_pool, bl
     pages = make_pages(block_table, page_size, k_pool.shape[0] // page_size)
     mimo_attn_prefill_chunk_paged(dims, q, k, v, cu_newlens, cu_newlens.numel() - 1, max_newlen, k_pool, v_pool,
                                   pages, ctx_lens, sink, out, lse, stream)
+    return out, lse
+
+
+def kv_append_fp8(k, v, cu_newlens, ctx_lens, k_cache, v_cache, kv_base, kv_capacity, k_scale, v_scale, dims=None,
+                  total_new: Optional[int] = None, stream=None):
+    dims = dims or make_dims()
+    if total_new is None:
+        total_new = k.shape[0]
+    mimo_kv_append_fp8(dims, k, v, cu_newlens, ctx_lens, cu_newlens.numel() - 1, total_new, k_cache, v_cache, kv_base,
+                       kv_capacity, k_scale, v_scale, stream)
+
+
+def decode_fp8(q, k_new, v_new, k_cache, v_cache, kv_base, k_scale, v_scale, ctx_lens, max_ctx: int, sink=None,
+               split_tokens: int = 0, dims=None, out=None, lse=None, workspace=None, stream=None):
+    dims = dims or make_dims()
+    B = q.shape[0]
+    if out is None:
+        out = torch.empty((B, dims.num_q_heads, dims.head_dim_v), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, dims.num_q_heads), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = mimo_attn_decode_workspace_size(dims, MIMO_LAYER_GA, B, max_ctx, split_tokens)
+        workspace = torch.empty(max(nbytes, 16) // 4 + 4, dtype=torch.float32, device=q.device)
+    mimo_attn_decode_fp8(dims, q, k_new, v_new, k_cache, v_cache, kv_base, k_scale, v_scale, ctx_lens, B, max_ctx,
+                         split_tokens, sink, out, lse, workspace, stream)
     return out, lse

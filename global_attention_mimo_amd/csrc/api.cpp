@@ -182,11 +182,29 @@ size_t mimo_attn_decode_workspace_size(const mimo_attn_dims* dims, int layer_typ
 
 namespace {
 
+// FP8 GA pool of a decode or append call: codes and per-KV-head scales.
+struct Fp8Pool {
+    const uint8_t* k = nullptr;
+    const uint8_t* v = nullptr;
+    const float* k_scale = nullptr;
+    const float* v_scale = nullptr;
+};
+
+int check_fp8(const Fp8Pool& f) {
+    if (!f.k || !f.v) return fail(MIMO_ERR_INVALID_ARG, "k_cache and v_cache must be non-NULL");
+    if (!aligned16(f.k) || !aligned16(f.v))
+        return fail(MIMO_ERR_INVALID_ARG, "k_cache and v_cache must be 16-byte aligned");
+    if (!f.k_scale || !f.v_scale) return fail(MIMO_ERR_INVALID_ARG, "k_scale and v_scale must be non-NULL");
+    if ((reinterpret_cast<uintptr_t>(f.k_scale) | reinterpret_cast<uintptr_t>(f.v_scale)) & 3u)
+        return fail(MIMO_ERR_INVALID_ARG, "k_scale and v_scale must be 4-byte aligned");
+    return MIMO_OK;
+}
+
 int decode_impl(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, const uint16_t* k_new,
                 const uint16_t* v_new, const uint16_t* k_cache, const uint16_t* v_cache, const int64_t* kv_base,
                 const mimo_kv_pages* pages, const int32_t* ctx_lens, int32_t batch, int32_t max_ctx,
                 int32_t split_tokens, const float* sink, uint16_t* out, float* lse, void* workspace,
-                size_t workspace_bytes, hipStream_t stream) {
+                size_t workspace_bytes, hipStream_t stream, const Fp8Pool* fp8 = nullptr) {
     if (int st = check_dims(dims, layer_type, 2)) return st;
     if (!q || !k_new || !v_new || !ctx_lens || !out)
         return fail(MIMO_ERR_INVALID_ARG, "q, k_new, v_new, ctx_lens and out must be non-NULL");
@@ -194,9 +212,13 @@ int decode_impl(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, c
         return fail(MIMO_ERR_INVALID_ARG, "q, k_new, v_new and out must be 16-byte aligned");
     if (batch < 1) return fail(MIMO_ERR_INVALID_ARG, "batch %d < 1", batch);
     if (max_ctx < 0 || max_ctx == INT32_MAX) return fail(MIMO_ERR_INVALID_ARG, "max_ctx %d out of range", max_ctx);
-    if (!k_cache || !v_cache) return fail(MIMO_ERR_INVALID_ARG, "k_cache and v_cache must be non-NULL");
-    if (!aligned16(k_cache) || !aligned16(v_cache))
-        return fail(MIMO_ERR_INVALID_ARG, "k_cache and v_cache must be 16-byte aligned");
+    if (fp8) {
+        if (int st = check_fp8(*fp8)) return st;
+    } else {
+        if (!k_cache || !v_cache) return fail(MIMO_ERR_INVALID_ARG, "k_cache and v_cache must be non-NULL");
+        if (!aligned16(k_cache) || !aligned16(v_cache))
+            return fail(MIMO_ERR_INVALID_ARG, "k_cache and v_cache must be 16-byte aligned");
+    }
     const int split = effective_split(split_tokens);
     mimo::PageTable pt;
     if (pages) {
@@ -209,7 +231,7 @@ int decode_impl(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, c
                         span, P, mimo::kMaxSplitPages);
     } else {
         // The kernels address a sequence's cache rows with 32-bit byte offsets.
-        const int64_t row_bytes = (int64_t)dims->num_kv_heads * dims->head_dim_qk * 2;
+        const int64_t row_bytes = (int64_t)dims->num_kv_heads * dims->head_dim_qk * (fp8 ? 1 : 2);
         const int64_t rows = layer_type == MIMO_LAYER_SWA ? (int64_t)dims->sliding_window : (int64_t)max_ctx + 1;
         if (rows * row_bytes > INT32_MAX)
             return fail(MIMO_ERR_UNSUPPORTED, "a sequence's cached keys exceed 2 GiB (%lld rows of %lld bytes)",
@@ -219,6 +241,12 @@ int decode_impl(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, c
                        max_ctx, split, dims->num_q_heads, dims->num_kv_heads, dims->sliding_window,
                        dims->softmax_scale, dims->value_scale};
     a.pages = pt;
+    if (fp8) {
+        a.k_cache8 = fp8->k;
+        a.v_cache8 = fp8->v;
+        a.k_scale = fp8->k_scale;
+        a.v_scale = fp8->v_scale;
+    }
     if (layer_type == MIMO_LAYER_SWA) {
         if (batch > INT32_MAX / 2) return fail(MIMO_ERR_UNSUPPORTED, "batch too large");
         return hip_status(mimo::launch_decode_swa(a, stream), "SWA decode launch");
@@ -236,12 +264,18 @@ int decode_impl(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, c
 int kv_append_impl(const mimo_attn_dims* dims, int layer_type, const uint16_t* k, const uint16_t* v,
                    const int32_t* cu_newlens, const int32_t* ctx_lens, int32_t batch, int32_t total_new,
                    uint16_t* k_cache, uint16_t* v_cache, const int64_t* kv_base, const int64_t* kv_capacity,
-                   const mimo_kv_pages* pages, hipStream_t stream) {
+                   const mimo_kv_pages* pages, hipStream_t stream, const Fp8Pool* fp8 = nullptr) {
     if (int st = check_dims(dims, layer_type, 2)) return st;
-    if (!k || !v || !cu_newlens || !ctx_lens || !k_cache || !v_cache)
-        return fail(MIMO_ERR_INVALID_ARG, "k, v, cu_newlens, ctx_lens, k_cache and v_cache must be non-NULL");
-    if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
-        return fail(MIMO_ERR_INVALID_ARG, "k, v, k_cache and v_cache must be 16-byte aligned");
+    if (!k || !v || !cu_newlens || !ctx_lens)
+        return fail(MIMO_ERR_INVALID_ARG, "k, v, cu_newlens and ctx_lens must be non-NULL");
+    if (!aligned16(k) || !aligned16(v)) return fail(MIMO_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
+    if (fp8) {
+        if (int st = check_fp8(*fp8)) return st;
+    } else {
+        if (!k_cache || !v_cache) return fail(MIMO_ERR_INVALID_ARG, "k_cache and v_cache must be non-NULL");
+        if (!aligned16(k_cache) || !aligned16(v_cache))
+            return fail(MIMO_ERR_INVALID_ARG, "k_cache and v_cache must be 16-byte aligned");
+    }
     if (batch < 1) return fail(MIMO_ERR_INVALID_ARG, "batch %d < 1", batch);
     if (total_new < 0) return fail(MIMO_ERR_INVALID_ARG, "total_new %d is negative", total_new);
     mimo::PageTable pt;
@@ -256,6 +290,12 @@ int kv_append_impl(const mimo_attn_dims* dims, int layer_type, const uint16_t* k
     mimo::AppendArgs a{k, v, cu_newlens, ctx_lens, k_cache, v_cache, kv_base, kv_capacity, batch, total_new,
                        dims->num_kv_heads, dims->sliding_window, layer_type == MIMO_LAYER_SWA};
     a.pages = pt;
+    if (fp8) {
+        a.k_cache8 = const_cast<uint8_t*>(fp8->k);
+        a.v_cache8 = const_cast<uint8_t*>(fp8->v);
+        a.k_scale = fp8->k_scale;
+        a.v_scale = fp8->v_scale;
+    }
     return hip_status(mimo::launch_kv_append(a, stream), "KV append launch");
 }
 
@@ -295,6 +335,25 @@ int mimo_kv_append_paged(const mimo_attn_dims* dims, const uint16_t* k, const ui
     if (!pages) return fail(MIMO_ERR_INVALID_ARG, "pages is NULL");
     return kv_append_impl(dims, MIMO_LAYER_GA, k, v, cu_newlens, ctx_lens, batch, total_new, k_cache, v_cache,
                           nullptr, nullptr, pages, stream);
+}
+
+int mimo_attn_decode_fp8(const mimo_attn_dims* dims, const uint16_t* q, const uint16_t* k_new,
+                         const uint16_t* v_new, const uint8_t* k_cache, const uint8_t* v_cache, const int64_t* kv_base,
+                         const float* k_scale, const float* v_scale, const int32_t* ctx_lens, int32_t batch,
+                         int32_t max_ctx, int32_t split_tokens, const float* sink, uint16_t* out, float* lse,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    const Fp8Pool f{k_cache, v_cache, k_scale, v_scale};
+    return decode_impl(dims, MIMO_LAYER_GA, q, k_new, v_new, nullptr, nullptr, kv_base, nullptr, ctx_lens, batch,
+                       max_ctx, split_tokens, sink, out, lse, workspace, workspace_bytes, stream, &f);
+}
+
+int mimo_kv_append_fp8(const mimo_attn_dims* dims, const uint16_t* k, const uint16_t* v, const int32_t* cu_newlens,
+                       const int32_t* ctx_lens, int32_t batch, int32_t total_new, uint8_t* k_cache, uint8_t* v_cache,
+                       const int64_t* kv_base, const int64_t* kv_capacity, const float* k_scale,
+                       const float* v_scale, hipStream_t stream) {
+    const Fp8Pool f{k_cache, v_cache, k_scale, v_scale};
+    return kv_append_impl(dims, MIMO_LAYER_GA, k, v, cu_newlens, ctx_lens, batch, total_new, nullptr, nullptr,
+                          kv_base, kv_capacity, nullptr, stream, &f);
 }
 
 const char* mimo_status_string(int status) {

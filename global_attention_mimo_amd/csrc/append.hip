@@ -11,6 +11,8 @@
 //
 // One thread moves one 16-byte chunk: a token is Hkv*24 chunks of K and
 // Hkv*16 chunks of V, so consecutive threads copy consecutive bytes of a row.
+// An FP8 GA pool stores OCP E4M3 codes of the values divided by a per-KV-head
+// scale instead (a storage format of the same cache).
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -62,10 +64,64 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     }
 }
 
+// FP8 GA pool: one thread turns 8 bf16 elements (16 bytes) of a new token into
+// 8 E4M3 codes (8 bytes).  A token is Hkv*24 such units of K then Hkv*16 of V;
+// unit c of K belongs to KV head c / 24, of V to head c / 16.  Each element is
+// divided by its head's scale in fp32 (IEEE division), clamped to +-448 (the
+// conversion does not saturate by itself) and rounded to nearest-even by the
+// hardware conversion.
+__global__ __launch_bounds__(256) void kv_append_fp8_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const int32_t* __restrict__ cu_newlens,
+    const int32_t* __restrict__ ctx_lens, int batch, int total_new, uint8_t* __restrict__ k_cache,
+    uint8_t* __restrict__ v_cache, const int64_t* __restrict__ kv_base, const int64_t* __restrict__ kv_capacity,
+    const float* __restrict__ k_scale, const float* __restrict__ v_scale, int hkv) {
+    const int kunits = hkv * (kDqk / 8), per_tok = hkv * ((kDqk + kDv) / 8);
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t tok = idx / per_tok;
+    const int c = (int)(idx % per_tok);
+    if (tok >= total_new) return;
+    int lo = 0, hi = batch - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cu_newlens[mid] <= tok) lo = mid; else hi = mid - 1;
+    }
+    const int b = lo;
+    const int n = cu_newlens[b + 1] - cu_newlens[b];
+    const int64_t ctx = ctx_lens[b];
+    if (ctx + n > kv_capacity[b]) return;  // the whole sequence is refused
+    const int64_t row = kv_base[b] + ctx + (tok - cu_newlens[b]);
+    const bool is_k = c < kunits;
+    const int u = is_k ? c : c - kunits;
+    const float scale = is_k ? k_scale[u / (kDqk / 8)] : v_scale[u / (kDv / 8)];
+    const uint16_t* src = is_k ? k + tok * hkv * kDqk + u * 8 : v + tok * hkv * kDv + u * 8;
+    uint8_t* dst = is_k ? k_cache + row * hkv * kDqk + u * 8 : v_cache + row * hkv * kDv + u * 8;
+    const u32x4 w = *reinterpret_cast<const u32x4*>(src);
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+        x[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = fminf(fmaxf(x[i] / scale, -448.0f), 448.0f);
+    int lo4 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+    lo4 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], lo4, true);
+    int hi4 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4], x[5], 0, false);
+    hi4 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6], x[7], hi4, true);
+    *reinterpret_cast<u32x2*>(dst) = u32x2{(uint32_t)lo4, (uint32_t)hi4};
+}
+
 }  // namespace
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream) {
     if (a.total_new <= 0) return hipSuccess;
+    if (a.k_cache8) {
+        const int64_t threads = (int64_t)a.total_new * a.hkv * ((kDqk + kDv) / 8);
+        hipLaunchKernelGGL(kv_append_fp8_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a.k,
+                           a.v, a.cu_newlens, a.ctx_lens, a.batch, a.total_new, a.k_cache8, a.v_cache8, a.kv_base,
+                           a.kv_capacity, a.k_scale, a.v_scale, a.hkv);
+        return hipGetLastError();
+    }
     const int64_t threads = (int64_t)a.total_new * a.hkv * ((kDqk + kDv) / 8);
     const int64_t blocks = (threads + 255) / 256;
     hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a.k, a.v, a.cu_newlens,

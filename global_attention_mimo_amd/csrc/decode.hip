@@ -52,6 +52,10 @@ constexpr int kBlockLdsBytes = 4 * kVTileBytes;   // one V tile per wave
 #define MIMO_GA_DECODE_DEPTH 2
 #endif
 constexpr int kGaDepth = MIMO_GA_DECODE_DEPTH;    // GA split: tiles in flight beyond the current one
+#ifndef MIMO_GA_FP8_DEPTH
+#define MIMO_GA_FP8_DEPTH 3
+#endif
+constexpr int kFp8Depth = MIMO_GA_FP8_DEPTH;      // FP8 split: a tile is half the bytes, so more in flight
 constexpr int kSwaDepth = 1;                      // SWA: a wave owns at most a few tiles
 
 // One 32-key tile of a wave: where its K and V rows come from.
@@ -442,6 +446,220 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     for (int db = 0; db < kDv / 16; ++db) *reinterpret_cast<f32x4*>(ws_o + row * kDv + 16 * db + 4 * G) = acc.o[db];
 }
 
+// ---------------------------------------------------------------------------
+// FP8 GA pool: OCP E4M3 codes, one fp32 scale per KV head for K and for V, so a
+// cached token is 768 B of K and 512 B of V for the 4 heads (half the bf16
+// pool).  Codes widen exactly to bf16 in registers (an E4M3 value has at most 4
+// significant bits and an exponent inside bf16's range), and
+// the bf16 MFMA tile runs on them unchanged; the K scale joins the score
+// multiplier, and the V scale multiplies the split's partial output once.  The
+// contraction over d is permuted so that one 16-byte load feeds two k-steps:
+// k-steps 2u and 2u+1 of lane group G = lane/16 take d = 64u + 16G .. +7 and
+// 64u + 16G + 8 .. +15, for K and for Q alike (a dot product does not depend
+// on the order of its terms).  The new token (bf16 k_new, v_new) is folded in
+// after the cached tiles in fp32, so its weight is not rounded to bf16.
+
+// 4 codes (one dword) -> 4 bf16 (two dwords), exact: v_cvt_scalef32_pk_bf16_fp8
+// with scale 1 turns the two codes of a 16-bit word straight into a bf16 pair.
+// (The route through v_cvt_pk_f32_fp8 and a byte permute was miscompiled here:
+// the compiler read both floats of the pair from the first register.)
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
+    return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true))};
+}
+
+// 8 codes (two dwords) -> one bf16x8 operand.
+__device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+    const u32x2 a = fp8x4_to_bf16x4(w0), c = fp8x4_to_bf16x4(w1);
+    return u32x4{a[0], a[1], c[0], c[1]};
+}
+
+// Lane-constant byte offsets inside an FP8 tile.  K: lane l reads keys l%16
+// (and +16), 16 codes at d = 64u + 16(l/16) for u = 0..2.  V: load i reads key
+// 8i + l/8, 16 codes at columns 16(l%8) .. +15.
+struct Fp8LaneOffsets {
+    int k0, k1, v;
+};
+
+__device__ __forceinline__ Fp8LaneOffsets fp8_lane_offsets(int lane, int g, int rowk8, int rowv8) {
+    Fp8LaneOffsets o;
+    o.k0 = (lane & 15) * rowk8 + g * kDqk + (lane >> 4) * 16;
+    o.k1 = o.k0 + 16 * rowk8;
+    o.v = (lane >> 3) * rowv8 + g * kDv + (lane & 7) * 16;
+    return o;
+}
+
+__device__ __forceinline__ void issue_k8(const TileSrc& t, const Fp8LaneOffsets& lo, u32x4 (&k)[6]) {
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+        k[u] = __builtin_amdgcn_raw_buffer_load_b128(t.k, lo.k0 + 64 * u, t.koff, 0);
+        k[3 + u] = __builtin_amdgcn_raw_buffer_load_b128(t.k, lo.k1 + 64 * u, t.koff, 0);
+    }
+}
+
+__device__ __forceinline__ void issue_v8(const TileSrc& t, const Fp8LaneOffsets& lo, int rowv8, u32x4 (&v)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(t.v, lo.v, t.voff + 8 * i * rowv8, 0);
+}
+
+// V codes to the wave's bf16 LDS tile, in the layout stage_v writes: load i
+// holds row r = 8i + l/8, bf16 chunks c = 2(l%8) and c+1, stored at chunk
+// positions c ^ 2(r%4) and that + 1 (c is even), i.e. one 32-byte run.
+__device__ __forceinline__ void stage_v8(const u32x4 (&v)[4], char* vbuf, int lane) {
+    const int r0 = lane >> 3, c0 = 2 * (lane & 7);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 8 * i + r0;
+        char* dst = vbuf + r * (kDv * 2) + ((c0 ^ (2 * (r0 & 3))) * 16);
+        *reinterpret_cast<u32x4*>(dst) = fp8x8_to_bf16x8(v[i][0], v[i][1]);
+        *reinterpret_cast<u32x4*>(dst + 16) = fp8x8_to_bf16x8(v[i][2], v[i][3]);
+    }
+    wave_lds_fence();
+}
+
+// K codes to attend_tile's A operands: k-step 2u+h of key block blk comes from
+// half h of load 3*blk + u.
+__device__ __forceinline__ void widen_k8(const u32x4 (&k8)[6], u32x4 (&kb)[12]) {
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            kb[6 * blk + 2 * u] = fp8x8_to_bf16x8(k8[3 * blk + u][0], k8[3 * blk + u][1]);
+            kb[6 * blk + 2 * u + 1] = fp8x8_to_bf16x8(k8[3 * blk + u][2], k8[3 * blk + u][3]);
+        }
+}
+
+// Q^T fragments in the permuted contraction order: qf[2u+h] holds
+// q[16*g + lane%16][64u + 16(lane/16) + 8h .. +7].
+__device__ __forceinline__ void load_q_perm(bf16x8 (&qf)[kDqk / 32], const uint16_t* q, int b, int g, int hq,
+                                            int lane) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(q + ((size_t)b * hq + g * kGroup + (lane & 15)) * kDqk);
+    const int G = lane >> 4;
+#pragma unroll
+    for (int u = 0; u < 3; ++u)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) qf[2 * u + h] = __builtin_bit_cast(bf16x8, src[8 * u + 2 * G + h]);
+}
+
+// As run_tiles, over FP8 tiles (D + 1 register sets of 6 K and 4 V loads).
+template <int D, class GetTile>
+__device__ __forceinline__ void run_tiles_fp8(WaveAcc& acc, const bf16x8 (&qf)[kDqk / 32], char* vbuf, int ntiles,
+                                              const GetTile& get, const Fp8LaneOffsets& lo, int rowv8, float c_log2,
+                                              int lane) {
+    if (ntiles <= 0) return;
+    u32x4 kr[D + 1][6], vr[D + 1][4];
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+        const TileSrc t = get(j);
+        issue_k8(t, lo, kr[j]);
+        issue_v8(t, lo, rowv8, vr[j]);
+    }
+    for (int i0 = 0; i0 < ntiles; i0 += D + 1) {
+#pragma unroll
+        for (int j = 0; j <= D; ++j) {
+            const TileSrc t = get(i0 + j + D);
+            issue_k8(t, lo, kr[(j + D) % (D + 1)]);
+            issue_v8(t, lo, rowv8, vr[(j + D) % (D + 1)]);
+            stage_v8(vr[j], vbuf, lane);
+            u32x4 kb[12];
+            widen_k8(kr[j], kb);
+            attend_tile(acc, qf, kb, vbuf, get(i0 + j).nvalid, c_log2, lane);
+        }
+    }
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// Folds the new token (bf16 k_new/v_new row of group g) into a wave's state in
+// fp32: its score from the permuted Q fragments (each lane a 48-term partial,
+// summed over the head's 4 lanes), then one more online-softmax step.  acc.l
+// must already be the full (cross-lane) sum.
+__device__ __forceinline__ void fold_new_token(WaveAcc& acc, const bf16x8 (&qf)[kDqk / 32], const uint16_t* krow,
+                                               const uint16_t* vrow, float c_log2, int lane) {
+    const int G = lane >> 4;
+    const u32x4* kn = reinterpret_cast<const u32x4*>(krow);
+    float dot = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 3; ++u)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const u32x4 kw = kn[8 * u + 2 * G + h];
+            const u32x4 qw = __builtin_bit_cast(u32x4, qf[2 * u + h]);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                dot += bf16_lo(qw[t]) * bf16_lo(kw[t]) + bf16_hi(qw[t]) * bf16_hi(kw[t]);
+        }
+    dot += __shfl_xor(dot, 16);
+    dot += __shfl_xor(dot, 32);
+    const float s = dot * c_log2;
+    const float m_new = fmaxf(acc.m, s);
+    const float alpha = fast_exp2(acc.m - m_new), pn = fast_exp2(s - m_new);
+#pragma unroll
+    for (int db = 0; db < kDv / 16; ++db) {
+        const u32x2 vw = *reinterpret_cast<const u32x2*>(vrow + 16 * db + 4 * G);
+        const f32x4 vv = {bf16_lo(vw[0]), bf16_hi(vw[0]), bf16_lo(vw[1]), bf16_hi(vw[1])};
+        acc.o[db] = acc.o[db] * alpha + pn * vv;
+    }
+    acc.l = acc.l * alpha + pn;
+    acc.m = m_new;
+}
+
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void ga_split_fp8_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const uint8_t* __restrict__ pool_k, const uint8_t* __restrict__ pool_v, const int64_t* __restrict__ kv_base,
+    const int32_t* __restrict__ ctx_lens, const float* __restrict__ k_scale, const float* __restrict__ v_scale,
+    int hq, int hkv, int split, int nsplit, float c_log2, float* __restrict__ ws_ml, float* __restrict__ ws_o) {
+    __shared__ __attribute__((aligned(1024))) char lds[kBlockLdsBytes];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int s = blockIdx.x, b = blockIdx.y;
+    const int g = blockIdx.z * 4 + wave;
+    if (g >= hkv) return;
+    const int p = ctx_lens[b];
+    const int k0 = s * split;
+    if (k0 > p) return;
+    const int k1 = min(k0 + split, p + 1);  // keys [k0, k1) of this split
+    const int kend = min(k1, p);            // of which [k0, kend) live in the pool
+    const int rowk8 = hkv * kDqk, rowv8 = hkv * kDv;
+
+    bf16x8 qf[kDqk / 32];
+    load_q_perm(qf, q, b, g, hq, lane);
+    const float ks = k_scale[g], vs = v_scale[g];
+    const size_t base = (size_t)kv_base[b];
+    const rsrc_t pk = make_rsrc(pool_k + base * rowk8, (uint32_t)p * rowk8);
+    const rsrc_t pv = make_rsrc(pool_v + base * rowv8, (uint32_t)p * rowv8);
+    const rsrc_t none = make_rsrc(pool_k, 0);
+    const int npool = (kend - k0 + kTile - 1) / kTile;
+    auto get = [&](int i) -> TileSrc {
+        if (i < npool) {
+            const int j0 = k0 + i * kTile;
+            return TileSrc{pk, pv, j0 * rowk8, j0 * rowv8, min(kend - j0, kTile)};
+        }
+        return TileSrc{none, none, 0, 0, 0};
+    };
+    const Fp8LaneOffsets lo = fp8_lane_offsets(lane, g, rowk8, rowv8);
+    WaveAcc acc;
+    acc_init(acc);
+    run_tiles_fp8<kFp8Depth>(acc, qf, lds + wave * kVTileBytes, npool, get, lo, rowv8, c_log2 * ks, lane);
+    acc.l += __shfl_xor(acc.l, 16);
+    acc.l += __shfl_xor(acc.l, 32);
+#pragma unroll
+    for (int db = 0; db < kDv / 16; ++db) acc.o[db] *= vs;
+    if (p < k1)
+        fold_new_token(acc, qf, k_new + ((size_t)b * hkv + g) * kDqk, v_new + ((size_t)b * hkv + g) * kDv, c_log2,
+                       lane);
+
+    const int G = lane >> 4, h = lane & 15;
+    const size_t row = ((size_t)b * nsplit + s) * hq + g * kGroup + h;
+    if (G == 0) {
+        ws_ml[row * 2 + 0] = acc.m;
+        ws_ml[row * 2 + 1] = acc.l;
+    }
+#pragma unroll
+    for (int db = 0; db < kDv / 16; ++db) *reinterpret_cast<f32x4*>(ws_o + row * kDv + 16 * db + 4 * G) = acc.o[db];
+}
+
 // Merge of the splits of one sequence: block (b, 16 heads), thread = (head, 8 columns).
 __global__ __launch_bounds__(256) void ga_combine_kernel(const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
                                                          const int32_t* __restrict__ ctx_lens, const float* __restrict__ sink,
@@ -497,11 +715,17 @@ hipError_t launch_decode_ga(const DecodeArgs& a, hipStream_t stream) {
     const int nsplit = ga_num_splits(a.max_ctx, a.split);
     float* ws_ml = static_cast<float*>(a.workspace);
     float* ws_o = ws_ml + (size_t)a.batch * nsplit * a.hq * 2;
-    hipLaunchKernelGGL(a.pages.table ? ga_split_kernel<true> : ga_split_kernel<false>,
-                       dim3(nsplit, a.batch, (a.hkv + 3) / 4), dim3(256), 0, stream, a.q, a.k_new, a.v_new,
-                       a.k_cache, a.v_cache, a.kv_base, a.ctx_lens, a.hq, a.hkv, a.split, nsplit,
-                       a.softmax_scale * kLog2e, ws_ml, ws_o, a.pages.table, a.pages.max_blocks, a.pages.shift,
-                       a.pages.num_pages);
+    if (a.k_cache8) {
+        hipLaunchKernelGGL(ga_split_fp8_kernel, dim3(nsplit, a.batch, (a.hkv + 3) / 4), dim3(256), 0, stream, a.q,
+                           a.k_new, a.v_new, a.k_cache8, a.v_cache8, a.kv_base, a.ctx_lens, a.k_scale, a.v_scale,
+                           a.hq, a.hkv, a.split, nsplit, a.softmax_scale * kLog2e, ws_ml, ws_o);
+    } else {
+        hipLaunchKernelGGL(a.pages.table ? ga_split_kernel<true> : ga_split_kernel<false>,
+                           dim3(nsplit, a.batch, (a.hkv + 3) / 4), dim3(256), 0, stream, a.q, a.k_new, a.v_new,
+                           a.k_cache, a.v_cache, a.kv_base, a.ctx_lens, a.hq, a.hkv, a.split, nsplit,
+                           a.softmax_scale * kLog2e, ws_ml, ws_o, a.pages.table, a.pages.max_blocks, a.pages.shift,
+                           a.pages.num_pages);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(ga_combine_kernel, dim3(a.batch, (a.hq + kGroup - 1) / kGroup), dim3(256), 0, stream, ws_ml, ws_o,

@@ -52,6 +52,11 @@ struct DecodeArgs {
     int batch, max_ctx, split, hq, hkv, window;
     float softmax_scale, value_scale;
     PageTable pages;
+    // FP8 GA pool (E4M3 codes) and its per-KV-head scales; k_cache/v_cache unused then.
+    const uint8_t* k_cache8 = nullptr;
+    const uint8_t* v_cache8 = nullptr;
+    const float* k_scale = nullptr;
+    const float* v_scale = nullptr;
 };
 // Pages a GA split kernel preloads per workgroup (two per lane of a wave).
 constexpr int kMaxSplitPages = 128;
@@ -76,6 +81,11 @@ struct AppendArgs {
     int batch, total_new, hkv, window;
     bool swa;
     PageTable pages;
+    // FP8 GA pool: new tokens are quantised to E4M3 codes under per-KV-head scales.
+    uint8_t* k_cache8 = nullptr;
+    uint8_t* v_cache8 = nullptr;
+    const float* k_scale = nullptr;
+    const float* v_scale = nullptr;
 };
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 

@@ -152,6 +152,20 @@ def paged_block_table(ctx_lens: Sequence[int], page_size: int, *, seed: int = 0,
     return table.to(device), npages
 
 
+def random_e4m3_codes(shape, *, seed: int = 0, device="cpu", chunk_elems: int = 1 << 28) -> torch.Tensor:
+    """Seeded uniform random OCP E4M3 codes (uint8) with the two NaN codes
+    (0x7f, 0xff) replaced by their finite neighbours 0x7e, 0xfe."""
+    g = _gen(seed, device)
+    out = torch.empty(shape, dtype=torch.uint8, device=device)
+    flat = out.view(-1)
+    for s in range(0, flat.numel(), chunk_elems):
+        part = torch.randint(0, 256, (min(chunk_elems, flat.numel() - s),), generator=g, device=device,
+                             dtype=torch.int32)
+        part = torch.where((part & 0x7F) == 0x7F, part ^ 1, part)
+        flat[s:s + part.numel()] = part.to(torch.uint8)
+    return out
+
+
 def bf16_bits(t: torch.Tensor) -> np.ndarray:
     """Host numpy uint16 view of a bf16 tensor's bit patterns."""
     if t.dtype != torch.bfloat16:

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MIMO_ATTN_ABI_VERSION 3
+#define MIMO_ATTN_ABI_VERSION 4
 
 /* Layer type: which key set a query sees (model doc, Key features; config
  * layer_types). */
@@ -284,6 +284,48 @@ int mimo_attn_prefill_chunk_paged(const mimo_attn_dims* dims,
                                   const uint16_t* k_cache, const uint16_t* v_cache,
                                   const mimo_kv_pages* pages, const int32_t* ctx_lens,
                                   const float* sink, uint16_t* out, float* lse, hipStream_t stream);
+
+/*
+ * FP8 GA pool.  A storage format of the same GA cache (the model doc defines
+ * none): OCP 8-bit floating point E4M3 codes ("OCP 8-bit Floating Point
+ * Specification (OFP8)": bias 7, largest finite 448, S.1111.111 = NaN, no
+ * infinities), half the bytes of the bf16 pool.  Each KV head g has one fp32
+ * scale for keys (k_scale[g]) and one for values (v_scale[g]): element x of
+ * head g is stored as E4M3(clamp(x / scale[g], -448, 448)) -- the division in
+ * fp32 (IEEE), the rounding to nearest-even -- and read back as
+ * value(code) * scale[g].
+ *
+ *   k_cache, v_cache  pool [N][Hkv][192] and [N][Hkv][128] of uint8 codes;
+ *                position j of sequence b lives in row kv_base[b] + j.
+ *   k_scale, v_scale  [Hkv] fp32 (device), positive and finite.
+ */
+
+/*
+ * mimo_kv_append for a GA layer whose cache is an FP8 pool: new tokens are
+ * quantised as above into rows kv_base[b] + position; capacity as for
+ * mimo_kv_append (a sequence past kv_capacity[b] is skipped entirely).
+ */
+int mimo_kv_append_fp8(const mimo_attn_dims* dims,
+                       const uint16_t* k, const uint16_t* v,
+                       const int32_t* cu_newlens, const int32_t* ctx_lens,
+                       int32_t batch, int32_t total_new,
+                       uint8_t* k_cache, uint8_t* v_cache,
+                       const int64_t* kv_base, const int64_t* kv_capacity,
+                       const float* k_scale, const float* v_scale, hipStream_t stream);
+
+/*
+ * GA decode (as mimo_attn_decode with layer_type GA) over an FP8 pool: cached
+ * positions j < p are read as value(code) * scale; the new token at p is read
+ * from k_new / v_new (bf16) as given.  Workspace: mimo_attn_decode_workspace_size
+ * (dims, MIMO_LAYER_GA, batch, max_ctx, split_tokens) bytes.
+ */
+int mimo_attn_decode_fp8(const mimo_attn_dims* dims,
+                         const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                         const uint8_t* k_cache, const uint8_t* v_cache, const int64_t* kv_base,
+                         const float* k_scale, const float* v_scale, const int32_t* ctx_lens,
+                         int32_t batch, int32_t max_ctx, int32_t split_tokens,
+                         const float* sink, uint16_t* out, float* lse,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static English name of a status code ("MIMO_OK", ...). */
 const char* mimo_status_string(int status);

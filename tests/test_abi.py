@@ -42,7 +42,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_version_and_status_strings(L):
-    assert B.mimo_abi_version() == 3
+    assert B.mimo_abi_version() == 4
     assert B.mimo_status_string(0) == "MIMO_OK"
     assert B.mimo_status_string(3) == "MIMO_ERR_WORKSPACE"
     assert B.mimo_status_string(99) == "MIMO_ERR_UNKNOWN"
@@ -257,6 +257,56 @@ def test_append_paged_rejects(L, case, status):
 def test_paged_empty_calls_are_ok(L):
     assert paged_chunk_call(L, maxlen=0) == B.MIMO_OK
     assert paged_append_call(L, total=0) == B.MIMO_OK
+
+
+def fp8_decode_call(L, q=FAKE, kc=FAKE, base=FAKE, ks=FAKE, vs=FAKE, ctx=FAKE, batch=2, max_ctx=100, ws=FAKE,
+                    ws_bytes=1 << 30, dims=None):
+    d = dims or B.make_dims()
+    return L.mimo_attn_decode_fp8(ctypes.byref(d), q, FAKE, FAKE, kc, FAKE, base, ks, vs, ctx, batch, max_ctx, 0,
+                                  None, FAKE, None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(q=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(kc=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(kc=FAKE_ODD), B.MIMO_ERR_INVALID_ARG),
+    (dict(base=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(ks=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(vs=FAKE + 2), B.MIMO_ERR_INVALID_ARG),
+    (dict(ctx=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(batch=0), B.MIMO_ERR_INVALID_ARG),
+    (dict(max_ctx=-1), B.MIMO_ERR_INVALID_ARG),
+    (dict(ws=None), B.MIMO_ERR_WORKSPACE),
+    (dict(max_ctx=2_800_000), B.MIMO_ERR_UNSUPPORTED),  # > 2 GiB of K codes for one sequence
+    (dict(dims=B.make_dims(head_dim_v=64)), B.MIMO_ERR_UNSUPPORTED),
+])
+def test_decode_fp8_rejects(L, case, status):
+    assert fp8_decode_call(L, **case) == status
+    assert B.mimo_last_error() != ""
+
+
+def fp8_append_call(L, k=FAKE, kc=FAKE, base=FAKE, cap=FAKE, ks=FAKE, vs=FAKE, batch=1, total=4):
+    return L.mimo_kv_append_fp8(ctypes.byref(B.make_dims()), k, FAKE, FAKE, FAKE, batch, total, kc, FAKE, base, cap,
+                                ks, vs, None)
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(k=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(kc=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(kc=FAKE_ODD), B.MIMO_ERR_INVALID_ARG),
+    (dict(base=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(cap=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(ks=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(vs=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(batch=0), B.MIMO_ERR_INVALID_ARG),
+    (dict(total=-1), B.MIMO_ERR_INVALID_ARG),
+])
+def test_append_fp8_rejects(L, case, status):
+    assert fp8_append_call(L, **case) == status
+
+
+def test_append_fp8_nothing_is_ok(L):
+    assert fp8_append_call(L, total=0) == B.MIMO_OK
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
