@@ -1,8 +1,9 @@
 """GPU parity of chunked prefill (new tokens continuing cached sequences) through
 the C ABI, against the fp64 oracle on host copies of the same buffers.
 
-The caches are filled by the library's own append from the sequences' first
-tokens; the chunk holds the rest.  Bars as in gpu_util.
+The GPU caches are filled by the library's append from the sequences' first
+tokens, the oracle's by its own append from host copies of the same tokens
+(checked equal byte for byte); the chunk holds the rest.  Bars as in gpu_util.
 """
 import numpy as np
 import pytest
@@ -42,12 +43,24 @@ def _caches(layer_type, lengths, headroom=8, window=129):
 
 
 def _fill(x, layer_type, cached, kc, vc, base, cap, window=129):
+    """Appends the cached prefixes on the GPU and, with the oracle, into host
+    caches of the same shape; returns the host caches after checking that the
+    two agree byte for byte."""
     pre, _, _ = _split(x, cached)
     cu_pre = synth.cu_from_lengths(cached, DEV)
     zeros = torch.zeros(len(cached), dtype=torch.int32, device=DEV)
+    kh, vh = np.zeros_like(bits(kc)), np.zeros_like(bits(vc))
     if sum(cached):
         B.kv_append(to_dev(x.k[pre]), to_dev(x.v[pre]), cu_pre, zeros, kc, vc, layer_type, kv_base=base,
                     kv_capacity=cap, dims=B.make_dims(sliding_window=window))
+        st = orc().kv_append(bits(x.k[pre]), bits(x.v[pre]), cu_pre.cpu().numpy(), zeros.cpu().numpy(), kh, vh,
+                             layer_type=layer_type, window=window,
+                             kv_base=None if base is None else base.cpu().numpy(),
+                             kv_capacity=None if cap is None else cap.cpu().numpy())
+        assert st == 0
+        torch.cuda.synchronize()
+    assert np.array_equal(bits(kc), kh) and np.array_equal(bits(vc), vh), "GPU append differs from the oracle's"
+    return kh, vh
 
 
 def _chunk(x, layer_type, cached, kc, vc, base, max_newlen=None, window=129):
@@ -71,10 +84,10 @@ def test_chunk_against_oracle_ragged(layer_type, window):
     log(f"[case] chunked prefill layer={layer_type} window={window} lengths={lengths} cached={cached}")
     x = synth.prefill_inputs(lengths, seed=40)
     kc, vc, base, cap = _caches(layer_type, lengths, window=window)
-    _fill(x, layer_type, cached, kc, vc, base, cap, window=window)
+    kh, vh = _fill(x, layer_type, cached, kc, vc, base, cap, window=window)
     out, lse, new, rest, cu_new, ctx = _chunk(x, layer_type, cached, kc, vc, base, window=window)
-    ro, rl = orc().prefill_chunk(bits(x.q[new]), bits(x.k[new]), bits(x.v[new]), cu_new.cpu().numpy(), bits(kc),
-                                 bits(vc), ctx.cpu().numpy(), layer_type=layer_type, window=window, scale=SCALE,
+    ro, rl = orc().prefill_chunk(bits(x.q[new]), bits(x.k[new]), bits(x.v[new]), cu_new.cpu().numpy(), kh,
+                                 vh, ctx.cpu().numpy(), layer_type=layer_type, window=window, scale=SCALE,
                                  sink=sink_array(x.sink), kv_base=None if base is None else base.cpu().numpy())
     compare(out, lse, ro, rl, f"chunked prefill layer {layer_type} window {window}")
 
@@ -112,12 +125,12 @@ def test_chunk_empty_sequences_and_max_newlen(layer_type):
     log(f"[case] chunk empties/max_newlen layer={layer_type}")
     x = synth.prefill_inputs(lengths, seed=42)
     kc, vc, base, cap = _caches(layer_type, lengths)
-    _fill(x, layer_type, cached, kc, vc, base, cap)
+    kh, vh = _fill(x, layer_type, cached, kc, vc, base, cap)
     _, new, rest = _split(x, cached)
     ctx = torch.tensor(cached, dtype=torch.int32, device=DEV)
     cu_new = synth.cu_from_lengths(rest, DEV)
-    ro, rl = orc().prefill_chunk(bits(x.q[new]), bits(x.k[new]), bits(x.v[new]), cu_new.cpu().numpy(), bits(kc),
-                                 bits(vc), ctx.cpu().numpy(), layer_type=layer_type, scale=SCALE,
+    ro, rl = orc().prefill_chunk(bits(x.q[new]), bits(x.k[new]), bits(x.v[new]), cu_new.cpu().numpy(), kh,
+                                 vh, ctx.cpu().numpy(), layer_type=layer_type, scale=SCALE,
                                  sink=sink_array(x.sink), kv_base=None if base is None else base.cpu().numpy())
     out, lse, *_ = _chunk(x, layer_type, cached, kc, vc, base)
     compare(out, lse, ro, rl, f"chunk with empty sequences layer {layer_type}")

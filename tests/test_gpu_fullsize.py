@@ -95,6 +95,9 @@ def test_hybrid_stack_48_layers():
     st = HybridStack(lengths, decode_steps=64, device=DEV)
     log(f"[case] hybrid stack: {sum(lengths)} prompt tokens, 48 layers, 64 steps")
     checked = {0: SWA, 5: GA}
+    # Host copies of every token appended to the checked layers' caches for the
+    # checked sequences: the oracle rebuilds those caches with its own append.
+    hist = {}
     order = np.argsort(lengths)
     seqs = [int(order[0]), int(order[-1])]
     cu = st.cu.cpu().numpy()
@@ -109,6 +112,7 @@ def test_hybrid_stack_48_layers():
             torch.cuda.synchronize()
             for b in seqs:
                 s0, s1 = int(cu[b]), int(cu[b + 1])
+                hist[(layer, b)] = ([bits(x.k[s0:s1])], [bits(x.v[s0:s1])])
                 L = s1 - s0
                 rows = sorted(set([0, 1, 128, 129, L // 2, L - 1]))
                 ro, rl = orc().prefill(bits(x.q[s0:s1]), bits(x.k[s0:s1]), bits(x.v[s0:s1]),
@@ -134,10 +138,30 @@ def test_hybrid_stack_48_layers():
                 for b in seqs:
                     if checked[layer] == GA:
                         b0 = int(st.kv_base[b])
-                        snap.append((bits(c.k[b0:b0 + ctx[b]]), bits(c.v[b0:b0 + ctx[b]])))
+                        gpu = (bits(c.k[b0:b0 + ctx[b]]), bits(c.v[b0:b0 + ctx[b]]))
+                        kc = np.zeros((ctx[b], 4, 192), np.uint16)
+                        vc = np.zeros((ctx[b], 4, 128), np.uint16)
+                        base, cap = np.zeros(1, np.int64), np.array([ctx[b]], np.int64)
                     else:
-                        snap.append((bits(c.k[b:b + 1]), bits(c.v[b:b + 1])))
+                        gpu = (bits(c.k[b:b + 1]), bits(c.v[b:b + 1]))
+                        kc = np.zeros((1, 128, 4, 192), np.uint16)
+                        vc = np.zeros((1, 128, 4, 128), np.uint16)
+                        base = cap = None
+                    pos = 0
+                    for kt, vt in zip(*hist[(layer, b)]):
+                        n = kt.shape[0]
+                        assert orc().kv_append(kt, vt, np.array([0, n], np.int32), np.array([pos], np.int32), kc, vc,
+                                               layer_type=checked[layer], kv_base=base, kv_capacity=cap) == 0
+                        pos += n
+                    assert pos == ctx[b]
+                    assert np.array_equal(gpu[0], kc) and np.array_equal(gpu[1], vc), \
+                        f"stack cache of layer {layer} seq {b} differs from the oracle's appends"
+                    snap.append((kc, vc))
             st.decode_layer(layer, q, kn, vn, sinks[layer], dout, dlse)
+            if layer in checked:
+                for b in seqs:
+                    hist[(layer, b)][0].append(bits(kn[b:b + 1]))
+                    hist[(layer, b)][1].append(bits(vn[b:b + 1]))
             if last and layer in checked:
                 torch.cuda.synchronize()
                 for (kc, vc), b in zip(snap, seqs):

@@ -62,7 +62,7 @@ def test_paged_append_and_decode(page_size):
     of, lf = B.decode(q, kn, vn, kf, vf, ctx_d, max(ctx), GA, sink=sink, kv_base=base)
     torch.cuda.synchronize()
     assert torch.equal(op, of) and torch.equal(lp, lf), "paged decode is not bit-identical to the contiguous pool"
-    ro, rl = orc().decode_paged(bits(x.q), bits(x.k_new), bits(x.v_new), bits(kp), bits(vp), table.numpy(),
+    ro, rl = orc().decode_paged(bits(x.q), bits(x.k_new), bits(x.v_new), kp_ref, vp_ref, table.numpy(),
                                 page_size, x.ctx_lens.numpy(), scale=SCALE, sink=sink_array(x.sink))
     compare(op, lp, ro, rl, f"paged decode page {page_size}")
 
@@ -96,6 +96,9 @@ def test_paged_chunk_prefill(page_size):
     zeros = torch.zeros(len(lengths), dtype=torch.int32, device=DEV)
     B.kv_append_paged(to_dev(x.k[pre]), to_dev(x.v[pre]), cu_pre, zeros, kp, vp, table_d, page_size)
     B.kv_append(to_dev(x.k[pre]), to_dev(x.v[pre]), cu_pre, zeros, kf, vf, GA, kv_base=base, kv_capacity=cap)
+    kp_ref, vp_ref = np.zeros_like(bits(kp)), np.zeros_like(bits(vp))
+    assert orc().kv_append_paged(bits(x.k[pre]), bits(x.v[pre]), cu_pre.cpu().numpy(), zeros.cpu().numpy(), kp_ref,
+                                 vp_ref, table.numpy(), page_size) == 0
     cu_new = synth.cu_from_lengths(rest, DEV)
     ctx = torch.tensor(cached, dtype=torch.int32, device=DEV)
     q, k, v, sink = to_dev(x.q[new]), to_dev(x.k[new]), to_dev(x.v[new]), to_dev(x.sink)
@@ -103,8 +106,9 @@ def test_paged_chunk_prefill(page_size):
     of, lf = B.prefill_chunk(q, k, v, cu_new, max(rest), kf, vf, ctx, GA, sink=sink, kv_base=base)
     torch.cuda.synchronize()
     assert torch.equal(op, of) and torch.equal(lp, lf), "paged chunk is not bit-identical to the contiguous pool"
+    assert np.array_equal(bits(kp), kp_ref) and np.array_equal(bits(vp), vp_ref), "paged append bytes"
     ro, rl = orc().prefill_chunk_paged(bits(x.q[new]), bits(x.k[new]), bits(x.v[new]), cu_new.cpu().numpy(),
-                                       bits(kp), bits(vp), table.numpy(), page_size, np.asarray(cached, np.int32),
+                                       kp_ref, vp_ref, table.numpy(), page_size, np.asarray(cached, np.int32),
                                        scale=SCALE, sink=sink_array(x.sink))
     compare(op, lp, ro, rl, f"paged chunk page {page_size}")
 
