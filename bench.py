@@ -365,6 +365,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next-rows", action="store_true",
+                    help="skip the rows timed apart from the step (chunked prefill, paged and FP8 pools)")
     ap.add_argument("--split", type=int, default=0, help="GA decode split (keys per workgroup), 0 = default")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device copy (a known-size reference for HBM byte counters)")
@@ -523,10 +525,10 @@ def main():
         "breakdown": breakdown,
         "roofline": roof,
         "device": dev_ctx,
-        # Rows beyond the step (continuing cached sequences, paged pool, FP8 pool); not part of `value`.
-        "next_rows": {**chunk_rows(dims, ga, swa), **paged_rows(dims, dga, ctx_ga, max_ctx, ws, ga),
-                      **fp8_rows(dims, dga, ctx_ga, max_ctx, ws)},
     }
+    if not args.no_next_rows:
+        res["next_rows"] = {**chunk_rows(dims, ga, swa), **paged_rows(dims, dga, ctx_ga, max_ctx, ws, ga),
+                            **fp8_rows(dims, dga, ctx_ga, max_ctx, ws)}
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample (cpu_baseline)")
         res["cpu_baseline"] = cpu_baseline(swa, ga, dga, ctx0, args.cpu_budget)
