@@ -73,6 +73,9 @@ class Oracle:
         lib.oracle_prefill_chunk_paged.restype = _I
         lib.oracle_prefill_chunk_paged.argtypes = [_I, _I, _I, _I, _F, _F, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I,
                                                    _I64, _P, _P, _P, _P, _I]
+        lib.oracle_prefill_backward.restype = _I
+        lib.oracle_prefill_backward.argtypes = [_I, _I, _I, _I, _I, _I, _F, _F, _P, _P, _P, _P, _P, _I, _P, _P,
+                                                _I64, _P, _I64, _P, _P, _P, _P, _I]
         lib.oracle_decode_fp8.restype = _I
         lib.oracle_decode_fp8.argtypes = [_I, _I, _I, _I, _F, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P,
                                           _P, _I]
@@ -219,6 +222,40 @@ class Oracle:
                                              cu.shape[0] - 1, self._ptr(k_cache), self._ptr(v_cache),
                                              self._ptr(base), self._ptr(cap)))
 
+
+    def prefill_backward(self, q, k, v, dout, cu_seqlens, *, layer_type: int, window: int = 129, scale: float,
+                         value_scale: float = 1.0, sink=None, q_rows=None, kv_rows=None, want_dsink: bool = True,
+                         nthreads: int = 0):
+        """Gradients of sum(dout * prefill(q, k, v)) (bf16 bits in, float64 out).
+
+        Returns (dq [nq][Hq][Dqk], dk [nkv][Hkv][Dqk], dv [nkv][Hkv][Dv], dsink [Hq] or None) for the
+        packed tokens q_rows / kv_rows (default: all tokens)."""
+        q = np.ascontiguousarray(q)
+        hq, dqk = q.shape[1], q.shape[2]
+        hkv, dv = k.shape[1], v.shape[2]
+        q = self._u16(q, (hq, dqk))
+        k = self._u16(k, (hkv, dqk))
+        v = self._u16(v, (hkv, dv))
+        do = self._u16(dout, (hq, dv))
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        nseq = cu.shape[0] - 1
+        T = int(cu[-1])
+        qr = np.arange(T, dtype=np.int64) if q_rows is None else np.ascontiguousarray(q_rows, dtype=np.int64)
+        kr = np.arange(T, dtype=np.int64) if kv_rows is None else np.ascontiguousarray(kv_rows, dtype=np.int64)
+        sk = None if sink is None else np.ascontiguousarray(sink, dtype=np.float32)
+        dq = np.empty((qr.shape[0], hq, dqk), np.float64)
+        dk = np.empty((kr.shape[0], hkv, dqk), np.float64)
+        dvv = np.empty((kr.shape[0], hkv, dv), np.float64)
+        ds = np.empty(hq, np.float64) if want_dsink else None
+        nth = nthreads if nthreads > 0 else self.default_threads()
+        rc = self.lib.oracle_prefill_backward(hq, hkv, dqk, dv, layer_type, window, scale, value_scale,
+                                              self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(do), self._ptr(cu),
+                                              nseq, self._ptr(sk), self._ptr(qr), qr.shape[0], self._ptr(kr),
+                                              kr.shape[0], self._ptr(dq), self._ptr(dk), self._ptr(dvv),
+                                              self._ptr(ds), nth)
+        if rc != OK:
+            raise ValueError(f"oracle_prefill_backward rejected its arguments (status {rc})")
+        return dq, dk, dvv, ds
 
     # -- paged GA pool ----------------------------------------------------
     @staticmethod

@@ -191,6 +191,19 @@ static int seq_of_token(const int32_t* cu, int nseq, int64_t t) {
     return lo;
 }
 
+/* Rows of the keys and values lo..p of the sequence whose first token is
+ * packed row base, KV head g (prefill: keys come from the same sequence);
+ * returns their count. */
+static int prefill_key_rows(const dims_t* d, const uint16_t* k, const uint16_t* v, int64_t base, int lo, int p, int g,
+                            const uint16_t** kr, const uint16_t** vr) {
+    int n = 0;
+    for (int j = lo; j <= p; ++j, ++n) {
+        kr[n] = k + ((size_t)(base + j) * d->hkv + g) * d->dqk;
+        vr[n] = v + ((size_t)(base + j) * d->hkv + g) * d->dv;
+    }
+    return n;
+}
+
 static void* prefill_worker(void* arg) {
     prefill_job_t* jb = (prefill_job_t*)arg;
     const dims_t* d = jb->d;
@@ -216,11 +229,7 @@ static void* prefill_worker(void* arg) {
         if (d->layer_type == ORACLE_SWA) lo = p - (d->window - 1) > 0 ? p - (d->window - 1) : 0;
         for (int h = 0; h < d->hq; ++h) {
             int g = h / group;
-            int n = 0;
-            for (int j = lo; j <= p; ++j, ++n) {
-                kr[n] = jb->k + ((size_t)(base + j) * d->hkv + g) * d->dqk;
-                vr[n] = jb->v + ((size_t)(base + j) * d->hkv + g) * d->dv;
-            }
+            int n = prefill_key_rows(d, jb->k, jb->v, base, lo, p, g, kr, vr);
             double sigma = 0.0;
             int hs = sink_present(jb->sink, h, &sigma);
             double* w = jb->weights ? jb->weights + ((size_t)r * d->hq + h) * jb->wstride : NULL;
@@ -288,6 +297,178 @@ int oracle_prefill(int hq, int hkv, int dqk, int dv, int layer_type, int window,
     pthread_mutex_init(&jb.mu, NULL);
     run_threads(prefill_worker, &jb, nthreads);
     pthread_mutex_destroy(&jb.mu);
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Backward of prefill: the gradient of sum(dO * out) for an upstream dO    */
+/* [T][Hq][Dv].  Differentiating o = value_scale * sum_j exp(s_j - LSE) v_j */
+/* with LSE = log(sum_j exp(s_j) + exp(sigma)) gives, for one query row     */
+/* (position p, head h, group g, key set J, weights P_j = exp(s_j - LSE)):  */
+/*   D       = sum_e dO[e] * o[e]                                           */
+/*   dP_j    = value_scale * sum_e dO[e] * v[j,g,e]                         */
+/*   dS_j    = P_j * (dP_j - D)                    (d sum(dO*o) / d s_j)     */
+/*   dq[x]   = scale * sum_j dS_j * k[j,g,x]                                */
+/*   dk[j,g,x] += scale * dS_j * q[x]      dv[j,g,e] += value_scale * P_j * dO[e] */
+/*   dsink[h] += -exp(sigma_h - LSE) * D   (d o / d sigma = -P_sink * o)    */
+/* dk and dv sum over the 16 heads of the group and over every query row    */
+/* whose key set holds j; dsink sums over every row of every sequence.      */
+
+typedef struct {
+    const dims_t* d;
+    const uint16_t *q, *k, *v, *dout;
+    const int32_t* cu;
+    int nseq;
+    const float* sink;
+    const int64_t* items; /* packed token indices of this phase */
+    int64_t nitems;
+    double *lse, *D, *psink; /* per [T][hq] row statistics (phase 0 writes, 2 reads) */
+    double *dq, *dk, *dv;    /* phase 1 writes dq [nitems][hq][dqk]; phase 2 dk/dv [nitems][hkv][.] */
+    int phase, maxkeys;
+    int64_t next;
+    pthread_mutex_t mu;
+} bwd_job_t;
+
+static void* bwd_worker(void* arg) {
+    bwd_job_t* jb = (bwd_job_t*)arg;
+    const dims_t* d = jb->d;
+    const uint16_t** kr = malloc(sizeof(*kr) * (size_t)(jb->maxkeys + 1));
+    const uint16_t** vr = malloc(sizeof(*vr) * (size_t)(jb->maxkeys + 1));
+    double* sc = malloc(sizeof(double) * (size_t)(jb->maxkeys + 1));
+    double* w = malloc(sizeof(double) * (size_t)(jb->maxkeys + 1));
+    double* o = malloc(sizeof(double) * (size_t)d->dv);
+    int group = d->hq / d->hkv;
+    for (;;) {
+        pthread_mutex_lock(&jb->mu);
+        int64_t it = jb->next++;
+        pthread_mutex_unlock(&jb->mu);
+        if (it >= jb->nitems) break;
+        int64_t t = jb->items[it];
+        int b = seq_of_token(jb->cu, jb->nseq, t);
+        int64_t base = jb->cu[b];
+        int L = jb->cu[b + 1] - jb->cu[b];
+        int p = (int)(t - base);
+        if (jb->phase <= 1) { /* a query row: forward, then row statistics or dq */
+            int lo = 0;
+            if (d->layer_type == ORACLE_SWA) lo = p - (d->window - 1) > 0 ? p - (d->window - 1) : 0;
+            for (int h = 0; h < d->hq; ++h) {
+                int g = h / group;
+                int n = prefill_key_rows(d, jb->k, jb->v, base, lo, p, g, kr, vr);
+                double sigma = 0.0, lse, wsink;
+                int hs = sink_present(jb->sink, h, &sigma);
+                attend_row(d, jb->q + ((size_t)t * d->hq + h) * d->dqk, n, kr, vr, NULL, hs, sigma, sc, o, &lse, w,
+                           &wsink);
+                const uint16_t* dorow = jb->dout + ((size_t)t * d->hq + h) * d->dv;
+                double D = 0.0;
+                for (int e = 0; e < d->dv; ++e) D += bf16_to_double(dorow[e]) * o[e];
+                if (jb->phase == 0) {
+                    jb->lse[(size_t)t * d->hq + h] = lse;
+                    jb->D[(size_t)t * d->hq + h] = D;
+                    jb->psink[(size_t)t * d->hq + h] = wsink;
+                    continue;
+                }
+                double* dq = jb->dq + ((size_t)it * d->hq + h) * d->dqk;
+                for (int x = 0; x < d->dqk; ++x) dq[x] = 0.0;
+                for (int j = 0; j < n; ++j) {
+                    double dp = 0.0;
+                    for (int e = 0; e < d->dv; ++e) dp += bf16_to_double(dorow[e]) * bf16_to_double(vr[j][e]);
+                    double ds = w[j] * (d->value_scale * dp - D);
+                    for (int x = 0; x < d->dqk; ++x) dq[x] += d->scale * ds * bf16_to_double(kr[j][x]);
+                }
+            }
+        } else { /* a key row: dk, dv over every query row that sees it */
+            int hi = L - 1;
+            if (d->layer_type == ORACLE_SWA && p + d->window - 1 < hi) hi = p + d->window - 1;
+            for (int g = 0; g < d->hkv; ++g) {
+                const uint16_t* krow = jb->k + ((size_t)t * d->hkv + g) * d->dqk;
+                const uint16_t* vrow = jb->v + ((size_t)t * d->hkv + g) * d->dv;
+                double* dk = jb->dk + ((size_t)it * d->hkv + g) * d->dqk;
+                double* dv = jb->dv + ((size_t)it * d->hkv + g) * d->dv;
+                for (int x = 0; x < d->dqk; ++x) dk[x] = 0.0;
+                for (int e = 0; e < d->dv; ++e) dv[e] = 0.0;
+                for (int h = g * group; h < (g + 1) * group; ++h)
+                    for (int i = p; i <= hi; ++i) {
+                        size_t row = (size_t)(base + i) * d->hq + h;
+                        const uint16_t* qrow = jb->q + row * d->dqk;
+                        const uint16_t* dorow = jb->dout + row * d->dv;
+                        double acc = 0.0;
+                        for (int x = 0; x < d->dqk; ++x) acc += bf16_to_double(qrow[x]) * bf16_to_double(krow[x]);
+                        double pw = exp(d->scale * acc - jb->lse[row]);
+                        double dp = 0.0;
+                        for (int e = 0; e < d->dv; ++e) dp += bf16_to_double(dorow[e]) * bf16_to_double(vrow[e]);
+                        double ds = pw * (d->value_scale * dp - jb->D[row]);
+                        for (int x = 0; x < d->dqk; ++x) dk[x] += d->scale * ds * bf16_to_double(qrow[x]);
+                        for (int e = 0; e < d->dv; ++e) dv[e] += d->value_scale * pw * bf16_to_double(dorow[e]);
+                    }
+            }
+        }
+    }
+    free(kr); free(vr); free(sc); free(w); free(o);
+    return NULL;
+}
+
+/* Gradients of sum(dO * out) for a packed prefill batch (layouts as for
+ * oracle_prefill; dout [T][hq][dv] bf16 bits).  dq is computed for the packed
+ * tokens q_rows [nq] (dq [nq][hq][dqk]), dk/dv for kv_rows [nkv] (dk
+ * [nkv][hkv][dqk], dv [nkv][hkv][dv]); dsink [hq] (NULL to skip) sums over
+ * every token of the batch and is 0 without a sink. */
+int oracle_prefill_backward(int hq, int hkv, int dqk, int dv, int layer_type, int window, float scale,
+                            float value_scale, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                            const uint16_t* dout, const int32_t* cu_seqlens, int nseq, const float* sink,
+                            const int64_t* q_rows, int64_t nq, const int64_t* kv_rows, int64_t nkv,
+                            double* dq, double* dk, double* dvv, double* dsink, int nthreads) {
+    dims_t d = {hq, hkv, dqk, dv, layer_type, window, (double)scale, (double)value_scale};
+    if (!check_dims(&d) || nseq < 1 || !q || !k || !v || !dout || !cu_seqlens || cu_seqlens[0] != 0)
+        return ORACLE_EINVAL;
+    if ((nq > 0 && (!q_rows || !dq)) || (nkv > 0 && (!kv_rows || !dk || !dvv)) || nq < 0 || nkv < 0)
+        return ORACLE_EINVAL;
+    int64_t T = cu_seqlens[nseq];
+    int maxkeys = 1;
+    for (int b = 0; b < nseq; ++b) {
+        int L = cu_seqlens[b + 1] - cu_seqlens[b];
+        if (L < 0) return ORACLE_EINVAL;
+        if (L > maxkeys) maxkeys = L;
+    }
+    for (int64_t i = 0; i < nq; ++i) if (q_rows[i] < 0 || q_rows[i] >= T) return ORACLE_EINVAL;
+    for (int64_t i = 0; i < nkv; ++i) if (kv_rows[i] < 0 || kv_rows[i] >= T) return ORACLE_EINVAL;
+    /* Rows whose statistics are needed: every query row that sees a kv row, and
+     * all rows for dsink. */
+    uint8_t* need = calloc((size_t)(T > 0 ? T : 1), 1);
+    for (int64_t i = 0; i < nkv; ++i) {
+        int64_t t = kv_rows[i];
+        int b = seq_of_token(cu_seqlens, nseq, t);
+        int64_t end = cu_seqlens[b + 1];
+        if (layer_type == ORACLE_SWA && t + window < end) end = t + window;
+        for (int64_t r = t; r < end; ++r) need[r] = 1;
+    }
+    if (dsink) memset(need, 1, (size_t)T);
+    int64_t nneed = 0;
+    for (int64_t r = 0; r < T; ++r) nneed += need[r];
+    int64_t* rows = malloc(sizeof(int64_t) * (size_t)(nneed > 0 ? nneed : 1));
+    nneed = 0;
+    for (int64_t r = 0; r < T; ++r) if (need[r]) rows[nneed++] = r;
+    double* lse = calloc((size_t)(T > 0 ? T : 1) * hq, sizeof(double));
+    double* D = calloc((size_t)(T > 0 ? T : 1) * hq, sizeof(double));
+    double* ps = calloc((size_t)(T > 0 ? T : 1) * hq, sizeof(double));
+    bwd_job_t jb;
+    memset(&jb, 0, sizeof jb);
+    jb.d = &d; jb.q = q; jb.k = k; jb.v = v; jb.dout = dout; jb.cu = cu_seqlens; jb.nseq = nseq; jb.sink = sink;
+    jb.lse = lse; jb.D = D; jb.psink = ps; jb.dq = dq; jb.dk = dk; jb.dv = dvv; jb.maxkeys = maxkeys;
+    pthread_mutex_init(&jb.mu, NULL);
+    const int64_t* phase_items[3] = {rows, q_rows, kv_rows};
+    int64_t phase_n[3] = {nneed, nq, nkv};
+    for (int ph = 0; ph < 3; ++ph) {
+        jb.phase = ph; jb.items = phase_items[ph]; jb.nitems = phase_n[ph]; jb.next = 0;
+        if (jb.nitems > 0) run_threads(bwd_worker, &jb, nthreads);
+    }
+    pthread_mutex_destroy(&jb.mu);
+    if (dsink)
+        for (int h = 0; h < hq; ++h) {
+            double acc = 0.0;
+            for (int64_t r = 0; r < T; ++r) acc -= ps[(size_t)r * hq + h] * D[(size_t)r * hq + h];
+            dsink[h] = acc;
+        }
+    free(need); free(rows); free(lse); free(D); free(ps);
     return ORACLE_OK;
 }
 

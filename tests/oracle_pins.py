@@ -12,6 +12,9 @@ the oracle disagrees with:
     SWA equals GA when the window covers the sequence; GQA equals MHA with the
     K/V heads repeated; value_scale is linear; decode at position p equals row
     p of prefill; ring-slot contents after appends);
+  * for the backward pass: torch fp64 autograd through a dense brute force of
+    the same attention (sink as an extra logit with no value), and the closed
+    form of one-token sequences;
   * for the FP8 (OCP E4M3) GA cache: the format's own table
     (tests/golden/ocp_e4m3.json) and torch's float8_e4m3fn conversions (a
     library implementation of the same format); FP8 decode equals bf16 decode
@@ -579,6 +582,126 @@ def pin_paged_append_places_positions(orc):
     st = orc.kv_append_paged(one, one, np.array([0, 1, 1], np.int32), np.array([12, 0], np.int32), kc, vc, table, P)
     assert st == oracle.ECAPACITY and np.array_equal(kc, before), "append past max_blocks * page_size not refused"
 
+
+
+# -- backward ------------------------------------------------------------------
+
+def _torch_grads(x, dout, layer_type, window, scale, value_scale, sink):
+    """Gradients of sum(dout * out) by torch fp64 autograd through a dense masked
+    attention per sequence, the sink appended as one more logit with no value."""
+    q = _f64(x.q).clone().requires_grad_(True)
+    k = _f64(x.k).clone().requires_grad_(True)
+    v = _f64(x.v).clone().requires_grad_(True)
+    sg = None if sink is None else torch.tensor(np.float64(sink)).requires_grad_(True)
+    hq, hkv = q.shape[1], k.shape[1]
+    G = hq // hkv
+    cu = x.cu_seqlens.tolist()
+    loss = 0.0
+    for b in range(len(cu) - 1):
+        s0, s1 = cu[b], cu[b + 1]
+        L = s1 - s0
+        if L == 0:
+            continue
+        qs = q[s0:s1].transpose(0, 1)                                   # [H, L, Dqk]
+        ks = k[s0:s1].transpose(0, 1).repeat_interleave(G, dim=0)       # [H, L, Dqk]
+        vs = v[s0:s1].transpose(0, 1).repeat_interleave(G, dim=0)       # [H, L, Dv]
+        sc = float(scale) * (qs @ ks.transpose(1, 2))
+        i = torch.arange(L)[:, None]
+        j = torch.arange(L)[None, :]
+        ok = j <= i
+        if layer_type == SWA:
+            ok = ok & (j >= i - (window - 1))
+        sc = sc.masked_fill(~ok, float("-inf"))
+        if sg is not None:
+            sc = torch.cat([sc, sg[:, None, None].expand(hq, L, 1)], dim=2)
+        pr = torch.softmax(sc, dim=2)[:, :, :L]
+        out = float(value_scale) * (pr @ vs)                              # [H, L, Dv]
+        loss = loss + (out * _f64(dout[s0:s1]).transpose(0, 1)).sum()
+    loss.backward()
+    ds = None if sg is None else sg.grad.numpy()
+    return q.grad.numpy(), k.grad.numpy(), v.grad.numpy(), ds
+
+
+def _rel_close(a, b, tol, what):
+    scale = max(1.0, float(np.max(np.abs(b))))
+    err = float(np.max(np.abs(a - b)))
+    assert err <= tol * scale, f"{what}: max abs diff {err:.3e} > {tol:.1e} x {scale:.3e}"
+
+
+def pin_backward_torch_autograd(orc):
+    """Oracle gradients (dq, dk, dv, dsink) equal torch fp64 autograd of a dense
+    brute force, for SWA windows 5 and 129, GA, value_scale 0.707, with and
+    without a sink, over a ragged batch."""
+    x = _make([1, 9, 40], seed=80)
+    dout = torch.randn((50, 64, 128), generator=torch.Generator().manual_seed(81)).to(torch.bfloat16)
+    sc = float(np.float32(synth.SOFTMAX_SCALE))
+    vsc = float(np.float32(0.707))
+    for lt, win, sink in ((SWA, 5, x.sink.numpy()), (SWA, 129, x.sink.numpy()), (GA, 129, x.sink.numpy()),
+                          (GA, 129, None)):
+        dq, dk, dv, ds = orc.prefill_backward(_bits(x.q), _bits(x.k), _bits(x.v), _bits(dout), x.cu_seqlens.numpy(),
+                                              layer_type=lt, window=win, scale=sc, value_scale=vsc, sink=sink)
+        tq, tk, tv, ts = _torch_grads(x, dout, lt, win, sc, vsc, sink)
+        _rel_close(dq, tq, 1e-12, f"dq lt={lt} W={win}")
+        _rel_close(dk, tk, 1e-12, f"dk lt={lt} W={win}")
+        _rel_close(dv, tv, 1e-12, f"dv lt={lt} W={win}")
+        if sink is None:
+            assert not ds.any(), "dsink without a sink must be 0"
+        else:
+            _rel_close(ds, ts, 1e-12, f"dsink lt={lt} W={win}")
+
+
+def pin_backward_one_token_closed_form(orc):
+    """One-token sequences: with s = scale q.k and P = 1 / (1 + exp(sigma - s)),
+    out = value_scale P v, so d/dv = value_scale P dO, d/dsigma =
+    -value_scale P (1 - P) dO.v, d/dq = scale value_scale P (1 - P) (dO.v) k and
+    d/dk likewise with q (GQA: dk and dv sum the 16 heads of a group)."""
+    x = _make([1, 1, 1], seed=82)
+    dout = torch.randn((3, 64, 128), generator=torch.Generator().manual_seed(83)).to(torch.bfloat16)
+    sc = float(np.float32(synth.SOFTMAX_SCALE))
+    vsc = float(np.float32(0.707))
+    sink = x.sink.numpy()
+    dq, dk, dv, ds = orc.prefill_backward(_bits(x.q), _bits(x.k), _bits(x.v), _bits(dout), x.cu_seqlens.numpy(),
+                                          layer_type=GA, scale=sc, value_scale=vsc, sink=sink)
+    q, k, v, do = _f64(x.q).numpy(), _f64(x.k).numpy(), _f64(x.v).numpy(), _f64(dout).numpy()
+    want_ds = np.zeros(64)
+    for t in range(3):
+        for h in range(64):
+            g = h // 16
+            s = sc * float(q[t, h] @ k[t, g])
+            P = 1.0 / (1.0 + math.exp(float(sink[h]) - s))
+            dov = float(do[t, h] @ v[t, g])
+            _close(dq[t, h], sc * vsc * P * (1 - P) * dov * k[t, g], 1e-12, f"one-token dq t={t} h={h}")
+            want_ds[h] -= vsc * P * (1 - P) * dov
+        for g in range(4):
+            hs = range(16 * g, 16 * g + 16)
+            Ps = [1.0 / (1.0 + math.exp(float(sink[h]) - sc * float(q[t, h] @ k[t, g]))) for h in hs]
+            wk = sum(sc * vsc * P * (1 - P) * float(do[t, h] @ v[t, g]) * q[t, h] for P, h in zip(Ps, hs))
+            wv = sum(vsc * P * do[t, h] for P, h in zip(Ps, hs))
+            _close(dk[t, g], wk, 1e-11, f"one-token dk t={t} g={g}")
+            _close(dv[t, g], wv, 1e-12, f"one-token dv t={t} g={g}")
+    _close(ds, want_ds, 1e-11, "one-token dsink")
+
+
+def pin_backward_rows_and_neg_inf_sink(orc):
+    """Sampled rows equal the full computation, and a sink of -inf gives the
+    no-sink gradients with dsink 0."""
+    x = _make([30, 64], seed=84)
+    dout = torch.randn((94, 64, 128), generator=torch.Generator().manual_seed(85)).to(torch.bfloat16)
+    sc = float(np.float32(synth.SOFTMAX_SCALE))
+    args = (_bits(x.q), _bits(x.k), _bits(x.v), _bits(dout), x.cu_seqlens.numpy())
+    for lt in (SWA, GA):
+        full = orc.prefill_backward(*args, layer_type=lt, window=17, scale=sc, sink=x.sink.numpy())
+        qr, kr = np.array([0, 29, 30, 77, 93]), np.array([3, 30, 31, 90, 93])
+        part = orc.prefill_backward(*args, layer_type=lt, window=17, scale=sc, sink=x.sink.numpy(), q_rows=qr,
+                                    kv_rows=kr, want_dsink=False)
+        assert np.array_equal(part[0], full[0][qr]) and np.array_equal(part[1], full[1][kr])
+        assert np.array_equal(part[2], full[2][kr]) and part[3] is None
+        none = orc.prefill_backward(*args, layer_type=lt, window=17, scale=sc, sink=None)
+        ninf = orc.prefill_backward(*args, layer_type=lt, window=17, scale=sc,
+                                    sink=np.full(64, -np.inf, np.float32))
+        for a, b in zip(none[:3], ninf[:3]):
+            assert np.array_equal(a, b), "sink -inf differs from no sink"
+        assert not ninf[3].any()
 
 # -- FP8 (OCP E4M3) GA cache -------------------------------------------------
 

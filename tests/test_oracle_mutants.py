@@ -28,13 +28,13 @@ MUTANTS = {
         "        for (int h = 0;",
         "        if (d->layer_type == ORACLE_SWA) lo = p - d->window > 0 ? p - d->window : 0;\n"
         "        for (int h = 0;"),
-    "causal bound excludes self": ("            for (int j = lo; j <= p; ++j, ++n) {\n",
-                                   "            for (int j = lo; j < p; ++j, ++n) {\n"),
-    "GQA heads interleaved instead of grouped": ("            int g = h / group;\n",
-                                                 "            int g = h % d->hkv;\n"),
+    "causal bound excludes self": ("    for (int j = lo; j <= p; ++j, ++n) {\n        kr[n] = k + ",
+                                   "    for (int j = lo; j < p; ++j, ++n) {\n        kr[n] = k + "),
+    "GQA heads interleaved instead of grouped": ("            int g = h / group;\n            int n = prefill_key_rows(",
+                                                 "            int g = h % d->hkv;\n            int n = prefill_key_rows("),
     "wrong KV head for keys": (
-        "                kr[n] = jb->k + ((size_t)(base + j) * d->hkv + g) * d->dqk;\n",
-        "                kr[n] = jb->k + ((size_t)(base + j) * d->hkv + (g + 1) % d->hkv) * d->dqk;\n"),
+        "        kr[n] = k + ((size_t)(base + j) * d->hkv + g) * d->dqk;\n",
+        "        kr[n] = k + ((size_t)(base + j) * d->hkv + (g + 1) % d->hkv) * d->dqk;\n"),
     "value_scale not applied": ("    for (int e = 0; e < d->dv; ++e) o[e] *= d->value_scale;\n", "\n"),
     "softmax scale not applied": ("        scores[j] = d->scale * acc;\n", "        scores[j] = acc;\n"),
     "LSE without the max": ("    double l = m + log(z);\n", "    double l = log(z);\n"),
@@ -92,6 +92,25 @@ MUTANTS = {
         "                    k_cache[(dst * hkv + g) * dqk + x] = e4m3_quantize(k[(src * hkv + g) * dqk + x], k_scale[g]);\n",
         "                    k_cache[(dst * hkv + g) * dqk + x] = e4m3_quantize(k[(src * hkv + g) * dqk + x], k_scale[0]);\n"),
     "FP8 quantiser multiplies by the scale": ("    return e4m3_from_float(f / scale);\n", "    return e4m3_from_float(f * scale);\n"),
+    "backward dS without the D term (dq)": ("                    double ds = w[j] * (d->value_scale * dp - D);\n",
+                                            "                    double ds = w[j] * (d->value_scale * dp);\n"),
+    "backward dS without value_scale (dk)": (
+        "                        double ds = pw * (d->value_scale * dp - jb->D[row]);\n",
+        "                        double ds = pw * (dp - jb->D[row]);\n"),
+    "backward dv without value_scale": (
+        "                        for (int e = 0; e < d->dv; ++e) dv[e] += d->value_scale * pw * bf16_to_double(dorow[e]);\n",
+        "                        for (int e = 0; e < d->dv; ++e) dv[e] += pw * bf16_to_double(dorow[e]);\n"),
+    "backward dk without the softmax scale": (
+        "                        for (int x = 0; x < d->dqk; ++x) dk[x] += d->scale * ds * bf16_to_double(qrow[x]);\n",
+        "                        for (int x = 0; x < d->dqk; ++x) dk[x] += ds * bf16_to_double(qrow[x]);\n"),
+    "backward dsink sign flipped": ("            for (int64_t r = 0; r < T; ++r) acc -= ps[(size_t)r * hq + h] * D[(size_t)r * hq + h];\n",
+                                    "            for (int64_t r = 0; r < T; ++r) acc += ps[(size_t)r * hq + h] * D[(size_t)r * hq + h];\n"),
+    "backward SWA receivers one too many": (
+        "            if (d->layer_type == ORACLE_SWA && p + d->window - 1 < hi) hi = p + d->window - 1;\n",
+        "            if (d->layer_type == ORACLE_SWA && p + d->window < hi) hi = p + d->window;\n"),
+    "backward D from the value instead of the output": (
+        "                for (int e = 0; e < d->dv; ++e) D += bf16_to_double(dorow[e]) * o[e];\n",
+        "                for (int e = 0; e < d->dv; ++e) D += bf16_to_double(dorow[e]) * o[e] / d->value_scale;\n"),
     "bf16 widened from the wrong half": ("    uint32_t w = ((uint32_t)bits) << 16;\n", "    uint32_t w = ((uint32_t)bits) << 15;\n"),
 }
 
