@@ -244,6 +244,34 @@ def fp8_rows(dims, dga, ctx, max_ctx, ws, reps=5):
     return res
 
 
+def backward_rows(dims, ga, swa, out_ga, lse_ga, out_swa, lse_swa, reps=3):
+    """Prefill backward (dq, dk, dv, dsink of sum(dout * out)) on the step's two
+    prefill inputs, timed apart from the step; dout is seeded N(0,1) bf16.
+    Algorithmic flops: 1664 per unmasked (query, key, head) triple (recomputed
+    S 384, dP 256, dV 256, dQ 384, dK 384)."""
+    dev = "cuda"
+    res = {}
+    g = torch.Generator(device=dev).manual_seed(7)
+    for name, x, out, lse, lt, L, n in (("backward_ga", ga, out_ga, lse_ga, 1, 32768, 1),
+                                         ("backward_swa", swa, out_swa, lse_swa, 0, 8192, 4)):
+        T = x.q.shape[0]
+        dout = torch.randn((T, HQ, DV), generator=g, device=dev).to(torch.bfloat16)
+        dq, dk, dv = torch.empty_like(x.q), torch.empty_like(x.k), torch.empty_like(x.v)
+        ds = torch.empty(HQ, dtype=torch.float32, device=dev)
+        ws = torch.empty(B.mimo_attn_prefill_backward_workspace_size(dims, T) // 4 + 4, dtype=torch.float32,
+                         device=dev)
+        call = lambda: B.mimo_attn_prefill_backward(dims, lt, x.q, x.k, x.v, out, lse, dout, x.cu_seqlens, n, L, T,
+                                                    x.sink, dq, dk, dv, ds, ws)
+        ms = _time_ms(call, reps)
+        flops = prefill_pairs([L] * n, lt) * HQ * 1664
+        tfs = flops / (ms * 1e-3) / 1e12
+        res[name] = {"workload": f"{n} x {L} tokens, {'GA' if lt else 'SWA'}", "ms": ms, "TFLOP/s": tfs,
+                     "frac_mfma_peak": tfs / PEAK_BF16_TFLOPS}
+        del dout, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def _time_ms(call, reps):
     call()
     torch.cuda.synchronize()
@@ -528,7 +556,8 @@ def main():
     }
     if not args.no_next_rows:
         res["next_rows"] = {**chunk_rows(dims, ga, swa), **paged_rows(dims, dga, ctx_ga, max_ctx, ws, ga),
-                            **fp8_rows(dims, dga, ctx_ga, max_ctx, ws)}
+                            **fp8_rows(dims, dga, ctx_ga, max_ctx, ws),
+                            **backward_rows(dims, ga, swa, out_ga, lse_ga, out_swa, lse_swa)}
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample (cpu_baseline)")
         res["cpu_baseline"] = cpu_baseline(swa, ga, dga, ctx0, args.cpu_budget)

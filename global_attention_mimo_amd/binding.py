@@ -27,7 +27,8 @@ MIMO_ERR_HIP = 4
 
 ENTRY_POINTS = ("mimo_attn_prefill", "mimo_attn_prefill_chunk", "mimo_attn_decode_workspace_size",
                 "mimo_attn_decode", "mimo_kv_append", "mimo_kv_append_paged", "mimo_attn_decode_paged",
-                "mimo_attn_prefill_chunk_paged", "mimo_kv_append_fp8", "mimo_attn_decode_fp8", "mimo_status_string",
+                "mimo_attn_prefill_chunk_paged", "mimo_kv_append_fp8", "mimo_attn_decode_fp8",
+                "mimo_attn_prefill_backward_workspace_size", "mimo_attn_prefill_backward", "mimo_status_string",
                 "mimo_last_error", "mimo_abi_version")
 
 
@@ -89,6 +90,11 @@ def lib() -> ctypes.CDLL:
         L.mimo_attn_decode_fp8.restype = ctypes.c_int
         L.mimo_attn_decode_fp8.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P,
                                            _P, _SZ, _P]
+        L.mimo_attn_prefill_backward_workspace_size.restype = _SZ
+        L.mimo_attn_prefill_backward_workspace_size.argtypes = [dims_p, _I32]
+        L.mimo_attn_prefill_backward.restype = ctypes.c_int
+        L.mimo_attn_prefill_backward.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
+                                                 _P, _P, _P, _P, _P, _P, _SZ, _P]
         L.mimo_status_string.restype = ctypes.c_char_p
         L.mimo_status_string.argtypes = [ctypes.c_int]
         L.mimo_last_error.restype = ctypes.c_char_p
@@ -222,6 +228,20 @@ def mimo_attn_decode_fp8(dims: mimo_attn_dims, q, k_new, v_new, k_cache, v_cache
                                       ws_bytes, _stream(stream)))
 
 
+def mimo_attn_prefill_backward_workspace_size(dims: mimo_attn_dims, total_tokens: int) -> int:
+    return int(lib().mimo_attn_prefill_backward_workspace_size(ctypes.byref(dims), total_tokens))
+
+
+def mimo_attn_prefill_backward(dims: mimo_attn_dims, layer_type: int, q, k, v, out, lse, dout, cu_seqlens,
+                               num_seqs: int, max_seqlen: int, total_tokens: int, sink, dq, dk, dv, dsink, workspace,
+                               stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().mimo_attn_prefill_backward(ctypes.byref(dims), layer_type, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                            _ptr(lse), _ptr(dout), _ptr(cu_seqlens), num_seqs, max_seqlen,
+                                            total_tokens, _ptr(sink), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dsink),
+                                            _ptr(workspace), ws_bytes, _stream(stream)))
+
+
 # -- tensor-level conveniences (allocation of outputs + the calls above) -------
 
 def prefill(q, k, v, cu_seqlens, max_seqlen: int, layer_type: int, sink=None, dims=None, out=None, lse=None,
@@ -339,3 +359,19 @@ def decode_fp8(q, k_new, v_new, k_cache, v_cache, kv_base, k_scale, v_scale, ctx
     mimo_attn_decode_fp8(dims, q, k_new, v_new, k_cache, v_cache, kv_base, k_scale, v_scale, ctx_lens, B, max_ctx,
                          split_tokens, sink, out, lse, workspace, stream)
     return out, lse
+
+
+def prefill_backward(q, k, v, out, lse, dout, cu_seqlens, max_seqlen: int, layer_type: int, sink=None, dims=None,
+                     want_dsink: bool = True, stream=None):
+    """(dq, dk, dv, dsink) of sum(dout * out) for a prefill call's inputs and outputs."""
+    dims = dims or make_dims()
+    T = q.shape[0]
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dsink = torch.empty(dims.num_q_heads, dtype=torch.float32, device=q.device) if want_dsink else None
+    nbytes = mimo_attn_prefill_backward_workspace_size(dims, T)
+    ws = torch.empty(max(nbytes, 16) // 4 + 4, dtype=torch.float32, device=q.device)
+    mimo_attn_prefill_backward(dims, layer_type, q, k, v, out, lse, dout, cu_seqlens, cu_seqlens.numel() - 1,
+                               max_seqlen, T, sink, dq, dk, dv, dsink, ws, stream)
+    return dq, dk, dv, dsink

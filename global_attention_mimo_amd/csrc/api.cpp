@@ -356,6 +356,40 @@ int mimo_kv_append_fp8(const mimo_attn_dims* dims, const uint16_t* k, const uint
                           kv_base, kv_capacity, nullptr, stream, &f);
 }
 
+size_t mimo_attn_prefill_backward_workspace_size(const mimo_attn_dims* dims, int32_t total_tokens) {
+    if (check_dims(dims, MIMO_LAYER_GA, 1) != MIMO_OK || total_tokens < 0) return 0;
+    return mimo::backward_workspace_bytes(total_tokens, dims->num_q_heads);
+}
+
+int mimo_attn_prefill_backward(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, const uint16_t* k,
+                               const uint16_t* v, const uint16_t* out, const float* lse, const uint16_t* dout,
+                               const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+                               int32_t total_tokens, const float* sink, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                               float* dsink, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (int st = check_dims(dims, layer_type, 1)) return st;
+    if (!q || !k || !v || !out || !lse || !dout || !cu_seqlens || !dq || !dk || !dv)
+        return fail(MIMO_ERR_INVALID_ARG, "q, k, v, out, lse, dout, cu_seqlens, dq, dk and dv must be non-NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) || !aligned16(dq) ||
+        !aligned16(dk) || !aligned16(dv))
+        return fail(MIMO_ERR_INVALID_ARG, "q, k, v, out, dout, dq, dk and dv must be 16-byte aligned");
+    if (num_seqs < 1 || num_seqs > kMaxGridYZ)
+        return fail(MIMO_ERR_INVALID_ARG, "num_seqs %d outside [1, %d]", num_seqs, kMaxGridYZ);
+    if (max_seqlen < 0) return fail(MIMO_ERR_INVALID_ARG, "max_seqlen %d is negative", max_seqlen);
+    if (total_tokens < 0) return fail(MIMO_ERR_INVALID_ARG, "total_tokens %d is negative", total_tokens);
+    if ((int64_t)total_tokens * dims->num_q_heads > (int64_t)INT32_MAX * 8)
+        return fail(MIMO_ERR_UNSUPPORTED, "total_tokens %d is too large", total_tokens);
+    const size_t need = mimo::backward_workspace_bytes(total_tokens, dims->num_q_heads);
+    if (max_seqlen == 0 || total_tokens == 0) return ok();
+    if (!workspace || workspace_bytes < need)
+        return fail(MIMO_ERR_WORKSPACE, "backward needs %zu workspace bytes (got %zu%s)", need, workspace_bytes,
+                    workspace ? "" : ", NULL");
+    if (!aligned16(workspace)) return fail(MIMO_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    mimo::BackwardArgs a{q, k, v, out, lse, dout, cu_seqlens, sink, dq, dk, dv, dsink, workspace, num_seqs,
+                         max_seqlen, total_tokens, dims->num_q_heads, dims->num_kv_heads, dims->sliding_window,
+                         dims->softmax_scale, dims->value_scale, layer_type == MIMO_LAYER_SWA};
+    return hip_status(mimo::launch_prefill_backward(a, stream), "backward launch");
+}
+
 const char* mimo_status_string(int status) {
     switch (status) {
         case MIMO_OK: return "MIMO_OK";

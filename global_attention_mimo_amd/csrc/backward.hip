@@ -1,0 +1,415 @@
+// backward.hip -- gradients of prefill attention: dq, dk, dv and the sink's.
+//
+// Operation (Hugging Face Transformers model doc "MiMo-V2-Flash": Key
+// features, SWA/GA with a learnable attention sink; MiMoV2FlashConfig, 64/4
+// heads, head_dim 192 / v_head_dim 128, sliding_window 129): the forward is
+// o = value_scale * sum_j P_j v_j with P_j = exp(s_j - LSE), s_j = scale q.k_j
+// and LSE = log(sum_j exp(s_j) + exp(sink)).  For an upstream dO the gradient
+// of sum(dO * o) is, per query row (token t, head h, group g):
+//   D     = dO . o                       dP_j = value_scale * dO . v_j
+//   dS_j  = P_j (dP_j - D)
+//   dq    = scale * sum_j dS_j k_j       dk_j += scale * dS_j q,  dv_j += value_scale * P_j dO
+//   dsink[h] = -sum_t exp(sink[h] - LSE_t) D_t
+// P is recomputed from the forward's LSE (natural log, sink included) and D
+// from its output o, so the sink needs no further term in dq/dk/dv.
+//
+// Kernels (all MFMAs v_mfma_f32_16x16x32_bf16, fp32 accumulate; P and dS are
+// rounded to bf16 as MFMA operands):
+//   bwd_rowdot_kernel  D = dO . o per (token, head), into the workspace;
+//   bwd_dq_kernel      one wave per token (16 heads of a KV group as the MFMA
+//                      N side); Q^T and dO^T stay in registers, 32-key tiles of
+//                      K and V are staged in LDS for 8 tokens; S^T = K Q^T and
+//                      dP^T = V dO^T, then dQ^T += K^T dS^T with K^T read from
+//                      the LDS tile by transposed reads;
+//   bwd_dkdv_kernel    one wave per 16 keys (the N side), K and V rows stay in
+//                      registers; blocks of 2 tokens x 16 heads of Q and dO are
+//                      staged in LDS for 128 keys; S = Q K^T and dP = dO V^T,
+//                      then dV^T += dO^T P and dK^T += Q^T dS;
+//   bwd_sink_kernel    dsink per head, a fixed-order block reduction.
+// LDS tiles are row-major with the 16-byte chunks of row r XOR-swizzled by
+// 2(r % 4), the layout the decode kernel reads V^T from.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace mimo {
+namespace {
+
+constexpr int kDqk = 192;
+constexpr int kDv = 128;
+constexpr int kGroup = 16;
+constexpr int kQRow = kDqk * 2;  // bytes of a staged Q or K row
+constexpr int kVRow = kDv * 2;   // bytes of a staged dO or V row
+
+__device__ __forceinline__ int swz(int r, int c) { return c ^ (2 * (r & 3)); }
+
+// 8 bf16 of tile row r, logical 16-byte chunk c (a direct MFMA operand).
+__device__ __forceinline__ bf16x8 lds_row8(const char* tile, int row_bytes, int r, int c) {
+    return *reinterpret_cast<const bf16x8*>(tile + r * row_bytes + swz(r, c) * 16);
+}
+
+__device__ __forceinline__ void lds_put16(char* tile, int row_bytes, int r, int c, const u32x4& x) {
+    *reinterpret_cast<u32x4*>(tile + r * row_bytes + swz(r, c) * 16) = x;
+}
+
+// Transposed A operand over tile rows 0..31, columns 16db .. 16db+15: lane l
+// (G = l/16) gets tile[row(8G+t)][16db + l%16] for t = 0..7 with row(8G+t) =
+// 4G+t (t < 4) or 16+4G+t-4 (t >= 4): the k order of a B operand packed from
+// two 16-row accumulator blocks (rows 4G+r of block 0, then of block 1).
+__device__ __forceinline__ bf16x8 lds_tr8(const char* tile, int row_bytes, int db, int lane) {
+    const int G = lane >> 4, tq = (lane & 15) >> 2;
+    const char* p = tile + (4 * G + tq) * row_bytes + 32 * (db ^ tq) + 8 * (lane & 3);
+    return join_tr(lds_read_tr16(reinterpret_cast<const uint16_t*>(p)),
+                   lds_read_tr16(reinterpret_cast<const uint16_t*>(p + 16 * row_bytes)));
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// ---------------------------------------------------------------------------
+// D = dO . o, 16 threads (8 elements each) per (token, head) row.
+__global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t* __restrict__ dout,
+                                                         const uint16_t* __restrict__ out, float* __restrict__ D,
+                                                         int64_t rows) {
+    const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const int c = threadIdx.x & 15;
+    float acc = 0.0f;
+    if (row < rows) {
+        const u32x4 a = reinterpret_cast<const u32x4*>(dout + row * kDv)[c];
+        const u32x4 o = reinterpret_cast<const u32x4*>(out + row * kDv)[c];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc += bf16_lo(a[i]) * bf16_lo(o[i]) + bf16_hi(a[i]) * bf16_hi(o[i]);
+    }
+    acc += __shfl_xor(acc, 8);
+    acc += __shfl_xor(acc, 4);
+    acc += __shfl_xor(acc, 2);
+    acc += __shfl_xor(acc, 1);
+    if (row < rows && c == 0) D[row] = acc;
+}
+
+// dsink[h] = -sum over the batch's tokens of exp(sink[h] - lse) * D, one block
+// per head; each thread sums a fixed stride of tokens, then a fixed tree.
+__global__ __launch_bounds__(256) void bwd_sink_kernel(const float* __restrict__ sink, const float* __restrict__ lse,
+                                                       const float* __restrict__ D, const int32_t* __restrict__ cu,
+                                                       int num_seqs, int max_seqlen, int hq,
+                                                       float* __restrict__ dsink) {
+    __shared__ float part[256];
+    const int h = blockIdx.x;
+    const float s = sink ? sink[h] : -__builtin_inff();
+    float acc = 0.0f;
+    if (s > -__builtin_inff()) {
+        for (int b = 0; b < num_seqs; ++b) {
+            const int s0 = cu[b], L = min(cu[b + 1] - s0, max_seqlen);
+            for (int t = threadIdx.x; t < L; t += 256) {
+                const size_t row = (size_t)(s0 + t) * hq + h;
+                acc += fast_exp2((s - lse[row]) * kLog2e) * D[row];
+            }
+        }
+    }
+    part[threadIdx.x] = acc;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) dsink[h] = -part[0];
+}
+
+// ---------------------------------------------------------------------------
+constexpr int kDqWaves = 8;    // tokens per dq workgroup
+constexpr int kDqKeys = 32;    // keys per staged K/V tile
+constexpr int kDqTileBytes = kDqKeys * (kQRow + kVRow);
+
+template <bool SWA>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void bwd_dq_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dws,
+    const int32_t* __restrict__ cu_seqlens, uint16_t* __restrict__ dq, int hq, int hkv, int window, float c_log2,
+    float scale, float value_scale, int max_seqlen, int nqb) {
+    __shared__ __attribute__((aligned(16))) char lds[2 * kDqTileBytes];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int G = lane >> 4;
+    const int b = blockIdx.z, g = blockIdx.y;
+    const int qb = SWA ? (int)blockIdx.x : nqb - 1 - (int)blockIdx.x;  // GA: longest rows first
+    const int s0 = cu_seqlens[b];
+    const int L = min(cu_seqlens[b + 1] - s0, max_seqlen);
+    const int q0 = qb * kDqWaves;
+    if (q0 >= L) return;
+    const int t = q0 + wave;
+    const bool valid = t < L;
+    const int tt = min(t, L - 1);
+    const int head = g * kGroup + (lane & 15);
+    const size_t qrow = (size_t)(s0 + tt) * hq + head;
+
+    // Q^T and dO^T of this token's 16 heads as MFMA B operands: lane holds
+    // d = 32st + 8G .. +7 of head lane%16.
+    bf16x8 qf[kDqk / 32], dof[kDv / 32];
+#pragma unroll
+    for (int st = 0; st < kDqk / 32; ++st)
+        qf[st] = __builtin_bit_cast(bf16x8, reinterpret_cast<const u32x4*>(q + qrow * kDqk)[4 * st + G]);
+#pragma unroll
+    for (int st = 0; st < kDv / 32; ++st)
+        dof[st] = __builtin_bit_cast(bf16x8, reinterpret_cast<const u32x4*>(dout + qrow * kDv)[4 * st + G]);
+    const float lse2 = lse[qrow] * kLog2e;
+    const float Drow = Dws[qrow];
+    f32x4 dqa[kDqk / 16];
+#pragma unroll
+    for (int db = 0; db < kDqk / 16; ++db) dqa[db] = f32x4{};
+
+    const int t_last = min(q0 + kDqWaves, L) - 1;
+    const int k_lo = SWA ? max(0, q0 - (window - 1)) : 0;
+    const int kt_begin = k_lo / kDqKeys, kt_end = t_last / kDqKeys;
+
+    // Staging: a tile is 32 K rows (24 chunks) then 32 V rows (16 chunks).
+    constexpr int kKChunks = kDqKeys * (kDqk / 8), kChunks = kKChunks + kDqKeys * (kDv / 8);
+    constexpr int kPer = (kChunks + 511) / 512;
+    u32x4 reg[kPer];
+    auto load_tile = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int c = min(tid + 512 * i, kChunks - 1);
+            const bool isk = c < kKChunks;
+            const int cc = isk ? c : c - kKChunks;
+            const int row = isk ? cc / (kDqk / 8) : cc / (kDv / 8);
+            const int ch = isk ? cc % (kDqk / 8) : cc % (kDv / 8);
+            const int key = min(kt * kDqKeys + row, L - 1);  // past the end: masked
+            const uint16_t* src = isk ? k + ((size_t)(s0 + key) * hkv + g) * kDqk : v + ((size_t)(s0 + key) * hkv + g) * kDv;
+            reg[i] = reinterpret_cast<const u32x4*>(src)[ch];
+        }
+    };
+    auto store_tile = [&](int buf) {
+        char* kt_ = lds + buf * kDqTileBytes;
+        char* vt_ = kt_ + kDqKeys * kQRow;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int c = tid + 512 * i;
+            if (c >= kChunks) continue;
+            if (c < kKChunks) lds_put16(kt_, kQRow, c / (kDqk / 8), c % (kDqk / 8), reg[i]);
+            else lds_put16(vt_, kVRow, (c - kKChunks) / (kDv / 8), (c - kKChunks) % (kDv / 8), reg[i]);
+        }
+    };
+    load_tile(kt_begin);
+    store_tile(0);
+    __syncthreads();
+    for (int kt = kt_begin; kt <= kt_end; ++kt) {
+        const int buf = (kt - kt_begin) & 1;
+        const bool more = kt < kt_end;
+        if (more) load_tile(kt + 1);
+        const char* Kt = lds + buf * kDqTileBytes;
+        const char* Vt = Kt + kDqKeys * kQRow;
+        // S^T and dP^T: lane holds key kt*32 + 16blk + 4G + r, head lane%16.
+        f32x4 s[2], dp[2];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            s[blk] = f32x4{};
+            dp[blk] = f32x4{};
+#pragma unroll
+            for (int st = 0; st < kDqk / 32; ++st)
+                s[blk] = mfma_16x16x32(lds_row8(Kt, kQRow, 16 * blk + (lane & 15), 4 * st + G), qf[st], s[blk]);
+#pragma unroll
+            for (int st = 0; st < kDv / 32; ++st)
+                dp[blk] = mfma_16x16x32(lds_row8(Vt, kVRow, 16 * blk + (lane & 15), 4 * st + G), dof[st], dp[blk]);
+        }
+        float ds[2][4];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = kt * kDqKeys + 16 * blk + 4 * G + r;
+                const bool ok = valid && key <= t && (!SWA || key >= t - (window - 1));
+                const float p = ok ? fast_exp2(__builtin_fmaf(s[blk][r], c_log2, -lse2)) : 0.0f;
+                ds[blk][r] = p * (value_scale * dp[blk][r] - Drow);
+            }
+        const bf16x8 dsf = pack_bf16x8(ds[0][0], ds[0][1], ds[0][2], ds[0][3], ds[1][0], ds[1][1], ds[1][2], ds[1][3]);
+#pragma unroll
+        for (int db = 0; db < kDqk / 16; ++db) dqa[db] = mfma_16x16x32(lds_tr8(Kt, kQRow, db, lane), dsf, dqa[db]);
+        if (more) store_tile(buf ^ 1);
+        __syncthreads();
+    }
+    if (!valid) return;
+    // lane holds dQ^T[d = 16db + 4G + r][head lane%16]
+    uint16_t* drow = dq + qrow * kDqk;
+#pragma unroll
+    for (int db = 0; db < kDqk / 16; ++db)
+        *reinterpret_cast<u32x2*>(drow + 16 * db + 4 * G) =
+            u32x2{pack_bf16x2(dqa[db][0] * scale, dqa[db][1] * scale), pack_bf16x2(dqa[db][2] * scale, dqa[db][3] * scale)};
+}
+
+// ---------------------------------------------------------------------------
+constexpr int kKvWaves = 8;                    // 16 keys per wave
+constexpr int kKvKeys = 16 * kKvWaves;         // keys per dk/dv workgroup
+constexpr int kKvTok = 2;                      // query tokens per staged block (2 x 16 heads = 32 rows)
+constexpr int kKvRows = kKvTok * kGroup;
+constexpr int kKvTileBytes = kKvRows * (kQRow + kVRow) + kKvRows * 8;  // Q, dO, then lse2 and D per row
+
+template <bool SWA>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void bwd_dkdv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dws,
+    const int32_t* __restrict__ cu_seqlens, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int hq, int hkv,
+    int window, float c_log2, float scale, float value_scale, int max_seqlen) {
+    __shared__ __attribute__((aligned(16))) char lds[2 * kKvTileBytes];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int G = lane >> 4;
+    const int b = blockIdx.z, g = blockIdx.y;
+    const int s0 = cu_seqlens[b];
+    const int L = min(cu_seqlens[b + 1] - s0, max_seqlen);
+    const int k0 = blockIdx.x * kKvKeys;  // GA: the first key blocks have the most queries and run first
+    if (k0 >= L) return;
+    const int key = k0 + 16 * wave + (lane & 15);
+    const int kk = min(key, L - 1);
+    const size_t krow = (size_t)(s0 + kk) * hkv + g;
+
+    // K and V rows of this lane's key as MFMA B operands (d = 32st + 8G .. +7).
+    bf16x8 kf[kDqk / 32], vf[kDv / 32];
+#pragma unroll
+    for (int st = 0; st < kDqk / 32; ++st)
+        kf[st] = __builtin_bit_cast(bf16x8, reinterpret_cast<const u32x4*>(k + krow * kDqk)[4 * st + G]);
+#pragma unroll
+    for (int st = 0; st < kDv / 32; ++st)
+        vf[st] = __builtin_bit_cast(bf16x8, reinterpret_cast<const u32x4*>(v + krow * kDv)[4 * st + G]);
+    f32x4 dka[kDqk / 16], dva[kDv / 16];
+#pragma unroll
+    for (int db = 0; db < kDqk / 16; ++db) dka[db] = f32x4{};
+#pragma unroll
+    for (int db = 0; db < kDv / 16; ++db) dva[db] = f32x4{};
+
+    // Queries that see a key of the block: tokens k0 .. q_end-1.
+    const int q_end = SWA ? min(L, k0 + kKvKeys - 1 + window) : L;
+    const int nblk = (q_end - k0 + kKvTok - 1) / kKvTok;
+
+    // Staging: 32 Q rows (24 chunks), 32 dO rows (16 chunks); row 16i + hh is
+    // token q0 + i, head 16g + hh.  Threads 0..31 also fetch lse2 and D.
+    constexpr int kQChunks = kKvRows * (kDqk / 8), kChunks = kQChunks + kKvRows * (kDv / 8);
+    constexpr int kPer = (kChunks + 511) / 512;
+    u32x4 reg[kPer];
+    float st_lse = 0.0f, st_d = 0.0f;
+    auto load_blk = [&](int q0) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int c = min(tid + 512 * i, kChunks - 1);
+            const bool isq = c < kQChunks;
+            const int cc = isq ? c : c - kQChunks;
+            const int row = isq ? cc / (kDqk / 8) : cc / (kDv / 8);
+            const int ch = isq ? cc % (kDqk / 8) : cc % (kDv / 8);
+            const int tok = min(q0 + row / kGroup, L - 1);  // past the end: masked
+            const size_t r = (size_t)(s0 + tok) * hq + g * kGroup + row % kGroup;
+            reg[i] = isq ? reinterpret_cast<const u32x4*>(q + r * kDqk)[ch]
+                         : reinterpret_cast<const u32x4*>(dout + r * kDv)[ch];
+        }
+        if (tid < kKvRows) {
+            const int tok = min(q0 + tid / kGroup, L - 1);
+            const size_t r = (size_t)(s0 + tok) * hq + g * kGroup + tid % kGroup;
+            st_lse = lse[r] * kLog2e;
+            st_d = Dws[r];
+        }
+    };
+    auto store_blk = [&](int buf) {
+        char* qt_ = lds + buf * kKvTileBytes;
+        char* ot_ = qt_ + kKvRows * kQRow;
+        float* sf = reinterpret_cast<float*>(ot_ + kKvRows * kVRow);
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int c = tid + 512 * i;
+            if (c >= kChunks) continue;
+            if (c < kQChunks) lds_put16(qt_, kQRow, c / (kDqk / 8), c % (kDqk / 8), reg[i]);
+            else lds_put16(ot_, kVRow, (c - kQChunks) / (kDv / 8), (c - kQChunks) % (kDv / 8), reg[i]);
+        }
+        if (tid < kKvRows) {
+            sf[tid] = st_lse;
+            sf[kKvRows + tid] = st_d;
+        }
+    };
+    load_blk(k0);
+    store_blk(0);
+    __syncthreads();
+    for (int ib = 0; ib < nblk; ++ib) {
+        const int buf = ib & 1;
+        const bool more = ib + 1 < nblk;
+        const int q0 = k0 + ib * kKvTok;
+        if (more) load_blk(q0 + kKvTok);
+        const char* Qt = lds + buf * kKvTileBytes;
+        const char* Ot = Qt + kKvRows * kQRow;
+        const float* sf = reinterpret_cast<const float*>(Ot + kKvRows * kVRow);
+        // S = Q K^T and dP = dO V^T: lane holds row 16blk + 4G + r (token
+        // q0 + blk, head 4G + r of the group) and key `key`.
+        f32x4 s[kKvTok], dp[kKvTok];
+#pragma unroll
+        for (int blk = 0; blk < kKvTok; ++blk) {
+            s[blk] = f32x4{};
+            dp[blk] = f32x4{};
+#pragma unroll
+            for (int st = 0; st < kDqk / 32; ++st)
+                s[blk] = mfma_16x16x32(lds_row8(Qt, kQRow, 16 * blk + (lane & 15), 4 * st + G), kf[st], s[blk]);
+#pragma unroll
+            for (int st = 0; st < kDv / 32; ++st)
+                dp[blk] = mfma_16x16x32(lds_row8(Ot, kVRow, 16 * blk + (lane & 15), 4 * st + G), vf[st], dp[blk]);
+        }
+        float p[kKvTok][4], ds[kKvTok][4];
+#pragma unroll
+        for (int blk = 0; blk < kKvTok; ++blk) {
+            const int tok = q0 + blk;
+            const bool tok_ok = tok < L && key < L && key <= tok && (!SWA || tok <= key + window - 1);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * blk + 4 * G + r;
+                const float pr = tok_ok ? fast_exp2(__builtin_fmaf(s[blk][r], c_log2, -sf[row])) : 0.0f;
+                p[blk][r] = pr;
+                ds[blk][r] = pr * (value_scale * dp[blk][r] - sf[kKvRows + row]);
+            }
+        }
+        const bf16x8 pf = pack_bf16x8(p[0][0], p[0][1], p[0][2], p[0][3], p[1][0], p[1][1], p[1][2], p[1][3]);
+        const bf16x8 dsf = pack_bf16x8(ds[0][0], ds[0][1], ds[0][2], ds[0][3], ds[1][0], ds[1][1], ds[1][2], ds[1][3]);
+#pragma unroll
+        for (int db = 0; db < kDv / 16; ++db) dva[db] = mfma_16x16x32(lds_tr8(Ot, kVRow, db, lane), pf, dva[db]);
+#pragma unroll
+        for (int db = 0; db < kDqk / 16; ++db) dka[db] = mfma_16x16x32(lds_tr8(Qt, kQRow, db, lane), dsf, dka[db]);
+        if (more) store_blk(buf ^ 1);
+        __syncthreads();
+    }
+    if (key >= L) return;
+    // lane holds dK^T[d = 16db + 4G + r][key] and dV^T likewise
+    uint16_t* kout = dk + krow * kDqk;
+    uint16_t* vout = dv + krow * kDv;
+#pragma unroll
+    for (int db = 0; db < kDqk / 16; ++db)
+        *reinterpret_cast<u32x2*>(kout + 16 * db + 4 * G) =
+            u32x2{pack_bf16x2(dka[db][0] * scale, dka[db][1] * scale), pack_bf16x2(dka[db][2] * scale, dka[db][3] * scale)};
+#pragma unroll
+    for (int db = 0; db < kDv / 16; ++db)
+        *reinterpret_cast<u32x2*>(vout + 16 * db + 4 * G) =
+            u32x2{pack_bf16x2(dva[db][0] * value_scale, dva[db][1] * value_scale),
+                  pack_bf16x2(dva[db][2] * value_scale, dva[db][3] * value_scale)};
+}
+
+}  // namespace
+
+hipError_t launch_prefill_backward(const BackwardArgs& a, hipStream_t stream) {
+    if (a.max_seqlen <= 0 || a.total_tokens <= 0) return hipSuccess;
+    float* D = static_cast<float*>(a.workspace);
+    const int64_t rows = (int64_t)a.total_tokens * a.hq;
+    hipLaunchKernelGGL(bwd_rowdot_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, a.dout, a.out, D,
+                       rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const float c_log2 = a.softmax_scale * kLog2e;
+    const int nqb = (a.max_seqlen + kDqWaves - 1) / kDqWaves;
+    hipLaunchKernelGGL(a.swa ? bwd_dq_kernel<true> : bwd_dq_kernel<false>, dim3(nqb, a.hkv, a.num_seqs), dim3(512), 0,
+                       stream, a.q, a.k, a.v, a.dout, a.lse, D, a.cu_seqlens, a.dq, a.hq, a.hkv, a.window, c_log2,
+                       a.softmax_scale, a.value_scale, a.max_seqlen, nqb);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int nkb = (a.max_seqlen + kKvKeys - 1) / kKvKeys;
+    hipLaunchKernelGGL(a.swa ? bwd_dkdv_kernel<true> : bwd_dkdv_kernel<false>, dim3(nkb, a.hkv, a.num_seqs),
+                       dim3(512), 0, stream, a.q, a.k, a.v, a.dout, a.lse, D, a.cu_seqlens, a.dk, a.dv, a.hq, a.hkv,
+                       a.window, c_log2, a.softmax_scale, a.value_scale, a.max_seqlen);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (a.dsink) {
+        hipLaunchKernelGGL(bwd_sink_kernel, dim3(a.hq), dim3(256), 0, stream, a.sink, a.lse, D, a.cu_seqlens,
+                           a.num_seqs, a.max_seqlen, a.hq, a.dsink);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+}  // namespace mimo

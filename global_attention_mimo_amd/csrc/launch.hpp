@@ -89,4 +89,26 @@ struct AppendArgs {
 };
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 
+struct BackwardArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const uint16_t* out;
+    const float* lse;
+    const uint16_t* dout;
+    const int32_t* cu_seqlens;
+    const float* sink;
+    uint16_t* dq;
+    uint16_t* dk;
+    uint16_t* dv;
+    float* dsink;
+    void* workspace;  // D = dO . o per (token, head), fp32
+    int num_seqs, max_seqlen, total_tokens, hq, hkv, window;
+    float softmax_scale, value_scale;
+    bool swa;
+};
+// Bytes of backward workspace: one fp32 per (token, query head).
+inline size_t backward_workspace_bytes(int total_tokens, int hq) { return (size_t)total_tokens * hq * sizeof(float); }
+hipError_t launch_prefill_backward(const BackwardArgs& a, hipStream_t stream);
+
 }  // namespace mimo

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MIMO_ATTN_ABI_VERSION 4
+#define MIMO_ATTN_ABI_VERSION 5
 
 /* Layer type: which key set a query sees (model doc, Key features; config
  * layer_types). */
@@ -326,6 +326,40 @@ int mimo_attn_decode_fp8(const mimo_attn_dims* dims,
                          int32_t batch, int32_t max_ctx, int32_t split_tokens,
                          const float* sink, uint16_t* out, float* lse,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Backward of mimo_attn_prefill: the gradients of sum(dout * out) for an
+ * upstream gradient dout, including the learnable sink's (model doc, Key
+ * features: the sink bias is learnable).  With P_j = exp(s_j - lse) for the
+ * query row's keys j (lse natural log, sink included) and o the row's output:
+ *   D     = dout . o                     dP_j = value_scale * dout . v_j
+ *   dS_j  = P_j * (dP_j - D)
+ *   dq    = softmax_scale * sum_j dS_j k_j
+ *   dk_j  = softmax_scale * sum over rows seeing j (16 heads of the group) of dS_j q
+ *   dv_j  = value_scale * sum over those rows of P_j dout
+ *   dsink[h] = -sum over tokens of exp(sink[h] - lse) * D
+ *
+ *   q, k, v, cu_seqlens, num_seqs, max_seqlen, sink  as for the forward call.
+ *   out, lse     the forward's out [T][Hq][128] bf16 and lse [T][Hq] fp32 (required).
+ *   dout         [T][Hq][128] bf16.
+ *   total_tokens (host) == cu_seqlens[num_seqs]; sizes the workspace.
+ *   dq, dk, dv   [T][Hq][192], [T][Hkv][192], [T][Hkv][128] bf16, rounded to
+ *                nearest even.  Rows of tokens past max_seqlen are left
+ *                unwritten, and such tokens contribute nothing.
+ *   dsink        [Hq] fp32, or NULL to skip; all zero when sink is NULL.
+ *   workspace    >= mimo_attn_prefill_backward_workspace_size(dims,
+ *                total_tokens) bytes of device memory, no initialisation.
+ * A call with max_seqlen == 0 or total_tokens == 0 enqueues nothing.
+ */
+size_t mimo_attn_prefill_backward_workspace_size(const mimo_attn_dims* dims, int32_t total_tokens);
+
+int mimo_attn_prefill_backward(const mimo_attn_dims* dims, int layer_type,
+                               const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                               const uint16_t* out, const float* lse, const uint16_t* dout,
+                               const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+                               int32_t total_tokens, const float* sink,
+                               uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dsink,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static English name of a status code ("MIMO_OK", ...). */
 const char* mimo_status_string(int status);

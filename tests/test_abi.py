@@ -42,7 +42,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_version_and_status_strings(L):
-    assert B.mimo_abi_version() == 4
+    assert B.mimo_abi_version() == 5
     assert B.mimo_status_string(0) == "MIMO_OK"
     assert B.mimo_status_string(3) == "MIMO_ERR_WORKSPACE"
     assert B.mimo_status_string(99) == "MIMO_ERR_UNKNOWN"
@@ -307,6 +307,42 @@ def test_append_fp8_rejects(L, case, status):
 
 def test_append_fp8_nothing_is_ok(L):
     assert fp8_append_call(L, total=0) == B.MIMO_OK
+
+
+def bwd_call(L, dims=None, layer=1, q=FAKE, out=FAKE, lse=FAKE, do=FAKE, cu=FAKE, nseq=2, maxlen=16, total=32,
+             dq=FAKE, dk=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    d = dims or B.make_dims()
+    return L.mimo_attn_prefill_backward(ctypes.byref(d), layer, q, FAKE, FAKE, out, lse, do, cu, nseq, maxlen, total,
+                                        None, dq, dk, FAKE, None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(layer=3), B.MIMO_ERR_INVALID_ARG),
+    (dict(q=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(out=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(lse=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(do=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(do=FAKE_ODD), B.MIMO_ERR_INVALID_ARG),
+    (dict(cu=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(dq=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(dk=FAKE_ODD), B.MIMO_ERR_INVALID_ARG),
+    (dict(nseq=0), B.MIMO_ERR_INVALID_ARG),
+    (dict(maxlen=-1), B.MIMO_ERR_INVALID_ARG),
+    (dict(total=-1), B.MIMO_ERR_INVALID_ARG),
+    (dict(ws=None), B.MIMO_ERR_WORKSPACE),
+    (dict(ws_bytes=100), B.MIMO_ERR_WORKSPACE),
+    (dict(dims=B.make_dims(head_dim_qk=128)), B.MIMO_ERR_UNSUPPORTED),
+])
+def test_backward_rejects(L, case, status):
+    assert bwd_call(L, **case) == status
+    assert B.mimo_last_error() != ""
+
+
+def test_backward_empty_and_workspace_size(L):
+    assert bwd_call(L, maxlen=0, ws=None) == B.MIMO_OK
+    assert bwd_call(L, total=0, ws=None) == B.MIMO_OK
+    assert B.mimo_attn_prefill_backward_workspace_size(B.make_dims(), 1000) == 1000 * 64 * 4
+    assert B.mimo_attn_prefill_backward_workspace_size(B.make_dims(head_dim_v=64), 1000) == 0
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
