@@ -13,21 +13,25 @@
 // P is recomputed from the forward's LSE (natural log, sink included) and D
 // from its output o, so the sink needs no further term in dq/dk/dv.
 //
-// Kernels (all MFMAs v_mfma_f32_16x16x32_bf16, fp32 accumulate; P and dS are
-// rounded to bf16 as MFMA operands):
+// Kernels (fp32 accumulate; P and dS are rounded to bf16 as MFMA operands):
 //   bwd_rowdot_kernel  D = dO . o per (token, head), into the workspace;
-//   bwd_dq_kernel      one wave per token (16 heads of a KV group as the MFMA
-//                      N side); Q^T and dO^T stay in registers, 32-key tiles of
-//                      K and V are staged in LDS for 8 tokens; S^T = K Q^T and
-//                      dP^T = V dO^T, then dQ^T += K^T dS^T with K^T read from
-//                      the LDS tile by transposed reads;
-//   bwd_dkdv_kernel    one wave per 16 keys (the N side), K and V rows stay in
-//                      registers; blocks of 2 tokens x 16 heads of Q and dO are
-//                      staged in LDS for 128 keys; S = Q K^T and dP = dO V^T,
-//                      then dV^T += dO^T P and dK^T += Q^T dS;
+//   bwd_dq_kernel      32x32x16 MFMAs, one wave per 2 tokens x 16 heads of a
+//                      KV group (the MFMA N side); Q^T and dO^T stay in
+//                      registers, 32-key tiles of K and V are staged in LDS for
+//                      16 tokens; S^T = K Q^T and dP^T = V dO^T, then
+//                      dQ^T += K^T dS^T with K^T read from the LDS tile by
+//                      transposed reads;
+//   bwd_dkdv_kernel    16x16x32 MFMAs, one wave per 16 keys (the N side), K and
+//                      V rows stay in registers; blocks of 2 tokens x 16 heads
+//                      of Q and dO are staged in LDS for 128 keys; S = Q K^T
+//                      and dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS.
+//                      (A 32x32x16 form with 32 keys per wave needs ~390
+//                      registers, i.e. one wave per SIMD, and ran 1.4x slower.)
 //   bwd_sink_kernel    dsink per head, a fixed-order block reduction.
-// LDS tiles are row-major with the 16-byte chunks of row r XOR-swizzled by
-// 2(r % 4), the layout the decode kernel reads V^T from.
+// LDS tiles: the dq kernel uses the forward's padded row strides (192 + 8 and
+// 128 + 32 bf16) and its transposed-read pattern; the dk/dv kernel uses
+// unpadded rows with the 16-byte chunks of row r XOR-swizzled by 2(r % 4),
+// the layout the decode kernel reads V^T from.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -115,53 +119,59 @@ __global__ __launch_bounds__(256) void bwd_sink_kernel(const float* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-constexpr int kDqWaves = 8;    // tokens per dq workgroup
-constexpr int kDqKeys = 32;    // keys per staged K/V tile
-constexpr int kDqTileBytes = kDqKeys * (kQRow + kVRow);
+// dq: the forward's tile shape with v_mfma_f32_32x32x16_bf16 -- each wave owns
+// 32 query rows (2 tokens x 16 heads of a KV group, lane row r32 = lane % 32,
+// hh = lane / 32 the half of the MFMA K dimension it feeds), so every 16-byte
+// operand read from LDS feeds 32 x 32 x 16 MACs.  K and V tiles (32 keys) sit
+// in LDS with the forward's padded row strides.
+constexpr int kDqTok = 16;           // tokens per workgroup (8 waves x 2)
+constexpr int kDqNK = 32;            // keys per staged tile
+constexpr int kKS = kDqk + 8;        // LDS row strides (bf16 elements)
+constexpr int kVS = kDv + 32;
+constexpr int kDqLdsK = kDqNK * kKS;
+constexpr int kDqLdsV = kDqNK * kVS;
 
 template <bool SWA>
-__global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void bwd_dq_kernel(
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dws,
     const int32_t* __restrict__ cu_seqlens, uint16_t* __restrict__ dq, int hq, int hkv, int window, float c_log2,
     float scale, float value_scale, int max_seqlen, int nqb) {
-    __shared__ __attribute__((aligned(16))) char lds[2 * kDqTileBytes];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_k[2 * kDqLdsK];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_v[2 * kDqLdsV];
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int G = lane >> 4;
+    const int wave = tid >> 6;
+    const int r32 = lane & 31, hh = lane >> 5;
     const int b = blockIdx.z, g = blockIdx.y;
     const int qb = SWA ? (int)blockIdx.x : nqb - 1 - (int)blockIdx.x;  // GA: longest rows first
     const int s0 = cu_seqlens[b];
     const int L = min(cu_seqlens[b + 1] - s0, max_seqlen);
-    const int q0 = qb * kDqWaves;
+    const int q0 = qb * kDqTok;
     if (q0 >= L) return;
-    const int t = q0 + wave;
-    const bool valid = t < L;
-    const int tt = min(t, L - 1);
-    const int head = g * kGroup + (lane & 15);
-    const size_t qrow = (size_t)(s0 + tt) * hq + head;
+    const int tok = q0 + 2 * wave + (r32 >> 4);
+    const bool valid = tok < L;
+    const int head = g * kGroup + (r32 & 15);
+    const size_t qrow = (size_t)(s0 + min(tok, L - 1)) * hq + head;
 
-    // Q^T and dO^T of this token's 16 heads as MFMA B operands: lane holds
-    // d = 32st + 8G .. +7 of head lane%16.
-    bf16x8 qf[kDqk / 32], dof[kDv / 32];
+    // Q^T and dO^T of the wave's 32 rows as MFMA B operands (d = 16s + 8hh .. +7).
+    bf16x8 qf[kDqk / 16], dof[kDv / 16];
 #pragma unroll
-    for (int st = 0; st < kDqk / 32; ++st)
-        qf[st] = __builtin_bit_cast(bf16x8, reinterpret_cast<const u32x4*>(q + qrow * kDqk)[4 * st + G]);
+    for (int st = 0; st < kDqk / 16; ++st)
+        qf[st] = __builtin_bit_cast(bf16x8, reinterpret_cast<const u32x4*>(q + qrow * kDqk)[2 * st + hh]);
 #pragma unroll
-    for (int st = 0; st < kDv / 32; ++st)
-        dof[st] = __builtin_bit_cast(bf16x8, reinterpret_cast<const u32x4*>(dout + qrow * kDv)[4 * st + G]);
+    for (int st = 0; st < kDv / 16; ++st)
+        dof[st] = __builtin_bit_cast(bf16x8, reinterpret_cast<const u32x4*>(dout + qrow * kDv)[2 * st + hh]);
     const float lse2 = lse[qrow] * kLog2e;
     const float Drow = Dws[qrow];
-    f32x4 dqa[kDqk / 16];
+    f32x16 dqa[kDqk / 32];
 #pragma unroll
-    for (int db = 0; db < kDqk / 16; ++db) dqa[db] = f32x4{};
+    for (int db = 0; db < kDqk / 32; ++db) dqa[db] = f32x16{};
 
-    const int t_last = min(q0 + kDqWaves, L) - 1;
+    const int t_last = min(q0 + kDqTok, L) - 1;
     const int k_lo = SWA ? max(0, q0 - (window - 1)) : 0;
-    const int kt_begin = k_lo / kDqKeys, kt_end = t_last / kDqKeys;
+    const int kt_begin = k_lo / kDqNK, kt_end = t_last / kDqNK;
 
-    // Staging: a tile is 32 K rows (24 chunks) then 32 V rows (16 chunks).
-    constexpr int kKChunks = kDqKeys * (kDqk / 8), kChunks = kKChunks + kDqKeys * (kDv / 8);
+    constexpr int kKChunks = kDqNK * (kDqk / 8), kChunks = kKChunks + kDqNK * (kDv / 8);
     constexpr int kPer = (kChunks + 511) / 512;
     u32x4 reg[kPer];
     auto load_tile = [&](int kt) {
@@ -172,67 +182,79 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void bwd_dq_ke
             const int cc = isk ? c : c - kKChunks;
             const int row = isk ? cc / (kDqk / 8) : cc / (kDv / 8);
             const int ch = isk ? cc % (kDqk / 8) : cc % (kDv / 8);
-            const int key = min(kt * kDqKeys + row, L - 1);  // past the end: masked
+            const int key = min(kt * kDqNK + row, L - 1);  // past the end: masked
             const uint16_t* src = isk ? k + ((size_t)(s0 + key) * hkv + g) * kDqk : v + ((size_t)(s0 + key) * hkv + g) * kDv;
             reg[i] = reinterpret_cast<const u32x4*>(src)[ch];
         }
     };
     auto store_tile = [&](int buf) {
-        char* kt_ = lds + buf * kDqTileBytes;
-        char* vt_ = kt_ + kDqKeys * kQRow;
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int c = tid + 512 * i;
             if (c >= kChunks) continue;
-            if (c < kKChunks) lds_put16(kt_, kQRow, c / (kDqk / 8), c % (kDqk / 8), reg[i]);
-            else lds_put16(vt_, kVRow, (c - kKChunks) / (kDv / 8), (c - kKChunks) % (kDv / 8), reg[i]);
+            if (c < kKChunks)
+                *reinterpret_cast<u32x4*>(lds_k + buf * kDqLdsK + (c / (kDqk / 8)) * kKS + (c % (kDqk / 8)) * 8) = reg[i];
+            else
+                *reinterpret_cast<u32x4*>(lds_v + buf * kDqLdsV + ((c - kKChunks) / (kDv / 8)) * kVS +
+                                          ((c - kKChunks) % (kDv / 8)) * 8) = reg[i];
         }
     };
+    // Direct A operands: key row r32, d = 16s + 8hh.  Transposed K^T reads
+    // (the forward's V^T pattern): rows 4hh + (lane%16)/4 (+8) of a 16-key step,
+    // columns 16((lane/16)%2) + 4(lane%4) of a 32-wide d block.
+    const int kdir = r32 * kKS + 8 * hh, vdir = r32 * kVS + 8 * hh;
+    const int ktr = (4 * hh + ((lane & 15) >> 2)) * kKS + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     load_tile(kt_begin);
     store_tile(0);
     __syncthreads();
     for (int kt = kt_begin; kt <= kt_end; ++kt) {
         const int buf = (kt - kt_begin) & 1;
         const bool more = kt < kt_end;
+        const uint16_t* ktile = lds_k + buf * kDqLdsK;
+        const uint16_t* vtile = lds_v + buf * kDqLdsV;
+        const int kbase = kt * kDqNK;
+        // S^T = K Q^T and dP^T = V dO^T: lane holds key kbase + 8(r/4) + 4hh + r%4, row r32.
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int st = 0; st < kDqk / 16; ++st)
+            s = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(ktile + kdir + 16 * st), qf[st], s);
+#pragma unroll
+        for (int st = 0; st < kDv / 16; ++st)
+            dp = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(vtile + vdir + 16 * st), dof[st], dp);
+        // The next tile's loads go out here rather than at the top: their
+        // registers then live only through the dQ MFMAs, not the S/dP ones.
         if (more) load_tile(kt + 1);
-        const char* Kt = lds + buf * kDqTileBytes;
-        const char* Vt = Kt + kDqKeys * kQRow;
-        // S^T and dP^T: lane holds key kt*32 + 16blk + 4G + r, head lane%16.
-        f32x4 s[2], dp[2];
+        float ds[16];
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            s[blk] = f32x4{};
-            dp[blk] = f32x4{};
-#pragma unroll
-            for (int st = 0; st < kDqk / 32; ++st)
-                s[blk] = mfma_16x16x32(lds_row8(Kt, kQRow, 16 * blk + (lane & 15), 4 * st + G), qf[st], s[blk]);
-#pragma unroll
-            for (int st = 0; st < kDv / 32; ++st)
-                dp[blk] = mfma_16x16x32(lds_row8(Vt, kVRow, 16 * blk + (lane & 15), 4 * st + G), dof[st], dp[blk]);
+        for (int r = 0; r < 16; ++r) {
+            const int key = kbase + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const bool ok = valid && key <= tok && (!SWA || key >= tok - (window - 1));
+            const float p = ok ? fast_exp2(__builtin_fmaf(s[r], c_log2, -lse2)) : 0.0f;
+            ds[r] = p * (value_scale * dp[r] - Drow);
         }
-        float ds[2][4];
+        // dQ^T += K^T dS^T: B operand of k-step ks holds keys 16ks + {4hh + t, 8 + 4hh + t - 4}.
+        const bf16x8 dsf0 = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+        const bf16x8 dsf1 = pack_bf16x8(ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]);
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = kt * kDqKeys + 16 * blk + 4 * G + r;
-                const bool ok = valid && key <= t && (!SWA || key >= t - (window - 1));
-                const float p = ok ? fast_exp2(__builtin_fmaf(s[blk][r], c_log2, -lse2)) : 0.0f;
-                ds[blk][r] = p * (value_scale * dp[blk][r] - Drow);
-            }
-        const bf16x8 dsf = pack_bf16x8(ds[0][0], ds[0][1], ds[0][2], ds[0][3], ds[1][0], ds[1][1], ds[1][2], ds[1][3]);
-#pragma unroll
-        for (int db = 0; db < kDqk / 16; ++db) dqa[db] = mfma_16x16x32(lds_tr8(Kt, kQRow, db, lane), dsf, dqa[db]);
+        for (int db = 0; db < kDqk / 32; ++db) {
+            const uint16_t* p0 = ktile + ktr + db * 32;
+            const uint16_t* p1 = p0 + 16 * kKS;
+            dqa[db] = mfma_32x32x16(join_tr(lds_read_tr16(p0), lds_read_tr16(p0 + 8 * kKS)), dsf0, dqa[db]);
+            dqa[db] = mfma_32x32x16(join_tr(lds_read_tr16(p1), lds_read_tr16(p1 + 8 * kKS)), dsf1, dqa[db]);
+        }
         if (more) store_tile(buf ^ 1);
         __syncthreads();
     }
     if (!valid) return;
-    // lane holds dQ^T[d = 16db + 4G + r][head lane%16]
+    // lane holds dQ^T[d = 32db + 8j + 4hh + (0..3)][row r32]
     uint16_t* drow = dq + qrow * kDqk;
 #pragma unroll
-    for (int db = 0; db < kDqk / 16; ++db)
-        *reinterpret_cast<u32x2*>(drow + 16 * db + 4 * G) =
-            u32x2{pack_bf16x2(dqa[db][0] * scale, dqa[db][1] * scale), pack_bf16x2(dqa[db][2] * scale, dqa[db][3] * scale)};
+    for (int db = 0; db < kDqk / 32; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<u32x2*>(drow + 32 * db + 8 * j + 4 * hh) =
+                u32x2{pack_bf16x2(dqa[db][4 * j] * scale, dqa[db][4 * j + 1] * scale),
+                      pack_bf16x2(dqa[db][4 * j + 2] * scale, dqa[db][4 * j + 3] * scale)};
 }
 
 // ---------------------------------------------------------------------------
@@ -394,7 +416,7 @@ hipError_t launch_prefill_backward(const BackwardArgs& a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const float c_log2 = a.softmax_scale * kLog2e;
-    const int nqb = (a.max_seqlen + kDqWaves - 1) / kDqWaves;
+    const int nqb = (a.max_seqlen + kDqTok - 1) / kDqTok;
     hipLaunchKernelGGL(a.swa ? bwd_dq_kernel<true> : bwd_dq_kernel<false>, dim3(nqb, a.hkv, a.num_seqs), dim3(512), 0,
                        stream, a.q, a.k, a.v, a.dout, a.lse, D, a.cu_seqlens, a.dq, a.hq, a.hkv, a.window, c_log2,
                        a.softmax_scale, a.value_scale, a.max_seqlen, nqb);
