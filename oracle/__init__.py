@@ -76,6 +76,8 @@ class Oracle:
         lib.oracle_prefill_backward.restype = _I
         lib.oracle_prefill_backward.argtypes = [_I, _I, _I, _I, _I, _I, _F, _F, _P, _P, _P, _P, _P, _I, _P, _P,
                                                 _I64, _P, _I64, _P, _P, _P, _P, _I]
+        lib.oracle_rope.restype = _I
+        lib.oracle_rope.argtypes = [_I, _I, _I, _P, _P, _P, _I64, ctypes.c_double, _I, _P, _P]
         lib.oracle_decode_fp8.restype = _I
         lib.oracle_decode_fp8.argtypes = [_I, _I, _I, _I, _F, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P,
                                           _P, _I]
@@ -256,6 +258,29 @@ class Oracle:
         if rc != OK:
             raise ValueError(f"oracle_prefill_backward rejected its arguments (status {rc})")
         return dq, dk, dvv, ds
+
+    def rope(self, q, k, positions, *, theta: float, rotary_dim: int):
+        """Rotary embedding of q [T][Hq][D] and k [T][Hkv][D] (bf16 bits, either may be None) at
+        positions [T]; returns float64 (q_out, k_out)."""
+        pos = np.ascontiguousarray(positions, dtype=np.int32)
+        T = pos.shape[0]
+        qq = None if q is None else np.ascontiguousarray(q)
+        kk = None if k is None else np.ascontiguousarray(k)
+        ref = qq if qq is not None else kk
+        d = ref.shape[2]
+        hq = 0 if qq is None else qq.shape[1]
+        hkv = 0 if kk is None else kk.shape[1]
+        if qq is not None:
+            qq = self._u16(qq, (hq, d))
+        if kk is not None:
+            kk = self._u16(kk, (hkv, d))
+        qo = None if qq is None else np.empty(qq.shape, np.float64)
+        ko = None if kk is None else np.empty(kk.shape, np.float64)
+        rc = self.lib.oracle_rope(hq, hkv, d, self._ptr(qq), self._ptr(kk), self._ptr(pos), T, float(theta),
+                                  rotary_dim, self._ptr(qo), self._ptr(ko))
+        if rc != OK:
+            raise ValueError(f"oracle_rope rejected its arguments (status {rc})")
+        return qo, ko
 
     # -- paged GA pool ----------------------------------------------------
     @staticmethod

@@ -836,6 +836,48 @@ int oracle_kv_append_paged(int hkv, int dqk, int dv, const uint16_t* k, const ui
 }
 
 /* ------------------------------------------------------------------------ */
+/* Rotary position embedding of queries and keys (model doc,              */
+/* MiMoV2FlashConfig, rope_parameters: rope_theta, with the Transformers   */
+/* RoPE convention): the first rd = rotary_dim dims of every head vector x  */
+/* at position p rotate in pairs (i, i + rd/2), i < rd/2, by the angle       */
+/* p * f_i with f_i = theta^(-2i/rd):                                       */
+/*   x'[i]        = x[i] cos(p f_i) - x[i + rd/2] sin(p f_i)                  */
+/*   x'[i + rd/2] = x[i + rd/2] cos(p f_i) + x[i] sin(p f_i)                  */
+/* and dims rd .. d-1 pass through.                                          */
+static void rope_row(const uint16_t* x, double* out, int d, int rd, double p, double theta) {
+    int half = rd / 2;
+    for (int e = 0; e < d; ++e) out[e] = bf16_to_double(x[e]);
+    for (int i = 0; i < half; ++i) {
+        double f = pow(theta, -2.0 * i / rd);
+        double c = cos(p * f), sn = sin(p * f);
+        double a = bf16_to_double(x[i]), b = bf16_to_double(x[i + half]);
+        out[i] = a * c - b * sn;
+        out[i + half] = b * c + a * sn;
+    }
+}
+
+/* q [T][hq][d], k [T][hkv][d] (bf16 bits; either may be NULL) at positions
+ * [T] -> q_out, k_out (double, same shapes). */
+int oracle_rope(int hq, int hkv, int d, const uint16_t* q, const uint16_t* k, const int32_t* positions, int64_t T,
+                double theta, int rotary_dim, double* q_out, double* k_out) {
+    if (hq < 0 || hkv < 0 || d <= 0 || T < 0 || !positions || rotary_dim < 0 || rotary_dim > d || rotary_dim % 2 ||
+        !(theta > 0.0))
+        return ORACLE_EINVAL;
+    if ((q && !q_out) || (k && !k_out)) return ORACLE_EINVAL;
+    for (int64_t t = 0; t < T; ++t) {
+        if (positions[t] < 0) return ORACLE_EINVAL;
+        double p = (double)positions[t];
+        if (q)
+            for (int h = 0; h < hq; ++h)
+                rope_row(q + ((size_t)t * hq + h) * d, q_out + ((size_t)t * hq + h) * d, d, rotary_dim, p, theta);
+        if (k)
+            for (int h = 0; h < hkv; ++h)
+                rope_row(k + ((size_t)t * hkv + h) * d, k_out + ((size_t)t * hkv + h) * d, d, rotary_dim, p, theta);
+    }
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* FP8 GA cache (see the header): pool [N][Hkv][D] of E4M3 codes, position j */
 /* of sequence b at row kv_base[b] + j, one scale per KV head for K and V.   */
 

@@ -15,6 +15,10 @@ the oracle disagrees with:
   * for the backward pass: torch fp64 autograd through a dense brute force of
     the same attention (sink as an extra logit with no value), and the closed
     form of one-token sequences;
+  * for the rotary embedding: Transformers' own MiMo-V2-Flash rotate-half
+    application and default inverse frequencies (a library implementation of
+    the same convention), and the invariants of a rotation (norms, dependence
+    of q.k on the position difference only, identity at position 0);
   * for the FP8 (OCP E4M3) GA cache: the format's own table
     (tests/golden/ocp_e4m3.json) and torch's float8_e4m3fn conversions (a
     library implementation of the same format); FP8 decode equals bf16 decode
@@ -702,6 +706,63 @@ def pin_backward_rows_and_neg_inf_sink(orc):
         for a, b in zip(none[:3], ninf[:3]):
             assert np.array_equal(a, b), "sink -inf differs from no sink"
         assert not ninf[3].any()
+
+
+# -- rotary embedding ---------------------------------------------------------
+
+def _rope_inputs(T, seed):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn((T, 64, 192), generator=g).to(torch.bfloat16)
+    k = torch.randn((T, 4, 192), generator=g).to(torch.bfloat16)
+    return q, k
+
+
+def pin_rope_transformers_convention(orc):
+    """The oracle's rotation equals Transformers' MiMo-V2-Flash apply_rotary_pos_emb
+    (run in fp64) on cos/sin built from its default inverse frequencies, for
+    rotary dims 64 (the library's 0.334 factor) and 192 and both of its thetas."""
+    from types import SimpleNamespace
+    from transformers.models.mimo_v2_flash import modeling_mimo_v2_flash as mm
+    q, k = _rope_inputs(40, 70)
+    pos = np.array(list(range(20)) + [1000 + 37 * i for i in range(20)], np.int32)
+    for theta, factor in ((1e4, 0.334), (5e6, 0.334), (1e4, 1.0)):
+        cfg = SimpleNamespace(rope_parameters={"x": {"rope_theta": theta, "partial_rotary_factor": factor}},
+                              head_dim=192, hidden_size=4096, num_attention_heads=64)
+        inv, _ = mm.MiMoV2FlashRotaryEmbedding.compute_default_rope_parameters(cfg, "cpu", layer_type="x")
+        rd = 2 * inv.shape[0]
+        assert rd == int(192 * factor) // 2 * 2
+        ang = torch.from_numpy(pos.astype(np.float64))[:, None] * inv.to(torch.float64)[None, :]
+        emb = torch.cat([ang, ang], dim=-1)
+        cos, sin = emb.cos()[None], emb.sin()[None]  # [1, T, rd]
+        lq, lk = mm.apply_rotary_pos_emb(_f64(q).transpose(0, 1)[None], _f64(k).transpose(0, 1)[None], cos, sin)
+        oq, ok = orc.rope(_bits(q), _bits(k), pos, theta=theta, rotary_dim=rd)
+        # the library's inverse frequencies are fp32: angles agree to ~1e-7 relative
+        tol = 2e-7 * float(pos.max()) * 8 + 1e-12
+        _close(oq, lq[0].transpose(0, 1).numpy(), tol, f"rope q theta={theta} rd={rd}")
+        _close(ok, lk[0].transpose(0, 1).numpy(), tol, f"rope k theta={theta} rd={rd}")
+
+
+def pin_rope_rotation_invariants(orc):
+    """Rotation invariants: each head vector keeps its norm, dims past the rotary
+    dims are untouched, position 0 is the identity, and q.k depends only on the
+    difference of the two positions."""
+    q, k = _rope_inputs(6, 71)
+    qf, kf = _f64(q).numpy(), _f64(k).numpy()
+    pos = np.array([0, 5, 129, 4096, 70000, 262143], np.int32)
+    for rd in (64, 192):
+        oq, ok = orc.rope(_bits(q), _bits(k), pos, theta=1e4, rotary_dim=rd)
+        _close(np.linalg.norm(oq, axis=-1), np.linalg.norm(qf, axis=-1), 1e-12, "rope keeps norms")
+        assert np.array_equal(oq[:, :, rd:], qf[:, :, rd:]) and np.array_equal(ok[:, :, rd:], kf[:, :, rd:])
+        assert np.array_equal(oq[0], qf[0]) and np.array_equal(ok[0], kf[0]), "position 0 is the identity"
+        # same q and k vectors at positions (p, j) and (p + c, j + c)
+        qq = np.repeat(_bits(q)[1:2], 4, axis=0)
+        kk = np.repeat(_bits(k)[1:2], 4, axis=0)
+        rq, _ = orc.rope(qq, None, np.array([300, 1300, 60300, 300], np.int32), theta=1e4, rotary_dim=rd)
+        _, rk = orc.rope(None, kk, np.array([100, 1100, 60100, 299], np.int32), theta=1e4, rotary_dim=rd)
+        dots = np.einsum("thd,tgd->thg", rq, rk)
+        _close(dots[1], dots[0], 1e-9, "rope shift invariance")
+        _close(dots[2], dots[0], 1e-8, "rope shift invariance (far)")
+        assert np.abs(dots[3] - dots[0]).max() > 1e-3, "a different offset must change q.k"
 
 # -- FP8 (OCP E4M3) GA cache -------------------------------------------------
 

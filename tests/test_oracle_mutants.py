@@ -111,6 +111,11 @@ MUTANTS = {
     "backward D from the value instead of the output": (
         "                for (int e = 0; e < d->dv; ++e) D += bf16_to_double(dorow[e]) * o[e];\n",
         "                for (int e = 0; e < d->dv; ++e) D += bf16_to_double(dorow[e]) * o[e] / d->value_scale;\n"),
+    "rope pairs neighbours instead of halves": ("        double a = bf16_to_double(x[i]), b = bf16_to_double(x[i + half]);\n",
+                                                "        double a = bf16_to_double(x[i]), b = bf16_to_double(x[(i ^ 1)]);\n"),
+    "rope rotates the wrong way": ("        out[i] = a * c - b * sn;\n", "        out[i] = a * c + b * sn;\n"),
+    "rope frequencies over the head dim": ("        double f = pow(theta, -2.0 * i / rd);\n",
+                                           "        double f = pow(theta, -2.0 * i / d);\n"),
     "bf16 widened from the wrong half": ("    uint32_t w = ((uint32_t)bits) << 16;\n", "    uint32_t w = ((uint32_t)bits) << 15;\n"),
 }
 
