@@ -272,6 +272,22 @@ def backward_rows(dims, ga, swa, out_ga, lse_ga, out_swa, lse_swa, reps=3):
     return res
 
 
+def rope_rows(dims, ga, reps=5):
+    """Rotary embedding of the GA prefill input's q and k in place (1 x 32768
+    tokens, rotary dims 64 of 192, theta 5e6), timed apart from the step; bytes
+    are the rotated dims read and written."""
+    dev = "cuda"
+    q, k = ga.q.clone(), ga.k.clone()
+    pos = torch.arange(q.shape[0], dtype=torch.int32, device=dev)
+    call = lambda: B.mimo_rope_apply(dims, q, k, pos, q.shape[0], 5e6, 64)
+    ms = _time_ms(call, reps)
+    nbytes = q.shape[0] * (HQ + HKV) * 64 * 2 * 2
+    del q, k
+    torch.cuda.empty_cache()
+    return {"rope_qk": {"workload": "1 x 32768 tokens, q and k, rotary dims 64, theta 5e6", "ms": ms,
+                        "GB/s": nbytes / (ms * 1e-3) / 1e9, "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS}}
+
+
 def _time_ms(call, reps):
     call()
     torch.cuda.synchronize()
@@ -557,7 +573,8 @@ def main():
     if not args.no_next_rows:
         res["next_rows"] = {**chunk_rows(dims, ga, swa), **paged_rows(dims, dga, ctx_ga, max_ctx, ws, ga),
                             **fp8_rows(dims, dga, ctx_ga, max_ctx, ws),
-                            **backward_rows(dims, ga, swa, out_ga, lse_ga, out_swa, lse_swa)}
+                            **backward_rows(dims, ga, swa, out_ga, lse_ga, out_swa, lse_swa),
+                            **rope_rows(dims, ga)}
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample (cpu_baseline)")
         res["cpu_baseline"] = cpu_baseline(swa, ga, dga, ctx0, args.cpu_budget)

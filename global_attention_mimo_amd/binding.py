@@ -28,7 +28,8 @@ MIMO_ERR_HIP = 4
 ENTRY_POINTS = ("mimo_attn_prefill", "mimo_attn_prefill_chunk", "mimo_attn_decode_workspace_size",
                 "mimo_attn_decode", "mimo_kv_append", "mimo_kv_append_paged", "mimo_attn_decode_paged",
                 "mimo_attn_prefill_chunk_paged", "mimo_kv_append_fp8", "mimo_attn_decode_fp8",
-                "mimo_attn_prefill_backward_workspace_size", "mimo_attn_prefill_backward", "mimo_status_string",
+                "mimo_attn_prefill_backward_workspace_size", "mimo_attn_prefill_backward", "mimo_rope_apply",
+                "mimo_status_string",
                 "mimo_last_error", "mimo_abi_version")
 
 
@@ -95,6 +96,8 @@ def lib() -> ctypes.CDLL:
         L.mimo_attn_prefill_backward.restype = ctypes.c_int
         L.mimo_attn_prefill_backward.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
                                                  _P, _P, _P, _P, _P, _P, _SZ, _P]
+        L.mimo_rope_apply.restype = ctypes.c_int
+        L.mimo_rope_apply.argtypes = [dims_p, _P, _P, _P, _I32, ctypes.c_float, _I32, _P]
         L.mimo_status_string.restype = ctypes.c_char_p
         L.mimo_status_string.argtypes = [ctypes.c_int]
         L.mimo_last_error.restype = ctypes.c_char_p
@@ -242,6 +245,12 @@ def mimo_attn_prefill_backward(dims: mimo_attn_dims, layer_type: int, q, k, v, o
                                             _ptr(workspace), ws_bytes, _stream(stream)))
 
 
+def mimo_rope_apply(dims: mimo_attn_dims, q, k, positions, total_tokens: int, rope_theta: float, rotary_dim: int,
+                    stream=None) -> None:
+    _check(lib().mimo_rope_apply(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(positions), total_tokens, rope_theta,
+                                 rotary_dim, _stream(stream)))
+
+
 # -- tensor-level conveniences (allocation of outputs + the calls above) -------
 
 def prefill(q, k, v, cu_seqlens, max_seqlen: int, layer_type: int, sink=None, dims=None, out=None, lse=None,
@@ -375,3 +384,10 @@ def prefill_backward(q, k, v, out, lse, dout, cu_seqlens, max_seqlen: int, layer
     mimo_attn_prefill_backward(dims, layer_type, q, k, v, out, lse, dout, cu_seqlens, cu_seqlens.numel() - 1,
                                max_seqlen, T, sink, dq, dk, dv, dsink, ws, stream)
     return dq, dk, dv, dsink
+
+
+def rope_apply(q, k, positions, rope_theta: float, rotary_dim: int, dims=None, stream=None):
+    """Rotates q and/or k in place at the tokens' positions."""
+    dims = dims or make_dims()
+    T = (q if q is not None else k).shape[0]
+    mimo_rope_apply(dims, q, k, positions, T, rope_theta, rotary_dim, stream)

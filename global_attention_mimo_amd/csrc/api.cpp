@@ -390,6 +390,24 @@ int mimo_attn_prefill_backward(const mimo_attn_dims* dims, int layer_type, const
     return hip_status(mimo::launch_prefill_backward(a, stream), "backward launch");
 }
 
+int mimo_rope_apply(const mimo_attn_dims* dims, uint16_t* q, uint16_t* k, const int32_t* positions,
+                    int32_t total_tokens, float rope_theta, int32_t rotary_dim, hipStream_t stream) {
+    if (int st = check_dims(dims, MIMO_LAYER_GA, 1)) return st;
+    if (!q && !k) return fail(MIMO_ERR_INVALID_ARG, "q and k are both NULL");
+    if (!positions) return fail(MIMO_ERR_INVALID_ARG, "positions must be non-NULL");
+    if ((q && !aligned16(q)) || (k && !aligned16(k))) return fail(MIMO_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
+    if (total_tokens < 0) return fail(MIMO_ERR_INVALID_ARG, "total_tokens %d is negative", total_tokens);
+    if (!std::isfinite(rope_theta) || !(rope_theta > 1.0f))
+        return fail(MIMO_ERR_INVALID_ARG, "rope_theta must be finite and above 1");
+    if (rotary_dim < 0 || rotary_dim > dims->head_dim_qk)
+        return fail(MIMO_ERR_INVALID_ARG, "rotary_dim %d outside [0, %d]", rotary_dim, dims->head_dim_qk);
+    if (rotary_dim % 16) return fail(MIMO_ERR_UNSUPPORTED, "rotary_dim %d is not a multiple of 16", rotary_dim);
+    if (total_tokens == 0 || rotary_dim == 0) return ok();
+    mimo::RopeArgs a{q, k, positions, total_tokens, dims->num_q_heads, dims->num_kv_heads, rotary_dim,
+                     (double)rope_theta};
+    return hip_status(mimo::launch_rope(a, stream), "rope launch");
+}
+
 const char* mimo_status_string(int status) {
     switch (status) {
         case MIMO_OK: return "MIMO_OK";

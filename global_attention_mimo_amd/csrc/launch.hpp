@@ -111,4 +111,13 @@ struct BackwardArgs {
 inline size_t backward_workspace_bytes(int total_tokens, int hq) { return (size_t)total_tokens * hq * sizeof(float); }
 hipError_t launch_prefill_backward(const BackwardArgs& a, hipStream_t stream);
 
+struct RopeArgs {
+    uint16_t* q;
+    uint16_t* k;
+    const int32_t* positions;
+    int total_tokens, hq, hkv, rotary_dim;
+    double theta;
+};
+hipError_t launch_rope(const RopeArgs& a, hipStream_t stream);
+
 }  // namespace mimo

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MIMO_ATTN_ABI_VERSION 5
+#define MIMO_ATTN_ABI_VERSION 6
 
 /* Layer type: which key set a query sees (model doc, Key features; config
  * layer_types). */
@@ -360,6 +360,26 @@ int mimo_attn_prefill_backward(const mimo_attn_dims* dims, int layer_type,
                                int32_t total_tokens, const float* sink,
                                uint16_t* dq, uint16_t* dk, uint16_t* dv, float* dsink,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Rotary position embedding of queries and keys, in place, before attention
+ * and append (model doc, MiMoV2FlashConfig: rope_parameters with rope_theta,
+ * the Transformers rotary convention; the pages give neither theta nor how
+ * many dims rotate, so both come from the caller).  For a head vector x of the
+ * token at position p, the first rd = rotary_dim dims rotate in pairs
+ * (i, i + rd/2), i < rd/2, by the angle p * theta^(-2i/rd):
+ *   x[i] <- x[i] cos - x[i + rd/2] sin,  x[i + rd/2] <- x[i + rd/2] cos + x[i] sin
+ * and the other dims are left as they are.
+ *
+ *   q, k         [T][Hq][192] and [T][Hkv][192] bf16, rotated in place (either
+ *                may be NULL, not both).  Results round to nearest even.
+ *   positions    [T] int32 (device): position of each token (prefill: 0..L-1
+ *                per sequence; a chunk: ctx_lens[b] + i; decode: ctx_lens[b]).
+ *   rope_theta   > 1 (host); rotary_dim in [0, 192], a multiple of 16 (host;
+ *                0 does nothing).  Angles are formed in fp64.
+ */
+int mimo_rope_apply(const mimo_attn_dims* dims, uint16_t* q, uint16_t* k, const int32_t* positions,
+                    int32_t total_tokens, float rope_theta, int32_t rotary_dim, hipStream_t stream);
 
 /* Static English name of a status code ("MIMO_OK", ...). */
 const char* mimo_status_string(int status);

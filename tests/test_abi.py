@@ -42,7 +42,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_version_and_status_strings(L):
-    assert B.mimo_abi_version() == 5
+    assert B.mimo_abi_version() == 6
     assert B.mimo_status_string(0) == "MIMO_OK"
     assert B.mimo_status_string(3) == "MIMO_ERR_WORKSPACE"
     assert B.mimo_status_string(99) == "MIMO_ERR_UNKNOWN"
@@ -343,6 +343,33 @@ def test_backward_empty_and_workspace_size(L):
     assert bwd_call(L, total=0, ws=None) == B.MIMO_OK
     assert B.mimo_attn_prefill_backward_workspace_size(B.make_dims(), 1000) == 1000 * 64 * 4
     assert B.mimo_attn_prefill_backward_workspace_size(B.make_dims(head_dim_v=64), 1000) == 0
+
+
+def rope_call(L, q=FAKE, k=FAKE, pos=FAKE, total=8, theta=1e4, rd=64, dims=None):
+    d = dims or B.make_dims()
+    return L.mimo_rope_apply(ctypes.byref(d), q, k, pos, total, theta, rd, None)
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(q=None, k=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(pos=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(q=FAKE_ODD), B.MIMO_ERR_INVALID_ARG),
+    (dict(total=-1), B.MIMO_ERR_INVALID_ARG),
+    (dict(theta=1.0), B.MIMO_ERR_INVALID_ARG),
+    (dict(theta=float("inf")), B.MIMO_ERR_INVALID_ARG),
+    (dict(rd=-16), B.MIMO_ERR_INVALID_ARG),
+    (dict(rd=208), B.MIMO_ERR_INVALID_ARG),
+    (dict(rd=24), B.MIMO_ERR_UNSUPPORTED),
+    (dict(dims=B.make_dims(head_dim_qk=128)), B.MIMO_ERR_UNSUPPORTED),
+])
+def test_rope_rejects(L, case, status):
+    assert rope_call(L, **case) == status
+    assert B.mimo_last_error() != ""
+
+
+def test_rope_nothing_to_do_is_ok(L):
+    assert rope_call(L, total=0) == B.MIMO_OK
+    assert rope_call(L, rd=0) == B.MIMO_OK
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
