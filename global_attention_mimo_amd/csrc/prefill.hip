@@ -177,8 +177,8 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     // Global -> register staging of one K/V tile.  Each thread always moves the
     // same (row, 16-byte column) slots of a tile, so its source pointers are
     // fixed up to the tile's key offset.  Keys past the sequence end are
-    // clamped to its last key: they are masked (key > every query position),
-    // so they only need to be finite.
+    // masked (key > every query position), so they only need to be finite:
+    // chunk rows are clamped to the last key, contiguous rows read as zeros.
     const uint16_t* kp[Cfg::kKPer];
     const uint16_t* vp[Cfg::kVPer];
     int krow_of[Cfg::kKPer], vrow_of[Cfg::kVPer];
@@ -195,6 +195,19 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         vp[i] = v + ((size_t)s0 * hkv + g) * kDv + (c % (kDv / 8)) * 8;
     }
     const size_t kstride = (size_t)hkv * kDqk, vstride = (size_t)hkv * kDv;
+    // Byte offsets of this thread's slots inside a tile (contiguous K/V).
+    const uint32_t kRowBytesK = (uint32_t)kstride * 2, kRowBytesV = (uint32_t)vstride * 2;
+    uint32_t koff[Cfg::kKPer], voff[Cfg::kVPer];
+#pragma unroll
+    for (int i = 0; i < Cfg::kKPer; ++i) {
+        const int c = min(tid + Cfg::kThreads * i, Cfg::kKChunks - 1);
+        koff[i] = (uint32_t)krow_of[i] * kRowBytesK + (c % (kDqk / 8)) * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < Cfg::kVPer; ++i) {
+        const int c = min(tid + Cfg::kThreads * i, Cfg::kVChunks - 1);
+        voff[i] = (uint32_t)vrow_of[i] * kRowBytesV + (c % (kDv / 8)) * 16;
+    }
     // Cache sources (CHUNK only): same per-thread columns, rows by position.
     const uint16_t* kcp[Cfg::kKPer];
     const uint16_t* vcp[Cfg::kVPer];
@@ -260,20 +273,19 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 #pragma unroll
             for (int i = 0; i < Cfg::kVPer; ++i)
                 vreg[i] = *reinterpret_cast<const u32x4*>(src_row(vcp[i], vp[i], vstride, kbase + vrow_of[i]));
-        } else if (kbase + NK <= L) {
-#pragma unroll
-            for (int i = 0; i < Cfg::kKPer; ++i)
-                kreg[i] = *reinterpret_cast<const u32x4*>(kp[i] + (size_t)(kbase + krow_of[i]) * kstride);
-#pragma unroll
-            for (int i = 0; i < Cfg::kVPer; ++i)
-                vreg[i] = *reinterpret_cast<const u32x4*>(vp[i] + (size_t)(kbase + vrow_of[i]) * vstride);
         } else {
+            // The tile's rows through the descriptor: its base and record count
+            // (the rows up to the sequence end) are wave-uniform scalars, the
+            // per-thread byte offsets fixed, so staging costs no vector address
+            // arithmetic.  Rows past the end read as zeros: such keys are masked
+            // and their zero values meet zero probabilities.
+            const uint32_t rows = (uint32_t)min(L - kbase, NK);
+            const rsrc_t kr = make_rsrc(k + ((size_t)(s0 + kbase) * hkv + g) * kDqk, rows * kRowBytesK);
+            const rsrc_t vr = make_rsrc(v + ((size_t)(s0 + kbase) * hkv + g) * kDv, rows * kRowBytesV);
 #pragma unroll
-            for (int i = 0; i < Cfg::kKPer; ++i)
-                kreg[i] = *reinterpret_cast<const u32x4*>(kp[i] + (size_t)min(kbase + krow_of[i], L - 1) * kstride);
+            for (int i = 0; i < Cfg::kKPer; ++i) kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, koff[i], 0, 0);
 #pragma unroll
-            for (int i = 0; i < Cfg::kVPer; ++i)
-                vreg[i] = *reinterpret_cast<const u32x4*>(vp[i] + (size_t)min(kbase + vrow_of[i], L - 1) * vstride);
+            for (int i = 0; i < Cfg::kVPer; ++i) vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, voff[i], 0, 0);
         }
     };
     auto store_tile = [&](int buf) {
