@@ -288,6 +288,95 @@ def rope_rows(dims, ga, reps=5):
                         "GB/s": nbytes / (ms * 1e-3) / 1e9, "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS}}
 
 
+def hybrid_rows(dims, decode_steps=64):
+    """The 48-layer hybrid stack (5 SWA : 1 GA), timed end to end: 32 prompts with
+    lengths log-uniform in [512, 32768] (seed 0), a varlen prefill of every layer
+    (attention + KV append), then `decode_steps` decode steps of all 48 layers
+    (attend + append per layer).  There are no weights, so each layer's q/k/v are
+    fresh seeded N(0,1) tensors in reused buffers, generated outside the timed
+    calls; the sinks are per-layer N(0,1).  Times are HIP-event GPU time of the
+    library calls only."""
+    from global_attention_mimo_amd.stack import HybridStack, GA as L_GA
+    dev = "cuda"
+    lengths = synth.hybrid_prompt_lengths(32, seed=0)
+    st = HybridStack(lengths, decode_steps=decode_steps, device=dev)
+    gen = torch.Generator(device=dev).manual_seed(0)
+    sinks = torch.randn((st.num_layers, HQ), generator=gen, device=dev)
+    out = torch.empty((st.total, HQ, DV), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((st.total, HQ), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    per_layer = []
+    for layer in range(st.num_layers):
+        x = synth.prefill_inputs(lengths, seed=1000 + layer, device=dev, with_sink=False)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        st.prefill_layer(layer, x.q, x.k, x.v, sinks[layer], out, lse, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per_layer.append(e0.elapsed_time(e1))
+        del x
+    lt = st.layer_types
+    ga_ms = sum(t for t, l in zip(per_layer, lt) if l == L_GA)
+    swa_ms = sum(t for t, l in zip(per_layer, lt) if l != L_GA)
+    n_ga = sum(1 for l in lt if l == L_GA)
+    f_ga = prefill_pairs(lengths, 1) * HQ * FLOP_PER_TRIPLE * n_ga
+    f_swa = prefill_pairs(lengths, 0) * HQ * FLOP_PER_TRIPLE * (len(lt) - n_ga)
+    b_swa = st.total * TOKEN_BYTES * (len(lt) - n_ga)
+    pre_ms = ga_ms + swa_ms
+    # Decode: every step draws all layers' q / k_new / v_new into static buffers
+    # first, then runs the 48 layers; the first half of the steps are issued call
+    # by call, the second half replay one HIP graph of the step.
+    Lyr, Bd = st.num_layers, st.batch
+    q = torch.empty((Lyr, Bd, HQ, DQK), dtype=torch.bfloat16, device=dev)
+    kn = torch.empty((Lyr, Bd, HKV, DQK), dtype=torch.bfloat16, device=dev)
+    vn = torch.empty((Lyr, Bd, HKV, DV), dtype=torch.bfloat16, device=dev)
+    dout = torch.empty((Lyr, Bd, HQ, DV), dtype=torch.bfloat16, device=dev)
+    dlse = torch.empty((Lyr, Bd, HQ), dtype=torch.float32, device=dev)
+
+    def draw():
+        q.copy_(torch.randn(q.shape, generator=gen, device=dev))
+        kn.copy_(torch.randn(kn.shape, generator=gen, device=dev))
+        vn.copy_(torch.randn(vn.shape, generator=gen, device=dev))
+
+    eager_ms, graph_ms, graph = [], [], None
+    for step in range(decode_steps):
+        draw()
+        if step == decode_steps // 2:
+            graph = st.capture_decode_step(q, kn, vn, sinks, dout, dlse)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        if graph is None:
+            st.decode_step(q, kn, vn, sinks, dout, dlse, stream)
+        else:
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        (eager_ms if graph is None else graph_ms).append(
+            (e0.elapsed_time(e1), (time.perf_counter() - t0) * 1e3))
+    kvb = st.kv_bytes()
+    del st, out, lse, dout, dlse, graph
+    torch.cuda.empty_cache()
+    dec_ms = float(np.mean([g for g, _ in graph_ms]))
+    eager_gpu = float(np.mean([g for g, _ in eager_ms]))
+    eager_wall = float(np.mean([w for _, w in eager_ms]))
+    return {"hybrid_stack": {
+        "workload": f"48 layers (5 SWA : 1 GA), 32 prompts log-uniform in [512, 32768] ({sum(lengths)} tokens), "
+                    f"prefill then {decode_steps} decode steps; attention + KV append per layer",
+        "prefill_ms": pre_ms, "prefill_tokens/s": sum(lengths) / (pre_ms * 1e-3),
+        "prefill_TFLOP/s": (f_ga + f_swa) / (pre_ms * 1e-3) / 1e12,
+        "prefill_ga_layers_ms": ga_ms, "prefill_ga_TFLOP/s": f_ga / (ga_ms * 1e-3) / 1e12,
+        "prefill_ga_frac_mfma_peak": f_ga / (ga_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "prefill_swa_layers_ms": swa_ms, "prefill_swa_GB/s": b_swa / (swa_ms * 1e-3) / 1e9,
+        "prefill_swa_frac_hbm_peak": b_swa / (swa_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "decode_step_ms": dec_ms, "decode_tokens/s": Bd / (dec_ms * 1e-3),
+        "decode_step_note": f"HIP-graph replay of the whole step (96 library calls + context advance), mean of "
+                            f"{len(graph_ms)} steps; the first {len(eager_ms)} steps issued call by call took "
+                            f"{eager_gpu:.3f} ms on the GPU clock and {eager_wall:.3f} ms host wall time",
+        "kv_cache_bytes": kvb["hybrid"], "kv_cache_bytes_all_ga": kvb["all_ga"]}}
+
+
 def _time_ms(call, reps):
     call()
     torch.cuda.synchronize()
@@ -410,7 +499,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next-rows", action="store_true",
-                    help="skip the rows timed apart from the step (chunked prefill, paged and FP8 pools)")
+                    help="skip the rows timed apart from the step (chunked prefill, paged and FP8 pools, "
+                         "backward, RoPE, the 48-layer hybrid stack)")
     ap.add_argument("--split", type=int, default=0, help="GA decode split (keys per workgroup), 0 = default")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device copy (a known-size reference for HBM byte counters)")
@@ -575,6 +665,8 @@ def main():
                             **fp8_rows(dims, dga, ctx_ga, max_ctx, ws),
                             **backward_rows(dims, ga, swa, out_ga, lse_ga, out_swa, lse_swa),
                             **rope_rows(dims, ga)}
+        log("hybrid stack: 48-layer prefill and decode")
+        res["hybrid_stack"] = hybrid_rows(dims)["hybrid_stack"]
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample (cpu_baseline)")
         res["cpu_baseline"] = cpu_baseline(swa, ga, dga, ctx0, args.cpu_budget)

@@ -105,6 +105,27 @@ class HybridStack:
         """All layers of a decode step are done: every sequence is one token longer."""
         self.ctx.add_(1)
 
+    def decode_step(self, q, k_new, v_new, sinks, out, lse=None, stream=None):
+        """One decode step of every layer (inputs and outputs indexed by layer first),
+        then the context advance, all on one stream."""
+        for layer in range(self.num_layers):
+            self.decode_layer(layer, q[layer], k_new[layer], v_new[layer], sinks[layer], out[layer],
+                              None if lse is None else lse[layer], stream)
+        self.advance()
+
+    def capture_decode_step(self, q, k_new, v_new, sinks, out, lse=None) -> torch.cuda.CUDAGraph:
+        """A HIP graph of `decode_step` over these buffers.  Each replay runs one step
+        at the contexts the device holds then (they live in device memory, as do the
+        cache positions the appends write) and advances them; replays read whatever
+        q / k_new / v_new hold at that time.  The library only launches kernels on
+        the stream it is given (no allocation, memset or synchronisation), so the
+        step is captured as it is; the context advance is a torch kernel."""
+        graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            self.decode_step(q, k_new, v_new, sinks, out, lse)
+        return graph
+
     def kv_bytes(self) -> dict:
         """KV-cache bytes actually allocated, and what an all-GA stack would need."""
         per_tok = self.hkv * (synth.DQK + synth.DV) * 2
