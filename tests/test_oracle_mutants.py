@@ -2,13 +2,15 @@
 
 Each case plants one plausible mistake (a dropped term, a wrong sign, index or
 bound, a transposed operand) in a private copy of ``oracle/mimo_oracle.c``,
-builds it with gcc into a temporary directory, runs every pin of
-``oracle_pins`` against that build in a subprocess, and requires at least one
-pin to fail.  The planted source never leaves the temporary directory.
+builds it with gcc into a temporary directory, runs the pins of
+``oracle_pins`` against that build in a subprocess until one fails, and
+requires that one does.  The planted source never leaves the temporary
+directory.  The mutants are checked in parallel, a few processes at a time.
 """
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import pytest
 
@@ -120,20 +122,39 @@ MUTANTS = {
 }
 
 
-@pytest.mark.parametrize("name", sorted(MUTANTS))
-def test_pins_catch_mutant(name, tmp_path):
+def _run_mutant(name, workdir):
+    """Build the oracle with one planted mistake and run the pins against it until
+    one fails.  Returns (caught, report)."""
     old, new = MUTANTS[name]
     src = open(oracle.SOURCE).read()
-    assert src.count(old) == 1, f"mutation site for '{name}' not found exactly once"
-    mpath = tmp_path / "mutant.c"
-    mpath.write_text(src.replace(old, new))
-    lib = str(tmp_path / "libmutant.so")
-    oracle.build(str(mpath), lib)
+    if src.count(old) != 1:
+        return False, f"mutation site for '{name}' not found exactly once"
+    mpath = os.path.join(workdir, "mutant.c")
+    with open(mpath, "w") as f:
+        f.write(src.replace(old, new))
+    lib = os.path.join(workdir, "libmutant.so")
+    oracle.build(mpath, lib)
     env = dict(os.environ, OMP_NUM_THREADS="2")
-    res = subprocess.run([sys.executable, os.path.join(HERE, "oracle_pins.py"), lib],
+    res = subprocess.run([sys.executable, os.path.join(HERE, "oracle_pins.py"), lib, "--first"],
                          capture_output=True, text=True, timeout=600, env=env)
     lines = [l for l in res.stdout.splitlines() if l.startswith("FAILED:")]
     # A crash of the planted build also counts as caught, but only a clean run
-    # that names failing pins tells which pin caught it.
-    caught = (res.returncode != 0) or (lines and lines[-1] != "FAILED:")
-    assert caught, f"no pin caught mutant '{name}'\n{res.stdout[-2000:]}\n{res.stderr[-2000:]}"
+    # that names a failing pin tells which pin caught it.
+    caught = (res.returncode != 0) or bool(lines and lines[-1] != "FAILED:")
+    return caught, f"{res.stdout[-2000:]}\n{res.stderr[-2000:]}"
+
+
+@pytest.fixture(scope="module")
+def mutant_results(tmp_path_factory):
+    """Every mutant, built and checked in parallel (each check is its own process)."""
+    workers = max(1, min(4, (os.cpu_count() or 2) // 2))
+    dirs = {name: str(tmp_path_factory.mktemp("mutant")) for name in MUTANTS}
+    with ThreadPoolExecutor(workers) as pool:
+        futures = {name: pool.submit(_run_mutant, name, dirs[name]) for name in MUTANTS}
+        return {name: f.result() for name, f in futures.items()}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, mutant_results):
+    caught, report = mutant_results[name]
+    assert caught, f"no pin caught mutant '{name}'\n{report}"
