@@ -28,10 +28,9 @@
 //                      (A 32x32x16 form with 32 keys per wave needs ~390
 //                      registers, i.e. one wave per SIMD, and ran 1.4x slower.)
 //   bwd_sink_kernel    dsink per head, a fixed-order block reduction.
-// LDS tiles: the dq kernel uses the forward's padded row strides (192 + 8 and
-// 128 + 32 bf16) and its transposed-read pattern; the dk/dv kernel uses
-// unpadded rows with the 16-byte chunks of row r XOR-swizzled by 2(r % 4),
-// the layout the decode kernel reads V^T from.
+// LDS tiles are laid out so that neither kernel's reads meet bank conflicts:
+// padded rows, and for the dq K tile a permuted row order within 16-row blocks
+// (dq_key_row); the dk/dv tiles keep row order at a different pitch.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -41,18 +40,23 @@ namespace {
 constexpr int kDqk = 192;
 constexpr int kDv = 128;
 constexpr int kGroup = 16;
-constexpr int kQRow = kDqk * 2;  // bytes of a staged Q or K row
-constexpr int kVRow = kDv * 2;   // bytes of a staged dO or V row
+// dk/dv LDS tiles of 32 query rows, in row order, padded to 416 bytes (Q)
+// and 288 bytes (dO): a row pitch of 2 mod 4 16-byte chunks is what keeps both
+// of this kernel's read patterns free of bank conflicts on gfx950, the 16-byte
+// row reads (lanes 16i..16i+15 on 16 consecutive rows, chunk i) and the
+// transposed reads below (measured with SQ_LDS_BANK_CONFLICT over pitches of
+// 256..528 bytes: odd-chunk pitches halve the row-read rate, multiples of 4
+// chunks cost 2-8x).
+constexpr int kQRow = kDqk * 2 + 32;  // bytes per staged Q row
+constexpr int kVRow = kDv * 2 + 32;   // bytes per staged dO row
 
-__device__ __forceinline__ int swz(int r, int c) { return c ^ (2 * (r & 3)); }
-
-// 8 bf16 of tile row r, logical 16-byte chunk c (a direct MFMA operand).
+// 8 bf16 of tile row r, 16-byte chunk c (a direct MFMA operand).
 __device__ __forceinline__ bf16x8 lds_row8(const char* tile, int row_bytes, int r, int c) {
-    return *reinterpret_cast<const bf16x8*>(tile + r * row_bytes + swz(r, c) * 16);
+    return *reinterpret_cast<const bf16x8*>(tile + r * row_bytes + c * 16);
 }
 
 __device__ __forceinline__ void lds_put16(char* tile, int row_bytes, int r, int c, const u32x4& x) {
-    *reinterpret_cast<u32x4*>(tile + r * row_bytes + swz(r, c) * 16) = x;
+    *reinterpret_cast<u32x4*>(tile + r * row_bytes + c * 16) = x;
 }
 
 // Transposed A operand over tile rows 0..31, columns 16db .. 16db+15: lane l
@@ -61,7 +65,7 @@ __device__ __forceinline__ void lds_put16(char* tile, int row_bytes, int r, int 
 // two 16-row accumulator blocks (rows 4G+r of block 0, then of block 1).
 __device__ __forceinline__ bf16x8 lds_tr8(const char* tile, int row_bytes, int db, int lane) {
     const int G = lane >> 4, tq = (lane & 15) >> 2;
-    const char* p = tile + (4 * G + tq) * row_bytes + 32 * (db ^ tq) + 8 * (lane & 3);
+    const char* p = tile + (4 * G + tq) * row_bytes + 32 * db + 8 * (lane & 3);
     return join_tr(lds_read_tr16(reinterpret_cast<const uint16_t*>(p)),
                    lds_read_tr16(reinterpret_cast<const uint16_t*>(p + 16 * row_bytes)));
 }
@@ -123,13 +127,21 @@ __global__ __launch_bounds__(256) void bwd_sink_kernel(const float* __restrict__
 // 32 query rows (2 tokens x 16 heads of a KV group, lane row r32 = lane % 32,
 // hh = lane / 32 the half of the MFMA K dimension it feeds), so every 16-byte
 // operand read from LDS feeds 32 x 32 x 16 MACs.  K and V tiles (32 keys) sit
-// in LDS with the forward's padded row strides.
+// in LDS with padded rows, K's in the order dq_key_row().
 constexpr int kDqTok = 16;           // tokens per workgroup (8 waves x 2)
 constexpr int kDqNK = 32;            // keys per staged tile
-constexpr int kKS = kDqk + 8;        // LDS row strides (bf16 elements)
-constexpr int kVS = kDv + 32;
+constexpr int kKS = kDqk + 8;        // LDS row strides (bf16 elements): 25 and 17 chunks
+constexpr int kVS = kDv + 8;
 constexpr int kDqLdsK = kDqNK * kKS;
 constexpr int kDqLdsV = kDqNK * kVS;
+
+// LDS row of key j of a dq K tile: within each 16-row block, j goes to
+// 4(j % 4) + j / 4, so the transposed K^T reads (keys 4hh + t, t = 0..3, in one
+// 32-lane phase) take rows 4 apart.  At the 400-byte pitch this order keeps
+// both the K^T reads and the direct key-row reads free of bank conflicts on
+// gfx950 (SQ_LDS_BANK_CONFLICT zero; in key order, with 320-byte V rows, the
+// kernel lost about half its LDS cycles to conflicts).
+__device__ __forceinline__ int dq_key_row(int j) { return (j & ~15) | ((j & 3) << 2) | ((j >> 2) & 3); }
 
 template <bool SWA>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(
@@ -193,17 +205,19 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_pe
             const int c = tid + 512 * i;
             if (c >= kChunks) continue;
             if (c < kKChunks)
-                *reinterpret_cast<u32x4*>(lds_k + buf * kDqLdsK + (c / (kDqk / 8)) * kKS + (c % (kDqk / 8)) * 8) = reg[i];
+                *reinterpret_cast<u32x4*>(lds_k + buf * kDqLdsK + dq_key_row(c / (kDqk / 8)) * kKS +
+                                          (c % (kDqk / 8)) * 8) = reg[i];
             else
                 *reinterpret_cast<u32x4*>(lds_v + buf * kDqLdsV + ((c - kKChunks) / (kDv / 8)) * kVS +
                                           ((c - kKChunks) % (kDv / 8)) * 8) = reg[i];
         }
     };
-    // Direct A operands: key row r32, d = 16s + 8hh.  Transposed K^T reads
-    // (the forward's V^T pattern): rows 4hh + (lane%16)/4 (+8) of a 16-key step,
-    // columns 16((lane/16)%2) + 4(lane%4) of a 32-wide d block.
-    const int kdir = r32 * kKS + 8 * hh, vdir = r32 * kVS + 8 * hh;
-    const int ktr = (4 * hh + ((lane & 15) >> 2)) * kKS + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    // Direct A operands: key r32, d = 16s + 8hh.  Transposed K^T reads (the
+    // forward's V^T pattern): keys 4hh + (lane%16)/4 (+8) of a 16-key step, i.e.
+    // LDS rows 4((lane%16)/4) + hh (+2), columns 16((lane/16)%2) + 4(lane%4) of
+    // a 32-wide d block.
+    const int kdir = dq_key_row(r32) * kKS + 8 * hh, vdir = r32 * kVS + 8 * hh;
+    const int ktr = (4 * ((lane & 15) >> 2) + hh) * kKS + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     load_tile(kt_begin);
     store_tile(0);
     __syncthreads();
@@ -239,8 +253,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_pe
         for (int db = 0; db < kDqk / 32; ++db) {
             const uint16_t* p0 = ktile + ktr + db * 32;
             const uint16_t* p1 = p0 + 16 * kKS;
-            dqa[db] = mfma_32x32x16(join_tr(lds_read_tr16(p0), lds_read_tr16(p0 + 8 * kKS)), dsf0, dqa[db]);
-            dqa[db] = mfma_32x32x16(join_tr(lds_read_tr16(p1), lds_read_tr16(p1 + 8 * kKS)), dsf1, dqa[db]);
+            dqa[db] = mfma_32x32x16(join_tr(lds_read_tr16(p0), lds_read_tr16(p0 + 2 * kKS)), dsf0, dqa[db]);
+            dqa[db] = mfma_32x32x16(join_tr(lds_read_tr16(p1), lds_read_tr16(p1 + 2 * kKS)), dsf1, dqa[db]);
         }
         if (more) store_tile(buf ^ 1);
         __syncthreads();
