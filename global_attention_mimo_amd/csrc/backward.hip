@@ -315,56 +315,66 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void bwd_dkdv_
     const int q_end = SWA ? min(L, k0 + kKvKeys - 1 + window) : L;
     const int nblk = (q_end - k0 + kKvTok - 1) / kKvTok;
 
-    // Staging: 32 Q rows (24 chunks), 32 dO rows (16 chunks); row 16i + hh is
-    // token q0 + i, head 16g + hh.  Threads 0..31 also fetch lse2 and D.
-    constexpr int kQChunks = kKvRows * (kDqk / 8), kChunks = kQChunks + kKvRows * (kDv / 8);
-    constexpr int kPer = (kChunks + 511) / 512;
-    u32x4 reg[kPer];
-    float st_lse = 0.0f, st_d = 0.0f;
-    auto load_blk = [&](int q0) {
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int c = min(tid + 512 * i, kChunks - 1);
-            const bool isq = c < kQChunks;
-            const int cc = isq ? c : c - kQChunks;
-            const int row = isq ? cc / (kDqk / 8) : cc / (kDv / 8);
-            const int ch = isq ? cc % (kDqk / 8) : cc % (kDv / 8);
-            const int tok = min(q0 + row / kGroup, L - 1);  // past the end: masked
-            const size_t r = (size_t)(s0 + tok) * hq + g * kGroup + row % kGroup;
-            reg[i] = isq ? reinterpret_cast<const u32x4*>(q + r * kDqk)[ch]
-                         : reinterpret_cast<const u32x4*>(dout + r * kDv)[ch];
-        }
-        if (tid < kKvRows) {
-            const int tok = min(q0 + tid / kGroup, L - 1);
-            const size_t r = (size_t)(s0 + tok) * hq + g * kGroup + tid % kGroup;
-            st_lse = lse[r] * kLog2e;
-            st_d = Dws[r];
-        }
+    // Staging of a block of 2 tokens x 16 heads: 32 Q rows (768 16-byte
+    // chunks), 32 dO rows (512 chunks), and the 32 rows' lse2 and D.  Row 16t +
+    // h is token q0 + t, head 16g + h.  Chunk owners are fixed per thread and
+    // uniform per wave: Q chunk tid (all waves), Q chunk 512 + tid (waves 0-3),
+    // dO chunk tid - 256 (waves 4-7), dO chunk 256 + tid (waves 0-3).  Loads go
+    // through descriptors whose base is the block's first row and whose record
+    // count ends at the sequence end, so rows past it read as zeros (their
+    // probabilities are forced to zero) and no per-block address arithmetic is
+    // vector work.  Blocks are loaded two ahead, alternating two register sets.
+    constexpr int kQChunks = kKvRows * (kDqk / 8);
+    const bool lo_waves = wave < 4;
+    const int qc1 = 512 + tid, oc0 = tid - 256, oc1 = 256 + tid;
+    auto q_off = [&](int qc) {
+        const int row = qc / (kDqk / 8);
+        return (uint32_t)(((row / kGroup) * hq + row % kGroup) * (kDqk * 2) + (qc % (kDqk / 8)) * 16);
     };
-    auto store_blk = [&](int buf) {
+    auto o_off = [&](int oc) {
+        const int row = oc / (kDv / 8);
+        return (uint32_t)(((row / kGroup) * hq + row % kGroup) * (kDv * 2) + (oc % (kDv / 8)) * 16);
+    };
+    const uint32_t off0 = q_off(tid);
+    const uint32_t off1 = lo_waves ? q_off(qc1) : o_off(oc0);
+    const uint32_t off2 = lo_waves ? o_off(oc1) : 0u;
+    const uint32_t off_s = (uint32_t)(((tid & 31) / kGroup) * hq + (tid & 31) % kGroup) * 4;
+    struct Stage {
+        u32x4 r[3];
+        float lse2, d;
+    };
+    auto load_blk = [&](Stage& st, int q0) {
+        const uint32_t toks = (uint32_t)max(0, min(L - q0, kKvTok));
+        const size_t row0 = (size_t)(s0 + q0) * hq + g * kGroup;
+        const rsrc_t rq = make_rsrc(q + row0 * kDqk, toks * (uint32_t)hq * (kDqk * 2));
+        const rsrc_t ro = make_rsrc(dout + row0 * kDv, toks * (uint32_t)hq * (kDv * 2));
+        const rsrc_t rl = make_rsrc(lse + row0, toks * (uint32_t)hq * 4);
+        const rsrc_t rd = make_rsrc(Dws + row0, toks * (uint32_t)hq * 4);
+        st.r[0] = __builtin_amdgcn_raw_buffer_load_b128(rq, off0, 0, 0);
+        st.r[1] = __builtin_amdgcn_raw_buffer_load_b128(lo_waves ? rq : ro, off1, 0, 0);
+        st.r[2] = __builtin_amdgcn_raw_buffer_load_b128(ro, off2, 0, 0);  // waves 4-7: unused
+        st.lse2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, off_s, 0, 0)) * kLog2e;
+        st.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, off_s, 0, 0));
+    };
+    auto store_blk = [&](const Stage& st, int buf) {
         char* qt_ = lds + buf * kKvTileBytes;
         char* ot_ = qt_ + kKvRows * kQRow;
         float* sf = reinterpret_cast<float*>(ot_ + kKvRows * kVRow);
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int c = tid + 512 * i;
-            if (c >= kChunks) continue;
-            if (c < kQChunks) lds_put16(qt_, kQRow, c / (kDqk / 8), c % (kDqk / 8), reg[i]);
-            else lds_put16(ot_, kVRow, (c - kQChunks) / (kDv / 8), (c - kQChunks) % (kDv / 8), reg[i]);
+        lds_put16(qt_, kQRow, tid / (kDqk / 8), tid % (kDqk / 8), st.r[0]);
+        if (lo_waves) {
+            lds_put16(qt_, kQRow, qc1 / (kDqk / 8), qc1 % (kDqk / 8), st.r[1]);
+            lds_put16(ot_, kVRow, oc1 / (kDv / 8), oc1 % (kDv / 8), st.r[2]);
+        } else {
+            lds_put16(ot_, kVRow, oc0 / (kDv / 8), oc0 % (kDv / 8), st.r[1]);
         }
         if (tid < kKvRows) {
-            sf[tid] = st_lse;
-            sf[kKvRows + tid] = st_d;
+            sf[tid] = st.lse2;
+            sf[kKvRows + tid] = st.d;
         }
     };
-    load_blk(k0);
-    store_blk(0);
-    __syncthreads();
-    for (int ib = 0; ib < nblk; ++ib) {
-        const int buf = ib & 1;
-        const bool more = ib + 1 < nblk;
+    static_assert(kQChunks == 768 && kKvRows * (kDv / 8) == 512, "chunk owners assume 32 rows of 192 + 128");
+    auto compute_blk = [&](int ib, int buf) {
         const int q0 = k0 + ib * kKvTok;
-        if (more) load_blk(q0 + kKvTok);
         const char* Qt = lds + buf * kKvTileBytes;
         const char* Ot = Qt + kKvRows * kQRow;
         const float* sf = reinterpret_cast<const float*>(Ot + kKvRows * kVRow);
@@ -401,9 +411,24 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void bwd_dkdv_
         for (int db = 0; db < kDv / 16; ++db) dva[db] = mfma_16x16x32(lds_tr8(Ot, kVRow, db, lane), pf, dva[db]);
 #pragma unroll
         for (int db = 0; db < kDqk / 16; ++db) dka[db] = mfma_16x16x32(lds_tr8(Qt, kQRow, db, lane), dsf, dka[db]);
-        if (more) store_blk(buf ^ 1);
+    };
+    Stage sa, sb;
+    load_blk(sa, k0);
+    store_blk(sa, 0);
+    load_blk(sb, k0 + kKvTok);
+    __syncthreads();
+    int ib = 0;
+    for (; ib + 1 < nblk; ib += 2) {
+        load_blk(sa, k0 + (ib + 2) * kKvTok);
+        compute_blk(ib, 0);
+        store_blk(sb, 1);
+        __syncthreads();
+        load_blk(sb, k0 + (ib + 3) * kKvTok);
+        compute_blk(ib + 1, 1);
+        if (ib + 2 < nblk) store_blk(sa, 0);
         __syncthreads();
     }
+    if (ib < nblk) compute_blk(ib, 0);
     if (key >= L) return;
     // lane holds dK^T[d = 16db + 4G + r][key] and dV^T likewise
     uint16_t* kout = dk + krow * kDqk;
