@@ -183,33 +183,43 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_pe
     const int k_lo = SWA ? max(0, q0 - (window - 1)) : 0;
     const int kt_begin = k_lo / kDqNK, kt_end = t_last / kDqNK;
 
-    constexpr int kKChunks = kDqNK * (kDqk / 8), kChunks = kKChunks + kDqNK * (kDv / 8);
-    constexpr int kPer = (kChunks + 511) / 512;
-    u32x4 reg[kPer];
+    // Staging of a 32-key tile: K rows (768 16-byte chunks), V rows (512).
+    // Chunk owners are fixed per thread and uniform per wave: K chunk tid (all
+    // waves), K chunk 512 + tid (waves 0-3), V chunk tid - 256 (waves 4-7), V
+    // chunk 256 + tid (waves 0-3).  Loads go through descriptors whose base is
+    // the tile's first key and whose record count ends at the sequence end
+    // (keys past it read as zeros and are masked).
+    static_assert(kDqNK * (kDqk / 8) == 768 && kDqNK * (kDv / 8) == 512, "chunk owners assume 32 keys");
+    const bool lo_waves = tid < 256;
+    const int kc1 = 512 + tid, vc0 = tid - 256, vc1 = 256 + tid;
+    const uint32_t krow_b = (uint32_t)hkv * (kDqk * 2), vrow_b = (uint32_t)hkv * (kDv * 2);
+    const uint32_t off0 = (uint32_t)(tid / (kDqk / 8)) * krow_b + (tid % (kDqk / 8)) * 16;
+    const uint32_t off1 = lo_waves ? (uint32_t)(kc1 / (kDqk / 8)) * krow_b + (kc1 % (kDqk / 8)) * 16
+                                   : (uint32_t)(vc0 / (kDv / 8)) * vrow_b + (vc0 % (kDv / 8)) * 16;
+    const uint32_t off2 = lo_waves ? (uint32_t)(vc1 / (kDv / 8)) * vrow_b + (vc1 % (kDv / 8)) * 16 : 0u;
+    u32x4 reg[3];
     auto load_tile = [&](int kt) {
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int c = min(tid + 512 * i, kChunks - 1);
-            const bool isk = c < kKChunks;
-            const int cc = isk ? c : c - kKChunks;
-            const int row = isk ? cc / (kDqk / 8) : cc / (kDv / 8);
-            const int ch = isk ? cc % (kDqk / 8) : cc % (kDv / 8);
-            const int key = min(kt * kDqNK + row, L - 1);  // past the end: masked
-            const uint16_t* src = isk ? k + ((size_t)(s0 + key) * hkv + g) * kDqk : v + ((size_t)(s0 + key) * hkv + g) * kDv;
-            reg[i] = reinterpret_cast<const u32x4*>(src)[ch];
-        }
+        const int kb = kt * kDqNK;
+        const uint32_t keys = (uint32_t)max(0, min(L - kb, kDqNK));
+        const rsrc_t rk = make_rsrc(k + ((size_t)(s0 + kb) * hkv + g) * kDqk, keys * krow_b);
+        const rsrc_t rv = make_rsrc(v + ((size_t)(s0 + kb) * hkv + g) * kDv, keys * vrow_b);
+        reg[0] = __builtin_amdgcn_raw_buffer_load_b128(rk, off0, 0, 0);
+        reg[1] = __builtin_amdgcn_raw_buffer_load_b128(lo_waves ? rk : rv, off1, 0, 0);
+        reg[2] = __builtin_amdgcn_raw_buffer_load_b128(rv, off2, 0, 0);  // waves 4-7: unused
+    };
+    auto put_k = [&](int buf, int c, const u32x4& x) {
+        *reinterpret_cast<u32x4*>(lds_k + buf * kDqLdsK + dq_key_row(c / (kDqk / 8)) * kKS + (c % (kDqk / 8)) * 8) = x;
+    };
+    auto put_v = [&](int buf, int c, const u32x4& x) {
+        *reinterpret_cast<u32x4*>(lds_v + buf * kDqLdsV + (c / (kDv / 8)) * kVS + (c % (kDv / 8)) * 8) = x;
     };
     auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int c = tid + 512 * i;
-            if (c >= kChunks) continue;
-            if (c < kKChunks)
-                *reinterpret_cast<u32x4*>(lds_k + buf * kDqLdsK + dq_key_row(c / (kDqk / 8)) * kKS +
-                                          (c % (kDqk / 8)) * 8) = reg[i];
-            else
-                *reinterpret_cast<u32x4*>(lds_v + buf * kDqLdsV + ((c - kKChunks) / (kDv / 8)) * kVS +
-                                          ((c - kKChunks) % (kDv / 8)) * 8) = reg[i];
+        put_k(buf, tid, reg[0]);
+        if (lo_waves) {
+            put_k(buf, kc1, reg[1]);
+            put_v(buf, vc1, reg[2]);
+        } else {
+            put_v(buf, vc0, reg[1]);
         }
     };
     // Direct A operands: key r32, d = 16s + 8hh.  Transposed K^T reads (the
@@ -236,8 +246,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_pe
         for (int st = 0; st < kDv / 16; ++st)
             dp = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(vtile + vdir + 16 * st), dof[st], dp);
         // The next tile's loads go out here rather than at the top: their
-        // registers then live only through the dQ MFMAs, not the S/dP ones.
-        if (more) load_tile(kt + 1);
+        // registers then live only through the dQ MFMAs, not the S/dP ones
+        // (at the top: equal time).  Past the last tile they read through an
+        // empty descriptor.
+        load_tile(kt + 1);
         float ds[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
