@@ -255,7 +255,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_pe
         for (int r = 0; r < 16; ++r) {
             const int key = kbase + 8 * (r >> 2) + 4 * hh + (r & 3);
             const bool ok = valid && key <= tok && (!SWA || key >= tok - (window - 1));
-            const float p = ok ? fast_exp2(__builtin_fmaf(s[r], c_log2, -lse2)) : 0.0f;
+            const float p = fast_exp2(ok ? __builtin_fmaf(s[r], c_log2, -lse2) : -__builtin_inff());  // masked: 0
             ds[r] = p * (value_scale * dp[r] - Drow);
         }
         // dQ^T += K^T dS^T: B operand of k-step ks holds keys 16ks + {4hh + t, 8 + 4hh + t - 4}.
@@ -409,12 +409,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void bwd_dkdv_
         for (int blk = 0; blk < kKvTok; ++blk) {
             const int tok = q0 + blk;
             const bool tok_ok = tok < L && key < L && key <= tok && (!SWA || tok <= key + window - 1);
+            // The lane's four rows 16blk + 4G + r are consecutive: one 16-byte read each for lse2 and D.
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(sf + 16 * blk + 4 * G);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(sf + kKvRows + 16 * blk + 4 * G);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = 16 * blk + 4 * G + r;
-                const float pr = tok_ok ? fast_exp2(__builtin_fmaf(s[blk][r], c_log2, -sf[row])) : 0.0f;
+                // Masked entries take exp2(-inf) = 0 rather than a branch around the exp.
+                const float arg = __builtin_fmaf(s[blk][r], c_log2, -l4[r]);
+                const float pr = fast_exp2(tok_ok ? arg : -__builtin_inff());
                 p[blk][r] = pr;
-                ds[blk][r] = pr * (value_scale * dp[blk][r] - sf[kKvRows + row]);
+                ds[blk][r] = pr * (value_scale * dp[blk][r] - d4[r]);
             }
         }
         const bf16x8 pf = pack_bf16x8(p[0][0], p[0][1], p[0][2], p[0][3], p[1][0], p[1][1], p[1][2], p[1][3]);
