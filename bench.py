@@ -502,6 +502,9 @@ def main():
                     help="skip the rows timed apart from the step (chunked prefill, paged and FP8 pools, "
                          "backward, RoPE, the 48-layer hybrid stack)")
     ap.add_argument("--split", type=int, default=0, help="GA decode split (keys per workgroup), 0 = default")
+    ap.add_argument("--no-hybrid", action="store_true", help="skip the 48-layer hybrid stack")
+    ap.add_argument("--hybrid-only", action="store_true",
+                    help="time only the 48-layer hybrid stack (prefill + decode steps) and print its JSON")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device copy (a known-size reference for HBM byte counters)")
     args = ap.parse_args()
@@ -512,6 +515,11 @@ def main():
     headroom = args.steps + args.warmup + 1
     dev = "cuda"
     torch.cuda.set_device(0)
+    if args.hybrid_only:
+        log("hybrid stack: 48-layer prefill and decode")
+        print(json.dumps({"metric": METRIC, "n_gpus": 1, "data": "synthetic", **hybrid_rows(B.make_dims())}),
+              flush=True)
+        return
     log("generating inputs on the device")
     swa = synth.prefill_inputs([8192] * 4, seed=0, device=dev)
     ga = synth.prefill_inputs([32768], seed=0, device=dev)
@@ -665,6 +673,7 @@ def main():
                             **fp8_rows(dims, dga, ctx_ga, max_ctx, ws),
                             **backward_rows(dims, ga, swa, out_ga, lse_ga, out_swa, lse_swa),
                             **rope_rows(dims, ga)}
+    if not args.no_next_rows and not args.no_hybrid:
         log("hybrid stack: 48-layer prefill and decode")
         res["hybrid_stack"] = hybrid_rows(dims)["hybrid_stack"]
     if not args.no_cpu_baseline:
