@@ -14,7 +14,7 @@
 // zero, so there are no per-key branches, and a tile's position is a scalar
 // offset.  K rows are loaded straight into MFMA A-operand registers; V rows are
 // loaded into registers, written to a wave-private LDS tile (row-major, the
-// 16-byte chunks of row r XOR-swizzled by 2*(r%4) so the transposed reads are
+// 16-byte chunks of row r XOR-swizzled by 2*(r%8) so the transposed reads are
 // bank-conflict free) and read back transposed with ds_read_b64_tr_b16.  Two
 // tiles are in flight per wave: the next tile's loads are issued before the
 // current one is computed.
@@ -127,14 +127,14 @@ __device__ __forceinline__ void issue_v(const PagedTileSrc& t, const LaneOffsets
         v[i] = __builtin_amdgcn_raw_buffer_load_b128(t.v[i / 4], lo.v, 4 * (i % 4) * rowv, 0);
 }
 
-// V rows to the wave's LDS tile: row 4i + G, logical chunk lane%16 stored at
-// chunk position (lane%16) ^ 2G.  The previous tile's transposed reads were
+// V rows to the wave's LDS tile: row r = 4i + G, logical chunk lane%16 stored
+// at chunk position (lane%16) ^ 2(r%8).  The previous tile's transposed reads were
 // issued earlier by this wave, and a wave's LDS operations run in order.
 __device__ __forceinline__ void stage_v(const u32x4 (&v)[kTile / 4], char* vbuf, int lane) {
     const int G = lane >> 4;
 #pragma unroll
     for (int i = 0; i < kTile / 4; ++i)
-        *reinterpret_cast<u32x4*>(vbuf + (4 * i + G) * (kDv * 2) + (((lane & 15) ^ (2 * G)) * 16)) = v[i];
+        *reinterpret_cast<u32x4*>(vbuf + (4 * i + G) * (kDv * 2) + (((lane & 15) ^ (2 * (4 * (i & 1) + G))) * 16)) = v[i];
     wave_lds_fence();
 }
 
@@ -176,12 +176,14 @@ __device__ __forceinline__ void attend_tile(WaveAcc& acc, const bf16x8 (&qf)[kDq
     // P^T as the B operand: position 8*G + t holds key 4*G + t (t < 4) or 16 + 4*G + t - 4.
     const bf16x8 pf = pack_bf16x8(s[0][0], s[0][1], s[0][2], s[0][3], s[1][0], s[1][1], s[1][2], s[1][3]);
     // V^T as the A operand, transposed out of the swizzled row-major tile: this
-    // lane addresses row 4*G + t' (t' = (lane%16)/4), columns 16*db + 4*(lane%4).
+    // lane addresses row r = 4*G + t' (t' = (lane%16)/4), columns 16*db +
+    // 4*(lane%4), i.e. the 32-byte pair db ^ (r%8) (and row r + 16, same pair).
     const int tq = (lane & 15) >> 2;
+    const int rsw = 4 * (G & 1) + tq;
     const char* vrow = vbuf + (4 * G + tq) * (kDv * 2) + 8 * (lane & 3);
 #pragma unroll
     for (int db = 0; db < kDv / 16; ++db) {
-        const char* p = vrow + 32 * (db ^ tq);
+        const char* p = vrow + 32 * (db ^ rsw);
         const bf16x8 a = join_tr(lds_read_tr16(reinterpret_cast<const uint16_t*>(p)),
                                  lds_read_tr16(reinterpret_cast<const uint16_t*>(p + 16 * kDv * 2)));
         acc.o[db] = mfma_16x16x32(a, pf, acc.o[db] * alpha);
@@ -504,13 +506,13 @@ __device__ __forceinline__ void issue_v8(const TileSrc& t, const Fp8LaneOffsets&
 
 // V codes to the wave's bf16 LDS tile, in the layout stage_v writes: load i
 // holds row r = 8i + l/8, bf16 chunks c = 2(l%8) and c+1, stored at chunk
-// positions c ^ 2(r%4) and that + 1 (c is even), i.e. one 32-byte run.
+// positions c ^ 2(r%8) and that + 1 (c is even), i.e. one 32-byte run.
 __device__ __forceinline__ void stage_v8(const u32x4 (&v)[4], char* vbuf, int lane) {
     const int r0 = lane >> 3, c0 = 2 * (lane & 7);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = 8 * i + r0;
-        char* dst = vbuf + r * (kDv * 2) + ((c0 ^ (2 * (r0 & 3))) * 16);
+        char* dst = vbuf + r * (kDv * 2) + ((c0 ^ (2 * r0)) * 16);
         *reinterpret_cast<u32x4*>(dst) = fp8x8_to_bf16x8(v[i][0], v[i][1]);
         *reinterpret_cast<u32x4*>(dst + 16) = fp8x8_to_bf16x8(v[i][2], v[i][3]);
     }
