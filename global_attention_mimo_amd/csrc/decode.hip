@@ -48,6 +48,13 @@ constexpr int kGroup = 16;
 constexpr int kTile = 32;                         // keys per wave tile
 constexpr int kVTileBytes = kTile * kDv * 2;      // 8 KB: 32 rows of 256 B
 constexpr int kBlockLdsBytes = 4 * kVTileBytes;   // one V tile per wave
+// SWA decode's cross-wave merge, in the same LDS once the tiles are done: per
+// wave 16 heads x 128 fp32 outputs in rows padded to 132 floats (a row pitch
+// of 528 bytes puts the 16 heads' 16-byte writes on distinct banks), then 16
+// (m, l) pairs per wave.
+constexpr int kMergeRow = kDv + 4;
+constexpr int kMergeBytes = (4 * kGroup * kMergeRow + 4 * kGroup * 2) * 4;
+constexpr int kSwaLdsBytes = kMergeBytes > kBlockLdsBytes ? kMergeBytes : kBlockLdsBytes;
 #ifndef MIMO_GA_DECODE_DEPTH
 #define MIMO_GA_DECODE_DEPTH 2
 #endif
@@ -279,7 +286,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     const float* __restrict__ sink, uint16_t* __restrict__ out, float* __restrict__ lse, int hq, int hkv, int R,
     float c_log2, float value_scale) {
     // V tiles of the 4 waves, reused afterwards for the cross-wave merge.
-    __shared__ __attribute__((aligned(1024))) char lds[kBlockLdsBytes];
+    __shared__ __attribute__((aligned(1024))) char lds[kSwaLdsBytes];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int b = blockIdx.x, g = blockIdx.y;
@@ -317,10 +324,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     acc.l += __shfl_xor(acc.l, 16);
     acc.l += __shfl_xor(acc.l, 32);
 
-    // Merge the 4 waves: per wave 16 x (m, l) and O [16 heads][128 dv] in fp32.
+    // Merge the 4 waves: per wave O [16 heads][128 dv] and 16 x (m, l) in fp32.
     __syncthreads();
-    float* mrg_ml = reinterpret_cast<float*>(lds);  // [wave][16][2]
-    float* mrg_o = mrg_ml + 4 * kGroup * 2;         // [wave][16][128]
+    float* mrg_o = reinterpret_cast<float*>(lds);     // [wave][16][kMergeRow]
+    float* mrg_ml = mrg_o + 4 * kGroup * kMergeRow;   // [wave][16][2]
     const int G = lane >> 4, h = lane & 15;
     if (G == 0) {
         mrg_ml[(wave * kGroup + h) * 2 + 0] = acc.m;
@@ -328,7 +335,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     }
 #pragma unroll
     for (int db = 0; db < kDv / 16; ++db)
-        *reinterpret_cast<f32x4*>(mrg_o + (wave * kGroup + h) * kDv + 16 * db + 4 * G) = acc.o[db];
+        *reinterpret_cast<f32x4*>(mrg_o + (wave * kGroup + h) * kMergeRow + 16 * db + 4 * G) = acc.o[db];
     __syncthreads();
 
     const int hl = tid >> 4;        // local head 0..15
@@ -345,7 +352,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     for (int w = 0; w < 4; ++w) {
         const float wt = fast_exp2(mrg_ml[(w * kGroup + hl) * 2] - M);
         Z += wt * mrg_ml[(w * kGroup + hl) * 2 + 1];
-        const float* src_o = mrg_o + (w * kGroup + hl) * kDv + e0;
+        const float* src_o = mrg_o + (w * kGroup + hl) * kMergeRow + e0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] += wt * src_o[e];
     }
