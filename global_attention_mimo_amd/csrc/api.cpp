@@ -30,6 +30,8 @@ int ok() {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 constexpr int kDefaultSplit = 2048;
+constexpr int kMinDefaultSplit = 256;
+constexpr int kMinSplitGroups = 256;
 constexpr int kMaxGridYZ = 65535;
 
 // Shape checks shared by every entry point.  min_window: 1 for prefill
@@ -84,8 +86,17 @@ int check_pages(const mimo_kv_pages* pg, mimo::PageTable* out) {
     return MIMO_OK;
 }
 
-int effective_split(int32_t split_tokens) {
-    int s = split_tokens <= 0 ? kDefaultSplit : split_tokens;
+// GA keys per split workgroup.  Default: the largest of 2048, 1024, 512 and 256
+// keys that still gives at least kMinSplitGroups workgroups (one per compute
+// unit of the part) for batch x max_ctx, so a few long sequences spread over
+// the chip while large batches keep long splits (fewer partial results).
+int effective_split(int32_t split_tokens, int32_t batch, int32_t max_ctx) {
+    if (split_tokens <= 0) {
+        int s = kDefaultSplit;
+        while (s > kMinDefaultSplit && (int64_t)batch * (((int64_t)max_ctx + s) / s) < kMinSplitGroups) s /= 2;
+        return s;
+    }
+    int s = split_tokens;
     if (s > (1 << 30)) s = 1 << 30;
     return (s + 31) / 32 * 32;
 }
@@ -173,9 +184,9 @@ int mimo_attn_prefill_chunk_paged(const mimo_attn_dims* dims, const uint16_t* q,
 
 size_t mimo_attn_decode_workspace_size(const mimo_attn_dims* dims, int layer_type, int32_t batch, int32_t max_ctx,
                                        int32_t split_tokens) {
-    if (check_dims(dims, layer_type, 2) != MIMO_OK || batch < 1 || max_ctx < 0) return 0;
-    if (layer_type == MIMO_LAYER_SWA) return 0;
-    return mimo::ga_workspace_bytes(batch, max_ctx, effective_split(split_tokens), dims->num_q_heads);
+    if (check_dims(dims, layer_type, 2) != MIMO_OK || batch < 1 || max_ctx < 0 || max_ctx == INT32_MAX) return 0;
+    if (layer_type == MIMO_LAYER_SWA || batch > kMaxGridYZ) return 0;
+    return mimo::ga_workspace_bytes(batch, max_ctx, effective_split(split_tokens, batch, max_ctx), dims->num_q_heads);
 }
 
 }  // extern "C"
@@ -219,7 +230,7 @@ int decode_impl(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, c
         if (!aligned16(k_cache) || !aligned16(v_cache))
             return fail(MIMO_ERR_INVALID_ARG, "k_cache and v_cache must be 16-byte aligned");
     }
-    const int split = effective_split(split_tokens);
+    const int split = effective_split(split_tokens, batch, max_ctx);
     mimo::PageTable pt;
     if (pages) {
         if (int st = check_pages(pages, &pt)) return st;

@@ -669,44 +669,69 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     for (int db = 0; db < kDv / 16; ++db) *reinterpret_cast<f32x4*>(ws_o + row * kDv + 16 * db + 4 * G) = acc.o[db];
 }
 
-// Merge of the splits of one sequence: block (b, 16 heads), thread = (head, 8 columns).
+// Merge of the splits of one (sequence, head): block (b, head), thread t =
+// (split group t/16, 8 output columns 8(t%16)).  Each thread folds the splits
+// s = t/16, t/16 + 16, ... with an online max (all its loads are independent,
+// so they are in flight together), then the 16 split groups are merged through
+// LDS by the threads of group 0, which add the sink once and write the row.
+constexpr int kCombGroups = 16;
 __global__ __launch_bounds__(256) void ga_combine_kernel(const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
                                                          const int32_t* __restrict__ ctx_lens, const float* __restrict__ sink,
                                                          uint16_t* __restrict__ out, float* __restrict__ lse, int hq,
                                                          int split, int nsplit, float value_scale) {
-    const int b = blockIdx.x;
-    const int head = blockIdx.y * kGroup + (threadIdx.x >> 4);
-    if (head >= hq) return;
-    const int e0 = (threadIdx.x & 15) * 8;
+    __shared__ float red_ml[kCombGroups][16][2];
+    __shared__ __attribute__((aligned(16))) float red_o[kCombGroups][16][8 + 4];  // padded rows
+    const int b = blockIdx.x, head = blockIdx.y;
+    const int sg = threadIdx.x >> 4, cb = threadIdx.x & 15, e0 = cb * 8;
     const int p = ctx_lens[b];
     const int ns = (p + 1 + split - 1) / split;
     uint16_t* orow = out + ((size_t)b * hq + head) * kDv + e0;
     if (ns > nsplit) {  // the grid did not cover this context: refuse loudly
-        *reinterpret_cast<u32x4*>(orow) = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
-        if (lse && e0 == 0) reinterpret_cast<uint32_t*>(lse)[(size_t)b * hq + head] = 0x7fc00000u;  // quiet NaN bits
+        if (sg == 0) {
+            *reinterpret_cast<u32x4*>(orow) = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
+            if (lse && cb == 0) reinterpret_cast<uint32_t*>(lse)[(size_t)b * hq + head] = 0x7fc00000u;  // quiet NaN bits
+        }
         return;
     }
+    const size_t row0 = (size_t)b * nsplit * hq + head;
+    float m = kNoMax, l = 0.0f;
+    f32x4 o0 = {}, o1 = {};
+    for (int s = sg; s < ns; s += kCombGroups) {
+        const size_t row = row0 + (size_t)s * hq;
+        const float ms = ws_ml[row * 2], ls = ws_ml[row * 2 + 1];
+        const f32x4* src = reinterpret_cast<const f32x4*>(ws_o + row * kDv + e0);
+        const f32x4 a0 = src[0], a1 = src[1];
+        const float mn = fmaxf(m, ms);
+        const float ca = fast_exp2(m - mn), cw = fast_exp2(ms - mn);
+        l = l * ca + ls * cw;
+        o0 = o0 * ca + a0 * cw;
+        o1 = o1 * ca + a1 * cw;
+        m = mn;
+    }
+    red_ml[sg][cb][0] = m;
+    red_ml[sg][cb][1] = l;
+    *reinterpret_cast<f32x4*>(&red_o[sg][cb][0]) = o0;
+    *reinterpret_cast<f32x4*>(&red_o[sg][cb][4]) = o1;
+    __syncthreads();
+    if (sg != 0) return;
     bool has;
     const float sl = sink_log2(sink, head, has);
-    const size_t stride = (size_t)hq;  // rows between consecutive splits of one (b, head)
-    const size_t row0 = (size_t)b * nsplit * hq + head;
     float M = sl;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, ws_ml[(row0 + s * stride) * 2]);
+#pragma unroll
+    for (int g = 0; g < kCombGroups; ++g) M = fmaxf(M, red_ml[g][cb][0]);
     float Z = has ? fast_exp2(sl - M) : 0.0f;
-    f32x4 o0 = {}, o1 = {};
-#pragma unroll 4
-    for (int s = 0; s < ns; ++s) {
-        const size_t row = row0 + s * stride;
-        const float wt = fast_exp2(ws_ml[row * 2] - M);
-        Z += wt * ws_ml[row * 2 + 1];
-        const f32x4* src = reinterpret_cast<const f32x4*>(ws_o + row * kDv + e0);
-        o0 += wt * src[0];
-        o1 += wt * src[1];
+    f32x4 t0 = {}, t1 = {};
+#pragma unroll
+    for (int g = 0; g < kCombGroups; ++g) {
+        const float wt = fast_exp2(red_ml[g][cb][0] - M);  // groups without splits: exp2(kNoMax - M) = 0
+        Z += wt * red_ml[g][cb][1];
+        t0 += wt * *reinterpret_cast<const f32x4*>(&red_o[g][cb][0]);
+        t1 += wt * *reinterpret_cast<const f32x4*>(&red_o[g][cb][4]);
     }
     const float inv = value_scale / Z;
-    *reinterpret_cast<u32x4*>(orow) = u32x4{pack_bf16x2(o0[0] * inv, o0[1] * inv), pack_bf16x2(o0[2] * inv, o0[3] * inv),
-                                           pack_bf16x2(o1[0] * inv, o1[1] * inv), pack_bf16x2(o1[2] * inv, o1[3] * inv)};
-    if (lse && e0 == 0) lse[(size_t)b * hq + head] = (M + __log2f(Z)) * kLn2;
+    *reinterpret_cast<u32x4*>(orow) = u32x4{pack_bf16x2(t0[0] * inv, t0[1] * inv), pack_bf16x2(t0[2] * inv, t0[3] * inv),
+                                           pack_bf16x2(t1[0] * inv, t1[1] * inv), pack_bf16x2(t1[2] * inv, t1[3] * inv)};
+    if (lse && cb == 0) lse[(size_t)b * hq + head] = (M + __log2f(Z)) * kLn2;
 }
 
 }  // namespace
@@ -737,7 +762,7 @@ hipError_t launch_decode_ga(const DecodeArgs& a, hipStream_t stream) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(ga_combine_kernel, dim3(a.batch, (a.hq + kGroup - 1) / kGroup), dim3(256), 0, stream, ws_ml, ws_o,
+    hipLaunchKernelGGL(ga_combine_kernel, dim3(a.batch, a.hq), dim3(256), 0, stream, ws_ml, ws_o,
                        a.ctx_lens, a.sink, a.out, a.lse, a.hq, a.split, nsplit, a.value_scale);
     return hipGetLastError();
 }

@@ -61,7 +61,7 @@ struct DecodeArgs {
 // Pages a GA split kernel preloads per workgroup (two per lane of a wave).
 constexpr int kMaxSplitPages = 128;
 // Number of GA splits of `split` keys covering positions 0..max_ctx.
-inline int ga_num_splits(int max_ctx, int split) { return (max_ctx + 1 + split - 1) / split; }
+inline int ga_num_splits(int max_ctx, int split) { return (int)(((int64_t)max_ctx + split) / split); }
 // Bytes of GA workspace: per (sequence, split, head) an (m, l) pair and 128 partial outputs.
 inline size_t ga_workspace_bytes(int batch, int max_ctx, int split, int hq) {
     return (size_t)batch * (size_t)ga_num_splits(max_ctx, split) * (size_t)hq * (2 + 128) * sizeof(float);

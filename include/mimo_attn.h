@@ -144,7 +144,8 @@ int mimo_attn_prefill_chunk(const mimo_attn_dims* dims, int layer_type,
  * Bytes of device workspace mimo_attn_decode needs for these arguments.  SWA
  * needs none (returns 0).  GA needs batch * ceil((max_ctx+1)/split) * Hq * 130
  * * 4 bytes for the per-split partial results.  split_tokens <= 0 selects the
- * default (2048).  Returns 0 for arguments mimo_attn_decode would reject.
+ * default split (see mimo_attn_decode).  Returns 0 for arguments
+ * mimo_attn_decode would reject.
  */
 size_t mimo_attn_decode_workspace_size(const mimo_attn_dims* dims, int layer_type,
                                        int32_t batch, int32_t max_ctx, int32_t split_tokens);
@@ -167,9 +168,13 @@ size_t mimo_attn_decode_workspace_size(const mimo_attn_dims* dims, int layer_typ
  *   batch        >= 1 (host).
  *   max_ctx      (host) >= every ctx_lens[b]; sizes the GA split grid.  A GA
  *                sequence with ctx_lens[b] > max_ctx gets NaN outputs.
- *   split_tokens GA keys per split workgroup (host); <= 0 selects 2048;
- *                rounded up to a multiple of 32.  Results do not depend on it
- *                beyond fp32 rounding.
+ *   split_tokens GA keys per split workgroup (host); rounded up to a multiple
+ *                of 32.  <= 0 selects the largest of 2048, 1024, 512 and 256
+ *                that gives batch * ceil((max_ctx+1)/split) >= 256 workgroups
+ *                (else 256).  A caller that knows the actual context lengths
+ *                may do better: splits that give a few workgroups per compute
+ *                unit for the sum of the contexts.  Results do not depend on
+ *                it beyond fp32 rounding.
  *   sink, out, lse  as for prefill, with T = batch; lse may be NULL.
  *   workspace    device buffer of >= mimo_attn_decode_workspace_size(...) bytes
  *                (GA only; NULL allowed for SWA).  Its contents need no
@@ -259,8 +264,8 @@ int mimo_kv_append_paged(const mimo_attn_dims* dims,
 
 /*
  * GA decode (as mimo_attn_decode with layer_type GA) over a paged pool.
- * split_tokens must span at most 128 pages: with the default split of 2048
- * every page_size >= 16 qualifies; otherwise MIMO_ERR_UNSUPPORTED.  The
+ * split_tokens must span at most 128 pages: with the default split (at most
+ * 2048) every page_size >= 16 qualifies; otherwise MIMO_ERR_UNSUPPORTED.  The
  * workspace is mimo_attn_decode_workspace_size(dims, MIMO_LAYER_GA, batch,
  * max_ctx, split_tokens) bytes.  Results are bit-identical to
  * mimo_attn_decode over a contiguous pool holding the same rows.

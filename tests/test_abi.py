@@ -154,6 +154,31 @@ def test_workspace_size(L):
     assert B.mimo_attn_decode_workspace_size(B.make_dims(head_dim_v=64), 1, 1, 10, 0) == 0
 
 
+def test_default_split_spreads_short_batches(L):
+    """split_tokens <= 0: the largest of 2048/1024/512/256 giving >= 256 nominal
+    split workgroups for batch x max_ctx (else 256); seen through the workspace."""
+    d = B.make_dims()
+    ws = lambda b, c, s: B.mimo_attn_decode_workspace_size(d, 1, b, c, s)
+    per_split = 64 * 130 * 4
+    assert ws(128, 262207, 0) == ws(128, 262207, 2048) == 128 * 129 * per_split  # large batch keeps 2048
+    assert ws(1, 262143, 0) == ws(1, 262143, 1024) == 1 * 256 * per_split       # one long sequence: 1024
+    assert ws(4, 65535, 0) == ws(4, 65535, 1024) == 4 * 64 * per_split
+    assert ws(3, 4095, 0) == ws(3, 4095, 256) == 3 * 16 * per_split             # floor of 256
+    big = (1 << 31) - 2                                                          # largest accepted max_ctx
+    assert ws(65535, big, 0) == 65535 * ((big + 2048) // 2048) * per_split        # 64-bit arithmetic
+    assert ws(65536, 10, 0) == 0 and ws(1, (1 << 31) - 1, 0) == 0                # what decode rejects
+
+
+def test_stack_split_from_known_lengths():
+    """The hybrid stack picks its decode split from the contexts it will hold."""
+    from types import SimpleNamespace
+    from global_attention_mimo_amd.stack import HybridStack
+    pick = lambda lengths, steps: HybridStack.decode_split(SimpleNamespace(lengths=lengths, decode_steps=steps))
+    assert pick([262144] * 128, 64) == 2048
+    assert pick([512 + 100 * i for i in range(32)], 64) == 256
+    assert pick([40000] * 32, 64) == 1024   # 32 x 40 splits of 1024 = 1280 >= 768
+
+
 def append_call(L, dims=None, layer=1, k=FAKE, v=FAKE, cu=FAKE, ctx=FAKE, batch=1, total=4, kc=FAKE, vc=FAKE,
                 base=FAKE, cap=FAKE):
     d = dims or B.make_dims()
