@@ -356,6 +356,7 @@ def hybrid_rows(dims, decode_steps=64):
         (eager_ms if graph is None else graph_ms).append(
             (e0.elapsed_time(e1), (time.perf_counter() - t0) * 1e3))
     kvb = st.kv_bytes()
+    calls = st.num_layers * (1 if st.fused else 2)
     del st, out, lse, dout, dlse, graph
     torch.cuda.empty_cache()
     dec_ms = float(np.mean([g for g, _ in graph_ms]))
@@ -371,7 +372,7 @@ def hybrid_rows(dims, decode_steps=64):
         "prefill_swa_layers_ms": swa_ms, "prefill_swa_GB/s": b_swa / (swa_ms * 1e-3) / 1e9,
         "prefill_swa_frac_hbm_peak": b_swa / (swa_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
         "decode_step_ms": dec_ms, "decode_tokens/s": Bd / (dec_ms * 1e-3),
-        "decode_step_note": f"HIP-graph replay of the whole step (96 library calls + context advance), mean of "
+        "decode_step_note": f"HIP-graph replay of the whole step ({calls} library calls + context advance), mean of "
                             f"{len(graph_ms)} steps; the first {len(eager_ms)} steps issued call by call took "
                             f"{eager_gpu:.3f} ms on the GPU clock and {eager_wall:.3f} ms host wall time",
         "kv_cache_bytes": kvb["hybrid"], "kv_cache_bytes_all_ga": kvb["all_ga"]}}

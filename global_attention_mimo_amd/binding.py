@@ -26,7 +26,8 @@ MIMO_ERR_WORKSPACE = 3
 MIMO_ERR_HIP = 4
 
 ENTRY_POINTS = ("mimo_attn_prefill", "mimo_attn_prefill_chunk", "mimo_attn_decode_workspace_size",
-                "mimo_attn_decode", "mimo_kv_append", "mimo_kv_append_paged", "mimo_attn_decode_paged",
+                "mimo_attn_decode", "mimo_attn_decode_append", "mimo_kv_append", "mimo_kv_append_paged",
+                "mimo_attn_decode_paged",
                 "mimo_attn_prefill_chunk_paged", "mimo_kv_append_fp8", "mimo_attn_decode_fp8",
                 "mimo_attn_prefill_backward_workspace_size", "mimo_attn_prefill_backward", "mimo_rope_apply",
                 "mimo_status_string",
@@ -75,6 +76,9 @@ def lib() -> ctypes.CDLL:
         L.mimo_attn_decode.restype = ctypes.c_int
         L.mimo_attn_decode.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P,
                                        _P, _P, _SZ, _P]
+        L.mimo_attn_decode_append.restype = ctypes.c_int
+        L.mimo_attn_decode_append.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
+                                              _P, _P, _P, _P, _SZ, _P]
         L.mimo_kv_append.restype = ctypes.c_int
         L.mimo_kv_append.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _P]
         pages_p = ctypes.POINTER(mimo_kv_pages)
@@ -171,6 +175,16 @@ def mimo_attn_decode(dims: mimo_attn_dims, layer_type: int, q, k_new, v_new, k_c
     _check(lib().mimo_attn_decode(ctypes.byref(dims), layer_type, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
                                   _ptr(v_cache), _ptr(kv_base), _ptr(ctx_lens), batch, max_ctx, split_tokens,
                                   _ptr(sink), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def mimo_attn_decode_append(dims: mimo_attn_dims, layer_type: int, q, k_new, v_new, k_cache, v_cache, kv_base,
+                            kv_capacity, ctx_lens, batch: int, max_ctx: int, split_tokens: int, sink, out, lse,
+                            workspace, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().mimo_attn_decode_append(ctypes.byref(dims), layer_type, _ptr(q), _ptr(k_new), _ptr(v_new),
+                                         _ptr(k_cache), _ptr(v_cache), _ptr(kv_base), _ptr(kv_capacity),
+                                         _ptr(ctx_lens), batch, max_ctx, split_tokens, _ptr(sink), _ptr(out),
+                                         _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def mimo_kv_append(dims: mimo_attn_dims, layer_type: int, k, v, cu_newlens, ctx_lens, batch: int, total_new: int,

@@ -215,7 +215,8 @@ int decode_impl(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, c
                 const uint16_t* v_new, const uint16_t* k_cache, const uint16_t* v_cache, const int64_t* kv_base,
                 const mimo_kv_pages* pages, const int32_t* ctx_lens, int32_t batch, int32_t max_ctx,
                 int32_t split_tokens, const float* sink, uint16_t* out, float* lse, void* workspace,
-                size_t workspace_bytes, hipStream_t stream, const Fp8Pool* fp8 = nullptr) {
+                size_t workspace_bytes, hipStream_t stream, const Fp8Pool* fp8 = nullptr, bool append = false,
+                const int64_t* kv_capacity = nullptr) {
     if (int st = check_dims(dims, layer_type, 2)) return st;
     if (!q || !k_new || !v_new || !ctx_lens || !out)
         return fail(MIMO_ERR_INVALID_ARG, "q, k_new, v_new, ctx_lens and out must be non-NULL");
@@ -257,6 +258,14 @@ int decode_impl(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, c
         a.v_cache8 = fp8->v;
         a.k_scale = fp8->k_scale;
         a.v_scale = fp8->v_scale;
+    }
+    if (append) {
+        if (fp8 || pages) return fail(MIMO_ERR_UNSUPPORTED, "fused append covers bf16 ring and contiguous pools only");
+        if (layer_type == MIMO_LAYER_GA && (!kv_base || !kv_capacity))
+            return fail(MIMO_ERR_INVALID_ARG, "GA decode with append needs kv_base and kv_capacity");
+        a.append_k = const_cast<uint16_t*>(k_cache);
+        a.append_v = const_cast<uint16_t*>(v_cache);
+        a.kv_capacity = kv_capacity;
     }
     if (layer_type == MIMO_LAYER_SWA) {
         if (batch > INT32_MAX / 2) return fail(MIMO_ERR_UNSUPPORTED, "batch too large");
@@ -320,6 +329,16 @@ int mimo_attn_decode(const mimo_attn_dims* dims, int layer_type, const uint16_t*
                      uint16_t* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     return decode_impl(dims, layer_type, q, k_new, v_new, k_cache, v_cache, kv_base, nullptr, ctx_lens, batch,
                        max_ctx, split_tokens, sink, out, lse, workspace, workspace_bytes, stream);
+}
+
+int mimo_attn_decode_append(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, const uint16_t* k_new,
+                            const uint16_t* v_new, uint16_t* k_cache, uint16_t* v_cache, const int64_t* kv_base,
+                            const int64_t* kv_capacity, const int32_t* ctx_lens, int32_t batch, int32_t max_ctx,
+                            int32_t split_tokens, const float* sink, uint16_t* out, float* lse, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+    return decode_impl(dims, layer_type, q, k_new, v_new, k_cache, v_cache, kv_base, nullptr, ctx_lens, batch,
+                       max_ctx, split_tokens, sink, out, lse, workspace, workspace_bytes, stream, nullptr, true,
+                       kv_capacity);
 }
 
 int mimo_attn_decode_paged(const mimo_attn_dims* dims, const uint16_t* q, const uint16_t* k_new,

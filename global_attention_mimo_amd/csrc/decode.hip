@@ -284,7 +284,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const uint16_t* __restrict__ ring_k, const uint16_t* __restrict__ ring_v, const int32_t* __restrict__ ctx_lens,
     const float* __restrict__ sink, uint16_t* __restrict__ out, float* __restrict__ lse, int hq, int hkv, int R,
-    float c_log2, float value_scale) {
+    float c_log2, float value_scale, uint16_t* __restrict__ app_k, uint16_t* __restrict__ app_v) {
     // V tiles of the 4 waves, reused afterwards for the cross-wave merge.
     __shared__ __attribute__((aligned(1024))) char lds[kSwaLdsBytes];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -337,6 +337,18 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     for (int db = 0; db < kDv / 16; ++db)
         *reinterpret_cast<f32x4*>(mrg_o + (wave * kGroup + h) * kMergeRow + 16 * db + 4 * G) = acc.o[db];
     __syncthreads();
+    if (app_k && tid < (kDqk + kDv) / 8) {
+        // Fused append: the new token goes to ring slot p mod R.  That slot
+        // (position p - R) was read by this workgroup only, and every wave's
+        // ring loads were consumed before the barrier above.
+        const size_t slot_row = (size_t)b * R + p % R;
+        if (tid < kDqk / 8)
+            reinterpret_cast<u32x4*>(app_k + (slot_row * hkv + g) * kDqk)[tid] =
+                reinterpret_cast<const u32x4*>(k_new + ((size_t)b * hkv + g) * kDqk)[tid];
+        else
+            reinterpret_cast<u32x4*>(app_v + (slot_row * hkv + g) * kDv)[tid - kDqk / 8] =
+                reinterpret_cast<const u32x4*>(v_new + ((size_t)b * hkv + g) * kDv)[tid - kDqk / 8];
+    }
 
     const int hl = tid >> 4;        // local head 0..15
     const int e0 = (tid & 15) * 8;  // 8 output columns
@@ -372,7 +384,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     const uint16_t* __restrict__ pool_k, const uint16_t* __restrict__ pool_v, const int64_t* __restrict__ kv_base,
     const int32_t* __restrict__ ctx_lens, int hq, int hkv, int split, int nsplit, float c_log2,
     float* __restrict__ ws_ml, float* __restrict__ ws_o, const int32_t* __restrict__ block_table, int max_blocks,
-    int page_shift, long long num_pages) {
+    int page_shift, long long num_pages, uint16_t* __restrict__ app_k, uint16_t* __restrict__ app_v,
+    const int64_t* __restrict__ kv_capacity) {
     __shared__ __attribute__((aligned(1024))) char lds[kBlockLdsBytes];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -382,6 +395,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     const int p = ctx_lens[b];
     const int k0 = s * split;
     if (k0 > p) return;
+    if (!PAGED && app_k && s == 0 && lane < (kDqk + kDv) / 8 && p < kv_capacity[b]) {
+        // Fused append: row kv_base[b] + p of KV head g.  No split of this
+        // launch reads row p (the new token comes from k_new / v_new).
+        const size_t row = (size_t)kv_base[b] + p;
+        if (lane < kDqk / 8)
+            reinterpret_cast<u32x4*>(app_k + (row * hkv + g) * kDqk)[lane] =
+                reinterpret_cast<const u32x4*>(k_new + ((size_t)b * hkv + g) * kDqk)[lane];
+        else
+            reinterpret_cast<u32x4*>(app_v + (row * hkv + g) * kDv)[lane - kDqk / 8] =
+                reinterpret_cast<const u32x4*>(v_new + ((size_t)b * hkv + g) * kDv)[lane - kDqk / 8];
+    }
     const int k1 = min(k0 + split, p + 1);  // keys [k0, k1) of this split
     const int kend = min(k1, p);            // of which [k0, kend) live in the pool
     const int rowk = hkv * kDqk * 2, rowv = hkv * kDv * 2;
@@ -741,7 +765,7 @@ hipError_t launch_decode_swa(const DecodeArgs& a, hipStream_t stream) {
     const bool short_ring = (R + kTile - 1) / kTile + 1 <= 8;
     hipLaunchKernelGGL(short_ring ? swa_decode_kernel<true> : swa_decode_kernel<false>, dim3(a.batch, a.hkv),
                        dim3(256), 0, stream, a.q, a.k_new, a.v_new, a.k_cache, a.v_cache, a.ctx_lens, a.sink, a.out,
-                       a.lse, a.hq, a.hkv, R, a.softmax_scale * kLog2e, a.value_scale);
+                       a.lse, a.hq, a.hkv, R, a.softmax_scale * kLog2e, a.value_scale, a.append_k, a.append_v);
     return hipGetLastError();
 }
 
@@ -758,7 +782,7 @@ hipError_t launch_decode_ga(const DecodeArgs& a, hipStream_t stream) {
                            dim3(nsplit, a.batch, (a.hkv + 3) / 4), dim3(256), 0, stream, a.q, a.k_new, a.v_new,
                            a.k_cache, a.v_cache, a.kv_base, a.ctx_lens, a.hq, a.hkv, a.split, nsplit,
                            a.softmax_scale * kLog2e, ws_ml, ws_o, a.pages.table, a.pages.max_blocks, a.pages.shift,
-                           a.pages.num_pages);
+                           a.pages.num_pages, a.pages.table ? nullptr : a.append_k, a.append_v, a.kv_capacity);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -57,6 +57,12 @@ struct DecodeArgs {
     const uint8_t* v_cache8 = nullptr;
     const float* k_scale = nullptr;
     const float* v_scale = nullptr;
+    // Fused append (bf16 ring or contiguous pool): the new token is also written
+    // to the cache, SWA ring slot p mod (window-1), GA row kv_base[b] + p when
+    // p < kv_capacity[b].  Null: attention only.
+    uint16_t* append_k = nullptr;
+    uint16_t* append_v = nullptr;
+    const int64_t* kv_capacity = nullptr;
 };
 // Pages a GA split kernel preloads per workgroup (two per lane of a wave).
 constexpr int kMaxSplitPages = 128;

@@ -45,6 +45,7 @@ class HybridStack:
     window: int = synth.WINDOW
     hq: int = synth.HQ
     hkv: int = synth.HKV
+    fused: bool = True  # decode steps append through mimo_attn_decode_append
     layer_types: List[int] = field(init=False)
     caches: List[LayerCache] = field(init=False)
 
@@ -105,11 +106,17 @@ class HybridStack:
                          c.kv_capacity, stream)
 
     def decode_layer(self, layer: int, q, k_new, v_new, sink, out, lse=None, stream=None):
-        """One decode step of one layer: attend over the cache + new token, then append it."""
+        """One decode step of one layer: attend over the cache + new token, then append
+        it (one fused library call, or decode then append when `fused` is off)."""
         lt = self.layer_types[layer]
         c = self.caches[layer]
+        ws = self.workspace if lt == GA else None
+        if self.fused:
+            B.mimo_attn_decode_append(self.dims, lt, q, k_new, v_new, c.k, c.v, c.kv_base, c.kv_capacity, self.ctx,
+                                      self.batch, self.max_ctx, self.split, sink, out, lse, ws, stream)
+            return
         B.mimo_attn_decode(self.dims, lt, q, k_new, v_new, c.k, c.v, c.kv_base, self.ctx, self.batch, self.max_ctx,
-                           self.split, sink, out, lse, self.workspace if lt == GA else None, stream)
+                           self.split, sink, out, lse, ws, stream)
         B.mimo_kv_append(self.dims, lt, k_new, v_new, self.cu_step, self.ctx, self.batch, self.batch, c.k, c.v,
                          c.kv_base, c.kv_capacity, stream)
 

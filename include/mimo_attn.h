@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MIMO_ATTN_ABI_VERSION 6
+#define MIMO_ATTN_ABI_VERSION 7
 
 /* Layer type: which key set a query sees (model doc, Key features; config
  * layer_types). */
@@ -219,6 +219,33 @@ int mimo_kv_append(const mimo_attn_dims* dims, int layer_type,
                    int32_t batch, int32_t total_new,
                    uint16_t* k_cache, uint16_t* v_cache,
                    const int64_t* kv_base, const int64_t* kv_capacity, hipStream_t stream);
+
+/*
+ * One decode step with its append in the same launch: the result, the
+ * outputs and the caches afterwards are those of mimo_attn_decode followed by
+ * mimo_kv_append of the one new token per sequence (cu_newlens = 0, 1, ...,
+ * batch; position ctx_lens[b]).  For the many small decode calls of a layer
+ * stack this saves the append's separate launch.
+ *
+ * Arguments as for mimo_attn_decode, with k_cache / v_cache writable, plus
+ *   kv_capacity  GA: [batch] int64 (device), rows reserved for sequence b; the
+ *                new row kv_base[b] + p is written only when p < kv_capacity[b]
+ *                (as mimo_kv_append refuses a sequence that would overflow).
+ *                SWA: ignored (may be NULL).
+ * The SWA workgroup of (b, KV head) writes ring slot p mod (W-1) after all of
+ * its own reads of the ring (that slot still holds position p-(W-1), which
+ * query p attends to).  The GA row p is not read by the attention of this
+ * call.  bf16 caches only (the paged and FP8 pools keep separate calls).
+ * ctx_lens is not advanced.  Errors as for mimo_attn_decode; GA without
+ * kv_base or kv_capacity is MIMO_ERR_INVALID_ARG.
+ */
+int mimo_attn_decode_append(const mimo_attn_dims* dims, int layer_type,
+                            const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                            uint16_t* k_cache, uint16_t* v_cache,
+                            const int64_t* kv_base, const int64_t* kv_capacity, const int32_t* ctx_lens,
+                            int32_t batch, int32_t max_ctx, int32_t split_tokens,
+                            const float* sink, uint16_t* out, float* lse,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Paged GA pool.  The cache of past_key_values (model doc,

@@ -42,7 +42,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_version_and_status_strings(L):
-    assert B.mimo_abi_version() == 6
+    assert B.mimo_abi_version() == 7
     assert B.mimo_status_string(0) == "MIMO_OK"
     assert B.mimo_status_string(3) == "MIMO_ERR_WORKSPACE"
     assert B.mimo_status_string(99) == "MIMO_ERR_UNKNOWN"
@@ -140,6 +140,24 @@ def decode_call(L, dims=None, layer=1, q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAK
 ])
 def test_decode_rejects(L, case, status):
     assert decode_call(L, **case) == status
+
+
+def decode_append_call(L, layer=1, q=FAKE, kc=FAKE, base=FAKE, cap=FAKE, ctx=FAKE, batch=2):
+    d = B.make_dims()
+    return L.mimo_attn_decode_append(ctypes.byref(d), layer, q, FAKE, FAKE, kc, FAKE, base, cap, ctx, batch, 100, 0,
+                                     None, FAKE, None, None, 0, None)
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(layer=5), B.MIMO_ERR_INVALID_ARG),
+    (dict(q=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(kc=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(batch=0), B.MIMO_ERR_INVALID_ARG),
+    (dict(cap=None), B.MIMO_ERR_INVALID_ARG),   # GA append needs the capacities
+    (dict(base=None), B.MIMO_ERR_INVALID_ARG),
+])
+def test_decode_append_rejects(L, case, status):
+    assert decode_append_call(L, **case) == status
 
 
 def test_workspace_size(L):
