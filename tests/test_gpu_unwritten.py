@@ -77,3 +77,44 @@ def test_decode_append_ignores_unwritten_cache(layer_type, ctx):
     for b, p in enumerate(ctx):
         row = kc[b, p % 128] if layer_type == SWA else kc[int(x.kv_base[b]) + p]
         assert torch.equal(row, x.k_new[b])
+
+
+@pytest.mark.parametrize("layer_type", [SWA, GA])
+def test_chunk_prefill_ignores_unwritten_cache(layer_type):
+    """Chunked prefill reads cached positions below ctx_lens[b] only: the rest of
+    the ring (while it fills) and of the pool, padding rows included, is NaN/Inf
+    in both the GPU caches and the oracle's host copies."""
+    import numpy as np
+    from test_gpu_chunk import SCALE, _caches, _chunk, _fill
+    from gpu_util import bits, orc, sink_array
+    lengths = [300, 170, 64, 260]
+    cached = [0, 1, 63, 131]
+    log(f"[case] unwritten cache, chunked prefill layer={layer_type} cached={cached}")
+    x = synth.prefill_inputs(lengths, seed=44)
+    kc, vc, base, cap = _caches(layer_type, lengths)
+    kh, vh = _fill(x, layer_type, cached, kc, vc, base, cap)
+    kd, vd = kc.view(torch.int16), vc.view(torch.int16)
+    kh16, vh16 = kh.view(np.int16), vh.view(np.int16)
+    if layer_type == SWA:
+        spans = [(b, c, 128) for b, c in enumerate(cached) if c < 128]
+        for b, lo, hi in spans:
+            kd[b, lo:hi] = NAN
+            vd[b, lo:hi] = INF
+            kh16[b, lo:hi] = NAN
+            vh16[b, lo:hi] = INF
+    else:
+        bl, cl = base.tolist(), cap.tolist()
+        spans = [(0, bl[0])] + [(bl[b] + c, bl[b] + cl[b]) for b, c in enumerate(cached)]
+        for lo, hi in spans:
+            kd[lo:hi] = NAN
+            vd[lo:hi] = INF
+            kh16[lo:hi] = NAN
+            vh16[lo:hi] = INF
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(kc), kh) and np.array_equal(bits(vc), vh)
+    out, lse, new, rest, cu_new, ctx = _chunk(x, layer_type, cached, kc, vc, base)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    ro, rl = orc().prefill_chunk(bits(x.q[new]), bits(x.k[new]), bits(x.v[new]), cu_new.cpu().numpy(), kh, vh,
+                                 ctx.cpu().numpy(), layer_type=layer_type, window=129, scale=SCALE,
+                                 sink=sink_array(x.sink), kv_base=None if base is None else base.cpu().numpy())
+    compare(out, lse, ro, rl, f"unwritten cache, chunked prefill layer {layer_type}")
