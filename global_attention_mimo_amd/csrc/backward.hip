@@ -95,7 +95,11 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t* __restr
 }
 
 // dsink[h] = -sum over the batch's tokens of exp(sink[h] - lse) * D, one block
-// per head; each thread sums a fixed stride of tokens, then a fixed tree.
+// per head; each thread sums a fixed stride of tokens into eight running sums
+// (token t + 256u goes to sum u, so the loads of eight tokens are in flight
+// together; the last few go to sum 0), then the sums and the threads are
+// added in a fixed tree.
+constexpr int kSinkUnroll = 8;
 __global__ __launch_bounds__(256) void bwd_sink_kernel(const float* __restrict__ sink, const float* __restrict__ lse,
                                                        const float* __restrict__ D, const int32_t* __restrict__ cu,
                                                        int num_seqs, int max_seqlen, int hq,
@@ -103,17 +107,30 @@ __global__ __launch_bounds__(256) void bwd_sink_kernel(const float* __restrict__
     __shared__ float part[256];
     const int h = blockIdx.x;
     const float s = sink ? sink[h] : -__builtin_inff();
-    float acc = 0.0f;
+    float acc[kSinkUnroll] = {};
     if (s > -__builtin_inff()) {
         for (int b = 0; b < num_seqs; ++b) {
             const int s0 = cu[b], L = min(cu[b + 1] - s0, max_seqlen);
-            for (int t = threadIdx.x; t < L; t += 256) {
+            int t = threadIdx.x;
+            for (; t + (kSinkUnroll - 1) * 256 < L; t += kSinkUnroll * 256) {
+                float l[kSinkUnroll], d[kSinkUnroll];
+#pragma unroll
+                for (int u = 0; u < kSinkUnroll; ++u) {
+                    const size_t row = (size_t)(s0 + t + 256 * u) * hq + h;
+                    l[u] = lse[row];
+                    d[u] = D[row];
+                }
+#pragma unroll
+                for (int u = 0; u < kSinkUnroll; ++u) acc[u] += fast_exp2((s - l[u]) * kLog2e) * d[u];
+            }
+            for (; t < L; t += 256) {
                 const size_t row = (size_t)(s0 + t) * hq + h;
-                acc += fast_exp2((s - lse[row]) * kLog2e) * D[row];
+                acc[0] += fast_exp2((s - lse[row]) * kLog2e) * D[row];
             }
         }
     }
-    part[threadIdx.x] = acc;
+    static_assert(kSinkUnroll == 8, "the tree below adds eight sums");
+    part[threadIdx.x] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
     __syncthreads();
     for (int w = 128; w > 0; w >>= 1) {
         if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
