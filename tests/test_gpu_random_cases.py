@@ -1,0 +1,76 @@
+"""Seeded random cases across the three attention entry points, against the oracle.
+
+Each case draws its own shape from a generator seeded with the case number:
+prefill over 1-5 ragged sequences (lengths at tile edges 15/16/17 or anywhere
+up to 700) with SWA windows from 1 to 300 (streaming and tiled kernels) or GA;
+decode over 1-9 sequences with contexts at ring and tile edges or up to 3000,
+ring sizes from 1 to 299 slots and GA splits of 32 to 1024 keys; chunked
+prefill with random cached prefixes.  Sinks are the seeded ones, absent, -inf
+on every third head, or six times larger; value_scale is 1 or 0.7071.  The
+bars are those of every other parity test.
+"""
+import random
+
+import pytest
+
+from global_attention_mimo_amd import synth
+from gpu_util import bits, compare, gpu_prefill, log, oracle_prefill, orc, sink_array
+from test_gpu_chunk import _caches, _chunk, _fill
+from test_gpu_decode import SCALE, gpu_decode, oracle_decode
+
+pytestmark = pytest.mark.gpu
+N_CASES = 48
+
+
+def _sink(rng, x):
+    c = rng.choice(["inputs", "none", "neginf", "big"])
+    if c == "inputs":
+        return c, "inputs"
+    if c == "none":
+        return c, None
+    s = x.sink.clone()
+    if c == "neginf":
+        s[::3] = float("-inf")
+    else:
+        s = s * 6.0
+    return c, s
+
+
+@pytest.mark.parametrize("case", range(N_CASES))
+def test_random_case(case):
+    rng = random.Random(7919 * case + 17)
+    kind = ("prefill", "decode", "chunk")[case % 3]
+    lt = rng.choice([0, 1])
+    seed = 2000 + case
+    if kind == "prefill":
+        lengths = [rng.choice([1, 2, 15, 16, 17, rng.randint(1, 700)]) for _ in range(rng.randint(1, 5))]
+        window = rng.choice([1, 2, 17, 64, 128, 129, 130, 145, 146, 300]) if lt == 0 else 129
+        vs = rng.choice([1.0, 0.7071])
+        x = synth.prefill_inputs(lengths, seed=seed)
+        sc, s = _sink(rng, x)
+        log(f"[case {case}] prefill layer={lt} lengths={lengths} window={window} value_scale={vs} sink={sc}")
+        out, lse = gpu_prefill(x, lt, window=window, value_scale=vs, sink=s)
+        ro, rl = oracle_prefill(x, lt, window=window, value_scale=vs, sink=s)
+    elif kind == "decode":
+        ctx = [rng.choice([0, 1, 2, 127, 128, 129, 255, 256, rng.randint(0, 3000)]) for _ in range(rng.randint(1, 9))]
+        window = rng.choice([2, 17, 129, 130, 200, 225, 300]) if lt == 0 else 129
+        split = rng.choice([0, 32, 64, 96, 256, 1024]) if lt == 1 else 0
+        vs = rng.choice([1.0, 0.7071])
+        x = synth.decode_inputs(ctx, lt, seed=seed, window=window)
+        sc, s = _sink(rng, x)
+        log(f"[case {case}] decode layer={lt} ctx={ctx} window={window} split={split} value_scale={vs} sink={sc}")
+        out, lse = gpu_decode(x, lt, split=split, sink=s, value_scale=vs, window=window)
+        ro, rl = oracle_decode(x, lt, sink=s, value_scale=vs, window=window)
+    else:
+        lengths = [rng.randint(1, 600) for _ in range(rng.randint(1, 5))]
+        cached = [rng.choice([0, 1, L - 1, rng.randint(0, L - 1)]) for L in lengths]
+        window = rng.choice([2, 17, 129, 145, 146, 300]) if lt == 0 else 129
+        x = synth.prefill_inputs(lengths, seed=seed)
+        log(f"[case {case}] chunked prefill layer={lt} lengths={lengths} cached={cached} window={window}")
+        kc, vc, base, cap = _caches(lt, lengths, window=window)
+        kh, vh = _fill(x, lt, cached, kc, vc, base, cap, window=window)
+        out, lse, new, rest, cu_new, ctxd = _chunk(x, lt, cached, kc, vc, base, window=window)
+        ro, rl = orc().prefill_chunk(bits(x.q[new]), bits(x.k[new]), bits(x.v[new]), cu_new.cpu().numpy(), kh, vh,
+                                     ctxd.cpu().numpy(), layer_type=lt, window=window, scale=SCALE,
+                                     sink=sink_array(x.sink), kv_base=None if base is None else base.cpu().numpy())
+    compare(out, lse, ro, rl, f"random case {case} ({kind})")
