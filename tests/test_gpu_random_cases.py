@@ -7,7 +7,10 @@ decode over 1-9 sequences with contexts at ring and tile edges or up to 3000,
 ring sizes from 1 to 299 slots and GA splits of 32 to 1024 keys; chunked
 prefill with random cached prefixes.  Sinks are the seeded ones, absent, -inf
 on every third head, or six times larger; value_scale is 1 or 0.7071.  The
-bars are those of every other parity test.
+bars are those of every other parity test.  Two more families: the prefill
+backward on seeded ragged batches (gradient bars of the backward tests), and
+the fused decode + append against decode followed by append (bit for bit),
+some GA sequences with no room left for the new token.
 """
 import random
 
@@ -74,3 +77,46 @@ def test_random_case(case):
                                      ctxd.cpu().numpy(), layer_type=lt, window=window, scale=SCALE,
                                      sink=sink_array(x.sink), kv_base=None if base is None else base.cpu().numpy())
     compare(out, lse, ro, rl, f"random case {case} ({kind})")
+
+
+N_BACKWARD = 16
+
+
+@pytest.mark.parametrize("case", range(N_BACKWARD))
+def test_random_backward_case(case):
+    """Prefill backward over a seeded ragged batch against the oracle's gradients."""
+    from test_gpu_backward import dout_like, grad_compare, oracle_grads, run
+    rng = random.Random(104729 * case + 3)
+    lt = rng.choice([0, 1])
+    lengths = [rng.choice([1, 2, 16, 17, 32, 33, rng.randint(1, 400)]) for _ in range(rng.randint(1, 4))]
+    window = rng.choice([2, 17, 64, 129, 130, 300]) if lt == 0 else 129
+    vs = rng.choice([1.0, 0.7071])
+    x = synth.prefill_inputs(lengths, seed=3000 + case)
+    sc, s = _sink(rng, x)
+    log(f"[case {case}] backward layer={lt} lengths={lengths} window={window} value_scale={vs} sink={sc}")
+    dout = dout_like(sum(lengths), 4000 + case)
+    dq, dk, dv, ds = run(x, dout, lt, window, vs, sink=s)
+    rq, rk, rv, rs = oracle_grads(x, dout, lt, window, vs, sink=s)
+    grad_compare(dq, rq, "dq")
+    grad_compare(dk, rk, "dk")
+    grad_compare(dv, rv, "dv")
+    grad_compare(ds, rs, "dsink")
+
+
+N_APPEND = 8
+
+
+@pytest.mark.parametrize("case", range(N_APPEND))
+def test_random_decode_append_case(case):
+    """Fused decode + append equals decode then append, bit for bit, on seeded contexts."""
+    import torch
+    from test_gpu_decode_append import _both
+    rng = random.Random(1299709 * case + 11)
+    lt = case % 2
+    ctx = [rng.choice([0, 1, 127, 128, 129, 255, 256, rng.randint(0, 5000)]) for _ in range(rng.randint(1, 9))]
+    split = rng.choice([0, 32, 64, 256]) if lt == 1 else 0
+    full = rng.randrange(len(ctx)) if lt == 1 and rng.random() < 0.5 else None
+    log(f"[case {case}] decode_append layer={lt} ctx={ctx} split={split} full={full}")
+    _, ((o0, l0, k0, v0), (o1, l1, k1, v1)) = _both(lt, ctx, split, full)
+    assert torch.equal(o0, o1) and torch.equal(l0, l1), "outputs differ"
+    assert torch.equal(k0, k1) and torch.equal(v0, v1), "caches differ"
