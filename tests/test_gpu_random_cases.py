@@ -10,7 +10,9 @@ on every third head, or six times larger; value_scale is 1 or 0.7071.  The
 bars are those of every other parity test.  Two more families: the prefill
 backward on seeded ragged batches (gradient bars of the backward tests), and
 the fused decode + append against decode followed by append (bit for bit),
-some GA sequences with no room left for the new token.
+some GA sequences with no room left for the new token; and the paged GA pool
+(page sizes 16-1024, splits 32-2048, contexts to 6000) against the oracle and
+bit for bit against the contiguous pool.
 """
 import random
 
@@ -120,3 +122,52 @@ def test_random_decode_append_case(case):
     _, ((o0, l0, k0, v0), (o1, l1, k1, v1)) = _both(lt, ctx, split, full)
     assert torch.equal(o0, o1) and torch.equal(l0, l1), "outputs differ"
     assert torch.equal(k0, k1) and torch.equal(v0, v1), "caches differ"
+
+
+N_PAGED = 8
+
+
+@pytest.mark.parametrize("case", range(N_PAGED))
+def test_random_paged_decode_case(case):
+    """Paged GA pool with seeded page sizes, splits and contexts: the paged append
+    matches the oracle's bytes, and the paged decode equals the contiguous pool's
+    decode bit for bit (same split) and the oracle within the bars."""
+    import numpy as np
+    import torch
+    from global_attention_mimo_amd import binding as B
+    from gpu_util import to_dev
+    from test_gpu_paged import _flat, _pools
+    rng = random.Random(15485863 * case + 5)
+    ctx = [rng.choice([0, 1, 15, 16, 17, 255, 256, 2047, 2048, rng.randint(0, 6000)])
+           for _ in range(rng.randint(1, 9))]
+    page = rng.choice([16, 32, 64, 128, 256, 1024])
+    split = rng.choice([0, 32, 64, 256, 2048])
+    log(f"[case {case}] paged decode ctx={ctx} page={page} split={split}")
+    x = synth.decode_inputs(ctx, 1, seed=5000 + case)
+    table, npages = synth.paged_block_table(ctx, page, seed=case)
+    table_d = table.to("cuda")
+    kp, vp = _pools(npages, page)
+    kf, vf, base, cap = _flat(ctx)
+    rows = torch.cat([torch.arange(int(x.kv_base[b]), int(x.kv_base[b]) + c) for b, c in enumerate(ctx)]).long()
+    k_pre, v_pre = to_dev(x.k_cache[rows]), to_dev(x.v_cache[rows])
+    cu = synth.cu_from_lengths(ctx, "cuda")
+    zeros = torch.zeros(len(ctx), dtype=torch.int32, device="cuda")
+    if sum(ctx):
+        B.kv_append_paged(k_pre, v_pre, cu, zeros, kp, vp, table_d, page)
+        B.kv_append(k_pre, v_pre, cu, zeros, kf, vf, 1, kv_base=base, kv_capacity=cap)
+    torch.cuda.synchronize()
+    kp_ref, vp_ref = np.zeros_like(bits(kp)), np.zeros_like(bits(vp))
+    if sum(ctx):
+        assert orc().kv_append_paged(bits(k_pre), bits(v_pre), cu.cpu().numpy(), zeros.cpu().numpy(), kp_ref, vp_ref,
+                                     table.numpy(), page) == 0
+    assert np.array_equal(bits(kp), kp_ref) and np.array_equal(bits(vp), vp_ref), "paged append bytes"
+    q, kn, vn, sink = to_dev(x.q), to_dev(x.k_new), to_dev(x.v_new), to_dev(x.sink)
+    ctx_d = to_dev(x.ctx_lens)
+    op, lp = B.decode_paged(q, kn, vn, kp, vp, table_d, page, ctx_d, max(ctx), sink=sink, split_tokens=split)
+    of, lf = B.decode(q, kn, vn, kf, vf, ctx_d, max(ctx), 1, sink=sink, kv_base=base, split_tokens=split)
+    torch.cuda.synchronize()
+    assert torch.equal(op, of) and torch.equal(lp, lf), "paged decode differs from the contiguous pool's"
+    ro, rl = orc().decode_paged(bits(x.q), bits(x.k_new), bits(x.v_new), kp_ref, vp_ref, table.numpy(), page,
+                                x.ctx_lens.numpy(), scale=float(np.float32(synth.SOFTMAX_SCALE)),
+                                sink=sink_array(x.sink))
+    compare(op, lp, ro, rl, f"random paged decode case {case}")
