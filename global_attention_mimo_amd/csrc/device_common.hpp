@@ -120,4 +120,21 @@ __device__ __forceinline__ void interleave_lds_mfma() {
 #endif
 }
 
+// As interleave_lds_mfma, with kValu VALU instructions after each MFMA: the
+// MFMAs of one tile run on the matrix core while the wave issues another
+// tile's independent vector work in their shadow.
+template <int kMfmas, int kReads, int kAhead, int kValu>
+__device__ __forceinline__ void interleave_mfma_valu() {
+#ifndef MIMO_NO_INTERLEAVE
+    static_assert(kAhead + kMfmas - 1 >= kReads, "reads must all be placed");
+    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+    for (int i = 0; i < kMfmas; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (kAhead + i < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
+    }
+#endif
+}
+
 }  // namespace mimo

@@ -617,20 +617,41 @@ void swa_stream_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
 #pragma unroll
         for (int db = 0; db < kDv / 32; ++db) oacc[db] = f32x16{};
 
-#pragma unroll
-        for (int j = 0; j < kStreamTiles; ++j) {
-            const int kbase = q0 - kStreamLead + 32 * j;
-            // Tiles wholly before key 0 or before the band of the block's first token.
-            if (kbase + 31 < -ctx0 || kbase + 31 < q0 - (window - 1)) continue;
+        // QK^T of tile j into acc: 12 MFMAs on K fragments read from the ring.
+        auto s_tile = [&](int j, f32x16& acc) {
             const int h = hq0 - 2 * kStreamTiles + 1 + 2 * j;
             const uint16_t* klo = ring_k + ring_slot(h) * (kSlotKeys * kKStride);
             const uint16_t* khi = ring_k + ring_slot(h + 1) * (kSlotKeys * kKStride);
             const uint16_t* krow = (r32 < 16 ? klo : khi) + ksrc_off;
-            f32x16 sacc = f32x16{};
+            acc = f32x16{};
 #pragma unroll
             for (int s = 0; s < kDqk / 16; ++s)
-                sacc = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(krow + 16 * s), qf[s], sacc);
+                acc = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(krow + 16 * s), qf[s], acc);
+        };
+        // Pipelined (the plain kernel): tile j+1's QK^T is issued between the
+        // exps of tile j (one MFMA, one K read and five VALU instructions at a
+        // time), so the matrix core works while the wave runs tile j's
+        // softmax.  The chunked kernel, whose cache addressing leaves no room
+        // for the second score tile (it spilled, 4% slower), issues each
+        // tile's QK^T at the top of its own step.  Tiles wholly outside the
+        // band (only near a sequence's start) are computed and masked: their
+        // slots hold zeros or earlier keys, so every score is finite.
+        constexpr bool kPipe = !CHUNK;
+        f32x16 sa, sb;
+        if constexpr (kPipe) {
+            s_tile(0, sa);
             interleave_lds_mfma<kDqk / 16, kDqk / 16, MIMO_STREAM_S_AHEAD, 1>();
+        }
+#pragma unroll
+        for (int j = 0; j < kStreamTiles; ++j) {
+            f32x16& sacc = (kPipe && (j & 1)) ? sb : sa;
+            f32x16& snext = (j & 1) ? sa : sb;
+            if constexpr (!kPipe) {
+                s_tile(j, sacc);
+                interleave_lds_mfma<kDqk / 16, kDqk / 16, MIMO_STREAM_S_AHEAD, 1>();
+            }
+            const int kbase = q0 - kStreamLead + 32 * j;
+            const int h = hq0 - 2 * kStreamTiles + 1 + 2 * j;
 
             // Mask unless every key of the tile is in every token's band: key
             // offset 8*(r/4) + (r%4) + 4*hh is kept when max(0, tok-(W-1)) <= key <= tok.
@@ -659,6 +680,7 @@ void swa_stream_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
                 m_run = m_cand;
             }
             const float neg_m = -m_run;
+            if (kPipe && j + 1 < kStreamTiles) s_tile(j + 1, snext);
             float rs = 0.0f;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -668,6 +690,7 @@ void swa_stream_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
             const bf16x8 p0 = pack_bf16x8(sacc[0], sacc[1], sacc[2], sacc[3], sacc[4], sacc[5], sacc[6], sacc[7]);
             const bf16x8 p1 =
                 pack_bf16x8(sacc[8], sacc[9], sacc[10], sacc[11], sacc[12], sacc[13], sacc[14], sacc[15]);
+            if (kPipe && j + 1 < kStreamTiles) interleave_mfma_valu<kDqk / 16, kDqk / 16, MIMO_STREAM_S_AHEAD, 5>();
             l_run += rs;
             const uint16_t* vlo = ring_v + ring_slot(h) * (kSlotKeys * kVStride) + vsrc_off;
             const uint16_t* vhi = ring_v + ring_slot(h + 1) * (kSlotKeys * kVStride) + vsrc_off;
