@@ -12,7 +12,8 @@ backward on seeded ragged batches (gradient bars of the backward tests), and
 the fused decode + append against decode followed by append (bit for bit),
 some GA sequences with no room left for the new token; and the paged GA pool
 (page sizes 16-1024, splits 32-2048, contexts to 6000) against the oracle and
-bit for bit against the contiguous pool.
+bit for bit against the contiguous pool; and the FP8 E4M3 pool (append codes
+bit for bit, decode within the bars).
 """
 import random
 
@@ -171,3 +172,50 @@ def test_random_paged_decode_case(case):
                                 x.ctx_lens.numpy(), scale=float(np.float32(synth.SOFTMAX_SCALE)),
                                 sink=sink_array(x.sink))
     compare(op, lp, ro, rl, f"random paged decode case {case}")
+
+
+N_FP8 = 6
+
+
+@pytest.mark.parametrize("case", range(N_FP8))
+def test_random_fp8_decode_case(case):
+    """FP8 E4M3 GA pool over seeded contexts and splits: the quantising append
+    matches the oracle's codes bit for bit, the decode the oracle within the bars."""
+    import numpy as np
+    import torch
+    from global_attention_mimo_amd import binding as B
+    from gpu_util import to_dev
+    from test_gpu_fp8 import K_SCALE, V_SCALE, _pools
+    rng = random.Random(32452843 * case + 7)
+    ctx = [rng.choice([0, 1, 31, 32, 33, 255, 256, rng.randint(0, 4000)]) for _ in range(rng.randint(1, 8))]
+    split = rng.choice([0, 32, 96, 256, 1024])
+    log(f"[case {case}] FP8 decode ctx={ctx} split={split}")
+    lengths = [max(c, 1) for c in ctx]
+    x = synth.prefill_inputs(lengths, seed=6000 + case)
+    d = synth.decode_inputs(ctx, 1, seed=7000 + case)
+    sc, s = _sink(rng, d)
+    caps = [c + 2 for c in lengths]
+    base = np.concatenate([[0], np.cumsum(caps)[:-1]]).astype(np.int64)
+    rows = int(sum(caps))
+    kc, vc = _pools(rows)
+    kr, vr = np.zeros((rows, 4, 192), np.uint8), np.zeros((rows, 4, 128), np.uint8)
+    ks, vs = torch.tensor(K_SCALE, device="cuda"), torch.tensor(V_SCALE, device="cuda")
+    base_d, cap_d = torch.tensor(base, device="cuda"), torch.tensor(caps, dtype=torch.int64, device="cuda")
+    cached = np.asarray(ctx, np.int32)
+    cu = x.cu_seqlens.numpy()
+    pre = np.concatenate([np.arange(cu[b], cu[b] + c) for b, c in enumerate(ctx)]).astype(np.int64)
+    cu_pre = np.concatenate([[0], np.cumsum(ctx)]).astype(np.int32)
+    zeros = np.zeros(len(ctx), np.int32)
+    if sum(ctx):
+        B.kv_append_fp8(to_dev(x.k[pre]), to_dev(x.v[pre]), torch.tensor(cu_pre, device="cuda"),
+                        torch.tensor(zeros, device="cuda"), kc, vc, base_d, cap_d, ks, vs)
+        assert orc().kv_append_fp8(bits(x.k[pre]), bits(x.v[pre]), cu_pre, zeros, kr, vr, base,
+                                   np.asarray(caps, np.int64), K_SCALE, V_SCALE) == 0
+    sd = d.sink if isinstance(s, str) else s
+    out, lse = B.decode_fp8(to_dev(d.q), to_dev(d.k_new), to_dev(d.v_new), kc, vc, base_d, ks, vs,
+                            torch.tensor(cached, device="cuda"), max(ctx), sink=to_dev(sd), split_tokens=split)
+    torch.cuda.synchronize()
+    assert np.array_equal(kc.cpu().numpy(), kr) and np.array_equal(vc.cpu().numpy(), vr), "FP8 append codes"
+    ro, rl = orc().decode_fp8(bits(d.q), bits(d.k_new), bits(d.v_new), kr, vr, base, K_SCALE, V_SCALE, cached,
+                              scale=SCALE, sink=sink_array(sd))
+    compare(out, lse, ro, rl, f"random FP8 decode case {case} (sink {sc})")
