@@ -22,6 +22,37 @@ namespace {
 constexpr int kDqk = 192;
 constexpr int kDv = 128;
 
+// Packed token, chunk (unit) within the token, and owning sequence of this
+// thread, for a flat grid of per_tok threads per token.  The 64-bit division
+// and the search for the sequence (the last b with cu_newlens[b] <= token) run
+// once per wave on the wave's first token, in scalar registers; a thread's
+// token lies at most a few tokens past it, reached by stepping over the
+// sequences that end before it (empty ones included).
+struct TokSeq {
+    int64_t tok;
+    int c;
+    int b;
+};
+__device__ __forceinline__ TokSeq locate(const int32_t* __restrict__ cu_newlens, int batch, int per_tok) {
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int64_t base = (int64_t)blockIdx.x * blockDim.x + (int64_t)w * 64;
+    const int64_t tok0 = base / per_tok;
+    const int local = (int)(base - tok0 * per_tok) + (int)(threadIdx.x & 63);
+    const int dt = local / per_tok;
+    TokSeq r;
+    r.tok = tok0 + dt;
+    r.c = local - dt * per_tok;
+    int lo = 0, hi = batch - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cu_newlens[mid] <= tok0) lo = mid; else hi = mid - 1;
+    }
+    int b = lo;
+    while (b + 1 < batch && cu_newlens[b + 1] <= r.tok) ++b;
+    r.b = b;
+    return r;
+}
+
 __global__ __launch_bounds__(256) void kv_append_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const int32_t* __restrict__ cu_newlens,
     const int32_t* __restrict__ ctx_lens, int batch, int total_new, uint16_t* __restrict__ k_cache,
@@ -29,17 +60,11 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     int hkv, int ring, int swa, const int32_t* __restrict__ block_table, int max_blocks, int page_shift,
     long long num_pages) {
     const int kchunks = hkv * (kDqk / 8), per_tok = hkv * ((kDqk + kDv) / 8);
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t tok = idx / per_tok;
-    const int c = (int)(idx % per_tok);
+    const TokSeq ts = locate(cu_newlens, batch, per_tok);
+    const int64_t tok = ts.tok;
+    const int c = ts.c;
     if (tok >= total_new) return;
-    // Sequence owning packed token `tok`: the last b with cu_newlens[b] <= tok.
-    int lo = 0, hi = batch - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (cu_newlens[mid] <= tok) lo = mid; else hi = mid - 1;
-    }
-    const int b = lo;
+    const int b = ts.b;
     const int n = cu_newlens[b + 1] - cu_newlens[b];
     const int64_t ctx = ctx_lens[b];
     const int64_t pos = ctx + (tok - cu_newlens[b]);
@@ -76,16 +101,11 @@ __global__ __launch_bounds__(256) void kv_append_fp8_kernel(
     uint8_t* __restrict__ v_cache, const int64_t* __restrict__ kv_base, const int64_t* __restrict__ kv_capacity,
     const float* __restrict__ k_scale, const float* __restrict__ v_scale, int hkv) {
     const int kunits = hkv * (kDqk / 8), per_tok = hkv * ((kDqk + kDv) / 8);
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t tok = idx / per_tok;
-    const int c = (int)(idx % per_tok);
+    const TokSeq ts = locate(cu_newlens, batch, per_tok);
+    const int64_t tok = ts.tok;
+    const int c = ts.c;
     if (tok >= total_new) return;
-    int lo = 0, hi = batch - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (cu_newlens[mid] <= tok) lo = mid; else hi = mid - 1;
-    }
-    const int b = lo;
+    const int b = ts.b;
     const int n = cu_newlens[b + 1] - cu_newlens[b];
     const int64_t ctx = ctx_lens[b];
     if (ctx + n > kv_capacity[b]) return;  // the whole sequence is refused
