@@ -23,7 +23,8 @@ constexpr int kDqk = 192;
 constexpr int kDv = 128;
 
 // Packed token, chunk (unit) within the token, and owning sequence of this
-// thread, for a flat grid of per_tok threads per token.  The 64-bit division
+// thread, for a flat grid of per_tok threads per token (the FP8 append, whose
+// per-element division makes per-thread index arithmetic costly).  The 64-bit division
 // and the search for the sequence (the last b with cu_newlens[b] <= token) run
 // once per wave on the wave's first token, in scalar registers; a thread's
 // token lies at most a few tokens past it, reached by stepping over the
@@ -59,12 +60,21 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     uint16_t* __restrict__ v_cache, const int64_t* __restrict__ kv_base, const int64_t* __restrict__ kv_capacity,
     int hkv, int ring, int swa, const int32_t* __restrict__ block_table, int max_blocks, int page_shift,
     long long num_pages) {
+    // Per-thread lookup: this kernel moves 16 bytes per thread and is bound by
+    // its chain of dependent loads, which the once-per-wave scalar search of
+    // locate() lengthens (132 -> 180 us per bulk append in the layer stack).
     const int kchunks = hkv * (kDqk / 8), per_tok = hkv * ((kDqk + kDv) / 8);
-    const TokSeq ts = locate(cu_newlens, batch, per_tok);
-    const int64_t tok = ts.tok;
-    const int c = ts.c;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t tok = idx / per_tok;
+    const int c = (int)(idx % per_tok);
     if (tok >= total_new) return;
-    const int b = ts.b;
+    // Sequence owning packed token `tok`: the last b with cu_newlens[b] <= tok.
+    int lo = 0, hi = batch - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cu_newlens[mid] <= tok) lo = mid; else hi = mid - 1;
+    }
+    const int b = lo;
     const int n = cu_newlens[b + 1] - cu_newlens[b];
     const int64_t ctx = ctx_lens[b];
     const int64_t pos = ctx + (tok - cu_newlens[b]);
