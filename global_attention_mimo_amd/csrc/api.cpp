@@ -52,7 +52,9 @@ int check_dims(const mimo_attn_dims* d, int layer_type, int min_window) {
     if (d->head_dim_qk != 192 || d->head_dim_v != 128)
         return fail(MIMO_ERR_UNSUPPORTED, "kernels need head_dim_qk 192 and head_dim_v 128 (got %d/%d)",
                     d->head_dim_qk, d->head_dim_v);
-    if (d->num_kv_heads > kMaxGridYZ) return fail(MIMO_ERR_UNSUPPORTED, "too many KV heads");
+    // Grids carry KV heads on y and the GA combine carries query heads on y.
+    if (d->num_q_heads > kMaxGridYZ)
+        return fail(MIMO_ERR_UNSUPPORTED, "num_q_heads %d above %d", d->num_q_heads, kMaxGridYZ);
     if (layer_type == MIMO_LAYER_SWA && d->sliding_window < min_window)
         return fail(MIMO_ERR_INVALID_ARG, "sliding_window %d is below %d", d->sliding_window, min_window);
     if (!std::isfinite(d->softmax_scale) || !std::isfinite(d->value_scale))

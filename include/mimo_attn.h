@@ -31,14 +31,16 @@
  *       out [T][Hq][128]     lse [T][Hq] (fp32)  sink [Hq] (fp32)
  *     Every tensor must be 16-byte aligned.
  *   - The caller allocates and owns every buffer (caches, workspace included).
- *     The library allocates nothing, keeps no state between calls, never
- *     synchronises the device and never writes ctx_lens.
+ *     The library allocates nothing, never synchronises the device and never
+ *     writes ctx_lens.  Its only state between calls is a per-thread copy of
+ *     the last failure's message (mimo_last_error); no call reads it.
  *   - Work is enqueued asynchronously on `stream` (NULL = the null stream).
  *   - Misuse detectable on the host returns a status BEFORE anything is
  *     enqueued.  A failed launch returns MIMO_ERR_HIP.  mimo_last_error()
  *     gives a message for the calling thread's most recent failure.
  *   - Supported shapes: head_dim_qk == 192, head_dim_v == 128 and
- *     num_q_heads == 16 * num_kv_heads; anything else is MIMO_ERR_UNSUPPORTED.
+ *     num_q_heads == 16 * num_kv_heads <= 65535; anything else is
+ *     MIMO_ERR_UNSUPPORTED.
  *   - Inputs must be finite.  Device-resident preconditions (monotone
  *     cu_seqlens, ctx_lens within the stated bounds) are not checked on the
  *     device except where an entry point says so.

@@ -61,6 +61,45 @@ def compare(out_gpu, lse_gpu, out_ref, lse_ref, what: str):
     return mx, mean, lmx
 
 
+class ParityTally:
+    """Element-wise comparison of a whole configuration, chunk by chunk: the
+    max-abs and mean-abs bars apply to all compared elements together, so the
+    chunks' sums are pooled before the mean is taken."""
+
+    def __init__(self, what: str):
+        self.what = what
+        self.max = 0.0
+        self.sum = 0.0
+        self.count = 0
+        self.lse_max = 0.0
+        self.rows = 0
+
+    def add(self, out_gpu, lse_gpu, out_ref, lse_ref, label: str = ""):
+        o = out_gpu.detach().float().cpu().numpy().astype(np.float64)
+        assert o.shape == out_ref.shape, (o.shape, out_ref.shape)
+        assert np.isfinite(o).all(), f"{self.what} {label}: non-finite output"
+        d = np.abs(o - out_ref)
+        self.max = max(self.max, float(d.max()))
+        self.sum += float(d.sum())
+        self.count += d.size
+        self.rows += o.shape[0]
+        if lse_gpu is not None:
+            l = lse_gpu.detach().cpu().numpy().astype(np.float64)
+            assert np.isfinite(l).all(), f"{self.what} {label}: non-finite LSE"
+            self.lse_max = max(self.lse_max, float(np.abs(l - lse_ref).max()))
+        log(f"[parity] {self.what} {label}: chunk max {float(d.max()):.3e} mean {float(d.mean()):.3e}")
+
+    def check(self):
+        mean = self.sum / max(self.count, 1)
+        log(f"[parity] {self.what}: {self.rows} rows, {self.count} elements: out max {self.max:.3e} "
+            f"mean {mean:.3e} lse max {self.lse_max:.3e}")
+        assert self.count > 0
+        assert self.max <= OUT_MAX, f"{self.what}: out max-abs {self.max:.3e} > {OUT_MAX}"
+        assert mean <= OUT_MEAN, f"{self.what}: out mean-abs {mean:.3e} > {OUT_MEAN}"
+        assert self.lse_max <= LSE_MAX, f"{self.what}: lse max-abs {self.lse_max:.3e} > {LSE_MAX}"
+        return self.max, mean, self.lse_max
+
+
 def gpu_prefill(x, layer_type, window=129, value_scale=1.0, sink="inputs", lse=True, stream=None):
     s = x.sink if isinstance(sink, str) else sink
     dims = B.make_dims(sliding_window=window, value_scale=value_scale)

@@ -318,18 +318,21 @@ def _append_positions(orc, kc, vc, k_tok, v_tok, chunks, layer_type, window=129,
 
 def pin_decode_equals_prefill_row(orc):
     """Cache positions 0..p-1 (bulk, then single tokens), decode token p: equals
-    row p of prefill over the first p+1 tokens."""
+    row p of prefill over the first p+1 tokens.  SWA rings of W-1 slots for
+    windows 300, 129, 17 and 2 (a ring reader or writer that assumed 128 slots
+    reads the wrong positions at every window but 129)."""
     L = 300
     x = _make([L], seed=12)
     sc = float(np.float32(synth.SOFTMAX_SCALE))
     kb, vb, qb = _bits(x.k), _bits(x.v), _bits(x.q)
     sink = x.sink.numpy()
-    for lt in (SWA, GA):
-        ofull, lfull = _run_prefill(orc, x, lt, 129, sc)
-        for p in (0, 1, 127, 128, 129, 200, 299):
+    for lt, W in ((SWA, 300), (SWA, 129), (SWA, 17), (SWA, 2), (GA, 129)):
+        R = W - 1
+        ofull, lfull = _run_prefill(orc, x, lt, W, sc)
+        for p in sorted({0, 1, R - 1, R, R + 1, 127, 128, 129, 200, 299} & set(range(1 if R == 0 else 0, L))):
             if lt == SWA:
-                kc = np.zeros((1, 128, 4, 192), np.uint16)
-                vc = np.zeros((1, 128, 4, 128), np.uint16)
+                kc = np.zeros((1, R, 4, 192), np.uint16)
+                vc = np.zeros((1, R, 4, 128), np.uint16)
                 base = cap = None
             else:
                 kc = np.zeros((L + 5, 4, 192), np.uint16)
@@ -338,32 +341,34 @@ def pin_decode_equals_prefill_row(orc):
                 cap = np.array([L], np.int64)
             chunks = [p // 2, p - p // 2 - min(3, p - p // 2)] + [1] * min(3, p - p // 2)
             chunks = [c for c in chunks if c > 0]
-            _append_positions(orc, kc, vc, kb, vb, chunks, lt, 129, base, cap)
+            _append_positions(orc, kc, vc, kb, vb, chunks, lt, W, base, cap)
             o, l = orc.decode(qb[p:p + 1], kb[p:p + 1], vb[p:p + 1], kc, vc, np.array([p], np.int32),
-                              layer_type=lt, window=129, scale=sc, sink=sink, kv_base=base)
-            _close(o[0], ofull[p], 1e-13, f"decode vs prefill out lt={lt} p={p}")
-            _close(l[0], lfull[p], 1e-13, f"decode vs prefill lse lt={lt} p={p}")
+                              layer_type=lt, window=W, scale=sc, sink=sink, kv_base=base)
+            _close(o[0], ofull[p], 1e-13, f"decode vs prefill out lt={lt} W={W} p={p}")
+            _close(l[0], lfull[p], 1e-13, f"decode vs prefill lse lt={lt} W={W} p={p}")
 
 
 def pin_ring_contents(orc):
-    """After positions 0..p-1 are appended, ring slot r holds the unique
-    position t = r (mod 128) with p-128 <= t <= p-1."""
-    R = 128
-    for p, chunks in ((5, [5]), (128, [100, 28]), (300, [250, 1, 1, 48]), (129, [129])):
-        tok = np.zeros((p, 1, 2), np.uint16)
-        tok[:, 0, 0] = np.arange(p) + 1  # position tag (non-zero)
-        kc = np.zeros((1, R, 1, 2), np.uint16)
-        vc = np.zeros((1, R, 1, 2), np.uint16)
-        pos = 0
-        for n in chunks:
-            st = orc.kv_append(tok[pos:pos + n], tok[pos:pos + n], np.array([0, n], np.int32),
-                               np.array([pos], np.int32), kc, vc, layer_type=SWA, window=R + 1)
-            assert st == oracle.OK
-            pos += n
-        for r in range(R):
-            want = [t for t in range(max(0, p - R), p) if t % R == r]
-            got = int(kc[0, r, 0, 0])
-            assert got == (want[0] + 1 if want else 0), f"ring slot {r} after {p}: {got}"
+    """After positions 0..p-1 are appended, ring slot r of a ring of R = W-1
+    slots holds the unique position t = r (mod R) with p-R <= t <= p-1 (rings
+    of 299, 128, 16 and 1 slots, i.e. windows 300, 129, 17 and 2)."""
+    for R in (299, 128, 16, 1):
+        for p, chunks in ((5, [5]), (R, [R]), (R + 1, [R + 1]), (128, [100, 28]), (300, [250, 1, 1, 48]),
+                          (129, [129]), (2 * R + 3, [R, 2, R + 1])):
+            tok = np.zeros((p, 1, 2), np.uint16)
+            tok[:, 0, 0] = np.arange(p) + 1  # position tag (non-zero)
+            kc = np.zeros((1, R, 1, 2), np.uint16)
+            vc = np.zeros((1, R, 1, 2), np.uint16)
+            pos = 0
+            for n in chunks:
+                st = orc.kv_append(tok[pos:pos + n], tok[pos:pos + n], np.array([0, n], np.int32),
+                                   np.array([pos], np.int32), kc, vc, layer_type=SWA, window=R + 1)
+                assert st == oracle.OK
+                pos += n
+            for r in range(R):
+                want = [t for t in range(max(0, p - R), p) if t % R == r]
+                got = int(kc[0, r, 0, 0])
+                assert got == (want[0] + 1 if want else 0), f"ring slot {r} of {R} after {p}: {got}"
 
 
 def pin_ga_capacity(orc):
@@ -378,9 +383,10 @@ def pin_ga_capacity(orc):
     assert st == oracle.OK and kc[4:8].all() and not kc[:4].any() and not kc[8:].any()
 
 
-def _caches(layer_type, batch, rows):
+def _caches(layer_type, batch, rows, window=129):
     if layer_type == SWA:
-        return np.zeros((batch, 128, 4, 192), np.uint16), np.zeros((batch, 128, 4, 128), np.uint16)
+        R = window - 1
+        return np.zeros((batch, R, 4, 192), np.uint16), np.zeros((batch, R, 4, 128), np.uint16)
     return np.zeros((rows, 4, 192), np.uint16), np.zeros((rows, 4, 128), np.uint16)
 
 
@@ -406,7 +412,8 @@ def pin_chunk_without_cache_is_prefill(orc):
 def pin_chunk_continues_prefill(orc):
     """Sequences of a ragged batch with their first c_b tokens cached (appended
     to the ring or pool) and the rest passed as one packed chunk: the chunk's
-    rows equal rows c_b..L_b-1 of prefill over the whole sequences."""
+    rows equal rows c_b..L_b-1 of prefill over the whole sequences.  SWA over
+    rings of W-1 slots for windows 300, 129, 17 and 2."""
     lengths = [300, 170, 64, 129, 260]
     cached = [0, 1, 63, 128, 131]
     x = _make(lengths, seed=31)
@@ -416,9 +423,9 @@ def pin_chunk_continues_prefill(orc):
     rest = [L - c for L, c in zip(lengths, cached)]
     starts = [int(cu[b]) + cached[b] for b in range(len(lengths))]
     cu_new = np.concatenate([[0], np.cumsum(rest)]).astype(np.int32)
-    for lt in (SWA, GA):
-        of, lf = _run_prefill(orc, x, lt, 129, sc)
-        kc, vc = _caches(lt, len(lengths), sum(lengths) + 7)
+    for lt, W in ((SWA, 300), (SWA, 129), (SWA, 17), (SWA, 2), (GA, 129)):
+        of, lf = _run_prefill(orc, x, lt, W, sc)
+        kc, vc = _caches(lt, len(lengths), sum(lengths) + 7, W)
         base = cap = None
         if lt == GA:
             base = np.concatenate([[5], 5 + np.cumsum(lengths)[:-1]]).astype(np.int64)
@@ -426,14 +433,14 @@ def pin_chunk_continues_prefill(orc):
         pre_cu = np.concatenate([[0], np.cumsum(cached)]).astype(np.int32)
         pre_k, pre_v = _pack(kb, cached, cu[:-1]), _pack(vb, cached, cu[:-1])
         st = orc.kv_append(pre_k, pre_v, pre_cu, np.zeros(len(lengths), np.int32), kc, vc, layer_type=lt,
-                           kv_base=base, kv_capacity=cap)
+                           window=W, kv_base=base, kv_capacity=cap)
         assert st == oracle.OK
         o, l = orc.prefill_chunk(_pack(qb, rest, starts), _pack(kb, rest, starts), _pack(vb, rest, starts), cu_new,
-                                 kc, vc, np.asarray(cached, np.int32), layer_type=lt, scale=sc,
+                                 kc, vc, np.asarray(cached, np.int32), layer_type=lt, window=W, scale=sc,
                                  sink=x.sink.numpy(), kv_base=base)
         rows = np.concatenate([np.arange(s, s + n) for s, n in zip(starts, rest)])
-        _close(o, of[rows], 1e-13, f"chunk vs prefill out lt={lt}")
-        _close(l, lf[rows], 1e-13, f"chunk vs prefill lse lt={lt}")
+        _close(o, of[rows], 1e-13, f"chunk vs prefill out lt={lt} W={W}")
+        _close(l, lf[rows], 1e-13, f"chunk vs prefill lse lt={lt} W={W}")
 
 
 def pin_chunk_of_one_token_is_decode(orc):

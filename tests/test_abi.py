@@ -68,6 +68,7 @@ def prefill_call(L, dims=None, layer=0, q=FAKE, k=FAKE, v=FAKE, cu=FAKE, nseq=1,
     (dict(dims=B.make_dims(head_dim_qk=128)), B.MIMO_ERR_UNSUPPORTED),
     (dict(dims=B.make_dims(head_dim_v=192)), B.MIMO_ERR_UNSUPPORTED),
     (dict(dims=B.make_dims(num_kv_heads=0)), B.MIMO_ERR_INVALID_ARG),
+    (dict(dims=B.make_dims(num_q_heads=16 * 4096, num_kv_heads=4096)), B.MIMO_ERR_UNSUPPORTED),
     (dict(dims=B.make_dims(sliding_window=0)), B.MIMO_ERR_INVALID_ARG),
     (dict(dims=B.make_dims(softmax_scale=float("nan"))), B.MIMO_ERR_INVALID_ARG),
     (dict(dims=B.make_dims(value_scale=float("inf"))), B.MIMO_ERR_INVALID_ARG),

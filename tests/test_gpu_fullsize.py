@@ -1,8 +1,19 @@
-"""Full-size parity at the benchmark's launch configurations, on sampled outputs.
+"""Full-size parity at the benchmark's launch configurations.
 
-The GPU computes every output of the workload; the fp64 oracle recomputes the
-sampled rows one by one from host copies of the same buffers.  Bars as in
-gpu_util (bf16 out max-abs 2e-2 / mean-abs 2e-3, LSE 1e-3).
+The GPU computes every output of each workload; the fp64 oracle recomputes, from
+host copies of the same buffers:
+  * SWA prefill 4 x 8192: every token and head (the whole configuration);
+  * GA prefill 1 x 32768: 304 query rows -- one in every 128-token stretch of
+    the sequence (cycling through the first, last and inner tokens of 16-token
+    query blocks, so every dispatch round of the heaviest-first schedule is
+    visited) plus three whole 16-token blocks (first, middle, last);
+  * decode B = 128 with contexts U[4096, 262144]: every sequence, GA over the
+    bf16 pool and SWA over the ring;
+  * the 48-layer hybrid stack: four layers (two SWA, two GA), every sequence,
+    sampled prefill rows and the whole last decode step, and the caches those
+    layers hold, byte for byte, against the oracle's own appends.
+Bars as in gpu_util (bf16 out max-abs 2e-2 / mean-abs 2e-3 over all compared
+elements of a configuration, LSE 1e-3).
 """
 import numpy as np
 import pytest
@@ -11,7 +22,7 @@ import torch
 from global_attention_mimo_amd import binding as B
 from global_attention_mimo_amd import synth
 from global_attention_mimo_amd.stack import HybridStack
-from gpu_util import bits, compare, log, orc
+from gpu_util import ParityTally, bits, compare, log, orc
 
 pytestmark = pytest.mark.gpu
 SWA, GA = 0, 1
@@ -27,55 +38,75 @@ def run_prefill(x, layer_type, nseq, max_len):
     return out, lse
 
 
-def oracle_rows(x, layer_type, rows):
-    return orc().prefill(bits(x.q), bits(x.k), bits(x.v), x.cu_seqlens.cpu().numpy(), layer_type=layer_type,
-                         scale=SCALE, sink=x.sink.cpu().numpy(), rows=np.asarray(rows, np.int64))
+def ga_prefill_rows(L=32768):
+    """One row per 128-token stretch, its offset cycling over first/last/inner
+    tokens of a 16-token block, plus whole blocks at the start, middle and end."""
+    offsets = (0, 15, 16, 31, 47, 64, 100, 127)
+    rows = {128 * k + offsets[k % len(offsets)] for k in range(L // 128)}
+    for b0 in (0, L // 2, L - 16):
+        rows.update(range(b0, b0 + 16))
+    return np.array(sorted(rows), np.int64)
 
 
-def test_swa_prefill_4x8192_sampled():
-    log("[case] SWA prefill 4x8192 (seed 0), sampled rows")
+@pytest.mark.timeout(600)
+def test_swa_prefill_4x8192_full():
+    log("[case] SWA prefill 4x8192 (seed 0), every token")
     x = synth.prefill_inputs([8192] * 4, seed=0, device=DEV)
     out, lse = run_prefill(x, SWA, 4, 8192)
-    rows = [s * 8192 + p for s in range(4) for p in (0, 1, 127, 128, 129, 130, 4321, 8190, 8191)]
-    ro, rl = oracle_rows(x, SWA, rows)
-    idx = torch.tensor(rows, device=DEV)
-    compare(out[idx], lse[idx], ro, rl, "SWA 4x8192 sampled rows")
-    assert torch.isfinite(lse).all()
+    qb, kb, vb = bits(x.q), bits(x.k), bits(x.v)
+    cu = x.cu_seqlens.cpu().numpy()
+    tally = ParityTally("SWA prefill 4x8192")
+    for s in range(4):
+        rows = np.arange(s * 8192, (s + 1) * 8192, dtype=np.int64)
+        ro, rl = orc().prefill(qb, kb, vb, cu, layer_type=SWA, scale=SCALE, sink=x.sink.cpu().numpy(), rows=rows)
+        tally.add(out[s * 8192:(s + 1) * 8192], lse[s * 8192:(s + 1) * 8192], ro, rl, f"sequence {s}")
+    tally.check()
+    assert tally.rows == 32768
 
 
-def test_ga_prefill_1x32768_sampled():
-    log("[case] GA prefill 1x32768 (seed 0), sampled rows")
+@pytest.mark.timeout(600)
+def test_ga_prefill_1x32768_spread_rows():
+    rows = ga_prefill_rows()
+    log(f"[case] GA prefill 1x32768 (seed 0), {len(rows)} rows")
     x = synth.prefill_inputs([32768], seed=0, device=DEV)
     out, lse = run_prefill(x, GA, 1, 32768)
-    g = np.random.default_rng(0)
-    rows = sorted(set([0, 1, 2, 15, 16, 63, 64, 4095, 4096, 16383, 32766, 32767] + list(g.integers(0, 32768, 6))))
-    ro, rl = oracle_rows(x, GA, rows)
-    idx = torch.tensor(rows, device=DEV)
-    compare(out[idx], lse[idx], ro, rl, "GA 1x32768 sampled rows")
     assert torch.isfinite(lse).all()
+    qb, kb, vb = bits(x.q), bits(x.k), bits(x.v)
+    cu = x.cu_seqlens.cpu().numpy()
+    tally = ParityTally("GA prefill 1x32768")
+    for part in np.array_split(rows, 4):
+        ro, rl = orc().prefill(qb, kb, vb, cu, layer_type=GA, scale=SCALE, sink=x.sink.cpu().numpy(), rows=part)
+        idx = torch.tensor(part, device=DEV)
+        tally.add(out[idx], lse[idx], ro, rl, f"rows {part[0]}..{part[-1]}")
+    tally.check()
+    assert tally.rows >= 256
 
 
-def test_decode_b128_long_contexts():
+@pytest.mark.timeout(900)
+def test_decode_b128_long_contexts_all_sequences():
     """Decode step for 128 sequences with contexts U[4096, 262144] (seed 0): GA over
-    the full bf16 pool (default split) for sampled sequences, SWA over the ring for all."""
+    the full bf16 pool (default split) and SWA over the ring, every sequence."""
     ctx = synth.long_context_lengths(128, seed=0)
-    log(f"[case] GA decode B=128 ctx U[4096,262144] total {sum(ctx)} tokens")
+    log(f"[case] GA decode B=128 ctx U[4096,262144] total {sum(ctx)} tokens, every sequence")
     x = synth.decode_inputs(ctx, GA, seed=0, device=DEV, headroom=4)
     out, lse = B.decode(x.q, x.k_new, x.v_new, x.k_cache, x.v_cache, x.ctx_lens, max(ctx) + 4, GA, sink=x.sink,
                         kv_base=x.kv_base)
     torch.cuda.synchronize()
     assert torch.isfinite(lse).all()
-    order = np.argsort(ctx)
-    pick = [int(order[0]), int(order[-1]), int(order[64])]
     base = x.kv_base.cpu().numpy()
-    for b in pick:
+    sink = x.sink.cpu().numpy()
+    qb, knb, vnb = bits(x.q), bits(x.k_new), bits(x.v_new)
+    tally = ParityTally("GA decode B=128")
+    for b in range(len(ctx)):
         c = ctx[b]
         kc = bits(x.k_cache[base[b]:base[b] + c])
         vc = bits(x.v_cache[base[b]:base[b] + c])
-        ro, rl = orc().decode(bits(x.q[b:b + 1]), bits(x.k_new[b:b + 1]), bits(x.v_new[b:b + 1]), kc, vc,
-                              np.array([c], np.int32), layer_type=GA, scale=SCALE, sink=x.sink.cpu().numpy(),
-                              kv_base=np.zeros(1, np.int64))
-        compare(out[b:b + 1], lse[b:b + 1], ro, rl, f"GA decode seq {b} ctx {c}")
+        ro, rl = orc().decode(qb[b:b + 1], knb[b:b + 1], vnb[b:b + 1], kc, vc, np.array([c], np.int32),
+                              layer_type=GA, scale=SCALE, sink=sink, kv_base=np.zeros(1, np.int64))
+        tally.add(out[b:b + 1], lse[b:b + 1], ro, rl, f"seq {b} ctx {c}")
+        del kc, vc
+    tally.check()
+    assert tally.rows == 128
     del x
     torch.cuda.empty_cache()
     log("[case] SWA decode B=128 ring")
@@ -87,39 +118,46 @@ def test_decode_b128_long_contexts():
     compare(out, lse, ro, rl, "SWA decode B=128 all sequences")
 
 
+@pytest.mark.timeout(900)
 def test_hybrid_stack_48_layers():
     """48 layers (5 SWA : 1 GA), 32 ragged prompts log-uniform in [512, 32768], varlen
-    prefill + append, then 64 decode steps (attend, append).  Sampled parity on an SWA
-    and a GA layer after prefill and at the last decode step."""
+    prefill + append, then 64 decode steps (attend, append).  Layers 0 and 22 (SWA)
+    and 5 and 47 (GA) are checked for every sequence: sampled prefill rows, the
+    whole last decode step, and the caches they hold before it."""
     lengths = synth.hybrid_prompt_lengths(32, seed=0)
     st = HybridStack(lengths, decode_steps=64, device=DEV)
     log(f"[case] hybrid stack: {sum(lengths)} prompt tokens, 48 layers, 64 steps")
-    checked = {0: SWA, 5: GA}
-    # Host copies of every token appended to the checked layers' caches for the
-    # checked sequences: the oracle rebuilds those caches with its own append.
+    checked = {0: SWA, 5: GA, 22: SWA, 47: GA}
+    for layer, lt in checked.items():
+        assert st.layer_types[layer] == lt
+    # Host copies of every token appended to the checked layers' caches: the
+    # oracle rebuilds those caches with its own append.
     hist = {}
-    order = np.argsort(lengths)
-    seqs = [int(order[0]), int(order[-1])]
+    seqs = list(range(st.batch))
     cu = st.cu.cpu().numpy()
     out = torch.empty((st.total, 64, 128), dtype=torch.bfloat16, device=DEV)
     lse = torch.empty((st.total, 64), dtype=torch.float32, device=DEV)
     gen = torch.Generator(device=DEV).manual_seed(0)
     sinks = torch.randn((48, 64), generator=gen, device=DEV)
+    pre = {layer: ParityTally(f"stack prefill layer {layer}") for layer in checked}
     for layer in range(48):
         x = synth.prefill_inputs(lengths, seed=1000 + layer, device=DEV, with_sink=False)
         st.prefill_layer(layer, x.q, x.k, x.v, sinks[layer], out, lse)
         if layer in checked:
             torch.cuda.synchronize()
+            qb, kb, vb = bits(x.q), bits(x.k), bits(x.v)
+            rows = []
             for b in seqs:
                 s0, s1 = int(cu[b]), int(cu[b + 1])
-                hist[(layer, b)] = ([bits(x.k[s0:s1])], [bits(x.v[s0:s1])])
+                hist[(layer, b)] = ([kb[s0:s1]], [vb[s0:s1]])
                 L = s1 - s0
-                rows = sorted(set([0, 1, 128, 129, L // 2, L - 1]))
-                ro, rl = orc().prefill(bits(x.q[s0:s1]), bits(x.k[s0:s1]), bits(x.v[s0:s1]),
-                                       np.array([0, L], np.int32), layer_type=checked[layer], scale=SCALE,
-                                       sink=sinks[layer].cpu().numpy(), rows=np.asarray(rows, np.int64))
-                idx = torch.tensor([s0 + r for r in rows], device=DEV)
-                compare(out[idx], lse[idx], ro, rl, f"stack prefill layer {layer} seq {b} (L={L})")
+                rows += [s0 + r for r in sorted({0, 1, 15, 16, 127, 128, 129, L // 2, L - 17, L - 16, L - 1})]
+            rows = np.asarray(rows, np.int64)
+            ro, rl = orc().prefill(qb, kb, vb, cu, layer_type=checked[layer], scale=SCALE,
+                                   sink=sinks[layer].cpu().numpy(), rows=rows)
+            idx = torch.tensor(rows, device=DEV)
+            pre[layer].add(out[idx], lse[idx], ro, rl, f"{len(rows)} rows over {len(seqs)} sequences")
+            pre[layer].check()
         del x
     log("[case] hybrid stack: decode steps")
     dout = torch.empty((st.batch, 64, 128), dtype=torch.bfloat16, device=DEV)
@@ -132,45 +170,57 @@ def test_hybrid_stack_48_layers():
             vn = torch.randn((st.batch, 4, 128), generator=gen, device=DEV).to(torch.bfloat16)
             if last and layer in checked:
                 torch.cuda.synchronize()
+                lt = checked[layer]
                 c = st.caches[layer]
                 ctx = st.ctx.cpu().numpy()
-                snap = []
+                if lt == GA:
+                    # The oracle's pool: every sequence at the stack's own base rows.
+                    rows = st.pool_rows
+                    kc = np.zeros((rows, 4, 192), np.uint16)
+                    vc = np.zeros((rows, 4, 128), np.uint16)
+                    base, cap = st.kv_base.cpu().numpy(), st.kv_capacity.cpu().numpy()
+                else:
+                    kc = np.zeros((st.batch, 128, 4, 192), np.uint16)
+                    vc = np.zeros((st.batch, 128, 4, 128), np.uint16)
+                    base = cap = None
                 for b in seqs:
-                    if checked[layer] == GA:
-                        b0 = int(st.kv_base[b])
-                        gpu = (bits(c.k[b0:b0 + ctx[b]]), bits(c.v[b0:b0 + ctx[b]]))
-                        kc = np.zeros((ctx[b], 4, 192), np.uint16)
-                        vc = np.zeros((ctx[b], 4, 128), np.uint16)
-                        base, cap = np.zeros(1, np.int64), np.array([ctx[b]], np.int64)
-                    else:
-                        gpu = (bits(c.k[b:b + 1]), bits(c.v[b:b + 1]))
-                        kc = np.zeros((1, 128, 4, 192), np.uint16)
-                        vc = np.zeros((1, 128, 4, 128), np.uint16)
-                        base = cap = None
                     pos = 0
                     for kt, vt in zip(*hist[(layer, b)]):
                         n = kt.shape[0]
-                        assert orc().kv_append(kt, vt, np.array([0, n], np.int32), np.array([pos], np.int32), kc, vc,
-                                               layer_type=checked[layer], kv_base=base, kv_capacity=cap) == 0
+                        bsel = None if base is None else base[b:b + 1]
+                        csel = None if cap is None else cap[b:b + 1]
+                        kview = kc if lt == GA else kc[b:b + 1]
+                        vview = vc if lt == GA else vc[b:b + 1]
+                        assert orc().kv_append(kt, vt, np.array([0, n], np.int32), np.array([pos], np.int32), kview,
+                                               vview, layer_type=lt, kv_base=bsel, kv_capacity=csel) == 0
                         pos += n
                     assert pos == ctx[b]
-                    assert np.array_equal(gpu[0], kc) and np.array_equal(gpu[1], vc), \
-                        f"stack cache of layer {layer} seq {b} differs from the oracle's appends"
-                    snap.append((kc, vc))
+                gk, gv = bits(c.k), bits(c.v)
+                if lt == GA:
+                    for b in seqs:
+                        r0, r1 = int(base[b]), int(base[b]) + int(ctx[b])
+                        assert np.array_equal(gk[r0:r1], kc[r0:r1]) and np.array_equal(gv[r0:r1], vc[r0:r1]), \
+                            f"stack cache of layer {layer} seq {b} differs from the oracle's appends"
+                else:
+                    assert np.array_equal(gk, kc) and np.array_equal(gv, vc), \
+                        f"stack ring of layer {layer} differs from the oracle's appends"
+                log(f"[parity] stack layer {layer}: caches of all {len(seqs)} sequences equal the oracle's appends")
+                snap = (kc, vc, base)
             st.decode_layer(layer, q, kn, vn, sinks[layer], dout, dlse)
             if layer in checked:
+                kb, vb = bits(kn), bits(vn)
                 for b in seqs:
-                    hist[(layer, b)][0].append(bits(kn[b:b + 1]))
-                    hist[(layer, b)][1].append(bits(vn[b:b + 1]))
+                    hist[(layer, b)][0].append(kb[b:b + 1])
+                    hist[(layer, b)][1].append(vb[b:b + 1])
             if last and layer in checked:
                 torch.cuda.synchronize()
-                for (kc, vc), b in zip(snap, seqs):
-                    ro, rl = orc().decode(bits(q[b:b + 1]), bits(kn[b:b + 1]), bits(vn[b:b + 1]), kc, vc,
-                                          np.array([ctx[b]], np.int32), layer_type=checked[layer], scale=SCALE,
-                                          sink=sinks[layer].cpu().numpy(),
-                                          kv_base=np.zeros(1, np.int64) if checked[layer] == GA else None)
-                    compare(dout[b:b + 1], dlse[b:b + 1], ro, rl,
-                            f"stack decode step 64 layer {layer} seq {b} (ctx={ctx[b]})")
+                kc, vc, base = snap
+                ro, rl = orc().decode(bits(q), bits(kn), bits(vn), kc, vc, ctx.astype(np.int32),
+                                      layer_type=checked[layer], scale=SCALE, sink=sinks[layer].cpu().numpy(),
+                                      kv_base=base)
+                t = ParityTally(f"stack decode step 64 layer {layer}")
+                t.add(dout, dlse, ro, rl, f"all {st.batch} sequences")
+                t.check()
         st.advance()
     torch.cuda.synchronize()
     assert int(st.ctx[0]) == lengths[0] + 64

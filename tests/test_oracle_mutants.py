@@ -65,6 +65,12 @@ MUTANTS = {
     "append ring slot off by one": (
         "            size_t dst = layer_type == ORACLE_SWA ? (size_t)b * ring_slots + (size_t)(pos % ring_slots)\n",
         "            size_t dst = layer_type == ORACLE_SWA ? (size_t)b * ring_slots + (size_t)((pos + 1) % ring_slots)\n"),
+    "ring reader hard-coded to 128 slots": (
+        "    if (d->layer_type == ORACLE_SWA) row = (size_t)b * ring + (size_t)(j % ring);\n",
+        "    if (d->layer_type == ORACLE_SWA) row = (size_t)b * ring + (size_t)(j % 128);\n"),
+    "ring append hard-coded to 128 slots": (
+        "            size_t dst = layer_type == ORACLE_SWA ? (size_t)b * ring_slots + (size_t)(pos % ring_slots)\n",
+        "            size_t dst = layer_type == ORACLE_SWA ? (size_t)b * ring_slots + (size_t)(pos % 128)\n"),
     "append capacity check off by one": ("        if (layer_type == ORACLE_GA && (int64_t)ctx_lens[b] + n > kv_capacity[b]) {\n",
                                          "        if (layer_type == ORACLE_GA && (int64_t)ctx_lens[b] + n >= kv_capacity[b]) {\n"),
     "paged row inside the page from the block index": (
