@@ -29,9 +29,6 @@ int ok() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-constexpr int kDefaultSplit = 2048;
-constexpr int kMinDefaultSplit = 256;
-constexpr int kMinSplitGroups = 256;
 constexpr int kMaxGridYZ = 65535;
 
 // Shape checks shared by every entry point.  min_window: 1 for prefill
@@ -88,19 +85,12 @@ int check_pages(const mimo_kv_pages* pg, mimo::PageTable* out) {
     return MIMO_OK;
 }
 
-// GA keys per split workgroup.  Default: the largest of 2048, 1024, 512 and 256
-// keys that still gives at least kMinSplitGroups workgroups (one per compute
-// unit of the part) for batch x max_ctx, so a few long sequences spread over
-// the chip while large batches keep long splits (fewer partial results).
-int effective_split(int32_t split_tokens, int32_t batch, int32_t max_ctx) {
-    if (split_tokens <= 0) {
-        int s = kDefaultSplit;
-        while (s > kMinDefaultSplit && (int64_t)batch * (((int64_t)max_ctx + s) / s) < kMinSplitGroups) s /= 2;
-        return s;
-    }
-    int s = split_tokens;
-    if (s > (1 << 30)) s = 1 << 30;
-    return (s + 31) / 32 * 32;
+// GA decode: the least number of 32-key units per chunk.  split_tokens <= 0
+// selects 256 keys; otherwise split_tokens rounded up to a multiple of 32.
+int min_units(int32_t split_tokens) {
+    if (split_tokens <= 0) return mimo::kDefaultMinUnits;
+    const int64_t s = split_tokens > (1 << 30) ? (1 << 30) : split_tokens;
+    return (int)((s + mimo::kTileKeys - 1) / mimo::kTileKeys);
 }
 
 }  // namespace
@@ -188,7 +178,8 @@ size_t mimo_attn_decode_workspace_size(const mimo_attn_dims* dims, int layer_typ
                                        int32_t split_tokens) {
     if (check_dims(dims, layer_type, 2) != MIMO_OK || batch < 1 || max_ctx < 0 || max_ctx == INT32_MAX) return 0;
     if (layer_type == MIMO_LAYER_SWA || batch > kMaxGridYZ) return 0;
-    return mimo::ga_workspace_bytes(batch, max_ctx, effective_split(split_tokens, batch, max_ctx), dims->num_q_heads);
+    const int chunks = mimo::ga_grid_chunks(batch, max_ctx, min_units(split_tokens));
+    return mimo::ga_workspace_bytes(batch, chunks, dims->num_q_heads);
 }
 
 }  // extern "C"
@@ -233,16 +224,9 @@ int decode_impl(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, c
         if (!aligned16(k_cache) || !aligned16(v_cache))
             return fail(MIMO_ERR_INVALID_ARG, "k_cache and v_cache must be 16-byte aligned");
     }
-    const int split = effective_split(split_tokens, batch, max_ctx);
     mimo::PageTable pt;
     if (pages) {
         if (int st = check_pages(pages, &pt)) return st;
-        // The split kernel preloads the pages of its keys: at most kMaxSplitPages.
-        const int P = pages->page_size;
-        const int span = split % P == 0 ? split / P : split / P + 2;
-        if (span > mimo::kMaxSplitPages)
-            return fail(MIMO_ERR_UNSUPPORTED, "a split of %d keys spans up to %d pages of %d (at most %d)", split,
-                        span, P, mimo::kMaxSplitPages);
     } else {
         // The kernels address a sequence's cache rows with 32-bit byte offsets.
         const int64_t row_bytes = (int64_t)dims->num_kv_heads * dims->head_dim_qk * (fp8 ? 1 : 2);
@@ -252,8 +236,9 @@ int decode_impl(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, c
                         (long long)rows, (long long)row_bytes);
     }
     mimo::DecodeArgs a{q, k_new, v_new, k_cache, v_cache, kv_base, ctx_lens, sink, out, lse, workspace, batch,
-                       max_ctx, split, dims->num_q_heads, dims->num_kv_heads, dims->sliding_window,
+                       max_ctx, min_units(split_tokens), dims->num_q_heads, dims->num_kv_heads, dims->sliding_window,
                        dims->softmax_scale, dims->value_scale};
+    a.max_chunks = mimo::kGaMaxChunks;
     a.pages = pt;
     if (fp8) {
         a.k_cache8 = fp8->k;
@@ -275,7 +260,8 @@ int decode_impl(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, c
     }
     if (!kv_base && !pages) return fail(MIMO_ERR_INVALID_ARG, "GA decode needs kv_base");
     if (batch > kMaxGridYZ) return fail(MIMO_ERR_UNSUPPORTED, "GA decode batch %d above %d", batch, kMaxGridYZ);
-    const size_t need = mimo::ga_workspace_bytes(batch, max_ctx, split, dims->num_q_heads);
+    const size_t need =
+        mimo::ga_workspace_bytes(batch, mimo::ga_grid_chunks(batch, max_ctx, a.min_units), dims->num_q_heads);
     if (!workspace || workspace_bytes < need)
         return fail(MIMO_ERR_WORKSPACE, "GA decode needs %zu workspace bytes (got %zu%s)", need, workspace_bytes,
                     workspace ? "" : ", NULL");

@@ -145,6 +145,19 @@ __device__ __forceinline__ void stage_v(const u32x4 (&v)[kTile / 4], char* vbuf,
     wave_lds_fence();
 }
 
+// As stage_v, with rows r >= nvalid stored as zeros: for tiles whose loads
+// were issued before the number of valid keys was known (the rows past it may
+// hold anything, and a zero probability times a non-finite value is NaN).
+__device__ __forceinline__ void stage_v_masked(const u32x4 (&v)[kTile / 4], char* vbuf, int lane, int nvalid) {
+    const int G = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < kTile / 4; ++i) {
+        const u32x4 x = (4 * i + G < nvalid) ? v[i] : u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(vbuf + (4 * i + G) * (kDv * 2) + (((lane & 15) ^ (2 * (4 * (i & 1) + G))) * 16)) = x;
+    }
+    wave_lds_fence();
+}
+
 // One tile whose K rows are in `k` and whose V rows are staged in `vbuf`.
 __device__ __forceinline__ void attend_tile(WaveAcc& acc, const bf16x8 (&qf)[kDqk / 32], const u32x4 (&k)[12],
                                             const char* vbuf, int nvalid, float c_log2, int lane) {
@@ -232,7 +245,9 @@ __device__ __forceinline__ void run_tiles(WaveAcc& acc, const bf16x8 (&qf)[kDqk 
 
 // At most two tiles (a wave's share of a ring of up to 224 slots plus the
 // new token): both tiles' loads are issued up front, unconditionally (tile 1
-// may be empty), and only the second tile's compute depends on ntiles.
+// may be empty), and only the second tile's compute depends on ntiles.  V
+// rows at or past a tile's nvalid are staged as zeros, so its descriptors may
+// cover rows that hold no key yet.
 template <class GetTile>
 __device__ __forceinline__ void run_two_tiles(WaveAcc& acc, const bf16x8 (&qf)[kDqk / 32], char* vbuf, int ntiles,
                                               const GetTile& get, const LaneOffsets& lo, int rowv, float c_log2,
@@ -242,11 +257,11 @@ __device__ __forceinline__ void run_two_tiles(WaveAcc& acc, const bf16x8 (&qf)[k
     issue_k(t0, lo, ka);
     issue_v(t0, lo, rowv, v);
     issue_k(t1, lo, kb);
-    stage_v(v, vbuf, lane);
+    stage_v_masked(v, vbuf, lane, t0.nvalid);
     issue_v(t1, lo, rowv, v);  // tile 1's V reuses the registers tile 0's V was staged from
     attend_tile(acc, qf, ka, vbuf, ntiles > 0 ? t0.nvalid : 0, c_log2, lane);
     if (ntiles > 1) {
-        stage_v(v, vbuf, lane);
+        stage_v_masked(v, vbuf, lane, t1.nvalid);
         attend_tile(acc, qf, kb, vbuf, t1.nvalid, c_log2, lane);
     }
 }
@@ -293,13 +308,22 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     const int p = ctx_lens[b];
     const int rowk = hkv * kDqk * 2, rowv = hkv * kDv * 2;
 
+    // Fused append: this thread's 16 bytes of the new token's K or V row of
+    // group g, loaded now and stored once the ring has been read.
+    u32x4 app_row = {};
+    if (app_k && tid < (kDqk + kDv) / 8)
+        app_row = tid < kDqk / 8 ? reinterpret_cast<const u32x4*>(k_new + ((size_t)b * hkv + g) * kDqk)[tid]
+                                 : reinterpret_cast<const u32x4*>(v_new + ((size_t)b * hkv + g) * kDv)[tid - kDqk / 8];
     bf16x8 qf[kDqk / 32];
     load_q(qf, q, b, g, hq, lane);
     // Slot j holds position p-R+((j-p) mod R); all R slots are in the window
-    // once p >= R, otherwise slots 0..p-1 are.
+    // once p >= R, otherwise slots 0..p-1 are.  The short-ring kernel reads
+    // the whole ring without waiting for p (its staging zeroes the rows past
+    // nvalid); the long-ring one bounds its descriptors by p.
     const int nring = min(p, R);
-    const rsrc_t rk = make_rsrc(ring_k + (size_t)b * R * hkv * kDqk, (uint32_t)nring * rowk);
-    const rsrc_t rv = make_rsrc(ring_v + (size_t)b * R * hkv * kDv, (uint32_t)nring * rowv);
+    const uint32_t ring_rows = kShortRing ? (uint32_t)R : (uint32_t)nring;
+    const rsrc_t rk = make_rsrc(ring_k + (size_t)b * R * hkv * kDqk, ring_rows * rowk);
+    const rsrc_t rv = make_rsrc(ring_v + (size_t)b * R * hkv * kDv, ring_rows * rowv);
     const rsrc_t nk = make_rsrc(k_new + (size_t)b * hkv * kDqk, (uint32_t)rowk);
     const rsrc_t nv = make_rsrc(v_new + (size_t)b * hkv * kDv, (uint32_t)rowv);
     const int ring_tiles = (R + kTile - 1) / kTile;
@@ -343,11 +367,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
         // ring loads were consumed before the barrier above.
         const size_t slot_row = (size_t)b * R + p % R;
         if (tid < kDqk / 8)
-            reinterpret_cast<u32x4*>(app_k + (slot_row * hkv + g) * kDqk)[tid] =
-                reinterpret_cast<const u32x4*>(k_new + ((size_t)b * hkv + g) * kDqk)[tid];
+            reinterpret_cast<u32x4*>(app_k + (slot_row * hkv + g) * kDqk)[tid] = app_row;
         else
-            reinterpret_cast<u32x4*>(app_v + (slot_row * hkv + g) * kDv)[tid - kDqk / 8] =
-                reinterpret_cast<const u32x4*>(v_new + ((size_t)b * hkv + g) * kDv)[tid - kDqk / 8];
+            reinterpret_cast<u32x4*>(app_v + (slot_row * hkv + g) * kDv)[tid - kDqk / 8] = app_row;
     }
 
     const int hl = tid >> 4;        // local head 0..15
@@ -376,107 +398,221 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 }
 
 // ---------------------------------------------------------------------------
-// PAGED: pool rows come through block_table (page_shift = log2 P); otherwise
-// sequence b's rows start at kv_base[b].
-template <bool PAGED>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void ga_split_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
-    const uint16_t* __restrict__ pool_k, const uint16_t* __restrict__ pool_v, const int64_t* __restrict__ kv_base,
-    const int32_t* __restrict__ ctx_lens, int hq, int hkv, int split, int nsplit, float c_log2,
-    float* __restrict__ ws_ml, float* __restrict__ ws_o, const int32_t* __restrict__ block_table, int max_blocks,
-    int page_shift, long long num_pages, uint16_t* __restrict__ app_k, uint16_t* __restrict__ app_v,
-    const int64_t* __restrict__ kv_capacity) {
-    __shared__ __attribute__((aligned(1024))) char lds[kBlockLdsBytes];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int s = blockIdx.x, b = blockIdx.y;
-    const int g = blockIdx.z * 4 + wave;
-    if (g >= hkv) return;
-    const int p = ctx_lens[b];
-    const int k0 = s * split;
-    if (k0 > p) return;
-    if (!PAGED && app_k && s == 0 && lane < (kDqk + kDv) / 8 && p < kv_capacity[b]) {
-        // Fused append: row kv_base[b] + p of KV head g.  No split of this
-        // launch reads row p (the new token comes from k_new / v_new).
-        const size_t row = (size_t)kv_base[b] + p;
-        if (lane < kDqk / 8)
-            reinterpret_cast<u32x4*>(app_k + (row * hkv + g) * kDqk)[lane] =
-                reinterpret_cast<const u32x4*>(k_new + ((size_t)b * hkv + g) * kDqk)[lane];
-        else
-            reinterpret_cast<u32x4*>(app_v + (row * hkv + g) * kDv)[lane - kDqk / 8] =
-                reinterpret_cast<const u32x4*>(v_new + ((size_t)b * hkv + g) * kDv)[lane - kDqk / 8];
-    }
-    const int k1 = min(k0 + split, p + 1);  // keys [k0, k1) of this split
-    const int kend = min(k1, p);            // of which [k0, kend) live in the pool
-    const int rowk = hkv * kDqk * 2, rowv = hkv * kDv * 2;
+// GA work plan (see ga_chunk_count): every split workgroup derives the unit
+// starts of the sequences from ctx_lens itself (256 threads, each summing a
+// contiguous run of sequences, one wave scanning the 256 sums), then finds the
+// sequence that holds the first unit of its chunk.  Workgroup (0, 0) also
+// writes the starts, K and n to the workspace header for the combine kernel.
+struct ChunkPlan {
+    long long c0, c1;  // units [c0, c1) of the flattened list
+    long long s_lo;    // first unit of sequence b_lo
+    int b_lo;          // the sequence holding unit c0
+    bool empty;        // chunk index >= n: nothing to do
+};
 
-    bf16x8 qf[kDqk / 32];
-    load_q(qf, q, b, g, hq, lane);
-    const rsrc_t nk = make_rsrc(k_new + (size_t)b * hkv * kDqk, (uint32_t)rowk);
-    const rsrc_t nv = make_rsrc(v_new + (size_t)b * hkv * kDv, (uint32_t)rowv);
-    const int npool = (kend - k0 + kTile - 1) / kTile;
-    const int ntiles = npool + (p < k1 ? 1 : 0);
-    const rsrc_t none = make_rsrc(k_new, 0);
-    const LaneOffsets lo = lane_offsets(lane, g, rowk, rowv);
-    WaveAcc acc;
-    acc_init(acc);
-    if constexpr (PAGED) {
-        // Pages of blocks first .. first+127 of this split, two per lane; -1
-        // past the table's end.
-        const int first = k0 >> page_shift;
-        const int32_t* tb = block_table + (size_t)b * max_blocks;
-        const int pg_lo = first + lane < max_blocks ? tb[first + lane] : -1;
-        const int pg_hi = first + 64 + lane < max_blocks ? tb[first + 64 + lane] : -1;
-        const int pmask = (1 << page_shift) - 1;
-        // Descriptor of the n valid keys from position j on (inside one page);
-        // no records when n <= 0 or the block is unmapped (reads as zero keys).
-        // Branch-free: the page number is picked with lane reads and selects.
-        auto half = [&](const uint16_t* pool, int row_elems, int j, int n) -> rsrc_t {
-            const int blk = (j >> page_shift) - first;  // 0..127 whenever n > 0 (host split check)
-            const int pa = __builtin_amdgcn_readlane(pg_lo, blk & 63);
-            const int pb = __builtin_amdgcn_readlane(pg_hi, blk & 63);
-            const int pg = (blk & 64) ? pb : pa;
-            const bool ok = n > 0 && pg >= 0 && pg < num_pages;
-            const size_t row = ((size_t)(ok ? pg : 0) << page_shift) + (size_t)(j & pmask);
-            return make_rsrc(pool + row * row_elems, ok ? (uint32_t)n * (uint32_t)(row_elems * 2) : 0u);
-        };
-        auto get = [&](int i) -> PagedTileSrc {
-            if (i < npool) {
-                const int j0 = k0 + i * kTile;
-                const int n = min(kend - j0, kTile);
-                return PagedTileSrc{{half(pool_k, hkv * kDqk, j0, min(n, 16)), half(pool_k, hkv * kDqk, j0 + 16, n - 16)},
-                                    {half(pool_v, hkv * kDv, j0, min(n, 16)), half(pool_v, hkv * kDv, j0 + 16, n - 16)},
-                                    n};
-            }
-            if (i < ntiles) return PagedTileSrc{{nk, none}, {nv, none}, 1};
-            return PagedTileSrc{{none, none}, {none, none}, 0};
-        };
-        run_tiles<kGaDepth>(acc, qf, lds + wave * kVTileBytes, ntiles, get, lo, rowv, c_log2, lane);
-    } else {
-        const size_t base = (size_t)kv_base[b];
-        const rsrc_t pk = make_rsrc(pool_k + base * hkv * kDqk, (uint32_t)p * rowk);
-        const rsrc_t pv = make_rsrc(pool_v + base * hkv * kDv, (uint32_t)p * rowv);
-        auto get = [&](int i) -> TileSrc {
-            if (i < npool) {
-                const int j0 = k0 + i * kTile;
-                return TileSrc{pk, pv, j0 * rowk, j0 * rowv, min(kend - j0, kTile)};
-            }
-            if (i < ntiles) return TileSrc{nk, nv, 0, 0, 1};
-            return TileSrc{none, none, 0, 0, 0};
-        };
-        run_tiles<kGaDepth>(acc, qf, lds + wave * kVTileBytes, ntiles, get, lo, rowv, c_log2, lane);
-    }
-    acc.l += __shfl_xor(acc.l, 16);
-    acc.l += __shfl_xor(acc.l, 32);
+// Position of sequence b's new token in its key order, and whether the grid
+// covers its context (ctx_lens[b] <= max_ctx).
+__device__ __forceinline__ int ga_new_pos(const int32_t* ctx_lens, int b, int max_ctx) {
+    const int c = ctx_lens[b];
+    return c > max_ctx ? 0 : c;
+}
 
+__device__ ChunkPlan ga_plan(const int32_t* __restrict__ ctx_lens, int batch, int max_ctx, int min_units,
+                             int max_chunks, int chunk, long long* __restrict__ header) {
+    __shared__ long long seg[256];
+    __shared__ long long plan_s, plan_k;
+    __shared__ int plan_b;
+    const int t = threadIdx.x;
+    const int per = (batch + 255) / 256;
+    const int b0 = min(t * per, batch), b1 = min(b0 + per, batch);
+    long long sum = 0;
+    for (int b = b0; b < b1; ++b) sum += ga_seq_units(ga_new_pos(ctx_lens, b, max_ctx));
+    seg[t] = sum;
+    __syncthreads();
+    if (t < 64) {
+        const long long a0 = seg[4 * t], a1 = seg[4 * t + 1], a2 = seg[4 * t + 2], a3 = seg[4 * t + 3];
+        const long long tot = a0 + a1 + a2 + a3;
+        long long inc = tot;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const long long y = __shfl_up(inc, d);
+            if (t >= d) inc += y;
+        }
+        const long long ex = inc - tot;
+        seg[4 * t] = ex;
+        seg[4 * t + 1] = ex + a0;
+        seg[4 * t + 2] = ex + a0 + a1;
+        seg[4 * t + 3] = ex + a0 + a1 + a2;
+        if (t == 63) plan_k = inc;
+    }
+    __syncthreads();
+    const long long K = plan_k;
+    const long long n = ga_chunk_count(K, min_units, max_chunks);
+    ChunkPlan pl;
+    pl.c0 = (long long)chunk * K / n;
+    pl.c1 = (long long)(chunk + 1) * K / n;
+    pl.empty = chunk >= n;
+    long long s = seg[t];
+    for (int b = b0; b < b1; ++b) {
+        const long long u = ga_seq_units(ga_new_pos(ctx_lens, b, max_ctx));
+        if (header) header[b] = s;
+        if (!pl.empty && s <= pl.c0 && pl.c0 < s + u) {
+            plan_b = b;
+            plan_s = s;
+        }
+        s += u;
+    }
+    if (header && t == 0) {
+        header[batch] = K;
+        header[batch + 1] = n;
+    }
+    __syncthreads();
+    pl.b_lo = __builtin_amdgcn_readfirstlane(plan_b);
+    pl.s_lo = plan_s;
+    return pl;
+}
+
+// Writes a wave's partial (m, l, O) of 16 heads to workspace slot `slot`.
+__device__ __forceinline__ void store_partial(const WaveAcc& acc, float* ws_ml, float* ws_o, size_t slot, int hq,
+                                              int g, int lane) {
     const int G = lane >> 4, h = lane & 15;
-    const size_t row = ((size_t)b * nsplit + s) * hq + g * kGroup + h;
+    const size_t row = slot * hq + g * kGroup + h;
     if (G == 0) {
         ws_ml[row * 2 + 0] = acc.m;
         ws_ml[row * 2 + 1] = acc.l;
     }
 #pragma unroll
     for (int db = 0; db < kDv / 16; ++db) *reinterpret_cast<f32x4*>(ws_o + row * kDv + 16 * db + 4 * G) = acc.o[db];
+}
+
+// Walks the pieces of a chunk: piece(b, u0, u1, p) gets units [u0, u1) of
+// sequence b (pool tiles u < ceil(p/32), then the new-token unit), in order.
+template <class Piece>
+__device__ __forceinline__ void for_each_piece(const ChunkPlan& pl, const int32_t* ctx_lens, int max_ctx,
+                                               const Piece& piece) {
+    int b = pl.b_lo;
+    long long s = pl.s_lo;
+    while (s < pl.c1) {
+        const int p = ga_new_pos(ctx_lens, b, max_ctx);
+        const long long u = ga_seq_units(p);
+        const int u0 = (int)(pl.c0 > s ? pl.c0 - s : 0);
+        const int u1 = (int)(pl.c1 - s < u ? pl.c1 - s : u);
+        piece(b, u0, u1, p);
+        s += u;
+        ++b;
+    }
+}
+
+// PAGED: pool rows come through block_table (page_shift = log2 P); otherwise
+// sequence b's rows start at kv_base[b].
+template <bool PAGED>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void ga_split_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const uint16_t* __restrict__ pool_k, const uint16_t* __restrict__ pool_v, const int64_t* __restrict__ kv_base,
+    const int32_t* __restrict__ ctx_lens, int batch, int max_ctx, int min_units, int max_chunks, int hq, int hkv,
+    float c_log2, long long* __restrict__ header, float* __restrict__ ws_ml, float* __restrict__ ws_o,
+    const int32_t* __restrict__ block_table, int max_blocks, int page_shift, long long num_pages,
+    uint16_t* __restrict__ app_k, uint16_t* __restrict__ app_v, const int64_t* __restrict__ kv_capacity) {
+    __shared__ __attribute__((aligned(1024))) char lds[kBlockLdsBytes];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int chunk = blockIdx.x;
+    const ChunkPlan pl = ga_plan(ctx_lens, batch, max_ctx, min_units, max_chunks, chunk,
+                                 chunk == 0 && blockIdx.z == 0 ? header : nullptr);
+    const int g = blockIdx.z * 4 + wave;
+    if (pl.empty || g >= hkv) return;
+    const int rowk = hkv * kDqk * 2, rowv = hkv * kDv * 2;
+    const LaneOffsets lo = lane_offsets(lane, g, rowk, rowv);
+    const rsrc_t none = make_rsrc(k_new, 0);
+    for_each_piece(pl, ctx_lens, max_ctx, [&](int b, int u0, int u1, int p) {
+        const int npool_units = (p + kTile - 1) / kTile;
+        const bool has_new = u1 > npool_units;  // the new-token unit is the sequence's last
+        const int k0 = u0 * kTile;
+        const int kend = min(min(u1, npool_units) * kTile, p);  // pool keys [k0, kend)
+        if (!PAGED && app_k && has_new && lane < (kDqk + kDv) / 8) {
+            // Fused append: row kv_base[b] + ctx of KV head g.  No piece of this
+            // launch reads that row (the new token comes from k_new / v_new).
+            const int ctx = ctx_lens[b];
+            if (ctx < kv_capacity[b]) {
+                const size_t row = (size_t)kv_base[b] + ctx;
+                if (lane < kDqk / 8)
+                    reinterpret_cast<u32x4*>(app_k + (row * hkv + g) * kDqk)[lane] =
+                        reinterpret_cast<const u32x4*>(k_new + ((size_t)b * hkv + g) * kDqk)[lane];
+                else
+                    reinterpret_cast<u32x4*>(app_v + (row * hkv + g) * kDv)[lane - kDqk / 8] =
+                        reinterpret_cast<const u32x4*>(v_new + ((size_t)b * hkv + g) * kDv)[lane - kDqk / 8];
+            }
+        }
+        bf16x8 qf[kDqk / 32];
+        load_q(qf, q, b, g, hq, lane);
+        const rsrc_t nk = make_rsrc(k_new + (size_t)b * hkv * kDqk, (uint32_t)rowk);
+        const rsrc_t nv = make_rsrc(v_new + (size_t)b * hkv * kDv, (uint32_t)rowv);
+        WaveAcc acc;
+        acc_init(acc);
+        if constexpr (PAGED) {
+            // Spans of at most kMaxSplitPages pages, cut at 32-key tile
+            // boundaries; each preloads its page numbers, two per lane (-1 past
+            // the table's end), and runs its tiles.
+            const int32_t* tb = block_table + (size_t)b * max_blocks;
+            const int pmask = (1 << page_shift) - 1;
+            int a = k0;
+            bool more = true;
+            while (more) {
+                const int first = a >> page_shift;
+                const long long lim = ((long long)(first + kMaxSplitPages) << page_shift) / kTile * kTile;
+                const int span_end = (int)(lim < kend ? lim : kend);
+                more = span_end < kend;
+                const int npool = (span_end - a + kTile - 1) / kTile;
+                const int ntiles = npool + (!more && has_new ? 1 : 0);
+                const int pg_lo = first + lane < max_blocks ? tb[first + lane] : -1;
+                const int pg_hi = first + 64 + lane < max_blocks ? tb[first + 64 + lane] : -1;
+                // Descriptor of the n valid keys from position j on (inside one
+                // page); no records when n <= 0 or the block is unmapped.
+                auto half = [&](const uint16_t* pool, int row_elems, int j, int n) -> rsrc_t {
+                    const int blk = (j >> page_shift) - first;  // 0..127 whenever n > 0
+                    const int pa = __builtin_amdgcn_readlane(pg_lo, blk & 63);
+                    const int pb = __builtin_amdgcn_readlane(pg_hi, blk & 63);
+                    const int pg = (blk & 64) ? pb : pa;
+                    const bool ok = n > 0 && pg >= 0 && pg < num_pages;
+                    const size_t row = ((size_t)(ok ? pg : 0) << page_shift) + (size_t)(j & pmask);
+                    return make_rsrc(pool + row * row_elems, ok ? (uint32_t)n * (uint32_t)(row_elems * 2) : 0u);
+                };
+                const int a0 = a;
+                auto get = [&](int i) -> PagedTileSrc {
+                    if (i < npool) {
+                        const int j0 = a0 + i * kTile;
+                        const int n = min(span_end - j0, kTile);
+                        return PagedTileSrc{
+                            {half(pool_k, hkv * kDqk, j0, min(n, 16)), half(pool_k, hkv * kDqk, j0 + 16, n - 16)},
+                            {half(pool_v, hkv * kDv, j0, min(n, 16)), half(pool_v, hkv * kDv, j0 + 16, n - 16)},
+                            n};
+                    }
+                    if (i < ntiles) return PagedTileSrc{{nk, none}, {nv, none}, 1};
+                    return PagedTileSrc{{none, none}, {none, none}, 0};
+                };
+                run_tiles<kGaDepth>(acc, qf, lds + wave * kVTileBytes, ntiles, get, lo, rowv, c_log2, lane);
+                a = span_end;
+            }
+        } else {
+            const size_t base = (size_t)kv_base[b];
+            const rsrc_t pk = make_rsrc(pool_k + base * hkv * kDqk, (uint32_t)p * rowk);
+            const rsrc_t pv = make_rsrc(pool_v + base * hkv * kDv, (uint32_t)p * rowv);
+            const int npool = (kend - k0 + kTile - 1) / kTile;
+            const int ntiles = npool + (has_new ? 1 : 0);
+            auto get = [&](int i) -> TileSrc {
+                if (i < npool) {
+                    const int j0 = k0 + i * kTile;
+                    return TileSrc{pk, pv, j0 * rowk, j0 * rowv, min(kend - j0, kTile)};
+                }
+                if (i < ntiles) return TileSrc{nk, nv, 0, 0, 1};
+                return TileSrc{none, none, 0, 0, 0};
+            };
+            run_tiles<kGaDepth>(acc, qf, lds + wave * kVTileBytes, ntiles, get, lo, rowv, c_log2, lane);
+        }
+        acc.l += __shfl_xor(acc.l, 16);
+        acc.l += __shfl_xor(acc.l, 32);
+        store_partial(acc, ws_ml, ws_o, (size_t)chunk + b, hq, g, lane);
+    });
 }
 
 // ---------------------------------------------------------------------------
@@ -642,82 +778,84 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const uint8_t* __restrict__ pool_k, const uint8_t* __restrict__ pool_v, const int64_t* __restrict__ kv_base,
     const int32_t* __restrict__ ctx_lens, const float* __restrict__ k_scale, const float* __restrict__ v_scale,
-    int hq, int hkv, int split, int nsplit, float c_log2, float* __restrict__ ws_ml, float* __restrict__ ws_o) {
+    int batch, int max_ctx, int min_units, int max_chunks, int hq, int hkv, float c_log2,
+    long long* __restrict__ header, float* __restrict__ ws_ml, float* __restrict__ ws_o) {
     __shared__ __attribute__((aligned(1024))) char lds[kBlockLdsBytes];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int s = blockIdx.x, b = blockIdx.y;
+    const int chunk = blockIdx.x;
+    const ChunkPlan pl = ga_plan(ctx_lens, batch, max_ctx, min_units, max_chunks, chunk,
+                                 chunk == 0 && blockIdx.z == 0 ? header : nullptr);
     const int g = blockIdx.z * 4 + wave;
-    if (g >= hkv) return;
-    const int p = ctx_lens[b];
-    const int k0 = s * split;
-    if (k0 > p) return;
-    const int k1 = min(k0 + split, p + 1);  // keys [k0, k1) of this split
-    const int kend = min(k1, p);            // of which [k0, kend) live in the pool
+    if (pl.empty || g >= hkv) return;
     const int rowk8 = hkv * kDqk, rowv8 = hkv * kDv;
-
-    bf16x8 qf[kDqk / 32];
-    load_q_perm(qf, q, b, g, hq, lane);
     const float ks = k_scale[g], vs = v_scale[g];
-    const size_t base = (size_t)kv_base[b];
-    const rsrc_t pk = make_rsrc(pool_k + base * rowk8, (uint32_t)p * rowk8);
-    const rsrc_t pv = make_rsrc(pool_v + base * rowv8, (uint32_t)p * rowv8);
     const rsrc_t none = make_rsrc(pool_k, 0);
-    const int npool = (kend - k0 + kTile - 1) / kTile;
-    auto get = [&](int i) -> TileSrc {
-        if (i < npool) {
-            const int j0 = k0 + i * kTile;
-            return TileSrc{pk, pv, j0 * rowk8, j0 * rowv8, min(kend - j0, kTile)};
-        }
-        return TileSrc{none, none, 0, 0, 0};
-    };
     const Fp8LaneOffsets lo = fp8_lane_offsets(lane, g, rowk8, rowv8);
-    WaveAcc acc;
-    acc_init(acc);
-    run_tiles_fp8<kFp8Depth>(acc, qf, lds + wave * kVTileBytes, npool, get, lo, rowv8, c_log2 * ks, lane);
-    acc.l += __shfl_xor(acc.l, 16);
-    acc.l += __shfl_xor(acc.l, 32);
+    for_each_piece(pl, ctx_lens, max_ctx, [&](int b, int u0, int u1, int p) {
+        const int npool_units = (p + kTile - 1) / kTile;
+        const bool has_new = u1 > npool_units;
+        const int k0 = u0 * kTile;
+        const int kend = min(min(u1, npool_units) * kTile, p);  // pool keys [k0, kend)
+        bf16x8 qf[kDqk / 32];
+        load_q_perm(qf, q, b, g, hq, lane);
+        const size_t base = (size_t)kv_base[b];
+        const rsrc_t pk = make_rsrc(pool_k + base * rowk8, (uint32_t)p * rowk8);
+        const rsrc_t pv = make_rsrc(pool_v + base * rowv8, (uint32_t)p * rowv8);
+        const int npool = (kend - k0 + kTile - 1) / kTile;
+        auto get = [&](int i) -> TileSrc {
+            if (i < npool) {
+                const int j0 = k0 + i * kTile;
+                return TileSrc{pk, pv, j0 * rowk8, j0 * rowv8, min(kend - j0, kTile)};
+            }
+            return TileSrc{none, none, 0, 0, 0};
+        };
+        WaveAcc acc;
+        acc_init(acc);
+        run_tiles_fp8<kFp8Depth>(acc, qf, lds + wave * kVTileBytes, npool, get, lo, rowv8, c_log2 * ks, lane);
+        acc.l += __shfl_xor(acc.l, 16);
+        acc.l += __shfl_xor(acc.l, 32);
 #pragma unroll
-    for (int db = 0; db < kDv / 16; ++db) acc.o[db] *= vs;
-    if (p < k1)
-        fold_new_token(acc, qf, k_new + ((size_t)b * hkv + g) * kDqk, v_new + ((size_t)b * hkv + g) * kDv, c_log2,
-                       lane);
-
-    const int G = lane >> 4, h = lane & 15;
-    const size_t row = ((size_t)b * nsplit + s) * hq + g * kGroup + h;
-    if (G == 0) {
-        ws_ml[row * 2 + 0] = acc.m;
-        ws_ml[row * 2 + 1] = acc.l;
-    }
-#pragma unroll
-    for (int db = 0; db < kDv / 16; ++db) *reinterpret_cast<f32x4*>(ws_o + row * kDv + 16 * db + 4 * G) = acc.o[db];
+        for (int db = 0; db < kDv / 16; ++db) acc.o[db] *= vs;
+        if (has_new)
+            fold_new_token(acc, qf, k_new + ((size_t)b * hkv + g) * kDqk, v_new + ((size_t)b * hkv + g) * kDv,
+                           c_log2, lane);
+        store_partial(acc, ws_ml, ws_o, (size_t)chunk + b, hq, g, lane);
+    });
 }
 
-// Merge of the splits of one (sequence, head): block (b, head), thread t =
-// (split group t/16, 8 output columns 8(t%16)).  Each thread folds the splits
-// s = t/16, t/16 + 16, ... with an online max (all its loads are independent,
-// so they are in flight together), then the 16 split groups are merged through
-// LDS by the threads of group 0, which add the sink once and write the row.
+// Merge of the pieces of one (sequence, head): block (b, head), thread t =
+// (piece group t/16, 8 output columns 8(t%16)).  The pieces of sequence b are
+// slots first + b .. last + b, first and last being the chunks holding its
+// first and last unit (workspace header: unit starts, K, n).  Each thread
+// folds the pieces s = t/16, t/16 + 16, ... with an online max (all its loads
+// are independent, so they are in flight together), then the 16 groups are
+// merged through LDS by the threads of group 0, which add the sink once and
+// write the row.
 constexpr int kCombGroups = 16;
-__global__ __launch_bounds__(256) void ga_combine_kernel(const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
-                                                         const int32_t* __restrict__ ctx_lens, const float* __restrict__ sink,
-                                                         uint16_t* __restrict__ out, float* __restrict__ lse, int hq,
-                                                         int split, int nsplit, float value_scale) {
+__global__ __launch_bounds__(256) void ga_combine_kernel(const long long* __restrict__ header,
+                                                         const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
+                                                         const int32_t* __restrict__ ctx_lens, int batch, int max_ctx,
+                                                         const float* __restrict__ sink, uint16_t* __restrict__ out,
+                                                         float* __restrict__ lse, int hq, float value_scale) {
     __shared__ float red_ml[kCombGroups][16][2];
     __shared__ __attribute__((aligned(16))) float red_o[kCombGroups][16][8 + 4];  // padded rows
     const int b = blockIdx.x, head = blockIdx.y;
     const int sg = threadIdx.x >> 4, cb = threadIdx.x & 15, e0 = cb * 8;
-    const int p = ctx_lens[b];
-    const int ns = (p + 1 + split - 1) / split;
     uint16_t* orow = out + ((size_t)b * hq + head) * kDv + e0;
-    if (ns > nsplit) {  // the grid did not cover this context: refuse loudly
+    if (ctx_lens[b] > max_ctx) {  // the grid did not cover this context: refuse loudly
         if (sg == 0) {
             *reinterpret_cast<u32x4*>(orow) = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
             if (lse && cb == 0) reinterpret_cast<uint32_t*>(lse)[(size_t)b * hq + head] = 0x7fc00000u;  // quiet NaN bits
         }
         return;
     }
-    const size_t row0 = (size_t)b * nsplit * hq + head;
+    const long long K = header[batch], n = header[batch + 1];
+    const long long s0 = header[b], s1 = header[b + 1];
+    const long long first = ((s0 + 1) * n - 1) / K;  // chunk holding unit s0
+    const long long last = (s1 * n - 1) / K;         // chunk holding unit s1 - 1
+    const int ns = (int)(last - first + 1);
+    const size_t row0 = (size_t)(first + b) * hq + head;
     float m = kNoMax, l = 0.0f;
     f32x4 o0 = {}, o1 = {};
     for (int s = sg; s < ns; s += kCombGroups) {
@@ -747,7 +885,7 @@ __global__ __launch_bounds__(256) void ga_combine_kernel(const float* __restrict
     f32x4 t0 = {}, t1 = {};
 #pragma unroll
     for (int g = 0; g < kCombGroups; ++g) {
-        const float wt = fast_exp2(red_ml[g][cb][0] - M);  // groups without splits: exp2(kNoMax - M) = 0
+        const float wt = fast_exp2(red_ml[g][cb][0] - M);  // groups without pieces: exp2(kNoMax - M) = 0
         Z += wt * red_ml[g][cb][1];
         t0 += wt * *reinterpret_cast<const f32x4*>(&red_o[g][cb][0]);
         t1 += wt * *reinterpret_cast<const f32x4*>(&red_o[g][cb][4]);
@@ -770,24 +908,25 @@ hipError_t launch_decode_swa(const DecodeArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_decode_ga(const DecodeArgs& a, hipStream_t stream) {
-    const int nsplit = ga_num_splits(a.max_ctx, a.split);
-    float* ws_ml = static_cast<float*>(a.workspace);
-    float* ws_o = ws_ml + (size_t)a.batch * nsplit * a.hq * 2;
+    const int grid = ga_grid_chunks(a.batch, a.max_ctx, a.min_units, a.max_chunks);
+    long long* header = static_cast<long long*>(a.workspace);
+    float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + ga_header_bytes(a.batch));
+    float* ws_o = ws_ml + (size_t)(grid + a.batch) * a.hq * 2;
     if (a.k_cache8) {
-        hipLaunchKernelGGL(ga_split_fp8_kernel, dim3(nsplit, a.batch, (a.hkv + 3) / 4), dim3(256), 0, stream, a.q,
-                           a.k_new, a.v_new, a.k_cache8, a.v_cache8, a.kv_base, a.ctx_lens, a.k_scale, a.v_scale,
-                           a.hq, a.hkv, a.split, nsplit, a.softmax_scale * kLog2e, ws_ml, ws_o);
+        hipLaunchKernelGGL(ga_split_fp8_kernel, dim3(grid, 1, (a.hkv + 3) / 4), dim3(256), 0, stream, a.q, a.k_new,
+                           a.v_new, a.k_cache8, a.v_cache8, a.kv_base, a.ctx_lens, a.k_scale, a.v_scale, a.batch,
+                           a.max_ctx, a.min_units, grid, a.hq, a.hkv, a.softmax_scale * kLog2e, header, ws_ml, ws_o);
     } else {
-        hipLaunchKernelGGL(a.pages.table ? ga_split_kernel<true> : ga_split_kernel<false>,
-                           dim3(nsplit, a.batch, (a.hkv + 3) / 4), dim3(256), 0, stream, a.q, a.k_new, a.v_new,
-                           a.k_cache, a.v_cache, a.kv_base, a.ctx_lens, a.hq, a.hkv, a.split, nsplit,
-                           a.softmax_scale * kLog2e, ws_ml, ws_o, a.pages.table, a.pages.max_blocks, a.pages.shift,
-                           a.pages.num_pages, a.pages.table ? nullptr : a.append_k, a.append_v, a.kv_capacity);
+        hipLaunchKernelGGL(a.pages.table ? ga_split_kernel<true> : ga_split_kernel<false>, dim3(grid, 1, (a.hkv + 3) / 4),
+                           dim3(256), 0, stream, a.q, a.k_new, a.v_new, a.k_cache, a.v_cache, a.kv_base, a.ctx_lens,
+                           a.batch, a.max_ctx, a.min_units, grid, a.hq, a.hkv, a.softmax_scale * kLog2e, header, ws_ml,
+                           ws_o, a.pages.table, a.pages.max_blocks, a.pages.shift, a.pages.num_pages,
+                           a.pages.table ? nullptr : a.append_k, a.append_v, a.kv_capacity);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(ga_combine_kernel, dim3(a.batch, a.hq), dim3(256), 0, stream, ws_ml, ws_o,
-                       a.ctx_lens, a.sink, a.out, a.lse, a.hq, a.split, nsplit, a.value_scale);
+    hipLaunchKernelGGL(ga_combine_kernel, dim3(a.batch, a.hq), dim3(256), 0, stream, header, ws_ml, ws_o, a.ctx_lens,
+                       a.batch, a.max_ctx, a.sink, a.out, a.lse, a.hq, a.value_scale);
     return hipGetLastError();
 }
 

@@ -49,7 +49,7 @@ struct DecodeArgs {
     uint16_t* out;
     float* lse;
     void* workspace;
-    int batch, max_ctx, split, hq, hkv, window;
+    int batch, max_ctx, min_units, hq, hkv, window;
     float softmax_scale, value_scale;
     PageTable pages;
     // FP8 GA pool (E4M3 codes) and its per-KV-head scales; k_cache/v_cache unused then.
@@ -63,14 +63,51 @@ struct DecodeArgs {
     uint16_t* append_k = nullptr;
     uint16_t* append_v = nullptr;
     const int64_t* kv_capacity = nullptr;
+    // GA: most chunks the split grid may use (sizes the grid and the workspace).
+    int max_chunks = 0;
 };
-// Pages a GA split kernel preloads per workgroup (two per lane of a wave).
+
+// GA decode work plan.  Sequence b's keys form units: ceil(p_b / 32) tiles of
+// 32 pool keys and one unit for the new token, p_b = ctx_lens[b] (0 when
+// ctx_lens[b] > max_ctx: such a sequence gets NaN outputs and only its new
+// token is touched).  The units of all sequences, in order, are one list of K
+// units cut into n balanced chunks, chunk i = units [floor(iK/n),
+// floor((i+1)K/n)); one split workgroup takes one chunk.  n is kGaRound (one
+// workgroup per compute unit, all resident at once: every extra round of
+// chunk start-ups measured slower on the layer stack's decode) when the
+// chunks then hold at least min_units units, else ceil(K / min_units).  The
+// piece of sequence b inside chunk i writes its partial result to slot i + b,
+// so a sequence's partials are consecutive slots and at most n + batch - 1
+// slots are used.
+constexpr int kTileKeys = 32;
+constexpr int kGaRound = 256;      // compute units of a gfx950 part (MI350X / MI355X)
+constexpr int kGaMaxRounds = 1;
+constexpr int kGaMaxChunks = kGaRound * kGaMaxRounds;
+constexpr int kDefaultMinUnits = 8;  // 256 keys
+// Pages a paged GA workgroup preloads at a time (two per lane of a wave).
 constexpr int kMaxSplitPages = 128;
-// Number of GA splits of `split` keys covering positions 0..max_ctx.
-inline int ga_num_splits(int max_ctx, int split) { return (int)(((int64_t)max_ctx + split) / split); }
-// Bytes of GA workspace: per (sequence, split, head) an (m, l) pair and 128 partial outputs.
-inline size_t ga_workspace_bytes(int batch, int max_ctx, int split, int hq) {
-    return (size_t)batch * (size_t)ga_num_splits(max_ctx, split) * (size_t)hq * (2 + 128) * sizeof(float);
+
+__host__ __device__ inline long long ga_chunk_count(long long units, int min_units, int max_chunks) {
+    const long long by_len = (units + min_units - 1) / min_units;
+    long long rounds = units / ((long long)kGaRound * min_units);
+    rounds = rounds < 1 ? 1 : (rounds > kGaMaxRounds ? kGaMaxRounds : rounds);
+    long long n = by_len < rounds * kGaRound ? by_len : rounds * kGaRound;
+    if (n > max_chunks) n = max_chunks;
+    return n < 1 ? 1 : n;
+}
+// Units of a sequence whose new token sits at position p.
+__host__ __device__ inline long long ga_seq_units(long long p) { return (p + kTileKeys - 1) / kTileKeys + 1; }
+// Split grid for a batch whose contexts are at most max_ctx (chunk counts only
+// grow with the unit count, so the device's n never exceeds it).
+inline int ga_grid_chunks(int batch, int max_ctx, int min_units, int max_chunks = kGaMaxChunks) {
+    return (int)ga_chunk_count((long long)batch * ga_seq_units(max_ctx), min_units, max_chunks);
+}
+// Workspace: a header of batch + 2 int64 (each sequence's first unit, then K
+// and n), padded to 256 bytes, then per slot and query head an (m, l) pair and
+// 128 partial outputs, fp32.
+inline size_t ga_header_bytes(int batch) { return ((size_t)(batch + 2) * 8 + 255) / 256 * 256; }
+inline size_t ga_workspace_bytes(int batch, int chunks, int hq) {
+    return ga_header_bytes(batch) + (size_t)(chunks + batch) * (size_t)hq * (2 + 128) * sizeof(float);
 }
 hipError_t launch_decode_swa(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_ga(const DecodeArgs& a, hipStream_t stream);

@@ -80,22 +80,11 @@ class HybridStack:
         self.zero_ctx = torch.zeros(self.batch, dtype=torch.int32, device=dev)
         self.cu_step = torch.arange(self.batch + 1, dtype=torch.int32, device=dev)
         self.max_ctx = self.max_len + self.decode_steps
-        self.split = self.decode_split()
+        self.split = 0  # the library's default GA decode chunking
         self.workspace = None
         ws = B.mimo_attn_decode_workspace_size(self.dims, GA, self.batch, self.max_ctx, self.split)
         if ws:
             self.workspace = torch.empty(ws // 4 + 4, dtype=torch.float32, device=dev)
-
-    def decode_split(self, per_cu: int = 3, cus: int = 256) -> int:
-        """GA keys per decode split workgroup, from the contexts this stack will
-        hold: the largest of 2048, 1024, 512, 256 that gives about `per_cu`
-        workgroups per compute unit over the sum of the contexts (the library's
-        own default sees only batch and max_ctx)."""
-        final = [L + self.decode_steps + 1 for L in self.lengths]
-        for s in (2048, 1024, 512):
-            if sum((n + s - 1) // s for n in final) >= per_cu * cus:
-                return s
-        return 256
 
     def prefill_layer(self, layer: int, q, k, v, sink, out, lse=None, stream=None):
         """Varlen prefill of one layer, then its KV append (cache positions 0..L-1)."""

@@ -144,10 +144,12 @@ int mimo_attn_prefill_chunk(const mimo_attn_dims* dims, int layer_type,
 
 /*
  * Bytes of device workspace mimo_attn_decode needs for these arguments.  SWA
- * needs none (returns 0).  GA needs batch * ceil((max_ctx+1)/split) * Hq * 130
- * * 4 bytes for the per-split partial results.  split_tokens <= 0 selects the
- * default split (see mimo_attn_decode).  Returns 0 for arguments
- * mimo_attn_decode would reject.
+ * needs none (returns 0).  GA splits the keys of all sequences into chunks of
+ * 32-key units (see mimo_attn_decode) and needs a header of batch + 2 int64,
+ * padded to 256 bytes, plus (chunks + batch) * Hq * 130 * 4 bytes of partial
+ * results, where chunks is at most 256 (so the size does not grow with
+ * max_ctx beyond that).  split_tokens <= 0 selects the default.  Returns 0 for
+ * arguments mimo_attn_decode would reject.
  */
 size_t mimo_attn_decode_workspace_size(const mimo_attn_dims* dims, int layer_type,
                                        int32_t batch, int32_t max_ctx, int32_t split_tokens);
@@ -168,15 +170,19 @@ size_t mimo_attn_decode_workspace_size(const mimo_attn_dims* dims, int layer_typ
  *   kv_base      GA: [batch] int64 (device); SWA: ignored (may be NULL).
  *   ctx_lens     [batch] int32 (device): tokens already cached; 0 <= p <= max_ctx.
  *   batch        >= 1 (host).
- *   max_ctx      (host) >= every ctx_lens[b]; sizes the GA split grid.  A GA
+ *   max_ctx      (host) >= every ctx_lens[b]; bounds the GA split grid.  A GA
  *                sequence with ctx_lens[b] > max_ctx gets NaN outputs.
- *   split_tokens GA keys per split workgroup (host); rounded up to a multiple
- *                of 32.  <= 0 selects the largest of 2048, 1024, 512 and 256
- *                that gives batch * ceil((max_ctx+1)/split) >= 256 workgroups
- *                (else 256).  A caller that knows the actual context lengths
- *                may do better: splits that give a few workgroups per compute
- *                unit for the sum of the contexts.  Results do not depend on
- *                it beyond fp32 rounding.
+ *   split_tokens GA: the least number of keys per split chunk (host), rounded
+ *                up to a multiple of 32; <= 0 selects 256.  GA splits the key
+ *                space of the whole batch -- per sequence ceil(p/32) tiles of
+ *                32 cached keys plus one unit for the new token -- into equal
+ *                chunks, one per split workgroup: 256 chunks (one per compute
+ *                unit of the part) when they hold at least split_tokens keys
+ *                each, else chunks of split_tokens keys; a chunk may cover
+ *                pieces of several sequences.  The plan is derived on the
+ *                device from ctx_lens, so no workgroup is launched for keys
+ *                that do not exist.  Results do not depend on it beyond fp32
+ *                rounding.
  *   sink, out, lse  as for prefill, with T = batch; lse may be NULL.
  *   workspace    device buffer of >= mimo_attn_decode_workspace_size(...) bytes
  *                (GA only; NULL allowed for SWA).  Its contents need no
@@ -292,9 +298,7 @@ int mimo_kv_append_paged(const mimo_attn_dims* dims,
                          const mimo_kv_pages* pages, hipStream_t stream);
 
 /*
- * GA decode (as mimo_attn_decode with layer_type GA) over a paged pool.
- * split_tokens must span at most 128 pages: with the default split (at most
- * 2048) every page_size >= 16 qualifies; otherwise MIMO_ERR_UNSUPPORTED.  The
+ * GA decode (as mimo_attn_decode with layer_type GA) over a paged pool.  The
  * workspace is mimo_attn_decode_workspace_size(dims, MIMO_LAYER_GA, batch,
  * max_ctx, split_tokens) bytes.  Results are bit-identical to
  * mimo_attn_decode over a contiguous pool holding the same rows.

@@ -161,41 +161,37 @@ def test_decode_append_rejects(L, case, status):
     assert decode_append_call(L, **case) == status
 
 
+def ga_workspace_expected(batch, max_ctx, split, hq=64):
+    """The GA decode workspace as the header states it: a header of batch + 2
+    int64 padded to 256 bytes, then (chunks + batch) slots of hq x 130 fp32,
+    chunks = the split grid for batch sequences of max_ctx cached keys (units of
+    32 keys plus one per new token, chunks of at least max(1, ceil(split/32))
+    units, default 8, in whole rounds of 256 up to 4 rounds)."""
+    units = batch * (-(-max_ctx // 32) + 1)
+    mu = 8 if split <= 0 else -(-min(split, 1 << 30) // 32)
+    by_len = -(-units // mu)
+    chunks = max(1, min(by_len, 256))
+    header = -(-8 * (batch + 2) // 256) * 256
+    return header + (chunks + batch) * hq * 130 * 4
+
+
 def test_workspace_size(L):
     d = B.make_dims()
-    # GA: batch * ceil((max_ctx+1)/split) * Hq * (2 + 128) * 4 bytes.
-    assert B.mimo_attn_decode_workspace_size(d, 1, 3, 4095, 2048) == 3 * 2 * 64 * 130 * 4
-    assert B.mimo_attn_decode_workspace_size(d, 1, 3, 4096, 2048) == 3 * 3 * 64 * 130 * 4
-    assert B.mimo_attn_decode_workspace_size(d, 1, 1, 0, 0) == 1 * 1 * 64 * 130 * 4
-    assert B.mimo_attn_decode_workspace_size(d, 1, 2, 100, 33) == 2 * 2 * 64 * 130 * 4  # split rounds to 64
+    ws = lambda b, c, s: B.mimo_attn_decode_workspace_size(d, 1, b, c, s)
+    for b, c, s in [(3, 4095, 2048), (3, 4096, 2048), (1, 0, 0), (2, 100, 33), (128, 262207, 0), (32, 32832, 0),
+                    (32, 32832, 384), (1, 262143, 0), (4, 65535, 1024), (3, 4095, 256), (7, 5, 32)]:
+        assert ws(b, c, s) == ga_workspace_expected(b, c, s), (b, c, s)
+    # Worked values: one short sequence needs one chunk; the long-context batch
+    # of 128 sequences caps at 256 chunks (12.8 MB, not per split).
+    assert ws(1, 0, 0) == 256 + 2 * 64 * 130 * 4
+    assert ws(128, 262207, 0) == 1280 + (256 + 128) * 64 * 130 * 4
+    assert ws(128, 262207, 0) == ws(128, 100000, 0)          # bounded by the chunk cap, not by max_ctx
+    big = (1 << 31) - 2                                       # largest accepted max_ctx
+    assert ws(65535, big, 0) == ga_workspace_expected(65535, big, 0)
+    assert ws(65536, 10, 0) == 0 and ws(1, (1 << 31) - 1, 0) == 0   # what decode rejects
     assert B.mimo_attn_decode_workspace_size(d, 0, 128, 262144, 0) == 0
     assert B.mimo_attn_decode_workspace_size(d, 1, 0, 10, 0) == 0
     assert B.mimo_attn_decode_workspace_size(B.make_dims(head_dim_v=64), 1, 1, 10, 0) == 0
-
-
-def test_default_split_spreads_short_batches(L):
-    """split_tokens <= 0: the largest of 2048/1024/512/256 giving >= 256 nominal
-    split workgroups for batch x max_ctx (else 256); seen through the workspace."""
-    d = B.make_dims()
-    ws = lambda b, c, s: B.mimo_attn_decode_workspace_size(d, 1, b, c, s)
-    per_split = 64 * 130 * 4
-    assert ws(128, 262207, 0) == ws(128, 262207, 2048) == 128 * 129 * per_split  # large batch keeps 2048
-    assert ws(1, 262143, 0) == ws(1, 262143, 1024) == 1 * 256 * per_split       # one long sequence: 1024
-    assert ws(4, 65535, 0) == ws(4, 65535, 1024) == 4 * 64 * per_split
-    assert ws(3, 4095, 0) == ws(3, 4095, 256) == 3 * 16 * per_split             # floor of 256
-    big = (1 << 31) - 2                                                          # largest accepted max_ctx
-    assert ws(65535, big, 0) == 65535 * ((big + 2048) // 2048) * per_split        # 64-bit arithmetic
-    assert ws(65536, 10, 0) == 0 and ws(1, (1 << 31) - 1, 0) == 0                # what decode rejects
-
-
-def test_stack_split_from_known_lengths():
-    """The hybrid stack picks its decode split from the contexts it will hold."""
-    from types import SimpleNamespace
-    from global_attention_mimo_amd.stack import HybridStack
-    pick = lambda lengths, steps: HybridStack.decode_split(SimpleNamespace(lengths=lengths, decode_steps=steps))
-    assert pick([262144] * 128, 64) == 2048
-    assert pick([512 + 100 * i for i in range(32)], 64) == 256
-    assert pick([40000] * 32, 64) == 1024   # 32 x 40 splits of 1024 = 1280 >= 768
 
 
 def append_call(L, dims=None, layer=1, k=FAKE, v=FAKE, cu=FAKE, ctx=FAKE, batch=1, total=4, kc=FAKE, vc=FAKE,
@@ -254,8 +250,6 @@ def paged_decode_call(L, pg=None, q=FAKE, kc=FAKE, ctx=FAKE, batch=2, max_ctx=10
     (dict(batch=0), B.MIMO_ERR_INVALID_ARG),
     (dict(ws=None), B.MIMO_ERR_WORKSPACE),
     (dict(ws_bytes=100), B.MIMO_ERR_WORKSPACE),
-    (dict(split=4096), B.MIMO_ERR_UNSUPPORTED),                 # 256 pages of 16 per split
-    (dict(pg=pages(page_size=64), split=8192 + 32), B.MIMO_ERR_UNSUPPORTED),
     (dict(dims=B.make_dims(head_dim_qk=64)), B.MIMO_ERR_UNSUPPORTED),
 ])
 def test_decode_paged_rejects(L, case, status):
