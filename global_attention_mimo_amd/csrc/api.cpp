@@ -209,7 +209,7 @@ int decode_impl(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, c
                 const mimo_kv_pages* pages, const int32_t* ctx_lens, int32_t batch, int32_t max_ctx,
                 int32_t split_tokens, const float* sink, uint16_t* out, float* lse, void* workspace,
                 size_t workspace_bytes, hipStream_t stream, const Fp8Pool* fp8 = nullptr, bool append = false,
-                const int64_t* kv_capacity = nullptr) {
+                const int64_t* kv_capacity = nullptr, int max_chunks = mimo::kGaMaxChunks) {
     if (int st = check_dims(dims, layer_type, 2)) return st;
     if (!q || !k_new || !v_new || !ctx_lens || !out)
         return fail(MIMO_ERR_INVALID_ARG, "q, k_new, v_new, ctx_lens and out must be non-NULL");
@@ -238,7 +238,7 @@ int decode_impl(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, c
     mimo::DecodeArgs a{q, k_new, v_new, k_cache, v_cache, kv_base, ctx_lens, sink, out, lse, workspace, batch,
                        max_ctx, min_units(split_tokens), dims->num_q_heads, dims->num_kv_heads, dims->sliding_window,
                        dims->softmax_scale, dims->value_scale};
-    a.max_chunks = mimo::kGaMaxChunks;
+    a.max_chunks = max_chunks;
     a.pages = pt;
     if (fp8) {
         a.k_cache8 = fp8->k;
@@ -260,8 +260,8 @@ int decode_impl(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, c
     }
     if (!kv_base && !pages) return fail(MIMO_ERR_INVALID_ARG, "GA decode needs kv_base");
     if (batch > kMaxGridYZ) return fail(MIMO_ERR_UNSUPPORTED, "GA decode batch %d above %d", batch, kMaxGridYZ);
-    const size_t need =
-        mimo::ga_workspace_bytes(batch, mimo::ga_grid_chunks(batch, max_ctx, a.min_units), dims->num_q_heads);
+    const size_t need = mimo::ga_workspace_bytes(batch, mimo::ga_grid_chunks(batch, max_ctx, a.min_units, max_chunks),
+                                                 dims->num_q_heads);
     if (!workspace || workspace_bytes < need)
         return fail(MIMO_ERR_WORKSPACE, "GA decode needs %zu workspace bytes (got %zu%s)", need, workspace_bytes,
                     workspace ? "" : ", NULL");
@@ -317,6 +317,32 @@ int mimo_attn_decode(const mimo_attn_dims* dims, int layer_type, const uint16_t*
                      uint16_t* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     return decode_impl(dims, layer_type, q, k_new, v_new, k_cache, v_cache, kv_base, nullptr, ctx_lens, batch,
                        max_ctx, split_tokens, sink, out, lse, workspace, workspace_bytes, stream);
+}
+
+int mimo_attn_decode_noalloc(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, const uint16_t* k_new,
+                             const uint16_t* v_new, const uint16_t* k_cache, const uint16_t* v_cache,
+                             const int64_t* kv_base, const int32_t* ctx_lens, int32_t batch, int32_t max_ctx,
+                             int32_t split_tokens, const float* sink, uint16_t* out, float* lse, hipStream_t stream) {
+    if (int st = check_dims(dims, layer_type, 2)) return st;
+    if (layer_type == MIMO_LAYER_SWA)  // SWA decode uses no workspace
+        return decode_impl(dims, layer_type, q, k_new, v_new, k_cache, v_cache, kv_base, nullptr, ctx_lens, batch,
+                           max_ctx, split_tokens, sink, out, lse, nullptr, 0, stream);
+    if (batch < 1 || batch > kMaxGridYZ) return fail(MIMO_ERR_INVALID_ARG, "batch %d outside [1, %d]", batch, kMaxGridYZ);
+    // The chunk count is capped so that header + (chunks + batch) slots fit the scratch array.
+    const size_t slot = (size_t)dims->num_q_heads * (2 + 128) * sizeof(float);
+    const size_t header = mimo::ga_header_bytes(batch);
+    const size_t room = mimo::kNoAllocScratchBytes > header ? (mimo::kNoAllocScratchBytes - header) / slot : 0;
+    const long long chunks = (long long)room - batch;
+    if (chunks < 1)
+        return fail(MIMO_ERR_UNSUPPORTED,
+                    "batch %d with %d query heads needs more than the %zu-byte scratch of the no-allocation decode "
+                    "(use mimo_attn_decode with a workspace)",
+                    batch, dims->num_q_heads, (size_t)mimo::kNoAllocScratchBytes);
+    void* ws = nullptr;
+    if (int st = hip_status(mimo::noalloc_scratch(&ws), "no-allocation scratch lookup")) return st;
+    return decode_impl(dims, layer_type, q, k_new, v_new, k_cache, v_cache, kv_base, nullptr, ctx_lens, batch,
+                       max_ctx, split_tokens, sink, out, lse, ws, mimo::kNoAllocScratchBytes, stream, nullptr, false,
+                       nullptr, (int)(chunks < mimo::kGaMaxChunks ? chunks : mimo::kGaMaxChunks));
 }
 
 int mimo_attn_decode_append(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, const uint16_t* k_new,

@@ -36,10 +36,42 @@
 // picked out per half-tile with a lane read, so the streaming loop issues no
 // dependent table loads; tiles, their order and the arithmetic are those of
 // the contiguous pool.
+#include <mutex>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
+// Device memory of the no-allocation decode entry point (GA workspace: plan
+// header and partial results).  Each GPU the library runs on holds its own
+// copy until the process ends.  Host code must not use this name as an
+// address: it is a host-side stand-in; noalloc_scratch() returns the device's
+// own address of it, looked up once per device.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[mimo::kNoAllocScratchBytes];
+
 namespace mimo {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 namespace {
 
 constexpr int kDqk = 192;

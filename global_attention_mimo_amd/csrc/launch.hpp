@@ -109,6 +109,11 @@ inline size_t ga_header_bytes(int batch) { return ((size_t)(batch + 2) * 8 + 255
 inline size_t ga_workspace_bytes(int batch, int chunks, int hq) {
     return ga_header_bytes(batch) + (size_t)(chunks + batch) * (size_t)hq * (2 + 128) * sizeof(float);
 }
+// Bytes of the per-device scratch array of mimo_attn_decode_noalloc.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+// The calling thread's current device's address of that array (looked up with
+// hipGetSymbolAddress on the first call per device, then cached).
+hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_decode_swa(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_ga(const DecodeArgs& a, hipStream_t stream);
 

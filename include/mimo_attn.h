@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define MIMO_ATTN_ABI_VERSION 7
+#define MIMO_ATTN_ABI_VERSION 8
 
 /* Layer type: which key set a query sees (model doc, Key features; config
  * layer_types). */
@@ -199,6 +199,30 @@ int mimo_attn_decode(const mimo_attn_dims* dims, int layer_type,
                      int32_t batch, int32_t max_ctx, int32_t split_tokens,
                      const float* sink, uint16_t* out, float* lse,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * mimo_attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Arguments, results and errors are those
+ * of mimo_attn_decode (split_tokens included); the GA plan header and partial
+ * results live in a 32 MiB device array inside the library, one per GPU the
+ * library runs on, held until the process ends (its address is looked up
+ * once per device, on the first call there).  The call itself allocates and
+ * frees nothing.  Limit: the plan needs a 256-byte-padded header of batch + 2
+ * int64 plus (chunks + batch) slots of Hq * 520 bytes within the 32 MiB; the
+ * chunk count is capped to fit (results then differ from mimo_attn_decode
+ * only by fp32 rounding), and a batch too large for even one chunk is
+ * MIMO_ERR_UNSUPPORTED (with 64 query heads, up to about 1,000 sequences fit).
+ * SWA needs no scratch.  Every call on a GPU shares that GPU's array: calls
+ * that overlap in time on one GPU (concurrent streams, threads) race and give
+ * wrong results; serialise them.
+ */
+int mimo_attn_decode_noalloc(const mimo_attn_dims* dims, int layer_type,
+                             const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                             const uint16_t* k_cache, const uint16_t* v_cache,
+                             const int64_t* kv_base, const int32_t* ctx_lens,
+                             int32_t batch, int32_t max_ctx, int32_t split_tokens,
+                             const float* sink, uint16_t* out, float* lse, hipStream_t stream);
 
 /*
  * KV append: writes new tokens' keys and values into the caches (model doc,

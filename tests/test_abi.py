@@ -42,7 +42,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_version_and_status_strings(L):
-    assert B.mimo_abi_version() == 7
+    assert B.mimo_abi_version() == 8
     assert B.mimo_status_string(0) == "MIMO_OK"
     assert B.mimo_status_string(3) == "MIMO_ERR_WORKSPACE"
     assert B.mimo_status_string(99) == "MIMO_ERR_UNKNOWN"
@@ -141,6 +141,25 @@ def decode_call(L, dims=None, layer=1, q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAK
 ])
 def test_decode_rejects(L, case, status):
     assert decode_call(L, **case) == status
+
+
+def noalloc_call(L, dims=None, layer=1, batch=2, max_ctx=100):
+    d = dims or B.make_dims()
+    return L.mimo_attn_decode_noalloc(ctypes.byref(d), layer, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, batch, max_ctx,
+                                      0, None, FAKE, None, None)
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(layer=5), B.MIMO_ERR_INVALID_ARG),
+    (dict(batch=0), B.MIMO_ERR_INVALID_ARG),
+    (dict(dims=B.make_dims(head_dim_qk=64)), B.MIMO_ERR_UNSUPPORTED),
+    (dict(batch=1008), B.MIMO_ERR_UNSUPPORTED),                                   # scratch holds 1007 slots of 64 heads
+    (dict(batch=300, dims=B.make_dims(num_q_heads=256, num_kv_heads=16)), B.MIMO_ERR_UNSUPPORTED),
+])
+def test_noalloc_rejects_before_touching_the_device(L, case, status):
+    """Checks that need no GPU: the scratch capacity (32 MiB) is a host-side bound."""
+    assert noalloc_call(L, **case) == status
+    assert B.mimo_last_error() != ""
 
 
 def decode_append_call(L, layer=1, q=FAKE, kc=FAKE, base=FAKE, cap=FAKE, ctx=FAKE, batch=2):
