@@ -31,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from global_attention_mimo_amd import binding as B  # noqa: E402
+from global_attention_mimo_amd import prof  # noqa: E402
 from global_attention_mimo_amd import synth  # noqa: E402
 
 HQ, HKV, DQK, DV, W = 64, 4, 192, 128, 129
@@ -70,31 +71,15 @@ def decode_stats(ctx, layer_type, window=W):
     return flops, bytes_
 
 
-def code_digest(paths):
-    """sha256 over the given sources with comments and whitespace removed, so that a
-    record stays valid across comment edits but not across any change to the code."""
-    import hashlib
-    import re
-    h = hashlib.sha256()
-    for src in paths:
-        text = open(os.path.join(ROOT, src), encoding="utf-8").read()
-        if src.endswith(".py"):
-            text = re.sub(r"#[^\n]*", "", text)
-        else:
-            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-            text = re.sub(r"//[^\n]*", "", text)
-        h.update(re.sub(r"\s+", "", text).encode())
-    return h.hexdigest()
-
-
 def measured_traffic(record="profiles/prefill_ga_1x32768_traffic.json"):
-    """HBM bytes per GA-prefill launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    record (copy-calibrated), or None when the kernel code changed since it was taken."""
+    """HBM bytes per GA-prefill launch from the rocprofv3 FETCH_SIZE/WRITE_SIZE record
+    that `python -m global_attention_mimo_amd.prof report --suite step` writes
+    (copy-calibrated), or None when the kernel code changed since it was taken."""
     path = os.path.join(ROOT, record)
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if code_digest(rec["sources"]) != rec.get("code_sha256"):
+    if prof.code_digest(rec["sources"]) != rec.get("code_sha256"):
         return None
     return rec["read_bytes"] + rec["write_bytes"]
 
@@ -436,60 +421,110 @@ def _hip_attribute(name, value):
     return out.value if hip.hipDeviceGetAttribute(ctypes.byref(out), value, 0) == 0 else 0
 
 
-def cpu_baseline(swa, ga, dga, ctx, budget_s):
-    """The fp64 oracle, as it stands, on a bounded sample of the same workload."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(swa, ga, dga, dswa, ctx, gpu):
+    """The fp64 oracle, as it stands, timed per configuration on the host cores,
+    next to the GPU figure of the same configuration (`gpu`: name -> dict).
+    Configs 1, 2 and 4-SWA run in full; configs 3, 4-GA and 5 run on a sample and
+    their time is extrapolated by algorithmic flops (labelled as such)."""
     import oracle
     orc = oracle.get()
     nth = orc.default_threads()
     scale = float(np.float32(synth.SOFTMAX_SCALE))
     rng = np.random.default_rng(0)
-    flops = 0
-    t0 = time.perf_counter()
-    parts = []
-    # SWA prefill rows: 64 random tokens of the 4x8192 batch (all their heads).
-    T = swa.q.shape[0]
-    rows = np.sort(rng.choice(T, 64, replace=False))
-    take = torch.as_tensor(rows)
-    # The oracle reads host copies of the device buffers; only the rows' keys are needed,
-    # but the SWA batch is small enough to copy whole.
-    qb, kb, vb = (synth.bf16_bits(t) for t in (swa.q, swa.k, swa.v))
-    orc.prefill(qb, kb, vb, swa.cu_seqlens.cpu().numpy(), layer_type=0, scale=scale, sink=swa.sink.cpu().numpy(),
-                rows=rows, nthreads=nth)
-    cu = swa.cu_seqlens.cpu().numpy()
-    pos = rows - cu[np.searchsorted(cu, rows, side="right") - 1]
-    flops += int(np.minimum(pos + 1, W).sum()) * HQ * FLOP_PER_TRIPLE
-    parts.append("64 SWA-prefill query tokens")
-    del take
-    # GA prefill rows: random tokens of the 32768 sequence until the budget's half is used.
-    qb, kb, vb = (synth.bf16_bits(t) for t in (ga.q, ga.k, ga.v))
-    cu = ga.cu_seqlens.cpu().numpy()
-    n_ga = 0
-    while time.perf_counter() - t0 < 0.5 * budget_s and n_ga < 256:
-        r = np.sort(rng.choice(qb.shape[0], 8, replace=False))
-        orc.prefill(qb, kb, vb, cu, layer_type=1, scale=scale, sink=ga.sink.cpu().numpy(), rows=r, nthreads=nth)
-        flops += int((r + 1).sum()) * HQ * FLOP_PER_TRIPLE
-        n_ga += 8
-    parts.append(f"{n_ga} GA-prefill query tokens")
-    del qb, kb, vb
-    # GA decode: whole sequences of the 128-sequence batch until the budget is used.
+    rows, tot_flops, tot_s = {}, 0, 0.0
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    def record(name, flops_done, secs, flops_config, coverage):
+        nonlocal tot_flops, tot_s
+        tot_flops += flops_done
+        tot_s += secs
+        est = secs * flops_config / flops_done
+        r = {"coverage": coverage, "oracle_s": secs, "oracle_GFLOP_s": flops_done / secs / 1e9,
+             "oracle_config_s": est, "oracle_config_s_kind": "measured" if flops_done == flops_config else
+             "extrapolated by algorithmic flops"}
+        if name in gpu and gpu[name].get("ms"):
+            r["gpu_ms"] = gpu[name]["ms"]
+            r["gpu_speedup"] = est * 1e3 / gpu[name]["ms"]
+        rows[name] = r
+        log(f"cpu_baseline {name}: {coverage}, {secs:.1f} s")
+
+    # 1: SWA prefill 1 x 256, whole configuration.
+    x1 = synth.prefill_inputs([256], seed=0)
+    b1 = [synth.bf16_bits(t) for t in (x1.q, x1.k, x1.v)]
+    f1 = prefill_pairs([256], 0) * HQ * FLOP_PER_TRIPLE
+    s1 = timed(lambda: orc.prefill(*b1, x1.cu_seqlens.numpy(), layer_type=0, scale=scale, sink=x1.sink.numpy(),
+                                   nthreads=nth))
+    record("config1_swa_prefill_1x256", f1, s1, f1, "full")
+    # 2: SWA prefill 4 x 8192, whole configuration.
+    b2 = [synth.bf16_bits(t) for t in (swa.q, swa.k, swa.v)]
+    cu2, sk2 = swa.cu_seqlens.cpu().numpy(), swa.sink.cpu().numpy()
+    f2 = prefill_pairs([8192] * 4, 0) * HQ * FLOP_PER_TRIPLE
+    s2 = timed(lambda: orc.prefill(*b2, cu2, layer_type=0, scale=scale, sink=sk2, nthreads=nth))
+    record("config2_swa_prefill_4x8192", f2, s2, f2, "full (32768 tokens)")
+    del b2
+    # 3: GA prefill 1 x 32768: 32 rows spread over the sequence.
+    b3 = [synth.bf16_bits(t) for t in (ga.q, ga.k, ga.v)]
+    r3 = np.sort(rng.choice(32768, 32, replace=False))
+    f3s = int((r3 + 1).sum()) * HQ * FLOP_PER_TRIPLE
+    s3 = timed(lambda: orc.prefill(*b3, ga.cu_seqlens.cpu().numpy(), layer_type=1, scale=scale,
+                                   sink=ga.sink.cpu().numpy(), rows=r3, nthreads=nth))
+    record("config3_ga_prefill_1x32768", f3s, s3, prefill_pairs([32768], 1) * HQ * FLOP_PER_TRIPLE,
+           "32 random query rows of 32768")
+    del b3
+    # 4-GA: 4 whole sequences of the 128.
     base = dga.kv_base.cpu().numpy()
-    n_dec = 0
-    order = rng.permutation(len(ctx))
-    for b in order:
-        if time.perf_counter() - t0 >= budget_s or n_dec >= 8:
-            break
+    pick = rng.choice(len(ctx), 4, replace=False)
+    f4s, s4 = 0, 0.0
+    for b in pick:
         c = int(ctx[b])
         kc = synth.bf16_bits(dga.k_cache[base[b]:base[b] + c])
         vc = synth.bf16_bits(dga.v_cache[base[b]:base[b] + c])
-        orc.decode(synth.bf16_bits(dga.q[b:b + 1]), synth.bf16_bits(dga.k_new[b:b + 1]),
-                   synth.bf16_bits(dga.v_new[b:b + 1]), kc, vc, np.array([c], np.int32), layer_type=1, scale=scale,
-                   sink=dga.sink.cpu().numpy(), kv_base=np.zeros(1, np.int64), nthreads=nth)
-        flops += (c + 1) * HQ * FLOP_PER_TRIPLE
-        n_dec += 1
-    parts.append(f"{n_dec} GA-decode sequences")
-    dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": nth, "kind": "oracle",
-            "sample": "; ".join(parts) + f" of the bench workload ({flops / 1e9:.1f} GFLOP in {dt:.1f} s, fp64)"}
+        args = [synth.bf16_bits(t[b:b + 1]) for t in (dga.q, dga.k_new, dga.v_new)]
+        s4 += timed(lambda: orc.decode(*args, kc, vc, np.array([c], np.int32), layer_type=1, scale=scale,
+                                       sink=dga.sink.cpu().numpy(), kv_base=np.zeros(1, np.int64), nthreads=nth))
+        f4s += (c + 1) * HQ * FLOP_PER_TRIPLE
+    record("config4_ga_decode_b128", f4s, s4, sum(int(c) + 1 for c in ctx) * HQ * FLOP_PER_TRIPLE,
+           "4 of the 128 sequences, whole")
+    # 4-SWA: all 128 sequences over the ring.
+    a5 = [synth.bf16_bits(t) for t in (dswa.q, dswa.k_new, dswa.v_new, dswa.k_cache, dswa.v_cache)]
+    f4w = len(ctx) * W * HQ * FLOP_PER_TRIPLE
+    s4w = timed(lambda: orc.decode(*a5, np.asarray(ctx, np.int32), layer_type=0, scale=scale,
+                                   sink=dswa.sink.cpu().numpy(), nthreads=nth))
+    record("config4_swa_decode_b128", f4w, s4w, f4w, f"full ({len(ctx)} sequences)")
+    # 5: the 48-layer stack: 24 rows of one prompt of median length per layer type, extrapolated to the
+    # stack's prefill flops (8 GA + 40 SWA layers) and 64 decode steps of all 48 layers.
+    lengths = synth.hybrid_prompt_lengths(32, seed=0)
+    Lm = int(np.median(lengths))
+    x5 = synth.prefill_inputs([Lm], seed=1000)
+    b5 = [synth.bf16_bits(t) for t in (x5.q, x5.k, x5.v)]
+    r5 = np.sort(rng.choice(Lm, 24, replace=False))
+    f5s, s5 = 0, 0.0
+    for lt in (0, 1):
+        s5 += timed(lambda: orc.prefill(*b5, x5.cu_seqlens.numpy(), layer_type=lt, scale=scale, sink=x5.sink.numpy(),
+                                        rows=r5, nthreads=nth))
+        f5s += int(np.minimum(r5 + 1, W if lt == 0 else 1 << 40).sum()) * HQ * FLOP_PER_TRIPLE
+    f5 = (8 * prefill_pairs(lengths, 1) + 40 * prefill_pairs(lengths, 0)) * HQ * FLOP_PER_TRIPLE
+    f5 += sum(8 * sum(L + s + 1 for L in lengths) + 40 * len(lengths) * W for s in range(64)) * HQ * FLOP_PER_TRIPLE
+    record("config5_hybrid_stack", f5s, s5, f5, f"24 query rows of a {Lm}-token prompt per layer type")
+    return {"value": tot_flops / tot_s / 1e12, "unit": "TFLOP/s", "cores": nth, "kind": "oracle",
+            "cpu_model": _cpu_model(),
+            "sample": f"per configuration below; {tot_flops / 1e9:.1f} GFLOP of fp64 oracle work in {tot_s:.1f} s "
+                      f"on {nth} host threads (configs 1, 2 and 4-SWA whole, 3, 4-GA and 5 sampled)",
+            "configs": rows}
 
 
 def main():
@@ -497,7 +532,6 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next-rows", action="store_true",
                     help="skip the rows timed apart from the step (chunked prefill, paged and FP8 pools, "
@@ -669,6 +703,14 @@ def main():
         "roofline": roof,
         "device": dev_ctx,
     }
+    # Config 1 (the small parity configuration, SWA prefill 1 x 256): latency, no roofline target.
+    x1 = synth.prefill_inputs([256], seed=0, device=dev)
+    o1 = torch.empty((256, HQ, DV), dtype=torch.bfloat16, device=dev)
+    l1 = torch.empty((256, HQ), dtype=torch.float32, device=dev)
+    small_ms = _time_ms(lambda: B.mimo_attn_prefill(dims, 0, x1.q, x1.k, x1.v, x1.cu_seqlens, 1, 256, x1.sink, o1, l1),
+                        20)
+    res["config1_swa_prefill_1x256"] = {"ms": small_ms,
+                                        "TFLOP/s": tf(prefill_pairs([256], 0) * HQ * FLOP_PER_TRIPLE, small_ms)}
     if not args.no_next_rows:
         res["next_rows"] = {**chunk_rows(dims, ga, swa), **paged_rows(dims, dga, ctx_ga, max_ctx, ws, ga),
                             **fp8_rows(dims, dga, ctx_ga, max_ctx, ws),
@@ -679,7 +721,14 @@ def main():
         res["hybrid_stack"] = hybrid_rows(dims)["hybrid_stack"]
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample (cpu_baseline)")
-        res["cpu_baseline"] = cpu_baseline(swa, ga, dga, ctx0, args.cpu_budget)
+        gpu = {"config2_swa_prefill_4x8192": breakdown["prefill_swa"],
+               "config3_ga_prefill_1x32768": breakdown["prefill_ga"],
+               "config4_ga_decode_b128": breakdown["decode_ga"], "config4_swa_decode_b128": breakdown["decode_swa"],
+               "config1_swa_prefill_1x256": {"ms": small_ms}}
+        if "hybrid_stack" in res:
+            h = res["hybrid_stack"]
+            gpu["config5_hybrid_stack"] = {"ms": h["prefill_ms"] + 64 * h["decode_step_ms"]}
+        res["cpu_baseline"] = cpu_baseline(swa, ga, dga, dswa, ctx0, gpu)
     print(json.dumps(res), flush=True)
 
 
