@@ -273,6 +273,45 @@ def rope_rows(dims, ga, reps=5):
                         "GB/s": nbytes / (ms * 1e-3) / 1e9, "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS}}
 
 
+def rope_fused_rows(dims, ga, swa, reps=5):
+    """Prefill with the rotary embedding fused in (mimo_attn_prefill_rope: K
+    rotated into k_rot with the tokens' cos/sin table, Q rotated as the kernels
+    load it) against the separate rotation of q and k (mimo_rope_apply) followed
+    by mimo_attn_prefill, on the step's SWA 4 x 8192 and GA 1 x 32768 inputs;
+    rotary dims 64, theta 1e4 (SWA) and 5e6 (GA)."""
+    dev = "cuda"
+    res = {}
+    for name, x, lt, nseq, L, theta in (("prefill_rope_swa", swa, 0, 4, 8192, 1e4),
+                                        ("prefill_rope_ga", ga, 1, 1, 32768, 5e6)):
+        T = x.q.shape[0]
+        pos = torch.cat([torch.arange(L, dtype=torch.int32, device=dev)] * nseq)
+        out = torch.empty((T, HQ, DV), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((T, HQ), dtype=torch.float32, device=dev)
+        krot = torch.empty_like(x.k)
+        ws = torch.empty(B.mimo_attn_prefill_rope_workspace_size(dims, T, 64) // 4 + 4, dtype=torch.float32,
+                         device=dev)
+        fused = lambda: B.mimo_attn_prefill_rope(dims, lt, x.q, x.k, x.v, pos, x.cu_seqlens, nseq, L, T, theta, 64,
+                                                 x.sink, out, lse, krot, ws)
+        q2, k2 = x.q.clone(), x.k.clone()
+
+        def separate():
+            B.mimo_rope_apply(dims, q2, k2, pos, T, theta, 64)
+            B.mimo_attn_prefill(dims, lt, q2, k2, x.v, x.cu_seqlens, nseq, L, x.sink, out, lse)
+        ms_f, ms_s = _time_ms(fused, reps), _time_ms(separate, reps)
+        f = prefill_pairs([L] * nseq, lt) * HQ * FLOP_PER_TRIPLE
+        res[name] = {"workload": f"{nseq} x {L} tokens, {'GA' if lt else 'SWA'}, rotary dims 64, theta {theta:g}",
+                     "ms": ms_f, "TFLOP/s": f / (ms_f * 1e-3) / 1e12, "separate_rope_then_prefill_ms": ms_s,
+                     "saved_ms": ms_s - ms_f}
+        if lt == 0:
+            res[name]["GB/s"] = T * TOKEN_BYTES / (ms_f * 1e-3) / 1e9
+            res[name]["frac_hbm_peak"] = res[name]["GB/s"] / PEAK_HBM_GBPS
+        else:
+            res[name]["frac_mfma_peak"] = res[name]["TFLOP/s"] / PEAK_BF16_TFLOPS
+        del out, lse, krot, ws, q2, k2
+    torch.cuda.empty_cache()
+    return res
+
+
 def hybrid_rows(dims, decode_steps=64):
     """The 48-layer hybrid stack (5 SWA : 1 GA), timed end to end: 32 prompts with
     lengths log-uniform in [512, 32768] (seed 0), a varlen prefill of every layer
@@ -715,7 +754,7 @@ def main():
         res["next_rows"] = {**chunk_rows(dims, ga, swa), **paged_rows(dims, dga, ctx_ga, max_ctx, ws, ga),
                             **fp8_rows(dims, dga, ctx_ga, max_ctx, ws),
                             **backward_rows(dims, ga, swa, out_ga, lse_ga, out_swa, lse_swa),
-                            **rope_rows(dims, ga)}
+                            **rope_rows(dims, ga), **rope_fused_rows(dims, ga, swa)}
     if not args.no_next_rows and not args.no_hybrid:
         log("hybrid stack: 48-layer prefill and decode")
         res["hybrid_stack"] = hybrid_rows(dims)["hybrid_stack"]

@@ -30,6 +30,7 @@ ENTRY_POINTS = ("mimo_attn_prefill", "mimo_attn_prefill_chunk", "mimo_attn_decod
                 "mimo_attn_decode_paged",
                 "mimo_attn_prefill_chunk_paged", "mimo_kv_append_fp8", "mimo_attn_decode_fp8",
                 "mimo_attn_prefill_backward_workspace_size", "mimo_attn_prefill_backward", "mimo_rope_apply",
+                "mimo_attn_prefill_rope_workspace_size", "mimo_attn_prefill_rope",
                 "mimo_status_string",
                 "mimo_last_error", "mimo_abi_version")
 
@@ -105,6 +106,11 @@ def lib() -> ctypes.CDLL:
                                                  _P, _P, _P, _P, _P, _P, _SZ, _P]
         L.mimo_rope_apply.restype = ctypes.c_int
         L.mimo_rope_apply.argtypes = [dims_p, _P, _P, _P, _I32, ctypes.c_float, _I32, _P]
+        L.mimo_attn_prefill_rope_workspace_size.restype = _SZ
+        L.mimo_attn_prefill_rope_workspace_size.argtypes = [dims_p, _I32, _I32]
+        L.mimo_attn_prefill_rope.restype = ctypes.c_int
+        L.mimo_attn_prefill_rope.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _P, _I32, _I32, _I32,
+                                             ctypes.c_float, _I32, _P, _P, _P, _P, _P, _SZ, _P]
         L.mimo_status_string.restype = ctypes.c_char_p
         L.mimo_status_string.argtypes = [ctypes.c_int]
         L.mimo_last_error.restype = ctypes.c_char_p
@@ -276,6 +282,20 @@ def mimo_rope_apply(dims: mimo_attn_dims, q, k, positions, total_tokens: int, ro
                                  rotary_dim, _stream(stream)))
 
 
+def mimo_attn_prefill_rope_workspace_size(dims: mimo_attn_dims, total_tokens: int, rotary_dim: int) -> int:
+    return int(lib().mimo_attn_prefill_rope_workspace_size(ctypes.byref(dims), total_tokens, rotary_dim))
+
+
+def mimo_attn_prefill_rope(dims: mimo_attn_dims, layer_type: int, q, k, v, positions, cu_seqlens, num_seqs: int,
+                           max_seqlen: int, total_tokens: int, rope_theta: float, rotary_dim: int, sink, out, lse,
+                           k_rot, workspace, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().mimo_attn_prefill_rope(ctypes.byref(dims), layer_type, _ptr(q), _ptr(k), _ptr(v), _ptr(positions),
+                                        _ptr(cu_seqlens), num_seqs, max_seqlen, total_tokens, rope_theta, rotary_dim,
+                                        _ptr(sink), _ptr(out), _ptr(lse), _ptr(k_rot), _ptr(workspace), ws_bytes,
+                                        _stream(stream)))
+
+
 # -- tensor-level conveniences (allocation of outputs + the calls above) -------
 
 def prefill(q, k, v, cu_seqlens, max_seqlen: int, layer_type: int, sink=None, dims=None, out=None, lse=None,
@@ -409,6 +429,24 @@ def prefill_backward(q, k, v, out, lse, dout, cu_seqlens, max_seqlen: int, layer
     mimo_attn_prefill_backward(dims, layer_type, q, k, v, out, lse, dout, cu_seqlens, cu_seqlens.numel() - 1,
                                max_seqlen, T, sink, dq, dk, dv, dsink, ws, stream)
     return dq, dk, dv, dsink
+
+
+def prefill_rope(q, k, v, positions, cu_seqlens, max_seqlen: int, layer_type: int, rope_theta: float,
+                 rotary_dim: int, sink=None, dims=None, out=None, lse=None, k_rot=None, stream=None):
+    """Fused-RoPE prefill; returns (out, lse, k_rot)."""
+    dims = dims or make_dims()
+    T = q.shape[0]
+    if out is None:
+        out = torch.empty((T, dims.num_q_heads, dims.head_dim_v), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, dims.num_q_heads), dtype=torch.float32, device=q.device)
+    if k_rot is None:
+        k_rot = torch.empty_like(k)
+    nbytes = mimo_attn_prefill_rope_workspace_size(dims, T, rotary_dim)
+    ws = torch.empty(max(nbytes, 16) // 4 + 4, dtype=torch.float32, device=q.device)
+    mimo_attn_prefill_rope(dims, layer_type, q, k, v, positions, cu_seqlens, cu_seqlens.numel() - 1, max_seqlen, T,
+                           rope_theta, rotary_dim, sink, out, lse, k_rot, ws, stream)
+    return out, lse, k_rot
 
 
 def rope_apply(q, k, positions, rope_theta: float, rotary_dim: int, dims=None, stream=None):

@@ -434,6 +434,49 @@ int mimo_attn_prefill_backward(const mimo_attn_dims* dims, int layer_type, const
     return hip_status(mimo::launch_prefill_backward(a, stream), "backward launch");
 }
 
+size_t mimo_attn_prefill_rope_workspace_size(const mimo_attn_dims* dims, int32_t total_tokens, int32_t rotary_dim) {
+    if (check_dims(dims, MIMO_LAYER_GA, 1) != MIMO_OK || total_tokens < 0 || rotary_dim < 32 ||
+        rotary_dim > dims->head_dim_qk || rotary_dim % 32)
+        return 0;
+    return mimo::rope_table_bytes(total_tokens, rotary_dim);
+}
+
+int mimo_attn_prefill_rope(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, const uint16_t* k,
+                           const uint16_t* v, const int32_t* positions, const int32_t* cu_seqlens, int32_t num_seqs,
+                           int32_t max_seqlen, int32_t total_tokens, float rope_theta, int32_t rotary_dim,
+                           const float* sink, uint16_t* out, float* lse, uint16_t* k_rot, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+    if (int st = check_dims(dims, layer_type, 1)) return st;
+    if (!q || !k || !v || !positions || !cu_seqlens || !out || !k_rot)
+        return fail(MIMO_ERR_INVALID_ARG, "q, k, v, positions, cu_seqlens, out and k_rot must be non-NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(k_rot))
+        return fail(MIMO_ERR_INVALID_ARG, "q, k, v, out and k_rot must be 16-byte aligned");
+    if (num_seqs < 1 || num_seqs > kMaxGridYZ)
+        return fail(MIMO_ERR_INVALID_ARG, "num_seqs %d outside [1, %d]", num_seqs, kMaxGridYZ);
+    if (max_seqlen < 0) return fail(MIMO_ERR_INVALID_ARG, "max_seqlen %d is negative", max_seqlen);
+    if (total_tokens < 0) return fail(MIMO_ERR_INVALID_ARG, "total_tokens %d is negative", total_tokens);
+    if (!std::isfinite(rope_theta) || !(rope_theta > 1.0f))
+        return fail(MIMO_ERR_INVALID_ARG, "rope_theta must be finite and above 1");
+    if (rotary_dim < 32 || rotary_dim > dims->head_dim_qk || rotary_dim % 32)
+        return fail(MIMO_ERR_UNSUPPORTED, "fused RoPE needs rotary_dim a multiple of 32 in [32, %d] (got %d)",
+                    dims->head_dim_qk, rotary_dim);
+    if (max_seqlen == 0 || total_tokens == 0) return ok();
+    const size_t need = mimo::rope_table_bytes(total_tokens, rotary_dim);
+    if (!workspace || workspace_bytes < need)
+        return fail(MIMO_ERR_WORKSPACE, "fused RoPE needs %zu workspace bytes (got %zu%s)", need, workspace_bytes,
+                    workspace ? "" : ", NULL");
+    if (!aligned16(workspace)) return fail(MIMO_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    mimo::RopePrepArgs r{k, positions, k_rot, static_cast<float*>(workspace), total_tokens, dims->num_kv_heads,
+                         rotary_dim, (double)rope_theta};
+    if (int st = hip_status(mimo::launch_rope_prep(r, stream), "RoPE preparation launch")) return st;
+    mimo::PrefillArgs a{q, k_rot, v, cu_seqlens, sink, out, lse, num_seqs, max_seqlen, dims->num_q_heads,
+                        dims->num_kv_heads, dims->sliding_window, dims->softmax_scale, dims->value_scale,
+                        layer_type == MIMO_LAYER_SWA};
+    a.rope_tab = static_cast<const float*>(workspace);
+    a.rope_half = rotary_dim / 2;
+    return hip_status(mimo::launch_prefill(a, stream), "prefill launch");
+}
+
 int mimo_rope_apply(const mimo_attn_dims* dims, uint16_t* q, uint16_t* k, const int32_t* positions,
                     int32_t total_tokens, float rope_theta, int32_t rotary_dim, hipStream_t stream) {
     if (int st = check_dims(dims, MIMO_LAYER_GA, 1)) return st;

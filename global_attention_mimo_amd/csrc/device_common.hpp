@@ -87,6 +87,60 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, floa
     return __builtin_bit_cast(bf16x8, u);
 }
 
+// Rotary embedding of one pair of dims (x, y) = (i, i + rd/2) of a head
+// vector by the angle whose fp32 cosine and sine are c and s (Transformers'
+// rotary convention; model doc, MiMoV2FlashConfig: rope_parameters).  The
+// standalone RoPE pass and the rotation of Q fragments in the prefill kernels
+// share this arithmetic, so both round to the same bf16 values.
+__device__ __forceinline__ void rope_pair(float x, float y, float c, float s, float& xo, float& yo) {
+    xo = __builtin_fmaf(x, c, -y * s);
+    yo = __builtin_fmaf(y, c, x * s);
+}
+
+__device__ __forceinline__ float bf16_word_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_word_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// Rotates Q^T fragments in place: frag[s] holds dims 16s + 8hh .. +7 of one
+// query row (the MFMA B-operand layout of the prefill kernels), so with
+// rd = 32 * NRS rotated dims the pair of dim i = 16s + 8hh + t is dim i + rd/2
+// in frag[s + NRS], same lane and slot.  tab holds the row's token's
+// (cos, sin) pairs, fp32, for i = 0 .. rd/2 - 1.
+template <int NRS>
+__device__ __forceinline__ void rope_frags(bf16x8* frag, const float* tab, int hh) {
+#pragma unroll
+    for (int s = 0; s < NRS; ++s) {
+        const f32x4* cs = reinterpret_cast<const f32x4*>(tab + 2 * (16 * s + 8 * hh));
+        const f32x4 c0 = cs[0], c1 = cs[1], c2 = cs[2], c3 = cs[3];  // (cos, sin) of 8 consecutive dims
+        const float c[8] = {c0[0], c0[2], c1[0], c1[2], c2[0], c2[2], c3[0], c3[2]};
+        const float sn[8] = {c0[1], c0[3], c1[1], c1[3], c2[1], c2[3], c3[1], c3[3]};
+        u32x4 x = __builtin_bit_cast(u32x4, frag[s]), y = __builtin_bit_cast(u32x4, frag[s + NRS]);
+        u32x4 xo, yo;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            float a0, a1, b0, b1;
+            rope_pair(bf16_word_lo(x[w]), bf16_word_lo(y[w]), c[2 * w], sn[2 * w], a0, b0);
+            rope_pair(bf16_word_hi(x[w]), bf16_word_hi(y[w]), c[2 * w + 1], sn[2 * w + 1], a1, b1);
+            xo[w] = pack_bf16x2(a0, a1);
+            yo[w] = pack_bf16x2(b0, b1);
+        }
+        frag[s] = __builtin_bit_cast(bf16x8, xo);
+        frag[s + NRS] = __builtin_bit_cast(bf16x8, yo);
+    }
+}
+
+// rope_frags for the rd (a multiple of 32, at most 192) known at run time.
+__device__ __forceinline__ void rope_frags_rd(bf16x8* frag, const float* tab, int rope_half, int hh) {
+    switch (rope_half / 16) {
+        case 1: rope_frags<1>(frag, tab, hh); break;
+        case 2: rope_frags<2>(frag, tab, hh); break;
+        case 3: rope_frags<3>(frag, tab, hh); break;
+        case 4: rope_frags<4>(frag, tab, hh); break;
+        case 5: rope_frags<5>(frag, tab, hh); break;
+        case 6: rope_frags<6>(frag, tab, hh); break;
+        default: break;
+    }
+}
+
 // Orders this wave's earlier LDS writes before its later LDS reads (the
 // compiler must not move accesses across it; the hardware keeps a wave's LDS
 // operations in order).

@@ -27,6 +27,10 @@ struct PrefillArgs {
     int num_seqs, max_seqlen, hq, hkv, window;
     float softmax_scale, value_scale;
     bool swa;
+    // Fused RoPE: Q is rotated as it is loaded, from the (cos, sin) table of
+    // each packed token (rope_half pairs per token); null: no rotation.
+    const float* rope_tab = nullptr;
+    int rope_half = 0;
     // Chunked prefill only: the caches the sequences continue and their lengths.
     const uint16_t* k_cache = nullptr;
     const uint16_t* v_cache = nullptr;
@@ -167,5 +171,20 @@ struct RopeArgs {
     double theta;
 };
 hipError_t launch_rope(const RopeArgs& a, hipStream_t stream);
+
+// Fused-RoPE prefill preparation: K rotated into k_rot and the (cos, sin)
+// table [T][rotary_dim/2][2] fp32 for the Q rotation inside the prefill kernels.
+struct RopePrepArgs {
+    const uint16_t* k;
+    const int32_t* positions;
+    uint16_t* k_rot;
+    float* tab;
+    int total_tokens, hkv, rotary_dim;
+    double theta;
+};
+hipError_t launch_rope_prep(const RopePrepArgs& a, hipStream_t stream);
+inline size_t rope_table_bytes(int total_tokens, int rotary_dim) {
+    return (size_t)total_tokens * (size_t)(rotary_dim / 2) * 2 * sizeof(float);
+}
 
 }  // namespace mimo

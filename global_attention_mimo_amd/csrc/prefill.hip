@@ -102,7 +102,8 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     int hq, int hkv, int window, float c_log2, float value_scale, int num_qblocks,
                     int max_seqlen, const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
                     const int64_t* __restrict__ kv_base, const int32_t* __restrict__ ctx_lens, int ring,
-                    const int32_t* __restrict__ block_table, int max_blocks, int page_shift, long long num_pages) {
+                    const int32_t* __restrict__ block_table, int max_blocks, int page_shift, long long num_pages,
+                    const float* __restrict__ rope_tab, int rope_half) {
     static_assert(!PAGED || (CHUNK && !SWA), "only GA chunks read a paged pool");
     using Cfg = PrefillCfg<WV, NB, NK>;
     constexpr int QT = Cfg::kTokens;
@@ -139,6 +140,7 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             const u32x4* src = reinterpret_cast<const u32x4*>(q + ((size_t)(s0 + tok[nb]) * hq + head) * kDqk);
 #pragma unroll
             for (int s = 0; s < kDqk / 16; ++s) qf[nb][s] = __builtin_bit_cast(bf16x8, src[2 * s + hh]);
+            if (rope_tab) rope_frags_rd(qf[nb], rope_tab + (size_t)(s0 + tok[nb]) * rope_half * 2, rope_half, hh);
         } else {
 #pragma unroll
             for (int s = 0; s < kDqk / 16; ++s) qf[nb][s] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
@@ -459,19 +461,31 @@ __device__ __forceinline__ int ring_slot(int h) { return (h + kRingSlots * 16) %
 // W-1 of them in the ring k_cache/v_cache [B][W-1][Hkv][D]).  Keys are counted
 // from the chunk's first token; a key at negative index j is cached position
 // ctx_lens[b] + j, staged from the ring instead of as zeros.
-template <bool CHUNK>
+// ROPE: each block's Q is rotated before its first score tile, from the
+// (cos, sin) pairs of its 16 tokens (rope_tab: the packed tokens' fp32 pairs,
+// rope_half per token).  The pairs of the next block are loaded with its Q,
+// written to one of two LDS tables at the hand-over, and used after the
+// block's closing barrier, so no wave waits for them mid-block.
+// The streaming kernel rotates up to 64 dims (one table entry per thread;
+// wider rotations go to the tiled kernel, whose Q is loaded once per
+// workgroup).
+constexpr int kStreamRopeHalf = 32;
+constexpr int kRopeEntries = kStreamTokens * kStreamRopeHalf;  // pairs per LDS table
+constexpr int kRopePerThread = kRopeEntries / 512;
+template <bool CHUNK, bool ROPE = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kStreamThreads, kStreamThreads), amdgpu_waves_per_eu(2, 2)))
 void swa_stream_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                        const uint16_t* __restrict__ v, const int32_t* __restrict__ cu_seqlens,
                        const float* __restrict__ sink, uint16_t* __restrict__ out, float* __restrict__ lse,
                        int hq, int hkv, int window, float c_log2, float value_scale, int strip_blocks,
                        int max_seqlen, const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
-                       const int32_t* __restrict__ ctx_lens) {
+                       const int32_t* __restrict__ ctx_lens, const float* __restrict__ rope_tab, int rope_half) {
     __shared__ __attribute__((aligned(16))) uint16_t ring_k[kRingSlots * kSlotKeys * kKStride];
     __shared__ __attribute__((aligned(16))) uint16_t ring_v[kRingSlots * kSlotKeys * kVStride];
     // Threads without a second chunk of their own write it here, so that every
     // load is consumed on every path (no load stays in flight across the loop).
     __shared__ __attribute__((aligned(16))) uint16_t discard[(2 * kStreamThreads - kSlotKChunks - kSlotVChunks) * 8];
+    __shared__ __attribute__((aligned(16))) f32x2 rope_lds[ROPE ? 2 * kRopeEntries : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -556,6 +570,22 @@ void swa_stream_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
 #pragma unroll
         for (int s = 0; s < kDqk / 16; ++s) qv[s] = __builtin_bit_cast(bf16x8, src[2 * s + hh]);
     };
+    // RoPE table entries of one block: thread tid holds entries tid + 512 j
+    // (token e / rope_half, pair e % rope_half); entries past the block's
+    // 16 * rope_half are loaded clamped and written to unused table places,
+    // so every load is consumed on every path.
+    auto load_tab = [&](int blk, f32x2 (&tv)[kRopePerThread]) {
+#pragma unroll
+        for (int j = 0; j < kRopePerThread; ++j) {
+            const int e = tid + kStreamThreads * j;
+            const int t = min(blk * kStreamTokens + min(e / rope_half, kStreamTokens - 1), L - 1);
+            tv[j] = reinterpret_cast<const f32x2*>(rope_tab)[(size_t)(s0 + t) * rope_half + e % rope_half];
+        }
+    };
+    auto store_tab = [&](int blk, const f32x2 (&tv)[kRopePerThread]) {
+#pragma unroll
+        for (int j = 0; j < kRopePerThread; ++j) rope_lds[(blk & 1) * kRopeEntries + tid + kStreamThreads * j] = tv[j];
+    };
 
     // Outputs of the block at q0 through buffer descriptors that cover only
     // its first `rows` rows: stores of rows past the sequence end are dropped
@@ -590,7 +620,12 @@ void swa_stream_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
     // Prologue: the first block's Q and its ten slots.
     bf16x8 qf[kDqk / 16], qn[kDqk / 16];
     u32x4 na, nb;
+    f32x2 tn[ROPE ? kRopePerThread : 1];
     load_q(blk_begin, qf);
+    if constexpr (ROPE) {
+        load_tab(blk_begin, tn);
+        store_tab(blk_begin, tn);
+    }
     {
         const int h0 = blk_begin * (kStreamTokens / kSlotKeys) - 2 * kStreamTiles + 1;
         u32x4 pa[2 * kStreamTiles], pb[2 * kStreamTiles];
@@ -607,9 +642,17 @@ void swa_stream_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
     for (int blk = blk_begin; blk < blk_end; ++blk) {
         const int q0 = blk * kStreamTokens;
         const int hq0 = q0 / kSlotKeys;  // slot index of the block's own keys
+        if constexpr (ROPE) {
+            const float* tab = reinterpret_cast<const float*>(rope_lds + (blk & 1) * kRopeEntries + tok_in_blk * rope_half);
+            if (rope_half == 32)
+                rope_frags<2>(qf, tab, hh);
+            else
+                rope_frags<1>(qf, tab, hh);
+        }
         // In flight while this block computes: the next block's Q and new slot.
         load_q(min(blk + 1, blk_end - 1), qn);
         load_slot(hq0 + 1, na, nb);
+        if constexpr (ROPE) load_tab(min(blk + 1, blk_end - 1), tn);
         const int tok = q0 + tok_in_blk;
         float m_run = has_sink ? sink_l2 : kNoMax;
         float l_run = (has_sink && hh == 0) ? 1.0f : 0.0f;
@@ -709,6 +752,7 @@ void swa_stream_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
         // to LDS, replacing key block hq0+1-11, which no block from here on
         // reads, and its Q to qf.
         store_slot(hq0 + 1, na, nb);
+        if constexpr (ROPE) store_tab(blk + 1, tn);
 #pragma unroll
         for (int s = 0; s < kDqk / 16; ++s) {
             qf[s] = qn[s];
@@ -734,7 +778,7 @@ hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
                        a.q, a.k, a.v, a.cu_seqlens, a.sink, a.out, a.lse, a.hq, a.hkv, a.window,
                        a.softmax_scale * kLog2e, a.value_scale, nqb, a.max_seqlen, a.k_cache, a.v_cache, a.kv_base,
                        a.ctx_lens, a.window - 1, a.pages.table, a.pages.max_blocks, a.pages.shift,
-                       a.pages.num_pages);
+                       a.pages.num_pages, a.rope_tab, a.rope_half);
     return hipGetLastError();
 }
 
@@ -782,9 +826,12 @@ hipError_t launch_swa_stream(const PrefillArgs& a, hipStream_t stream) {
     const long long target = (long long)max(cus, 1) * MIMO_STREAM_ROUNDS;
     const int strip = (int)max(1LL, min(min(per_seq, (long long)MIMO_STREAM_MAX_STRIP), (total + target - 1) / target));
     dim3 grid((unsigned)((per_seq + strip - 1) / strip), a.hkv, a.num_seqs);
-    hipLaunchKernelGGL(swa_stream_kernel<CHUNK>, grid, dim3(kStreamThreads), 0, stream, a.q, a.k, a.v, a.cu_seqlens,
+    auto kern = swa_stream_kernel<CHUNK, false>;
+    if constexpr (!CHUNK)
+        if (a.rope_tab) kern = swa_stream_kernel<false, true>;
+    hipLaunchKernelGGL(kern, grid, dim3(kStreamThreads), 0, stream, a.q, a.k, a.v, a.cu_seqlens,
                        a.sink, a.out, a.lse, a.hq, a.hkv, a.window, a.softmax_scale * kLog2e, a.value_scale, strip,
-                       a.max_seqlen, a.k_cache, a.v_cache, a.ctx_lens);
+                       a.max_seqlen, a.k_cache, a.v_cache, a.ctx_lens, a.rope_tab, a.rope_half);
     return hipGetLastError();
 }
 
@@ -799,7 +846,8 @@ hipError_t launch_prefill_chunk(const PrefillArgs& a, hipStream_t stream) {
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     if (a.max_seqlen <= 0) return hipSuccess;
-    if (a.swa && a.window <= kStreamMaxWindow) return launch_swa_stream<false>(a, stream);
+    if (a.swa && a.window <= kStreamMaxWindow && (!a.rope_tab || a.rope_half <= kStreamRopeHalf))
+        return launch_swa_stream<false>(a, stream);
     if (a.swa) return launch_swa<MIMO_SWA_CFG>(a, stream);
     return launch_ga<MIMO_GA_CFG>(a, stream);
 }

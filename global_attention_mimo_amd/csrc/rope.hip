@@ -26,8 +26,6 @@ namespace {
 
 constexpr int kD = 192;
 
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
 // The frequencies f_i = theta^(-2i/rd), formed once on the host in double.
 struct InvFreq {
@@ -56,9 +54,11 @@ __global__ __launch_bounds__(256) void rope_kernel(uint16_t* __restrict__ q, uin
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
             const int i = 8 * j + 2 * w;
-            const float x0 = bf_lo(x[w]), x1 = bf_hi(x[w]), y0 = bf_lo(y[w]), y1 = bf_hi(y[w]);
-            xo[w] = pack_bf16x2(__builtin_fmaf(x0, cs[i], -y0 * sn[i]), __builtin_fmaf(x1, cs[i + 1], -y1 * sn[i + 1]));
-            yo[w] = pack_bf16x2(__builtin_fmaf(y0, cs[i], x0 * sn[i]), __builtin_fmaf(y1, cs[i + 1], x1 * sn[i + 1]));
+            float a0, a1, b0, b1;
+            rope_pair(bf16_word_lo(x[w]), bf16_word_lo(y[w]), cs[i], sn[i], a0, b0);
+            rope_pair(bf16_word_hi(x[w]), bf16_word_hi(y[w]), cs[i + 1], sn[i + 1], a1, b1);
+            xo[w] = pack_bf16x2(a0, a1);
+            yo[w] = pack_bf16x2(b0, b1);
         }
         *px = xo;
         *py = yo;
@@ -90,14 +90,77 @@ __global__ __launch_bounds__(256) void rope_kernel(uint16_t* __restrict__ q, uin
     }
 }
 
+// Preparation for attention with fused RoPE: per token, the (cos, sin) pairs
+// of its rd/2 angles (formed exactly as rope_kernel forms them) go to tab
+// [T][rd/2][2] fp32, for the prefill kernels to rotate Q with, and the
+// token's K rows are written to k_rot rotated (dims rd .. 191 copied).  A block
+// serves kPrepTokens consecutive tokens.
+constexpr int kPrepTokens = 8;
+__global__ __launch_bounds__(256) void rope_prep_kernel(const uint16_t* __restrict__ k,
+                                                        const int32_t* __restrict__ positions, int total_tokens,
+                                                        int hkv, const InvFreq freq, int rd,
+                                                        uint16_t* __restrict__ k_rot, float* __restrict__ tab) {
+    __shared__ float cs[kPrepTokens][kD / 2], sn[kPrepTokens][kD / 2];
+    const int64_t t0 = (int64_t)blockIdx.x * kPrepTokens;
+    const int ntok = (int)min((int64_t)kPrepTokens, total_tokens - t0);
+    const int half = rd / 2;
+    const int pairs = half / 8;             // 16-byte pair units per head row
+    const int per = pairs + (kD - rd) / 8;  // plus the untouched chunks
+    for (int e = threadIdx.x; e < ntok * half; e += blockDim.x) {
+        const int tt = e / half, i = e % half;
+        double s, c;
+        sincos((double)positions[t0 + tt] * freq.f[i], &s, &c);
+        cs[tt][i] = (float)c;
+        sn[tt][i] = (float)s;
+        reinterpret_cast<f32x2*>(tab)[(size_t)(t0 + tt) * half + i] = f32x2{(float)c, (float)s};
+    }
+    __syncthreads();
+    for (int u = threadIdx.x; u < ntok * hkv * per; u += blockDim.x) {
+        const int tt = u / (hkv * per), h = (u / per) % hkv, j = u % per;
+        const size_t row = ((size_t)(t0 + tt) * hkv + h) * kD;
+        const u32x4* src = reinterpret_cast<const u32x4*>(k + row);
+        u32x4* dst = reinterpret_cast<u32x4*>(k_rot + row);
+        if (j < pairs) {
+            const u32x4 x = src[j], y = src[j + pairs];
+            u32x4 xo, yo;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const int i = 8 * j + 2 * w;
+                float a0, a1, b0, b1;
+                rope_pair(bf16_word_lo(x[w]), bf16_word_lo(y[w]), cs[tt][i], sn[tt][i], a0, b0);
+                rope_pair(bf16_word_hi(x[w]), bf16_word_hi(y[w]), cs[tt][i + 1], sn[tt][i + 1], a1, b1);
+                xo[w] = pack_bf16x2(a0, a1);
+                yo[w] = pack_bf16x2(b0, b1);
+            }
+            dst[j] = xo;
+            dst[j + pairs] = yo;
+        } else {
+            const int c = rd / 8 + (j - pairs);
+            dst[c] = src[c];
+        }
+    }
+}
+
+InvFreq inv_freq(double theta, int rd) {
+    InvFreq freq{};
+    for (int i = 0; i < rd / 2; ++i) freq.f[i] = std::pow(theta, -2.0 * i / rd);
+    return freq;
+}
+
 }  // namespace
+
+hipError_t launch_rope_prep(const RopePrepArgs& a, hipStream_t stream) {
+    if (a.total_tokens <= 0) return hipSuccess;
+    hipLaunchKernelGGL(rope_prep_kernel, dim3((unsigned)((a.total_tokens + kPrepTokens - 1) / kPrepTokens)), dim3(256), 0,
+                       stream, a.k, a.positions, a.total_tokens, a.hkv, inv_freq(a.theta, a.rotary_dim), a.rotary_dim,
+                       a.k_rot, a.tab);
+    return hipGetLastError();
+}
 
 hipError_t launch_rope(const RopeArgs& a, hipStream_t stream) {
     if (a.total_tokens <= 0 || a.rotary_dim == 0) return hipSuccess;
-    InvFreq freq{};
-    for (int i = 0; i < a.rotary_dim / 2; ++i) freq.f[i] = std::pow(a.theta, -2.0 * i / a.rotary_dim);
     hipLaunchKernelGGL(rope_kernel, dim3((unsigned)a.total_tokens), dim3(256), 0, stream, a.q, a.k, a.positions, a.hq,
-                       a.hkv, freq, a.rotary_dim);
+                       a.hkv, inv_freq(a.theta, a.rotary_dim), a.rotary_dim);
     return hipGetLastError();
 }
 

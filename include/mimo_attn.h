@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define MIMO_ATTN_ABI_VERSION 8
+#define MIMO_ATTN_ABI_VERSION 9
 
 /* Layer type: which key set a query sees (model doc, Key features; config
  * layer_types). */
@@ -442,6 +442,42 @@ int mimo_attn_prefill_backward(const mimo_attn_dims* dims, int layer_type,
  */
 int mimo_rope_apply(const mimo_attn_dims* dims, uint16_t* q, uint16_t* k, const int32_t* positions,
                     int32_t total_tokens, float rope_theta, int32_t rotary_dim, hipStream_t stream);
+
+/*
+ * Prefill with the rotary embedding fused in (model doc, MiMoV2FlashConfig:
+ * rope_parameters / rope_theta; MiMoV2FlashModel.forward: position_ids): the
+ * result is that of mimo_rope_apply on copies of q and k followed by
+ * mimo_attn_prefill, bit for bit, without the separate pass over q.  Q is
+ * rotated as the attention kernels load it; K is rotated once, by a pass over
+ * K alone that also forms each token's cos/sin table, into k_rot, which the
+ * attention reads and the caller then appends (mimo_kv_append), so that the
+ * caches hold post-RoPE keys.
+ *
+ *   q, k, v        as for mimo_attn_prefill, before the rotation; q, k and v
+ *                  are only read (k_rot == k is allowed and rotates k in place).
+ *   positions      [total_tokens] int32 (device): the position id of each
+ *                  packed token (0 .. L-1 within a sequence for a plain
+ *                  prefill); positions only steer the rotation, the masks use
+ *                  token order as for mimo_attn_prefill.
+ *   total_tokens   (host) == cu_seqlens[num_seqs].
+ *   rope_theta     > 1 (host); rotary_dim a multiple of 32 in [32, 192] (host):
+ *                  the pairs (i, i + rotary_dim/2) rotate by the angle
+ *                  p * theta^(-2i/rotary_dim), formed in fp64, as for
+ *                  mimo_rope_apply; other rotary_dim values are
+ *                  MIMO_ERR_UNSUPPORTED (use mimo_rope_apply).
+ *   k_rot          [total_tokens][Hkv][192] bf16 (device): K after the rotation.
+ *   workspace      >= mimo_attn_prefill_rope_workspace_size(dims, total_tokens,
+ *                  rotary_dim) bytes of device memory (the tokens' fp32 cos/sin
+ *                  table), no initialisation, scratch after the call.
+ * A call with max_seqlen == 0 or total_tokens == 0 enqueues nothing.
+ */
+size_t mimo_attn_prefill_rope_workspace_size(const mimo_attn_dims* dims, int32_t total_tokens, int32_t rotary_dim);
+
+int mimo_attn_prefill_rope(const mimo_attn_dims* dims, int layer_type,
+                           const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* positions,
+                           const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen, int32_t total_tokens,
+                           float rope_theta, int32_t rotary_dim, const float* sink, uint16_t* out, float* lse,
+                           uint16_t* k_rot, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static English name of a status code ("MIMO_OK", ...). */
 const char* mimo_status_string(int status);

@@ -42,7 +42,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_version_and_status_strings(L):
-    assert B.mimo_abi_version() == 8
+    assert B.mimo_abi_version() == 9
     assert B.mimo_status_string(0) == "MIMO_OK"
     assert B.mimo_status_string(3) == "MIMO_ERR_WORKSPACE"
     assert B.mimo_status_string(99) == "MIMO_ERR_UNKNOWN"
@@ -434,3 +434,38 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIBRARY", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         B.lib()
+
+
+def rope_prefill_call(L, dims=None, layer=0, k_rot=FAKE, pos=FAKE, total=64, theta=1e4, rd=64, ws=FAKE,
+                      ws_bytes=1 << 20, maxlen=16):
+    d = dims or B.make_dims()
+    return L.mimo_attn_prefill_rope(ctypes.byref(d), layer, FAKE, FAKE, FAKE, pos, FAKE, 1, maxlen, total, theta, rd,
+                                    None, FAKE, None, k_rot, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(k_rot=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(pos=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(k_rot=FAKE_ODD), B.MIMO_ERR_INVALID_ARG),
+    (dict(theta=1.0), B.MIMO_ERR_INVALID_ARG),
+    (dict(theta=float("inf")), B.MIMO_ERR_INVALID_ARG),
+    (dict(rd=16), B.MIMO_ERR_UNSUPPORTED),      # pairs across half-waves: use mimo_rope_apply
+    (dict(rd=0), B.MIMO_ERR_UNSUPPORTED),
+    (dict(rd=224), B.MIMO_ERR_UNSUPPORTED),
+    (dict(total=-1), B.MIMO_ERR_INVALID_ARG),
+    (dict(ws=None), B.MIMO_ERR_WORKSPACE),
+    (dict(ws_bytes=64 * 32 * 8 - 1), B.MIMO_ERR_WORKSPACE),
+    (dict(layer=3), B.MIMO_ERR_INVALID_ARG),
+])
+def test_prefill_rope_rejects(L, case, status):
+    assert rope_prefill_call(L, **case) == status
+    assert B.mimo_last_error() != ""
+
+
+def test_prefill_rope_workspace_and_empty(L):
+    d = B.make_dims()
+    assert B.mimo_attn_prefill_rope_workspace_size(d, 32768, 64) == 32768 * 32 * 2 * 4
+    assert B.mimo_attn_prefill_rope_workspace_size(d, 10, 192) == 10 * 96 * 8
+    assert B.mimo_attn_prefill_rope_workspace_size(d, 10, 48) == 0
+    assert rope_prefill_call(L, total=0) == B.MIMO_OK
+    assert rope_prefill_call(L, maxlen=0) == B.MIMO_OK
