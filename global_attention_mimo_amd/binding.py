@@ -15,7 +15,10 @@ from typing import Optional
 import torch
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIBRARY = os.path.join(PKG, "libmimo_attn.so")
+# The library built in-tree; MIMO_ATTN_LIBRARY names another build of the same
+# ABI (the sanitizer test loads a host-only instrumented build of the
+# validation layer this way).
+LIBRARY = os.environ.get("MIMO_ATTN_LIBRARY") or os.path.join(PKG, "libmimo_attn.so")
 
 MIMO_LAYER_SWA = 0
 MIMO_LAYER_GA = 1
