@@ -273,6 +273,34 @@ def rope_rows(dims, ga, reps=5):
                         "GB/s": nbytes / (ms * 1e-3) / 1e9, "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS}}
 
 
+def swa_decode_rotated_rows(dims, ctx, sets=8, rounds=4):
+    """SWA decode of the step's batch (128 sequences, 128-slot rings) cycling
+    over `sets` independent ring / q / new-token / output sets (47.5 MB each,
+    380 MB for 8, more than the 256 MB MALL holds), so each call's ring comes
+    from HBM rather than from the last-level cache.  The calls are enqueued
+    back to back and timed together; bytes as for the step's SWA decode."""
+    dev = "cuda"
+    Bd = len(ctx)
+    xs = [synth.decode_inputs(ctx, 0, seed=300 + i, device=dev) for i in range(sets)]
+    outs = [(torch.empty((Bd, HQ, DV), dtype=torch.bfloat16, device=dev),
+             torch.empty((Bd, HQ), dtype=torch.float32, device=dev)) for _ in range(sets)]
+    ctx_d = torch.tensor(ctx, dtype=torch.int32, device=dev)
+
+    def call_all():
+        for x, (o, l) in zip(xs, outs):
+            B.mimo_attn_decode(dims, 0, x.q, x.k_new, x.v_new, x.k_cache, x.v_cache, None, ctx_d, Bd, max(ctx), 0,
+                               x.sink, o, l, None)
+    ms = _time_ms(call_all, rounds) / sets
+    _, nbytes = decode_stats(ctx, 0)
+    del xs, outs
+    torch.cuda.empty_cache()
+    return {"decode_swa_rotated_rings": {
+        "workload": f"SWA decode B={Bd}, 128-slot rings, {sets} independent ring/q/output sets cycled "
+                    f"({sets * nbytes / 1e6:.0f} MB, beyond the 256 MB MALL)",
+        "ms": ms, "tokens/s": Bd / (ms * 1e-3), "GB/s": nbytes / (ms * 1e-3) / 1e9,
+        "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS}}
+
+
 def rope_fused_rows(dims, ga, swa, reps=5):
     """Prefill with the rotary embedding fused in (mimo_attn_prefill_rope: K
     rotated into k_rot with the tokens' cos/sin table, Q rotated as the kernels
@@ -470,11 +498,12 @@ def _cpu_model():
     return "unknown"
 
 
-def cpu_baseline(swa, ga, dga, dswa, ctx, gpu):
+def cpu_baseline(swa, ga, dga, dswa, ctx, gpu, sample_s=4.0):
     """The fp64 oracle, as it stands, timed per configuration on the host cores,
     next to the GPU figure of the same configuration (`gpu`: name -> dict).
-    Configs 1, 2 and 4-SWA run in full; configs 3, 4-GA and 5 run on a sample and
-    their time is extrapolated by algorithmic flops (labelled as such)."""
+    Configs 1, 2 and 4-SWA run in full; configs 3, 4-GA and 5 run on a sample of
+    about `sample_s` seconds each and their time is extrapolated by algorithmic
+    flops (labelled as such)."""
     import oracle
     orc = oracle.get()
     nth = orc.default_threads()
@@ -515,20 +544,26 @@ def cpu_baseline(swa, ga, dga, dswa, ctx, gpu):
     s2 = timed(lambda: orc.prefill(*b2, cu2, layer_type=0, scale=scale, sink=sk2, nthreads=nth))
     record("config2_swa_prefill_4x8192", f2, s2, f2, "full (32768 tokens)")
     del b2
-    # 3: GA prefill 1 x 32768: 32 rows spread over the sequence.
+    # 3: GA prefill 1 x 32768: random query rows, 16 at a time, for about `sample_s` seconds.
     b3 = [synth.bf16_bits(t) for t in (ga.q, ga.k, ga.v)]
-    r3 = np.sort(rng.choice(32768, 32, replace=False))
-    f3s = int((r3 + 1).sum()) * HQ * FLOP_PER_TRIPLE
-    s3 = timed(lambda: orc.prefill(*b3, ga.cu_seqlens.cpu().numpy(), layer_type=1, scale=scale,
-                                   sink=ga.sink.cpu().numpy(), rows=r3, nthreads=nth))
+    order3 = rng.permutation(32768)
+    f3s, s3, n3 = 0, 0.0, 0
+    while s3 < sample_s and n3 < 2048:
+        r3 = np.sort(order3[n3:n3 + 16])
+        s3 += timed(lambda: orc.prefill(*b3, ga.cu_seqlens.cpu().numpy(), layer_type=1, scale=scale,
+                                        sink=ga.sink.cpu().numpy(), rows=r3, nthreads=nth))
+        f3s += int((r3 + 1).sum()) * HQ * FLOP_PER_TRIPLE
+        n3 += 16
     record("config3_ga_prefill_1x32768", f3s, s3, prefill_pairs([32768], 1) * HQ * FLOP_PER_TRIPLE,
-           "32 random query rows of 32768")
+           f"{n3} random query rows of 32768")
     del b3
-    # 4-GA: 4 whole sequences of the 128.
+    # 4-GA: whole sequences of the 128, in random order, for about `sample_s` seconds.
     base = dga.kv_base.cpu().numpy()
-    pick = rng.choice(len(ctx), 4, replace=False)
-    f4s, s4 = 0, 0.0
+    pick = rng.permutation(len(ctx))
+    f4s, s4, n4 = 0, 0.0, 0
     for b in pick:
+        if s4 >= sample_s:
+            break
         c = int(ctx[b])
         kc = synth.bf16_bits(dga.k_cache[base[b]:base[b] + c])
         vc = synth.bf16_bits(dga.v_cache[base[b]:base[b] + c])
@@ -536,8 +571,9 @@ def cpu_baseline(swa, ga, dga, dswa, ctx, gpu):
         s4 += timed(lambda: orc.decode(*args, kc, vc, np.array([c], np.int32), layer_type=1, scale=scale,
                                        sink=dga.sink.cpu().numpy(), kv_base=np.zeros(1, np.int64), nthreads=nth))
         f4s += (c + 1) * HQ * FLOP_PER_TRIPLE
+        n4 += 1
     record("config4_ga_decode_b128", f4s, s4, sum(int(c) + 1 for c in ctx) * HQ * FLOP_PER_TRIPLE,
-           "4 of the 128 sequences, whole")
+           f"{n4} of the {len(ctx)} sequences, whole")
     # 4-SWA: all 128 sequences over the ring.
     a5 = [synth.bf16_bits(t) for t in (dswa.q, dswa.k_new, dswa.v_new, dswa.k_cache, dswa.v_cache)]
     f4w = len(ctx) * W * HQ * FLOP_PER_TRIPLE
@@ -550,15 +586,18 @@ def cpu_baseline(swa, ga, dga, dswa, ctx, gpu):
     Lm = int(np.median(lengths))
     x5 = synth.prefill_inputs([Lm], seed=1000)
     b5 = [synth.bf16_bits(t) for t in (x5.q, x5.k, x5.v)]
-    r5 = np.sort(rng.choice(Lm, 24, replace=False))
-    f5s, s5 = 0, 0.0
-    for lt in (0, 1):
-        s5 += timed(lambda: orc.prefill(*b5, x5.cu_seqlens.numpy(), layer_type=lt, scale=scale, sink=x5.sink.numpy(),
-                                        rows=r5, nthreads=nth))
-        f5s += int(np.minimum(r5 + 1, W if lt == 0 else 1 << 40).sum()) * HQ * FLOP_PER_TRIPLE
+    order5 = rng.permutation(Lm)
+    f5s, s5, n5 = 0, 0.0, 0
+    while s5 < sample_s and n5 < Lm:
+        r5 = np.sort(order5[n5:n5 + 24])
+        for lt in (0, 1):
+            s5 += timed(lambda: orc.prefill(*b5, x5.cu_seqlens.numpy(), layer_type=lt, scale=scale,
+                                            sink=x5.sink.numpy(), rows=r5, nthreads=nth))
+            f5s += int(np.minimum(r5 + 1, W if lt == 0 else 1 << 40).sum()) * HQ * FLOP_PER_TRIPLE
+        n5 += len(r5)
     f5 = (8 * prefill_pairs(lengths, 1) + 40 * prefill_pairs(lengths, 0)) * HQ * FLOP_PER_TRIPLE
     f5 += sum(8 * sum(L + s + 1 for L in lengths) + 40 * len(lengths) * W for s in range(64)) * HQ * FLOP_PER_TRIPLE
-    record("config5_hybrid_stack", f5s, s5, f5, f"24 query rows of a {Lm}-token prompt per layer type")
+    record("config5_hybrid_stack", f5s, s5, f5, f"{n5} query rows of a {Lm}-token prompt per layer type")
     return {"value": tot_flops / tot_s / 1e12, "unit": "TFLOP/s", "cores": nth, "kind": "oracle",
             "cpu_model": _cpu_model(),
             "sample": f"per configuration below; {tot_flops / 1e9:.1f} GFLOP of fp64 oracle work in {tot_s:.1f} s "
@@ -754,7 +793,8 @@ def main():
         res["next_rows"] = {**chunk_rows(dims, ga, swa), **paged_rows(dims, dga, ctx_ga, max_ctx, ws, ga),
                             **fp8_rows(dims, dga, ctx_ga, max_ctx, ws),
                             **backward_rows(dims, ga, swa, out_ga, lse_ga, out_swa, lse_swa),
-                            **rope_rows(dims, ga), **rope_fused_rows(dims, ga, swa)}
+                            **rope_rows(dims, ga), **rope_fused_rows(dims, ga, swa),
+                            **swa_decode_rotated_rows(dims, ctx0)}
     if not args.no_next_rows and not args.no_hybrid:
         log("hybrid stack: 48-layer prefill and decode")
         res["hybrid_stack"] = hybrid_rows(dims)["hybrid_stack"]
