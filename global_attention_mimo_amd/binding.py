@@ -27,6 +27,11 @@ MIMO_ERR_INVALID_ARG = 1
 MIMO_ERR_UNSUPPORTED = 2
 MIMO_ERR_WORKSPACE = 3
 MIMO_ERR_HIP = 4
+MIMO_ERR_PRECONDITION = 5
+
+# Check-mode findings (MIMO_CHECK_* of include/mimo_attn.h).
+CHECK_BITS = {"CU_START": 0x001, "CU_ORDER": 0x002, "CU_LENGTH": 0x004, "CU_TOTAL": 0x008, "CTX_RANGE": 0x010,
+              "KV_BASE": 0x020, "CAPACITY": 0x040, "BLOCK_TABLE": 0x080, "SINK": 0x100, "FP8_SCALE": 0x200}
 
 ENTRY_POINTS = ("mimo_attn_prefill", "mimo_attn_prefill_chunk", "mimo_attn_decode_workspace_size",
                 "mimo_attn_decode", "mimo_attn_decode_noalloc", "mimo_attn_decode_append", "mimo_kv_append", "mimo_kv_append_paged",
@@ -34,7 +39,7 @@ ENTRY_POINTS = ("mimo_attn_prefill", "mimo_attn_prefill_chunk", "mimo_attn_decod
                 "mimo_attn_prefill_chunk_paged", "mimo_kv_append_fp8", "mimo_attn_decode_fp8",
                 "mimo_attn_prefill_backward_workspace_size", "mimo_attn_prefill_backward", "mimo_rope_apply",
                 "mimo_attn_prefill_rope_workspace_size", "mimo_attn_prefill_rope",
-                "mimo_status_string",
+                "mimo_attn_set_check", "mimo_attn_check_flags", "mimo_status_string",
                 "mimo_last_error", "mimo_abi_version")
 
 
@@ -68,60 +73,69 @@ def lib() -> ctypes.CDLL:
     if _lib is None:
         if not os.path.exists(LIBRARY):
             raise ImportError(f"{LIBRARY} is missing: build it with `python -m global_attention_mimo_amd.build`")
-        L = ctypes.CDLL(LIBRARY)
-        dims_p = ctypes.POINTER(mimo_attn_dims)
-        L.mimo_attn_prefill.restype = ctypes.c_int
-        L.mimo_attn_prefill.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P]
-        L.mimo_attn_prefill_chunk.restype = ctypes.c_int
-        L.mimo_attn_prefill_chunk.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _P,
-                                              _P, _P, _P]
-        L.mimo_attn_decode_workspace_size.restype = _SZ
-        L.mimo_attn_decode_workspace_size.argtypes = [dims_p, ctypes.c_int, _I32, _I32, _I32]
-        L.mimo_attn_decode.restype = ctypes.c_int
-        L.mimo_attn_decode.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P,
-                                       _P, _P, _SZ, _P]
-        L.mimo_attn_decode_noalloc.restype = ctypes.c_int
-        L.mimo_attn_decode_noalloc.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P,
-                                               _P, _P, _P]
-        L.mimo_attn_decode_append.restype = ctypes.c_int
-        L.mimo_attn_decode_append.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
-                                              _P, _P, _P, _P, _SZ, _P]
-        L.mimo_kv_append.restype = ctypes.c_int
-        L.mimo_kv_append.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _P]
-        pages_p = ctypes.POINTER(mimo_kv_pages)
-        L.mimo_kv_append_paged.restype = ctypes.c_int
-        L.mimo_kv_append_paged.argtypes = [dims_p, _P, _P, _P, _P, _I32, _I32, _P, _P, pages_p, _P]
-        L.mimo_attn_decode_paged.restype = ctypes.c_int
-        L.mimo_attn_decode_paged.argtypes = [dims_p, _P, _P, _P, _P, _P, pages_p, _P, _I32, _I32, _I32, _P, _P, _P,
-                                             _P, _SZ, _P]
-        L.mimo_attn_prefill_chunk_paged.restype = ctypes.c_int
-        L.mimo_attn_prefill_chunk_paged.argtypes = [dims_p, _P, _P, _P, _P, _I32, _I32, _P, _P, pages_p, _P, _P, _P,
-                                                    _P, _P]
-        L.mimo_kv_append_fp8.restype = ctypes.c_int
-        L.mimo_kv_append_fp8.argtypes = [dims_p, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P]
-        L.mimo_attn_decode_fp8.restype = ctypes.c_int
-        L.mimo_attn_decode_fp8.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P,
-                                           _P, _SZ, _P]
-        L.mimo_attn_prefill_backward_workspace_size.restype = _SZ
-        L.mimo_attn_prefill_backward_workspace_size.argtypes = [dims_p, _I32]
-        L.mimo_attn_prefill_backward.restype = ctypes.c_int
-        L.mimo_attn_prefill_backward.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
-                                                 _P, _P, _P, _P, _P, _P, _SZ, _P]
-        L.mimo_rope_apply.restype = ctypes.c_int
-        L.mimo_rope_apply.argtypes = [dims_p, _P, _P, _P, _I32, ctypes.c_float, _I32, _P]
-        L.mimo_attn_prefill_rope_workspace_size.restype = _SZ
-        L.mimo_attn_prefill_rope_workspace_size.argtypes = [dims_p, _I32, _I32]
-        L.mimo_attn_prefill_rope.restype = ctypes.c_int
-        L.mimo_attn_prefill_rope.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _P, _I32, _I32, _I32,
-                                             ctypes.c_float, _I32, _P, _P, _P, _P, _P, _SZ, _P]
-        L.mimo_status_string.restype = ctypes.c_char_p
-        L.mimo_status_string.argtypes = [ctypes.c_int]
-        L.mimo_last_error.restype = ctypes.c_char_p
-        L.mimo_last_error.argtypes = []
-        L.mimo_abi_version.restype = ctypes.c_int
-        L.mimo_abi_version.argtypes = []
-        _lib = L
+        _lib = load(LIBRARY)
     return _lib
+
+
+def load(path: str) -> ctypes.CDLL:
+    """Opens a build of the C ABI at `path` with every entry point's signature set."""
+    L = ctypes.CDLL(path)
+    dims_p = ctypes.POINTER(mimo_attn_dims)
+    L.mimo_attn_prefill.restype = ctypes.c_int
+    L.mimo_attn_prefill.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P]
+    L.mimo_attn_prefill_chunk.restype = ctypes.c_int
+    L.mimo_attn_prefill_chunk.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _P,
+                                          _P, _P, _P]
+    L.mimo_attn_decode_workspace_size.restype = _SZ
+    L.mimo_attn_decode_workspace_size.argtypes = [dims_p, ctypes.c_int, _I32, _I32, _I32]
+    L.mimo_attn_decode.restype = ctypes.c_int
+    L.mimo_attn_decode.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P,
+                                   _P, _P, _SZ, _P]
+    L.mimo_attn_decode_noalloc.restype = ctypes.c_int
+    L.mimo_attn_decode_noalloc.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P,
+                                           _P, _P, _P]
+    L.mimo_attn_decode_append.restype = ctypes.c_int
+    L.mimo_attn_decode_append.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
+                                          _P, _P, _P, _P, _SZ, _P]
+    L.mimo_kv_append.restype = ctypes.c_int
+    L.mimo_kv_append.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _P]
+    pages_p = ctypes.POINTER(mimo_kv_pages)
+    L.mimo_kv_append_paged.restype = ctypes.c_int
+    L.mimo_kv_append_paged.argtypes = [dims_p, _P, _P, _P, _P, _I32, _I32, _P, _P, pages_p, _P]
+    L.mimo_attn_decode_paged.restype = ctypes.c_int
+    L.mimo_attn_decode_paged.argtypes = [dims_p, _P, _P, _P, _P, _P, pages_p, _P, _I32, _I32, _I32, _P, _P, _P,
+                                         _P, _SZ, _P]
+    L.mimo_attn_prefill_chunk_paged.restype = ctypes.c_int
+    L.mimo_attn_prefill_chunk_paged.argtypes = [dims_p, _P, _P, _P, _P, _I32, _I32, _P, _P, pages_p, _P, _P, _P,
+                                                _P, _P]
+    L.mimo_kv_append_fp8.restype = ctypes.c_int
+    L.mimo_kv_append_fp8.argtypes = [dims_p, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P]
+    L.mimo_attn_decode_fp8.restype = ctypes.c_int
+    L.mimo_attn_decode_fp8.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P,
+                                       _P, _SZ, _P]
+    L.mimo_attn_prefill_backward_workspace_size.restype = _SZ
+    L.mimo_attn_prefill_backward_workspace_size.argtypes = [dims_p, _I32]
+    L.mimo_attn_prefill_backward.restype = ctypes.c_int
+    L.mimo_attn_prefill_backward.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
+                                             _P, _P, _P, _P, _P, _P, _SZ, _P]
+    L.mimo_rope_apply.restype = ctypes.c_int
+    L.mimo_rope_apply.argtypes = [dims_p, _P, _P, _P, _I32, ctypes.c_float, _I32, _P]
+    L.mimo_attn_prefill_rope_workspace_size.restype = _SZ
+    L.mimo_attn_prefill_rope_workspace_size.argtypes = [dims_p, _I32, _I32]
+    L.mimo_attn_prefill_rope.restype = ctypes.c_int
+    L.mimo_attn_prefill_rope.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _P, _I32, _I32, _I32,
+                                         ctypes.c_float, _I32, _P, _P, _P, _P, _P, _SZ, _P]
+    L.mimo_status_string.restype = ctypes.c_char_p
+    L.mimo_attn_set_check.restype = ctypes.c_int
+    L.mimo_attn_set_check.argtypes = [ctypes.c_int]
+    L.mimo_attn_check_flags.restype = ctypes.c_int
+    L.mimo_attn_check_flags.argtypes = [ctypes.POINTER(ctypes.c_uint32), ctypes.c_int]
+    L.mimo_status_string.argtypes = [ctypes.c_int]
+    L.mimo_last_error.restype = ctypes.c_char_p
+    L.mimo_last_error.argtypes = []
+    L.mimo_abi_version.restype = ctypes.c_int
+    L.mimo_abi_version.argtypes = []
+    return L
 
 
 def make_dims(num_q_heads=64, num_kv_heads=4, head_dim_qk=192, head_dim_v=128, sliding_window=129,
@@ -161,6 +175,18 @@ def mimo_last_error() -> str:
 
 def mimo_abi_version() -> int:
     return int(lib().mimo_abi_version())
+
+
+def mimo_attn_set_check(enable: bool) -> bool:
+    """Switches check mode on or off; returns the previous setting."""
+    return bool(lib().mimo_attn_set_check(1 if enable else 0))
+
+
+def mimo_attn_check_flags(clear: bool = False) -> int:
+    """The current device's sticky check-mode word (MIMO_CHECK_* bits)."""
+    word = ctypes.c_uint32(0)
+    _check(lib().mimo_attn_check_flags(ctypes.byref(word), 1 if clear else 0))
+    return int(word.value)
 
 
 def mimo_attn_prefill(dims: mimo_attn_dims, layer_type: int, q, k, v, cu_seqlens, num_seqs: int, max_seqlen: int,

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libmimo_attn.so")
-SOURCES = ["prefill.hip", "decode.hip", "append.hip", "backward.hip", "rope.hip", "api.cpp"]
+SOURCES = ["prefill.hip", "decode.hip", "append.hip", "backward.hip", "rope.hip", "check.hip", "api.cpp"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

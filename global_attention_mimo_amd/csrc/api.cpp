@@ -2,10 +2,13 @@
 //
 // Every check here runs on the host before anything is enqueued, so misuse is
 // reported by status code without touching the device.
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 
 #include "../../include/mimo_attn.h"
 #include "launch.hpp"
@@ -64,6 +67,45 @@ int hip_status(hipError_t e, const char* what) {
     return ok();
 }
 
+// Check mode: -1 until first read from MIMO_ATTN_CHECK, then 0 or 1.
+std::atomic<int> g_check{-1};
+
+bool check_on() {
+    int v = g_check.load(std::memory_order_relaxed);
+    if (v < 0) {
+        const char* env = std::getenv("MIMO_ATTN_CHECK");
+        int expected = -1;
+        g_check.compare_exchange_strong(expected, env && std::strcmp(env, "1") == 0 ? 1 : 0);
+        v = g_check.load();
+    }
+    return v == 1;
+}
+
+const char* const kCheckNames[] = {
+    "cu_seqlens[0] is not 0", "cu_seqlens decreases", "a sequence is longer than the maximum length",
+    "cu_seqlens does not end at the token count", "ctx_lens out of range", "kv_base is negative",
+    "the context passes the pool capacity", "a block-table entry lies outside the pool", "a sink is NaN or +inf",
+    "an FP8 scale is not positive and finite"};
+
+// Check mode's gate in front of a call's kernels: MIMO_OK, or
+// MIMO_ERR_PRECONDITION naming the violated rules (nothing else enqueued).
+int precheck(const mimo::CheckArgs& c, hipStream_t stream, const char* who) {
+    if (!check_on()) return MIMO_OK;
+    bool gated = false;
+    uint32_t bits = 0;
+    if (int st = hip_status(mimo::run_check(c, stream, &gated, &bits), "check-mode pass")) return st;
+    if (!gated || !bits) return MIMO_OK;
+    char names[200] = "";
+    size_t used = 0;
+    for (int i = 0; i < (int)(sizeof kCheckNames / sizeof *kCheckNames); ++i) {
+        if (!(bits >> i & 1u)) continue;
+        const int n = std::snprintf(names + used, sizeof names - used, "%s%s", used ? "; " : "", kCheckNames[i]);
+        if (n < 0 || (size_t)n >= sizeof names - used) break;
+        used += (size_t)n;
+    }
+    return fail(MIMO_ERR_PRECONDITION, "%s: check mode found 0x%03x (%s)", who, bits, names);
+}
+
 // Paged pool description -> internal page table; MIMO_OK or a failure status.
 int check_pages(const mimo_kv_pages* pg, mimo::PageTable* out) {
     if (!pg) return fail(MIMO_ERR_INVALID_ARG, "pages is NULL");
@@ -112,6 +154,13 @@ int mimo_attn_prefill(const mimo_attn_dims* dims, int layer_type, const uint16_t
     mimo::PrefillArgs a{q, k, v, cu_seqlens, sink, out, lse, num_seqs, max_seqlen, dims->num_q_heads,
                         dims->num_kv_heads, dims->sliding_window, dims->softmax_scale, dims->value_scale,
                         layer_type == MIMO_LAYER_SWA};
+    mimo::CheckArgs c;
+    c.cu = cu_seqlens;
+    c.n_seqs = num_seqs;
+    c.max_len = max_seqlen;
+    c.sink = sink;
+    c.hq = dims->num_q_heads;
+    if (int st = precheck(c, stream, "mimo_attn_prefill")) return st;
     return hip_status(mimo::launch_prefill(a, stream), "prefill launch");
 }
 
@@ -148,6 +197,18 @@ int prefill_chunk_impl(const mimo_attn_dims* dims, int layer_type, const uint16_
     a.kv_base = kv_base;
     a.ctx_lens = ctx_lens;
     a.pages = pt;
+    mimo::CheckArgs c;
+    c.cu = cu_newlens;
+    c.n_seqs = num_seqs;
+    c.max_len = max_newlen;
+    c.ctx = ctx_lens;
+    c.batch = num_seqs;
+    c.new_from_cu = true;
+    if (layer_type == MIMO_LAYER_GA && !pages) c.kv_base = kv_base;
+    c.pages = pt;
+    c.sink = sink;
+    c.hq = dims->num_q_heads;
+    if (int st = precheck(c, stream, "chunked prefill")) return st;
     return hip_status(mimo::launch_prefill_chunk(a, stream), "chunked prefill launch");
 }
 
@@ -254,8 +315,26 @@ int decode_impl(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, c
         a.append_v = const_cast<uint16_t*>(v_cache);
         a.kv_capacity = kv_capacity;
     }
+    mimo::CheckArgs c;
+    c.ctx = ctx_lens;
+    c.batch = batch;
+    c.max_ctx = max_ctx;
+    c.new_tokens = 1;
+    if (layer_type == MIMO_LAYER_GA && !pages) {
+        c.kv_base = kv_base;
+        if (append) c.kv_capacity = kv_capacity;
+    }
+    c.pages = pt;
+    c.sink = sink;
+    c.hq = dims->num_q_heads;
+    if (fp8) {
+        c.scales = fp8->k_scale;
+        c.scales_v = fp8->v_scale;
+        c.n_scales = dims->num_kv_heads;
+    }
     if (layer_type == MIMO_LAYER_SWA) {
         if (batch > INT32_MAX / 2) return fail(MIMO_ERR_UNSUPPORTED, "batch too large");
+        if (int st = precheck(c, stream, "SWA decode")) return st;
         return hip_status(mimo::launch_decode_swa(a, stream), "SWA decode launch");
     }
     if (!kv_base && !pages) return fail(MIMO_ERR_INVALID_ARG, "GA decode needs kv_base");
@@ -266,6 +345,7 @@ int decode_impl(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, c
         return fail(MIMO_ERR_WORKSPACE, "GA decode needs %zu workspace bytes (got %zu%s)", need, workspace_bytes,
                     workspace ? "" : ", NULL");
     if (!aligned16(workspace)) return fail(MIMO_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    if (int st = precheck(c, stream, "GA decode")) return st;
     return hip_status(mimo::launch_decode_ga(a, stream), "GA decode launch");
 }
 
@@ -304,6 +384,25 @@ int kv_append_impl(const mimo_attn_dims* dims, int layer_type, const uint16_t* k
         a.k_scale = fp8->k_scale;
         a.v_scale = fp8->v_scale;
     }
+    mimo::CheckArgs c;
+    c.cu = cu_newlens;
+    c.n_seqs = batch;
+    c.total = total_new;
+    c.ctx = ctx_lens;
+    c.batch = batch;
+    c.new_from_cu = true;
+    if (layer_type == MIMO_LAYER_GA && !pages) {
+        c.kv_base = kv_base;
+        c.kv_capacity = kv_capacity;
+    }
+    c.pages = pt;
+    c.pages_cover_new = true;
+    if (fp8) {
+        c.scales = fp8->k_scale;
+        c.scales_v = fp8->v_scale;
+        c.n_scales = dims->num_kv_heads;
+    }
+    if (int st = precheck(c, stream, "KV append")) return st;
     return hip_status(mimo::launch_kv_append(a, stream), "KV append launch");
 }
 
@@ -431,6 +530,14 @@ int mimo_attn_prefill_backward(const mimo_attn_dims* dims, int layer_type, const
     mimo::BackwardArgs a{q, k, v, out, lse, dout, cu_seqlens, sink, dq, dk, dv, dsink, workspace, num_seqs,
                          max_seqlen, total_tokens, dims->num_q_heads, dims->num_kv_heads, dims->sliding_window,
                          dims->softmax_scale, dims->value_scale, layer_type == MIMO_LAYER_SWA};
+    mimo::CheckArgs c;
+    c.cu = cu_seqlens;
+    c.n_seqs = num_seqs;
+    c.max_len = max_seqlen;
+    c.total = total_tokens;
+    c.sink = sink;
+    c.hq = dims->num_q_heads;
+    if (int st = precheck(c, stream, "backward")) return st;
     return hip_status(mimo::launch_prefill_backward(a, stream), "backward launch");
 }
 
@@ -466,6 +573,14 @@ int mimo_attn_prefill_rope(const mimo_attn_dims* dims, int layer_type, const uin
         return fail(MIMO_ERR_WORKSPACE, "fused RoPE needs %zu workspace bytes (got %zu%s)", need, workspace_bytes,
                     workspace ? "" : ", NULL");
     if (!aligned16(workspace)) return fail(MIMO_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    mimo::CheckArgs c;
+    c.cu = cu_seqlens;
+    c.n_seqs = num_seqs;
+    c.max_len = max_seqlen;
+    c.total = total_tokens;
+    c.sink = sink;
+    c.hq = dims->num_q_heads;
+    if (int st = precheck(c, stream, "mimo_attn_prefill_rope")) return st;
     mimo::RopePrepArgs r{k, positions, k_rot, static_cast<float*>(workspace), total_tokens, dims->num_kv_heads,
                          rotary_dim, (double)rope_theta};
     if (int st = hip_status(mimo::launch_rope_prep(r, stream), "RoPE preparation launch")) return st;
@@ -502,8 +617,20 @@ const char* mimo_status_string(int status) {
         case MIMO_ERR_UNSUPPORTED: return "MIMO_ERR_UNSUPPORTED";
         case MIMO_ERR_WORKSPACE: return "MIMO_ERR_WORKSPACE";
         case MIMO_ERR_HIP: return "MIMO_ERR_HIP";
+        case MIMO_ERR_PRECONDITION: return "MIMO_ERR_PRECONDITION";
         default: return "MIMO_ERR_UNKNOWN";
     }
+}
+
+int mimo_attn_set_check(int enable) {
+    const int before = check_on() ? 1 : 0;
+    g_check.store(enable ? 1 : 0);
+    return before;
+}
+
+int mimo_attn_check_flags(uint32_t* flags, int clear) {
+    if (!flags) return fail(MIMO_ERR_INVALID_ARG, "flags is NULL");
+    return hip_status(mimo::check_flags(flags, clear != 0), "check word read");
 }
 
 const char* mimo_last_error(void) { return g_last_error; }

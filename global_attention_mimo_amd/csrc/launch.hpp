@@ -187,4 +187,35 @@ inline size_t rope_table_bytes(int total_tokens, int rotary_dim) {
     return (size_t)total_tokens * (size_t)(rotary_dim / 2) * 2 * sizeof(float);
 }
 
+// Check mode: device-resident preconditions of one call, evaluated by a
+// one-pass kernel enqueued ahead of the call's own kernels.  Null pointers and
+// negative bounds switch a rule off.  The rules are in check_rules.hpp.
+struct CheckArgs {
+    const int32_t* cu = nullptr;       // [n_seqs + 1] cu_seqlens / cu_newlens
+    int n_seqs = 0;
+    int max_len = -1;                  // longest sequence the call allows
+    long long total = -1;              // required cu[n_seqs]
+    const int32_t* ctx = nullptr;      // [batch] ctx_lens
+    int batch = 0;
+    int max_ctx = -1;                  // largest ctx_lens[b] allowed
+    int new_tokens = 0;                // tokens each sequence appends (cu == null)
+    bool new_from_cu = false;          // sequence b appends cu[b+1] - cu[b] tokens
+    const int64_t* kv_base = nullptr;  // [batch]
+    const int64_t* kv_capacity = nullptr;
+    PageTable pages;
+    bool pages_cover_new = false;      // block entries of the appended positions (else of positions < ctx)
+    const float* sink = nullptr;       // [hq]
+    int hq = 0;
+    const float* scales = nullptr;     // FP8 per-KV-head scales, k then v: [2][n_scales]
+    const float* scales_v = nullptr;
+    int n_scales = 0;
+};
+// Enqueues the check kernel on `stream`.  Unless the stream is capturing a
+// graph, waits for it and returns this call's violation bits in *bits with
+// *gated = true; under capture *gated = false and the bits only reach the
+// device's sticky word.
+hipError_t run_check(const CheckArgs& a, hipStream_t stream, bool* gated, uint32_t* bits);
+// The current device's sticky word (every violation since it was last cleared).
+hipError_t check_flags(uint32_t* bits, bool clear);
+
 }  // namespace mimo

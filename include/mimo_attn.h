@@ -31,9 +31,11 @@
  *       out [T][Hq][128]     lse [T][Hq] (fp32)  sink [Hq] (fp32)
  *     Every tensor must be 16-byte aligned.
  *   - The caller allocates and owns every buffer (caches, workspace included).
- *     The library allocates nothing, never synchronises the device and never
- *     writes ctx_lens.  Its only state between calls is a per-thread copy of
- *     the last failure's message (mimo_last_error); no call reads it.
+ *     The library allocates nothing, never synchronises the device (check
+ *     mode aside) and never writes ctx_lens.  Its state between calls: a
+ *     per-thread copy of the last failure's message (mimo_last_error), the
+ *     check-mode switch and per-device word, and the no-allocation decode's
+ *     scratch array; no computed result depends on them.
  *   - Work is enqueued asynchronously on `stream` (NULL = the null stream).
  *   - Misuse detectable on the host returns a status BEFORE anything is
  *     enqueued.  A failed launch returns MIMO_ERR_HIP.  mimo_last_error()
@@ -42,8 +44,19 @@
  *     num_q_heads == 16 * num_kv_heads <= 65535; anything else is
  *     MIMO_ERR_UNSUPPORTED.
  *   - Inputs must be finite.  Device-resident preconditions (monotone
- *     cu_seqlens, ctx_lens within the stated bounds) are not checked on the
- *     device except where an entry point says so.
+ *     cu_seqlens, ctx_lens within the stated bounds, ...) are not checked on
+ *     the device except where an entry point says so, or in check mode.
+ *   - Check mode (environment MIMO_ATTN_CHECK=1 when the library is first
+ *     called, or mimo_attn_set_check): every call that reads device-resident
+ *     sizes, offsets, block tables, sinks or FP8 scales first enqueues a
+ *     check of them (the MIMO_CHECK_* rules below).  Outside graph capture
+ *     the call then waits for its stream and, on a violation, returns
+ *     MIMO_ERR_PRECONDITION without enqueuing its own kernels.  Under capture
+ *     the check joins the graph and only records its findings: the call's
+ *     kernels are captured too.  Findings also accumulate in a sticky word
+ *     per device, read with mimo_attn_check_flags.  Meant for debugging: it
+ *     synchronises, and concurrent checked calls on one device share the
+ *     word that reports the latest check.
  *   - Calls are reentrant; calls on different streams may run concurrently
  *     when their output buffers do not overlap.
  */
@@ -58,7 +71,7 @@
 extern "C" {
 #endif
 
-#define MIMO_ATTN_ABI_VERSION 9
+#define MIMO_ATTN_ABI_VERSION 10
 
 /* Layer type: which key set a query sees (model doc, Key features; config
  * layer_types). */
@@ -72,8 +85,25 @@ typedef enum {
     MIMO_ERR_INVALID_ARG = 1, /* NULL pointer, negative size, bad layer type ... */
     MIMO_ERR_UNSUPPORTED = 2, /* shape outside the specialised kernels        */
     MIMO_ERR_WORKSPACE = 3,   /* decode workspace missing or too small         */
-    MIMO_ERR_HIP = 4          /* a HIP launch or query failed                  */
+    MIMO_ERR_HIP = 4,         /* a HIP launch or query failed                  */
+    MIMO_ERR_PRECONDITION = 5 /* check mode: a device-resident argument breaks
+                                 its contract (MIMO_CHECK_* bits)              */
 } mimo_status;
+
+/* Check-mode findings, one bit per rule. */
+#define MIMO_CHECK_CU_START    0x001u /* cu_seqlens[0] != 0                            */
+#define MIMO_CHECK_CU_ORDER    0x002u /* cu_seqlens decreases somewhere                */
+#define MIMO_CHECK_CU_LENGTH   0x004u /* a sequence longer than max_seqlen / max_newlen */
+#define MIMO_CHECK_CU_TOTAL    0x008u /* cu_seqlens[num_seqs] != total_tokens / total_new */
+#define MIMO_CHECK_CTX_RANGE   0x010u /* ctx_lens[b] < 0, above max_ctx, or ctx + new
+                                         positions past INT32_MAX                     */
+#define MIMO_CHECK_KV_BASE     0x020u /* kv_base[b] < 0                                */
+#define MIMO_CHECK_CAPACITY    0x040u /* ctx + new above kv_capacity[b], or positions
+                                         past max_blocks * page_size                  */
+#define MIMO_CHECK_BLOCK_TABLE 0x080u /* a block entry the call reads or writes is
+                                         outside [0, num_pages)                       */
+#define MIMO_CHECK_SINK        0x100u /* a sink value is NaN or +inf                   */
+#define MIMO_CHECK_FP8_SCALE   0x200u /* an FP8 scale is not positive and finite       */
 
 /* Attention shape, mirroring MiMoV2FlashConfig (model doc, MiMoV2FlashConfig):
  * num_attention_heads, num_key_value_heads, head_dim, v_head_dim,
@@ -478,6 +508,24 @@ int mimo_attn_prefill_rope(const mimo_attn_dims* dims, int layer_type,
                            const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen, int32_t total_tokens,
                            float rope_theta, int32_t rotary_dim, const float* sink, uint16_t* out, float* lse,
                            uint16_t* k_rot, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Check mode (see the conventions above).  mimo_attn_set_check switches it on
+ * (enable != 0) or off for the whole process and returns the previous
+ * setting; before the first call of either function the setting is
+ * MIMO_ATTN_CHECK=1 from the environment.  Switching needs no device.
+ */
+int mimo_attn_set_check(int enable);
+
+/*
+ * Reads the current device's sticky check word into *flags (host): the OR of
+ * the MIMO_CHECK_* bits of every check since the word was last cleared, on
+ * any stream, captured graphs' replays included.  clear != 0 then resets it.
+ * Synchronous: call it once the checked work has finished (e.g. after
+ * hipDeviceSynchronize).  NULL flags is MIMO_ERR_INVALID_ARG; a HIP failure
+ * is MIMO_ERR_HIP.
+ */
+int mimo_attn_check_flags(uint32_t* flags, int clear);
 
 /* Static English name of a status code ("MIMO_OK", ...). */
 const char* mimo_status_string(int status);

@@ -3,8 +3,18 @@
 // can be built alone with AddressSanitizer and UndefinedBehaviorSanitizer
 // and exercised on a machine without a GPU.  Every launch reports that no
 // device is present; no test of the validation layer expects a launch to
-// succeed.  Test infrastructure only.
+// succeed.  The check-mode pass is the exception: it evaluates the library's
+// own rules (check_rules.hpp) on the host, so that with HOST pointers in place
+// of device ones the gate in front of every launch can be exercised on the
+// CPU.  Test infrastructure only.
+#include <cstdint>
+
+#include "../../global_attention_mimo_amd/csrc/check_rules.hpp"
 #include "../../global_attention_mimo_amd/csrc/launch.hpp"
+
+namespace {
+uint32_t g_sticky = 0;
+}
 
 namespace mimo {
 hipError_t launch_prefill(const PrefillArgs&, hipStream_t) { return hipErrorNoDevice; }
@@ -15,6 +25,17 @@ hipError_t launch_kv_append(const AppendArgs&, hipStream_t) { return hipErrorNoD
 hipError_t launch_prefill_backward(const BackwardArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_rope(const RopeArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_rope_prep(const RopePrepArgs&, hipStream_t) { return hipErrorNoDevice; }
+hipError_t run_check(const CheckArgs& a, hipStream_t, bool* gated, uint32_t* bits) {
+    *bits = check_rules(a, 0, 1);
+    *gated = true;
+    g_sticky |= *bits;
+    return hipSuccess;
+}
+hipError_t check_flags(uint32_t* bits, bool clear) {
+    *bits = g_sticky;
+    if (clear) g_sticky = 0;
+    return hipSuccess;
+}
 hipError_t noalloc_scratch(void** ptr) {
     *ptr = nullptr;
     return hipErrorNoDevice;

@@ -2,10 +2,11 @@
 exercised by the existing tests, on the CPU:
 
   * the C-ABI validation layer (global_attention_mimo_amd/csrc/api.cpp: every
-    argument check, size computation and error mapping) built with g++ and the
-    sanitizers, linked with host-only launcher stand-ins
-    (tests/sanitize/launch_stub.cpp), and loaded by tests/test_abi.py through
-    MIMO_ATTN_LIBRARY;
+    argument check, size computation and error mapping, and check mode's
+    rules and gate) built with g++ and the sanitizers, linked with host-only
+    launcher stand-ins (tests/sanitize/launch_stub.cpp), and loaded by
+    tests/test_abi.py through MIMO_ATTN_LIBRARY and by
+    tests/test_check_mode.py through MIMO_ATTN_HOST_STUB;
   * the fp64 oracle (oracle/mimo_oracle.c) built with gcc and the sanitizers
     and run against every pin of tests/oracle_pins.py.
 
@@ -49,9 +50,10 @@ def test_validation_layer_under_asan_and_ubsan(tmp_path):
     subprocess.run(cmd, check=True)
     nm = subprocess.run(["nm", "-D", lib], capture_output=True, text=True).stdout
     assert "__asan" in nm and "__ubsan" in nm, "the validation layer was not instrumented"
-    res = subprocess.run([sys.executable, "-m", "pytest", os.path.join(HERE, "test_abi.py"), "-q", "-x",
-                          "-p", "no:cacheprovider"], cwd=ROOT, capture_output=True, text=True, timeout=600,
-                         env=_env(MIMO_ATTN_LIBRARY=lib))
+    res = subprocess.run([sys.executable, "-m", "pytest", os.path.join(HERE, "test_abi.py"),
+                          os.path.join(HERE, "test_check_mode.py"), "-q", "-x", "-p", "no:cacheprovider"], cwd=ROOT,
+                         capture_output=True, text=True, timeout=600,
+                         env=_env(MIMO_ATTN_LIBRARY=lib, MIMO_ATTN_HOST_STUB=lib))
     assert res.returncode == 0, res.stdout[-3000:] + res.stderr[-3000:]
     assert " passed" in res.stdout
 
