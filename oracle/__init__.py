@@ -83,6 +83,18 @@ class Oracle:
                                           _P, _I]
         lib.oracle_kv_append_fp8.restype = _I
         lib.oracle_kv_append_fp8.argtypes = [_I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P]
+        lib.oracle_decode_fp8_paged.restype = _I
+        lib.oracle_decode_fp8_paged.argtypes = [_I, _I, _I, _I, _F, _F, _P, _P, _P, _P, _P, _P, _I, _I, _I64, _P,
+                                                _P, _P, _I, _P, _P, _P, _I]
+        lib.oracle_prefill_chunk_fp8.restype = _I
+        lib.oracle_prefill_chunk_fp8.argtypes = [_I, _I, _I, _I, _F, _F, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P,
+                                                 _P, _P, _P, _P, _I]
+        lib.oracle_prefill_chunk_fp8_paged.restype = _I
+        lib.oracle_prefill_chunk_fp8_paged.argtypes = [_I, _I, _I, _I, _F, _F, _P, _P, _P, _P, _I, _P, _P, _P, _I,
+                                                       _I, _I64, _P, _P, _P, _P, _P, _P, _I]
+        lib.oracle_kv_append_fp8_paged.restype = _I
+        lib.oracle_kv_append_fp8_paged.argtypes = [_I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I64, _P,
+                                                   _P]
         lib.oracle_e4m3_encode.restype = None
         lib.oracle_e4m3_encode.argtypes = [_P, _P, _I64]
         lib.oracle_e4m3_decode.restype = None
@@ -430,6 +442,95 @@ class Oracle:
                                                  self._ptr(ctx), cu.shape[0] - 1, self._ptr(k_pool),
                                                  self._ptr(v_pool), self._ptr(base), self._ptr(cap), self._ptr(ks),
                                                  self._ptr(vs)))
+
+    @staticmethod
+    def _codes(pool, hkv, d):
+        c = np.ascontiguousarray(pool, dtype=np.uint8)
+        if c.shape[1:] != (hkv, d):
+            raise ValueError("FP8 pools are [N][Hkv][D] uint8")
+        return c
+
+    def decode_fp8_paged(self, q, k_new, v_new, k_pool, v_pool, block_table, page_size: int, k_scale, v_scale,
+                         ctx_lens, *, scale: float, value_scale: float = 1.0, sink=None, nthreads: int = 0):
+        """GA decode over a paged FP8 pool: cached position j of sequence b is the code row
+        block_table[b][j // page_size] * page_size + j % page_size, read as code * scale[g]."""
+        q = np.ascontiguousarray(q)
+        batch, hq, dqk = q.shape
+        hkv, dv = v_new.shape[1], v_new.shape[2]
+        q = self._u16(q, (hq, dqk))
+        kn = self._u16(k_new, (hkv, dqk))
+        vn = self._u16(v_new, (hkv, dv))
+        kc, vc = self._codes(k_pool, hkv, dqk), self._codes(v_pool, hkv, dv)
+        tb, mb, npages = self._table(block_table, page_size, kc)
+        ks, vs = self._scales(k_scale, hkv), self._scales(v_scale, hkv)
+        ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+        sk = None if sink is None else np.ascontiguousarray(sink, dtype=np.float32)
+        out = np.empty((batch, hq, dv), np.float64)
+        lse = np.empty((batch, hq), np.float64)
+        nth = nthreads if nthreads > 0 else self.default_threads()
+        rc = self.lib.oracle_decode_fp8_paged(hq, hkv, dqk, dv, scale, value_scale, self._ptr(q), self._ptr(kn),
+                                              self._ptr(vn), self._ptr(kc), self._ptr(vc), self._ptr(tb), mb,
+                                              page_size, npages, self._ptr(ks), self._ptr(vs), self._ptr(ctx), batch,
+                                              self._ptr(sk), self._ptr(out), self._ptr(lse), nth)
+        if rc != OK:
+            raise ValueError(f"oracle_decode_fp8_paged rejected its arguments (status {rc})")
+        return out, lse
+
+    def prefill_chunk_fp8(self, q, k, v, cu_newlens, k_pool, v_pool, k_scale, v_scale, ctx_lens, *,
+                          kv_base=None, block_table=None, page_size: int = 0, scale: float,
+                          value_scale: float = 1.0, sink=None, nthreads: int = 0):
+        """GA chunked prefill whose cached positions are FP8 codes, in a contiguous pool (kv_base) or a
+        paged one (block_table, page_size), read as code * scale[g]; the chunk's k, v are bf16."""
+        q = np.ascontiguousarray(q)
+        hq, dqk = q.shape[1], q.shape[2]
+        hkv, dv = k.shape[1], v.shape[2]
+        q = self._u16(q, (hq, dqk))
+        k = self._u16(k, (hkv, dqk))
+        v = self._u16(v, (hkv, dv))
+        kc, vc = self._codes(k_pool, hkv, dqk), self._codes(v_pool, hkv, dv)
+        ks, vs = self._scales(k_scale, hkv), self._scales(v_scale, hkv)
+        cu = np.ascontiguousarray(cu_newlens, dtype=np.int32)
+        batch = cu.shape[0] - 1
+        ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+        sk = None if sink is None else np.ascontiguousarray(sink, dtype=np.float32)
+        tn = int(cu[-1])
+        out = np.empty((tn, hq, dv), np.float64)
+        lse = np.empty((tn, hq), np.float64)
+        nth = nthreads if nthreads > 0 else self.default_threads()
+        if block_table is not None:
+            tb, mb, npages = self._table(block_table, page_size, kc)
+            rc = self.lib.oracle_prefill_chunk_fp8_paged(
+                hq, hkv, dqk, dv, scale, value_scale, self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(cu), batch,
+                self._ptr(kc), self._ptr(vc), self._ptr(tb), mb, page_size, npages, self._ptr(ks), self._ptr(vs),
+                self._ptr(ctx), self._ptr(sk), self._ptr(out), self._ptr(lse), nth)
+        else:
+            base = np.ascontiguousarray(kv_base, dtype=np.int64)
+            rc = self.lib.oracle_prefill_chunk_fp8(
+                hq, hkv, dqk, dv, scale, value_scale, self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(cu), batch,
+                self._ptr(kc), self._ptr(vc), self._ptr(base), self._ptr(ks), self._ptr(vs), self._ptr(ctx),
+                self._ptr(sk), self._ptr(out), self._ptr(lse), nth)
+        if rc != OK:
+            raise ValueError(f"oracle_prefill_chunk_fp8 rejected its arguments (status {rc})")
+        return out, lse
+
+    def kv_append_fp8_paged(self, k, v, cu_newlens, ctx_lens, k_pool, v_pool, block_table, page_size: int, k_scale,
+                            v_scale) -> int:
+        """Quantises new tokens into a paged FP8 pool in place; returns the status code."""
+        k = np.ascontiguousarray(k)
+        v = np.ascontiguousarray(v)
+        hkv, dqk, dv = k.shape[1], k.shape[2], v.shape[2]
+        for c in (k_pool, v_pool):
+            if not (c.flags["C_CONTIGUOUS"] and c.dtype == np.uint8):
+                raise TypeError("FP8 pools must be C-contiguous uint8 arrays")
+        tb, mb, npages = self._table(block_table, page_size, k_pool)
+        cu = np.ascontiguousarray(cu_newlens, dtype=np.int32)
+        ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+        ks, vs = self._scales(k_scale, hkv), self._scales(v_scale, hkv)
+        return int(self.lib.oracle_kv_append_fp8_paged(hkv, dqk, dv, self._ptr(k), self._ptr(v), self._ptr(cu),
+                                                       self._ptr(ctx), cu.shape[0] - 1, self._ptr(k_pool),
+                                                       self._ptr(v_pool), self._ptr(tb), mb, page_size, npages,
+                                                       self._ptr(ks), self._ptr(vs)))
+
 
 _default: Optional[Oracle] = None
 

@@ -561,8 +561,8 @@ static void* decode_worker(void* arg) {
         if (d->layer_type == ORACLE_SWA) lo = p - (d->window - 1) > 0 ? p - (d->window - 1) : 0;
         int n = 0;
         for (int j = lo; j < p; ++j, ++n) {
-            if (jb->k8) { /* FP8 pool: codes of row kv_base[b] + j */
-                size_t row = (size_t)(jb->kv_base[b] + j);
+            if (jb->k8) { /* FP8 pool: codes of row kv_base[b] + j, or of the paged row */
+                size_t row = jb->pages ? (size_t)paged_row(jb->pages, b, j) : (size_t)(jb->kv_base[b] + j);
                 kr[n] = vr[n] = NULL;
                 k8r[n] = jb->k8 + (row * d->hkv + g) * d->dqk;
                 v8r[n] = jb->v8 + (row * d->hkv + g) * d->dv;
@@ -646,9 +646,16 @@ int oracle_decode_paged(int hq, int hkv, int dqk, int dv, float scale, float val
 /* as in decode), the others from the chunk's own k/v rows.  The cache is   */
 /* read, never written (appending the chunk is a separate call).            */
 
+/* An FP8 GA cache of a chunked prefill: code pools and per-KV-head scales. */
+typedef struct {
+    const uint8_t *k8, *v8;
+    const float *kscale, *vscale;
+} chunk_fp8_t;
+
 typedef struct {
     const dims_t* d;
     const uint16_t *q, *k, *v, *k_cache, *v_cache;
+    const chunk_fp8_t* f8;  /* cached rows are FP8 codes when set */
     const int32_t* cu;
     const int64_t* kv_base;
     const pages_t* pages;
@@ -665,6 +672,8 @@ static void* chunk_worker(void* arg) {
     const dims_t* d = jb->d;
     const uint16_t** kr = malloc(sizeof(*kr) * (size_t)jb->maxkeys);
     const uint16_t** vr = malloc(sizeof(*vr) * (size_t)jb->maxkeys);
+    const uint8_t** k8r = malloc(sizeof(*k8r) * (size_t)jb->maxkeys);
+    const uint8_t** v8r = malloc(sizeof(*v8r) * (size_t)jb->maxkeys);
     double* sc = malloc(sizeof(double) * (size_t)jb->maxkeys);
     int group = d->hq / d->hkv;
     for (;;) {
@@ -681,7 +690,13 @@ static void* chunk_worker(void* arg) {
         if (d->layer_type == ORACLE_SWA) lo = p - (d->window - 1) > 0 ? p - (d->window - 1) : 0;
         int n = 0;
         for (int j = lo; j <= p; ++j, ++n) {
-            if (j < c) {
+            k8r[n] = v8r[n] = NULL;
+            if (j < c && jb->f8) { /* FP8 codes of the GA pool row (contiguous or paged) */
+                size_t row = jb->pages ? (size_t)paged_row(jb->pages, b, j) : (size_t)(jb->kv_base[b] + j);
+                kr[n] = vr[n] = NULL;
+                k8r[n] = jb->f8->k8 + (row * d->hkv + g) * d->dqk;
+                v8r[n] = jb->f8->v8 + (row * d->hkv + g) * d->dv;
+            } else if (j < c) {
                 kr[n] = cached_row(d, jb->k_cache, jb->ring, jb->kv_base, jb->pages, b, j, g, 0);
                 vr[n] = cached_row(d, jb->v_cache, jb->ring, jb->kv_base, jb->pages, b, j, g, 1);
             } else {
@@ -692,17 +707,18 @@ static void* chunk_worker(void* arg) {
         }
         double sigma = 0.0;
         int hs = sink_present(jb->sink, h, &sigma);
-        attend_row(d, jb->q + ((size_t)t * d->hq + h) * d->dqk, n, kr, vr, NULL, hs, sigma, sc,
+        fp8_rows_t f8 = {k8r, v8r, jb->f8 ? (double)jb->f8->kscale[g] : 1.0, jb->f8 ? (double)jb->f8->vscale[g] : 1.0};
+        attend_row(d, jb->q + ((size_t)t * d->hq + h) * d->dqk, n, kr, vr, jb->f8 ? &f8 : NULL, hs, sigma, sc,
                    jb->out + ((size_t)t * d->hq + h) * d->dv, jb->lse + (size_t)t * d->hq + h, NULL, NULL);
     }
-    free(kr); free(vr); free(sc);
+    free(kr); free(vr); free(k8r); free(v8r); free(sc);
     return NULL;
 }
 
 static int chunk_impl(const dims_t* d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       const int32_t* cu_newlens, int batch, const uint16_t* k_cache, const uint16_t* v_cache,
-                      int ring_slots, const int64_t* kv_base, const pages_t* pages, const int32_t* ctx_lens,
-                      const float* sink, double* out, double* lse, int nthreads) {
+                      int ring_slots, const int64_t* kv_base, const pages_t* pages, const chunk_fp8_t* f8,
+                      const int32_t* ctx_lens, const float* sink, double* out, double* lse, int nthreads) {
     if (!check_dims(d) || batch < 1 || !q || !k || !v || !cu_newlens || !ctx_lens || !out || !lse)
         return ORACLE_EINVAL;
     if (d->layer_type == ORACLE_SWA && ring_slots != d->window - 1) return ORACLE_EINVAL;
@@ -712,13 +728,13 @@ static int chunk_impl(const dims_t* d, const uint16_t* q, const uint16_t* k, con
     for (int b = 0; b < batch; ++b) {
         int n = cu_newlens[b + 1] - cu_newlens[b];
         if (n < 0 || ctx_lens[b] < 0) return ORACLE_EINVAL;
-        if (ctx_lens[b] > 0 && (!k_cache || !v_cache)) return ORACLE_EINVAL;
+        if (ctx_lens[b] > 0 && !f8 && (!k_cache || !v_cache)) return ORACLE_EINVAL;
         if (ctx_lens[b] + n > maxkeys) maxkeys = ctx_lens[b] + n;
     }
     if (pages && !pages_cover(pages, ctx_lens, batch)) return ORACLE_EINVAL;
     chunk_job_t jb;
     memset(&jb, 0, sizeof jb);
-    jb.d = d; jb.q = q; jb.k = k; jb.v = v; jb.k_cache = k_cache; jb.v_cache = v_cache;
+    jb.d = d; jb.q = q; jb.k = k; jb.v = v; jb.k_cache = k_cache; jb.v_cache = v_cache; jb.f8 = f8;
     jb.cu = cu_newlens; jb.kv_base = kv_base; jb.pages = pages; jb.ctx = ctx_lens; jb.batch = batch;
     jb.ring = ring_slots; jb.maxkeys = maxkeys; jb.sink = sink; jb.out = out; jb.lse = lse;
     jb.total = cu_newlens[batch];
@@ -739,8 +755,8 @@ int oracle_prefill_chunk(int hq, int hkv, int dqk, int dv, int layer_type, int w
                          const int64_t* kv_base, const int32_t* ctx_lens,
                          const float* sink, double* out, double* lse, int nthreads) {
     dims_t d = {hq, hkv, dqk, dv, layer_type, window, (double)scale, (double)value_scale};
-    return chunk_impl(&d, q, k, v, cu_newlens, batch, k_cache, v_cache, ring_slots, kv_base, NULL, ctx_lens, sink,
-                      out, lse, nthreads);
+    return chunk_impl(&d, q, k, v, cu_newlens, batch, k_cache, v_cache, ring_slots, kv_base, NULL, NULL, ctx_lens,
+                      sink, out, lse, nthreads);
 }
 
 /* GA chunked prefill whose cached positions live in a paged pool (as for
@@ -754,8 +770,8 @@ int oracle_prefill_chunk_paged(int hq, int hkv, int dqk, int dv, float scale, fl
                                int nthreads) {
     dims_t d = {hq, hkv, dqk, dv, ORACLE_GA, 0, (double)scale, (double)value_scale};
     pages_t pg = {block_table, max_blocks, page_size, num_pages};
-    return chunk_impl(&d, q, k, v, cu_newlens, batch, k_cache, v_cache, 0, NULL, &pg, ctx_lens, sink, out, lse,
-                      nthreads);
+    return chunk_impl(&d, q, k, v, cu_newlens, batch, k_cache, v_cache, 0, NULL, &pg, NULL, ctx_lens, sink, out,
+                      lse, nthreads);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -888,6 +904,28 @@ static int scales_ok(const float* s, int hkv) {
     return 1;
 }
 
+static int decode_fp8_impl(const dims_t* d, const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                           const uint8_t* k_cache, const uint8_t* v_cache, const int64_t* kv_base,
+                           const pages_t* pages, const float* k_scale, const float* v_scale,
+                           const int32_t* ctx_lens, int batch, const float* sink, double* out, double* lse,
+                           int nthreads) {
+    if (!check_dims(d) || batch < 1 || !q || !k_new || !v_new || !ctx_lens || !out || !lse ||
+        (!kv_base && !pages) || !k_cache || !v_cache || !scales_ok(k_scale, d->hkv) || !scales_ok(v_scale, d->hkv))
+        return ORACLE_EINVAL;
+    for (int b = 0; b < batch; ++b)
+        if (ctx_lens[b] < 0) return ORACLE_EINVAL;
+    if (pages && !pages_cover(pages, ctx_lens, batch)) return ORACLE_EINVAL;
+    decode_job_t jb;
+    memset(&jb, 0, sizeof jb);
+    jb.d = d; jb.q = q; jb.k_new = k_new; jb.v_new = v_new; jb.k8 = k_cache; jb.v8 = v_cache;
+    jb.k8scale = k_scale; jb.v8scale = v_scale; jb.kv_base = kv_base; jb.pages = pages; jb.ctx = ctx_lens;
+    jb.batch = batch; jb.sink = sink; jb.out = out; jb.lse = lse;
+    pthread_mutex_init(&jb.mu, NULL);
+    run_threads(decode_worker, &jb, nthreads);
+    pthread_mutex_destroy(&jb.mu);
+    return ORACLE_OK;
+}
+
 /* GA decode over an FP8 pool: cached positions j < p read as code * scale. */
 int oracle_decode_fp8(int hq, int hkv, int dqk, int dv, float scale, float value_scale,
                       const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
@@ -895,44 +933,99 @@ int oracle_decode_fp8(int hq, int hkv, int dqk, int dv, float scale, float value
                       const float* k_scale, const float* v_scale, const int32_t* ctx_lens, int batch,
                       const float* sink, double* out, double* lse, int nthreads) {
     dims_t d = {hq, hkv, dqk, dv, ORACLE_GA, 0, (double)scale, (double)value_scale};
-    if (!check_dims(&d) || batch < 1 || !q || !k_new || !v_new || !ctx_lens || !out || !lse || !kv_base ||
-        !k_cache || !v_cache || !scales_ok(k_scale, hkv) || !scales_ok(v_scale, hkv))
-        return ORACLE_EINVAL;
-    for (int b = 0; b < batch; ++b)
-        if (ctx_lens[b] < 0) return ORACLE_EINVAL;
-    decode_job_t jb;
-    memset(&jb, 0, sizeof jb);
-    jb.d = &d; jb.q = q; jb.k_new = k_new; jb.v_new = v_new; jb.k8 = k_cache; jb.v8 = v_cache;
-    jb.k8scale = k_scale; jb.v8scale = v_scale; jb.kv_base = kv_base; jb.ctx = ctx_lens; jb.batch = batch;
-    jb.sink = sink; jb.out = out; jb.lse = lse;
-    pthread_mutex_init(&jb.mu, NULL);
-    run_threads(decode_worker, &jb, nthreads);
-    pthread_mutex_destroy(&jb.mu);
-    return ORACLE_OK;
+    if (!kv_base) return ORACLE_EINVAL;
+    return decode_fp8_impl(&d, q, k_new, v_new, k_cache, v_cache, kv_base, NULL, k_scale, v_scale, ctx_lens, batch,
+                           sink, out, lse, nthreads);
+}
+
+/* GA decode over a paged FP8 pool: the codes of position j of sequence b in
+ * the row the block table gives (as oracle_decode_paged), read as code * scale. */
+int oracle_decode_fp8_paged(int hq, int hkv, int dqk, int dv, float scale, float value_scale,
+                            const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                            const uint8_t* k_cache, const uint8_t* v_cache,
+                            const int32_t* block_table, int max_blocks, int page_size, int64_t num_pages,
+                            const float* k_scale, const float* v_scale, const int32_t* ctx_lens, int batch,
+                            const float* sink, double* out, double* lse, int nthreads) {
+    dims_t d = {hq, hkv, dqk, dv, ORACLE_GA, 0, (double)scale, (double)value_scale};
+    pages_t pg = {block_table, max_blocks, page_size, num_pages};
+    return decode_fp8_impl(&d, q, k_new, v_new, k_cache, v_cache, NULL, &pg, k_scale, v_scale, ctx_lens, batch,
+                           sink, out, lse, nthreads);
+}
+
+/* GA chunked prefill whose cached positions are FP8 codes (contiguous pool at
+ * kv_base[b] + j, or paged when block_table is non-NULL), read as code * scale;
+ * the chunk's own keys and values are bf16 as given. */
+static int chunk_fp8_impl(int hq, int hkv, int dqk, int dv, float scale, float value_scale,
+                          const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                          const int32_t* cu_newlens, int batch, const uint8_t* k_cache, const uint8_t* v_cache,
+                          const int64_t* kv_base, const pages_t* pages, const float* k_scale, const float* v_scale,
+                          const int32_t* ctx_lens, const float* sink, double* out, double* lse, int nthreads) {
+    dims_t d = {hq, hkv, dqk, dv, ORACLE_GA, 0, (double)scale, (double)value_scale};
+    if (!k_cache || !v_cache || !scales_ok(k_scale, hkv) || !scales_ok(v_scale, hkv)) return ORACLE_EINVAL;
+    chunk_fp8_t f8 = {k_cache, v_cache, k_scale, v_scale};
+    return chunk_impl(&d, q, k, v, cu_newlens, batch, NULL, NULL, 0, kv_base, pages, &f8, ctx_lens, sink, out, lse,
+                      nthreads);
+}
+
+int oracle_prefill_chunk_fp8(int hq, int hkv, int dqk, int dv, float scale, float value_scale,
+                             const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             const int32_t* cu_newlens, int batch, const uint8_t* k_cache, const uint8_t* v_cache,
+                             const int64_t* kv_base, const float* k_scale, const float* v_scale,
+                             const int32_t* ctx_lens, const float* sink, double* out, double* lse, int nthreads) {
+    if (!kv_base) return ORACLE_EINVAL;
+    return chunk_fp8_impl(hq, hkv, dqk, dv, scale, value_scale, q, k, v, cu_newlens, batch, k_cache, v_cache,
+                          kv_base, NULL, k_scale, v_scale, ctx_lens, sink, out, lse, nthreads);
+}
+
+int oracle_prefill_chunk_fp8_paged(int hq, int hkv, int dqk, int dv, float scale, float value_scale,
+                                   const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   const int32_t* cu_newlens, int batch, const uint8_t* k_cache,
+                                   const uint8_t* v_cache, const int32_t* block_table, int max_blocks,
+                                   int page_size, int64_t num_pages, const float* k_scale, const float* v_scale,
+                                   const int32_t* ctx_lens, const float* sink, double* out, double* lse,
+                                   int nthreads) {
+    pages_t pg = {block_table, max_blocks, page_size, num_pages};
+    return chunk_fp8_impl(hq, hkv, dqk, dv, scale, value_scale, q, k, v, cu_newlens, batch, k_cache, v_cache, NULL,
+                          &pg, k_scale, v_scale, ctx_lens, sink, out, lse, nthreads);
 }
 
 /* KV append into an FP8 GA pool: as oracle_kv_append for GA (rows kv_base[b]
  * + position, a sequence past its capacity skipped whole with
  * ORACLE_ECAPACITY), each element stored as its E4M3 code under the scale of
  * its KV head. */
-int oracle_kv_append_fp8(int hkv, int dqk, int dv, const uint16_t* k, const uint16_t* v,
-                         const int32_t* cu_newlens, const int32_t* ctx_lens, int batch,
-                         uint8_t* k_cache, uint8_t* v_cache, const int64_t* kv_base, const int64_t* kv_capacity,
-                         const float* k_scale, const float* v_scale) {
+static int kv_append_fp8_impl(int hkv, int dqk, int dv, const uint16_t* k, const uint16_t* v,
+                              const int32_t* cu_newlens, const int32_t* ctx_lens, int batch,
+                              uint8_t* k_cache, uint8_t* v_cache, const int64_t* kv_base, const int64_t* kv_capacity,
+                              const pages_t* pages, const float* k_scale, const float* v_scale) {
     if (hkv <= 0 || dqk <= 0 || dv <= 0 || batch < 1 || !k || !v || !cu_newlens || !ctx_lens || !k_cache ||
-        !v_cache || !kv_base || !kv_capacity || !scales_ok(k_scale, hkv) || !scales_ok(v_scale, hkv))
+        !v_cache || !scales_ok(k_scale, hkv) || !scales_ok(v_scale, hkv))
+        return ORACLE_EINVAL;
+    if (pages ? (!pages->table || pages->max_blocks < 1 || pages->page_size < 1 || pages->num_pages < 1)
+              : (!kv_base || !kv_capacity))
         return ORACLE_EINVAL;
     int status = ORACLE_OK;
     for (int b = 0; b < batch; ++b) {
         int n = cu_newlens[b + 1] - cu_newlens[b];
         if (n < 0) return ORACLE_EINVAL;
-        if ((int64_t)ctx_lens[b] + n > kv_capacity[b]) {
+        int64_t room = pages ? (int64_t)pages->max_blocks * pages->page_size : kv_capacity[b];
+        if ((int64_t)ctx_lens[b] + n > room) {
             status = ORACLE_ECAPACITY;
             continue;
         }
         for (int i = 0; i < n; ++i) {
             size_t src = (size_t)cu_newlens[b] + i;
-            size_t dst = (size_t)(kv_base[b] + ctx_lens[b] + i);
+            int64_t pos = (int64_t)ctx_lens[b] + i;
+            size_t dst;
+            if (pages) {
+                int32_t page = pages->table[(size_t)b * pages->max_blocks + (size_t)(pos / pages->page_size)];
+                if (page < 0 || page >= pages->num_pages) {
+                    status = ORACLE_ECAPACITY;
+                    continue;
+                }
+                dst = (size_t)paged_row(pages, b, pos);
+            } else {
+                dst = (size_t)(kv_base[b] + pos);
+            }
             for (int g = 0; g < hkv; ++g) {
                 for (int x = 0; x < dqk; ++x)
                     k_cache[(dst * hkv + g) * dqk + x] = e4m3_quantize(k[(src * hkv + g) * dqk + x], k_scale[g]);
@@ -942,6 +1035,26 @@ int oracle_kv_append_fp8(int hkv, int dqk, int dv, const uint16_t* k, const uint
         }
     }
     return status;
+}
+
+int oracle_kv_append_fp8(int hkv, int dqk, int dv, const uint16_t* k, const uint16_t* v,
+                         const int32_t* cu_newlens, const int32_t* ctx_lens, int batch,
+                         uint8_t* k_cache, uint8_t* v_cache, const int64_t* kv_base, const int64_t* kv_capacity,
+                         const float* k_scale, const float* v_scale) {
+    return kv_append_fp8_impl(hkv, dqk, dv, k, v, cu_newlens, ctx_lens, batch, k_cache, v_cache, kv_base,
+                              kv_capacity, NULL, k_scale, v_scale);
+}
+
+/* KV append into a paged FP8 GA pool: the codes as oracle_kv_append_fp8, the
+ * rows, refusals and ORACLE_ECAPACITY as oracle_kv_append_paged. */
+int oracle_kv_append_fp8_paged(int hkv, int dqk, int dv, const uint16_t* k, const uint16_t* v,
+                               const int32_t* cu_newlens, const int32_t* ctx_lens, int batch,
+                               uint8_t* k_cache, uint8_t* v_cache,
+                               const int32_t* block_table, int max_blocks, int page_size, int64_t num_pages,
+                               const float* k_scale, const float* v_scale) {
+    pages_t pg = {block_table, max_blocks, page_size, num_pages};
+    return kv_append_fp8_impl(hkv, dqk, dv, k, v, cu_newlens, ctx_lens, batch, k_cache, v_cache, NULL, NULL, &pg,
+                              k_scale, v_scale);
 }
 
 /* The E4M3 codec on its own (for the pins): codes of n floats, values of n codes. */

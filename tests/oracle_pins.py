@@ -920,6 +920,148 @@ def pin_fp8_append_codes(orc):
     assert not kc[:3].any() and not kc[8:].any() and not vc[8:].any(), "FP8 append wrote outside its rows"
     assert kc[3, 1, 0] == 0x7e and kc[3, 1, 1] == 0xfe, "saturation"
 
+def pin_fp8_paged_decode_is_flat_decode(orc):
+    """FP8 decode over a paged pool whose pages hold the flat FP8 pool's code
+    rows in a shuffled order equals FP8 decode over the flat pool (page sizes 1,
+    16, 64; contexts around page boundaries)."""
+    ctx = [0, 1, 15, 16, 17, 64, 200]
+    ks, vs = np.float32([0.37, 0.011, 1.7, 0.05]), np.float32([0.021, 0.9, 0.33, 3.1])
+    x, kc, vc, _ = _fp8_pool_case(ctx, 64, ks, vs, False)
+    sc = float(np.float32(synth.SOFTMAX_SCALE))
+    base, cl = x.kv_base.numpy(), x.ctx_lens.numpy()
+    args = (_bits(x.q), _bits(x.k_new), _bits(x.v_new))
+    of, lf = orc.decode_fp8(*args, kc, vc, base, ks, vs, cl, scale=sc, sink=x.sink.numpy())
+    rng = np.random.default_rng(64)
+    for P in (1, 16, 64):
+        mb = max((c + P - 1) // P for c in ctx) + 1
+        (kp, vp), tb = _paged_from_flat([kc, vc], base, ctx, P, mb, rng)
+        op, lp = orc.decode_fp8_paged(*args, kp, vp, tb, P, ks, vs, cl, scale=sc, sink=x.sink.numpy())
+        assert np.array_equal(op, of) and np.array_equal(lp, lf), f"paged FP8 decode differs from flat (page {P})"
+
+
+def _fp8_chunk_case(seed, k_scale, v_scale, exact_bf16):
+    """Chunked-prefill inputs over an FP8 pool: sequence b has cached[b]
+    positions (code rows at base[b] ..) and brings rest[b] new bf16 tokens."""
+    lengths = [40, 170, 64, 33]
+    cached = [0, 33, 64, 32]
+    rest = [L - c for L, c in zip(lengths, cached)]
+    x = _make(rest, seed=seed)
+    rng = np.random.default_rng(seed)
+    base = np.array([3, 50, 120, 300], np.int64)
+    rows = 340
+    kc = rng.integers(0, 256, (rows, 4, 192)).astype(np.uint8)
+    vc = rng.integers(0, 256, (rows, 4, 128)).astype(np.uint8)
+    kc[(kc & 0x7f) == 0x7f] ^= 1
+    vc[(vc & 0x7f) == 0x7f] ^= 1
+    pools = None
+    if exact_bf16:
+        dec = _torch_decode_all()
+        kf = (dec[kc] * np.asarray(k_scale)[None, :, None]).astype(np.float32)
+        vf = (dec[vc] * np.asarray(v_scale)[None, :, None]).astype(np.float32)
+        kb = torch.from_numpy(kf).to(torch.bfloat16)
+        vb = torch.from_numpy(vf).to(torch.bfloat16)
+        assert np.array_equal(kb.float().numpy(), kf) and np.array_equal(vb.float().numpy(), vf)
+        pools = (_bits(kb), _bits(vb))
+    return x, np.asarray(cached, np.int32), base, kc, vc, pools
+
+
+def pin_fp8_chunk_equals_bf16_where_exact(orc):
+    """With power-of-two scales every dequantised cached value is exact in
+    bf16: chunked prefill over the FP8 codes equals chunked prefill over a bf16
+    pool of those values (cached prefixes 0, 33, 64, 32)."""
+    ks, vs = np.float32([0.5, 1.0, 2.0, 0.25]), np.float32([2.0, 0.125, 1.0, 4.0])
+    x, cached, base, kc, vc, (kb, vb) = _fp8_chunk_case(65, ks, vs, True)
+    sc = float(np.float32(synth.SOFTMAX_SCALE))
+    args = (_bits(x.q), _bits(x.k), _bits(x.v), x.cu_seqlens.numpy())
+    o8, l8 = orc.prefill_chunk_fp8(*args, kc, vc, ks, vs, cached, kv_base=base, scale=sc, sink=x.sink.numpy())
+    ob, lb = orc.prefill_chunk(*args, kb, vb, cached, layer_type=GA, scale=sc, sink=x.sink.numpy(), kv_base=base)
+    assert np.array_equal(o8, ob) and np.array_equal(l8, lb), "FP8 chunk differs from bf16 chunk on exact values"
+
+
+def pin_fp8_chunk_brute_force_and_paged(orc):
+    """Scales that are not powers of two: FP8 chunked prefill against a dense
+    numpy brute force on sampled tokens (dequantised cached keys, then the
+    chunk's own keys up to the token, sink-seeded softmax); the same cache in a
+    shuffled paged pool gives the same results."""
+    ks, vs = np.float32([0.37, 0.011, 1.7, 0.05]), np.float32([0.021, 0.9, 0.33, 3.1])
+    x, cached, base, kc, vc, _ = _fp8_chunk_case(66, ks, vs, False)
+    sc = float(np.float32(synth.SOFTMAX_SCALE))
+    sink = x.sink.numpy()
+    cu = x.cu_seqlens.numpy()
+    args = (_bits(x.q), _bits(x.k), _bits(x.v), cu)
+    o8, l8 = orc.prefill_chunk_fp8(*args, kc, vc, ks, vs, cached, kv_base=base, scale=sc, value_scale=0.707,
+                                   sink=sink)
+    dec = _torch_decode_all()
+    q, k, v = _f64(x.q).numpy(), _f64(x.k).numpy(), _f64(x.v).numpy()
+    for b in range(len(cached)):
+        c, n = int(cached[b]), int(cu[b + 1] - cu[b])
+        for i in sorted({0, n // 2, n - 1}) if n else ():
+            t = int(cu[b]) + i
+            for h in (0, 17, 38, 63):
+                g = h // 16
+                K = np.concatenate([dec[kc[base[b]:base[b] + c, g]] * float(ks[g]), k[cu[b]:t + 1, g]])
+                V = np.concatenate([dec[vc[base[b]:base[b] + c, g]] * float(vs[g]), v[cu[b]:t + 1, g]])
+                s = np.float64(sc) * (K @ q[t, h])
+                allv = np.append(s, float(sink[h]))
+                mx = allv.max()
+                lse = mx + np.log(np.exp(allv - mx).sum())
+                o = float(np.float32(0.707)) * (np.exp(s - lse) @ V)
+                _close(o8[t, h], o, 1e-13 * (1 + np.abs(V).max()), f"fp8 chunk brute force t={t} h={h}")
+                assert abs(l8[t, h] - lse) < 1e-13 * (1 + np.abs(s).max())
+    rng = np.random.default_rng(66)
+    for P in (1, 16, 32):
+        mb = max((int(c) + P - 1) // P for c in cached) + 2
+        (kp, vp), tb = _paged_from_flat([kc, vc], base, [int(c) for c in cached], P, mb, rng)
+        op, lp = orc.prefill_chunk_fp8(*args, kp, vp, ks, vs, cached, block_table=tb, page_size=P, scale=sc,
+                                       value_scale=0.707, sink=sink)
+        assert np.array_equal(op, o8) and np.array_equal(lp, l8), f"paged FP8 chunk differs from flat (page {P})"
+
+
+def pin_fp8_paged_append_places_codes(orc):
+    """Appending to a paged FP8 pool writes, for every mapped position, the
+    codes the flat FP8 append writes for it (bulk, then single tokens); a
+    sequence that would need more than max_blocks blocks is refused whole, and
+    a token on an unmapped block is not written."""
+    P, mb = 4, 3
+    table = np.array([[5, 0, 2], [1, -1, 3]], np.int32)
+    npages = 7
+    ks, vs = np.float32([0.37, 0.011, 1.7, 0.05]), np.float32([0.021, 0.9, 0.33, 3.1])
+    lengths = [12, 6]
+    x = _make(lengths, seed=67)
+    kb, vb = _bits(x.k), _bits(x.v)
+    cu = x.cu_seqlens.numpy()
+    flat_k = np.zeros((40, 4, 192), np.uint8)
+    flat_v = np.zeros((40, 4, 128), np.uint8)
+    base = np.array([0, 20], np.int64)
+    st = orc.kv_append_fp8(kb, vb, cu, np.zeros(2, np.int32), flat_k, flat_v, base, np.array([20, 20], np.int64),
+                           ks, vs)
+    assert st == oracle.OK
+    kp = np.zeros((npages * P, 4, 192), np.uint8)
+    vp = np.zeros((npages * P, 4, 128), np.uint8)
+    pos = [0, 0]
+    for chunk in ((7, 3), (1, 1), (4, 2)):
+        sel = np.concatenate([np.arange(cu[b] + pos[b], cu[b] + pos[b] + n) for b, n in enumerate(chunk)])
+        cu_c = np.array([0, chunk[0], sum(chunk)], np.int32)
+        st = orc.kv_append_fp8_paged(kb[sel], vb[sel], cu_c, np.array(pos, np.int32), kp, vp, table, P, ks, vs)
+        want = oracle.ECAPACITY if any(4 <= p < 8 for p in range(pos[1], pos[1] + chunk[1])) else oracle.OK
+        assert st == want, f"append status {st}, expected {want}"
+        pos = [p + n for p, n in zip(pos, chunk)]
+    ek, ev = np.zeros_like(kp), np.zeros_like(vp)
+    for b, L in enumerate(lengths):
+        for j in range(L):
+            page = table[b, j // P]
+            if page >= 0:
+                ek[page * P + j % P] = flat_k[base[b] + j]
+                ev[page * P + j % P] = flat_v[base[b] + j]
+    assert np.array_equal(kp, ek) and np.array_equal(vp, ev), "paged FP8 append placement"
+    full = np.zeros((2, 1, 192), np.uint16), np.zeros((2, 1, 128), np.uint16)
+    kq = np.zeros((npages * P, 1, 192), np.uint8)
+    vq = np.zeros((npages * P, 1, 128), np.uint8)
+    st = orc.kv_append_fp8_paged(*full, np.array([0, 1, 2], np.int32), np.array([12, 11], np.int32), kq, vq,
+                                 table, P, ks[:1], vs[:1])
+    assert st == oracle.ECAPACITY and not kq.any(), "past max_blocks * P: sequence 0 refused whole"
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]
 
 

@@ -54,7 +54,20 @@ MUTANTS = {
         "        int n = 0;\n        for (int j = lo; j < p; ++j, ++n) {",
         "        if (d->layer_type == ORACLE_SWA) lo = p - (d->window - 2) > 0 ? p - (d->window - 2) : 0;\n"
         "        int n = 0;\n        for (int j = lo; j < p; ++j, ++n) {"),
-    "chunk reads its first own key from the cache": ("            if (j < c) {\n", "            if (j <= c) {\n"),
+    "chunk reads its first own key from the cache": ("            } else if (j < c) {\n", "            } else if (j <= c) {\n"),
+    "FP8 chunk reads its cached codes one row late": (
+        "/* FP8 codes of the GA pool row (contiguous or paged) */\n"
+        "                size_t row = jb->pages ? (size_t)paged_row(jb->pages, b, j) : (size_t)(jb->kv_base[b] + j);\n",
+        "/* FP8 codes of the GA pool row (contiguous or paged) */\n"
+        "                size_t row = jb->pages ? (size_t)paged_row(jb->pages, b, j) : (size_t)(jb->kv_base[b] + j + 1);\n"),
+    "FP8 chunk cached keys without the K scale": (
+        "        fp8_rows_t f8 = {k8r, v8r, jb->f8 ? (double)jb->f8->kscale[g] : 1.0,",
+        "        fp8_rows_t f8 = {k8r, v8r, 1.0,"),
+    "FP8 paged append at the flat row": ("                dst = (size_t)paged_row(pages, b, pos);\n",
+                                          "                dst = (size_t)pos;\n"),
+    "FP8 paged append room one row short": (
+        "        int64_t room = pages ? (int64_t)pages->max_blocks * pages->page_size : kv_capacity[b];\n",
+        "        int64_t room = pages ? (int64_t)pages->max_blocks * pages->page_size - 1 : kv_capacity[b];\n"),
     "chunk query position without the cached offset": ("        int p = c + (int)(t - jb->cu[b]);\n",
                                                        "        int p = (int)(t - jb->cu[b]);\n"),
     "chunk window one key too wide": (
