@@ -189,12 +189,14 @@ def paged_rows(dims, dga, ctx, max_ctx, ws, ga, page_size=16, reps=5):
     return res
 
 
-def fp8_rows(dims, dga, ctx, max_ctx, ws, reps=5):
+def fp8_rows(dims, dga, ctx, max_ctx, ws, ga, page_size=16, reps=5):
     """FP8 (OCP E4M3) GA pool, timed apart from the step: the decode step's GA
     attention (128 sequences at the contexts the timed steps left) over the
     pool quantised by the library's append with one scale per KV head (an amax
     calibration of N(0,1) data: 4.5 / 448), next to the same call over the bf16
-    pool.  The quantising append of all cached positions is timed too."""
+    pool, and over the same codes in pages of 16 (random order).  The
+    quantising append of all cached positions is timed too, and the GA chunk
+    (28672 cached + 4096 new) over an FP8 pool next to the bf16 one."""
     dev = "cuda"
     ctx_list = [int(c) for c in ctx.cpu()]
     Bd = len(ctx_list)
@@ -224,7 +226,48 @@ def fp8_rows(dims, dga, ctx, max_ctx, ws, reps=5):
                              "speedup_vs_bf16_pool": ms_b / ms_8},
            "append_fp8_bulk": {"workload": f"quantise {rows} pool rows (bf16 -> E4M3)", "ms": ms_app,
                                "GB/s": rows * (KV_TOKEN_BYTES + KV_TOKEN_BYTES // 2) / (ms_app * 1e-3) / 1e9}}
+    # the same codes in pages of 16 rows, random page order
+    table, npages = synth.paged_block_table(ctx_list, page_size, seed=1, device=dev)
+    kp = torch.empty((npages * page_size, HKV, DQK), dtype=torch.uint8, device=dev)
+    vp = torch.empty((npages * page_size, HKV, DV), dtype=torch.uint8, device=dev)
+    for b, c in enumerate(ctx_list):
+        j = torch.arange(c, device=dev)
+        dst = table[b, j // page_size].long() * page_size + j % page_size
+        src = int(dga.kv_base[b]) + j
+        kp[dst] = k8[src]
+        vp[dst] = v8[src]
     del k8, v8
+    pages = B.make_pages(table, page_size, npages)
+    p8 = lambda: B.mimo_attn_decode_fp8_paged(dims, dga.q, dga.k_new, dga.v_new, kp, vp, pages, ks, vs, ctx, Bd,
+                                              max_ctx, 0, dga.sink, out, lse, ws)
+    ms_p = _time_ms(p8, reps)
+    res["decode_ga_fp8_paged"] = {"workload": f"decode step B=128, E4M3 pool in pages of {page_size} (random order)",
+                                  "ms": ms_p, "tokens/s": Bd / (ms_p * 1e-3), "GB/s": nbytes / (ms_p * 1e-3) / 1e9,
+                                  "frac_hbm_peak": nbytes / (ms_p * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                                  "contiguous_fp8_ms": ms_8}
+    del kp, vp, table
+    torch.cuda.empty_cache()
+    # GA chunk over an FP8 pool: 28672 cached positions quantised by the append, then 4096 new tokens.
+    c, n = 28672, 4096
+    kc8 = torch.zeros((32768, HKV, DQK), dtype=torch.uint8, device=dev)
+    vc8 = torch.zeros((32768, HKV, DV), dtype=torch.uint8, device=dev)
+    base = torch.zeros(1, dtype=torch.int64, device=dev)
+    cap = torch.full((1,), 32768, dtype=torch.int64, device=dev)
+    zero = torch.zeros(1, dtype=torch.int32, device=dev)
+    B.mimo_kv_append_fp8(dims, ga.k[:c].contiguous(), ga.v[:c].contiguous(),
+                         torch.tensor([0, c], dtype=torch.int32, device=dev), zero, 1, c, kc8, vc8, base, cap, ks, vs)
+    cu1 = torch.tensor([0, n], dtype=torch.int32, device=dev)
+    ctxc = torch.full((1,), c, dtype=torch.int32, device=dev)
+    q, k, v = ga.q[c:].contiguous(), ga.k[c:].contiguous(), ga.v[c:].contiguous()
+    out_c = torch.empty((n, HQ, DV), dtype=torch.bfloat16, device=dev)
+    lse_c = torch.empty((n, HQ), dtype=torch.float32, device=dev)
+    call = lambda: B.mimo_attn_prefill_chunk_fp8(dims, q, k, v, cu1, 1, n, kc8, vc8, base, ks, vs, ctxc, ga.sink,
+                                                 out_c, lse_c)
+    ms = _time_ms(call, reps)
+    tfs = (n * c + n * (n + 1) // 2) * HQ * FLOP_PER_TRIPLE / (ms * 1e-3) / 1e12
+    res["prefill_chunk_ga_fp8"] = {"workload": "1 sequence, 28672 cached (E4M3 pool) + 4096 new", "ms": ms,
+                                   "TFLOP/s": tfs, "frac_mfma_peak": tfs / PEAK_BF16_TFLOPS}
+    del kc8, vc8, q, k, v, out_c, lse_c
     torch.cuda.empty_cache()
     return res
 
@@ -791,7 +834,7 @@ def main():
                                         "TFLOP/s": tf(prefill_pairs([256], 0) * HQ * FLOP_PER_TRIPLE, small_ms)}
     if not args.no_next_rows:
         res["next_rows"] = {**chunk_rows(dims, ga, swa), **paged_rows(dims, dga, ctx_ga, max_ctx, ws, ga),
-                            **fp8_rows(dims, dga, ctx_ga, max_ctx, ws),
+                            **fp8_rows(dims, dga, ctx_ga, max_ctx, ws, ga),
                             **backward_rows(dims, ga, swa, out_ga, lse_ga, out_swa, lse_swa),
                             **rope_rows(dims, ga), **rope_fused_rows(dims, ga, swa),
                             **swa_decode_rotated_rows(dims, ctx0)}

@@ -37,6 +37,8 @@ ENTRY_POINTS = ("mimo_attn_prefill", "mimo_attn_prefill_chunk", "mimo_attn_decod
                 "mimo_attn_decode", "mimo_attn_decode_noalloc", "mimo_attn_decode_append", "mimo_kv_append", "mimo_kv_append_paged",
                 "mimo_attn_decode_paged",
                 "mimo_attn_prefill_chunk_paged", "mimo_kv_append_fp8", "mimo_attn_decode_fp8",
+                "mimo_kv_append_fp8_paged", "mimo_attn_decode_fp8_paged", "mimo_attn_prefill_chunk_fp8",
+                "mimo_attn_prefill_chunk_fp8_paged",
                 "mimo_attn_prefill_backward_workspace_size", "mimo_attn_prefill_backward", "mimo_rope_apply",
                 "mimo_attn_prefill_rope_workspace_size", "mimo_attn_prefill_rope",
                 "mimo_attn_set_check", "mimo_attn_check_flags", "mimo_status_string",
@@ -114,6 +116,17 @@ def load(path: str) -> ctypes.CDLL:
     L.mimo_attn_decode_fp8.argtypes = [dims_p, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P,
                                        _P, _SZ, _P]
     L.mimo_attn_prefill_backward_workspace_size.restype = _SZ
+    L.mimo_kv_append_fp8_paged.restype = ctypes.c_int
+    L.mimo_kv_append_fp8_paged.argtypes = [dims_p, _P, _P, _P, _P, _I32, _I32, _P, _P, pages_p, _P, _P, _P]
+    L.mimo_attn_decode_fp8_paged.restype = ctypes.c_int
+    L.mimo_attn_decode_fp8_paged.argtypes = [dims_p, _P, _P, _P, _P, _P, pages_p, _P, _P, _P, _I32, _I32, _I32, _P,
+                                             _P, _P, _P, _SZ, _P]
+    L.mimo_attn_prefill_chunk_fp8.restype = ctypes.c_int
+    L.mimo_attn_prefill_chunk_fp8.argtypes = [dims_p, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
+                                              _P, _P]
+    L.mimo_attn_prefill_chunk_fp8_paged.restype = ctypes.c_int
+    L.mimo_attn_prefill_chunk_fp8_paged.argtypes = [dims_p, _P, _P, _P, _P, _I32, _I32, _P, _P, pages_p, _P, _P, _P,
+                                                    _P, _P, _P, _P]
     L.mimo_attn_prefill_backward_workspace_size.argtypes = [dims_p, _I32]
     L.mimo_attn_prefill_backward.restype = ctypes.c_int
     L.mimo_attn_prefill_backward.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
@@ -291,6 +304,40 @@ def mimo_attn_decode_fp8(dims: mimo_attn_dims, q, k_new, v_new, k_cache, v_cache
                                       ws_bytes, _stream(stream)))
 
 
+def mimo_kv_append_fp8_paged(dims: mimo_attn_dims, k, v, cu_newlens, ctx_lens, batch: int, total_new: int, k_cache,
+                             v_cache, pages: Optional[mimo_kv_pages], k_scale, v_scale, stream=None) -> None:
+    _check(lib().mimo_kv_append_fp8_paged(ctypes.byref(dims), _ptr(k), _ptr(v), _ptr(cu_newlens), _ptr(ctx_lens),
+                                          batch, total_new, _ptr(k_cache), _ptr(v_cache), _pages_ref(pages),
+                                          _ptr(k_scale), _ptr(v_scale), _stream(stream)))
+
+
+def mimo_attn_decode_fp8_paged(dims: mimo_attn_dims, q, k_new, v_new, k_cache, v_cache,
+                               pages: Optional[mimo_kv_pages], k_scale, v_scale, ctx_lens, batch: int, max_ctx: int,
+                               split_tokens: int, sink, out, lse, workspace, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().mimo_attn_decode_fp8_paged(ctypes.byref(dims), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                            _ptr(v_cache), _pages_ref(pages), _ptr(k_scale), _ptr(v_scale),
+                                            _ptr(ctx_lens), batch, max_ctx, split_tokens, _ptr(sink), _ptr(out),
+                                            _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def mimo_attn_prefill_chunk_fp8(dims: mimo_attn_dims, q, k, v, cu_newlens, num_seqs: int, max_newlen: int, k_cache,
+                                v_cache, kv_base, k_scale, v_scale, ctx_lens, sink, out, lse, stream=None) -> None:
+    _check(lib().mimo_attn_prefill_chunk_fp8(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_newlens),
+                                             num_seqs, max_newlen, _ptr(k_cache), _ptr(v_cache), _ptr(kv_base),
+                                             _ptr(k_scale), _ptr(v_scale), _ptr(ctx_lens), _ptr(sink), _ptr(out),
+                                             _ptr(lse), _stream(stream)))
+
+
+def mimo_attn_prefill_chunk_fp8_paged(dims: mimo_attn_dims, q, k, v, cu_newlens, num_seqs: int, max_newlen: int,
+                                      k_cache, v_cache, pages: Optional[mimo_kv_pages], k_scale, v_scale, ctx_lens,
+                                      sink, out, lse, stream=None) -> None:
+    _check(lib().mimo_attn_prefill_chunk_fp8_paged(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_newlens),
+                                                   num_seqs, max_newlen, _ptr(k_cache), _ptr(v_cache),
+                                                   _pages_ref(pages), _ptr(k_scale), _ptr(v_scale), _ptr(ctx_lens),
+                                                   _ptr(sink), _ptr(out), _ptr(lse), _stream(stream)))
+
+
 def mimo_attn_prefill_backward_workspace_size(dims: mimo_attn_dims, total_tokens: int) -> int:
     return int(lib().mimo_attn_prefill_backward_workspace_size(ctypes.byref(dims), total_tokens))
 
@@ -441,6 +488,55 @@ def decode_fp8(q, k_new, v_new, k_cache, v_cache, kv_base, k_scale, v_scale, ctx
         workspace = torch.empty(max(nbytes, 16) // 4 + 4, dtype=torch.float32, device=q.device)
     mimo_attn_decode_fp8(dims, q, k_new, v_new, k_cache, v_cache, kv_base, k_scale, v_scale, ctx_lens, B, max_ctx,
                          split_tokens, sink, out, lse, workspace, stream)
+    return out, lse
+
+
+def kv_append_fp8_paged(k, v, cu_newlens, ctx_lens, k_pool, v_pool, block_table, page_size: int, k_scale, v_scale,
+                        dims=None, total_new: Optional[int] = None, stream=None):
+    dims = dims or make_dims()
+    if total_new is None:
+        total_new = k.shape[0]
+    pages = make_pages(block_table, page_size, k_pool.shape[0] // page_size)
+    mimo_kv_append_fp8_paged(dims, k, v, cu_newlens, ctx_lens, cu_newlens.numel() - 1, total_new, k_pool, v_pool,
+                             pages, k_scale, v_scale, stream)
+
+
+def decode_fp8_paged(q, k_new, v_new, k_pool, v_pool, block_table, page_size: int, k_scale, v_scale, ctx_lens,
+                     max_ctx: int, sink=None, split_tokens: int = 0, dims=None, out=None, lse=None, workspace=None,
+                     stream=None):
+    dims = dims or make_dims()
+    B = q.shape[0]
+    if out is None:
+        out = torch.empty((B, dims.num_q_heads, dims.head_dim_v), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, dims.num_q_heads), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = mimo_attn_decode_workspace_size(dims, MIMO_LAYER_GA, B, max_ctx, split_tokens)
+        workspace = torch.empty(max(nbytes, 16) // 4 + 4, dtype=torch.float32, device=q.device)
+    pages = make_pages(block_table, page_size, k_pool.shape[0] // page_size)
+    mimo_attn_decode_fp8_paged(dims, q, k_new, v_new, k_pool, v_pool, pages, k_scale, v_scale, ctx_lens, B, max_ctx,
+                               split_tokens, sink, out, lse, workspace, stream)
+    return out, lse
+
+
+def prefill_chunk_fp8(q, k, v, cu_newlens, max_newlen: int, k_cache, v_cache, k_scale, v_scale, ctx_lens,
+                      kv_base=None, block_table=None, page_size: int = 0, sink=None, dims=None, out=None, lse=None,
+                      stream=None):
+    """GA chunked prefill over an FP8 pool: contiguous (kv_base) or paged (block_table, page_size)."""
+    dims = dims or make_dims()
+    T = q.shape[0]
+    if out is None:
+        out = torch.empty((T, dims.num_q_heads, dims.head_dim_v), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, dims.num_q_heads), dtype=torch.float32, device=q.device)
+    n = cu_newlens.numel() - 1
+    if block_table is not None:
+        pages = make_pages(block_table, page_size, k_cache.shape[0] // page_size)
+        mimo_attn_prefill_chunk_fp8_paged(dims, q, k, v, cu_newlens, n, max_newlen, k_cache, v_cache, pages, k_scale,
+                                          v_scale, ctx_lens, sink, out, lse, stream)
+    else:
+        mimo_attn_prefill_chunk_fp8(dims, q, k, v, cu_newlens, n, max_newlen, k_cache, v_cache, kv_base, k_scale,
+                                    v_scale, ctx_lens, sink, out, lse, stream)
     return out, lse
 
 

@@ -168,12 +168,36 @@ int mimo_attn_prefill(const mimo_attn_dims* dims, int layer_type, const uint16_t
 
 namespace {
 
+// FP8 GA pool of a chunk, decode or append call: codes and per-KV-head scales.
+struct Fp8Pool {
+    const uint8_t* k = nullptr;
+    const uint8_t* v = nullptr;
+    const float* k_scale = nullptr;
+    const float* v_scale = nullptr;
+};
+
+int check_fp8(const Fp8Pool& f) {
+    if (!f.k || !f.v) return fail(MIMO_ERR_INVALID_ARG, "k_cache and v_cache must be non-NULL");
+    if (!aligned16(f.k) || !aligned16(f.v))
+        return fail(MIMO_ERR_INVALID_ARG, "k_cache and v_cache must be 16-byte aligned");
+    if (!f.k_scale || !f.v_scale) return fail(MIMO_ERR_INVALID_ARG, "k_scale and v_scale must be non-NULL");
+    if ((reinterpret_cast<uintptr_t>(f.k_scale) | reinterpret_cast<uintptr_t>(f.v_scale)) & 3u)
+        return fail(MIMO_ERR_INVALID_ARG, "k_scale and v_scale must be 4-byte aligned");
+    return MIMO_OK;
+}
+
 int prefill_chunk_impl(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, const uint16_t* k,
                        const uint16_t* v, const int32_t* cu_newlens, int32_t num_seqs, int32_t max_newlen,
                        const uint16_t* k_cache, const uint16_t* v_cache, const int64_t* kv_base,
                        const mimo_kv_pages* pages, const int32_t* ctx_lens, const float* sink, uint16_t* out,
-                       float* lse, hipStream_t stream) {
+                       float* lse, hipStream_t stream, const Fp8Pool* fp8 = nullptr) {
     if (int st = check_dims(dims, layer_type, 2)) return st;
+    if (fp8) {
+        if (int st = check_fp8(*fp8)) return st;
+        // The code pools stand in for the bf16 caches in the checks below.
+        k_cache = reinterpret_cast<const uint16_t*>(fp8->k);
+        v_cache = reinterpret_cast<const uint16_t*>(fp8->v);
+    }
     if (!q || !k || !v || !cu_newlens || !out || !k_cache || !v_cache || !ctx_lens)
         return fail(MIMO_ERR_INVALID_ARG, "q, k, v, cu_newlens, out, k_cache, v_cache and ctx_lens must be non-NULL");
     mimo::PageTable pt;
@@ -197,6 +221,13 @@ int prefill_chunk_impl(const mimo_attn_dims* dims, int layer_type, const uint16_
     a.kv_base = kv_base;
     a.ctx_lens = ctx_lens;
     a.pages = pt;
+    if (fp8) {
+        a.k_cache = a.v_cache = nullptr;
+        a.k_cache8 = fp8->k;
+        a.v_cache8 = fp8->v;
+        a.k_scale = fp8->k_scale;
+        a.v_scale = fp8->v_scale;
+    }
     mimo::CheckArgs c;
     c.cu = cu_newlens;
     c.n_seqs = num_seqs;
@@ -208,6 +239,11 @@ int prefill_chunk_impl(const mimo_attn_dims* dims, int layer_type, const uint16_
     c.pages = pt;
     c.sink = sink;
     c.hq = dims->num_q_heads;
+    if (fp8) {
+        c.scales = fp8->k_scale;
+        c.scales_v = fp8->v_scale;
+        c.n_scales = dims->num_kv_heads;
+    }
     if (int st = precheck(c, stream, "chunked prefill")) return st;
     return hip_status(mimo::launch_prefill_chunk(a, stream), "chunked prefill launch");
 }
@@ -235,6 +271,28 @@ int mimo_attn_prefill_chunk_paged(const mimo_attn_dims* dims, const uint16_t* q,
                               nullptr, pages, ctx_lens, sink, out, lse, stream);
 }
 
+int mimo_attn_prefill_chunk_fp8(const mimo_attn_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                const int32_t* cu_newlens, int32_t num_seqs, int32_t max_newlen, const uint8_t* k_cache,
+                                const uint8_t* v_cache, const int64_t* kv_base, const float* k_scale,
+                                const float* v_scale, const int32_t* ctx_lens, const float* sink, uint16_t* out,
+                                float* lse, hipStream_t stream) {
+    const Fp8Pool f{k_cache, v_cache, k_scale, v_scale};
+    return prefill_chunk_impl(dims, MIMO_LAYER_GA, q, k, v, cu_newlens, num_seqs, max_newlen, nullptr, nullptr,
+                              kv_base, nullptr, ctx_lens, sink, out, lse, stream, &f);
+}
+
+int mimo_attn_prefill_chunk_fp8_paged(const mimo_attn_dims* dims, const uint16_t* q, const uint16_t* k,
+                                      const uint16_t* v, const int32_t* cu_newlens, int32_t num_seqs,
+                                      int32_t max_newlen, const uint8_t* k_cache, const uint8_t* v_cache,
+                                      const mimo_kv_pages* pages, const float* k_scale, const float* v_scale,
+                                      const int32_t* ctx_lens, const float* sink, uint16_t* out, float* lse,
+                                      hipStream_t stream) {
+    if (!pages) return fail(MIMO_ERR_INVALID_ARG, "pages is NULL");
+    const Fp8Pool f{k_cache, v_cache, k_scale, v_scale};
+    return prefill_chunk_impl(dims, MIMO_LAYER_GA, q, k, v, cu_newlens, num_seqs, max_newlen, nullptr, nullptr,
+                              nullptr, pages, ctx_lens, sink, out, lse, stream, &f);
+}
+
 size_t mimo_attn_decode_workspace_size(const mimo_attn_dims* dims, int layer_type, int32_t batch, int32_t max_ctx,
                                        int32_t split_tokens) {
     if (check_dims(dims, layer_type, 2) != MIMO_OK || batch < 1 || max_ctx < 0 || max_ctx == INT32_MAX) return 0;
@@ -246,24 +304,6 @@ size_t mimo_attn_decode_workspace_size(const mimo_attn_dims* dims, int layer_typ
 }  // extern "C"
 
 namespace {
-
-// FP8 GA pool of a decode or append call: codes and per-KV-head scales.
-struct Fp8Pool {
-    const uint8_t* k = nullptr;
-    const uint8_t* v = nullptr;
-    const float* k_scale = nullptr;
-    const float* v_scale = nullptr;
-};
-
-int check_fp8(const Fp8Pool& f) {
-    if (!f.k || !f.v) return fail(MIMO_ERR_INVALID_ARG, "k_cache and v_cache must be non-NULL");
-    if (!aligned16(f.k) || !aligned16(f.v))
-        return fail(MIMO_ERR_INVALID_ARG, "k_cache and v_cache must be 16-byte aligned");
-    if (!f.k_scale || !f.v_scale) return fail(MIMO_ERR_INVALID_ARG, "k_scale and v_scale must be non-NULL");
-    if ((reinterpret_cast<uintptr_t>(f.k_scale) | reinterpret_cast<uintptr_t>(f.v_scale)) & 3u)
-        return fail(MIMO_ERR_INVALID_ARG, "k_scale and v_scale must be 4-byte aligned");
-    return MIMO_OK;
-}
 
 int decode_impl(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, const uint16_t* k_new,
                 const uint16_t* v_new, const uint16_t* k_cache, const uint16_t* v_cache, const int64_t* kv_base,
@@ -497,6 +537,28 @@ int mimo_kv_append_fp8(const mimo_attn_dims* dims, const uint16_t* k, const uint
     const Fp8Pool f{k_cache, v_cache, k_scale, v_scale};
     return kv_append_impl(dims, MIMO_LAYER_GA, k, v, cu_newlens, ctx_lens, batch, total_new, nullptr, nullptr,
                           kv_base, kv_capacity, nullptr, stream, &f);
+}
+
+int mimo_attn_decode_fp8_paged(const mimo_attn_dims* dims, const uint16_t* q, const uint16_t* k_new,
+                               const uint16_t* v_new, const uint8_t* k_cache, const uint8_t* v_cache,
+                               const mimo_kv_pages* pages, const float* k_scale, const float* v_scale,
+                               const int32_t* ctx_lens, int32_t batch, int32_t max_ctx, int32_t split_tokens,
+                               const float* sink, uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+    if (!pages) return fail(MIMO_ERR_INVALID_ARG, "pages is NULL");
+    const Fp8Pool f{k_cache, v_cache, k_scale, v_scale};
+    return decode_impl(dims, MIMO_LAYER_GA, q, k_new, v_new, nullptr, nullptr, nullptr, pages, ctx_lens, batch,
+                       max_ctx, split_tokens, sink, out, lse, workspace, workspace_bytes, stream, &f);
+}
+
+int mimo_kv_append_fp8_paged(const mimo_attn_dims* dims, const uint16_t* k, const uint16_t* v,
+                             const int32_t* cu_newlens, const int32_t* ctx_lens, int32_t batch, int32_t total_new,
+                             uint8_t* k_cache, uint8_t* v_cache, const mimo_kv_pages* pages, const float* k_scale,
+                             const float* v_scale, hipStream_t stream) {
+    if (!pages) return fail(MIMO_ERR_INVALID_ARG, "pages is NULL");
+    const Fp8Pool f{k_cache, v_cache, k_scale, v_scale};
+    return kv_append_impl(dims, MIMO_LAYER_GA, k, v, cu_newlens, ctx_lens, batch, total_new, nullptr, nullptr,
+                          nullptr, nullptr, pages, stream, &f);
 }
 
 size_t mimo_attn_prefill_backward_workspace_size(const mimo_attn_dims* dims, int32_t total_tokens) {

@@ -99,8 +99,8 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     }
 }
 
-// FP8 GA pool: one thread turns 8 bf16 elements (16 bytes) of a new token into
-// 8 E4M3 codes (8 bytes).  A token is Hkv*24 such units of K then Hkv*16 of V;
+// FP8 GA pool (contiguous, or paged as above): one thread turns 8 bf16
+// elements (16 bytes) of a new token into 8 E4M3 codes (8 bytes).  A token is Hkv*24 such units of K then Hkv*16 of V;
 // unit c of K belongs to KV head c / 24, of V to head c / 16.  Each element is
 // divided by its head's scale in fp32 (IEEE division), clamped to +-448 (the
 // conversion does not saturate by itself) and rounded to nearest-even by the
@@ -109,7 +109,8 @@ __global__ __launch_bounds__(256) void kv_append_fp8_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const int32_t* __restrict__ cu_newlens,
     const int32_t* __restrict__ ctx_lens, int batch, int total_new, uint8_t* __restrict__ k_cache,
     uint8_t* __restrict__ v_cache, const int64_t* __restrict__ kv_base, const int64_t* __restrict__ kv_capacity,
-    const float* __restrict__ k_scale, const float* __restrict__ v_scale, int hkv) {
+    const float* __restrict__ k_scale, const float* __restrict__ v_scale, int hkv,
+    const int32_t* __restrict__ block_table, int max_blocks, int page_shift, long long num_pages) {
     const int kunits = hkv * (kDqk / 8), per_tok = hkv * ((kDqk + kDv) / 8);
     const TokSeq ts = locate(cu_newlens, batch, per_tok);
     const int64_t tok = ts.tok;
@@ -118,8 +119,17 @@ __global__ __launch_bounds__(256) void kv_append_fp8_kernel(
     const int b = ts.b;
     const int n = cu_newlens[b + 1] - cu_newlens[b];
     const int64_t ctx = ctx_lens[b];
-    if (ctx + n > kv_capacity[b]) return;  // the whole sequence is refused
-    const int64_t row = kv_base[b] + ctx + (tok - cu_newlens[b]);
+    const int64_t pos = ctx + (tok - cu_newlens[b]);
+    int64_t row;
+    if (block_table) {
+        if (ctx + n > ((int64_t)max_blocks << page_shift)) return;  // the whole sequence is refused
+        const int64_t page = block_table[(int64_t)b * max_blocks + (pos >> page_shift)];
+        if (page < 0 || page >= num_pages) return;  // unmapped block: not written
+        row = (page << page_shift) | (pos & ((1 << page_shift) - 1));
+    } else {
+        if (ctx + n > kv_capacity[b]) return;  // the whole sequence is refused
+        row = kv_base[b] + pos;
+    }
     const bool is_k = c < kunits;
     const int u = is_k ? c : c - kunits;
     const float scale = is_k ? k_scale[u / (kDqk / 8)] : v_scale[u / (kDv / 8)];
@@ -149,7 +159,8 @@ hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream) {
         const int64_t threads = (int64_t)a.total_new * a.hkv * ((kDqk + kDv) / 8);
         hipLaunchKernelGGL(kv_append_fp8_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a.k,
                            a.v, a.cu_newlens, a.ctx_lens, a.batch, a.total_new, a.k_cache8, a.v_cache8, a.kv_base,
-                           a.kv_capacity, a.k_scale, a.v_scale, a.hkv);
+                           a.kv_capacity, a.k_scale, a.v_scale, a.hkv, a.pages.table, a.pages.max_blocks,
+                           a.pages.shift, a.pages.num_pages);
         return hipGetLastError();
     }
     const int64_t threads = (int64_t)a.total_new * a.hkv * ((kDqk + kDv) / 8);

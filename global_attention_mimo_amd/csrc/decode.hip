@@ -535,6 +535,54 @@ __device__ __forceinline__ void for_each_piece(const ChunkPlan& pl, const int32_
     }
 }
 
+// Pool keys [k0, kend) of one sequence of a paged pool (tb: its block-table
+// row, page_shift = log2 P), in spans of at most kMaxSplitPages pages cut at
+// 32-key tile boundaries.  Each span preloads its page numbers, two per lane
+// (-1 past the table's end), and calls span(npool, last, pool_tile):
+// pool_tile(i) describes the span's i-th 32-key tile through a descriptor per
+// 16-key half (each inside one page), with no records for keys past the span
+// or on an unmapped block.  Row sizes are in bytes (the bf16 and the FP8 pool
+// share this walk).  A span is visited even when it has no pool tile.
+template <class Span>
+__device__ __forceinline__ void for_each_page_span(const int32_t* __restrict__ tb, int max_blocks, int page_shift,
+                                                   long long num_pages, const void* pool_k, const void* pool_v,
+                                                   int rowk_bytes, int rowv_bytes, int k0, int kend, int lane,
+                                                   const Span& span) {
+    const int pmask = (1 << page_shift) - 1;
+    int a = k0;
+    bool more = true;
+    while (more) {
+        const int first = a >> page_shift;
+        const long long lim = ((long long)(first + kMaxSplitPages) << page_shift) / kTile * kTile;
+        const int span_end = (int)(lim < kend ? lim : kend);
+        more = span_end < kend;
+        const int npool = (span_end - a + kTile - 1) / kTile;
+        const int pg_lo = first + lane < max_blocks ? tb[first + lane] : -1;
+        const int pg_hi = first + 64 + lane < max_blocks ? tb[first + 64 + lane] : -1;
+        // Descriptor of the n valid keys from position j on (inside one page);
+        // no records when n <= 0 or the block is unmapped.
+        auto half = [&](const void* pool, int row_bytes, int j, int n) -> rsrc_t {
+            const int blk = (j >> page_shift) - first;  // 0..127 whenever n > 0
+            const int pa = __builtin_amdgcn_readlane(pg_lo, blk & 63);
+            const int pb = __builtin_amdgcn_readlane(pg_hi, blk & 63);
+            const int pg = (blk & 64) ? pb : pa;
+            const bool ok = n > 0 && pg >= 0 && pg < num_pages;
+            const size_t row = ((size_t)(ok ? pg : 0) << page_shift) + (size_t)(j & pmask);
+            return make_rsrc(static_cast<const char*>(pool) + row * row_bytes, ok ? (uint32_t)n * (uint32_t)row_bytes : 0u);
+        };
+        const int a0 = a;
+        auto pool_tile = [&](int i) -> PagedTileSrc {
+            const int j0 = a0 + i * kTile;
+            const int n = min(span_end - j0, kTile);
+            return PagedTileSrc{{half(pool_k, rowk_bytes, j0, min(n, 16)), half(pool_k, rowk_bytes, j0 + 16, n - 16)},
+                                {half(pool_v, rowv_bytes, j0, min(n, 16)), half(pool_v, rowv_bytes, j0 + 16, n - 16)},
+                                n};
+        };
+        span(npool, !more, pool_tile);
+        a = span_end;
+    }
+}
+
 // PAGED: pool rows come through block_table (page_shift = log2 P); otherwise
 // sequence b's rows start at kv_base[b].
 template <bool PAGED>
@@ -582,49 +630,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
         WaveAcc acc;
         acc_init(acc);
         if constexpr (PAGED) {
-            // Spans of at most kMaxSplitPages pages, cut at 32-key tile
-            // boundaries; each preloads its page numbers, two per lane (-1 past
-            // the table's end), and runs its tiles.
-            const int32_t* tb = block_table + (size_t)b * max_blocks;
-            const int pmask = (1 << page_shift) - 1;
-            int a = k0;
-            bool more = true;
-            while (more) {
-                const int first = a >> page_shift;
-                const long long lim = ((long long)(first + kMaxSplitPages) << page_shift) / kTile * kTile;
-                const int span_end = (int)(lim < kend ? lim : kend);
-                more = span_end < kend;
-                const int npool = (span_end - a + kTile - 1) / kTile;
-                const int ntiles = npool + (!more && has_new ? 1 : 0);
-                const int pg_lo = first + lane < max_blocks ? tb[first + lane] : -1;
-                const int pg_hi = first + 64 + lane < max_blocks ? tb[first + 64 + lane] : -1;
-                // Descriptor of the n valid keys from position j on (inside one
-                // page); no records when n <= 0 or the block is unmapped.
-                auto half = [&](const uint16_t* pool, int row_elems, int j, int n) -> rsrc_t {
-                    const int blk = (j >> page_shift) - first;  // 0..127 whenever n > 0
-                    const int pa = __builtin_amdgcn_readlane(pg_lo, blk & 63);
-                    const int pb = __builtin_amdgcn_readlane(pg_hi, blk & 63);
-                    const int pg = (blk & 64) ? pb : pa;
-                    const bool ok = n > 0 && pg >= 0 && pg < num_pages;
-                    const size_t row = ((size_t)(ok ? pg : 0) << page_shift) + (size_t)(j & pmask);
-                    return make_rsrc(pool + row * row_elems, ok ? (uint32_t)n * (uint32_t)(row_elems * 2) : 0u);
-                };
-                const int a0 = a;
+            for_each_page_span(block_table + (size_t)b * max_blocks, max_blocks, page_shift, num_pages, pool_k, pool_v,
+                               rowk, rowv, k0, kend, lane, [&](int npool, bool last, const auto& pool_tile) {
+                const int ntiles = npool + (last && has_new ? 1 : 0);
                 auto get = [&](int i) -> PagedTileSrc {
-                    if (i < npool) {
-                        const int j0 = a0 + i * kTile;
-                        const int n = min(span_end - j0, kTile);
-                        return PagedTileSrc{
-                            {half(pool_k, hkv * kDqk, j0, min(n, 16)), half(pool_k, hkv * kDqk, j0 + 16, n - 16)},
-                            {half(pool_v, hkv * kDv, j0, min(n, 16)), half(pool_v, hkv * kDv, j0 + 16, n - 16)},
-                            n};
-                    }
+                    if (i < npool) return pool_tile(i);
                     if (i < ntiles) return PagedTileSrc{{nk, none}, {nv, none}, 1};
                     return PagedTileSrc{{none, none}, {none, none}, 0};
                 };
                 run_tiles<kGaDepth>(acc, qf, lds + wave * kVTileBytes, ntiles, get, lo, rowv, c_log2, lane);
-                a = span_end;
-            }
+            });
         } else {
             const size_t base = (size_t)kv_base[b];
             const rsrc_t pk = make_rsrc(pool_k + base * hkv * kDqk, (uint32_t)p * rowk);
@@ -660,21 +675,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 // on the order of its terms).  The new token (bf16 k_new, v_new) is folded in
 // after the cached tiles in fp32, so its weight is not rounded to bf16.
 
-// 4 codes (one dword) -> 4 bf16 (two dwords), exact: v_cvt_scalef32_pk_bf16_fp8
-// with scale 1 turns the two codes of a 16-bit word straight into a bf16 pair.
-// (The route through v_cvt_pk_f32_fp8 and a byte permute was miscompiled here:
-// the compiler read both floats of the pair from the first register.)
-__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
-    return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false)),
-                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true))};
-}
-
-// 8 codes (two dwords) -> one bf16x8 operand.
-__device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
-    const u32x2 a = fp8x4_to_bf16x4(w0), c = fp8x4_to_bf16x4(w1);
-    return u32x4{a[0], a[1], c[0], c[1]};
-}
-
 // Lane-constant byte offsets inside an FP8 tile.  K: lane l reads keys l%16
 // (and +16), 16 codes at d = 64u + 16(l/16) for u = 0..2.  V: load i reads key
 // 8i + l/8, 16 codes at columns 16(l%8) .. +15.
@@ -701,6 +701,21 @@ __device__ __forceinline__ void issue_k8(const TileSrc& t, const Fp8LaneOffsets&
 __device__ __forceinline__ void issue_v8(const TileSrc& t, const Fp8LaneOffsets& lo, int rowv8, u32x4 (&v)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(t.v, lo.v, t.voff + 8 * i * rowv8, 0);
+}
+
+// Paged halves: K rows l%16 of each half; V load i takes key 8i + l/8, i.e.
+// half i/2 at row 8(i%2) + l/8.
+__device__ __forceinline__ void issue_k8(const PagedTileSrc& t, const Fp8LaneOffsets& lo, u32x4 (&k)[6]) {
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+        k[u] = __builtin_amdgcn_raw_buffer_load_b128(t.k[0], lo.k0 + 64 * u, 0, 0);
+        k[3 + u] = __builtin_amdgcn_raw_buffer_load_b128(t.k[1], lo.k0 + 64 * u, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void issue_v8(const PagedTileSrc& t, const Fp8LaneOffsets& lo, int rowv8, u32x4 (&v)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(t.v[i / 2], lo.v, 8 * (i % 2) * rowv8, 0);
 }
 
 // V codes to the wave's bf16 LDS tile, in the layout stage_v writes: load i
@@ -751,14 +766,14 @@ __device__ __forceinline__ void run_tiles_fp8(WaveAcc& acc, const bf16x8 (&qf)[k
     u32x4 kr[D + 1][6], vr[D + 1][4];
 #pragma unroll
     for (int j = 0; j < D; ++j) {
-        const TileSrc t = get(j);
+        const auto t = get(j);
         issue_k8(t, lo, kr[j]);
         issue_v8(t, lo, rowv8, vr[j]);
     }
     for (int i0 = 0; i0 < ntiles; i0 += D + 1) {
 #pragma unroll
         for (int j = 0; j <= D; ++j) {
-            const TileSrc t = get(i0 + j + D);
+            const auto t = get(i0 + j + D);
             issue_k8(t, lo, kr[(j + D) % (D + 1)]);
             issue_v8(t, lo, rowv8, vr[(j + D) % (D + 1)]);
             stage_v8(vr[j], vbuf, lane);
@@ -806,12 +821,15 @@ __device__ __forceinline__ void fold_new_token(WaveAcc& acc, const bf16x8 (&qf)[
     acc.m = m_new;
 }
 
+// PAGED: code rows come through block_table, as for the bf16 pool.
+template <bool PAGED>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void ga_split_fp8_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const uint8_t* __restrict__ pool_k, const uint8_t* __restrict__ pool_v, const int64_t* __restrict__ kv_base,
     const int32_t* __restrict__ ctx_lens, const float* __restrict__ k_scale, const float* __restrict__ v_scale,
     int batch, int max_ctx, int min_units, int max_chunks, int hq, int hkv, float c_log2,
-    long long* __restrict__ header, float* __restrict__ ws_ml, float* __restrict__ ws_o) {
+    long long* __restrict__ header, float* __restrict__ ws_ml, float* __restrict__ ws_o,
+    const int32_t* __restrict__ block_table, int max_blocks, int page_shift, long long num_pages) {
     __shared__ __attribute__((aligned(1024))) char lds[kBlockLdsBytes];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -831,20 +849,32 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
         const int kend = min(min(u1, npool_units) * kTile, p);  // pool keys [k0, kend)
         bf16x8 qf[kDqk / 32];
         load_q_perm(qf, q, b, g, hq, lane);
-        const size_t base = (size_t)kv_base[b];
-        const rsrc_t pk = make_rsrc(pool_k + base * rowk8, (uint32_t)p * rowk8);
-        const rsrc_t pv = make_rsrc(pool_v + base * rowv8, (uint32_t)p * rowv8);
-        const int npool = (kend - k0 + kTile - 1) / kTile;
-        auto get = [&](int i) -> TileSrc {
-            if (i < npool) {
-                const int j0 = k0 + i * kTile;
-                return TileSrc{pk, pv, j0 * rowk8, j0 * rowv8, min(kend - j0, kTile)};
-            }
-            return TileSrc{none, none, 0, 0, 0};
-        };
         WaveAcc acc;
         acc_init(acc);
-        run_tiles_fp8<kFp8Depth>(acc, qf, lds + wave * kVTileBytes, npool, get, lo, rowv8, c_log2 * ks, lane);
+        if constexpr (PAGED) {
+            for_each_page_span(block_table + (size_t)b * max_blocks, max_blocks, page_shift, num_pages, pool_k, pool_v,
+                               rowk8, rowv8, k0, kend, lane, [&](int npool, bool, const auto& pool_tile) {
+                auto get = [&](int i) -> PagedTileSrc {
+                    if (i < npool) return pool_tile(i);
+                    return PagedTileSrc{{none, none}, {none, none}, 0};
+                };
+                run_tiles_fp8<kFp8Depth>(acc, qf, lds + wave * kVTileBytes, npool, get, lo, rowv8, c_log2 * ks,
+                                         lane);
+            });
+        } else {
+            const size_t base = (size_t)kv_base[b];
+            const rsrc_t pk = make_rsrc(pool_k + base * rowk8, (uint32_t)p * rowk8);
+            const rsrc_t pv = make_rsrc(pool_v + base * rowv8, (uint32_t)p * rowv8);
+            const int npool = (kend - k0 + kTile - 1) / kTile;
+            auto get = [&](int i) -> TileSrc {
+                if (i < npool) {
+                    const int j0 = k0 + i * kTile;
+                    return TileSrc{pk, pv, j0 * rowk8, j0 * rowv8, min(kend - j0, kTile)};
+                }
+                return TileSrc{none, none, 0, 0, 0};
+            };
+            run_tiles_fp8<kFp8Depth>(acc, qf, lds + wave * kVTileBytes, npool, get, lo, rowv8, c_log2 * ks, lane);
+        }
         acc.l += __shfl_xor(acc.l, 16);
         acc.l += __shfl_xor(acc.l, 32);
 #pragma unroll
@@ -945,9 +975,11 @@ hipError_t launch_decode_ga(const DecodeArgs& a, hipStream_t stream) {
     float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + ga_header_bytes(a.batch));
     float* ws_o = ws_ml + (size_t)(grid + a.batch) * a.hq * 2;
     if (a.k_cache8) {
-        hipLaunchKernelGGL(ga_split_fp8_kernel, dim3(grid, 1, (a.hkv + 3) / 4), dim3(256), 0, stream, a.q, a.k_new,
-                           a.v_new, a.k_cache8, a.v_cache8, a.kv_base, a.ctx_lens, a.k_scale, a.v_scale, a.batch,
-                           a.max_ctx, a.min_units, grid, a.hq, a.hkv, a.softmax_scale * kLog2e, header, ws_ml, ws_o);
+        hipLaunchKernelGGL(a.pages.table ? ga_split_fp8_kernel<true> : ga_split_fp8_kernel<false>,
+                           dim3(grid, 1, (a.hkv + 3) / 4), dim3(256), 0, stream, a.q, a.k_new, a.v_new, a.k_cache8,
+                           a.v_cache8, a.kv_base, a.ctx_lens, a.k_scale, a.v_scale, a.batch, a.max_ctx, a.min_units,
+                           grid, a.hq, a.hkv, a.softmax_scale * kLog2e, header, ws_ml, ws_o, a.pages.table,
+                           a.pages.max_blocks, a.pages.shift, a.pages.num_pages);
     } else {
         hipLaunchKernelGGL(a.pages.table ? ga_split_kernel<true> : ga_split_kernel<false>, dim3(grid, 1, (a.hkv + 3) / 4),
                            dim3(256), 0, stream, a.q, a.k_new, a.v_new, a.k_cache, a.v_cache, a.kv_base, a.ctx_lens,

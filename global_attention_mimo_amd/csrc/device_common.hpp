@@ -144,6 +144,23 @@ __device__ __forceinline__ void rope_frags_rd(bf16x8* frag, const float* tab, in
 // Orders this wave's earlier LDS writes before its later LDS reads (the
 // compiler must not move accesses across it; the hardware keeps a wave's LDS
 // operations in order).
+// OCP E4M3 codes -> bf16, exact (an E4M3 value has at most 4 significant bits
+// and an exponent inside bf16's range).  4 codes (one dword) -> 4 bf16 (two
+// dwords): v_cvt_scalef32_pk_bf16_fp8 with scale 1 turns the two codes of a
+// 16-bit word straight into a bf16 pair.  (The route through v_cvt_pk_f32_fp8
+// and a byte permute was miscompiled here: the compiler read both floats of
+// the pair from the first register.)
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
+    return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true))};
+}
+
+// 8 codes (two dwords) -> 8 bf16 (one 16-byte operand).
+__device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+    const u32x2 a = fp8x4_to_bf16x4(w0), c = fp8x4_to_bf16x4(w1);
+    return u32x4{a[0], a[1], c[0], c[1]};
+}
+
 __device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
 
 // Raw buffer resource (gfx9-family descriptor) over `bytes` bytes at `base`:

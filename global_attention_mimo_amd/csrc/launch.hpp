@@ -37,6 +37,12 @@ struct PrefillArgs {
     const int64_t* kv_base = nullptr;
     const int32_t* ctx_lens = nullptr;
     PageTable pages;
+    // Chunked prefill over an FP8 GA pool (E4M3 codes, per-KV-head scales);
+    // k_cache/v_cache unused then.
+    const uint8_t* k_cache8 = nullptr;
+    const uint8_t* v_cache8 = nullptr;
+    const float* k_scale = nullptr;
+    const float* v_scale = nullptr;
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_chunk(const PrefillArgs& a, hipStream_t stream);

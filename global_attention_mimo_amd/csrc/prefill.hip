@@ -93,7 +93,14 @@ constexpr float kRescaleThreshold = MIMO_RESCALE_THRESHOLD;
 // staged from the cache below that length and from the chunk above it.
 // PAGED (GA chunks only): the pool is paged, position j in row j mod P of page
 // block_table[b][j / P] (P = 2^page_shift); each staged row looks its page up.
-template <int WV, int NB, int NK, bool SWA, int WAVES_PER_EU, bool CHUNK, bool PAGED = false>
+// FP8 (GA chunks only): the pool holds OCP E4M3 codes (k_cache8, v_cache8)
+// with one scale per KV head.  A cached row is loaded as 8 codes per 16-byte
+// slot and widened exactly to bf16 when the tile is written to LDS, so the
+// MFMAs see the codes' values; the K scale joins the score multiplier and the
+// V scale the probabilities of the cached keys (for a tile wholly from the
+// cache: exp2 of the shifted exponent, its row sum divided back; for the tile
+// that straddles ctx_lens[b]: key by key).
+template <int WV, int NB, int NK, bool SWA, int WAVES_PER_EU, bool CHUNK, bool PAGED = false, bool FP8 = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WV, 64 * WV),
                           amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
 void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -103,8 +110,11 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     int max_seqlen, const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
                     const int64_t* __restrict__ kv_base, const int32_t* __restrict__ ctx_lens, int ring,
                     const int32_t* __restrict__ block_table, int max_blocks, int page_shift, long long num_pages,
-                    const float* __restrict__ rope_tab, int rope_half) {
+                    const float* __restrict__ rope_tab, int rope_half, const uint8_t* __restrict__ k_cache8,
+                    const uint8_t* __restrict__ v_cache8, const float* __restrict__ k_scale,
+                    const float* __restrict__ v_scale) {
     static_assert(!PAGED || (CHUNK && !SWA), "only GA chunks read a paged pool");
+    static_assert(!FP8 || (CHUNK && !SWA), "only GA chunks read an FP8 pool");
     using Cfg = PrefillCfg<WV, NB, NK>;
     constexpr int QT = Cfg::kTokens;
     // Two K/V buffers: tile t is computed from buffer t%2 while tile t+1 is staged into the other.
@@ -213,13 +223,28 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     // Cache sources (CHUNK only): same per-thread columns, rows by position.
     const uint16_t* kcp[Cfg::kKPer];
     const uint16_t* vcp[Cfg::kVPer];
+    int kcol8[Cfg::kKPer], vcol8[Cfg::kVPer];  // FP8: byte offsets of the slots inside a pool row
     int64_t cache_row0 = 0;
     if constexpr (CHUNK && !PAGED) cache_row0 = SWA ? (int64_t)b * ring : kv_base[b];
     if constexpr (CHUNK) {
 #pragma unroll
-        for (int i = 0; i < Cfg::kKPer; ++i) kcp[i] = k_cache + (kp[i] - k) - (size_t)s0 * kstride;
+        for (int i = 0; i < Cfg::kKPer; ++i) {
+            if constexpr (FP8) kcol8[i] = (int)((kp[i] - k) - (size_t)s0 * kstride);  // one byte per element
+            else kcp[i] = k_cache + (kp[i] - k) - (size_t)s0 * kstride;
+        }
 #pragma unroll
-        for (int i = 0; i < Cfg::kVPer; ++i) vcp[i] = v_cache + (vp[i] - v) - (size_t)s0 * vstride;
+        for (int i = 0; i < Cfg::kVPer; ++i) {
+            if constexpr (FP8) vcol8[i] = (int)((vp[i] - v) - (size_t)s0 * vstride);
+            else vcp[i] = v_cache + (vp[i] - v) - (size_t)s0 * vstride;
+        }
+    }
+    // FP8: the K scale, and the V scale as a log2 shift and a reciprocal (wave-uniform).
+    float k_sc = 1.0f, v_sc = 1.0f, v_lg = 0.0f, v_inv = 1.0f;
+    if constexpr (FP8) {
+        k_sc = k_scale[g];
+        v_sc = v_scale[g];
+        v_lg = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, __log2f(v_sc))));
+        v_inv = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, 1.0f / v_sc)));
     }
     u32x4 kreg[Cfg::kKPer], vreg[Cfg::kVPer];
     // PAGED: a tile of NK keys (NK a multiple of 16, kbase a multiple of NK)
@@ -253,28 +278,54 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                 }
                 pgv = fetch_pages(kt + 1);
             }
-            // Position j: cache row below ctx0, else chunk row j - ctx0 (past the
-            // chunk's last token clamped to it: such keys are masked).
-            auto src_row = [&](const uint16_t* cache_col, const uint16_t* chunk_col, size_t stride, int j) {
-                if (j < ctx0) {
-                    if constexpr (PAGED) {
-                        const int t = ((j - kbase) >> page_shift) & (kTilePages - 1);  // 0 when P >= NK
-                        int page = pg[0];
+            // Cache row of position j < ctx0.
+            auto cache_row = [&](int j) -> size_t {
+                if constexpr (PAGED) {
+                    const int t = ((j - kbase) >> page_shift) & (kTilePages - 1);  // 0 when P >= NK
+                    int page = pg[0];
 #pragma unroll
-                        for (int u = 1; u < kTilePages; ++u) page = t == u ? pg[u] : page;
-                        const size_t row = ((size_t)page << page_shift) | (size_t)(j & ((1 << page_shift) - 1));
-                        return cache_col + row * stride;
-                    }
-                    return cache_col + (size_t)(cache_row0 + (SWA ? j % ring : j)) * stride;
+                    for (int u = 1; u < kTilePages; ++u) page = t == u ? pg[u] : page;
+                    return ((size_t)page << page_shift) | (size_t)(j & ((1 << page_shift) - 1));
                 }
-                return chunk_col + (size_t)min(j - ctx0, L - 1) * stride;
+                return (size_t)(cache_row0 + (SWA ? j % ring : j));
             };
+            if constexpr (FP8) {
+                // Cached rows: 8 codes into the low half of the slot (widened
+                // in store_tile); chunk rows: 8 bf16 as they are.
 #pragma unroll
-            for (int i = 0; i < Cfg::kKPer; ++i)
-                kreg[i] = *reinterpret_cast<const u32x4*>(src_row(kcp[i], kp[i], kstride, kbase + krow_of[i]));
+                for (int i = 0; i < Cfg::kKPer; ++i) {
+                    const int j = kbase + krow_of[i];
+                    if (j < ctx0) {
+                        const u32x2 w = *reinterpret_cast<const u32x2*>(k_cache8 + cache_row(j) * kstride + kcol8[i]);
+                        kreg[i] = u32x4{w[0], w[1], 0u, 0u};
+                    } else {
+                        kreg[i] = *reinterpret_cast<const u32x4*>(kp[i] + (size_t)min(j - ctx0, L - 1) * kstride);
+                    }
+                }
 #pragma unroll
-            for (int i = 0; i < Cfg::kVPer; ++i)
-                vreg[i] = *reinterpret_cast<const u32x4*>(src_row(vcp[i], vp[i], vstride, kbase + vrow_of[i]));
+                for (int i = 0; i < Cfg::kVPer; ++i) {
+                    const int j = kbase + vrow_of[i];
+                    if (j < ctx0) {
+                        const u32x2 w = *reinterpret_cast<const u32x2*>(v_cache8 + cache_row(j) * vstride + vcol8[i]);
+                        vreg[i] = u32x4{w[0], w[1], 0u, 0u};
+                    } else {
+                        vreg[i] = *reinterpret_cast<const u32x4*>(vp[i] + (size_t)min(j - ctx0, L - 1) * vstride);
+                    }
+                }
+            } else {
+                // Position j: cache row below ctx0, else chunk row j - ctx0 (past
+                // the chunk's last token clamped to it: such keys are masked).
+                auto src_row = [&](const uint16_t* cache_col, const uint16_t* chunk_col, size_t stride, int j) {
+                    if (j < ctx0) return cache_col + cache_row(j) * stride;
+                    return chunk_col + (size_t)min(j - ctx0, L - 1) * stride;
+                };
+#pragma unroll
+                for (int i = 0; i < Cfg::kKPer; ++i)
+                    kreg[i] = *reinterpret_cast<const u32x4*>(src_row(kcp[i], kp[i], kstride, kbase + krow_of[i]));
+#pragma unroll
+                for (int i = 0; i < Cfg::kVPer; ++i)
+                    vreg[i] = *reinterpret_cast<const u32x4*>(src_row(vcp[i], vp[i], vstride, kbase + vrow_of[i]));
+            }
         } else {
             // The tile's rows through the descriptor: its base and record count
             // (the rows up to the sequence end) are wave-uniform scalars, the
@@ -290,9 +341,18 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             for (int i = 0; i < Cfg::kVPer; ++i) vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, voff[i], 0, 0);
         }
     };
-    auto store_tile = [&](int buf) {
+    // Writes the staged tile kt to LDS buffer buf (FP8: cached rows widened here).
+    auto store_tile = [&](int buf, int kt) {
         uint16_t* kb_ = lds_k + buf * Cfg::kLdsK;
         uint16_t* vb_ = lds_v + buf * Cfg::kLdsV;
+        if constexpr (FP8) {
+#pragma unroll
+            for (int i = 0; i < Cfg::kKPer; ++i)
+                if (kt * NK + krow_of[i] < ctx0) kreg[i] = fp8x8_to_bf16x8(kreg[i][0], kreg[i][1]);
+#pragma unroll
+            for (int i = 0; i < Cfg::kVPer; ++i)
+                if (kt * NK + vrow_of[i] < ctx0) vreg[i] = fp8x8_to_bf16x8(vreg[i][0], vreg[i][1]);
+        }
 #pragma unroll
         for (int i = 0; i < Cfg::kKPer; ++i) {
             const int c = tid + Cfg::kThreads * i;
@@ -308,7 +368,7 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     };
 
     load_tile(kt_begin);
-    store_tile(0);
+    store_tile(0, kt_begin);
     __syncthreads();
     // Source address of this lane for the transposed V reads: row 4*hh + (lane%16)/4
     // of a K-step, columns 16*((lane/16)%2) + 4*(lane%4) of a 32-column block.
@@ -341,6 +401,26 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             }
         }
         interleave_lds_mfma<(NK / 32) * (kDqk / 16) * NB, (NK / 32) * (kDqk / 16), MIMO_S_AHEAD, 1>();
+        // FP8: keys [kbase, kbase + ncached) of this tile come from the cache.
+        // A tile wholly from the cache takes the K scale into its score
+        // multiplier and the V scale into its exponent shift; the tile across
+        // ctx_lens[b] scales key by key (key of element r at offset
+        // 32*kb + 8*(r/4) + (r%4) + 4*hh).
+        const int ncached = FP8 ? min(max(ctx0 - kbase, 0), NK) : 0;
+        const bool all_cached = FP8 && ncached == NK;
+        const bool straddles = FP8 && ncached > 0 && ncached < NK;
+        const int ncached_lane = ncached - 4 * hh;  // element r is cached when its tile offset is below this
+        const float c_t = all_cached ? c_log2 * k_sc : c_log2;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            if (straddles) {
+#pragma unroll
+                for (int kb = 0; kb < NK / 32; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (kb * 32 + 8 * (r >> 2) + (r & 3) < ncached_lane) sacc[kb][nb][r] *= k_sc;
+            }
+        }
         // ---- mask, online softmax, P^T -> bf16, O^T += V^T * P^T -----------------
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
@@ -366,7 +446,7 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 #pragma unroll
                 for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[kb][nb][r], sacc[kb][nb][r + 1]));
             mx = max_with_partner_half(mx);
-            const float m_cand = fmaxf(m_run[nb], mx * c_log2);
+            const float m_cand = fmaxf(m_run[nb], mx * c_t);
             if (__builtin_amdgcn_ballot_w64(m_cand > m_run[nb] + kRescaleThreshold)) {
                 const float alpha = fast_exp2(m_run[nb] - m_cand);
                 l_run[nb] *= alpha;
@@ -374,15 +454,24 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                 for (int db = 0; db < kDv / 32; ++db) oacc[db][nb] *= alpha;
                 m_run[nb] = m_cand;
             }
-            const float neg_m = -m_run[nb];
+            // all_cached: exp2(s - m + log2 vs) = p * vs, whose sum is divided back by vs.
+            const float neg_m = all_cached ? v_lg - m_run[nb] : -m_run[nb];
             float rs = 0.0f;
 #pragma unroll
             for (int kb = 0; kb < NK / 32; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    sacc[kb][nb][r] = fast_exp2(__builtin_fmaf(sacc[kb][nb][r], c_log2, neg_m));
+                    sacc[kb][nb][r] = fast_exp2(__builtin_fmaf(sacc[kb][nb][r], c_t, neg_m));
                     rs += sacc[kb][nb][r];
                 }
+            if (all_cached) rs *= v_inv;
+            if (straddles) {
+#pragma unroll
+                for (int kb = 0; kb < NK / 32; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (kb * 32 + 8 * (r >> 2) + (r & 3) < ncached_lane) sacc[kb][nb][r] *= v_sc;
+            }
             bf16x8 pf[NK / 16];
 #pragma unroll
             for (int ks = 0; ks < NK / 16; ++ks) {
@@ -403,7 +492,7 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             }
             interleave_lds_mfma<(kDv / 32) * (NK / 16), 2 * (kDv / 32) * (NK / 16), MIMO_PV_AHEAD, 2>();
         }
-        if (more) store_tile(buf ^ 1);
+        if (more) store_tile(buf ^ 1, kt + 1);
         __syncthreads();
     }
 
@@ -769,16 +858,16 @@ void swa_stream_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
     }
 }
 
-template <int WV, int NB, int NK, bool SWA, int WPE, bool CHUNK = false, bool PAGED = false>
+template <int WV, int NB, int NK, bool SWA, int WPE, bool CHUNK = false, bool PAGED = false, bool FP8 = false>
 hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
     using Cfg = PrefillCfg<WV, NB, NK>;
     const int nqb = (a.max_seqlen + Cfg::kTokens - 1) / Cfg::kTokens;
     dim3 grid(nqb, a.hkv, a.num_seqs);
-    hipLaunchKernelGGL((prefill_kernel<WV, NB, NK, SWA, WPE, CHUNK, PAGED>), grid, dim3(Cfg::kThreads), 0, stream,
-                       a.q, a.k, a.v, a.cu_seqlens, a.sink, a.out, a.lse, a.hq, a.hkv, a.window,
+    hipLaunchKernelGGL((prefill_kernel<WV, NB, NK, SWA, WPE, CHUNK, PAGED, FP8>), grid, dim3(Cfg::kThreads), 0,
+                       stream, a.q, a.k, a.v, a.cu_seqlens, a.sink, a.out, a.lse, a.hq, a.hkv, a.window,
                        a.softmax_scale * kLog2e, a.value_scale, nqb, a.max_seqlen, a.k_cache, a.v_cache, a.kv_base,
                        a.ctx_lens, a.window - 1, a.pages.table, a.pages.max_blocks, a.pages.shift,
-                       a.pages.num_pages, a.rope_tab, a.rope_half);
+                       a.pages.num_pages, a.rope_tab, a.rope_half, a.k_cache8, a.v_cache8, a.k_scale, a.v_scale);
     return hipGetLastError();
 }
 
@@ -797,6 +886,10 @@ template <int WV, int NB, int NK, int WPE>
 hipError_t launch_swa(const PrefillArgs& a, hipStream_t s) { return launch<WV, NB, NK, true, WPE>(a, s); }
 template <int WV, int NB, int NK, int WPE>
 hipError_t launch_ga_chunk(const PrefillArgs& a, hipStream_t s) {
+    if (a.k_cache8) {
+        if (a.pages.table) return launch<WV, NB, NK, false, WPE, true, true, true>(a, s);
+        return launch<WV, NB, NK, false, WPE, true, false, true>(a, s);
+    }
     if (a.pages.table) return launch<WV, NB, NK, false, WPE, true, true>(a, s);
     return launch<WV, NB, NK, false, WPE, true>(a, s);
 }

@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define MIMO_ATTN_ABI_VERSION 10
+#define MIMO_ATTN_ABI_VERSION 11
 
 /* Layer type: which key set a query sees (model doc, Key features; config
  * layer_types). */
@@ -418,6 +418,54 @@ int mimo_attn_decode_fp8(const mimo_attn_dims* dims,
                          int32_t batch, int32_t max_ctx, int32_t split_tokens,
                          const float* sink, uint16_t* out, float* lse,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The FP8 GA pool in the other cache layouts (ABI version 11); codes and
+ * scales exactly as above, results bit-identical to the bf16 entry points'
+ * treatment of the same layout wherever the dequantised values are exact.
+ *
+ * mimo_kv_append_fp8_paged: as mimo_kv_append_paged (rows through the block
+ * table; a sequence past max_blocks * page_size skipped whole, a token on a
+ * block outside [0, num_pages) not written), storing E4M3 codes.
+ *
+ * mimo_attn_decode_fp8_paged: as mimo_attn_decode_fp8 with the code rows of
+ * position j of sequence b in row block_table[b][j / P] * P + j mod P
+ * (mimo_kv_pages, passed by host pointer); workspace as for
+ * mimo_attn_decode_fp8.
+ *
+ * mimo_attn_prefill_chunk_fp8 / _fp8_paged: GA chunked prefill
+ * (mimo_attn_prefill_chunk, mimo_attn_prefill_chunk_paged) whose cached
+ * positions j < ctx_lens[b] are read from an FP8 pool as value(code) *
+ * scale[g]; the chunk's own keys and values (k, v) are bf16 as given.
+ */
+int mimo_kv_append_fp8_paged(const mimo_attn_dims* dims,
+                             const uint16_t* k, const uint16_t* v,
+                             const int32_t* cu_newlens, const int32_t* ctx_lens,
+                             int32_t batch, int32_t total_new,
+                             uint8_t* k_cache, uint8_t* v_cache, const mimo_kv_pages* pages,
+                             const float* k_scale, const float* v_scale, hipStream_t stream);
+
+int mimo_attn_decode_fp8_paged(const mimo_attn_dims* dims,
+                               const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                               const uint8_t* k_cache, const uint8_t* v_cache, const mimo_kv_pages* pages,
+                               const float* k_scale, const float* v_scale, const int32_t* ctx_lens,
+                               int32_t batch, int32_t max_ctx, int32_t split_tokens,
+                               const float* sink, uint16_t* out, float* lse,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+int mimo_attn_prefill_chunk_fp8(const mimo_attn_dims* dims,
+                                const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                const int32_t* cu_newlens, int32_t num_seqs, int32_t max_newlen,
+                                const uint8_t* k_cache, const uint8_t* v_cache, const int64_t* kv_base,
+                                const float* k_scale, const float* v_scale, const int32_t* ctx_lens,
+                                const float* sink, uint16_t* out, float* lse, hipStream_t stream);
+
+int mimo_attn_prefill_chunk_fp8_paged(const mimo_attn_dims* dims,
+                                      const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                      const int32_t* cu_newlens, int32_t num_seqs, int32_t max_newlen,
+                                      const uint8_t* k_cache, const uint8_t* v_cache, const mimo_kv_pages* pages,
+                                      const float* k_scale, const float* v_scale, const int32_t* ctx_lens,
+                                      const float* sink, uint16_t* out, float* lse, hipStream_t stream);
 
 /*
  * Backward of mimo_attn_prefill: the gradients of sum(dout * out) for an

@@ -42,7 +42,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_version_and_status_strings(L):
-    assert B.mimo_abi_version() == 10
+    assert B.mimo_abi_version() == 11
     assert B.mimo_status_string(0) == "MIMO_OK"
     assert B.mimo_status_string(3) == "MIMO_ERR_WORKSPACE"
     assert B.mimo_status_string(99) == "MIMO_ERR_UNKNOWN"
@@ -364,6 +364,75 @@ def test_append_fp8_rejects(L, case, status):
 
 def test_append_fp8_nothing_is_ok(L):
     assert fp8_append_call(L, total=0) == B.MIMO_OK
+
+
+def fp8_paged_decode_call(L, pg=None, kc=FAKE, ks=FAKE, vs=FAKE, ctx=FAKE, batch=2, max_ctx=100, ws=FAKE,
+                          ws_bytes=1 << 30):
+    pref = None if pg is False else ctypes.byref(pg or pages())
+    return L.mimo_attn_decode_fp8_paged(ctypes.byref(B.make_dims()), FAKE, FAKE, FAKE, kc, FAKE, pref, ks, vs, ctx,
+                                        batch, max_ctx, 0, None, FAKE, None, ws, ws_bytes, None)
+
+
+def fp8_paged_append_call(L, pg=None, kc=FAKE, ks=FAKE, vs=FAKE, batch=1, total=4):
+    pref = None if pg is False else ctypes.byref(pg or pages())
+    return L.mimo_kv_append_fp8_paged(ctypes.byref(B.make_dims()), FAKE, FAKE, FAKE, FAKE, batch, total, kc, FAKE,
+                                      pref, ks, vs, None)
+
+
+def fp8_chunk_call(L, paged=False, pg=None, kc=FAKE, base=FAKE, ks=FAKE, vs=FAKE, ctx=FAKE, nseq=2, maxlen=16):
+    d = ctypes.byref(B.make_dims())
+    if paged:
+        pref = None if pg is False else ctypes.byref(pg or pages())
+        return L.mimo_attn_prefill_chunk_fp8_paged(d, FAKE, FAKE, FAKE, FAKE, nseq, maxlen, kc, FAKE, pref, ks, vs,
+                                                   ctx, None, FAKE, None, None)
+    return L.mimo_attn_prefill_chunk_fp8(d, FAKE, FAKE, FAKE, FAKE, nseq, maxlen, kc, FAKE, base, ks, vs, ctx, None,
+                                         FAKE, None, None)
+
+
+FP8_COMMON_BAD = [
+    (dict(kc=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(kc=FAKE_ODD), B.MIMO_ERR_INVALID_ARG),
+    (dict(ks=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(vs=FAKE + 2), B.MIMO_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("case,status", FP8_COMMON_BAD + [(dict(pg=pages(**c)), st) for c, st in PAGES_BAD] + [
+    (dict(pg=False), B.MIMO_ERR_INVALID_ARG),
+    (dict(ctx=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(batch=0), B.MIMO_ERR_INVALID_ARG),
+    (dict(ws=None), B.MIMO_ERR_WORKSPACE),
+])
+def test_decode_fp8_paged_rejects(L, case, status):
+    assert fp8_paged_decode_call(L, **case) == status
+    assert B.mimo_last_error() != ""
+
+
+@pytest.mark.parametrize("case,status", FP8_COMMON_BAD + [(dict(pg=pages(**c)), st) for c, st in PAGES_BAD] + [
+    (dict(pg=False), B.MIMO_ERR_INVALID_ARG),
+    (dict(batch=0), B.MIMO_ERR_INVALID_ARG),
+    (dict(total=-1), B.MIMO_ERR_INVALID_ARG),
+])
+def test_append_fp8_paged_rejects(L, case, status):
+    assert fp8_paged_append_call(L, **case) == status
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("case,status", FP8_COMMON_BAD + [
+    (dict(ctx=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(nseq=0), B.MIMO_ERR_INVALID_ARG),
+    (dict(maxlen=-1), B.MIMO_ERR_INVALID_ARG),
+])
+def test_prefill_chunk_fp8_rejects(L, paged, case, status):
+    assert fp8_chunk_call(L, paged=paged, **case) == status
+
+
+def test_fp8_layout_rejects_and_empty_calls(L):
+    assert fp8_chunk_call(L, base=None) == B.MIMO_ERR_INVALID_ARG  # contiguous GA needs kv_base
+    assert fp8_chunk_call(L, paged=True, pg=False) == B.MIMO_ERR_INVALID_ARG
+    assert fp8_chunk_call(L, maxlen=0) == B.MIMO_OK
+    assert fp8_chunk_call(L, paged=True, maxlen=0) == B.MIMO_OK
+    assert fp8_paged_append_call(L, total=0) == B.MIMO_OK
 
 
 def bwd_call(L, dims=None, layer=1, q=FAKE, out=FAKE, lse=FAKE, do=FAKE, cu=FAKE, nseq=2, maxlen=16, total=32,

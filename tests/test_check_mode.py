@@ -226,6 +226,32 @@ def test_fp8_scales(L, kscale, vscale, bits):
     expect(L, st, bits)
 
 
+def test_fp8_paged_and_chunk_entry_points(L):
+    ks, vs = np.full(4, 0.01, np.float32), np.full(4, 2.0, np.float32)
+    bad_vs = np.array([2.0, 0.0, 2.0, 2.0], np.float32)
+    ctx, table = i32(33, 0), i32(5, 6, 7, 99, -1, -1, -1, -1)
+    bad_table = i32(5, 6, 70, 99, -1, -1, -1, -1)  # block 2 of sequence 0 outside the 8-page pool
+    for tb, scale_v, bits in ((table, vs, 0), (bad_table, vs, C["BLOCK_TABLE"]), (table, bad_vs, C["FP8_SCALE"])):
+        st = L.mimo_attn_decode_fp8_paged(dims(), FAKE, FAKE, FAKE, FAKE, FAKE, pages(tb, 4), p(ks), p(scale_v),
+                                          p(ctx), 2, 64, 0, None, FAKE, None, FAKE, HUGE_WS, None)
+        expect(L, st, bits)
+        cu = i32(0, 3, 5)
+        st = L.mimo_attn_prefill_chunk_fp8_paged(dims(), FAKE, FAKE, FAKE, p(cu), 2, 3, FAKE, FAKE, pages(tb, 4), p(ks),
+                                                 p(scale_v), p(ctx), None, FAKE, None, None)
+        expect(L, st, bits)
+    base = i64(0, 100)
+    st = L.mimo_attn_prefill_chunk_fp8(dims(), FAKE, FAKE, FAKE, p(i32(0, 3, 5)), 2, 3, FAKE, FAKE, p(base), p(ks),
+                                       p(bad_vs), p(ctx), None, FAKE, None, None)
+    expect(L, st, C["FP8_SCALE"])
+    st = L.mimo_attn_prefill_chunk_fp8(dims(), FAKE, FAKE, FAKE, p(i32(0, 3, 5)), 2, 3, FAKE, FAKE, p(i64(0, -4)),
+                                       p(ks), p(vs), p(ctx), None, FAKE, None, None)
+    expect(L, st, C["KV_BASE"])
+    # paged FP8 append: sequence 0 writes positions 62..64 of a 4 x 16 table
+    st = L.mimo_kv_append_fp8_paged(dims(), FAKE, FAKE, p(i32(0, 3, 5)), p(i32(62, 0)), 2, 5, FAKE, FAKE,
+                                    pages(i32(0, 1, 2, 3, 4, 9, 9, 9), 4), p(ks), p(vs), None)
+    expect(L, st, C["CAPACITY"])
+
+
 # --------------------------------------------------------------------------- append
 @pytest.mark.parametrize("layer,cu,total,ctx,cap,bits", [
     (1, i32(0, 3, 5), 5, i32(10, 0), i64(13, 2), 0),
