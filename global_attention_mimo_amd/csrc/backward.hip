@@ -340,9 +340,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void bwd_dkdv_
 #pragma unroll
     for (int db = 0; db < kDv / 16; ++db) dva[db] = f32x4{};
 
-    // Queries that see a key of the block: tokens k0 .. q_end-1.
+    // Queries that see a key of the block: tokens k0 .. q_end-1, in blocks of
+    // kKvTok tokens.  GA walks them from the sequence end down, so that the
+    // workgroups of all key blocks of a group start at the same query block
+    // and stay near each other: a staged block is then fetched from HBM about
+    // once per L2 rather than once per workgroup.
     const int q_end = SWA ? min(L, k0 + kKvKeys - 1 + window) : L;
     const int nblk = (q_end - k0 + kKvTok - 1) / kKvTok;
+    auto q0_of = [&](int i) { return k0 + (SWA ? i : nblk - 1 - i) * kKvTok; };
 
     // Staging of a block of 2 tokens x 16 heads: 32 Q rows (768 16-byte
     // chunks), 32 dO rows (512 chunks), and the 32 rows' lse2 and D.  Row 16t +
@@ -372,8 +377,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void bwd_dkdv_
         u32x4 r[3];
         float lse2, d;
     };
-    auto load_blk = [&](Stage& st, int q0) {
-        const uint32_t toks = (uint32_t)max(0, min(L - q0, kKvTok));
+    auto load_blk = [&](Stage& st, int i) {  // block i of the walk; past the last one nothing is read
+        const int q0 = i < nblk ? q0_of(i) : k0;
+        const uint32_t toks = i < nblk ? (uint32_t)max(0, min(L - q0, kKvTok)) : 0u;
         const size_t row0 = (size_t)(s0 + q0) * hq + g * kGroup;
         const rsrc_t rq = make_rsrc(q + row0 * kDqk, toks * (uint32_t)hq * (kDqk * 2));
         const rsrc_t ro = make_rsrc(dout + row0 * kDv, toks * (uint32_t)hq * (kDv * 2));
@@ -403,7 +409,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void bwd_dkdv_
     };
     static_assert(kQChunks == 768 && kKvRows * (kDv / 8) == 512, "chunk owners assume 32 rows of 192 + 128");
     auto compute_blk = [&](int ib, int buf) {
-        const int q0 = k0 + ib * kKvTok;
+        const int q0 = q0_of(ib);
         const char* Qt = lds + buf * kKvTileBytes;
         const char* Ot = Qt + kKvRows * kQRow;
         const float* sf = reinterpret_cast<const float*>(Ot + kKvRows * kVRow);
@@ -446,17 +452,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void bwd_dkdv_
         for (int db = 0; db < kDqk / 16; ++db) dka[db] = mfma_16x16x32(lds_tr8(Qt, kQRow, db, lane), dsf, dka[db]);
     };
     Stage sa, sb;
-    load_blk(sa, k0);
+    load_blk(sa, 0);
     store_blk(sa, 0);
-    load_blk(sb, k0 + kKvTok);
+    load_blk(sb, 1);
     __syncthreads();
     int ib = 0;
     for (; ib + 1 < nblk; ib += 2) {
-        load_blk(sa, k0 + (ib + 2) * kKvTok);
+        load_blk(sa, ib + 2);
         compute_blk(ib, 0);
         store_blk(sb, 1);
         __syncthreads();
-        load_blk(sb, k0 + (ib + 3) * kKvTok);
+        load_blk(sb, ib + 3);
         compute_blk(ib + 1, 1);
         if (ib + 2 < nblk) store_blk(sa, 0);
         __syncthreads();

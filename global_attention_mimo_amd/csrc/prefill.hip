@@ -247,6 +247,7 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         v_inv = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, 1.0f / v_sc)));
     }
     u32x4 kreg[Cfg::kKPer], vreg[Cfg::kVPer];
+    u32x2 k8lo[Cfg::kKPer], k8hi[Cfg::kKPer], v8lo[Cfg::kVPer], v8hi[Cfg::kVPer];  // FP8 staging halves
     // PAGED: a tile of NK keys (NK a multiple of 16, kbase a multiple of NK)
     // spans max(1, NK / P) whole pages.  Their numbers come one tile ahead:
     // load_tile(kt) reads tile kt's from `pgv` (lane t holds block kt*NK/P + t)
@@ -290,27 +291,29 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                 return (size_t)(cache_row0 + (SWA ? j % ring : j));
             };
             if constexpr (FP8) {
-                // Cached rows: 8 codes into the low half of the slot (widened
-                // in store_tile); chunk rows: 8 bf16 as they are.
+                // The low 8 bytes of a slot come from the cache (8 codes) or
+                // the chunk (4 bf16) through one select of the address, the
+                // high 8 bytes always from the chunk row (for a cached row
+                // that is the chunk's first row, unused), so every load lands
+                // in its own registers and none waits.  Codes are widened in
+                // store_tile.
 #pragma unroll
                 for (int i = 0; i < Cfg::kKPer; ++i) {
                     const int j = kbase + krow_of[i];
-                    if (j < ctx0) {
-                        const u32x2 w = *reinterpret_cast<const u32x2*>(k_cache8 + cache_row(j) * kstride + kcol8[i]);
-                        kreg[i] = u32x4{w[0], w[1], 0u, 0u};
-                    } else {
-                        kreg[i] = *reinterpret_cast<const u32x4*>(kp[i] + (size_t)min(j - ctx0, L - 1) * kstride);
-                    }
+                    const uint16_t* crow = kp[i] + (size_t)min(max(j - ctx0, 0), L - 1) * kstride;
+                    const void* lo = j < ctx0 ? static_cast<const void*>(k_cache8 + cache_row(j) * kstride + kcol8[i])
+                                              : static_cast<const void*>(crow);
+                    k8lo[i] = *reinterpret_cast<const u32x2*>(lo);
+                    k8hi[i] = *reinterpret_cast<const u32x2*>(crow + 4);
                 }
 #pragma unroll
                 for (int i = 0; i < Cfg::kVPer; ++i) {
                     const int j = kbase + vrow_of[i];
-                    if (j < ctx0) {
-                        const u32x2 w = *reinterpret_cast<const u32x2*>(v_cache8 + cache_row(j) * vstride + vcol8[i]);
-                        vreg[i] = u32x4{w[0], w[1], 0u, 0u};
-                    } else {
-                        vreg[i] = *reinterpret_cast<const u32x4*>(vp[i] + (size_t)min(j - ctx0, L - 1) * vstride);
-                    }
+                    const uint16_t* crow = vp[i] + (size_t)min(max(j - ctx0, 0), L - 1) * vstride;
+                    const void* lo = j < ctx0 ? static_cast<const void*>(v_cache8 + cache_row(j) * vstride + vcol8[i])
+                                              : static_cast<const void*>(crow);
+                    v8lo[i] = *reinterpret_cast<const u32x2*>(lo);
+                    v8hi[i] = *reinterpret_cast<const u32x2*>(crow + 4);
                 }
             } else {
                 // Position j: cache row below ctx0, else chunk row j - ctx0 (past
@@ -348,10 +351,12 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         if constexpr (FP8) {
 #pragma unroll
             for (int i = 0; i < Cfg::kKPer; ++i)
-                if (kt * NK + krow_of[i] < ctx0) kreg[i] = fp8x8_to_bf16x8(kreg[i][0], kreg[i][1]);
+                kreg[i] = kt * NK + krow_of[i] < ctx0 ? fp8x8_to_bf16x8(k8lo[i][0], k8lo[i][1])
+                                                      : u32x4{k8lo[i][0], k8lo[i][1], k8hi[i][0], k8hi[i][1]};
 #pragma unroll
             for (int i = 0; i < Cfg::kVPer; ++i)
-                if (kt * NK + vrow_of[i] < ctx0) vreg[i] = fp8x8_to_bf16x8(vreg[i][0], vreg[i][1]);
+                vreg[i] = kt * NK + vrow_of[i] < ctx0 ? fp8x8_to_bf16x8(v8lo[i][0], v8lo[i][1])
+                                                      : u32x4{v8lo[i][0], v8lo[i][1], v8hi[i][0], v8hi[i][1]};
         }
 #pragma unroll
         for (int i = 0; i < Cfg::kKPer; ++i) {
