@@ -208,4 +208,31 @@ __device__ __forceinline__ void interleave_mfma_valu() {
 #endif
 }
 
+// PV MFMAs of a tile taken in two halves of kHalf MFMAs each (two transposed
+// LDS reads per MFMA): the first half's 2*kHalf exps come first, then the
+// first half's MFMAs with the second half's exps placed two per MFMA, and the
+// reads kAhead ahead.
+template <int kHalf, int kAhead>
+__device__ __forceinline__ void interleave_pv_trans() {
+#ifndef MIMO_NO_INTERLEAVE
+    constexpr int kReads = 4 * kHalf;
+    __builtin_amdgcn_sched_group_barrier(0x400, 2 * kHalf, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+    int placed = kAhead;
+#pragma unroll
+    for (int i = 0; i < kHalf; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (placed < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        placed += 2;
+        __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kHalf; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (placed < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        placed += 2;
+    }
+#endif
+}
+
 }  // namespace mimo

@@ -462,6 +462,58 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             // all_cached: exp2(s - m + log2 vs) = p * vs, whose sum is divided back by vs.
             const float neg_m = all_cached ? v_lg - m_run[nb] : -m_run[nb];
             float rs = 0.0f;
+            if constexpr (!FP8 && NK == 64) {
+                // Keys 0..31 first: exps, P^T, then their PV MFMAs with the
+                // exps of keys 32..63 placed among them.  Transcendental
+                // instructions issue in the shadow of independent MFMAs on this
+                // part (FMA-class VALU work does not), and the MFMAs of the first
+                // half do not wait for them.  Same operations and order per
+                // accumulator and per row sum as the plain form below.
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    sacc[0][nb][r] = fast_exp2(__builtin_fmaf(sacc[0][nb][r], c_t, neg_m));
+                    rs += sacc[0][nb][r];
+                }
+                bf16x8 ph[4];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const f32x16& sv = sacc[0][nb];
+                    ph[h] = pack_bf16x8(sv[8 * h + 0], sv[8 * h + 1], sv[8 * h + 2], sv[8 * h + 3], sv[8 * h + 4],
+                                        sv[8 * h + 5], sv[8 * h + 6], sv[8 * h + 7]);
+                }
+#pragma unroll
+                for (int db = 0; db < kDv / 32; ++db) {
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) {
+                        const uint16_t* p = vtile + vsrc_off + ks * 16 * kVStride + db * 32;
+                        const bf16x8 a = join_tr(lds_read_tr16(p), lds_read_tr16(p + 8 * kVStride));
+                        oacc[db][nb] = mfma_32x32x16(a, ph[ks], oacc[db][nb]);
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    sacc[1][nb][r] = fast_exp2(__builtin_fmaf(sacc[1][nb][r], c_t, neg_m));
+                    rs += sacc[1][nb][r];
+                }
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const f32x16& sv = sacc[1][nb];
+                    ph[2 + h] = pack_bf16x8(sv[8 * h + 0], sv[8 * h + 1], sv[8 * h + 2], sv[8 * h + 3], sv[8 * h + 4],
+                                            sv[8 * h + 5], sv[8 * h + 6], sv[8 * h + 7]);
+                }
+                l_run[nb] += rs;
+#pragma unroll
+                for (int db = 0; db < kDv / 32; ++db) {
+#pragma unroll
+                    for (int ks = 2; ks < 4; ++ks) {
+                        const uint16_t* p = vtile + vsrc_off + ks * 16 * kVStride + db * 32;
+                        const bf16x8 a = join_tr(lds_read_tr16(p), lds_read_tr16(p + 8 * kVStride));
+                        oacc[db][nb] = mfma_32x32x16(a, ph[ks], oacc[db][nb]);
+                    }
+                }
+                interleave_pv_trans<kDv / 32 * 2, MIMO_PV_AHEAD>();
+                continue;
+            }
 #pragma unroll
             for (int kb = 0; kb < NK / 32; ++kb)
 #pragma unroll
