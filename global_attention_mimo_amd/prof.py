@@ -91,7 +91,14 @@ WORKLOADS = {
 # Sources whose digest keys the GA prefill traffic record (any code change voids it).
 TRAFFIC_SOURCES = ["global_attention_mimo_amd/csrc/prefill.hip", "global_attention_mimo_amd/csrc/device_common.hpp",
                    "global_attention_mimo_amd/csrc/launch.hpp", "global_attention_mimo_amd/build.py"]
-GA_PREFILL = "prefill_kernel<8, 1, 64, false, 2, false, false>"
+def is_ga_prefill(short: str) -> bool:
+    """The GA (non-chunked, bf16) instantiation of prefill_kernel: template
+    arguments <waves, blocks, keys, SWA=false, waves per SIMD, then every
+    remaining flag (chunked, paged, FP8, ...) false>."""
+    if not short.startswith("prefill_kernel<") or not short.endswith(">"):
+        return False
+    args = [a.strip() for a in short[len("prefill_kernel<"):-1].split(",")]
+    return len(args) >= 6 and args[3] == "false" and all(a == "false" for a in args[5:])
 
 
 # -- names and numbers -------------------------------------------------------
@@ -304,7 +311,7 @@ def write_markdown(suite: str, out: str, res: dict, path: str) -> None:
 
 def write_traffic_record(res: dict, path: str, suite: str = "step") -> Optional[dict]:
     """The GA prefill launch's calibrated HBM bytes, keyed by the digest of its sources."""
-    kern = next((k for k in res.get("traffic", {}).get("kernels", {}) if short_name(k) == GA_PREFILL), None)
+    kern = next((k for k in res.get("traffic", {}).get("kernels", {}) if is_ga_prefill(short_name(k))), None)
     if kern is None:
         return None
     t = res["traffic"]

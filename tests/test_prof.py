@@ -28,6 +28,15 @@ def test_short_names():
     assert prof.short_name("__amd_rocclr_copyBuffer") == "__amd_rocclr_copyBuffer"
 
 
+def test_ga_prefill_instantiation_is_recognised():
+    assert prof.is_ga_prefill("prefill_kernel<8, 1, 64, false, 2, false, false>")
+    assert prof.is_ga_prefill("prefill_kernel<8, 1, 64, false, 2, false, false, false>")
+    assert not prof.is_ga_prefill("prefill_kernel<4, 1, 32, true, 2, false, false, false>")  # SWA
+    assert not prof.is_ga_prefill("prefill_kernel<8, 1, 64, false, 2, true, false, false>")  # chunked
+    assert not prof.is_ga_prefill("prefill_kernel<8, 1, 64, false, 2, true, false, true>")  # FP8 chunk
+    assert not prof.is_ga_prefill("swa_stream_kernel<false, false>")
+
+
 def test_trace_stats_from_fixture():
     st = prof.trace_stats(prof._csv_rows(os.path.join(FIX, "trace"), "kernel_trace.csv"))
     p = st[full(st, "prefill_kernel<8, 1, 64, false, 2, false, false>")]
