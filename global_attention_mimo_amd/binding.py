@@ -40,7 +40,7 @@ ENTRY_POINTS = ("mimo_attn_prefill", "mimo_attn_prefill_chunk", "mimo_attn_decod
                 "mimo_kv_append_fp8_paged", "mimo_attn_decode_fp8_paged", "mimo_attn_prefill_chunk_fp8",
                 "mimo_attn_prefill_chunk_fp8_paged",
                 "mimo_attn_prefill_backward_workspace_size", "mimo_attn_prefill_backward", "mimo_rope_apply",
-                "mimo_attn_prefill_rope_workspace_size", "mimo_attn_prefill_rope",
+                "mimo_attn_prefill_rope_workspace_size", "mimo_attn_prefill_rope", "mimo_attn_prefill_chunk_rope",
                 "mimo_attn_set_check", "mimo_attn_check_flags", "mimo_status_string",
                 "mimo_last_error", "mimo_abi_version")
 
@@ -139,6 +139,9 @@ def load(path: str) -> ctypes.CDLL:
     L.mimo_attn_prefill_rope.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _P, _I32, _I32, _I32,
                                          ctypes.c_float, _I32, _P, _P, _P, _P, _P, _SZ, _P]
     L.mimo_status_string.restype = ctypes.c_char_p
+    L.mimo_attn_prefill_chunk_rope.restype = ctypes.c_int
+    L.mimo_attn_prefill_chunk_rope.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P,
+                                               pages_p, _P, ctypes.c_float, _I32, _P, _P, _P, _P, _P, _SZ, _P]
     L.mimo_attn_set_check.restype = ctypes.c_int
     L.mimo_attn_set_check.argtypes = [ctypes.c_int]
     L.mimo_attn_check_flags.restype = ctypes.c_int
@@ -571,6 +574,39 @@ def prefill_rope(q, k, v, positions, cu_seqlens, max_seqlen: int, layer_type: in
     ws = torch.empty(max(nbytes, 16) // 4 + 4, dtype=torch.float32, device=q.device)
     mimo_attn_prefill_rope(dims, layer_type, q, k, v, positions, cu_seqlens, cu_seqlens.numel() - 1, max_seqlen, T,
                            rope_theta, rotary_dim, sink, out, lse, k_rot, ws, stream)
+    return out, lse, k_rot
+
+
+def mimo_attn_prefill_chunk_rope(dims: mimo_attn_dims, layer_type: int, q, k, v, positions, cu_newlens, num_seqs: int,
+                                 max_newlen: int, total_new: int, k_cache, v_cache, kv_base,
+                                 pages: Optional[mimo_kv_pages], ctx_lens, rope_theta: float, rotary_dim: int, sink,
+                                 out, lse, k_rot, workspace, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().mimo_attn_prefill_chunk_rope(ctypes.byref(dims), layer_type, _ptr(q), _ptr(k), _ptr(v),
+                                              _ptr(positions), _ptr(cu_newlens), num_seqs, max_newlen, total_new,
+                                              _ptr(k_cache), _ptr(v_cache), _ptr(kv_base), _pages_ref(pages),
+                                              _ptr(ctx_lens), rope_theta, rotary_dim, _ptr(sink), _ptr(out),
+                                              _ptr(lse), _ptr(k_rot), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def prefill_chunk_rope(q, k, v, positions, cu_newlens, max_newlen: int, k_cache, v_cache, ctx_lens, layer_type: int,
+                       rope_theta: float, rotary_dim: int, sink=None, kv_base=None, block_table=None,
+                       page_size: int = 0, dims=None, out=None, lse=None, k_rot=None, stream=None):
+    """Chunked prefill with fused RoPE; returns (out, lse, k_rot)."""
+    dims = dims or make_dims()
+    T = q.shape[0]
+    if out is None:
+        out = torch.empty((T, dims.num_q_heads, dims.head_dim_v), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, dims.num_q_heads), dtype=torch.float32, device=q.device)
+    if k_rot is None:
+        k_rot = torch.empty_like(k)
+    nbytes = mimo_attn_prefill_rope_workspace_size(dims, T, rotary_dim)
+    ws = torch.empty(max(nbytes, 16) // 4 + 4, dtype=torch.float32, device=q.device)
+    pages = None if block_table is None else make_pages(block_table, page_size, k_cache.shape[0] // page_size)
+    mimo_attn_prefill_chunk_rope(dims, layer_type, q, k, v, positions, cu_newlens, cu_newlens.numel() - 1, max_newlen,
+                                 T, k_cache, v_cache, kv_base, pages, ctx_lens, rope_theta, rotary_dim, sink, out,
+                                 lse, k_rot, ws, stream)
     return out, lse, k_rot
 
 

@@ -186,12 +186,58 @@ int check_fp8(const Fp8Pool& f) {
     return MIMO_OK;
 }
 
+// Fused RoPE of a prefill-style call: the tokens' position ids, the rotation
+// and the caller's k_rot and table workspace.
+struct RopeReq {
+    const int32_t* positions = nullptr;
+    int32_t total_tokens = 0;
+    float theta = 0.0f;
+    int32_t rotary_dim = 0;
+    uint16_t* k_rot = nullptr;
+    void* workspace = nullptr;
+    size_t workspace_bytes = 0;
+};
+
+// Host checks of a RopeReq (the non-NULL pointers and the sizes).
+int check_rope(const mimo_attn_dims* dims, const RopeReq& r) {
+    if (!r.positions || !r.k_rot) return fail(MIMO_ERR_INVALID_ARG, "positions and k_rot must be non-NULL");
+    if (!aligned16(r.k_rot)) return fail(MIMO_ERR_INVALID_ARG, "k_rot must be 16-byte aligned");
+    if (r.total_tokens < 0) return fail(MIMO_ERR_INVALID_ARG, "total_tokens %d is negative", r.total_tokens);
+    if (!std::isfinite(r.theta) || !(r.theta > 1.0f))
+        return fail(MIMO_ERR_INVALID_ARG, "rope_theta must be finite and above 1");
+    if (r.rotary_dim < 32 || r.rotary_dim > dims->head_dim_qk || r.rotary_dim % 32)
+        return fail(MIMO_ERR_UNSUPPORTED, "fused RoPE needs rotary_dim a multiple of 32 in [32, %d] (got %d)",
+                    dims->head_dim_qk, r.rotary_dim);
+    return MIMO_OK;
+}
+
+// The (cos, sin) table workspace of a RopeReq with total_tokens > 0.
+int check_rope_workspace(const RopeReq& r) {
+    const size_t need = mimo::rope_table_bytes(r.total_tokens, r.rotary_dim);
+    if (!r.workspace || r.workspace_bytes < need)
+        return fail(MIMO_ERR_WORKSPACE, "fused RoPE needs %zu workspace bytes (got %zu%s)", need, r.workspace_bytes,
+                    r.workspace ? "" : ", NULL");
+    if (!aligned16(r.workspace)) return fail(MIMO_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    return MIMO_OK;
+}
+
+// Enqueues the K rotation (k -> k_rot) and the (cos, sin) table for a fused
+// RoPE call whose attention then reads k_rot and rotates Q from the table.
+int rope_prepare(const mimo_attn_dims* dims, const uint16_t* k, const RopeReq& r, hipStream_t stream) {
+    mimo::RopePrepArgs pa{k, r.positions, r.k_rot, static_cast<float*>(r.workspace), r.total_tokens,
+                          dims->num_kv_heads, r.rotary_dim, (double)r.theta};
+    return hip_status(mimo::launch_rope_prep(pa, stream), "RoPE preparation launch");
+}
+
 int prefill_chunk_impl(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, const uint16_t* k,
                        const uint16_t* v, const int32_t* cu_newlens, int32_t num_seqs, int32_t max_newlen,
                        const uint16_t* k_cache, const uint16_t* v_cache, const int64_t* kv_base,
                        const mimo_kv_pages* pages, const int32_t* ctx_lens, const float* sink, uint16_t* out,
-                       float* lse, hipStream_t stream, const Fp8Pool* fp8 = nullptr) {
+                       float* lse, hipStream_t stream, const Fp8Pool* fp8 = nullptr, const RopeReq* rope = nullptr) {
     if (int st = check_dims(dims, layer_type, 2)) return st;
+    if (rope) {
+        if (int st = check_rope(dims, *rope)) return st;
+    }
     if (fp8) {
         if (int st = check_fp8(*fp8)) return st;
         // The code pools stand in for the bf16 caches in the checks below.
@@ -212,10 +258,17 @@ int prefill_chunk_impl(const mimo_attn_dims* dims, int layer_type, const uint16_
     if (num_seqs < 1 || num_seqs > kMaxGridYZ)
         return fail(MIMO_ERR_INVALID_ARG, "num_seqs %d outside [1, %d]", num_seqs, kMaxGridYZ);
     if (max_newlen < 0) return fail(MIMO_ERR_INVALID_ARG, "max_newlen %d is negative", max_newlen);
-    if (max_newlen == 0) return ok();
-    mimo::PrefillArgs a{q, k, v, cu_newlens, sink, out, lse, num_seqs, max_newlen, dims->num_q_heads,
-                        dims->num_kv_heads, dims->sliding_window, dims->softmax_scale, dims->value_scale,
-                        layer_type == MIMO_LAYER_SWA};
+    if (max_newlen == 0 || (rope && rope->total_tokens == 0)) return ok();
+    if (rope) {
+        if (int st = check_rope_workspace(*rope)) return st;
+    }
+    mimo::PrefillArgs a{q, rope ? rope->k_rot : k, v, cu_newlens, sink, out, lse, num_seqs, max_newlen,
+                        dims->num_q_heads, dims->num_kv_heads, dims->sliding_window, dims->softmax_scale,
+                        dims->value_scale, layer_type == MIMO_LAYER_SWA};
+    if (rope) {
+        a.rope_tab = static_cast<const float*>(rope->workspace);
+        a.rope_half = rope->rotary_dim / 2;
+    }
     a.k_cache = k_cache;
     a.v_cache = v_cache;
     a.kv_base = kv_base;
@@ -244,7 +297,11 @@ int prefill_chunk_impl(const mimo_attn_dims* dims, int layer_type, const uint16_
         c.scales_v = fp8->v_scale;
         c.n_scales = dims->num_kv_heads;
     }
+    if (rope) c.total = rope->total_tokens;
     if (int st = precheck(c, stream, "chunked prefill")) return st;
+    if (rope) {
+        if (int st = rope_prepare(dims, k, *rope, stream)) return st;
+    }
     return hip_status(mimo::launch_prefill_chunk(a, stream), "chunked prefill launch");
 }
 
@@ -269,6 +326,27 @@ int mimo_attn_prefill_chunk_paged(const mimo_attn_dims* dims, const uint16_t* q,
     if (!pages) return fail(MIMO_ERR_INVALID_ARG, "pages is NULL");
     return prefill_chunk_impl(dims, MIMO_LAYER_GA, q, k, v, cu_newlens, num_seqs, max_newlen, k_cache, v_cache,
                               nullptr, pages, ctx_lens, sink, out, lse, stream);
+}
+
+int mimo_attn_prefill_chunk_rope(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, const uint16_t* k,
+                                 const uint16_t* v, const int32_t* positions, const int32_t* cu_newlens,
+                                 int32_t num_seqs, int32_t max_newlen, int32_t total_new, const uint16_t* k_cache,
+                                 const uint16_t* v_cache, const int64_t* kv_base, const mimo_kv_pages* pages,
+                                 const int32_t* ctx_lens, float rope_theta, int32_t rotary_dim, const float* sink,
+                                 uint16_t* out, float* lse, uint16_t* k_rot, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+    if (pages && layer_type != MIMO_LAYER_GA)
+        return fail(MIMO_ERR_INVALID_ARG, "a paged pool holds a GA layer's cache only");
+    RopeReq r;
+    r.positions = positions;
+    r.total_tokens = total_new;
+    r.theta = rope_theta;
+    r.rotary_dim = rotary_dim;
+    r.k_rot = k_rot;
+    r.workspace = workspace;
+    r.workspace_bytes = workspace_bytes;
+    return prefill_chunk_impl(dims, layer_type, q, k, v, cu_newlens, num_seqs, max_newlen, k_cache, v_cache, kv_base,
+                              pages, ctx_lens, sink, out, lse, stream, nullptr, &r);
 }
 
 int mimo_attn_prefill_chunk_fp8(const mimo_attn_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -623,18 +701,17 @@ int mimo_attn_prefill_rope(const mimo_attn_dims* dims, int layer_type, const uin
     if (num_seqs < 1 || num_seqs > kMaxGridYZ)
         return fail(MIMO_ERR_INVALID_ARG, "num_seqs %d outside [1, %d]", num_seqs, kMaxGridYZ);
     if (max_seqlen < 0) return fail(MIMO_ERR_INVALID_ARG, "max_seqlen %d is negative", max_seqlen);
-    if (total_tokens < 0) return fail(MIMO_ERR_INVALID_ARG, "total_tokens %d is negative", total_tokens);
-    if (!std::isfinite(rope_theta) || !(rope_theta > 1.0f))
-        return fail(MIMO_ERR_INVALID_ARG, "rope_theta must be finite and above 1");
-    if (rotary_dim < 32 || rotary_dim > dims->head_dim_qk || rotary_dim % 32)
-        return fail(MIMO_ERR_UNSUPPORTED, "fused RoPE needs rotary_dim a multiple of 32 in [32, %d] (got %d)",
-                    dims->head_dim_qk, rotary_dim);
+    RopeReq r;
+    r.positions = positions;
+    r.total_tokens = total_tokens;
+    r.theta = rope_theta;
+    r.rotary_dim = rotary_dim;
+    r.k_rot = k_rot;
+    r.workspace = workspace;
+    r.workspace_bytes = workspace_bytes;
+    if (int st = check_rope(dims, r)) return st;
     if (max_seqlen == 0 || total_tokens == 0) return ok();
-    const size_t need = mimo::rope_table_bytes(total_tokens, rotary_dim);
-    if (!workspace || workspace_bytes < need)
-        return fail(MIMO_ERR_WORKSPACE, "fused RoPE needs %zu workspace bytes (got %zu%s)", need, workspace_bytes,
-                    workspace ? "" : ", NULL");
-    if (!aligned16(workspace)) return fail(MIMO_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    if (int st = check_rope_workspace(r)) return st;
     mimo::CheckArgs c;
     c.cu = cu_seqlens;
     c.n_seqs = num_seqs;
@@ -643,9 +720,7 @@ int mimo_attn_prefill_rope(const mimo_attn_dims* dims, int layer_type, const uin
     c.sink = sink;
     c.hq = dims->num_q_heads;
     if (int st = precheck(c, stream, "mimo_attn_prefill_rope")) return st;
-    mimo::RopePrepArgs r{k, positions, k_rot, static_cast<float*>(workspace), total_tokens, dims->num_kv_heads,
-                         rotary_dim, (double)rope_theta};
-    if (int st = hip_status(mimo::launch_rope_prep(r, stream), "RoPE preparation launch")) return st;
+    if (int st = rope_prepare(dims, k, r, stream)) return st;
     mimo::PrefillArgs a{q, k_rot, v, cu_seqlens, sink, out, lse, num_seqs, max_seqlen, dims->num_q_heads,
                         dims->num_kv_heads, dims->sliding_window, dims->softmax_scale, dims->value_scale,
                         layer_type == MIMO_LAYER_SWA};

@@ -976,9 +976,7 @@ hipError_t launch_swa_stream(const PrefillArgs& a, hipStream_t stream) {
     const long long target = (long long)max(cus, 1) * MIMO_STREAM_ROUNDS;
     const int strip = (int)max(1LL, min(min(per_seq, (long long)MIMO_STREAM_MAX_STRIP), (total + target - 1) / target));
     dim3 grid((unsigned)((per_seq + strip - 1) / strip), a.hkv, a.num_seqs);
-    auto kern = swa_stream_kernel<CHUNK, false>;
-    if constexpr (!CHUNK)
-        if (a.rope_tab) kern = swa_stream_kernel<false, true>;
+    auto kern = a.rope_tab ? swa_stream_kernel<CHUNK, true> : swa_stream_kernel<CHUNK, false>;
     hipLaunchKernelGGL(kern, grid, dim3(kStreamThreads), 0, stream, a.q, a.k, a.v, a.cu_seqlens,
                        a.sink, a.out, a.lse, a.hq, a.hkv, a.window, a.softmax_scale * kLog2e, a.value_scale, strip,
                        a.max_seqlen, a.k_cache, a.v_cache, a.ctx_lens, a.rope_tab, a.rope_half);
@@ -989,7 +987,8 @@ hipError_t launch_swa_stream(const PrefillArgs& a, hipStream_t stream) {
 
 hipError_t launch_prefill_chunk(const PrefillArgs& a, hipStream_t stream) {
     if (a.max_seqlen <= 0) return hipSuccess;
-    if (a.swa && a.window <= kStreamMaxWindow) return launch_swa_stream<true>(a, stream);
+    if (a.swa && a.window <= kStreamMaxWindow && (!a.rope_tab || a.rope_half <= kStreamRopeHalf))
+        return launch_swa_stream<true>(a, stream);
     if (a.swa) return launch_swa_chunk<MIMO_SWA_CFG>(a, stream);
     return launch_ga_chunk<MIMO_GA_CFG>(a, stream);
 }

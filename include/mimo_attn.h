@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define MIMO_ATTN_ABI_VERSION 11
+#define MIMO_ATTN_ABI_VERSION 12
 
 /* Layer type: which key set a query sees (model doc, Key features; config
  * layer_types). */
@@ -556,6 +556,36 @@ int mimo_attn_prefill_rope(const mimo_attn_dims* dims, int layer_type,
                            const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen, int32_t total_tokens,
                            float rope_theta, int32_t rotary_dim, const float* sink, uint16_t* out, float* lse,
                            uint16_t* k_rot, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Chunked prefill with the rotary embedding fused in (ABI version 12): as
+ * mimo_attn_prefill_chunk (layer_type SWA or GA; pages non-NULL selects the
+ * paged GA pool, else kv_base) for the chunk's un-rotated q and k, rotated as
+ * mimo_attn_prefill_rope does it -- K once into k_rot by a K-only pass that
+ * also writes each token's (cos, sin) table into the workspace, Q in
+ * registers as the attention kernels load it -- at the caller's position ids
+ * (normally ctx_lens[b] + i for token i of sequence b).  The cached keys are
+ * read as they are: the caches hold post-RoPE keys (what the caller appended
+ * from k_rot).  Bit-identical to mimo_rope_apply on copies of q and k
+ * followed by mimo_attn_prefill_chunk(_paged) over the rotated copies.
+ *
+ *   positions    [total_new] int32 (device).
+ *   total_new    (host) == cu_newlens[num_seqs].
+ *   k_rot        [total_new][Hkv][192] bf16 (device), written; may alias k.
+ *   workspace    mimo_attn_prefill_rope_workspace_size(dims, total_new,
+ *                rotary_dim) bytes of device memory, scratch after the call.
+ *   rope_theta, rotary_dim  as mimo_attn_prefill_rope.
+ * A call with max_newlen == 0 or total_new == 0 enqueues nothing.  Other
+ * errors as mimo_attn_prefill_chunk and mimo_attn_prefill_rope.
+ */
+int mimo_attn_prefill_chunk_rope(const mimo_attn_dims* dims, int layer_type,
+                                 const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* positions,
+                                 const int32_t* cu_newlens, int32_t num_seqs, int32_t max_newlen, int32_t total_new,
+                                 const uint16_t* k_cache, const uint16_t* v_cache, const int64_t* kv_base,
+                                 const mimo_kv_pages* pages, const int32_t* ctx_lens,
+                                 float rope_theta, int32_t rotary_dim, const float* sink,
+                                 uint16_t* out, float* lse, uint16_t* k_rot,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Check mode (see the conventions above).  mimo_attn_set_check switches it on

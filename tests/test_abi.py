@@ -42,7 +42,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_version_and_status_strings(L):
-    assert B.mimo_abi_version() == 11
+    assert B.mimo_abi_version() == 12
     assert B.mimo_status_string(0) == "MIMO_OK"
     assert B.mimo_status_string(3) == "MIMO_ERR_WORKSPACE"
     assert B.mimo_status_string(99) == "MIMO_ERR_UNKNOWN"
@@ -529,6 +529,45 @@ def rope_prefill_call(L, dims=None, layer=0, k_rot=FAKE, pos=FAKE, total=64, the
 def test_prefill_rope_rejects(L, case, status):
     assert rope_prefill_call(L, **case) == status
     assert B.mimo_last_error() != ""
+
+
+def chunk_rope_call(L, layer=1, q=FAKE, pos=FAKE, kc=FAKE, base=FAKE, pg=None, ctx=FAKE, total=64, maxlen=16,
+                    theta=1e4, rd=64, krot=FAKE, ws=FAKE, ws_bytes=64 * 32 * 8):
+    pref = ctypes.byref(pg) if pg is not None else None
+    return L.mimo_attn_prefill_chunk_rope(ctypes.byref(B.make_dims()), layer, q, FAKE, FAKE, pos, FAKE, 2, maxlen,
+                                          total, kc, FAKE, base, pref, ctx, theta, rd, None, FAKE, None, krot, ws,
+                                          ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(q=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(pos=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(krot=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(krot=FAKE_ODD), B.MIMO_ERR_INVALID_ARG),
+    (dict(kc=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(ctx=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(base=None), B.MIMO_ERR_INVALID_ARG),            # contiguous GA needs kv_base
+    (dict(layer=0, pg=pages()), B.MIMO_ERR_INVALID_ARG),  # a paged pool is GA only
+    (dict(pg=pages(page_size=8)), B.MIMO_ERR_UNSUPPORTED),
+    (dict(total=-1), B.MIMO_ERR_INVALID_ARG),
+    (dict(theta=1.0), B.MIMO_ERR_INVALID_ARG),
+    (dict(theta=float("nan")), B.MIMO_ERR_INVALID_ARG),
+    (dict(rd=48), B.MIMO_ERR_UNSUPPORTED),
+    (dict(rd=224), B.MIMO_ERR_UNSUPPORTED),
+    (dict(ws=None), B.MIMO_ERR_WORKSPACE),
+    (dict(ws_bytes=64 * 32 * 8 - 1), B.MIMO_ERR_WORKSPACE),
+    (dict(ws=FAKE_ODD), B.MIMO_ERR_INVALID_ARG),
+    (dict(layer=2), B.MIMO_ERR_INVALID_ARG),
+])
+def test_prefill_chunk_rope_rejects(L, case, status):
+    assert chunk_rope_call(L, **case) == status
+    assert B.mimo_last_error() != ""
+
+
+def test_prefill_chunk_rope_empty(L):
+    assert chunk_rope_call(L, total=0, ws=None) == B.MIMO_OK
+    assert chunk_rope_call(L, maxlen=0, ws=None) == B.MIMO_OK
+    assert chunk_rope_call(L, layer=0, base=None, total=0) == B.MIMO_OK  # SWA ignores kv_base
 
 
 def test_prefill_rope_workspace_and_empty(L):

@@ -110,6 +110,15 @@ def test_prefill(L, cu, maxlen, sink, bits, layer):
     expect(L, st, bits)
 
 
+@pytest.mark.parametrize("total,bits", [(7, 0), (8, C["CU_TOTAL"])])
+def test_chunked_fused_rope_total(L, total, bits):
+    cu, ctx, base = i32(0, 4, 7), i32(100, 0), i64(0, 4096)
+    pos = np.arange(total, dtype=np.int32)
+    st = L.mimo_attn_prefill_chunk_rope(dims(), 1, FAKE, FAKE, FAKE, p(pos), p(cu), 2, 4, total, FAKE, FAKE, p(base),
+                                        None, p(ctx), 1e4, 64, None, FAKE, None, FAKE, FAKE, HUGE_WS, None)
+    expect(L, st, bits)
+
+
 @pytest.mark.parametrize("total,bits", [(9, 0), (10, C["CU_TOTAL"]), (8, C["CU_TOTAL"])])
 def test_backward_and_fused_rope_total(L, total, bits):
     cu = i32(0, 5, 9)
