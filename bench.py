@@ -394,7 +394,8 @@ def hybrid_rows(dims, decode_steps=64):
     from global_attention_mimo_amd.stack import HybridStack, GA as L_GA
     dev = "cuda"
     lengths = synth.hybrid_prompt_lengths(32, seed=0)
-    st = HybridStack(lengths, decode_steps=decode_steps, device=dev)
+    rope_steps = 16  # per RoPE mode, after the plain steps
+    st = HybridStack(lengths, decode_steps=decode_steps + 2 * rope_steps, device=dev)
     gen = torch.Generator(device=dev).manual_seed(0)
     sinks = torch.randn((st.num_layers, HQ), generator=gen, device=dev)
     out = torch.empty((st.total, HQ, DV), dtype=torch.bfloat16, device=dev)
@@ -450,9 +451,30 @@ def hybrid_rows(dims, decode_steps=64):
         torch.cuda.synchronize()
         (eager_ms if graph is None else graph_ms).append(
             (e0.elapsed_time(e1), (time.perf_counter() - t0) * 1e3))
+    del graph
+    # The same step with q / k_new rotated at their positions (rotary dims 64,
+    # theta 5e6): inside the decode calls, or by a separate in-place pass per layer.
+    rope_ms = {}
+    for mode in ("fused", "separate"):
+        st.rope_mode = mode
+        graph, times = None, []
+        for step in range(rope_steps):
+            draw()
+            if graph is None:
+                graph = st.capture_decode_step(q, kn, vn, sinks, dout, dlse)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        rope_ms[mode] = float(np.mean(times))
+        del graph
+    st.rope_mode = None
     kvb = st.kv_bytes()
     calls = st.num_layers * (1 if st.fused else 2)
-    del st, out, lse, dout, dlse, graph
+    del st, out, lse, dout, dlse
     torch.cuda.empty_cache()
     dec_ms = float(np.mean([g for g, _ in graph_ms]))
     eager_gpu = float(np.mean([g for g, _ in eager_ms]))
@@ -470,6 +492,10 @@ def hybrid_rows(dims, decode_steps=64):
         "decode_step_note": f"HIP-graph replay of the whole step ({calls} library calls + context advance), mean of "
                             f"{len(graph_ms)} steps; the first {len(eager_ms)} steps issued call by call took "
                             f"{eager_gpu:.3f} ms on the GPU clock and {eager_wall:.3f} ms host wall time",
+        "decode_step_rope_fused_ms": rope_ms["fused"], "decode_step_rope_separate_ms": rope_ms["separate"],
+        "decode_step_rope_note": f"the step with RoPE (rotary dims 64, theta 5e6, positions = contexts) on each "
+                                 f"layer's q and k_new, HIP-graph replay, mean of {rope_steps} steps each: fused "
+                                 f"(mimo_attn_decode_append_rope) against mimo_rope_apply + mimo_attn_decode_append",
         "kv_cache_bytes": kvb["hybrid"], "kv_cache_bytes_all_ga": kvb["all_ga"]}}
 
 

@@ -34,7 +34,8 @@ CHECK_BITS = {"CU_START": 0x001, "CU_ORDER": 0x002, "CU_LENGTH": 0x004, "CU_TOTA
               "KV_BASE": 0x020, "CAPACITY": 0x040, "BLOCK_TABLE": 0x080, "SINK": 0x100, "FP8_SCALE": 0x200}
 
 ENTRY_POINTS = ("mimo_attn_prefill", "mimo_attn_prefill_chunk", "mimo_attn_decode_workspace_size",
-                "mimo_attn_decode", "mimo_attn_decode_noalloc", "mimo_attn_decode_append", "mimo_kv_append", "mimo_kv_append_paged",
+                "mimo_attn_decode", "mimo_attn_decode_noalloc", "mimo_attn_decode_append", "mimo_attn_decode_append_rope",
+                "mimo_kv_append", "mimo_kv_append_paged",
                 "mimo_attn_decode_paged",
                 "mimo_attn_prefill_chunk_paged", "mimo_kv_append_fp8", "mimo_attn_decode_fp8",
                 "mimo_kv_append_fp8_paged", "mimo_attn_decode_fp8_paged", "mimo_attn_prefill_chunk_fp8",
@@ -99,6 +100,9 @@ def load(path: str) -> ctypes.CDLL:
     L.mimo_attn_decode_append.restype = ctypes.c_int
     L.mimo_attn_decode_append.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
                                           _P, _P, _P, _P, _SZ, _P]
+    L.mimo_attn_decode_append_rope.restype = ctypes.c_int
+    L.mimo_attn_decode_append_rope.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32,
+                                               _I32, _I32, ctypes.c_float, _I32, _P, _P, _P, _P, _SZ, _P]
     L.mimo_kv_append.restype = ctypes.c_int
     L.mimo_kv_append.argtypes = [dims_p, ctypes.c_int, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _P]
     pages_p = ctypes.POINTER(mimo_kv_pages)
@@ -247,6 +251,17 @@ def mimo_attn_decode_append(dims: mimo_attn_dims, layer_type: int, q, k_new, v_n
                                          _ptr(k_cache), _ptr(v_cache), _ptr(kv_base), _ptr(kv_capacity),
                                          _ptr(ctx_lens), batch, max_ctx, split_tokens, _ptr(sink), _ptr(out),
                                          _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def mimo_attn_decode_append_rope(dims: mimo_attn_dims, layer_type: int, q, k_new, v_new, positions, k_cache,
+                                 v_cache, kv_base, kv_capacity, ctx_lens, batch: int, max_ctx: int, split_tokens: int,
+                                 rope_theta: float, rotary_dim: int, sink, out, lse, workspace, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().mimo_attn_decode_append_rope(ctypes.byref(dims), layer_type, _ptr(q), _ptr(k_new), _ptr(v_new),
+                                              _ptr(positions), _ptr(k_cache), _ptr(v_cache), _ptr(kv_base),
+                                              _ptr(kv_capacity), _ptr(ctx_lens), batch, max_ctx, split_tokens,
+                                              rope_theta, rotary_dim, _ptr(sink), _ptr(out), _ptr(lse),
+                                              _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def mimo_kv_append(dims: mimo_attn_dims, layer_type: int, k, v, cu_newlens, ctx_lens, batch: int, total_new: int,
@@ -416,6 +431,24 @@ def decode(q, k_new, v_new, k_cache, v_cache, ctx_lens, max_ctx: int, layer_type
         workspace = torch.empty(max(nbytes, 16) // 4 + 4, dtype=torch.float32, device=q.device) if nbytes else None
     mimo_attn_decode(dims, layer_type, q, k_new, v_new, k_cache, v_cache, kv_base, ctx_lens, B, max_ctx,
                      split_tokens, sink, out, lse, workspace, stream)
+    return out, lse
+
+
+def decode_append_rope(q, k_new, v_new, positions, k_cache, v_cache, ctx_lens, max_ctx: int, layer_type: int,
+                       rope_theta: float, rotary_dim: int, sink=None, kv_base=None, kv_capacity=None,
+                       split_tokens: int = 0, dims=None, out=None, lse=None, workspace=None, stream=None):
+    dims = dims or make_dims()
+    B = q.shape[0]
+    if out is None:
+        out = torch.empty((B, dims.num_q_heads, dims.head_dim_v), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, dims.num_q_heads), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = mimo_attn_decode_workspace_size(dims, layer_type, B, max_ctx, split_tokens)
+        workspace = torch.empty(max(nbytes, 16) // 4 + 4, dtype=torch.float32, device=q.device) if nbytes else None
+    mimo_attn_decode_append_rope(dims, layer_type, q, k_new, v_new, positions, k_cache, v_cache, kv_base,
+                                 kv_capacity, ctx_lens, B, max_ctx, split_tokens, rope_theta, rotary_dim, sink, out,
+                                 lse, workspace, stream)
     return out, lse
 
 

@@ -388,7 +388,8 @@ int decode_impl(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, c
                 const mimo_kv_pages* pages, const int32_t* ctx_lens, int32_t batch, int32_t max_ctx,
                 int32_t split_tokens, const float* sink, uint16_t* out, float* lse, void* workspace,
                 size_t workspace_bytes, hipStream_t stream, const Fp8Pool* fp8 = nullptr, bool append = false,
-                const int64_t* kv_capacity = nullptr, int max_chunks = mimo::kGaMaxChunks) {
+                const int64_t* kv_capacity = nullptr, int max_chunks = mimo::kGaMaxChunks,
+                const mimo::DecodeRope* rope = nullptr) {
     if (int st = check_dims(dims, layer_type, 2)) return st;
     if (!q || !k_new || !v_new || !ctx_lens || !out)
         return fail(MIMO_ERR_INVALID_ARG, "q, k_new, v_new, ctx_lens and out must be non-NULL");
@@ -433,6 +434,7 @@ int decode_impl(const mimo_attn_dims* dims, int layer_type, const uint16_t* q, c
         a.append_v = const_cast<uint16_t*>(v_cache);
         a.kv_capacity = kv_capacity;
     }
+    if (rope) a.rope = *rope;
     mimo::CheckArgs c;
     c.ctx = ctx_lens;
     c.batch = batch;
@@ -570,6 +572,26 @@ int mimo_attn_decode_append(const mimo_attn_dims* dims, int layer_type, const ui
     return decode_impl(dims, layer_type, q, k_new, v_new, k_cache, v_cache, kv_base, nullptr, ctx_lens, batch,
                        max_ctx, split_tokens, sink, out, lse, workspace, workspace_bytes, stream, nullptr, true,
                        kv_capacity);
+}
+
+int mimo_attn_decode_append_rope(const mimo_attn_dims* dims, int layer_type, const uint16_t* q,
+                                 const uint16_t* k_new, const uint16_t* v_new, const int32_t* positions,
+                                 uint16_t* k_cache, uint16_t* v_cache, const int64_t* kv_base,
+                                 const int64_t* kv_capacity, const int32_t* ctx_lens, int32_t batch, int32_t max_ctx,
+                                 int32_t split_tokens, float rope_theta, int32_t rotary_dim, const float* sink,
+                                 uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+    if (int st = check_dims(dims, layer_type, 2)) return st;
+    if (!positions) return fail(MIMO_ERR_INVALID_ARG, "positions must be non-NULL");
+    if (!std::isfinite(rope_theta) || !(rope_theta > 1.0f))
+        return fail(MIMO_ERR_INVALID_ARG, "rope_theta must be finite and above 1");
+    if (rotary_dim < 64 || rotary_dim > dims->head_dim_qk || rotary_dim % 64)
+        return fail(MIMO_ERR_UNSUPPORTED, "fused decode RoPE needs rotary_dim a multiple of 64 in [64, %d] (got %d)",
+                    dims->head_dim_qk, rotary_dim);
+    mimo::DecodeRope r{positions, rotary_dim / 2, mimo::rope_inv_freq((double)rope_theta, rotary_dim)};
+    return decode_impl(dims, layer_type, q, k_new, v_new, k_cache, v_cache, kv_base, nullptr, ctx_lens, batch,
+                       max_ctx, split_tokens, sink, out, lse, workspace, workspace_bytes, stream, nullptr, true,
+                       kv_capacity, mimo::kGaMaxChunks, &r);
 }
 
 int mimo_attn_decode_paged(const mimo_attn_dims* dims, const uint16_t* q, const uint16_t* k_new,

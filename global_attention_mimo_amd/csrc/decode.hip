@@ -37,6 +37,7 @@
 // dependent table loads; tiles, their order and the arithmetic are those of
 // the contiguous pool.
 #include <mutex>
+#include <type_traits>
 
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -243,6 +244,17 @@ __device__ __forceinline__ void attend_tile(WaveAcc& acc, const bf16x8 (&qf)[kDq
     wave_lds_fence();  // the next tile's V writes come after these reads
 }
 
+// Hooks of the tile loops (used by the fused RoPE): prep() runs once, after
+// the first tiles' loads are issued and before any tile is computed (it may
+// rewrite qf); khook(i, k) runs on tile i's K registers right before tile i
+// is computed.  The defaults do nothing.
+struct NoPrep {
+    __device__ void operator()() const {}
+};
+struct NoKHook {
+    __device__ void operator()(int, u32x4 (&)[12]) const {}
+};
+
 // Runs tiles 0..ntiles-1 (get(i) describes tile i) with the loads of the next
 // D tiles in flight: D + 1 register sets rotate, and tile i+D is issued right
 // before tile i is staged and computed.  Every step issues its loads
@@ -251,11 +263,14 @@ __device__ __forceinline__ void attend_tile(WaveAcc& acc, const bf16x8 (&qf)[kDq
 // memory, and no valid key, so the attention update is an exact no-op).  The
 // count of loads in flight is then the same on every path, which keeps the
 // compiler's vmcnt bookkeeping exact.
-template <int D, class GetTile>
+template <int D, class GetTile, class Prep = NoPrep, class KHook = NoKHook>
 __device__ __forceinline__ void run_tiles(WaveAcc& acc, const bf16x8 (&qf)[kDqk / 32], char* vbuf, int ntiles,
                                           const GetTile& get, const LaneOffsets& lo, int rowv, float c_log2,
-                                          int lane) {
-    if (ntiles <= 0) return;
+                                          int lane, const Prep& prep = Prep{}, const KHook& khook = KHook{}) {
+    if (ntiles <= 0) {
+        prep();
+        return;
+    }
     u32x4 kr[D + 1][12], vr[D + 1][kTile / 4];
 #pragma unroll
     for (int j = 0; j < D; ++j) {
@@ -263,6 +278,7 @@ __device__ __forceinline__ void run_tiles(WaveAcc& acc, const bf16x8 (&qf)[kDqk 
         issue_k(t, lo, kr[j]);
         issue_v(t, lo, rowv, vr[j]);
     }
+    prep();
     for (int i0 = 0; i0 < ntiles; i0 += D + 1) {
 #pragma unroll
         for (int j = 0; j <= D; ++j) {
@@ -270,6 +286,7 @@ __device__ __forceinline__ void run_tiles(WaveAcc& acc, const bf16x8 (&qf)[kDqk 
             issue_k(t, lo, kr[(j + D) % (D + 1)]);
             issue_v(t, lo, rowv, vr[(j + D) % (D + 1)]);
             stage_v(vr[j], vbuf, lane);
+            khook(i0 + j, kr[j]);
             attend_tile(acc, qf, kr[j], vbuf, get(i0 + j).nvalid, c_log2, lane);
         }
     }
@@ -280,20 +297,23 @@ __device__ __forceinline__ void run_tiles(WaveAcc& acc, const bf16x8 (&qf)[kDqk 
 // may be empty), and only the second tile's compute depends on ntiles.  V
 // rows at or past a tile's nvalid are staged as zeros, so its descriptors may
 // cover rows that hold no key yet.
-template <class GetTile>
+template <class GetTile, class Prep = NoPrep, class KHook = NoKHook>
 __device__ __forceinline__ void run_two_tiles(WaveAcc& acc, const bf16x8 (&qf)[kDqk / 32], char* vbuf, int ntiles,
                                               const GetTile& get, const LaneOffsets& lo, int rowv, float c_log2,
-                                              int lane) {
+                                              int lane, const Prep& prep = Prep{}, const KHook& khook = KHook{}) {
     u32x4 ka[12], kb[12], v[kTile / 4];
     const TileSrc t0 = get(0), t1 = get(1);
     issue_k(t0, lo, ka);
     issue_v(t0, lo, rowv, v);
     issue_k(t1, lo, kb);
+    prep();
     stage_v_masked(v, vbuf, lane, t0.nvalid);
     issue_v(t1, lo, rowv, v);  // tile 1's V reuses the registers tile 0's V was staged from
+    khook(0, ka);
     attend_tile(acc, qf, ka, vbuf, ntiles > 0 ? t0.nvalid : 0, c_log2, lane);
     if (ntiles > 1) {
         stage_v_masked(v, vbuf, lane, t1.nvalid);
+        khook(1, kb);
         attend_tile(acc, qf, kb, vbuf, t1.nvalid, c_log2, lane);
     }
 }
@@ -325,15 +345,62 @@ __device__ __forceinline__ float sink_log2(const float* sink, int head, bool& ha
 }
 
 // ---------------------------------------------------------------------------
+// Fused RoPE of a decode step (the rotation of the standalone pass, applied to
+// the decode kernels' registers).  NoRope stands in for the argument in the
+// kernels without it.
+struct NoRope {};
+template <bool ROPE>
+using RopeArg = typename std::conditional<ROPE, DecodeRope, NoRope>::type;
+
+// (cos, sin) of the rd/2 angles p * f_i into tab[2i], tab[2i + 1]: the angle
+// and its sine and cosine in fp64, rounded to fp32, as the standalone pass
+// forms them.  Threads t0, t0 + step, ... share the angles.
+__device__ __forceinline__ void rope_table(float* tab, int p, const RopeFreq& f, int half, int t0, int step) {
+    for (int i = t0; i < half; i += step) {
+        double sn, cs;
+        sincos((double)p * f.f[i], &sn, &cs);
+        tab[2 * i] = (float)cs;
+        tab[2 * i + 1] = (float)sn;
+    }
+}
+
+// 16-byte chunk c (dims 8c .. 8c+7) of a K row after the rotation, from the
+// chunk itself and its pair (the chunk rd/16 after it in the first half of the
+// rotated dims, before it in the second): x' = x cos - y sin in the first
+// half, y' = y cos + x sin in the second (rope_pair's operations), later
+// chunks unchanged.
+__device__ __forceinline__ u32x4 rope_chunk(const u32x4& own, const u32x4& pair, int c, const float* tab, int half) {
+    const int hc = half / 8;
+    if (c >= 2 * hc) return own;
+    const bool first = c < hc;
+    const int i0 = 8 * (first ? c : c - hc);
+    const u32x4 x = first ? own : pair, y = first ? pair : own;
+    u32x4 o;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const int i = i0 + 2 * w;
+        float a0, a1, b0, b1;
+        rope_pair(bf16_word_lo(x[w]), bf16_word_lo(y[w]), tab[2 * i], tab[2 * i + 1], a0, b0);
+        rope_pair(bf16_word_hi(x[w]), bf16_word_hi(y[w]), tab[2 * i + 2], tab[2 * i + 3], a1, b1);
+        o[w] = first ? pack_bf16x2(a0, a1) : pack_bf16x2(b0, b1);
+    }
+    return o;
+}
+
+// ---------------------------------------------------------------------------
 // kShortRing: the ring has at most 224 slots, so every wave owns at most two tiles.
-template <bool kShortRing>
+// ROPE: q and the new token's k arrive unrotated and rotate at rope.pos[b]
+// (with the fused append only); the ring holds rotated keys.
+template <bool kShortRing, bool ROPE>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(kShortRing ? 2 : 1, kShortRing ? 2 : 1))) void swa_decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const uint16_t* __restrict__ ring_k, const uint16_t* __restrict__ ring_v, const int32_t* __restrict__ ctx_lens,
     const float* __restrict__ sink, uint16_t* __restrict__ out, float* __restrict__ lse, int hq, int hkv, int R,
-    float c_log2, float value_scale, uint16_t* __restrict__ app_k, uint16_t* __restrict__ app_v) {
+    float c_log2, float value_scale, uint16_t* __restrict__ app_k, uint16_t* __restrict__ app_v,
+    const RopeArg<ROPE> rope) {
     // V tiles of the 4 waves, reused afterwards for the cross-wave merge.
     __shared__ __attribute__((aligned(1024))) char lds[kSwaLdsBytes];
+    __shared__ __attribute__((aligned(16))) float rtab[ROPE ? kDqk : 4];  // (cos, sin) of the rotated dims
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int b = blockIdx.x, g = blockIdx.y;
@@ -342,10 +409,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 
     // Fused append: this thread's 16 bytes of the new token's K or V row of
     // group g, loaded now and stored once the ring has been read.
-    u32x4 app_row = {};
+    u32x4 app_row = {}, app_pair = {};
+    const u32x4* knew_row = reinterpret_cast<const u32x4*>(k_new + ((size_t)b * hkv + g) * kDqk);
     if (app_k && tid < (kDqk + kDv) / 8)
-        app_row = tid < kDqk / 8 ? reinterpret_cast<const u32x4*>(k_new + ((size_t)b * hkv + g) * kDqk)[tid]
+        app_row = tid < kDqk / 8 ? knew_row[tid]
                                  : reinterpret_cast<const u32x4*>(v_new + ((size_t)b * hkv + g) * kDv)[tid - kDqk / 8];
+    int hc = 0;  // ROPE: K chunks in the first half of the rotated dims
+    if constexpr (ROPE) {
+        hc = rope.half / 8;
+        if (app_k && tid < 2 * hc) app_pair = knew_row[tid < hc ? tid + hc : tid - hc];
+    }
     bf16x8 qf[kDqk / 32];
     load_q(qf, q, b, g, hq, lane);
     // Slot j holds position p-R+((j-p) mod R); all R slots are in the window
@@ -373,10 +446,30 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     const LaneOffsets lo = lane_offsets(lane, g, rowk, rowv);
     WaveAcc acc;
     acc_init(acc);
-    if constexpr (kShortRing)
-        run_two_tiles(acc, qf, lds + wave * kVTileBytes, ntiles, get, lo, rowv, c_log2, lane);
-    else
-        run_tiles<kSwaDepth>(acc, qf, lds + wave * kVTileBytes, ntiles, get, lo, rowv, c_log2, lane);
+    if constexpr (ROPE) {
+        // The angles are formed while the first tiles load; then q rotates in
+        // registers, the new token's K registers right before its tile, and
+        // the row the fused append writes.
+        auto prep = [&]() {
+            rope_table(rtab, rope.pos[b], rope.freq, rope.half, tid, 256);
+            __syncthreads();
+            rope_frags32_rd(qf, rtab, rope.half, lane >> 4);
+            if (app_k && tid < 2 * hc) app_row = rope_chunk(app_row, app_pair, tid, rtab, rope.half);
+        };
+        const int new_idx = ntiles > mine ? mine : -1;
+        auto khook = [&](int i, u32x4 (&kr)[12]) {
+            if (i == new_idx) rope_frags32_rd(kr, rtab, rope.half, lane >> 4);
+        };
+        if constexpr (kShortRing)
+            run_two_tiles(acc, qf, lds + wave * kVTileBytes, ntiles, get, lo, rowv, c_log2, lane, prep, khook);
+        else
+            run_tiles<kSwaDepth>(acc, qf, lds + wave * kVTileBytes, ntiles, get, lo, rowv, c_log2, lane, prep, khook);
+    } else {
+        if constexpr (kShortRing)
+            run_two_tiles(acc, qf, lds + wave * kVTileBytes, ntiles, get, lo, rowv, c_log2, lane);
+        else
+            run_tiles<kSwaDepth>(acc, qf, lds + wave * kVTileBytes, ntiles, get, lo, rowv, c_log2, lane);
+    }
     acc.l += __shfl_xor(acc.l, 16);
     acc.l += __shfl_xor(acc.l, 32);
 
@@ -584,16 +677,21 @@ __device__ __forceinline__ void for_each_page_span(const int32_t* __restrict__ t
 }
 
 // PAGED: pool rows come through block_table (page_shift = log2 P); otherwise
-// sequence b's rows start at kv_base[b].
-template <bool PAGED>
+// sequence b's rows start at kv_base[b].  ROPE (contiguous pool, fused append):
+// q and the new token's k arrive unrotated and rotate at rope.pos[b]; each wave
+// forms the angles of the sequence of each piece it computes.
+template <bool PAGED, bool ROPE>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void ga_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const uint16_t* __restrict__ pool_k, const uint16_t* __restrict__ pool_v, const int64_t* __restrict__ kv_base,
     const int32_t* __restrict__ ctx_lens, int batch, int max_ctx, int min_units, int max_chunks, int hq, int hkv,
     float c_log2, long long* __restrict__ header, float* __restrict__ ws_ml, float* __restrict__ ws_o,
     const int32_t* __restrict__ block_table, int max_blocks, int page_shift, long long num_pages,
-    uint16_t* __restrict__ app_k, uint16_t* __restrict__ app_v, const int64_t* __restrict__ kv_capacity) {
+    uint16_t* __restrict__ app_k, uint16_t* __restrict__ app_v, const int64_t* __restrict__ kv_capacity,
+    const RopeArg<ROPE> rope) {
+    static_assert(!(PAGED && ROPE), "fused RoPE covers the contiguous pool");
     __shared__ __attribute__((aligned(1024))) char lds[kBlockLdsBytes];
+    __shared__ __attribute__((aligned(16))) float rtab_all[ROPE ? 4 * kDqk : 4];  // per wave (cos, sin)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int chunk = blockIdx.x;
@@ -609,20 +707,30 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
         const bool has_new = u1 > npool_units;  // the new-token unit is the sequence's last
         const int k0 = u0 * kTile;
         const int kend = min(min(u1, npool_units) * kTile, p);  // pool keys [k0, kend)
-        if (!PAGED && app_k && has_new && lane < (kDqk + kDv) / 8) {
-            // Fused append: row kv_base[b] + ctx of KV head g.  No piece of this
-            // launch reads that row (the new token comes from k_new / v_new).
-            const int ctx = ctx_lens[b];
-            if (ctx < kv_capacity[b]) {
-                const size_t row = (size_t)kv_base[b] + ctx;
-                if (lane < kDqk / 8)
-                    reinterpret_cast<u32x4*>(app_k + (row * hkv + g) * kDqk)[lane] =
-                        reinterpret_cast<const u32x4*>(k_new + ((size_t)b * hkv + g) * kDqk)[lane];
-                else
-                    reinterpret_cast<u32x4*>(app_v + (row * hkv + g) * kDv)[lane - kDqk / 8] =
-                        reinterpret_cast<const u32x4*>(v_new + ((size_t)b * hkv + g) * kDv)[lane - kDqk / 8];
+        // Fused append: row kv_base[b] + ctx of KV head g.  No piece of this
+        // launch reads that row (the new token comes from k_new / v_new).
+        auto append = [&](const float* rtab) {
+            if (!PAGED && app_k && has_new && lane < (kDqk + kDv) / 8) {
+                const int ctx = ctx_lens[b];
+                if (ctx < kv_capacity[b]) {
+                    const size_t row = (size_t)kv_base[b] + ctx;
+                    const u32x4* knew_row = reinterpret_cast<const u32x4*>(k_new + ((size_t)b * hkv + g) * kDqk);
+                    if (lane < kDqk / 8) {
+                        u32x4 x = knew_row[lane];
+                        if constexpr (ROPE) {
+                            const int hc = rope.half / 8;
+                            if (lane < 2 * hc)
+                                x = rope_chunk(x, knew_row[lane < hc ? lane + hc : lane - hc], lane, rtab, rope.half);
+                        }
+                        reinterpret_cast<u32x4*>(app_k + (row * hkv + g) * kDqk)[lane] = x;
+                    } else {
+                        reinterpret_cast<u32x4*>(app_v + (row * hkv + g) * kDv)[lane - kDqk / 8] =
+                            reinterpret_cast<const u32x4*>(v_new + ((size_t)b * hkv + g) * kDv)[lane - kDqk / 8];
+                    }
+                }
             }
-        }
+        };
+        if constexpr (!ROPE) append(nullptr);
         bf16x8 qf[kDqk / 32];
         load_q(qf, q, b, g, hq, lane);
         const rsrc_t nk = make_rsrc(k_new + (size_t)b * hkv * kDqk, (uint32_t)rowk);
@@ -654,7 +762,25 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
                 if (i < ntiles) return TileSrc{nk, nv, 0, 0, 1};
                 return TileSrc{none, none, 0, 0, 0};
             };
-            run_tiles<kGaDepth>(acc, qf, lds + wave * kVTileBytes, ntiles, get, lo, rowv, c_log2, lane);
+            if constexpr (ROPE) {
+                // The wave's angles for sequence b are formed while its first
+                // tiles load; the new-token tile is the piece's last.
+                float* rtab = rtab_all + wave * kDqk;
+                auto prep = [&]() {
+                    rope_table(rtab, rope.pos[b], rope.freq, rope.half, lane, 64);
+                    wave_lds_fence();
+                    rope_frags32_rd(qf, rtab, rope.half, lane >> 4);
+                    append(rtab);
+                };
+                const int new_idx = has_new ? npool : -1;
+                auto khook = [&](int i, u32x4 (&kr)[12]) {
+                    if (i == new_idx) rope_frags32_rd(kr, rtab, rope.half, lane >> 4);
+                };
+                run_tiles<kGaDepth>(acc, qf, lds + wave * kVTileBytes, ntiles, get, lo, rowv, c_log2, lane, prep,
+                                    khook);
+            } else {
+                run_tiles<kGaDepth>(acc, qf, lds + wave * kVTileBytes, ntiles, get, lo, rowv, c_log2, lane);
+            }
         }
         acc.l += __shfl_xor(acc.l, 16);
         acc.l += __shfl_xor(acc.l, 32);
@@ -963,9 +1089,17 @@ __global__ __launch_bounds__(256) void ga_combine_kernel(const long long* __rest
 hipError_t launch_decode_swa(const DecodeArgs& a, hipStream_t stream) {
     const int R = a.window - 1;
     const bool short_ring = (R + kTile - 1) / kTile + 1 <= 8;
-    hipLaunchKernelGGL(short_ring ? swa_decode_kernel<true> : swa_decode_kernel<false>, dim3(a.batch, a.hkv),
-                       dim3(256), 0, stream, a.q, a.k_new, a.v_new, a.k_cache, a.v_cache, a.ctx_lens, a.sink, a.out,
-                       a.lse, a.hq, a.hkv, R, a.softmax_scale * kLog2e, a.value_scale, a.append_k, a.append_v);
+    if (a.rope.pos) {
+        auto kern = short_ring ? swa_decode_kernel<true, true> : swa_decode_kernel<false, true>;
+        hipLaunchKernelGGL(kern, dim3(a.batch, a.hkv), dim3(256), 0, stream, a.q, a.k_new, a.v_new, a.k_cache, a.v_cache,
+                           a.ctx_lens, a.sink, a.out, a.lse, a.hq, a.hkv, R, a.softmax_scale * kLog2e, a.value_scale,
+                           a.append_k, a.append_v, a.rope);
+        return hipGetLastError();
+    }
+    auto kern = short_ring ? swa_decode_kernel<true, false> : swa_decode_kernel<false, false>;
+    hipLaunchKernelGGL(kern, dim3(a.batch, a.hkv), dim3(256), 0, stream, a.q, a.k_new, a.v_new, a.k_cache, a.v_cache,
+                       a.ctx_lens, a.sink, a.out, a.lse, a.hq, a.hkv, R, a.softmax_scale * kLog2e, a.value_scale,
+                       a.append_k, a.append_v, NoRope{});
     return hipGetLastError();
 }
 
@@ -980,12 +1114,19 @@ hipError_t launch_decode_ga(const DecodeArgs& a, hipStream_t stream) {
                            a.v_cache8, a.kv_base, a.ctx_lens, a.k_scale, a.v_scale, a.batch, a.max_ctx, a.min_units,
                            grid, a.hq, a.hkv, a.softmax_scale * kLog2e, header, ws_ml, ws_o, a.pages.table,
                            a.pages.max_blocks, a.pages.shift, a.pages.num_pages);
+    } else if (a.rope.pos) {
+        auto kern = ga_split_kernel<false, true>;
+        hipLaunchKernelGGL(kern, dim3(grid, 1, (a.hkv + 3) / 4), dim3(256), 0, stream, a.q,
+                           a.k_new, a.v_new, a.k_cache, a.v_cache, a.kv_base, a.ctx_lens, a.batch, a.max_ctx,
+                           a.min_units, grid, a.hq, a.hkv, a.softmax_scale * kLog2e, header, ws_ml, ws_o, nullptr, 0,
+                           0, 0LL, a.append_k, a.append_v, a.kv_capacity, a.rope);
     } else {
-        hipLaunchKernelGGL(a.pages.table ? ga_split_kernel<true> : ga_split_kernel<false>, dim3(grid, 1, (a.hkv + 3) / 4),
-                           dim3(256), 0, stream, a.q, a.k_new, a.v_new, a.k_cache, a.v_cache, a.kv_base, a.ctx_lens,
-                           a.batch, a.max_ctx, a.min_units, grid, a.hq, a.hkv, a.softmax_scale * kLog2e, header, ws_ml,
-                           ws_o, a.pages.table, a.pages.max_blocks, a.pages.shift, a.pages.num_pages,
-                           a.pages.table ? nullptr : a.append_k, a.append_v, a.kv_capacity);
+        auto kern = a.pages.table ? ga_split_kernel<true, false> : ga_split_kernel<false, false>;
+        hipLaunchKernelGGL(kern, dim3(grid, 1, (a.hkv + 3) / 4), dim3(256), 0, stream, a.q, a.k_new, a.v_new, a.k_cache,
+                           a.v_cache, a.kv_base, a.ctx_lens, a.batch, a.max_ctx, a.min_units, grid, a.hq, a.hkv,
+                           a.softmax_scale * kLog2e, header, ws_ml, ws_o, a.pages.table, a.pages.max_blocks,
+                           a.pages.shift, a.pages.num_pages, a.pages.table ? nullptr : a.append_k, a.append_v,
+                           a.kv_capacity, NoRope{});
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

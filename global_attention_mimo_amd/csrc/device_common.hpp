@@ -100,16 +100,17 @@ __device__ __forceinline__ void rope_pair(float x, float y, float c, float s, fl
 __device__ __forceinline__ float bf16_word_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_word_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
-// Rotates Q^T fragments in place: frag[s] holds dims 16s + 8hh .. +7 of one
-// query row (the MFMA B-operand layout of the prefill kernels), so with
-// rd = 32 * NRS rotated dims the pair of dim i = 16s + 8hh + t is dim i + rd/2
-// in frag[s + NRS], same lane and slot.  tab holds the row's token's
-// (cos, sin) pairs, fp32, for i = 0 .. rd/2 - 1.
-template <int NRS>
-__device__ __forceinline__ void rope_frags(bf16x8* frag, const float* tab, int hh) {
+// Rotates head-vector fragments in place: frag[s] holds dims STRIDE*s + 8*sub
+// .. +7 of one row (the prefill kernels' Q^T fragments: STRIDE 16, sub = hh;
+// the decode kernels' Q^T and K fragments: STRIDE 32, sub = lane/16), so with
+// rd = 2 * STRIDE * NRS rotated dims the pair of dim i = STRIDE*s + 8*sub + t
+// is dim i + rd/2 in frag[s + NRS], same lane and slot.  tab holds the row's
+// token's (cos, sin) pairs, fp32, for i = 0 .. rd/2 - 1.
+template <int NRS, int STRIDE = 16, class F>
+__device__ __forceinline__ void rope_frags(F* frag, const float* tab, int sub) {
 #pragma unroll
     for (int s = 0; s < NRS; ++s) {
-        const f32x4* cs = reinterpret_cast<const f32x4*>(tab + 2 * (16 * s + 8 * hh));
+        const f32x4* cs = reinterpret_cast<const f32x4*>(tab + 2 * (STRIDE * s + 8 * sub));
         const f32x4 c0 = cs[0], c1 = cs[1], c2 = cs[2], c3 = cs[3];  // (cos, sin) of 8 consecutive dims
         const float c[8] = {c0[0], c0[2], c1[0], c1[2], c2[0], c2[2], c3[0], c3[2]};
         const float sn[8] = {c0[1], c0[3], c1[1], c1[3], c2[1], c2[3], c3[1], c3[3]};
@@ -123,8 +124,8 @@ __device__ __forceinline__ void rope_frags(bf16x8* frag, const float* tab, int h
             xo[w] = pack_bf16x2(a0, a1);
             yo[w] = pack_bf16x2(b0, b1);
         }
-        frag[s] = __builtin_bit_cast(bf16x8, xo);
-        frag[s + NRS] = __builtin_bit_cast(bf16x8, yo);
+        frag[s] = __builtin_bit_cast(F, xo);
+        frag[s + NRS] = __builtin_bit_cast(F, yo);
     }
 }
 
@@ -137,6 +138,17 @@ __device__ __forceinline__ void rope_frags_rd(bf16x8* frag, const float* tab, in
         case 4: rope_frags<4>(frag, tab, hh); break;
         case 5: rope_frags<5>(frag, tab, hh); break;
         case 6: rope_frags<6>(frag, tab, hh); break;
+        default: break;
+    }
+}
+
+// The decode layout (STRIDE 32): rd a multiple of 64, at most 192.
+template <class F>
+__device__ __forceinline__ void rope_frags32_rd(F* frag, const float* tab, int rope_half, int sub) {
+    switch (rope_half / 32) {
+        case 1: rope_frags<1, 32>(frag, tab, sub); break;
+        case 2: rope_frags<2, 32>(frag, tab, sub); break;
+        case 3: rope_frags<3, 32>(frag, tab, sub); break;
         default: break;
     }
 }

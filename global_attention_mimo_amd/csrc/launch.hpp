@@ -47,6 +47,21 @@ struct PrefillArgs {
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_chunk(const PrefillArgs& a, hipStream_t stream);
 
+// RoPE frequencies f_i = theta^(-2i/rd), i < rd/2 <= 96, formed on the host
+// in double (every rotation in the library uses the same values).
+struct RopeFreq {
+    double f[96];
+};
+RopeFreq rope_inv_freq(double theta, int rotary_dim);
+
+// Fused RoPE of a decode step: the queries and the new token's keys of
+// sequence b rotate at position pos[b] (half = rotary_dim / 2).
+struct DecodeRope {
+    const int32_t* pos;
+    int half;
+    RopeFreq freq;
+};
+
 struct DecodeArgs {
     const uint16_t* q;
     const uint16_t* k_new;
@@ -75,6 +90,8 @@ struct DecodeArgs {
     const int64_t* kv_capacity = nullptr;
     // GA: most chunks the split grid may use (sizes the grid and the workspace).
     int max_chunks = 0;
+    // Fused RoPE (with the fused append only): rope.pos null means none.
+    DecodeRope rope{};
 };
 
 // GA decode work plan.  Sequence b's keys form units: ceil(p_b / 32) tiles of

@@ -27,10 +27,7 @@ namespace {
 constexpr int kD = 192;
 
 
-// The frequencies f_i = theta^(-2i/rd), formed once on the host in double.
-struct InvFreq {
-    double f[kD / 2];
-};
+using InvFreq = RopeFreq;
 
 __global__ __launch_bounds__(256) void rope_kernel(uint16_t* __restrict__ q, uint16_t* __restrict__ k,
                                                    const int32_t* __restrict__ positions, int hq, int hkv,
@@ -141,13 +138,15 @@ __global__ __launch_bounds__(256) void rope_prep_kernel(const uint16_t* __restri
     }
 }
 
-InvFreq inv_freq(double theta, int rd) {
-    InvFreq freq{};
+InvFreq inv_freq(double theta, int rd) { return rope_inv_freq(theta, rd); }
+
+}  // namespace
+
+RopeFreq rope_inv_freq(double theta, int rd) {
+    RopeFreq freq{};
     for (int i = 0; i < rd / 2; ++i) freq.f[i] = std::pow(theta, -2.0 * i / rd);
     return freq;
 }
-
-}  // namespace
 
 hipError_t launch_rope_prep(const RopePrepArgs& a, hipStream_t stream) {
     if (a.total_tokens <= 0) return hipSuccess;

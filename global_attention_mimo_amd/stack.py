@@ -46,6 +46,12 @@ class HybridStack:
     hq: int = synth.HQ
     hkv: int = synth.HKV
     fused: bool = True  # decode steps append through mimo_attn_decode_append
+    # Rotary embedding of each decode step's q and k_new at position ctx[b]:
+    # None (inputs taken as rotated already), "fused" (mimo_attn_decode_append_rope)
+    # or "separate" (mimo_rope_apply in place, then the decode call).
+    rope_mode: Optional[str] = None
+    rope_theta: float = 5e6
+    rotary_dim: int = 64
     layer_types: List[int] = field(init=False)
     caches: List[LayerCache] = field(init=False)
 
@@ -96,10 +102,21 @@ class HybridStack:
 
     def decode_layer(self, layer: int, q, k_new, v_new, sink, out, lse=None, stream=None):
         """One decode step of one layer: attend over the cache + new token, then append
-        it (one fused library call, or decode then append when `fused` is off)."""
+        it (one fused library call, or decode then append when `fused` is off); with
+        rope_mode set, q and k_new are rotated first (inside that call when "fused",
+        in place by a separate pass when "separate")."""
         lt = self.layer_types[layer]
         c = self.caches[layer]
         ws = self.workspace if lt == GA else None
+        if self.rope_mode == "fused":
+            B.mimo_attn_decode_append_rope(self.dims, lt, q, k_new, v_new, self.ctx, c.k, c.v, c.kv_base,
+                                           c.kv_capacity, self.ctx, self.batch, self.max_ctx, self.split,
+                                           self.rope_theta, self.rotary_dim, sink, out, lse, ws, stream)
+            return
+        if self.rope_mode == "separate":
+            B.mimo_rope_apply(self.dims, q, k_new, self.ctx, self.batch, self.rope_theta, self.rotary_dim, stream)
+        elif self.rope_mode is not None:
+            raise ValueError(f"rope_mode {self.rope_mode!r} is not None, 'fused' or 'separate'")
         if self.fused:
             B.mimo_attn_decode_append(self.dims, lt, q, k_new, v_new, c.k, c.v, c.kv_base, c.kv_capacity, self.ctx,
                                       self.batch, self.max_ctx, self.split, sink, out, lse, ws, stream)

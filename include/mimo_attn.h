@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define MIMO_ATTN_ABI_VERSION 12
+#define MIMO_ATTN_ABI_VERSION 13
 
 /* Layer type: which key set a query sees (model doc, Key features; config
  * layer_types). */
@@ -586,6 +586,40 @@ int mimo_attn_prefill_chunk_rope(const mimo_attn_dims* dims, int layer_type,
                                  float rope_theta, int32_t rotary_dim, const float* sink,
                                  uint16_t* out, float* lse, uint16_t* k_rot,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * A decode step with the rotary embedding fused in (ABI version 13; model
+ * doc, MiMoV2FlashConfig: rope_parameters / rope_theta;
+ * MiMoV2FlashModel.forward: position_ids, past_key_values): the outputs and
+ * the caches afterwards are those of mimo_rope_apply on copies of q and k_new
+ * (one token per sequence) followed by mimo_attn_decode_append over the
+ * rotated copies, bit for bit, in one launch (GA: the split kernel and its
+ * combine).  The queries rotate in registers as the kernels load them, the
+ * new token's key where it joins the attention and again where the fused
+ * append writes it, so the caches hold post-RoPE keys; each workgroup forms
+ * the angles of its sequence (fp64, as mimo_rope_apply does).
+ *
+ * Arguments as for mimo_attn_decode_append (bf16 ring or contiguous GA pool),
+ * with q and k_new before the rotation (only read), plus
+ *   positions    [batch] int32 (device): the position id of sequence b's new
+ *                token (normally ctx_lens[b]).
+ *   rope_theta   > 1 (host).
+ *   rotary_dim   a multiple of 64 in [64, 192] (host): the decode kernels hold
+ *                dims 32s + 8j .. +7 of a head in one register group, so the
+ *                pair (i, i + rotary_dim/2) lies in one lane for these
+ *                values; others are MIMO_ERR_UNSUPPORTED (use
+ *                mimo_rope_apply and mimo_attn_decode_append).
+ * Errors as for mimo_attn_decode_append; NULL positions or a rope_theta that
+ * is not finite and above 1 is MIMO_ERR_INVALID_ARG.
+ */
+int mimo_attn_decode_append_rope(const mimo_attn_dims* dims, int layer_type,
+                                 const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                                 const int32_t* positions, uint16_t* k_cache, uint16_t* v_cache,
+                                 const int64_t* kv_base, const int64_t* kv_capacity, const int32_t* ctx_lens,
+                                 int32_t batch, int32_t max_ctx, int32_t split_tokens,
+                                 float rope_theta, int32_t rotary_dim, const float* sink,
+                                 uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
 
 /*
  * Check mode (see the conventions above).  mimo_attn_set_check switches it on

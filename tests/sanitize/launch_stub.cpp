@@ -7,6 +7,7 @@
 // own rules (check_rules.hpp) on the host, so that with HOST pointers in place
 // of device ones the gate in front of every launch can be exercised on the
 // CPU.  Test infrastructure only.
+#include <cmath>
 #include <cstdint>
 
 #include "../../global_attention_mimo_amd/csrc/check_rules.hpp"
@@ -25,6 +26,11 @@ hipError_t launch_kv_append(const AppendArgs&, hipStream_t) { return hipErrorNoD
 hipError_t launch_prefill_backward(const BackwardArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_rope(const RopeArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_rope_prep(const RopePrepArgs&, hipStream_t) { return hipErrorNoDevice; }
+RopeFreq rope_inv_freq(double theta, int rd) {
+    RopeFreq f{};
+    for (int i = 0; i < rd / 2 && i < 96; ++i) f.f[i] = std::pow(theta, -2.0 * i / rd);
+    return f;
+}
 hipError_t run_check(const CheckArgs& a, hipStream_t, bool* gated, uint32_t* bits) {
     *bits = check_rules(a, 0, 1);
     *gated = true;

@@ -42,7 +42,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_version_and_status_strings(L):
-    assert B.mimo_abi_version() == 12
+    assert B.mimo_abi_version() == 13
     assert B.mimo_status_string(0) == "MIMO_OK"
     assert B.mimo_status_string(3) == "MIMO_ERR_WORKSPACE"
     assert B.mimo_status_string(99) == "MIMO_ERR_UNKNOWN"
@@ -178,6 +178,34 @@ def decode_append_call(L, layer=1, q=FAKE, kc=FAKE, base=FAKE, cap=FAKE, ctx=FAK
 ])
 def test_decode_append_rejects(L, case, status):
     assert decode_append_call(L, **case) == status
+
+
+def decode_append_rope_call(L, layer=1, q=FAKE, pos=FAKE, kc=FAKE, base=FAKE, cap=FAKE, ctx=FAKE, batch=2,
+                            theta=1e4, rd=64):
+    d = B.make_dims()
+    return L.mimo_attn_decode_append_rope(ctypes.byref(d), layer, q, FAKE, FAKE, pos, kc, FAKE, base, cap, ctx,
+                                          batch, 100, 0, theta, rd, None, FAKE, None, None, 0, None)
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(layer=5), B.MIMO_ERR_INVALID_ARG),
+    (dict(q=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(pos=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(kc=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(batch=0), B.MIMO_ERR_INVALID_ARG),
+    (dict(cap=None), B.MIMO_ERR_INVALID_ARG),
+    (dict(theta=1.0), B.MIMO_ERR_INVALID_ARG),
+    (dict(theta=float("inf")), B.MIMO_ERR_INVALID_ARG),
+    (dict(theta=float("nan")), B.MIMO_ERR_INVALID_ARG),
+    (dict(rd=32), B.MIMO_ERR_UNSUPPORTED),      # the pair would sit in another lane: use mimo_rope_apply
+    (dict(rd=96), B.MIMO_ERR_UNSUPPORTED),
+    (dict(rd=0), B.MIMO_ERR_UNSUPPORTED),
+    (dict(rd=256), B.MIMO_ERR_UNSUPPORTED),
+    (dict(layer=0, rd=100), B.MIMO_ERR_UNSUPPORTED),
+])
+def test_decode_append_rope_rejects(L, case, status):
+    assert decode_append_rope_call(L, **case) == status
+    assert B.mimo_last_error() != ""
 
 
 def ga_workspace_expected(batch, max_ctx, split, hq=64):

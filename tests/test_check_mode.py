@@ -198,6 +198,10 @@ def test_decode_append_capacity(L, ctx, cap, bits):
     st = L.mimo_attn_decode_append(dims(), 1, FAKE, FAKE, FAKE, FAKE, FAKE, p(base), p(cap), p(ctx), 2, 200, 0, None,
                                    FAKE, None, FAKE, HUGE_WS, None)
     expect(L, st, bits)
+    # the same step with the rotation fused in is checked alike
+    st = L.mimo_attn_decode_append_rope(dims(), 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, p(base), p(cap), p(ctx), 2,
+                                        200, 0, 1e4, 64, None, FAKE, None, FAKE, HUGE_WS, None)
+    expect(L, st, bits)
     # without append, the capacity does not enter
     st = L.mimo_attn_decode(dims(), 1, FAKE, FAKE, FAKE, FAKE, FAKE, p(base), p(ctx), 2, 200, 0, None, FAKE, None,
                             FAKE, HUGE_WS, None)
