@@ -62,13 +62,20 @@ SUITES = {
     "next-rows": ("--steps 1 --warmup 1 --no-cpu-baseline --no-hybrid",
                   "--steps 1 --warmup 0 --no-cpu-baseline --no-hybrid"),
 }
+# Where the waves' time goes: per-wave cycles split into waiting on
+# dependencies (s_waitcnt: loads, LDS, barriers), ready but not issued (the
+# unit it needs is busy, e.g. the matrix core or the memory pipeline) and
+# issuing, the last by instruction kind.
+STALL_COUNTERS = ["SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU",
+                  "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_MISC", "SQ_ACTIVE_INST_VMEM"]
 PASSES = {
     "trace": ["--kernel-trace", "--stats"],
     "fetch": ["--pmc", "FETCH_SIZE"],
     "write": ["--pmc", "WRITE_SIZE"],
     "mfma": ["--pmc", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "GRBM_GUI_ACTIVE"],
+    "stalls": ["--pmc", *STALL_COUNTERS],
 }
-PASS_LIMIT_S = {"trace": 900, "fetch": 600, "write": 600, "mfma": 600}
+PASS_LIMIT_S = {"trace": 900, "fetch": 600, "write": 600, "mfma": 600, "stalls": 600}
 
 TITLES = {
     "step": "one bench step of the hybrid-attention hot path",
@@ -147,13 +154,13 @@ def code_digest(paths: Iterable[str], root: str = ROOT) -> str:
 def pass_command(suite: str, which: str, out: str, python: str = sys.executable) -> List[str]:
     trace_args, pmc_args = SUITES[suite]
     bench_args = shlex.split(trace_args if which == "trace" else pmc_args)
-    if which in ("fetch", "write", "mfma") and "--copy-calibration" not in bench_args:
+    if which != "trace" and "--copy-calibration" not in bench_args:
         bench_args.append("--copy-calibration")
     return (["rocprofv3", *PASSES[which], "--output-format", "csv", "-d", os.path.join(out, which), "-o", "run",
              "--", python, os.path.join(ROOT, "bench.py"), *bench_args])
 
 
-def run(suite: str, out: str, passes: Iterable[str] = ("trace", "fetch", "write", "mfma")) -> None:
+def run(suite: str, out: str, passes: Iterable[str] = ("trace", "fetch", "write", "mfma", "stalls")) -> None:
     """Runs the profiler passes one after another (each under its own time limit,
     output to <out>/<pass>.log); stops at the first pass that fails."""
     os.makedirs(out, exist_ok=True)
@@ -267,6 +274,15 @@ def summarize(out: str) -> dict:
             med = res["trace"].get(k, {}).get("median_us")
             res["mfma"][k] = {"insts_mfma": _mean(insts.get(k, [])), "busy": mfma_busy(_mean(busy[k]), g),
                               "clock_ghz": (g / XCDS) / (med * 1e3) if med and med > 50 else None}
+    srows = _csv_rows(os.path.join(out, "stalls"), "counter_collection.csv")
+    if srows:
+        vals = {c: counter_values(srows, c) for c in STALL_COUNTERS}
+        res["stalls"] = {}
+        for k, cyc in vals["SQ_WAVE_CYCLES"].items():
+            if not is_library_kernel(k) or _mean(cyc) <= 0:
+                continue
+            w = _mean(cyc)
+            res["stalls"][k] = {"wave_cycles": w, **{c: _mean(vals[c].get(k, [])) / w for c in STALL_COUNTERS[1:]}}
     return res
 
 
@@ -305,6 +321,19 @@ def write_markdown(suite: str, out: str, res: dict, path: str) -> None:
         for k, v in sorted(res["mfma"].items(), key=lambda kv: -kv[1]["insts_mfma"]):
             L.append(f"| `{short_name(k)}` | {v['insts_mfma']:.0f} | {100 * v['busy']:.1f}% | "
                      f"{_fmt(v['clock_ghz'], '.2f')} |")
+    if res.get("stalls"):
+        L += ["", "## Where the waves' cycles go (fractions of SQ_WAVE_CYCLES per dispatch)", "",
+              "Per-wave cycles (several waves share a SIMD, so these are not SIMD time): waiting on dependencies "
+              "(SQ_WAIT_ANY: loads, LDS, barriers), ready but not issued (SQ_WAIT_INST_ANY: the unit it needs is "
+              "busy -- the matrix core, the memory pipeline -- or another wave issues), and issuing "
+              "(SQ_ACTIVE_INST_ANY), the last split by kind (VALU includes MFMA).", "",
+              "| kernel | waiting on data | ready, not issued | issuing | VALU+MFMA | LDS | VMEM | other |",
+              "|---|---|---|---|---|---|---|---|"]
+        for k, v in sorted(res["stalls"].items(), key=lambda kv: -kv[1]["wave_cycles"]):
+            L.append(f"| `{short_name(k)}` | {100 * v['SQ_WAIT_ANY']:.1f}% | {100 * v['SQ_WAIT_INST_ANY']:.1f}% | "
+                     f"{100 * v['SQ_ACTIVE_INST_ANY']:.1f}% | {100 * v['SQ_ACTIVE_INST_VALU']:.1f}% | "
+                     f"{100 * v['SQ_ACTIVE_INST_LDS']:.1f}% | {100 * v['SQ_ACTIVE_INST_VMEM']:.1f}% | "
+                     f"{100 * v['SQ_ACTIVE_INST_MISC']:.1f}% |")
     with open(path, "w") as f:
         f.write("\n".join(L) + "\n")
 
@@ -345,7 +374,7 @@ def main(argv=None):
     ap.add_argument("action", choices=("run", "report", "all"))
     ap.add_argument("--suite", choices=tuple(SUITES), default="step")
     ap.add_argument("--out", required=True, help="directory for the profiler output (e.g. under gpurun_out/)")
-    ap.add_argument("--passes", default="trace,fetch,write,mfma")
+    ap.add_argument("--passes", default="trace,fetch,write,mfma,stalls")
     ap.add_argument("--md", default=None, help="markdown summary path (default: the suite's file under profiles/)")
     a = ap.parse_args(argv)
     if a.action in ("run", "all"):

@@ -1,7 +1,8 @@
 """The rocprof harness's parser and report writer on a small committed fixture
-(tests/golden/rocprof/: rows cut from a real rocprofv3 --output-format csv run
-of the bench step on an MI355X -- kernel trace, FETCH_SIZE, WRITE_SIZE and
-MFMA counter passes, including the 1 GiB calibration copy).  CPU only; the
+(tests/golden/rocprof/: rows cut from real rocprofv3 --output-format csv runs
+on an MI355X -- kernel trace, FETCH_SIZE, WRITE_SIZE and MFMA counter passes of
+the bench step, including the 1 GiB calibration copy, and a pass of the eight
+stall counters over the GA and SWA prefill and the GA decode split kernel).  CPU only; the
 expected figures are worked out by hand from the fixture rows quoted here."""
 import json
 import os
@@ -117,3 +118,31 @@ def test_bench_reads_the_committed_traffic_record():
         assert bench.measured_traffic() == pytest.approx(rec["read_bytes"] + rec["write_bytes"])
     else:
         assert bench.measured_traffic() is None
+
+
+def test_stall_fractions_from_fixture():
+    """tests/golden/rocprof/stalls: one dispatch each of the GA prefill, the streaming SWA prefill and the GA
+    split kernel (rows of a real --pmc run of the eight stall counters), plus a torch copy that is not reported."""
+    res = prof.summarize(FIX)
+    s = {prof.short_name(k): v for k, v in res["stalls"].items()}
+    assert set(s) == {"prefill_kernel<8, 1, 64, false, 2, false, false, false>", "swa_stream_kernel<false, false>",
+                      "ga_split_kernel<false>"}
+    p = s["prefill_kernel<8, 1, 64, false, 2, false, false, false>"]
+    # dispatch 15: SQ_WAVE_CYCLES 16968076230, SQ_WAIT_ANY 4509090417, SQ_WAIT_INST_ANY 6215074302,
+    # SQ_ACTIVE_INST_ANY 6243911511, SQ_ACTIVE_INST_VALU 3961405721
+    assert p["wave_cycles"] == 16968076230
+    assert p["SQ_WAIT_ANY"] == pytest.approx(4509090417 / 16968076230)
+    assert p["SQ_WAIT_INST_ANY"] == pytest.approx(6215074302 / 16968076230)
+    assert p["SQ_ACTIVE_INST_ANY"] == pytest.approx(6243911511 / 16968076230)
+    assert p["SQ_ACTIVE_INST_VALU"] == pytest.approx(3961405721 / 16968076230)
+    g = s["ga_split_kernel<false>"]  # dispatch 97: 58552621 of 73456964 wave cycles ready but not issued
+    assert g["SQ_WAIT_INST_ANY"] == pytest.approx(58552621 / 73456964)
+
+
+def test_report_writes_the_stall_table(tmp_path):
+    res = prof.summarize(FIX)
+    md = tmp_path / "r.md"
+    prof.write_markdown("step", FIX, res, str(md))
+    text = md.read_text()
+    assert "## Where the waves' cycles go" in text
+    assert "| `swa_stream_kernel<false, false>` | 38.4% |" in text  # 133432366 / 347661741
