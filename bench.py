@@ -499,6 +499,18 @@ def hybrid_rows(dims, decode_steps=64):
         "kv_cache_bytes": kvb["hybrid"], "kv_cache_bytes_all_ga": kvb["all_ga"]}}
 
 
+def copy_calibration(dev):
+    """A plain 1 GiB device-to-device copy, for scaling the HBM byte counters of
+    a profiled run (its FETCH_SIZE / WRITE_SIZE against the known bytes)."""
+    src = torch.empty(1 << 29, dtype=torch.int16, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)  # reads 1 GiB, writes 1 GiB
+    torch.cuda.synchronize()
+    del src, dst
+    log("copy calibration: 1 GiB device-to-device copy done")
+
+
 def _time_ms(call, reps):
     call()
     torch.cuda.synchronize()
@@ -698,6 +710,8 @@ def main():
     dev = "cuda"
     torch.cuda.set_device(0)
     if args.hybrid_only:
+        if args.copy_calibration:
+            copy_calibration(dev)
         log("hybrid stack: 48-layer prefill and decode")
         print(json.dumps({"metric": METRIC, "n_gpus": 1, "data": "synthetic", **hybrid_rows(B.make_dims())}),
               flush=True)
@@ -728,13 +742,7 @@ def main():
         f"workspace {ws_bytes / 1e6:.0f} MB")
 
     if args.copy_calibration:
-        src = torch.empty(1 << 29, dtype=torch.int16, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)  # reads 1 GiB, writes 1 GiB
-        torch.cuda.synchronize()
-        del src, dst
-        log("copy calibration: 1 GiB device-to-device copy done")
+        copy_calibration(dev)
 
     stream = torch.cuda.current_stream()
     names = ["prefill_swa", "prefill_ga", "decode_swa", "append_swa", "decode_ga", "append_ga", "ctx_advance"]
