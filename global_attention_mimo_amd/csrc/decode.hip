@@ -352,16 +352,31 @@ struct NoRope {};
 template <bool ROPE>
 using RopeArg = typename std::conditional<ROPE, DecodeRope, NoRope>::type;
 
-// (cos, sin) of the rd/2 angles p * f_i into tab[2i], tab[2i + 1]: the angle
-// and its sine and cosine in fp64, rounded to fp32, as the standalone pass
-// forms them.  Threads t0, t0 + step, ... share the angles.
-__device__ __forceinline__ void rope_table(float* tab, int p, const RopeFreq& f, int half, int t0, int step) {
-    for (int i = t0; i < half; i += step) {
-        double sn, cs;
-        sincos((double)p * f.f[i], &sn, &cs);
-        tab[2 * i] = (float)cs;
-        tab[2 * i + 1] = (float)sn;
+// A lane's frequencies for the angle table, f_lane and f_(lane+64) (rd/2 <=
+// 96), loaded once per kernel so that no table waits on them.
+struct RopeLane {
+    double f0, f1;
+};
+__device__ __forceinline__ RopeLane rope_lane_freq(const RopeFreq& f, int half, int lane) {
+    return RopeLane{lane < half ? f.f[lane] : 0.0, lane + 64 < half ? f.f[lane + 64] : 0.0};
+}
+
+// One wave writes the (cos, sin) of the rd/2 angles p * f_i into its own
+// table tab[2i], tab[2i + 1]: the angle and its sine and cosine in fp64,
+// rounded to fp32, as the standalone pass forms them.
+__device__ __forceinline__ void rope_table_wave(float* tab, int p, const RopeLane& fl, int half, int lane) {
+    double sn, cs;
+    if (lane < half) {
+        sincos((double)p * fl.f0, &sn, &cs);
+        tab[2 * lane] = (float)cs;
+        tab[2 * lane + 1] = (float)sn;
     }
+    if (lane + 64 < half) {
+        sincos((double)p * fl.f1, &sn, &cs);
+        tab[2 * (lane + 64)] = (float)cs;
+        tab[2 * (lane + 64) + 1] = (float)sn;
+    }
+    wave_lds_fence();
 }
 
 // 16-byte chunk c (dims 8c .. 8c+7) of a K row after the rotation, from the
@@ -400,7 +415,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     const RopeArg<ROPE> rope) {
     // V tiles of the 4 waves, reused afterwards for the cross-wave merge.
     __shared__ __attribute__((aligned(1024))) char lds[kSwaLdsBytes];
-    __shared__ __attribute__((aligned(16))) float rtab[ROPE ? kDqk : 4];  // (cos, sin) of the rotated dims
+    __shared__ __attribute__((aligned(16))) float rtab_all[ROPE ? 4 * kDqk : 4];  // per wave (cos, sin)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int b = blockIdx.x, g = blockIdx.y;
@@ -415,9 +430,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
         app_row = tid < kDqk / 8 ? knew_row[tid]
                                  : reinterpret_cast<const u32x4*>(v_new + ((size_t)b * hkv + g) * kDv)[tid - kDqk / 8];
     int hc = 0;  // ROPE: K chunks in the first half of the rotated dims
+    RopeLane fl{};
+    int rpos = 0;
     if constexpr (ROPE) {
         hc = rope.half / 8;
         if (app_k && tid < 2 * hc) app_pair = knew_row[tid < hc ? tid + hc : tid - hc];
+        fl = rope_lane_freq(rope.freq, rope.half, lane);
+        rpos = rope.pos[b];
     }
     bf16x8 qf[kDqk / 32];
     load_q(qf, q, b, g, hq, lane);
@@ -447,12 +466,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     WaveAcc acc;
     acc_init(acc);
     if constexpr (ROPE) {
-        // The angles are formed while the first tiles load; then q rotates in
-        // registers, the new token's K registers right before its tile, and
-        // the row the fused append writes.
+        // Each wave forms the angles while its first tiles load; then q rotates
+        // in registers, the new token's K registers right before its tile, and
+        // (wave 0) the row the fused append writes.
+        float* rtab = rtab_all + wave * kDqk;
         auto prep = [&]() {
-            rope_table(rtab, rope.pos[b], rope.freq, rope.half, tid, 256);
-            __syncthreads();
+            rope_table_wave(rtab, rpos, fl, rope.half, lane);
             rope_frags32_rd(qf, rtab, rope.half, lane >> 4);
             if (app_k && tid < 2 * hc) app_row = rope_chunk(app_row, app_pair, tid, rtab, rope.half);
         };
@@ -702,7 +721,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     const int rowk = hkv * kDqk * 2, rowv = hkv * kDv * 2;
     const LaneOffsets lo = lane_offsets(lane, g, rowk, rowv);
     const rsrc_t none = make_rsrc(k_new, 0);
+    RopeLane fl{};
+    if constexpr (ROPE) fl = rope_lane_freq(rope.freq, rope.half, lane);
     for_each_piece(pl, ctx_lens, max_ctx, [&](int b, int u0, int u1, int p) {
+        int rpos = 0;
+        if constexpr (ROPE) rpos = rope.pos[b];
         const int npool_units = (p + kTile - 1) / kTile;
         const bool has_new = u1 > npool_units;  // the new-token unit is the sequence's last
         const int k0 = u0 * kTile;
@@ -767,8 +790,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
                 // tiles load; the new-token tile is the piece's last.
                 float* rtab = rtab_all + wave * kDqk;
                 auto prep = [&]() {
-                    rope_table(rtab, rope.pos[b], rope.freq, rope.half, lane, 64);
-                    wave_lds_fence();
+                    rope_table_wave(rtab, rpos, fl, rope.half, lane);
                     rope_frags32_rd(qf, rtab, rope.half, lane >> 4);
                     append(rtab);
                 };
