@@ -20,8 +20,9 @@
 // current one is computed.
 //
 // SWA decode (one workgroup per (sequence, KV group)): the ring slots are
-// split into 32-key tiles over the 4 waves, the new token is one more tile,
-// and the waves' partial (m, l, O) are merged in LDS together with the sink.
+// split into 32-key tiles over the 4 waves, and the waves' partial (m, l, O)
+// are merged in LDS together with the sink and the new token, whose score the
+// merge threads form as a dot product.
 //
 // GA decode: split-K.  Workgroup (split s, sequence b) covers keys
 // [s*C, (s+1)*C) of the sequence with one wave per KV group, streaming pool
@@ -292,9 +293,9 @@ __device__ __forceinline__ void run_tiles(WaveAcc& acc, const bf16x8 (&qf)[kDqk 
     }
 }
 
-// At most two tiles (a wave's share of a ring of up to 224 slots plus the
-// new token): both tiles' loads are issued up front, unconditionally (tile 1
-// may be empty), and only the second tile's compute depends on ntiles.  V
+// At most two tiles (a wave's share of a ring of up to 256 slots): both
+// tiles' loads are issued up front, unconditionally (tile 1 may be empty), and
+// only the second tile's compute depends on ntiles.  V
 // rows at or past a tile's nvalid are staged as zeros, so its descriptors may
 // cover rows that hold no key yet.
 template <class GetTile, class Prep = NoPrep, class KHook = NoKHook>
@@ -402,8 +403,47 @@ __device__ __forceinline__ u32x4 rope_chunk(const u32x4& own, const u32x4& pair,
     return o;
 }
 
+// The rotation of a merge thread's strided values v[m] = dim jd + 16m of a
+// head (q and the new key): with rd/2 = 16 HM the pair of dim d < rd/2 is
+// v[m + HM], and each rotated value is rounded to bf16 as the standalone pass
+// stores it.
+template <int HM>
+__device__ __forceinline__ void rope_strided(float (&qv)[kDqk / 16], float (&kv)[kDqk / 16], const float* tab,
+                                             int jd) {
+    float qr[kDqk / 16], kr[kDqk / 16];
+#pragma unroll
+    for (int m = 0; m < kDqk / 16; ++m) {
+        qr[m] = qv[m];
+        kr[m] = kv[m];
+    }
+#pragma unroll
+    for (int m = 0; m < HM; ++m) {
+        const int i = jd + 16 * m;
+        const float c = tab[2 * i], sn = tab[2 * i + 1];
+        float x, y;
+        rope_pair(qv[m], qv[m + HM], c, sn, x, y);
+        qr[m] = bf16_word_lo(pack_bf16x2(x, 0.0f));
+        qr[m + HM] = bf16_word_lo(pack_bf16x2(y, 0.0f));
+        rope_pair(kv[m], kv[m + HM], c, sn, x, y);
+        kr[m] = bf16_word_lo(pack_bf16x2(x, 0.0f));
+        kr[m + HM] = bf16_word_lo(pack_bf16x2(y, 0.0f));
+    }
+#pragma unroll
+    for (int m = 0; m < kDqk / 16; ++m) {
+        qv[m] = qr[m];
+        kv[m] = kr[m];
+    }
+}
+
 // ---------------------------------------------------------------------------
-// kShortRing: the ring has at most 224 slots, so every wave owns at most two tiles.
+// SWA decode: the ring's 32-key tiles go to the 4 waves; the new token joins in
+// the merge instead of as a tile of its own (a one-key MFMA tile would double
+// the work of the wave holding it): merge thread (local head tid/16, j =
+// tid%16) holds dims j + 16m (m < 12) of the head's query and of the new key
+// and 8 values of the new value row, and the 16 threads of a head sum the dot
+// product.  The stride of 16 keeps each rotated pair (i, i + rd/2 with rd/2 a
+// multiple of 32) inside one thread.
+// kShortRing: the ring has at most 256 slots, so every wave owns at most two tiles.
 // ROPE: q and the new token's k arrive unrotated and rotate at rope.pos[b]
 // (with the fused append only); the ring holds rotated keys.
 template <bool kShortRing, bool ROPE>
@@ -421,14 +461,29 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     const int b = blockIdx.x, g = blockIdx.y;
     const int p = ctx_lens[b];
     const int rowk = hkv * kDqk * 2, rowv = hkv * kDv * 2;
+    const int hl = tid >> 4;  // merge: local head 0..15
+    const int jd = tid & 15;  // merge: dims jd + 16m of q and k, values 8jd .. 8jd+7
+    const int head = g * kGroup + hl;
 
     // Fused append: this thread's 16 bytes of the new token's K or V row of
     // group g, loaded now and stored once the ring has been read.
     u32x4 app_row = {}, app_pair = {};
-    const u32x4* knew_row = reinterpret_cast<const u32x4*>(k_new + ((size_t)b * hkv + g) * kDqk);
+    const uint16_t* knew = k_new + ((size_t)b * hkv + g) * kDqk;
+    const u32x4* knew_row = reinterpret_cast<const u32x4*>(knew);
     if (app_k && tid < (kDqk + kDv) / 8)
         app_row = tid < kDqk / 8 ? knew_row[tid]
                                  : reinterpret_cast<const u32x4*>(v_new + ((size_t)b * hkv + g) * kDv)[tid - kDqk / 8];
+    // The new token's share of this merge thread.
+    uint16_t qn[kDqk / 16], kn[kDqk / 16];
+    {
+        const uint16_t* qrow = q + ((size_t)b * hq + head) * kDqk;
+#pragma unroll
+        for (int m = 0; m < kDqk / 16; ++m) {
+            qn[m] = qrow[jd + 16 * m];
+            kn[m] = knew[jd + 16 * m];
+        }
+    }
+    const u32x4 vn = reinterpret_cast<const u32x4*>(v_new + ((size_t)b * hkv + g) * kDv)[jd];
     int hc = 0;  // ROPE: K chunks in the first half of the rotated dims
     RopeLane fl{};
     int rpos = 0;
@@ -448,51 +503,72 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     const uint32_t ring_rows = kShortRing ? (uint32_t)R : (uint32_t)nring;
     const rsrc_t rk = make_rsrc(ring_k + (size_t)b * R * hkv * kDqk, ring_rows * rowk);
     const rsrc_t rv = make_rsrc(ring_v + (size_t)b * R * hkv * kDv, ring_rows * rowv);
-    const rsrc_t nk = make_rsrc(k_new + (size_t)b * hkv * kDqk, (uint32_t)rowk);
-    const rsrc_t nv = make_rsrc(v_new + (size_t)b * hkv * kDv, (uint32_t)rowv);
     const int ring_tiles = (R + kTile - 1) / kTile;
-    const int mine = (ring_tiles - wave + 3) / 4;             // ring tiles wave, wave+4, ...
-    const int ntiles = mine + (wave == ring_tiles % 4 ? 1 : 0);  // plus the new token's tile
+    const int ntiles = (ring_tiles - wave + 3) / 4;  // ring tiles wave, wave+4, ...
     const rsrc_t none = make_rsrc(k_new, 0);
     auto get = [&](int i) -> TileSrc {
-        if (i < mine) {
+        if (i < ntiles) {
             const int rt = wave + 4 * i;
             return TileSrc{rk, rv, rt * kTile * rowk, rt * kTile * rowv, min(max(nring - rt * kTile, 0), kTile)};
         }
-        if (i < ntiles) return TileSrc{nk, nv, 0, 0, 1};
         return TileSrc{none, none, 0, 0, 0};
     };
     const LaneOffsets lo = lane_offsets(lane, g, rowk, rowv);
     WaveAcc acc;
     acc_init(acc);
+    float* rtab = rtab_all + (ROPE ? wave * kDqk : 0);
+    // The new token's score for head hl (log2 domain): 12 products per thread,
+    // summed over the 16 threads of the head; formed while the ring tiles load.
+    float sv = 0.0f;
+    auto new_score = [&]() {
+        float qv[kDqk / 16], kv[kDqk / 16];
+#pragma unroll
+        for (int m = 0; m < kDqk / 16; ++m) {
+            qv[m] = __builtin_bit_cast(float, (uint32_t)qn[m] << 16);
+            kv[m] = __builtin_bit_cast(float, (uint32_t)kn[m] << 16);
+        }
+        if constexpr (ROPE) {
+            switch (rope.half / 32) {
+                case 1: rope_strided<2>(qv, kv, rtab, jd); break;
+                case 2: rope_strided<4>(qv, kv, rtab, jd); break;
+                case 3: rope_strided<6>(qv, kv, rtab, jd); break;
+                default: break;
+            }
+        }
+        float part = 0.0f;
+#pragma unroll
+        for (int m = 0; m < kDqk / 16; ++m) part = __builtin_fmaf(qv[m], kv[m], part);
+        part += __shfl_xor(part, 8);
+        part += __shfl_xor(part, 4);
+        part += __shfl_xor(part, 2);
+        part += __shfl_xor(part, 1);
+        sv = part * c_log2;
+    };
     if constexpr (ROPE) {
         // Each wave forms the angles while its first tiles load; then q rotates
-        // in registers, the new token's K registers right before its tile, and
+        // in registers, the new token's q and k values of the merge thread, and
         // (wave 0) the row the fused append writes.
-        float* rtab = rtab_all + wave * kDqk;
         auto prep = [&]() {
             rope_table_wave(rtab, rpos, fl, rope.half, lane);
             rope_frags32_rd(qf, rtab, rope.half, lane >> 4);
             if (app_k && tid < 2 * hc) app_row = rope_chunk(app_row, app_pair, tid, rtab, rope.half);
-        };
-        const int new_idx = ntiles > mine ? mine : -1;
-        auto khook = [&](int i, u32x4 (&kr)[12]) {
-            if (i == new_idx) rope_frags32_rd(kr, rtab, rope.half, lane >> 4);
+            new_score();
         };
         if constexpr (kShortRing)
-            run_two_tiles(acc, qf, lds + wave * kVTileBytes, ntiles, get, lo, rowv, c_log2, lane, prep, khook);
+            run_two_tiles(acc, qf, lds + wave * kVTileBytes, ntiles, get, lo, rowv, c_log2, lane, prep);
         else
-            run_tiles<kSwaDepth>(acc, qf, lds + wave * kVTileBytes, ntiles, get, lo, rowv, c_log2, lane, prep, khook);
+            run_tiles<kSwaDepth>(acc, qf, lds + wave * kVTileBytes, ntiles, get, lo, rowv, c_log2, lane, prep);
     } else {
         if constexpr (kShortRing)
-            run_two_tiles(acc, qf, lds + wave * kVTileBytes, ntiles, get, lo, rowv, c_log2, lane);
+            run_two_tiles(acc, qf, lds + wave * kVTileBytes, ntiles, get, lo, rowv, c_log2, lane, new_score);
         else
-            run_tiles<kSwaDepth>(acc, qf, lds + wave * kVTileBytes, ntiles, get, lo, rowv, c_log2, lane);
+            run_tiles<kSwaDepth>(acc, qf, lds + wave * kVTileBytes, ntiles, get, lo, rowv, c_log2, lane, new_score);
     }
     acc.l += __shfl_xor(acc.l, 16);
     acc.l += __shfl_xor(acc.l, 32);
 
-    // Merge the 4 waves: per wave O [16 heads][128 dv] and 16 x (m, l) in fp32.
+    // Merge the 4 waves and the new token: per wave O [16 heads][128 dv] and
+    // 16 x (m, l) in fp32.
     __syncthreads();
     float* mrg_o = reinterpret_cast<float*>(lds);     // [wave][16][kMergeRow]
     float* mrg_ml = mrg_o + 4 * kGroup * kMergeRow;   // [wave][16][2]
@@ -516,12 +592,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
             reinterpret_cast<u32x4*>(app_v + (slot_row * hkv + g) * kDv)[tid - kDqk / 8] = app_row;
     }
 
-    const int hl = tid >> 4;        // local head 0..15
-    const int e0 = (tid & 15) * 8;  // 8 output columns
-    const int head = g * kGroup + hl;
+    const int e0 = jd * 8;  // 8 output columns
     bool has;
     const float sl = sink_log2(sink, head, has);
-    float M = sl;
+    float M = fmaxf(sl, sv);
 #pragma unroll
     for (int w = 0; w < 4; ++w) M = fmaxf(M, mrg_ml[(w * kGroup + hl) * 2]);
     float Z = has ? fast_exp2(sl - M) : 0.0f;
@@ -533,6 +607,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
         const float* src_o = mrg_o + (w * kGroup + hl) * kMergeRow + e0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] += wt * src_o[e];
+    }
+    const float pn = fast_exp2(sv - M);
+    Z += pn;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        o[2 * e] += pn * bf16_word_lo(vn[e]);
+        o[2 * e + 1] += pn * bf16_word_hi(vn[e]);
     }
     const float inv = value_scale / Z;
     u32x4 w4 = {pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv),
@@ -1110,7 +1191,7 @@ __global__ __launch_bounds__(256) void ga_combine_kernel(const long long* __rest
 
 hipError_t launch_decode_swa(const DecodeArgs& a, hipStream_t stream) {
     const int R = a.window - 1;
-    const bool short_ring = (R + kTile - 1) / kTile + 1 <= 8;
+    const bool short_ring = (R + kTile - 1) / kTile <= 8;  // at most two ring tiles per wave
     if (a.rope.pos) {
         auto kern = short_ring ? swa_decode_kernel<true, true> : swa_decode_kernel<false, true>;
         hipLaunchKernelGGL(kern, dim3(a.batch, a.hkv), dim3(256), 0, stream, a.q, a.k_new, a.v_new, a.k_cache, a.v_cache,

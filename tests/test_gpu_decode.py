@@ -45,10 +45,11 @@ def test_decode_context_sweep(layer_type):
     compare(out, lse, ro, rl, f"decode layer {layer_type}")
 
 
-@pytest.mark.parametrize("window", [2, 33, 97, 225, 226, 300])
+@pytest.mark.parametrize("window", [2, 33, 97, 225, 226, 257, 258, 300])
 def test_swa_decode_ring_sizes(window):
-    """Rings of window-1 slots: 1 slot, partial tiles, the two-tile limit (224
-    slots) and rings long enough that waves loop over several tiles."""
+    """Rings of window-1 slots: 1 slot, partial tiles, the two-tile limit (256
+    slots: windows 257 and 258 fall on either side of it) and rings long enough
+    that waves loop over several tiles."""
     log(f"[case] SWA decode window={window}")
     x = synth.decode_inputs([0, 1, window - 2, window - 1, window, 3 * window + 5, 1000], SWA, seed=29, window=window)
     out, lse = gpu_decode(x, SWA, window=window)
