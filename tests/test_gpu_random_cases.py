@@ -12,8 +12,11 @@ backward on seeded ragged batches (gradient bars of the backward tests), and
 the fused decode + append against decode followed by append (bit for bit),
 some GA sequences with no room left for the new token; and the paged GA pool
 (page sizes 16-1024, splits 32-2048, contexts to 6000) against the oracle and
-bit for bit against the contiguous pool; and the FP8 E4M3 pool (append codes
-bit for bit, decode within the bars).
+bit for bit against the contiguous pool; the FP8 E4M3 pool (append codes
+bit for bit, decode within the bars); and the fused-RoPE prefill, chunked
+prefill and decode step (rotary dims 32-192, position offsets) bit for bit
+against the rotation followed by the unfused call and within the bars of the
+oracle.
 """
 import random
 
@@ -219,3 +222,102 @@ def test_random_fp8_decode_case(case):
     ro, rl = orc().decode_fp8(bits(d.q), bits(d.k_new), bits(d.v_new), kr, vr, base, K_SCALE, V_SCALE, cached,
                               scale=SCALE, sink=sink_array(sd))
     compare(out, lse, ro, rl, f"random FP8 decode case {case} (sink {sc})")
+
+
+N_ROPE = 9
+
+
+@pytest.mark.parametrize("case", range(N_ROPE))
+def test_random_rope_case(case):
+    """The fused-RoPE entry points on seeded shapes, rotary dims and position
+    offsets: prefill, chunked prefill and the decode step, each bit for bit
+    against mimo_rope_apply on copies followed by the unfused call (where both
+    run the same kernel) and within the bars of the oracle's rotation followed
+    by the oracle's attention."""
+    import numpy as np
+    import torch
+    from global_attention_mimo_amd import binding as B
+    from gpu_util import to_dev
+    rng = random.Random(15485863 * case + 3)
+    kind = ("prefill", "chunk", "decode")[case % 3]
+    lt = rng.choice([0, 1])
+    window = rng.choice([17, 129, 145, 146, 300]) if lt == 0 else 129
+    theta = rng.choice([1e4, 1e6, 5e6])
+    dims = B.make_dims(sliding_window=window)
+    dev = "cuda"
+    if kind == "decode":
+        from test_gpu_rope_decode import _run
+        rd = rng.choice([64, 128, 192])
+        ctx = [rng.choice([0, 1, window - 2, window - 1, window, rng.randint(0, 4000)]) for _ in
+               range(rng.randint(1, 7))]
+        split = rng.choice([0, 32, 64]) if lt == 1 else 0
+        offset = rng.choice([0, 0, rng.randint(1, 100000)])
+        log(f"[case {case}] decode rope layer={lt} W={window} ctx={ctx} split={split} rd={rd} theta={theta} "
+            f"offset={offset}")
+        x, pos, ((of, lf, kf, vf), (os_, ls, ks, vs)) = _run(lt, ctx, window, split, rd, theta, offset,
+                                                             seed=6000 + case)
+        assert torch.equal(of, os_) and torch.equal(lf, ls), "fused decode differs from rope + decode_append"
+        assert torch.equal(kf, ks) and torch.equal(vf, vs), "caches differ"
+        rq, rk = orc().rope(bits(x.q), bits(x.k_new), pos.cpu().numpy(), theta=float(np.float32(theta)),
+                            rotary_dim=rd)
+        ro, rl = orc().decode(synth.bf16_bits(torch.from_numpy(rq).to(torch.bfloat16)),
+                              synth.bf16_bits(torch.from_numpy(rk).to(torch.bfloat16)), bits(x.v_new),
+                              bits(x.k_cache), bits(x.v_cache), x.ctx_lens.cpu().numpy(), layer_type=lt,
+                              window=window, scale=SCALE, sink=sink_array(x.sink),
+                              kv_base=None if x.kv_base is None else x.kv_base.cpu().numpy())
+        compare(of, lf, ro, rl, f"random decode rope case {case}")
+        return
+    rd = rng.choice([32, 64, 128, 192])
+    lengths = [rng.choice([1, 16, 17, 64, 65, rng.randint(1, 600)]) for _ in range(rng.randint(1, 4))]
+    x = synth.prefill_inputs(lengths, seed=6100 + case)
+    # the same kernel on both sides unless a streaming-window SWA call rotates more than 64 dims
+    same_kernel = not (lt == 0 and window <= 145 and rd > 64)
+    if kind == "prefill":
+        offs = [rng.choice([0, rng.randint(1, 50000)]) for _ in lengths]
+        pos = np.concatenate([np.arange(L) + o for L, o in zip(lengths, offs)]).astype(np.int32)
+        posd = torch.tensor(pos, device=dev)
+        q, k, v, cu, sink = (to_dev(t) for t in (x.q, x.k, x.v, x.cu_seqlens, x.sink))
+        log(f"[case {case}] prefill rope layer={lt} W={window} lengths={lengths} rd={rd} theta={theta}")
+        of, lf, krot = B.prefill_rope(q, k, v, posd, cu, max(lengths), lt, theta, rd, sink=sink, dims=dims)
+        q2, k2 = q.clone(), k.clone()
+        B.rope_apply(q2, k2, posd, theta, rd)
+        os_, ls = B.prefill(q2, k2, v, cu, max(lengths), lt, sink=sink, dims=dims)
+        torch.cuda.synchronize()
+        assert torch.equal(krot, k2), "k_rot differs from mimo_rope_apply's k"
+        if same_kernel:
+            assert torch.equal(of, os_) and torch.equal(lf, ls), "fused prefill differs from rope + prefill"
+        rq, rk = orc().rope(bits(x.q), bits(x.k), pos, theta=float(np.float32(theta)), rotary_dim=rd)
+        ro, rl = orc().prefill(synth.bf16_bits(torch.from_numpy(rq).to(torch.bfloat16)),
+                               synth.bf16_bits(torch.from_numpy(rk).to(torch.bfloat16)), bits(x.v),
+                               x.cu_seqlens.numpy(), layer_type=lt, window=window, scale=SCALE,
+                               sink=sink_array(x.sink))
+        compare(of, lf, ro, rl, f"random prefill rope case {case}")
+        return
+    from test_gpu_chunk import _split
+    cached = [rng.randint(0, L - 1) if rng.random() < 0.8 else 0 for L in lengths]
+    kc, vc, base, cap = _caches(lt, lengths, window=window)
+    kh, vh = _fill(x, lt, cached, kc, vc, base, cap, window=window)
+    _, new, rest = _split(x, cached)
+    cu_new = synth.cu_from_lengths(rest, dev)
+    ctx = torch.tensor(cached, dtype=torch.int32, device=dev)
+    offset = rng.choice([0, rng.randint(1, 50000)])
+    pos = np.concatenate([np.arange(n) + c + offset for c, n in zip(cached, rest)]).astype(np.int32)
+    posd = torch.tensor(pos, device=dev)
+    q, k, v, sink = to_dev(x.q[new]), to_dev(x.k[new]), to_dev(x.v[new]), to_dev(x.sink)
+    log(f"[case {case}] chunk rope layer={lt} W={window} lengths={lengths} cached={cached} rd={rd} theta={theta}")
+    of, lf, krot = B.prefill_chunk_rope(q, k, v, posd, cu_new, max(rest), kc, vc, ctx, lt, theta, rd, sink=sink,
+                                        kv_base=base, dims=dims)
+    q2, k2 = q.clone(), k.clone()
+    B.rope_apply(q2, k2, posd, theta, rd)
+    os_, ls = B.prefill_chunk(q2, k2, v, cu_new, max(rest), kc, vc, ctx, lt, sink=sink, kv_base=base, dims=dims)
+    torch.cuda.synchronize()
+    assert torch.equal(krot, k2), "k_rot differs from mimo_rope_apply's k"
+    if same_kernel:
+        assert torch.equal(of, os_) and torch.equal(lf, ls), "fused chunk differs from rope + chunk"
+    rq, rk = orc().rope(bits(x.q[new]), bits(x.k[new]), pos, theta=float(np.float32(theta)), rotary_dim=rd)
+    ro, rl = orc().prefill_chunk(synth.bf16_bits(torch.from_numpy(rq).to(torch.bfloat16)),
+                                 synth.bf16_bits(torch.from_numpy(rk).to(torch.bfloat16)), bits(x.v[new]),
+                                 cu_new.cpu().numpy(), kh, vh, ctx.cpu().numpy(), layer_type=lt, window=window,
+                                 scale=SCALE, sink=sink_array(x.sink),
+                                 kv_base=None if base is None else base.cpu().numpy())
+    compare(of, lf, ro, rl, f"random chunk rope case {case}")
