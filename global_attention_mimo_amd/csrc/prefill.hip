@@ -322,12 +322,30 @@ void prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     if (j < ctx0) return cache_col + cache_row(j) * stride;
                     return chunk_col + (size_t)min(j - ctx0, L - 1) * stride;
                 };
+                // GA over the contiguous pool: a tile wholly below ctx0 is a
+                // run of pool rows and a tile wholly at or past it a run of chunk
+                // rows, so both take the descriptor loads of the plain prefill
+                // (chunk rows past the chunk's end read as zeros, and are
+                // masked); only the tile across ctx0 picks its rows one by one.
+                const bool whole = !SWA && !PAGED && (kbase + NK <= ctx0 || kbase >= ctx0);
+                if (whole) {
+                    const bool cached = kbase + NK <= ctx0;
+                    const size_t row0 = cached ? (size_t)(cache_row0 + kbase) : (size_t)s0 + (kbase - ctx0);
+                    const uint32_t rows = cached ? (uint32_t)NK : (uint32_t)max(min(L - (kbase - ctx0), NK), 0);
+                    const rsrc_t kr = make_rsrc((cached ? k_cache : k) + (row0 * hkv + g) * kDqk, rows * kRowBytesK);
+                    const rsrc_t vr = make_rsrc((cached ? v_cache : v) + (row0 * hkv + g) * kDv, rows * kRowBytesV);
 #pragma unroll
-                for (int i = 0; i < Cfg::kKPer; ++i)
-                    kreg[i] = *reinterpret_cast<const u32x4*>(src_row(kcp[i], kp[i], kstride, kbase + krow_of[i]));
+                    for (int i = 0; i < Cfg::kKPer; ++i) kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, koff[i], 0, 0);
 #pragma unroll
-                for (int i = 0; i < Cfg::kVPer; ++i)
-                    vreg[i] = *reinterpret_cast<const u32x4*>(src_row(vcp[i], vp[i], vstride, kbase + vrow_of[i]));
+                    for (int i = 0; i < Cfg::kVPer; ++i) vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, voff[i], 0, 0);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < Cfg::kKPer; ++i)
+                        kreg[i] = *reinterpret_cast<const u32x4*>(src_row(kcp[i], kp[i], kstride, kbase + krow_of[i]));
+#pragma unroll
+                    for (int i = 0; i < Cfg::kVPer; ++i)
+                        vreg[i] = *reinterpret_cast<const u32x4*>(src_row(vcp[i], vp[i], vstride, kbase + vrow_of[i]));
+                }
             }
         } else {
             // The tile's rows through the descriptor: its base and record count
