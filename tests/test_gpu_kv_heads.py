@@ -2,7 +2,9 @@
 grouped-query attention with 16 query heads per KV head): one KV head (a
 single wave of the GA decode split workgroup) and five (the split workgroup's
 second z-slice holds one working wave and three that exit).  Prefill, decode
-and append through the C ABI against the fp64 oracle; appends bit for bit."""
+and append through the C ABI against the fp64 oracle; appends bit for bit; the
+fused decode step with RoPE bit for bit against the rotation and the unfused
+step."""
 import numpy as np
 import pytest
 import torch
@@ -62,3 +64,40 @@ def test_decode_and_append_kv_heads(hkv, lt):
     assert np.array_equal(bits(d["k_cache"]), kc) and np.array_equal(bits(d["v_cache"]), vc), \
         f"append lt={lt} hkv={hkv} differs from the oracle's"
     log(f"[parity] append lt={lt} hkv={hkv}: caches bit-exact")
+
+
+@pytest.mark.parametrize("hkv", [1, 5])
+@pytest.mark.parametrize("lt", [SWA, GA])
+def test_decode_append_rope_kv_heads(hkv, lt):
+    """The fused decode step with RoPE at one and five KV heads: bit for bit
+    against mimo_rope_apply + mimo_attn_decode_append (outputs and caches)."""
+    hq = 16 * hkv
+    ctx = [0, 1, 127, 128, 700, 3000]
+    log(f"[case] decode_append_rope lt={lt} hkv={hkv} ctx={ctx}")
+    x = synth.decode_inputs(ctx, lt, seed=90 + hkv, hq=hq, hkv=hkv, headroom=3)
+    dims = B.make_dims(num_q_heads=hq, num_kv_heads=hkv)
+    d = {f: to_dev(getattr(x, f)) for f in ("q", "k_new", "v_new", "k_cache", "v_cache", "kv_base", "kv_capacity",
+                                            "ctx_lens", "sink")}
+    bsz, max_ctx = len(ctx), max(ctx) + 1
+    nbytes = B.mimo_attn_decode_workspace_size(dims, lt, bsz, max_ctx, 64)
+    ws = torch.empty(nbytes // 4 + 4, dtype=torch.float32, device="cuda") if nbytes else None
+    pos = (d["ctx_lens"] + 11).to(torch.int32)
+    res = []
+    for fused in (True, False):
+        kc, vc = d["k_cache"].clone(), d["v_cache"].clone()
+        out = torch.empty((bsz, hq, 128), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((bsz, hq), dtype=torch.float32, device="cuda")
+        if fused:
+            B.mimo_attn_decode_append_rope(dims, lt, d["q"], d["k_new"], d["v_new"], pos, kc, vc, d["kv_base"],
+                                           d["kv_capacity"], d["ctx_lens"], bsz, max_ctx, 64, 5e6, 128, d["sink"],
+                                           out, lse, ws)
+        else:
+            q2, k2 = d["q"].clone(), d["k_new"].clone()
+            B.rope_apply(q2, k2, pos, 5e6, 128, dims=dims)
+            B.mimo_attn_decode_append(dims, lt, q2, k2, d["v_new"], kc, vc, d["kv_base"], d["kv_capacity"],
+                                      d["ctx_lens"], bsz, max_ctx, 64, d["sink"], out, lse, ws)
+        torch.cuda.synchronize()
+        res.append((out, lse, kc, vc))
+    (of, lf, kf, vf), (os_, ls, ks, vs) = res
+    assert torch.equal(of, os_) and torch.equal(lf, ls), f"lt={lt} hkv={hkv}: outputs differ"
+    assert torch.equal(kf, ks) and torch.equal(vf, vs), f"lt={lt} hkv={hkv}: caches differ"
