@@ -312,175 +312,201 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void bwd_dkdv_
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dws,
     const int32_t* __restrict__ cu_seqlens, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int hq, int hkv,
-    int window, float c_log2, float scale, float value_scale, int max_seqlen) {
+    int window, float c_log2, float scale, float value_scale, int max_seqlen, int nkb) {
     __shared__ __attribute__((aligned(16))) char lds[2 * kKvTileBytes];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int G = lane >> 4;
-    const int b = blockIdx.z, g = blockIdx.y;
+    const int b = blockIdx.z;
     const int s0 = cu_seqlens[b];
     const int L = min(cu_seqlens[b + 1] - s0, max_seqlen);
-    const int k0 = blockIdx.x * kKvKeys;  // GA: the first key blocks have the most queries and run first
-    if (k0 >= L) return;
-    const int key = k0 + 16 * wave + (lane & 15);
-    const int kk = min(key, L - 1);
-    const size_t krow = (size_t)(s0 + kk) * hkv + g;
-
-    // K and V rows of this lane's key as MFMA B operands (d = 32st + 8G .. +7).
-    bf16x8 kf[kDqk / 32], vf[kDv / 32];
-#pragma unroll
-    for (int st = 0; st < kDqk / 32; ++st)
-        kf[st] = __builtin_bit_cast(bf16x8, reinterpret_cast<const u32x4*>(k + krow * kDqk)[4 * st + G]);
-#pragma unroll
-    for (int st = 0; st < kDv / 32; ++st)
-        vf[st] = __builtin_bit_cast(bf16x8, reinterpret_cast<const u32x4*>(v + krow * kDv)[4 * st + G]);
-    f32x4 dka[kDqk / 16], dva[kDv / 16];
-#pragma unroll
-    for (int db = 0; db < kDqk / 16; ++db) dka[db] = f32x4{};
-#pragma unroll
-    for (int db = 0; db < kDv / 16; ++db) dva[db] = f32x4{};
-
-    // Queries that see a key of the block: tokens k0 .. q_end-1, in blocks of
-    // kKvTok tokens.  GA walks them from the sequence end down, so that the
-    // workgroups of all key blocks of a group start at the same query block
-    // and stay near each other: a staged block is then fetched from HBM about
-    // once per L2 rather than once per workgroup.
-    const int q_end = SWA ? min(L, k0 + kKvKeys - 1 + window) : L;
-    const int nblk = (q_end - k0 + kKvTok - 1) / kKvTok;
-    auto q0_of = [&](int i) { return k0 + (SWA ? i : nblk - 1 - i) * kKvTok; };
-
-    // Staging of a block of 2 tokens x 16 heads: 32 Q rows (768 16-byte
-    // chunks), 32 dO rows (512 chunks), and the 32 rows' lse2 and D.  Row 16t +
-    // h is token q0 + t, head 16g + h.  Chunk owners are fixed per thread and
-    // uniform per wave: Q chunk tid (all waves), Q chunk 512 + tid (waves 0-3),
-    // dO chunk tid - 256 (waves 4-7), dO chunk 256 + tid (waves 0-3).  Loads go
-    // through descriptors whose base is the block's first row and whose record
-    // count ends at the sequence end, so rows past it read as zeros (their
-    // probabilities are forced to zero) and no per-block address arithmetic is
-    // vector work.  Blocks are loaded two ahead, alternating two register sets.
-    constexpr int kQChunks = kKvRows * (kDqk / 8);
-    const bool lo_waves = wave < 4;
-    const int qc1 = 512 + tid, oc0 = tid - 256, oc1 = 256 + tid;
-    auto q_off = [&](int qc) {
-        const int row = qc / (kDqk / 8);
-        return (uint32_t)(((row / kGroup) * hq + row % kGroup) * (kDqk * 2) + (qc % (kDqk / 8)) * 16);
-    };
-    auto o_off = [&](int oc) {
-        const int row = oc / (kDv / 8);
-        return (uint32_t)(((row / kGroup) * hq + row % kGroup) * (kDv * 2) + (oc % (kDv / 8)) * 16);
-    };
-    const uint32_t off0 = q_off(tid);
-    const uint32_t off1 = lo_waves ? q_off(qc1) : o_off(oc0);
-    const uint32_t off2 = lo_waves ? o_off(oc1) : 0u;
-    const uint32_t off_s = (uint32_t)(((tid & 31) / kGroup) * hq + (tid & 31) % kGroup) * 4;
-    struct Stage {
-        u32x4 r[3];
-        float lse2, d;
-    };
-    auto load_blk = [&](Stage& st, int i) {  // block i of the walk; past the last one nothing is read
-        const int q0 = i < nblk ? q0_of(i) : k0;
-        const uint32_t toks = i < nblk ? (uint32_t)max(0, min(L - q0, kKvTok)) : 0u;
-        const size_t row0 = (size_t)(s0 + q0) * hq + g * kGroup;
-        const rsrc_t rq = make_rsrc(q + row0 * kDqk, toks * (uint32_t)hq * (kDqk * 2));
-        const rsrc_t ro = make_rsrc(dout + row0 * kDv, toks * (uint32_t)hq * (kDv * 2));
-        const rsrc_t rl = make_rsrc(lse + row0, toks * (uint32_t)hq * 4);
-        const rsrc_t rd = make_rsrc(Dws + row0, toks * (uint32_t)hq * 4);
-        st.r[0] = __builtin_amdgcn_raw_buffer_load_b128(rq, off0, 0, 0);
-        st.r[1] = __builtin_amdgcn_raw_buffer_load_b128(lo_waves ? rq : ro, off1, 0, 0);
-        st.r[2] = __builtin_amdgcn_raw_buffer_load_b128(ro, off2, 0, 0);  // waves 4-7: unused
-        st.lse2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, off_s, 0, 0)) * kLog2e;
-        st.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, off_s, 0, 0));
-    };
-    auto store_blk = [&](const Stage& st, int buf) {
-        char* qt_ = lds + buf * kKvTileBytes;
-        char* ot_ = qt_ + kKvRows * kQRow;
-        float* sf = reinterpret_cast<float*>(ot_ + kKvRows * kVRow);
-        lds_put16(qt_, kQRow, tid / (kDqk / 8), tid % (kDqk / 8), st.r[0]);
-        if (lo_waves) {
-            lds_put16(qt_, kQRow, qc1 / (kDqk / 8), qc1 % (kDqk / 8), st.r[1]);
-            lds_put16(ot_, kVRow, oc1 / (kDv / 8), oc1 % (kDv / 8), st.r[2]);
-        } else {
-            lds_put16(ot_, kVRow, oc0 / (kDv / 8), oc0 % (kDv / 8), st.r[1]);
-        }
-        if (tid < kKvRows) {
-            sf[tid] = st.lse2;
-            sf[kKvRows + tid] = st.d;
-        }
-    };
-    static_assert(kQChunks == 768 && kKvRows * (kDv / 8) == 512, "chunk owners assume 32 rows of 192 + 128");
-    auto compute_blk = [&](int ib, int buf) {
-        const int q0 = q0_of(ib);
-        const char* Qt = lds + buf * kKvTileBytes;
-        const char* Ot = Qt + kKvRows * kQRow;
-        const float* sf = reinterpret_cast<const float*>(Ot + kKvRows * kVRow);
-        // S = Q K^T and dP = dO V^T: lane holds row 16blk + 4G + r (token
-        // q0 + blk, head 4G + r of the group) and key `key`.
-        f32x4 s[kKvTok], dp[kKvTok];
-#pragma unroll
-        for (int blk = 0; blk < kKvTok; ++blk) {
-            s[blk] = f32x4{};
-            dp[blk] = f32x4{};
-#pragma unroll
-            for (int st = 0; st < kDqk / 32; ++st)
-                s[blk] = mfma_16x16x32(lds_row8(Qt, kQRow, 16 * blk + (lane & 15), 4 * st + G), kf[st], s[blk]);
-#pragma unroll
-            for (int st = 0; st < kDv / 32; ++st)
-                dp[blk] = mfma_16x16x32(lds_row8(Ot, kVRow, 16 * blk + (lane & 15), 4 * st + G), vf[st], dp[blk]);
-        }
-        float p[kKvTok][4], ds[kKvTok][4];
-#pragma unroll
-        for (int blk = 0; blk < kKvTok; ++blk) {
-            const int tok = q0 + blk;
-            const bool tok_ok = tok < L && key < L && key <= tok && (!SWA || tok <= key + window - 1);
-            // The lane's four rows 16blk + 4G + r are consecutive: one 16-byte read each for lse2 and D.
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(sf + 16 * blk + 4 * G);
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(sf + kKvRows + 16 * blk + 4 * G);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                // Masked entries take exp2(-inf) = 0 rather than a branch around the exp.
-                const float arg = __builtin_fmaf(s[blk][r], c_log2, -l4[r]);
-                const float pr = fast_exp2(tok_ok ? arg : -__builtin_inff());
-                p[blk][r] = pr;
-                ds[blk][r] = pr * (value_scale * dp[blk][r] - d4[r]);
-            }
-        }
-        const bf16x8 pf = pack_bf16x8(p[0][0], p[0][1], p[0][2], p[0][3], p[1][0], p[1][1], p[1][2], p[1][3]);
-        const bf16x8 dsf = pack_bf16x8(ds[0][0], ds[0][1], ds[0][2], ds[0][3], ds[1][0], ds[1][1], ds[1][2], ds[1][3]);
-#pragma unroll
-        for (int db = 0; db < kDv / 16; ++db) dva[db] = mfma_16x16x32(lds_tr8(Ot, kVRow, db, lane), pf, dva[db]);
-#pragma unroll
-        for (int db = 0; db < kDqk / 16; ++db) dka[db] = mfma_16x16x32(lds_tr8(Qt, kQRow, db, lane), dsf, dka[db]);
-    };
-    Stage sa, sb;
-    load_blk(sa, 0);
-    store_blk(sa, 0);
-    load_blk(sb, 1);
-    __syncthreads();
-    int ib = 0;
-    for (; ib + 1 < nblk; ib += 2) {
-        load_blk(sa, ib + 2);
-        compute_blk(ib, 0);
-        store_blk(sb, 1);
-        __syncthreads();
-        load_blk(sb, ib + 3);
-        compute_blk(ib + 1, 1);
-        if (ib + 2 < nblk) store_blk(sa, 0);
-        __syncthreads();
+    // SWA: workgroup (key block, group).  GA pairs the key blocks: workgroup
+    // (p, g) -- g the fastest index, so that with 4 groups each XCD serves one
+    // group -- takes key block p, walking its query blocks from the sequence
+    // end down to its diagonal, then key block nkb-1-p, walking up from its
+    // diagonal to the end.  At step s of the first walk every workgroup reads
+    // query block T-2-2s, at step s of the second 2s-128 (T = 128 nkb): all
+    // workgroups of a round read the same block at the same time, and each is
+    // fetched about once per L2.  Each workgroup's two walks add up to T+128
+    // query tokens.
+    int g, kb_a, kb_b;
+    if constexpr (SWA) {
+        g = blockIdx.y;
+        kb_a = blockIdx.x;
+        kb_b = -1;
+    } else {
+        g = (int)blockIdx.x % hkv;
+        kb_a = (int)blockIdx.x / hkv;
+        kb_b = nkb - 1 - kb_a;
+        if (kb_b == kb_a) kb_b = -1;
     }
-    if (ib < nblk) compute_blk(ib, 0);
-    if (key >= L) return;
-    // lane holds dK^T[d = 16db + 4G + r][key] and dV^T likewise
-    uint16_t* kout = dk + krow * kDqk;
-    uint16_t* vout = dv + krow * kDv;
+    auto key_block = [&](const int kb, const bool down) {
+        const int k0 = kb * kKvKeys;
+        if (k0 >= L) return;
+        const int key = k0 + 16 * wave + (lane & 15);
+        const int kk = min(key, L - 1);
+        const size_t krow = (size_t)(s0 + kk) * hkv + g;
+
+        // K and V rows of this lane's key as MFMA B operands (d = 32st + 8G .. +7).
+        bf16x8 kf[kDqk / 32], vf[kDv / 32];
 #pragma unroll
-    for (int db = 0; db < kDqk / 16; ++db)
-        *reinterpret_cast<u32x2*>(kout + 16 * db + 4 * G) =
-            u32x2{pack_bf16x2(dka[db][0] * scale, dka[db][1] * scale), pack_bf16x2(dka[db][2] * scale, dka[db][3] * scale)};
+        for (int st = 0; st < kDqk / 32; ++st)
+            kf[st] = __builtin_bit_cast(bf16x8, reinterpret_cast<const u32x4*>(k + krow * kDqk)[4 * st + G]);
 #pragma unroll
-    for (int db = 0; db < kDv / 16; ++db)
-        *reinterpret_cast<u32x2*>(vout + 16 * db + 4 * G) =
-            u32x2{pack_bf16x2(dva[db][0] * value_scale, dva[db][1] * value_scale),
-                  pack_bf16x2(dva[db][2] * value_scale, dva[db][3] * value_scale)};
+        for (int st = 0; st < kDv / 32; ++st)
+            vf[st] = __builtin_bit_cast(bf16x8, reinterpret_cast<const u32x4*>(v + krow * kDv)[4 * st + G]);
+        f32x4 dka[kDqk / 16], dva[kDv / 16];
+#pragma unroll
+        for (int db = 0; db < kDqk / 16; ++db) dka[db] = f32x4{};
+#pragma unroll
+        for (int db = 0; db < kDv / 16; ++db) dva[db] = f32x4{};
+
+        // Queries that see a key of the block: tokens k0 .. q_end-1, in blocks of
+        // kKvTok tokens, walked down from the end or up from k0 (see above).
+        const int q_end = SWA ? min(L, k0 + kKvKeys - 1 + window) : L;
+        const int nblk = (q_end - k0 + kKvTok - 1) / kKvTok;
+        auto q0_of = [&](int i) { return k0 + (down ? nblk - 1 - i : i) * kKvTok; };
+
+        // Staging of a block of 2 tokens x 16 heads: 32 Q rows (768 16-byte
+        // chunks), 32 dO rows (512 chunks), and the 32 rows' lse2 and D.  Row 16t +
+        // h is token q0 + t, head 16g + h.  Chunk owners are fixed per thread and
+        // uniform per wave: Q chunk tid (all waves), Q chunk 512 + tid (waves 0-3),
+        // dO chunk tid - 256 (waves 4-7), dO chunk 256 + tid (waves 0-3).  Loads go
+        // through descriptors whose base is the block's first row and whose record
+        // count ends at the sequence end, so rows past it read as zeros (their
+        // probabilities are forced to zero) and no per-block address arithmetic is
+        // vector work.  Blocks are loaded two ahead, alternating two register sets.
+        constexpr int kQChunks = kKvRows * (kDqk / 8);
+        const bool lo_waves = wave < 4;
+        const int qc1 = 512 + tid, oc0 = tid - 256, oc1 = 256 + tid;
+        auto q_off = [&](int qc) {
+            const int row = qc / (kDqk / 8);
+            return (uint32_t)(((row / kGroup) * hq + row % kGroup) * (kDqk * 2) + (qc % (kDqk / 8)) * 16);
+        };
+        auto o_off = [&](int oc) {
+            const int row = oc / (kDv / 8);
+            return (uint32_t)(((row / kGroup) * hq + row % kGroup) * (kDv * 2) + (oc % (kDv / 8)) * 16);
+        };
+        const uint32_t off0 = q_off(tid);
+        const uint32_t off1 = lo_waves ? q_off(qc1) : o_off(oc0);
+        const uint32_t off2 = lo_waves ? o_off(oc1) : 0u;
+        const uint32_t off_s = (uint32_t)(((tid & 31) / kGroup) * hq + (tid & 31) % kGroup) * 4;
+        struct Stage {
+            u32x4 r[3];
+            float lse2, d;
+        };
+        auto load_blk = [&](Stage& st, int i) {  // block i of the walk; past the last one nothing is read
+            const int q0 = i < nblk ? q0_of(i) : k0;
+            const uint32_t toks = i < nblk ? (uint32_t)max(0, min(L - q0, kKvTok)) : 0u;
+            const size_t row0 = (size_t)(s0 + q0) * hq + g * kGroup;
+            const rsrc_t rq = make_rsrc(q + row0 * kDqk, toks * (uint32_t)hq * (kDqk * 2));
+            const rsrc_t ro = make_rsrc(dout + row0 * kDv, toks * (uint32_t)hq * (kDv * 2));
+            const rsrc_t rl = make_rsrc(lse + row0, toks * (uint32_t)hq * 4);
+            const rsrc_t rd = make_rsrc(Dws + row0, toks * (uint32_t)hq * 4);
+            st.r[0] = __builtin_amdgcn_raw_buffer_load_b128(rq, off0, 0, 0);
+            st.r[1] = __builtin_amdgcn_raw_buffer_load_b128(lo_waves ? rq : ro, off1, 0, 0);
+            st.r[2] = __builtin_amdgcn_raw_buffer_load_b128(ro, off2, 0, 0);  // waves 4-7: unused
+            st.lse2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, off_s, 0, 0)) * kLog2e;
+            st.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, off_s, 0, 0));
+        };
+        auto store_blk = [&](const Stage& st, int buf) {
+            char* qt_ = lds + buf * kKvTileBytes;
+            char* ot_ = qt_ + kKvRows * kQRow;
+            float* sf = reinterpret_cast<float*>(ot_ + kKvRows * kVRow);
+            lds_put16(qt_, kQRow, tid / (kDqk / 8), tid % (kDqk / 8), st.r[0]);
+            if (lo_waves) {
+                lds_put16(qt_, kQRow, qc1 / (kDqk / 8), qc1 % (kDqk / 8), st.r[1]);
+                lds_put16(ot_, kVRow, oc1 / (kDv / 8), oc1 % (kDv / 8), st.r[2]);
+            } else {
+                lds_put16(ot_, kVRow, oc0 / (kDv / 8), oc0 % (kDv / 8), st.r[1]);
+            }
+            if (tid < kKvRows) {
+                sf[tid] = st.lse2;
+                sf[kKvRows + tid] = st.d;
+            }
+        };
+        static_assert(kQChunks == 768 && kKvRows * (kDv / 8) == 512, "chunk owners assume 32 rows of 192 + 128");
+        auto compute_blk = [&](int ib, int buf) {
+            const int q0 = q0_of(ib);
+            const char* Qt = lds + buf * kKvTileBytes;
+            const char* Ot = Qt + kKvRows * kQRow;
+            const float* sf = reinterpret_cast<const float*>(Ot + kKvRows * kVRow);
+            // S = Q K^T and dP = dO V^T: lane holds row 16blk + 4G + r (token
+            // q0 + blk, head 4G + r of the group) and key `key`.
+            f32x4 s[kKvTok], dp[kKvTok];
+#pragma unroll
+            for (int blk = 0; blk < kKvTok; ++blk) {
+                s[blk] = f32x4{};
+                dp[blk] = f32x4{};
+#pragma unroll
+                for (int st = 0; st < kDqk / 32; ++st)
+                    s[blk] = mfma_16x16x32(lds_row8(Qt, kQRow, 16 * blk + (lane & 15), 4 * st + G), kf[st], s[blk]);
+#pragma unroll
+                for (int st = 0; st < kDv / 32; ++st)
+                    dp[blk] = mfma_16x16x32(lds_row8(Ot, kVRow, 16 * blk + (lane & 15), 4 * st + G), vf[st], dp[blk]);
+            }
+            float p[kKvTok][4], ds[kKvTok][4];
+#pragma unroll
+            for (int blk = 0; blk < kKvTok; ++blk) {
+                const int tok = q0 + blk;
+                const bool tok_ok = tok < L && key < L && key <= tok && (!SWA || tok <= key + window - 1);
+                // The lane's four rows 16blk + 4G + r are consecutive: one 16-byte read each for lse2 and D.
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(sf + 16 * blk + 4 * G);
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(sf + kKvRows + 16 * blk + 4 * G);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    // Masked entries take exp2(-inf) = 0 rather than a branch around the exp.
+                    const float arg = __builtin_fmaf(s[blk][r], c_log2, -l4[r]);
+                    const float pr = fast_exp2(tok_ok ? arg : -__builtin_inff());
+                    p[blk][r] = pr;
+                    ds[blk][r] = pr * (value_scale * dp[blk][r] - d4[r]);
+                }
+            }
+            const bf16x8 pf = pack_bf16x8(p[0][0], p[0][1], p[0][2], p[0][3], p[1][0], p[1][1], p[1][2], p[1][3]);
+            const bf16x8 dsf =
+                pack_bf16x8(ds[0][0], ds[0][1], ds[0][2], ds[0][3], ds[1][0], ds[1][1], ds[1][2], ds[1][3]);
+#pragma unroll
+            for (int db = 0; db < kDv / 16; ++db) dva[db] = mfma_16x16x32(lds_tr8(Ot, kVRow, db, lane), pf, dva[db]);
+#pragma unroll
+            for (int db = 0; db < kDqk / 16; ++db) dka[db] = mfma_16x16x32(lds_tr8(Qt, kQRow, db, lane), dsf, dka[db]);
+        };
+        Stage sa, sb;
+        load_blk(sa, 0);
+        store_blk(sa, 0);
+        load_blk(sb, 1);
+        __syncthreads();
+        int ib = 0;
+        for (; ib + 1 < nblk; ib += 2) {
+            load_blk(sa, ib + 2);
+            compute_blk(ib, 0);
+            store_blk(sb, 1);
+            __syncthreads();
+            load_blk(sb, ib + 3);
+            compute_blk(ib + 1, 1);
+            if (ib + 2 < nblk) store_blk(sa, 0);
+            __syncthreads();
+        }
+        if (ib < nblk) compute_blk(ib, 0);
+        if (key >= L) return;
+        // lane holds dK^T[d = 16db + 4G + r][key] and dV^T likewise
+        uint16_t* kout = dk + krow * kDqk;
+        uint16_t* vout = dv + krow * kDv;
+#pragma unroll
+        for (int db = 0; db < kDqk / 16; ++db)
+            *reinterpret_cast<u32x2*>(kout + 16 * db + 4 * G) =
+                u32x2{pack_bf16x2(dka[db][0] * scale, dka[db][1] * scale),
+                      pack_bf16x2(dka[db][2] * scale, dka[db][3] * scale)};
+#pragma unroll
+        for (int db = 0; db < kDv / 16; ++db)
+            *reinterpret_cast<u32x2*>(vout + 16 * db + 4 * G) =
+                u32x2{pack_bf16x2(dva[db][0] * value_scale, dva[db][1] * value_scale),
+                      pack_bf16x2(dva[db][2] * value_scale, dva[db][3] * value_scale)};
+    };
+    key_block(kb_a, !SWA);
+    if (kb_b >= 0) {
+        __syncthreads();  // the first walk's last reads of the staging buffers come before the second's writes
+        key_block(kb_b, false);
+    }
 }
 
 }  // namespace
@@ -500,9 +526,10 @@ hipError_t launch_prefill_backward(const BackwardArgs& a, hipStream_t stream) {
                        a.softmax_scale, a.value_scale, a.max_seqlen, nqb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int nkb = (a.max_seqlen + kKvKeys - 1) / kKvKeys;
-    hipLaunchKernelGGL(a.swa ? bwd_dkdv_kernel<true> : bwd_dkdv_kernel<false>, dim3(nkb, a.hkv, a.num_seqs),
-                       dim3(512), 0, stream, a.q, a.k, a.v, a.dout, a.lse, D, a.cu_seqlens, a.dk, a.dv, a.hq, a.hkv,
-                       a.window, c_log2, a.softmax_scale, a.value_scale, a.max_seqlen);
+    const dim3 kv_grid = a.swa ? dim3(nkb, a.hkv, a.num_seqs) : dim3((unsigned)((nkb + 1) / 2 * a.hkv), 1, a.num_seqs);
+    hipLaunchKernelGGL(a.swa ? bwd_dkdv_kernel<true> : bwd_dkdv_kernel<false>, kv_grid, dim3(512), 0, stream, a.q,
+                       a.k, a.v, a.dout, a.lse, D, a.cu_seqlens, a.dk, a.dv, a.hq, a.hkv, a.window, c_log2,
+                       a.softmax_scale, a.value_scale, a.max_seqlen, nkb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (a.dsink) {
         hipLaunchKernelGGL(bwd_sink_kernel, dim3(a.hq), dim3(256), 0, stream, a.sink, a.lse, D, a.cu_seqlens,
