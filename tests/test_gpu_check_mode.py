@@ -72,6 +72,14 @@ def test_valid_calls_unchanged(check_on):
         d = decode_setup([0, 5, 300, 129], lt, 141 + lt)
         both_modes(lambda: B.decode(d["q"], d["k_new"], d["v_new"], d["k_cache"], d["v_cache"], d["ctx_lens"], 300,
                                     lt, sink=d["sink"], kv_base=d["kv_base"]))
+        cap = torch.full((4,), 400, dtype=torch.int64, device=DEV) if lt == GA else None
+
+        def step_rope(d=d, lt=lt, cap=cap):
+            kc, vc = d["k_cache"].clone(), d["v_cache"].clone()
+            out, lse = B.decode_append_rope(d["q"], d["k_new"], d["v_new"], d["ctx_lens"], kc, vc, d["ctx_lens"], 300,
+                                            lt, 5e6, 64, sink=d["sink"], kv_base=d["kv_base"], kv_capacity=cap)
+            return out, lse, kc, vc
+        both_modes(step_rope)
     # GA append, then chunked prefill over what it wrote
     base = torch.tensor([0, 300, 700], dtype=torch.int64, device=DEV)
     cap = torch.tensor([300, 400, 300], dtype=torch.int64, device=DEV)
@@ -167,6 +175,14 @@ def test_violations_are_refused_before_any_kernel(check_on):
     refused(C["CTX_RANGE"], lambda: B.decode(d["q"], d["k_new"], d["v_new"], d["k_cache"], d["v_cache"],
                                              d["ctx_lens"], 300, GA, sink=d["sink"], kv_base=d["kv_base"], out=dout,
                                              lse=dlse), dout, dlse)
+
+    # the fused decode step with RoPE: a context past max_ctx
+    kd, vd = d["k_cache"].clone(), d["v_cache"].clone()
+    capd = torch.full((3,), 500, dtype=torch.int64, device=DEV)
+    refused(C["CTX_RANGE"], lambda: B.decode_append_rope(d["q"], d["k_new"], d["v_new"], d["ctx_lens"], kd, vd,
+                                                         d["ctx_lens"], 300, GA, 5e6, 64, sink=d["sink"],
+                                                         kv_base=d["kv_base"], kv_capacity=capd, out=dout, lse=dlse),
+            dout, dlse, kd, vd)
 
     # append past a sequence's capacity
     base = torch.tensor([0, 300, 700], dtype=torch.int64, device=DEV)
