@@ -471,6 +471,22 @@ def hybrid_rows(dims, decode_steps=64):
             times.append(e0.elapsed_time(e1))
         rope_ms[mode] = float(np.mean(times))
         del graph
+    # The 48-layer prefill again with RoPE on q and k (positions 0 .. L-1):
+    # fused into the prefill (rotated keys appended), or a separate pass first.
+    rope_prefill_ms = {}
+    for mode in ("fused", "separate"):
+        st.rope_mode = mode
+        total = 0.0
+        for layer in range(st.num_layers):
+            x = synth.prefill_inputs(lengths, seed=3000 + layer, device=dev, with_sink=False)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            st.prefill_layer(layer, x.q, x.k, x.v, sinks[layer], out, lse, stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            total += e0.elapsed_time(e1)
+            del x
+        rope_prefill_ms[mode] = total
     st.rope_mode = None
     kvb = st.kv_bytes()
     calls = st.num_layers * (1 if st.fused else 2)
@@ -492,10 +508,13 @@ def hybrid_rows(dims, decode_steps=64):
         "decode_step_note": f"HIP-graph replay of the whole step ({calls} library calls + context advance), mean of "
                             f"{len(graph_ms)} steps; the first {len(eager_ms)} steps issued call by call took "
                             f"{eager_gpu:.3f} ms on the GPU clock and {eager_wall:.3f} ms host wall time",
+        "prefill_rope_fused_ms": rope_prefill_ms["fused"], "prefill_rope_separate_ms": rope_prefill_ms["separate"],
         "decode_step_rope_fused_ms": rope_ms["fused"], "decode_step_rope_separate_ms": rope_ms["separate"],
         "decode_step_rope_note": f"the step with RoPE (rotary dims 64, theta 5e6, positions = contexts) on each "
                                  f"layer's q and k_new, HIP-graph replay, mean of {rope_steps} steps each: fused "
-                                 f"(mimo_attn_decode_append_rope) against mimo_rope_apply + mimo_attn_decode_append",
+                                 f"(mimo_attn_decode_append_rope) against mimo_rope_apply + mimo_attn_decode_append; "
+                                 f"prefill_rope_*: all 48 layers' prefill + append with RoPE at positions 0..L-1, "
+                                 f"fused (mimo_attn_prefill_rope, k_rot appended) against mimo_rope_apply first",
         "kv_cache_bytes": kvb["hybrid"], "kv_cache_bytes_all_ga": kvb["all_ga"]}}
 
 

@@ -46,9 +46,11 @@ class HybridStack:
     hq: int = synth.HQ
     hkv: int = synth.HKV
     fused: bool = True  # decode steps append through mimo_attn_decode_append
-    # Rotary embedding of each decode step's q and k_new at position ctx[b]:
-    # None (inputs taken as rotated already), "fused" (mimo_attn_decode_append_rope)
-    # or "separate" (mimo_rope_apply in place, then the decode call).
+    # Rotary embedding of q and k (prefill: token i of a prompt at position i;
+    # decode: the new token at position ctx[b]): None (inputs taken as rotated
+    # already), "fused" (mimo_attn_prefill_rope, whose rotated keys are then
+    # appended, and mimo_attn_decode_append_rope) or "separate" (mimo_rope_apply
+    # in place, then the unfused calls).
     rope_mode: Optional[str] = None
     rope_theta: float = 5e6
     rotary_dim: int = 64
@@ -91,11 +93,33 @@ class HybridStack:
         ws = B.mimo_attn_decode_workspace_size(self.dims, GA, self.batch, self.max_ctx, self.split)
         if ws:
             self.workspace = torch.empty(ws // 4 + 4, dtype=torch.float32, device=dev)
+        # Prefill positions (0 .. L-1 per prompt) and, for the fused rotation, the
+        # rotated keys and the (cos, sin) table workspace, allocated on first use.
+        self.positions = torch.cat([torch.arange(L, dtype=torch.int32) for L in self.lengths]).to(dev)
+        self._k_rot = None
+        self._rope_ws = None
 
     def prefill_layer(self, layer: int, q, k, v, sink, out, lse=None, stream=None):
-        """Varlen prefill of one layer, then its KV append (cache positions 0..L-1)."""
+        """Varlen prefill of one layer, then its KV append (cache positions 0..L-1);
+        with rope_mode set, q and k are rotated first (fused: inside the prefill,
+        whose rotated keys are what is appended; separate: in place)."""
         lt = self.layer_types[layer]
         c = self.caches[layer]
+        if self.rope_mode == "fused":
+            if self._k_rot is None:
+                self._k_rot = torch.empty_like(k)
+                n = B.mimo_attn_prefill_rope_workspace_size(self.dims, self.total, self.rotary_dim)
+                self._rope_ws = torch.empty(n // 4 + 4, dtype=torch.float32, device=k.device)
+            B.mimo_attn_prefill_rope(self.dims, lt, q, k, v, self.positions, self.cu, self.batch, self.max_len,
+                                     self.total, self.rope_theta, self.rotary_dim, sink, out, lse, self._k_rot,
+                                     self._rope_ws, stream)
+            B.mimo_kv_append(self.dims, lt, self._k_rot, v, self.cu, self.zero_ctx, self.batch, self.total, c.k,
+                             c.v, c.kv_base, c.kv_capacity, stream)
+            return
+        if self.rope_mode == "separate":
+            B.mimo_rope_apply(self.dims, q, k, self.positions, self.total, self.rope_theta, self.rotary_dim, stream)
+        elif self.rope_mode is not None:
+            raise ValueError(f"rope_mode {self.rope_mode!r} is not None, 'fused' or 'separate'")
         B.mimo_attn_prefill(self.dims, lt, q, k, v, self.cu, self.batch, self.max_len, sink, out, lse, stream)
         B.mimo_kv_append(self.dims, lt, k, v, self.cu, self.zero_ctx, self.batch, self.total, c.k, c.v, c.kv_base,
                          c.kv_capacity, stream)

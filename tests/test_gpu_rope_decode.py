@@ -134,3 +134,32 @@ def test_stack_step_with_fused_rope_graph_equals_separate_rope():
         assert torch.equal(fused.caches[layer].k, sep.caches[layer].k), f"layer {layer}: K cache differs"
         assert torch.equal(fused.caches[layer].v, sep.caches[layer].v), f"layer {layer}: V cache differs"
     assert torch.equal(fused.ctx, sep.ctx)
+
+
+def test_stack_prefill_with_fused_rope_equals_separate():
+    """The hybrid stack's prefill with RoPE (positions 0..L-1): the fused form
+    (mimo_attn_prefill_rope, its rotated keys appended) against mimo_rope_apply
+    + mimo_attn_prefill + append, bit for bit per layer (outputs, LSE) and in the
+    caches afterwards."""
+    from global_attention_mimo_amd.stack import HybridStack
+    lengths = [300, 77, 128, 129, 1000, 5]
+    layers = 12
+    log(f"[case] stack prefill with fused RoPE: lengths {lengths}, {layers} layers")
+    gen = torch.Generator(device=DEV).manual_seed(11)
+    sinks = torch.randn((layers, 64), generator=gen, device=DEV)
+    fused = HybridStack(lengths, num_layers=layers, decode_steps=1, device=DEV, rope_mode="fused")
+    sep = HybridStack(lengths, num_layers=layers, decode_steps=1, device=DEV, rope_mode="separate")
+    T = sum(lengths)
+    for layer in range(layers):
+        x = synth.prefill_inputs(lengths, seed=700 + layer, device=DEV, with_sink=False)
+        outs = []
+        for st in (fused, sep):
+            out = torch.empty((T, 64, 128), dtype=torch.bfloat16, device=DEV)
+            lse = torch.empty((T, 64), dtype=torch.float32, device=DEV)
+            st.prefill_layer(layer, x.q.clone(), x.k.clone(), x.v.clone(), sinks[layer], out, lse)
+            outs.append((out, lse))
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1]), f"layer {layer} differs"
+    for layer in range(layers):
+        assert torch.equal(fused.caches[layer].k, sep.caches[layer].k), f"layer {layer}: K cache differs"
+        assert torch.equal(fused.caches[layer].v, sep.caches[layer].v), f"layer {layer}: V cache differs"
