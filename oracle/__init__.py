@@ -75,7 +75,7 @@ class Oracle:
                                                    _I64, _P, _P, _P, _P, _I]
         lib.oracle_prefill_backward.restype = _I
         lib.oracle_prefill_backward.argtypes = [_I, _I, _I, _I, _I, _I, _F, _F, _P, _P, _P, _P, _P, _I, _P, _P,
-                                                _I64, _P, _I64, _P, _P, _P, _P, _I]
+                                                _I64, _P, _I64, _P, _P, _P, _P, _I, _I]
         lib.oracle_rope.restype = _I
         lib.oracle_rope.argtypes = [_I, _I, _I, _P, _P, _P, _I64, ctypes.c_double, _I, _P, _P]
         lib.oracle_decode_fp8.restype = _I
@@ -239,11 +239,12 @@ class Oracle:
 
     def prefill_backward(self, q, k, v, dout, cu_seqlens, *, layer_type: int, window: int = 129, scale: float,
                          value_scale: float = 1.0, sink=None, q_rows=None, kv_rows=None, want_dsink: bool = True,
-                         nthreads: int = 0):
+                         stored_out: bool = False, nthreads: int = 0):
         """Gradients of sum(dout * prefill(q, k, v)) (bf16 bits in, float64 out).
 
         Returns (dq [nq][Hq][Dqk], dk [nkv][Hkv][Dqk], dv [nkv][Hkv][Dv], dsink [Hq] or None) for the
-        packed tokens q_rows / kv_rows (default: all tokens)."""
+        packed tokens q_rows / kv_rows (default: all tokens).  stored_out: take D = dO . o from the output
+        rounded to bf16 as a forward stores it, instead of the exact output."""
         q = np.ascontiguousarray(q)
         hq, dqk = q.shape[1], q.shape[2]
         hkv, dv = k.shape[1], v.shape[2]
@@ -266,7 +267,7 @@ class Oracle:
                                               self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(do), self._ptr(cu),
                                               nseq, self._ptr(sk), self._ptr(qr), qr.shape[0], self._ptr(kr),
                                               kr.shape[0], self._ptr(dq), self._ptr(dk), self._ptr(dvv),
-                                              self._ptr(ds), nth)
+                                              self._ptr(ds), int(bool(stored_out)), nth)
         if rc != OK:
             raise ValueError(f"oracle_prefill_backward rejected its arguments (status {rc})")
         return dq, dk, dvv, ds

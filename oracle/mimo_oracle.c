@@ -62,6 +62,24 @@ static double bf16_to_double(uint16_t bits) {
     return (double)f;
 }
 
+/* x rounded once to the nearest bf16 value, ties to the even significand.
+ * bf16 keeps 8 significant bits: in the binade [2^b, 2^(b+1)) the grid step is
+ * 2^(b-7); below 2^-126 (subnormals) it is 2^-133.  Magnitudes that round past
+ * the largest finite value (2 - 2^-7) * 2^127 become infinite. */
+static double round_bf16(double x) {
+    if (!isfinite(x) || x == 0.0) return x;
+    double a = fabs(x);
+    int b = -126;
+    if (a >= 0x1p-126) {
+        frexp(a, &b);
+        b -= 1;
+    }
+    double step = ldexp(1.0, b - 7);
+    double r = nearbyint(a / step) * step; /* a / step is exact; nearbyint rounds half to even */
+    if (r > 0x1.fep127) r = INFINITY;
+    return copysign(r, x);
+}
+
 /* OCP 8-bit floating point, E4M3 (OCP "OCP 8-bit Floating Point Specification
  * (OFP8)"): sign bit, 4 exponent bits with bias 7, 3 mantissa bits.  Exponent
  * field 0 holds zero and the subnormals m/8 * 2^-6; fields 1..15 hold
@@ -325,6 +343,7 @@ typedef struct {
     double *lse, *D, *psink; /* per [T][hq] row statistics (phase 0 writes, 2 reads) */
     double *dq, *dk, *dv;    /* phase 1 writes dq [nitems][hq][dqk]; phase 2 dk/dv [nitems][hkv][.] */
     int phase, maxkeys;
+    int stored_out;          /* D from the output rounded to bf16 */
     int64_t next;
     pthread_mutex_t mu;
 } bwd_job_t;
@@ -360,7 +379,8 @@ static void* bwd_worker(void* arg) {
                            &wsink);
                 const uint16_t* dorow = jb->dout + ((size_t)t * d->hq + h) * d->dv;
                 double D = 0.0;
-                for (int e = 0; e < d->dv; ++e) D += bf16_to_double(dorow[e]) * o[e];
+                for (int e = 0; e < d->dv; ++e)
+                    D += bf16_to_double(dorow[e]) * (jb->stored_out ? round_bf16(o[e]) : o[e]);
                 if (jb->phase == 0) {
                     jb->lse[(size_t)t * d->hq + h] = lse;
                     jb->D[(size_t)t * d->hq + h] = D;
@@ -411,12 +431,19 @@ static void* bwd_worker(void* arg) {
  * oracle_prefill; dout [T][hq][dv] bf16 bits).  dq is computed for the packed
  * tokens q_rows [nq] (dq [nq][hq][dqk]), dk/dv for kv_rows [nkv] (dk
  * [nkv][hkv][dqk], dv [nkv][hkv][dv]); dsink [hq] (NULL to skip) sums over
- * every token of the batch and is 0 without a sink. */
+ * every token of the batch and is 0 without a sink.
+ *
+ * D_t = dO_t . o_t is the one place the forward output enters.  With
+ * stored_out = 0 it is the exact output, so the results are the exact
+ * gradients.  With stored_out = 1 it is the output as a bf16 forward stores
+ * it (each element rounded once to the nearest bf16, ties to even): the
+ * gradients a backward computes when it is handed the forward's stored output,
+ * as the row-sum step of the flash-attention backward is.  dv does not depend on D. */
 int oracle_prefill_backward(int hq, int hkv, int dqk, int dv, int layer_type, int window, float scale,
                             float value_scale, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             const uint16_t* dout, const int32_t* cu_seqlens, int nseq, const float* sink,
                             const int64_t* q_rows, int64_t nq, const int64_t* kv_rows, int64_t nkv,
-                            double* dq, double* dk, double* dvv, double* dsink, int nthreads) {
+                            double* dq, double* dk, double* dvv, double* dsink, int stored_out, int nthreads) {
     dims_t d = {hq, hkv, dqk, dv, layer_type, window, (double)scale, (double)value_scale};
     if (!check_dims(&d) || nseq < 1 || !q || !k || !v || !dout || !cu_seqlens || cu_seqlens[0] != 0)
         return ORACLE_EINVAL;
@@ -454,6 +481,7 @@ int oracle_prefill_backward(int hq, int hkv, int dqk, int dv, int layer_type, in
     memset(&jb, 0, sizeof jb);
     jb.d = &d; jb.q = q; jb.k = k; jb.v = v; jb.dout = dout; jb.cu = cu_seqlens; jb.nseq = nseq; jb.sink = sink;
     jb.lse = lse; jb.D = D; jb.psink = ps; jb.dq = dq; jb.dk = dk; jb.dv = dvv; jb.maxkeys = maxkeys;
+    jb.stored_out = stored_out != 0;
     pthread_mutex_init(&jb.mu, NULL);
     const int64_t* phase_items[3] = {rows, q_rows, kv_rows};
     int64_t phase_n[3] = {nneed, nq, nkv};

@@ -693,6 +693,65 @@ def pin_backward_one_token_closed_form(orc):
     _close(ds, want_ds, 1e-11, "one-token dsink")
 
 
+def _bf16_nearest_even(x):
+    """float64 array -> nearest bf16 values (as float64), ties to the even bit
+    pattern, decided by exact rational distances among torch's conversion and
+    its two bf16 neighbours (torch converts through float32, which can round
+    twice)."""
+    from fractions import Fraction
+    flat = np.asarray(x, np.float64).ravel()
+    b = torch.from_numpy(flat).to(torch.bfloat16).view(torch.int16).numpy().astype(np.int32)
+    out = np.empty_like(flat)
+    for i, (xv, bv) in enumerate(zip(flat, b)):
+        cands = []
+        for c in (bv - 1, bv, bv + 1):
+            val = float(torch.tensor([c], dtype=torch.int32).to(torch.int16).view(torch.bfloat16).double())
+            cands.append((abs(Fraction(val) - Fraction(float(xv))), c & 1, val))
+        out[i] = min(cands)[2]
+    return out.reshape(np.shape(x))
+
+
+def pin_backward_stored_output_closed_form(orc):
+    """With stored_out, D takes the forward output as a bf16 forward stores it.
+    One-token sequences: out = bf16(value_scale P v) elementwise (rounded once,
+    to nearest, ties to even), D' = dO.out, dS = P (value_scale dO.v - D'), so
+    d/dq = scale dS k, d/dk sums scale dS q over the group, d/dsigma =
+    -(1 - P) D', and d/dv is value_scale P dO as without the option.  Where the
+    output is exact in bf16 (value_scale 1, no sink: out = v) the option changes
+    nothing."""
+    x = _make([1, 1, 1], seed=86)
+    dout = torch.randn((3, 64, 128), generator=torch.Generator().manual_seed(87)).to(torch.bfloat16)
+    sc = float(np.float32(synth.SOFTMAX_SCALE))
+    vsc = float(np.float32(0.707))
+    sink = x.sink.numpy()
+    args = (_bits(x.q), _bits(x.k), _bits(x.v), _bits(dout), x.cu_seqlens.numpy())
+    dq, dk, dv, ds = orc.prefill_backward(*args, layer_type=GA, scale=sc, value_scale=vsc, sink=sink,
+                                          stored_out=True)
+    exact = orc.prefill_backward(*args, layer_type=GA, scale=sc, value_scale=vsc, sink=sink)
+    assert np.array_equal(dv, exact[2]), "dv depends on D"
+    assert not np.array_equal(dk, exact[1]), "the stored output's rounding did not reach dk"
+    q, k, v, do = _f64(x.q).numpy(), _f64(x.k).numpy(), _f64(x.v).numpy(), _f64(dout).numpy()
+    want_ds = np.zeros(64)
+    wk = np.zeros((3, 4, 192))
+    for t in range(3):
+        for h in range(64):
+            g = h // 16
+            P = 1.0 / (1.0 + math.exp(float(sink[h]) - sc * float(q[t, h] @ k[t, g])))
+            out = _bf16_nearest_even(vsc * P * v[t, g])
+            Dp = float(do[t, h] @ out)
+            dS = P * (vsc * float(do[t, h] @ v[t, g]) - Dp)
+            _close(dq[t, h], sc * dS * k[t, g], 1e-12, f"stored-out one-token dq t={t} h={h}")
+            wk[t, g] += sc * dS * q[t, h]
+            want_ds[h] -= (1.0 - P) * Dp
+    _close(dk, wk, 1e-11, "stored-out one-token dk")
+    _close(ds, want_ds, 1e-11, "stored-out one-token dsink")
+    for lt in (SWA, GA):
+        a = orc.prefill_backward(*args, layer_type=lt, scale=sc, sink=None, stored_out=True)
+        b = orc.prefill_backward(*args, layer_type=lt, scale=sc, sink=None)
+        for u, w in zip(a[:3], b[:3]):
+            assert np.array_equal(u, w), "an exact bf16 output changed the gradients"
+
+
 def pin_backward_rows_and_neg_inf_sink(orc):
     """Sampled rows equal the full computation, and a sink of -inf gives the
     no-sink gradients with dsink 0."""

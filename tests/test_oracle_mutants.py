@@ -98,7 +98,8 @@ MUTANTS = {
     "paged append writes tokens on unmapped blocks": (
         "            if (page < 0 || page >= num_pages) {\n                status = ORACLE_ECAPACITY;\n                continue;\n            }\n",
         "            if (page >= num_pages) {\n                status = ORACLE_ECAPACITY;\n                continue;\n            }\n"),
-    "E4M3 rounds half away from zero": ("    double r = nearbyint(a / step) * step;", "    double r = round(a / step) * step;"),
+    "E4M3 rounds half away from zero": ("    double step = ldexp(1.0, b - 3);\n    double r = nearbyint(a / step) * step;",
+                                        "    double step = ldexp(1.0, b - 3);\n    double r = round(a / step) * step;"),
     "E4M3 not saturated at 448": ("    if (a > 448.0) a = 448.0;\n", "\n"),
     "E4M3 subnormal step one binade off": ("    int b = -6;\n", "    int b = -7;\n"),
     "E4M3 decode exponent bias off by one": ("    return sgn * ldexp(1.0 + (double)m / 8.0, e - 7);\n",
@@ -130,8 +131,12 @@ MUTANTS = {
         "            if (d->layer_type == ORACLE_SWA && p + d->window - 1 < hi) hi = p + d->window - 1;\n",
         "            if (d->layer_type == ORACLE_SWA && p + d->window < hi) hi = p + d->window;\n"),
     "backward D from the value instead of the output": (
-        "                for (int e = 0; e < d->dv; ++e) D += bf16_to_double(dorow[e]) * o[e];\n",
-        "                for (int e = 0; e < d->dv; ++e) D += bf16_to_double(dorow[e]) * o[e] / d->value_scale;\n"),
+        "                    D += bf16_to_double(dorow[e]) * (jb->stored_out ? round_bf16(o[e]) : o[e]);\n",
+        "                    D += bf16_to_double(dorow[e]) * (jb->stored_out ? round_bf16(o[e]) : o[e]) / d->value_scale;\n"),
+    "backward stored output left unrounded": ("(jb->stored_out ? round_bf16(o[e]) : o[e])", "o[e]"),
+    "bf16 rounding truncates": ("    double step = ldexp(1.0, b - 7);\n    double r = nearbyint(a / step) * step;",
+                                "    double step = ldexp(1.0, b - 7);\n    double r = floor(a / step) * step;"),
+    "bf16 rounding keeps one bit too few": ("    double step = ldexp(1.0, b - 7);\n", "    double step = ldexp(1.0, b - 6);\n"),
     "rope pairs neighbours instead of halves": ("        double a = bf16_to_double(x[i]), b = bf16_to_double(x[i + half]);\n",
                                                 "        double a = bf16_to_double(x[i]), b = bf16_to_double(x[(i ^ 1)]);\n"),
     "rope rotates the wrong way": ("        out[i] = a * c - b * sn;\n", "        out[i] = a * c + b * sn;\n"),
