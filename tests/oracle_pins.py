@@ -774,6 +774,69 @@ def pin_backward_rows_and_neg_inf_sink(orc):
         assert not ninf[3].any()
 
 
+def _transformers_attention(layer_type, window, q, k, v, sinks, value_scale, scale):
+    """One sequence through the installed Transformers MiMo-V2-Flash attention
+    module (MiMoV2FlashAttention.forward, eager path, fp64): its projections are
+    selection matrices that hand it q, k and v unchanged, the rotary embedding is
+    the identity (cos 1, sin 0), the additive mask is the library's own causal or
+    sliding-window mask for `window`, and the output projection reads the heads'
+    outputs back.  Returns out [L][Hq][Dv]."""
+    from transformers.masking_utils import causal_mask_function, eager_mask, sliding_window_causal_mask_function
+    from transformers.models.mimo_v2_flash import modeling_mimo_v2_flash as mm
+    from transformers.models.mimo_v2_flash.configuration_mimo_v2_flash import MiMoV2FlashConfig
+    L, hq, dqk = q.shape
+    hkv, dv = k.shape[1], v.shape[2]
+    swa = layer_type == SWA
+    nq, nk, nv, no = hq * dqk, hkv * dqk, hkv * dv, hq * dv
+    hidden = nq + nk + nv
+    cfg = MiMoV2FlashConfig(hidden_size=hidden, num_attention_heads=hq,
+                            num_key_value_heads=hkv // 2 if swa else hkv,  # the library doubles SWA's KV heads
+                            head_dim=dqk, v_head_dim=dv, num_hidden_layers=1, sliding_window=window,
+                            layer_types=["sliding_attention" if swa else "full_attention"],
+                            attention_value_scale=value_scale)
+    cfg._attn_implementation = "eager"
+    mod = mm.MiMoV2FlashAttention(cfg, 0).double().eval()
+    assert mod.num_key_value_groups == hq // hkv and (mod.sinks is not None) == swa
+    eye = torch.eye(hidden, dtype=torch.float64)
+    with torch.no_grad():
+        mod.q_proj.weight.copy_(eye[:nq])
+        mod.k_proj.weight.copy_(eye[nq:nq + nk])
+        mod.v_proj.weight.copy_(eye[nq + nk:])
+        mod.o_proj.weight.copy_(torch.eye(hidden, no, dtype=torch.float64))
+        if swa:
+            mod.sinks.copy_(torch.as_tensor(sinks, dtype=torch.float64))
+    mod.scaling = scale
+    x = torch.cat([q.reshape(L, nq), k.reshape(L, nk), v.reshape(L, nv)], dim=1)[None]
+    cos = torch.ones((1, L, dqk), dtype=torch.float64)
+    sin = torch.zeros((1, L, dqk), dtype=torch.float64)
+    fn = sliding_window_causal_mask_function(window) if swa else causal_mask_function
+    mask = eager_mask(1, L, L, mask_function=fn, dtype=torch.float64)
+    with torch.no_grad():
+        out, _ = mod(x, (cos, sin), attention_mask=mask)
+    return out[0, :, :no].reshape(L, hq, dv).numpy()
+
+
+def pin_prefill_equals_transformers_attention_module(orc):
+    """The oracle's prefill equals the installed Transformers MiMo-V2-Flash
+    attention module run on the same q, k, v in fp64: its sink is one more logit
+    per head, taken unscaled and dropped after the softmax (reading: denominator
+    only), its value scale multiplies V before the attention (the same as scaling
+    the output), its GQA repeats each KV head for a contiguous group of query
+    heads, and its sliding-window mask for window W keeps the W keys up to and
+    including the query.  SWA layers with a sink (windows 1, 4, 129 > L) and a GA
+    layer without one, 4 query heads over 2 KV heads."""
+    vs = float(np.float32(0.707))
+    scale = float(np.float32(8 ** -0.5))
+    for lt, window, seed in ((SWA, 4, 90), (SWA, 1, 91), (SWA, 129, 92), (GA, 129, 93)):
+        x = _make([23], seed=seed, hq=4, hkv=2, dqk=8, dv=6)
+        sink = x.sink.numpy() * 3.0 if lt == SWA else None
+        o, _ = orc.prefill(_bits(x.q), _bits(x.k), _bits(x.v), x.cu_seqlens.numpy(), layer_type=lt, window=window,
+                           scale=scale, value_scale=vs, sink=None if sink is None else sink.astype(np.float32))
+        ref = _transformers_attention(lt, window, _f64(x.q), _f64(x.k), _f64(x.v),
+                                      None if sink is None else sink.astype(np.float32).astype(np.float64), vs, scale)
+        _close(o, ref, 1e-12, f"transformers module lt={lt} W={window}")
+
+
 # -- rotary embedding ---------------------------------------------------------
 
 def _rope_inputs(T, seed):
