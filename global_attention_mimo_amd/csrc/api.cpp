@@ -684,14 +684,18 @@ int mimo_attn_prefill_backward(const mimo_attn_dims* dims, int layer_type, const
     if ((int64_t)total_tokens * dims->num_q_heads > (int64_t)INT32_MAX * 8)
         return fail(MIMO_ERR_UNSUPPORTED, "total_tokens %d is too large", total_tokens);
     const size_t need = mimo::backward_workspace_bytes(total_tokens, dims->num_q_heads);
-    if (max_seqlen == 0 || total_tokens == 0) return ok();
+    mimo::BackwardArgs a{q, k, v, out, lse, dout, cu_seqlens, sink, dq, dk, dv, dsink, workspace, num_seqs,
+                         max_seqlen, total_tokens, dims->num_q_heads, dims->num_kv_heads, dims->sliding_window,
+                         dims->softmax_scale, dims->value_scale, layer_type == MIMO_LAYER_SWA};
+    if (max_seqlen == 0 || total_tokens == 0) {
+        // Nothing contributes: no workspace is used, only dsink (if given) is written, as zeros.
+        if (!dsink) return ok();
+        return hip_status(mimo::launch_prefill_backward(a, stream), "backward launch");
+    }
     if (!workspace || workspace_bytes < need)
         return fail(MIMO_ERR_WORKSPACE, "backward needs %zu workspace bytes (got %zu%s)", need, workspace_bytes,
                     workspace ? "" : ", NULL");
     if (!aligned16(workspace)) return fail(MIMO_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-    mimo::BackwardArgs a{q, k, v, out, lse, dout, cu_seqlens, sink, dq, dk, dv, dsink, workspace, num_seqs,
-                         max_seqlen, total_tokens, dims->num_q_heads, dims->num_kv_heads, dims->sliding_window,
-                         dims->softmax_scale, dims->value_scale, layer_type == MIMO_LAYER_SWA};
     mimo::CheckArgs c;
     c.cu = cu_seqlens;
     c.n_seqs = num_seqs;

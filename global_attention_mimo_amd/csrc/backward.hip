@@ -136,7 +136,7 @@ __global__ __launch_bounds__(256) void bwd_sink_kernel(const float* __restrict__
         if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
         __syncthreads();
     }
-    if (threadIdx.x == 0) dsink[h] = -part[0];
+    if (threadIdx.x == 0) dsink[h] = 0.0f - part[0];  // +0 for an empty sum (0 - x is exactly -x otherwise)
 }
 
 // ---------------------------------------------------------------------------
@@ -512,7 +512,15 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void bwd_dkdv_
 }  // namespace
 
 hipError_t launch_prefill_backward(const BackwardArgs& a, hipStream_t stream) {
-    if (a.max_seqlen <= 0 || a.total_tokens <= 0) return hipSuccess;
+    if (a.max_seqlen <= 0 || a.total_tokens <= 0) {
+        // No token contributes: there are no rows to write, and dsink, a sum
+        // over no tokens, is zero (the sink kernel over zero sequences reads
+        // nothing and writes it).
+        if (!a.dsink) return hipSuccess;
+        hipLaunchKernelGGL(bwd_sink_kernel, dim3(a.hq), dim3(256), 0, stream, a.sink, nullptr, nullptr, a.cu_seqlens,
+                           0, 0, a.hq, a.dsink);
+        return hipGetLastError();
+    }
     float* D = static_cast<float*>(a.workspace);
     const int64_t rows = (int64_t)a.total_tokens * a.hq;
     hipLaunchKernelGGL(bwd_rowdot_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, a.dout, a.out, D,

@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define MIMO_ATTN_ABI_VERSION 13
+#define MIMO_ATTN_ABI_VERSION 14
 
 /* Layer type: which key set a query sees (model doc, Key features; config
  * layer_types). */
@@ -489,7 +489,9 @@ int mimo_attn_prefill_chunk_fp8_paged(const mimo_attn_dims* dims,
  *   dsink        [Hq] fp32, or NULL to skip; all zero when sink is NULL.
  *   workspace    >= mimo_attn_prefill_backward_workspace_size(dims,
  *                total_tokens) bytes of device memory, no initialisation.
- * A call with max_seqlen == 0 or total_tokens == 0 enqueues nothing.
+ * A call with max_seqlen == 0 or total_tokens == 0 computes no rows (dq, dk
+ * and dv are left unwritten) and needs no workspace; it writes dsink, when
+ * given, as zeros (a sum over no tokens).
  */
 size_t mimo_attn_prefill_backward_workspace_size(const mimo_attn_dims* dims, int32_t total_tokens);
 
