@@ -267,11 +267,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_pe
         // (at the top: equal time).  Past the last tile they read through an
         // empty descriptor.
         load_tile(kt + 1);
+        // Key offset o = 8(r/4) + (r%4) of element r is kept when lo <= o <= hi:
+        // the row's causal bound (and window) relative to this lane's keys, with
+        // rows past the sequence end given an empty range.
+        const int hi = valid ? tok - kbase - 4 * hh : -1;
+        const int lo = SWA ? hi - (window - 1) : INT32_MIN;
         float ds[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int key = kbase + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const bool ok = valid && key <= tok && (!SWA || key >= tok - (window - 1));
+            const int o = 8 * (r >> 2) + (r & 3);
+            const bool ok = o <= hi && (!SWA || o >= lo);
             const float p = fast_exp2(ok ? __builtin_fmaf(s[r], c_log2, -lse2) : -__builtin_inff());  // masked: 0
             ds[r] = p * (value_scale * dp[r] - Drow);
         }
