@@ -85,7 +85,7 @@ def test_random_case(case):
     compare(out, lse, ro, rl, f"random case {case} ({kind})")
 
 
-N_BACKWARD = 16
+N_BACKWARD = 40
 
 
 @pytest.mark.parametrize("case", range(N_BACKWARD))
