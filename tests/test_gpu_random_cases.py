@@ -28,7 +28,7 @@ from test_gpu_chunk import _caches, _chunk, _fill
 from test_gpu_decode import SCALE, gpu_decode, oracle_decode
 
 pytestmark = pytest.mark.gpu
-N_CASES = 48
+N_CASES = 96
 
 
 def _sink(rng, x):
@@ -109,7 +109,7 @@ def test_random_backward_case(case):
     grad_compare(ds, rs, "dsink")
 
 
-N_APPEND = 8
+N_APPEND = 16
 
 
 @pytest.mark.parametrize("case", range(N_APPEND))
@@ -128,7 +128,7 @@ def test_random_decode_append_case(case):
     assert torch.equal(k0, k1) and torch.equal(v0, v1), "caches differ"
 
 
-N_PAGED = 8
+N_PAGED = 16
 
 
 @pytest.mark.parametrize("case", range(N_PAGED))
@@ -177,7 +177,7 @@ def test_random_paged_decode_case(case):
     compare(op, lp, ro, rl, f"random paged decode case {case}")
 
 
-N_FP8 = 6
+N_FP8 = 12
 
 
 @pytest.mark.parametrize("case", range(N_FP8))
@@ -224,7 +224,7 @@ def test_random_fp8_decode_case(case):
     compare(out, lse, ro, rl, f"random FP8 decode case {case} (sink {sc})")
 
 
-N_ROPE = 9
+N_ROPE = 18
 
 
 @pytest.mark.parametrize("case", range(N_ROPE))
