@@ -102,9 +102,17 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
 // FP8 GA pool (contiguous, or paged as above): one thread turns 8 bf16
 // elements (16 bytes) of a new token into 8 E4M3 codes (8 bytes).  A token is Hkv*24 such units of K then Hkv*16 of V;
 // unit c of K belongs to KV head c / 24, of V to head c / 16.  Each element is
-// divided by its head's scale in fp32 (IEEE division), clamped to +-448 (the
-// conversion does not saturate by itself) and rounded to nearest-even by the
-// hardware conversion.
+// divided by its head's scale in fp32, clamped to +-448 (the conversion does
+// not saturate by itself) and rounded to nearest-even by the hardware
+// conversion.  The codes are those of the IEEE fp32 quotient; the quotient is
+// formed from the correctly rounded reciprocal y = 1/b (one division per
+// thread) by Markstein's correction: q0 = a*y, r = fma(-b, q0, a) (exact),
+// q = fma(r, y, q0), which equals the rounded a/b when nothing underflows or
+// overflows (P. Markstein, "Computation of elementary functions on the IBM
+// RISC System/6000 processor", 1990).  A q0 that overflows is kept (it clamps
+// to +-448 as the true quotient does), as is a zero q0 (its sign then stays).
+// Below the normal range q can differ from a/b by an ulp; such quotients are
+// far below the smallest E4M3 step and give the same code.
 __global__ __launch_bounds__(256) void kv_append_fp8_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const int32_t* __restrict__ cu_newlens,
     const int32_t* __restrict__ ctx_lens, int batch, int total_new, uint8_t* __restrict__ k_cache,
@@ -142,8 +150,14 @@ __global__ __launch_bounds__(256) void kv_append_fp8_kernel(
         x[2 * i] = __builtin_bit_cast(float, w[i] << 16);
         x[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
     }
+    const float y = 1.0f / scale;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = fminf(fmaxf(x[i] / scale, -448.0f), 448.0f);
+    for (int i = 0; i < 8; ++i) {
+        const float q0 = x[i] * y;
+        const float q = __builtin_fmaf(__builtin_fmaf(-scale, q0, x[i]), y, q0);
+        const float qs = (q0 == 0.0f || !__builtin_isfinite(q0)) ? q0 : q;
+        x[i] = fminf(fmaxf(qs, -448.0f), 448.0f);
+    }
     int lo4 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
     lo4 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], lo4, true);
     int hi4 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4], x[5], 0, false);

@@ -65,6 +65,48 @@ def test_fp8_append_bytes():
     assert kr[base[1] + 2, 2, 0] == 0x7E and kr[base[1] + 2, 2, 1] == 0xFE  # saturated
 
 
+def _every_bf16_token_rows(width):
+    """Every finite bf16 bit pattern (the 254 NaN patterns left out), laid out
+    row-major in [T][4][width] tokens (zero-padded)."""
+    pats = np.arange(65536, dtype=np.uint32)
+    exp, man = (pats >> 7) & 0xFF, pats & 0x7F
+    pats = pats[~((exp == 0xFF) & (man != 0))].astype(np.uint16)
+    T = -(-pats.size // (4 * width))
+    a = np.zeros(T * 4 * width, np.uint16)
+    a[:pats.size] = pats
+    return a.reshape(T, 4, width)
+
+
+@pytest.mark.parametrize("k_scale,v_scale", [
+    ([1.0, 0.01, 4.5 / 448, 0.7], [448.0, 3.0, 1.0 / 448, 0.1]),
+    ([1e-30, 3e38, 1e-38, 1.9999999], [0.0173, 7.0, 1e-20, 1e20]),
+])
+def test_fp8_append_every_bf16_value(k_scale, v_scale):
+    """Every finite bf16 value through the quantising append (as K and as V),
+    under ordinary, tiny and huge per-head scales: codes bit for bit against
+    the oracle's E4M3(clamp(x / scale)) with the fp32 IEEE quotient."""
+    ks, vs = np.float32(k_scale), np.float32(v_scale)
+    kb, vb = _every_bf16_token_rows(192), _every_bf16_token_rows(128)
+    T = max(kb.shape[0], vb.shape[0])
+    kh = np.zeros((T, 4, 192), np.uint16)
+    vh = np.zeros((T, 4, 128), np.uint16)
+    kh[:kb.shape[0]], vh[:vb.shape[0]] = kb, vb
+    log(f"[case] FP8 append of every bf16 value: {T} tokens, K scales {ks.tolist()}, V scales {vs.tolist()}")
+    as_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(DEV)
+    kc, vc = _pools(T)
+    cu = np.array([0, T], np.int32)
+    base, caps = np.zeros(1, np.int64), np.array([T], np.int64)
+    B.kv_append_fp8(as_dev(kh), as_dev(vh), torch.tensor(cu, device=DEV), torch.zeros(1, dtype=torch.int32, device=DEV),
+                    kc, vc, torch.tensor(base, device=DEV), torch.tensor(caps, device=DEV), torch.tensor(ks, device=DEV),
+                    torch.tensor(vs, device=DEV))
+    kr, vr = np.zeros((T, 4, 192), np.uint8), np.zeros((T, 4, 128), np.uint8)
+    orc().kv_append_fp8(kh, vh, cu, np.zeros(1, np.int32), kr, vr, base, caps, ks, vs)
+    torch.cuda.synchronize()
+    gk, gv = kc.cpu().numpy(), vc.cpu().numpy()
+    nk, nv = int((gk != kr).sum()), int((gv != vr).sum())
+    assert nk == 0 and nv == 0, f"{nk} K and {nv} V codes differ from the oracle's"
+
+
 @pytest.mark.parametrize("split", [0, 96])
 def test_fp8_decode_against_oracle(split):
     """Contexts on and around tile and split boundaries; the pool holds N(0,1)
