@@ -130,31 +130,40 @@ def test_backward_max_seqlen_bounds_rows():
     grad_compare(ds, rs, "dsink max_seqlen")
 
 
+def assert_vanishing(x, dout, dq, dk, what=""):
+    """dq and dk of one-token sequences without a sink at value_scale 1, whose
+    exact values are zero: the only weight is exactly 1 and the output is v, so
+    dS = dP - D = 0.  What is left is the fp32 rounding of two 128-term dot
+    products of bf16 values (dP by the MFMA, D by the row-dot kernel), each
+    within 128 u sum|dO v| with u = 2^-24 (the bound below allows twice both)."""
+    q, k, v, do = (t.float().numpy().astype(np.float64) for t in (x.q, x.k, x.v, dout))
+    T = q.shape[0]
+    g = np.arange(64) // 16
+    ds_bound = 4 * 128 * 2.0 ** -24 * np.abs(do * v[:, g]).sum(-1)            # [T][64]
+    q_bound = SCALE * ds_bound[..., None] * np.abs(k[:, g])                     # dq = scale dS k
+    k_bound = SCALE * (ds_bound[..., None] * np.abs(q)).reshape(T, 4, 16, 192).sum(2)
+    got_q = dq.float().cpu().numpy().astype(np.float64)
+    got_k = dk.float().cpu().numpy().astype(np.float64)
+    log(f"[parity] {what}one key: |dq| max {np.abs(got_q).max():.2e} (bound {q_bound.max():.2e}), "
+        f"|dk| max {np.abs(got_k).max():.2e} (bound {k_bound.max():.2e})")
+    assert (np.abs(got_q) <= q_bound).all(), "dq of a lone key does not vanish"
+    assert (np.abs(got_k) <= k_bound).all(), "dk of a lone key does not vanish"
+
+
 def test_backward_one_key_without_sink_vanishes():
-    """One-token sequences without a sink and value_scale 1: the only weight is
-    exactly 1 and the output is v, so dS = dP - D = 0 and dq, dk vanish; what is
-    left is the fp32 rounding of two 128-term dot products of bf16 values
-    (dP by the MFMA, D by the row-dot kernel), each within 128 u sum|dO v|
-    with u = 2^-24.  dv = sum over the group of dO, against the oracle."""
+    """One-token sequences without a sink and value_scale 1: dq and dk vanish
+    (within the rounding bound of assert_vanishing); dv = sum over the group of
+    dO, against the oracle."""
     lengths = [1, 1, 1, 1, 1]
     log(f"[case] backward one key, no sink: lengths {lengths}")
     x = synth.prefill_inputs(lengths, seed=98)
     dout = dout_like(len(lengths), 99)
     dq, dk, dv, ds = run(x, dout, GA, value_scale=1.0, sink=None)
-    _, _, rv, _ = oracle_grads(x, dout, GA, value_scale=1.0, sink=None)
+    rq, rk, rv, _ = oracle_grads(x, dout, GA, value_scale=1.0, sink=None)
+    assert not rq.any() and not rk.any(), "the oracle's dq and dk of lone keys are not zero"
     grad_compare(dv, rv, "dv one key")
     assert not ds.any(), "dsink without a sink must be 0"
-    q, k, v, do = (t.float().numpy().astype(np.float64) for t in (x.q, x.k, x.v, dout))
-    g = np.arange(64) // 16
-    ds_bound = 4 * 128 * 2.0 ** -24 * np.abs(do * v[:, g]).sum(-1)            # [T][64]
-    q_bound = SCALE * ds_bound[..., None] * np.abs(k[:, g])                     # dq = scale dS k
-    k_bound = SCALE * (ds_bound[..., None] * np.abs(q)).reshape(len(lengths), 4, 16, 192).sum(2)
-    got_q = dq.float().cpu().numpy().astype(np.float64)
-    got_k = dk.float().cpu().numpy().astype(np.float64)
-    log(f"[parity] one key: |dq| max {np.abs(got_q).max():.2e} (bound {q_bound.max():.2e}), "
-        f"|dk| max {np.abs(got_k).max():.2e} (bound {k_bound.max():.2e})")
-    assert (np.abs(got_q) <= q_bound).all(), "dq of a lone key does not vanish"
-    assert (np.abs(got_k) <= k_bound).all(), "dk of a lone key does not vanish"
+    assert_vanishing(x, dout, dq, dk)
 
 
 def test_backward_ga_1x32768_sampled():
